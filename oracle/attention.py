@@ -1,0 +1,114 @@
+"""fp64 paged decode attention: reassemble each sequence's K/V, then attend.
+
+Test infrastructure only (see the package docstring).
+
+What is computed (the pages' statement of the problem):
+
+* A sequence's cache is a list of fixed-size blocks found through its block
+  table: logical block j holds token positions [j*bs, (j+1)*bs) and lives in
+  physical block ``table[j]`` ("03 · PagedAttention", "Blocks and block tables";
+  "Serving: vLLM and PagedAttention", section 2.2).
+* One decode step scores the new query against every key of the sequence,
+  gathering K and V from the listed blocks ("PagedAttention" daily term,
+  decode-step figure).
+* The result is the ordinary attention over the sequence's tokens in logical
+  order: only the layout differs from a contiguous cache ("paged-attention"
+  lesson, closing paragraph; "PagedAttention" daily term, "Pros": not an
+  approximation).
+
+So: out[i, h] = sum_t softmax_t(sigma * q[i,h] . K_i[t, g]) * V_i[t, g] with
+g = h // G (grouped-query attention, consecutive grouping), over the L_i tokens
+of sequence i; a row with L_i <= 0 is zero.
+
+Storage layout of the pools (the pages fix none; the reading taken):
+  k_cache[P][Hkv][bs][d]   token-major within each (block, kv-head) tile
+  v_cache[P][Hkv][d][bs]   channel-major within each (block, kv-head) tile
+Both tiles are contiguous, and the bs tokens of a block sit together in each.
+
+Element storage: "f32" float32, "bf16" uint16 bit patterns, "fp8" uint8 OCP
+E4M3 codes whose value is decode(code) * scale (one float32 scale per tensor).
+"""
+
+import numpy as np
+
+from .codecs import bf16_bits_to_f64, f32_to_f64, e4m3_decode
+
+
+def widen(arr, dtype, scale=1.0):
+    """Stored elements -> exact float64 values (fp8 includes the tensor scale)."""
+    if dtype == "f32":
+        return f32_to_f64(arr)
+    if dtype == "bf16":
+        return bf16_bits_to_f64(arr)
+    if dtype == "fp8":
+        # decode(code) has at most 4 significant bits and the scale 24, so the
+        # float64 product is exact.
+        return e4m3_decode(arr) * np.float64(np.float32(scale))
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def reassemble(pool, table_row, L, bs, which):
+    """Gather one sequence's K or V into logical order: [L][Hkv][d] (storage dtype).
+
+    ``which`` is "k" for the [P][Hkv][bs][d] pool and "v" for the
+    [P][Hkv][d][bs] pool. Position p lives in logical block p // bs at offset
+    p % bs (0-based positions).
+    """
+    P = pool.shape[0]
+    n = -(-L // bs)
+    ids = np.asarray(table_row[:n], dtype=np.int64)
+    if n and (ids.min() < 0 or ids.max() >= P):
+        raise ValueError("block table entry outside the pool")
+    tiles = pool[ids]
+    if which == "k":            # [n][Hkv][bs][d] -> [n][bs][Hkv][d]
+        tiles = tiles.transpose(0, 2, 1, 3)
+    elif which == "v":          # [n][Hkv][d][bs] -> [n][bs][Hkv][d]
+        tiles = tiles.transpose(0, 3, 1, 2)
+    else:
+        raise ValueError(which)
+    flat = tiles.reshape(n * bs, tiles.shape[2], tiles.shape[3])
+    return flat[:L]
+
+
+def contiguous_decode_attn(q_i, K, V, sigma):
+    """Textbook single-query attention over contiguous float64 K/V.
+
+    q_i: [Hq][d]; K, V: [L][Hkv][d]; sigma: the softmax scale. Returns [Hq][d].
+    """
+    Hq, d = q_i.shape
+    L, Hkv, _ = K.shape
+    G = Hq // Hkv
+    if L <= 0:
+        return np.zeros((Hq, d))
+    qg = q_i.reshape(Hkv, G, d)
+    Kh = K.transpose(1, 0, 2)              # [Hkv][L][d]
+    Vh = V.transpose(1, 0, 2)
+    s = sigma * (qg @ Kh.transpose(0, 2, 1))   # [Hkv][G][L]
+    m = s.max(axis=-1, keepdims=True)
+    p = np.exp(s - m)
+    o = (p @ Vh) / p.sum(axis=-1, keepdims=True)
+    return o.reshape(Hq, d)
+
+
+def paged_decode_attn(q, k_cache, v_cache, block_tables, context_lens, *, bs,
+                      softmax_scale, q_dtype, cache_dtype, k_scale=1.0, v_scale=1.0,
+                      seqs=None):
+    """Oracle output, float64 [S][Hq][d] (or only the rows in ``seqs``).
+
+    softmax_scale is taken as the float32 value the kernel receives, widened.
+    """
+    S, Hq, d = q.shape
+    sigma = np.float64(np.float32(softmax_scale))
+    ks = k_scale if cache_dtype == "fp8" else 1.0
+    vs = v_scale if cache_dtype == "fp8" else 1.0
+    rows = range(S) if seqs is None else seqs
+    out = np.zeros((S, Hq, d)) if seqs is None else np.zeros((len(seqs), Hq, d))
+    for r, i in enumerate(rows):
+        L = int(context_lens[i])
+        if L <= 0:
+            continue
+        K = widen(reassemble(k_cache, block_tables[i], L, bs, "k"), cache_dtype, ks)
+        V = widen(reassemble(v_cache, block_tables[i], L, bs, "v"), cache_dtype, vs)
+        qi = widen(q[i], q_dtype)
+        out[r] = contiguous_decode_attn(qi, K, V, sigma)
+    return out

@@ -1,0 +1,62 @@
+"""The KV-cache write: scatter each new token's K and V into its physical slot.
+
+Test infrastructure only (see the package docstring).
+
+The decode-step figure of the "PagedAttention" daily term puts "write the new K
+and V into the current block" in the same per-step launch as the gather. A slot
+is the flat index block * bs + offset; slot -1 means "skip this token" (padding).
+
+Per token t with slot >= 0: (b, o) = divmod(slot, bs), then for every kv head h
+and channel c
+    K[b][h][o][c] = enc(K_new[t][h][c])        (k_cache is [P][Hkv][bs][d])
+    V[b][h][c][o] = enc(V_new[t][h][c])        (v_cache is [P][Hkv][d][bs])
+Every other element of the pools is left as it was.
+
+enc is the identity on the stored bits when source and cache dtypes agree
+(f32 -> f32, bf16 -> bf16). For an fp8 cache the source (bf16) value x becomes
+e4m3_encode(float32(x) * float32(inv_scale)): one float32 multiplication rounded
+to nearest-even, then the codec of ``codecs.py``.
+"""
+
+import numpy as np
+
+from .codecs import bf16_bits_to_f64, e4m3_encode
+
+
+def _quantise(x_bits, src_dtype, inv_scale):
+    if src_dtype == "bf16":
+        x = bf16_bits_to_f64(x_bits).astype(np.float32)    # exact
+    elif src_dtype == "f32":
+        x = np.asarray(x_bits, dtype=np.float32)
+    else:
+        raise ValueError(src_dtype)
+    y = x * np.float32(inv_scale)                          # float32 product, RNE
+    return e4m3_encode(y)
+
+
+def kv_cache_write(k_new, v_new, k_cache, v_cache, slot_mapping, *, bs, src_dtype,
+                   cache_dtype, k_inv_scale=1.0, v_inv_scale=1.0):
+    """Return (k_cache', v_cache'): copies of the pools with the new tokens written.
+
+    k_new, v_new: [T][Hkv][d] in the source storage dtype; slot_mapping: int64[T].
+    """
+    k_out = np.array(k_cache, copy=True)
+    v_out = np.array(v_cache, copy=True)
+    if cache_dtype == "fp8":
+        kq = _quantise(k_new, src_dtype, k_inv_scale)
+        vq = _quantise(v_new, src_dtype, v_inv_scale)
+    elif cache_dtype == src_dtype:
+        kq = np.asarray(k_new)
+        vq = np.asarray(v_new)
+    else:
+        raise ValueError(f"unsupported write {src_dtype} -> {cache_dtype}")
+    P = k_cache.shape[0]
+    for t, slot in enumerate(np.asarray(slot_mapping, dtype=np.int64)):
+        if slot < 0:
+            continue
+        b, o = divmod(int(slot), bs)
+        if b >= P:
+            raise ValueError("slot outside the pool")
+        k_out[b, :, o, :] = kq[t]
+        v_out[b, :, :, o] = vq[t]
+    return k_out, v_out
