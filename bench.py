@@ -1,0 +1,270 @@
+#!/usr/bin/env python3
+"""Benchmark one decode step of paged attention on one MI355X.
+
+A step is the whole hot path over one batch: the KV-cache write of each
+sequence's new token (pkv_kv_cache_write), then paged decode attention over
+every sequence's context including that token (pkv_paged_decode_attn: the
+partition kernel and, for split sequences, the merge kernel). Inputs are
+seeded synthetic workloads already resident in HBM.
+
+Timing: W untimed warm-up steps, then K timed steps. Before each timed step
+(outside its event pair) a 1 GiB buffer is written so neither the 256 MB
+Infinity Cache nor L2 still holds the KV pool; each step is bracketed by HIP
+events on the stream the kernels run on, with a third event between the write
+and the attention call. Bytes are algorithmic: what the method must move (each
+valid token's K and V once, shared blocks once, q, the fp32 output, the table
+entries and lengths; for the write, the new tokens read and stored and the slot
+mapping).
+
+Prints ONE JSON line.
+"""
+
+import argparse
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published peak
+
+ELEM = {"f32": 4, "bf16": 2, "fp8": 1}
+
+
+def algorithmic_bytes(w, cache_dtype):
+    """(attention bytes, write bytes, logical KV bytes) for one step of workload w."""
+    s = w.spec
+    bs, Hkv, d = s.bs, s.Hkv, s.d
+    fill = {}
+    n_entries = 0
+    for i, L in enumerate(w.context_lens):
+        L = int(L)
+        n = -(-L // bs) if L > 0 else 0
+        n_entries += n
+        for j in range(n):
+            b = int(w.block_tables[i, j])
+            f = min(bs, L - j * bs)
+            if f > fill.get(b, 0):
+                fill[b] = f
+    unique_tokens = sum(fill.values())
+    logical_tokens = int(np.maximum(w.context_lens, 0).sum())
+    kv_elem = ELEM[cache_dtype]
+    kv = unique_tokens * 2 * Hkv * d * kv_elem
+    q = s.S * s.Hq * d * ELEM[s.q_dtype]
+    out = s.S * s.Hq * d * 4
+    attn = kv + q + out + 4 * n_entries + 4 * s.S
+    T = s.S
+    write = T * 2 * Hkv * d * (ELEM[s.src_dtype] + kv_elem) + 8 * T
+    return attn, write, logical_tokens * 2 * Hkv * d * kv_elem, unique_tokens
+
+
+def _oracle_pools(w, cache_dtype, seqs):
+    """The oracle's own pools after this step's write, for the listed sequences'
+    blocks (fp8: the oracle quantises those blocks itself). Not timed."""
+    import oracle
+    s = w.spec
+    slots = oracle.decode_slots(w.block_tables, w.context_lens, s.bs)
+    if cache_dtype != "fp8":
+        return oracle.kv_cache_write(w.k_new, w.v_new, w.k_pool, w.v_pool, slots, bs=s.bs,
+                                     src_dtype=s.src_dtype, cache_dtype=cache_dtype)
+    blocks = np.unique(w.block_tables[seqs].reshape(-1))
+    blocks = blocks[blocks >= 0]
+    kq = np.zeros(w.k_pool.shape, dtype=np.uint8)
+    vq = np.zeros(w.v_pool.shape, dtype=np.uint8)
+    kq[blocks] = oracle.quantise(w.k_pool[blocks], "bf16", w.k_inv_scale)
+    vq[blocks] = oracle.quantise(w.v_pool[blocks], "bf16", w.v_inv_scale)
+    return oracle.kv_cache_write(w.k_new, w.v_new, kq, vq, slots, bs=s.bs, src_dtype="bf16",
+                                 cache_dtype="fp8", k_inv_scale=w.k_inv_scale,
+                                 v_inv_scale=w.v_inv_scale)
+
+
+def cpu_baseline(w, cache_dtype, budget_s=12.0):
+    """Time the fp64 oracle (as it stands) on a bounded sample of sequences:
+    sequences in order, one call each, until the time budget is spent."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([t.get("num_threads", 1) for t in threadpool_info()] + [1])
+    except Exception:
+        threads = 1
+    s = w.spec
+    # sequences the budget can plausibly cover (bounded prep for big pools)
+    est = max(1, min(s.S, int(budget_s * 2e8 / max(1, 2 * s.Hkv * s.d * 8 * np.mean(w.context_lens)))))
+    kc, vc = _oracle_pools(w, cache_dtype, list(range(min(s.S, est + 2))))
+    done, t_used, kv_bytes = [], 0.0, 0
+    sample = list(range(min(s.S, est + 2)))
+    for n in range(10**6):                 # passes over the sample until the budget is spent
+        i = sample[n % len(sample)]
+        t0 = time.perf_counter()
+        oracle.paged_decode_attn(w.q, kc, vc, w.block_tables, w.context_lens, bs=s.bs,
+                                 softmax_scale=w.softmax_scale, q_dtype=s.q_dtype,
+                                 cache_dtype=cache_dtype, k_scale=w.k_scale, v_scale=w.v_scale,
+                                 seqs=[i])
+        t_used += time.perf_counter() - t0
+        done.append(i)
+        kv_bytes += int(w.context_lens[i]) * 2 * s.Hkv * s.d * ELEM[cache_dtype] \
+            + s.Hq * s.d * (ELEM[s.q_dtype] + 4)
+        if t_used >= budget_s:
+            break
+    return {
+        "value": round(len(done) / t_used, 3), "unit": "seq-steps/s",
+        "gbs": round(kv_bytes / t_used / 1e9, 4), "cores": int(threads),
+        "affinity_cpus": len(os.sched_getaffinity(0)), "kind": "oracle",
+        "sample": f"oracle paged_decode_attn, {len(done)} calls of one sequence each over "
+                  f"sequences 0..{len(sample) - 1} of {s.S} "
+                  f"({int(sum(int(w.context_lens[i]) for i in done))} tokens), {t_used:.1f} s",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="llama8b",
+                    choices=["tiny", "small", "llama8b", "beam", "long"])
+    ap.add_argument("--bs", type=int, default=None)
+    ap.add_argument("--kv", default=None, choices=[None, "bf16", "fp8", "f32"])
+    ap.add_argument("--partition", type=int, default=None)
+    ap.add_argument("--no-flush", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus_requested": args.gpus}))
+        sys.exit(2)
+
+    import torch
+    import paged_kv_cache_108_amd as pkv
+    from paged_kv_cache_108_amd import workloads as W
+
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(1)
+
+    w = W.make(args.config, bs=args.bs, cache_dtype=args.kv)
+    s = w.spec
+    cache_dtype = s.cache_dtype
+    part = s.partition_size if args.partition is None else args.partition
+
+    def dev(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(a).cuda()
+
+    q = dev(w.q)
+    tables = dev(w.block_tables)
+    lens = dev(w.context_lens)
+    k_new, v_new = dev(w.k_new), dev(w.v_new)
+    if cache_dtype == "fp8":
+        vk, vv = dev(w.k_pool), dev(w.v_pool)
+        k_cache = torch.empty(vk.shape, dtype=torch.uint8, device="cuda")
+        v_cache = torch.empty(vv.shape, dtype=torch.uint8, device="cuda")
+        pkv.quantise_pool(vk, vv, k_cache, v_cache, k_inv_scale=w.k_inv_scale,
+                          v_inv_scale=w.v_inv_scale)
+        del vk, vv
+    else:
+        k_cache, v_cache = dev(w.k_pool), dev(w.v_pool)
+    slots = dev(pkv.slots_from_tables(w.block_tables, w.context_lens - 1, s.bs))
+    out = torch.empty((s.S, s.Hq, s.d), dtype=torch.float32, device="cuda")
+    need = pkv.paged_decode_attn_workspace_size(s.S, s.Hq, s.d, w.max_context_len, part)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda") if need else None
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def write():
+        pkv.kv_cache_write(k_new, v_new, k_cache, v_cache, slots, k_inv_scale=w.k_inv_scale,
+                           v_inv_scale=w.v_inv_scale, stream=stream)
+
+    def attend():
+        pkv.paged_decode_attn(out, q, k_cache, v_cache, tables, lens,
+                              max_context_len=w.max_context_len, softmax_scale=w.softmax_scale,
+                              k_scale=w.k_scale, v_scale=w.v_scale, partition_size=part,
+                              workspace=ws, stream=stream)
+
+    for _ in range(args.warmup):
+        write()
+        attend()
+    torch.cuda.synchronize()
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    for k in range(args.steps):
+        if not args.no_flush:
+            flush.fill_(k & 0xFF)
+        a, b, c = ev[k]
+        a.record(stream)
+        write()
+        b.record(stream)
+        attend()
+        c.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+
+    step_ms = [a.elapsed_time(c) for a, b, c in ev]
+    write_ms = [a.elapsed_time(b) for a, b, c in ev]
+    attn_ms = [b.elapsed_time(c) for a, b, c in ev]
+    step_mean = statistics.mean(step_ms)
+    attn_mean = statistics.mean(attn_ms)
+
+    attn_bytes, write_bytes, logical_kv, unique_tokens = algorithmic_bytes(w, cache_dtype)
+    step_bytes = attn_bytes + write_bytes
+    value = step_bytes / (step_mean * 1e-3) / 1e9
+    attn_gbs = attn_bytes / (attn_mean * 1e-3) / 1e9
+    n_part = -(-w.max_context_len // part) if part else 1
+
+    result = {
+        "metric": "paged decode attention: achieved HBM GB/s (% of peak) and seq-steps/sec at 1 GPU",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_mean, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"f32": "f32", "bf16": "bf16", "fp8": "fp8-e4m3 KV, bf16 q"}[cache_dtype],
+        "data": "synthetic (seeded; N(0,1) values, lognormal lengths)",
+        "pct_of_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "seq_steps_per_s": round(s.S / (step_mean * 1e-3), 1),
+        "config": {
+            "workload": f"{s.name}: {s.description}",
+            "sequences": s.S, "q_heads": s.Hq, "kv_heads": s.Hkv, "head_dim": s.d,
+            "block_size": s.bs, "kv_dtype": cache_dtype, "partition_size": part,
+            "context_tokens": int(w.context_lens.sum()), "unique_tokens": int(unique_tokens),
+            "max_context_len": w.max_context_len, "pool_blocks": w.P,
+            "cache_flush_between_steps": not args.no_flush,
+        },
+        "timing": {
+            "step_ms_mean": round(step_mean, 5), "step_ms_median": round(statistics.median(step_ms), 5),
+            "write_ms_mean": round(statistics.mean(write_ms), 5),
+            "attn_ms_mean": round(attn_mean, 5), "attn_ms_median": round(statistics.median(attn_ms), 5),
+            "attn_ms_min": round(min(attn_ms), 5),
+            "wall_s_timed_region": round(wall, 4),
+        },
+        "bytes": {"attn_algorithmic": attn_bytes, "write_algorithmic": write_bytes,
+                  "kv_logical": logical_kv},
+        "roofline": {
+            "kernel": "paged_decode_attn call (partition kernel"
+                      + (" + merge kernel)" if n_part > 1 else ")"),
+            "bound": "hbm", "achieved": round(attn_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(attn_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+        },
+        "device": torch.cuda.get_device_name(0),
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, cache_dtype, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

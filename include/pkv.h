@@ -1,0 +1,263 @@
+/*
+ * pkv.h - C ABI of libpkv.so: paged decode attention for AMD Instinct MI355X
+ * (gfx950), the KV-cache write, and the host-side block allocator.
+ *
+ * What is computed follows the pages' statement of PagedAttention:
+ *  - "03 · PagedAttention" (sunilkunchoor.github.io), sections "Blocks and
+ *    block tables", "The part the analogy hides: the kernel", "Sharing:
+ *    copy-on-write" and "When the pool runs dry";
+ *  - "PagedAttention" daily term (mlapandio.dev), the decode-step figure
+ *    (gather K and V through the block table, score q against every key,
+ *    write the new K and V into the current block) and "Pros" (a plain free
+ *    list; not an approximation);
+ *  - "Serving: vLLM and PagedAttention" (henryfzh-note.com), section 2.2
+ *    (block table as page table, last-block fill, coalesced in-block reads).
+ *
+ * Conventions for every function:
+ *  - The return value is a pkv_status; PKV_OK (0) is success. On any other
+ *    value pkv_last_error() returns a message for the calling thread.
+ *  - Every argument check runs before any HIP call: an invalid call returns
+ *    PKV_E_INVALID / PKV_E_WORKSPACE synchronously and launches nothing.
+ *  - Device functions take device pointers the caller owns, enqueue their
+ *    kernels on `stream` (a hipStream_t; NULL is the default stream), never
+ *    allocate device memory and never synchronise. A launch failure returns
+ *    PKV_E_HIP with HIP's error string.
+ *  - Host allocator functions run on the CPU only and are not thread-safe:
+ *    the caller serialises calls on one allocator.
+ *
+ * Notation: S sequences, Hq query heads, Hkv kv heads (Hq % Hkv == 0, query
+ * head h uses kv head h / (Hq/Hkv)), d head dim, bs tokens per block, P
+ * blocks in the pool, L_i the context length of sequence i.
+ *
+ * Pool layout (the pages fix none; tokens of a block are contiguous in both):
+ *   k_cache[P][Hkv][bs][d]   each (block, kv head) tile token-major
+ *   v_cache[P][Hkv][d][bs]   each (block, kv head) tile channel-major
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    PKV_OK = 0,
+    PKV_E_INVALID = 1,    /* bad argument; nothing was changed or launched      */
+    PKV_E_WORKSPACE = 2,  /* workspace missing or smaller than required          */
+    PKV_E_NO_BLOCKS = 3,  /* pool exhausted; allocator state unchanged           */
+    PKV_E_NOT_FOUND = 4,  /* unknown sequence id                                 */
+    PKV_E_STATE = 5,      /* operation conflicts with current state              */
+    PKV_E_HIP = 6         /* a HIP call or kernel launch failed                  */
+} pkv_status;
+
+typedef enum {
+    PKV_F32 = 0,          /* IEEE binary32                                       */
+    PKV_BF16 = 1,         /* bfloat16 (upper half of binary32)                   */
+    PKV_FP8_E4M3 = 2      /* OCP 8-bit E4M3 ("fn": no inf, NaN = S.1111.111)     */
+} pkv_dtype;
+
+/* Message for the last non-OK status returned on this thread ("" if none). */
+const char* pkv_last_error(void);
+/* Library version string. */
+const char* pkv_version(void);
+
+/* ------------------------------------------------------------------------ */
+/* Device operations                                                         */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * KV-cache write: scatter each new token's K and V into its physical slot
+ * ("PagedAttention" daily term, decode-step figure: "write the new K and V
+ * into the current block").
+ *
+ * For each t < T with 0 <= slot_mapping[t] < P*bs: (b, o) = divmod(slot, bs);
+ *   k_cache[b][h][o][c] = cvt(k_new[t][h][c]),  v_cache[b][h][c][o] = cvt(v_new[t][h][c])
+ * for all h < Hkv, c < d. Any other slot value (-1 by convention) skips the
+ * token. Every other byte of the pools is left unchanged.
+ *
+ * cvt: a bit copy when src_dtype == cache_dtype (F32->F32, BF16->BF16);
+ * for BF16 -> FP8_E4M3: e4m3(float32(x) * inv_scale), rounded to nearest with
+ * ties to even, |value| > 448 (and +-inf) saturating to +-448, NaN -> 0x7F
+ * with its sign, the sign of zero kept. k_inv_scale / v_inv_scale are used only
+ * for an FP8 cache and must then be finite and > 0.
+ *
+ * k_new, v_new: [T][Hkv][d] in src_dtype. slot_mapping: int64 [T].
+ * Two tokens with the same slot race (the result is one of them).
+ * T == 0 is a no-op. Requires T >= 0, Hkv > 0, d in {64, 128},
+ * bs in {8, 16, 32}, P > 0.
+ */
+pkv_status pkv_kv_cache_write(const void* k_new, const void* v_new,
+                              void* k_cache, void* v_cache,
+                              const int64_t* slot_mapping,
+                              int32_t T, int32_t Hkv, int32_t d, int32_t bs, int32_t P,
+                              pkv_dtype src_dtype, pkv_dtype cache_dtype,
+                              float k_inv_scale, float v_inv_scale, void* stream);
+
+/*
+ * Bytes of workspace pkv_paged_decode_attn needs for these sizes: 0 when no
+ * sequence can span more than one partition (partition_size == 0 or
+ * max_context_len <= partition_size), else
+ *   S * Hq * n_part * (d + 2) * 4,   n_part = ceil(max_context_len / partition_size).
+ */
+size_t pkv_paged_decode_attn_workspace_size(int32_t S, int32_t Hq, int32_t d,
+                                            int32_t max_context_len,
+                                            int32_t partition_size);
+
+/*
+ * Paged decode attention: one new query per sequence attends to the
+ * sequence's L_i cached tokens, gathered block by block through the block
+ * table ("03 · PagedAttention", "The part the analogy hides: the kernel";
+ * "PagedAttention" daily term, decode-step figure). The result is the
+ * ordinary attention over the tokens in logical order:
+ *
+ *   s_t   = softmax_scale * k_scale * sum_c q[i][h][c] * K_i[t][g][c]
+ *   out[i][h][c] = v_scale * sum_t exp(s_t - max s) V_i[t][g][c] / sum_t exp(s_t - max s)
+ *
+ * with g = h / (Hq / Hkv), K_i[t] the token at position t (0-based) of
+ * sequence i: logical block t / bs at offset t % bs, physical block
+ * block_tables[i][t / bs]. For an FP8 cache K and V are the decoded E4M3
+ * values and k_scale / v_scale the per-tensor scales; for F32 and BF16
+ * caches k_scale and v_scale are ignored (taken as 1).
+ *
+ * out:           float32 [S][Hq][d]; a row with L_i <= 0 is written as 0.
+ * q:             [S][Hq][d] in q_dtype.
+ * k_cache, v_cache: the pools (layout above) in cache_dtype.
+ * block_tables:  int32 [S][max_blocks]; entries j >= ceil(L_i/bs) are never read.
+ * context_lens:  int32 [S] (device); the caller guarantees
+ *                L_i <= max_context_len. Lengths above it are clamped to it and
+ *                block ids outside [0, P) are clamped into range, so the kernel
+ *                never reads outside the table row or the pool; the output of
+ *                such a sequence is then unspecified.
+ * Supported (q_dtype, cache_dtype): (F32, F32), (BF16, BF16), (BF16, FP8_E4M3).
+ * Requires S > 0, Hkv > 0, Hq % Hkv == 0, 1 <= Hq/Hkv <= 16, d in {64, 128},
+ * bs in {8, 16, 32}, P > 0, max_blocks > 0, 0 <= max_context_len <=
+ * max_blocks * bs, softmax_scale finite; for FP8 finite k_scale, v_scale.
+ *
+ * partition_size: 0 = every (sequence, kv head) in one pass; otherwise a
+ * multiple of 32 tokens: a sequence longer than partition_size is split into
+ * ceil(L_i / partition_size) partitions whose partial results are merged
+ * exactly (max, sum of exponentials, unnormalised output) in a fixed order.
+ * workspace: device memory of at least
+ * pkv_paged_decode_attn_workspace_size(...) bytes (may be NULL when that is 0);
+ * its contents on entry do not matter.
+ *
+ * The result is deterministic: no atomics, fixed reduction order.
+ */
+pkv_status pkv_paged_decode_attn(float* out, const void* q,
+                                 const void* k_cache, const void* v_cache,
+                                 const int32_t* block_tables, const int32_t* context_lens,
+                                 int32_t S, int32_t Hq, int32_t Hkv, int32_t d, int32_t bs,
+                                 int32_t P, int32_t max_blocks, int32_t max_context_len,
+                                 float softmax_scale, float k_scale, float v_scale,
+                                 pkv_dtype q_dtype, pkv_dtype cache_dtype,
+                                 int32_t partition_size,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Host block allocator and builders (CPU only)                              */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * A pool of P equal blocks of bs tokens, all free at creation; a LIFO free
+ * list whose first pop returns block 0 ("PagedAttention" daily term, "Pros":
+ * uniform blocks, a simple free list, no search).
+ */
+typedef struct pkv_allocator pkv_allocator;
+
+typedef struct {
+    int32_t num_blocks;       /* P                                              */
+    int32_t free_blocks;      /* blocks on the free list                        */
+    int32_t used_blocks;      /* P - free_blocks                                */
+    int64_t slots_allocated;  /* used_blocks * bs                               */
+    int64_t tokens_stored;    /* tokens held in used blocks (a shared block counted once) */
+    double waste;             /* 1 - tokens_stored / slots_allocated (0 if none) */
+} pkv_stats;
+
+/* Create an allocator (P > 0, bs > 0). *out receives the handle. */
+pkv_status pkv_allocator_create(int32_t P, int32_t bs, pkv_allocator** out);
+/* Destroy an allocator; NULL is ignored. */
+void pkv_allocator_destroy(pkv_allocator* a);
+
+/* Register an empty sequence. PKV_E_STATE if the id exists. */
+pkv_status pkv_seq_create(pkv_allocator* a, int64_t seq_id);
+
+/*
+ * Append n_tokens positions to a sequence, taking a new block only when the
+ * previous one is full ("03 · PagedAttention", "Blocks and block tables": the
+ * 17th token takes a block, tokens 18-32 take none). slots_out[k] receives the
+ * slot (block*bs + offset) of the k-th appended position (may be NULL when
+ * n_tokens == 0).
+ *
+ * Copy-on-write ("03 · PagedAttention", "Sharing: copy-on-write"; daily term,
+ * copy-on-write figure): if the sequence's last block is partially filled and
+ * shared (refcount > 1), a new block is taken first, the (src, dst) pair is
+ * written to *cow_src / *cow_dst with *n_cow = 1, the sequence's table points
+ * at dst and src's refcount drops by one; the caller copies the block's data
+ * (the pair is reported, not copied). Otherwise *n_cow = 0. cow_src, cow_dst
+ * and n_cow may be NULL only if the caller never shares blocks; a CoW with
+ * NULL outputs returns PKV_E_INVALID without changing anything.
+ *
+ * All or nothing: if fewer blocks are free than the append needs,
+ * PKV_E_NO_BLOCKS and no state changes (the scheduler's cue to preempt:
+ * "03 · PagedAttention", "When the pool runs dry").
+ */
+pkv_status pkv_seq_append(pkv_allocator* a, int64_t seq_id, int32_t n_tokens,
+                          int64_t* slots_out, int32_t* cow_src, int32_t* cow_dst,
+                          int32_t* n_cow);
+
+/* child shares every block of parent (refcount + 1 each) and its length.
+ * PKV_E_NOT_FOUND if parent is unknown, PKV_E_STATE if child exists. */
+pkv_status pkv_seq_fork(pkv_allocator* a, int64_t parent, int64_t child);
+
+/* Release a sequence: refcount - 1 for each block, last logical block first;
+ * a block whose count reaches 0 returns to the free list. */
+pkv_status pkv_seq_free(pkv_allocator* a, int64_t seq_id);
+
+/* Current context length and block count of a sequence. */
+pkv_status pkv_seq_info(const pkv_allocator* a, int64_t seq_id, int64_t* length,
+                        int32_t* num_blocks);
+
+/*
+ * Block tables for the listed sequences: tables_out int32 [S][max_blocks]
+ * (row i = sequence seq_ids[i]'s physical blocks, padded with -1) and
+ * lens_out int32 [S] (their lengths). PKV_E_INVALID if a sequence holds more
+ * than max_blocks blocks or is longer than INT32_MAX; PKV_E_NOT_FOUND for an
+ * unknown id. Outputs are written only on success.
+ */
+pkv_status pkv_build_block_tables(const pkv_allocator* a, const int64_t* seq_ids,
+                                  int32_t S, int32_t max_blocks,
+                                  int32_t* tables_out, int32_t* lens_out);
+
+/*
+ * Slot of token position positions[i] of each sequence from its table row:
+ * tables[i][p / bs] * bs + p % bs; a negative position gives -1. PKV_E_INVALID
+ * if p / bs >= max_blocks or the entry is negative (nothing written then).
+ * For a decode step the position is L_i - 1 (the token being written).
+ */
+pkv_status pkv_slots_from_tables(const int32_t* tables, const int32_t* positions,
+                                 int32_t S, int32_t max_blocks, int32_t bs,
+                                 int64_t* slots_out);
+
+/* Pool-wide statistics ("03 · PagedAttention", "In Production": the block
+ * pool's fill is the capacity signal). */
+pkv_status pkv_allocator_stats(const pkv_allocator* a, pkv_stats* out);
+
+/*
+ * Tail-waste arithmetic for n lengths at block size bs ("paged-attention"
+ * lesson, worked example; "03 · PagedAttention", waste table):
+ *   paged_slots = sum ceil(L/bs)*bs, naive_slots = n*max_len, used = sum L,
+ *   waste_paged = 1 - used/paged_slots, waste_naive = 1 - used/naive_slots.
+ * Negative lengths count as 0. Any output pointer may be NULL.
+ */
+pkv_status pkv_waste_stats(const int32_t* lens, int32_t n, int32_t bs, int32_t max_len,
+                           int64_t* paged_slots, int64_t* naive_slots, int64_t* used,
+                           double* waste_paged, double* waste_naive);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

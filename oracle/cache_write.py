@@ -23,7 +23,8 @@ import numpy as np
 from .codecs import bf16_bits_to_f64, e4m3_encode
 
 
-def _quantise(x_bits, src_dtype, inv_scale):
+def quantise(x_bits, src_dtype, inv_scale):
+    """Source elements -> E4M3 codes, exactly as the write stores them."""
     if src_dtype == "bf16":
         x = bf16_bits_to_f64(x_bits).astype(np.float32)    # exact
     elif src_dtype == "f32":
@@ -43,8 +44,8 @@ def kv_cache_write(k_new, v_new, k_cache, v_cache, slot_mapping, *, bs, src_dtyp
     k_out = np.array(k_cache, copy=True)
     v_out = np.array(v_cache, copy=True)
     if cache_dtype == "fp8":
-        kq = _quantise(k_new, src_dtype, k_inv_scale)
-        vq = _quantise(v_new, src_dtype, v_inv_scale)
+        kq = quantise(k_new, src_dtype, k_inv_scale)
+        vq = quantise(v_new, src_dtype, v_inv_scale)
     elif cache_dtype == src_dtype:
         kq = np.asarray(k_new)
         vq = np.asarray(v_new)

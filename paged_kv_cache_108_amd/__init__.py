@@ -1,0 +1,17 @@
+"""pkv: paged decode attention and the KV-cache write for AMD MI355X (gfx950).
+
+The computation lives in ``libpkv.so`` (hand-written HIP kernels and a C++
+host allocator, C ABI in ``include/pkv.h``); this package only passes
+arguments to it. ``workloads`` draws the seeded synthetic inputs.
+"""
+
+from .api import (kv_cache_write, paged_decode_attn, paged_decode_attn_workspace_size, Allocator,
+                  slots_from_tables, waste_stats, last_error, version, quantise_pool, PkvError,
+                  NoBlocks)
+from ._lib import lib, LIB_PATH, SIGNATURES, PKV_F32, PKV_BF16, PKV_FP8_E4M3
+
+__all__ = [
+    "kv_cache_write", "paged_decode_attn", "paged_decode_attn_workspace_size", "Allocator",
+    "slots_from_tables", "waste_stats", "last_error", "version", "quantise_pool", "PkvError",
+    "NoBlocks", "lib", "LIB_PATH", "SIGNATURES", "PKV_F32", "PKV_BF16", "PKV_FP8_E4M3",
+]

@@ -1,0 +1,213 @@
+"""Python names for the C ABI of libpkv.so (argument marshalling only).
+
+Device functions take torch tensors that already live on the GPU (their data
+pointers and torch's current HIP stream are passed through); every step of
+the computation runs in the library's kernels. Host functions take numpy
+arrays. Errors from the library raise PkvError with its message.
+"""
+
+import ctypes
+
+import numpy as np
+
+from ._lib import (lib, check, PkvError, PkvStats, PKV_F32, PKV_BF16, PKV_FP8_E4M3, PKV_OK,
+                   PKV_E_NO_BLOCKS, P_i32, P_i64, P_f64, c_vp, c_i64, c_i32, c_f64)
+
+__all__ = [
+    "kv_cache_write", "paged_decode_attn", "paged_decode_attn_workspace_size", "Allocator",
+    "slots_from_tables", "waste_stats", "last_error", "version", "quantise_pool",
+    "PkvError", "NoBlocks",
+]
+
+
+class NoBlocks(PkvError):
+    """The pool has fewer free blocks than the append needs (nothing changed)."""
+
+
+def last_error():
+    return lib().pkv_last_error().decode()
+
+
+def version():
+    return lib().pkv_version().decode()
+
+
+# ------------------------------------------------------------------ device ops
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.float32:
+        return PKV_F32
+    if t.dtype == torch.bfloat16:
+        return PKV_BF16
+    if t.dtype in (torch.uint8, torch.float8_e4m3fn):
+        return PKV_FP8_E4M3
+    raise TypeError(f"unsupported tensor dtype {t.dtype}")
+
+
+def _dev(t, name):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def kv_cache_write(k_new, v_new, k_cache, v_cache, slot_mapping, *, k_inv_scale=1.0,
+                   v_inv_scale=1.0, stream=None):
+    """pkv_kv_cache_write. k_new/v_new [T][Hkv][d]; k_cache [P][Hkv][bs][d];
+    v_cache [P][Hkv][d][bs]; slot_mapping int64 [T]."""
+    import torch
+    T, Hkv, d = k_new.shape
+    P, _, bs, _ = k_cache.shape
+    if v_new.shape != k_new.shape or tuple(v_cache.shape) != (P, Hkv, d, bs) \
+            or tuple(k_cache.shape) != (P, Hkv, bs, d):
+        raise ValueError("kv_cache_write: shape mismatch")
+    if slot_mapping.dtype != torch.int64 or slot_mapping.shape != (T,):
+        raise ValueError("kv_cache_write: slot_mapping must be int64 [T]")
+    check(lib().pkv_kv_cache_write(
+        _dev(k_new, "k_new"), _dev(v_new, "v_new"), _dev(k_cache, "k_cache"),
+        _dev(v_cache, "v_cache"), _dev(slot_mapping, "slot_mapping"), T, Hkv, d, bs, P,
+        _dtype_code(k_new), _dtype_code(k_cache), float(k_inv_scale), float(v_inv_scale),
+        _stream(stream)))
+
+
+def paged_decode_attn_workspace_size(S, Hq, d, max_context_len, partition_size):
+    return int(lib().pkv_paged_decode_attn_workspace_size(S, Hq, d, max_context_len,
+                                                          partition_size))
+
+
+def paged_decode_attn(out, q, k_cache, v_cache, block_tables, context_lens, *, max_context_len,
+                      softmax_scale, k_scale=1.0, v_scale=1.0, partition_size=512,
+                      workspace=None, stream=None):
+    """pkv_paged_decode_attn. out float32 [S][Hq][d]; q [S][Hq][d]; tables int32
+    [S][max_blocks]; context_lens int32 [S]; workspace a uint8 device tensor of at
+    least paged_decode_attn_workspace_size(...) bytes (or None when that is 0)."""
+    import torch
+    S, Hq, d = q.shape
+    P, Hkv, bs, _ = k_cache.shape
+    if tuple(out.shape) != (S, Hq, d) or out.dtype != torch.float32:
+        raise ValueError("paged_decode_attn: out must be float32 [S][Hq][d]")
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise ValueError("paged_decode_attn: tables and lengths must be int32")
+    if block_tables.shape[0] != S or context_lens.shape != (S,):
+        raise ValueError("paged_decode_attn: tables/lengths shape mismatch")
+    ws_ptr, ws_bytes = ctypes.c_void_p(0), 0
+    if workspace is not None:
+        ws_ptr, ws_bytes = _dev(workspace, "workspace"), workspace.numel() * workspace.element_size()
+    check(lib().pkv_paged_decode_attn(
+        _dev(out, "out"), _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+        _dev(block_tables, "block_tables"), _dev(context_lens, "context_lens"),
+        S, Hq, Hkv, d, bs, P, block_tables.shape[1], int(max_context_len),
+        float(softmax_scale), float(k_scale), float(v_scale), _dtype_code(q),
+        _dtype_code(k_cache), int(partition_size), ws_ptr, ws_bytes, _stream(stream)))
+
+
+def quantise_pool(values_k, values_v, codes_k, codes_v, *, k_inv_scale, v_inv_scale, stream=None):
+    """Fill whole fp8 pools from bf16 pools of the same layout, through the
+    library's cache write (every slot written once, in order)."""
+    import torch
+    P, Hkv, bs, d = values_k.shape
+    tok_k = values_k.permute(0, 2, 1, 3).reshape(P * bs, Hkv, d).contiguous()
+    tok_v = values_v.permute(0, 3, 1, 2).reshape(P * bs, Hkv, d).contiguous()
+    slots = torch.arange(P * bs, dtype=torch.int64, device=values_k.device)
+    kv_cache_write(tok_k, tok_v, codes_k, codes_v, slots, k_inv_scale=k_inv_scale,
+                   v_inv_scale=v_inv_scale, stream=stream)
+
+
+# ------------------------------------------------------------------ host side
+def _i32(a):
+    return np.ascontiguousarray(a, dtype=np.int32)
+
+
+def _ptr(a, ctype):
+    return a.ctypes.data_as(ctype)
+
+
+def slots_from_tables(tables, positions, bs):
+    """pkv_slots_from_tables -> int64 [S]."""
+    tables = _i32(tables)
+    positions = _i32(positions)
+    S, maxb = tables.shape
+    out = np.empty(S, dtype=np.int64)
+    check(lib().pkv_slots_from_tables(_ptr(tables, P_i32), _ptr(positions, P_i32), S, maxb, bs,
+                                      _ptr(out, P_i64)))
+    return out
+
+
+def waste_stats(lens, bs, max_len):
+    """pkv_waste_stats -> dict."""
+    lens = _i32(lens)
+    p, nv, u = c_i64(), c_i64(), c_i64()
+    wp, wn = c_f64(), c_f64()
+    check(lib().pkv_waste_stats(_ptr(lens, P_i32), len(lens), bs, max_len, ctypes.byref(p),
+                                ctypes.byref(nv), ctypes.byref(u), ctypes.byref(wp),
+                                ctypes.byref(wn)))
+    return {"paged_slots": p.value, "naive_slots": nv.value, "used": u.value,
+            "waste_paged": wp.value, "waste_naive": wn.value}
+
+
+class Allocator:
+    """The library's host block allocator (pkv_allocator_*)."""
+
+    def __init__(self, num_blocks, block_size):
+        h = c_vp()
+        check(lib().pkv_allocator_create(num_blocks, block_size, ctypes.byref(h)))
+        self._h = h
+        self.num_blocks = num_blocks
+        self.block_size = block_size
+
+    def close(self):
+        if self._h:
+            lib().pkv_allocator_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def create(self, seq_id):
+        check(lib().pkv_seq_create(self._h, seq_id))
+
+    def append(self, seq_id, n_tokens):
+        """Returns (slots int64[n], cow_pairs list of (src, dst))."""
+        slots = np.empty(max(n_tokens, 1), dtype=np.int64)
+        src, dst, n = c_i32(), c_i32(), c_i32()
+        st = lib().pkv_seq_append(self._h, seq_id, n_tokens, _ptr(slots, P_i64), ctypes.byref(src),
+                                  ctypes.byref(dst), ctypes.byref(n))
+        if st == PKV_E_NO_BLOCKS:
+            raise NoBlocks(st, last_error())
+        check(st)
+        return slots[:n_tokens], ([(src.value, dst.value)] if n.value else [])
+
+    def fork(self, parent, child):
+        check(lib().pkv_seq_fork(self._h, parent, child))
+
+    def release(self, seq_id):
+        check(lib().pkv_seq_free(self._h, seq_id))
+
+    def info(self, seq_id):
+        L, n = c_i64(), c_i32()
+        check(lib().pkv_seq_info(self._h, seq_id, ctypes.byref(L), ctypes.byref(n)))
+        return L.value, n.value
+
+    def tables(self, seq_ids, max_blocks):
+        ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
+        S = len(ids)
+        tab = np.empty((S, max_blocks), dtype=np.int32)
+        lens = np.empty(S, dtype=np.int32)
+        check(lib().pkv_build_block_tables(self._h, _ptr(ids, P_i64), S, max_blocks,
+                                           _ptr(tab, P_i32), _ptr(lens, P_i32)))
+        return tab, lens
+
+    def stats(self):
+        s = PkvStats()
+        check(lib().pkv_allocator_stats(self._h, ctypes.byref(s)))
+        return {k: getattr(s, k) for k, _ in PkvStats._fields_}

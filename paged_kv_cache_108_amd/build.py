@@ -1,0 +1,56 @@
+"""Build libpkv.so in-tree: host C++ with g++, device code with hipcc for gfx950.
+
+``python -m paged_kv_cache_108_amd.build`` (or ``build()``) always recompiles.
+"""
+
+import os
+import shutil
+import subprocess
+import sys
+import tempfile
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(HERE, "libpkv.so")
+
+HIP_FLAGS = [
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
+    # no packed-fp32 instructions anywhere in device code
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+]
+
+
+def _run(cmd, verbose):
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    out = "\n".join(l for l in r.stdout.splitlines()
+                    if "packed-fp32-ops" not in l and "argument unused during compilation" not in l)
+    if r.returncode != 0:
+        raise RuntimeError(f"build failed ({r.returncode}): {' '.join(cmd)}\n{out}")
+    if verbose and out.strip():
+        print(out)
+
+
+def build(verbose=False, out=LIB, extra_hip_flags=()):
+    hipcc = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
+    cxx = os.environ.get("CXX", shutil.which("g++") or "g++")
+    with tempfile.TemporaryDirectory(prefix="pkv_build_") as tmp:
+        host_o = os.path.join(tmp, "host.o")
+        dev_o = os.path.join(tmp, "device.o")
+        _run([cxx, "-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-I", INCLUDE, "-c",
+              os.path.join(CSRC, "host.cpp"), "-o", host_o], verbose)
+        _run([hipcc, *HIP_FLAGS, *extra_hip_flags, "-I", INCLUDE, "-c",
+              os.path.join(CSRC, "device.hip"), "-o", dev_o], verbose)
+        tmp_so = os.path.join(tmp, "libpkv.so")
+        _run([hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", host_o, dev_o, "-o", tmp_so],
+             verbose)
+        shutil.move(tmp_so, out + ".tmp")
+        os.replace(out + ".tmp", out)
+    return out
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

@@ -1,0 +1,244 @@
+"""CPU tests of the C ABI: exports, host allocator against the oracle's twin,
+builders against the oracle, and every argument check of the device entry
+points (all of which return before any HIP call)."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import paged_kv_cache_108_amd as pkv
+from paged_kv_cache_108_amd import _lib
+from paged_kv_cache_108_amd import workloads as W
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "pkv.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pkv_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    names = declared_functions()
+    assert len(names) >= 16
+    handle = ctypes.CDLL(pkv.LIB_PATH)
+    for n in names:
+        assert hasattr(handle, n), n
+    assert set(names) == set(_lib.SIGNATURES), "binding and header disagree"
+    assert pkv.version().startswith("pkv")
+
+
+# ------------------------------------------------------------------ allocator parity
+def _run_both(ops, P, bs):
+    a, t = pkv.Allocator(P, bs), oracle.TwinAllocator(P, bs)
+    for op in ops:
+        kind = op[0]
+        if kind == "create":
+            a.create(op[1]); t.create(op[1])
+        elif kind == "append":
+            try:
+                got = a.append(op[1], op[2])
+                got = (list(got[0]), got[1])
+            except pkv.NoBlocks:
+                got = "noblocks"
+            try:
+                want = t.append(op[1], op[2])
+            except oracle.NoBlocks:
+                want = "noblocks"
+            assert got == want, op
+        elif kind == "fork":
+            a.fork(op[1], op[2]); t.fork(op[1], op[2])
+        elif kind == "free":
+            a.release(op[1]); t.release(op[1])
+    return a, t
+
+
+def _random_ops(seed, n=1500):
+    rng = np.random.default_rng(seed)
+    ops, live, nxt = [], [], 0
+    for _ in range(n):
+        k = rng.integers(5)
+        if k == 0 or not live:
+            ops.append(("create", nxt)); live.append(nxt); nxt += 1
+        elif k in (1, 2):
+            ops.append(("append", int(live[rng.integers(len(live))]), int(rng.integers(0, 40))))
+        elif k == 3:
+            ops.append(("fork", int(live[rng.integers(len(live))]), nxt)); live.append(nxt); nxt += 1
+        else:
+            ops.append(("free", int(live.pop(int(rng.integers(len(live)))))))
+    return ops
+
+
+@pytest.mark.parametrize("seed,P,bs", [(0, 64, 8), (1, 200, 16), (2, 30, 32), (3, 500, 16)])
+def test_allocator_matches_twin(seed, P, bs):
+    ops = _random_ops(seed)
+    a, t = _run_both(ops, P, bs)
+    ids = sorted(t.seqs)
+    maxb = max([len(t.seqs[s][0]) for s in ids] + [1])
+    tab, lens = a.tables(ids, maxb)
+    ttab, tlens = t.tables(ids, maxb)
+    assert np.array_equal(tab, np.array(ttab, dtype=np.int32).reshape(len(ids), maxb))
+    assert list(lens) == tlens
+    sa, st = a.stats(), t.stats()
+    for k in ("num_blocks", "free_blocks", "used_blocks", "slots_allocated", "tokens_stored"):
+        assert sa[k] == st[k], k
+    assert abs(sa["waste"] - st["waste"]) < 1e-12
+
+
+def test_allocator_reproduces_beam_layout():
+    # The generator's beam tables are the sequential ids a first-pop-0 pool
+    # hands out for: prefix append, 3 forks, private appends.
+    private = np.random.default_rng([108, 4, 0]).integers(1, 201, 128)
+    for bs in (8, 16, 32):
+        seq_tab, lens, used = W.beam_layout(bs, private)
+        a = pkv.Allocator(used, bs)
+        for g in range(32):
+            a.create(4 * g)
+            a.append(4 * g, 1024)
+            for b in (1, 2, 3):
+                a.fork(4 * g, 4 * g + b)
+            for b in range(4):
+                _, cow = a.append(4 * g + b, int(private[4 * g + b]))
+                assert cow == []                       # block-aligned prefix: never copies
+        tab, L = a.tables(list(range(128)), seq_tab.shape[1])
+        assert np.array_equal(tab, seq_tab) and np.array_equal(L, lens)
+        assert a.stats()["free_blocks"] == 0
+
+
+def test_allocator_reproduces_churned_pool():
+    ops = W.churn_ops()
+    a = pkv.Allocator(36045, 16)
+    for op in ops:
+        if op[0] == "alloc":
+            a.create(op[1] + 10**6)
+            a.append(op[1] + 10**6, op[2] * 16)
+        else:
+            a.release(op[1] + 10**6)
+    for s in range(16):
+        a.create(s)
+    for j in range(2048):
+        for s in range(16):
+            a.append(s, 16)
+    tab, lens = a.tables(list(range(16)), 2048)
+    assert np.array_equal(tab, W.churned_tables()) and set(lens) == {32768}
+
+
+def test_allocator_cow_pair_and_errors():
+    a = pkv.Allocator(6, 16)
+    a.create(1)
+    a.append(1, 20)
+    a.fork(1, 2)
+    slots, cow = a.append(2, 1)
+    assert cow == [(1, 2)] and list(slots) == [2 * 16 + 4]
+    assert a.info(2) == (21, 2)
+    with pytest.raises(pkv.PkvError, match="PKV_E_STATE"):
+        a.create(1)
+    with pytest.raises(pkv.PkvError, match="PKV_E_NOT_FOUND"):
+        a.append(99, 1)
+    with pytest.raises(pkv.PkvError, match="PKV_E_NOT_FOUND"):
+        a.release(99)
+    with pytest.raises(pkv.PkvError, match="PKV_E_STATE"):
+        a.fork(1, 2)
+    with pytest.raises(pkv.PkvError, match="PKV_E_INVALID"):
+        a.append(1, -1)
+    before = a.stats()
+    with pytest.raises(pkv.NoBlocks):
+        a.append(1, 16 * 10)
+    assert a.stats() == before
+    with pytest.raises(pkv.PkvError, match="PKV_E_INVALID"):
+        a.tables([1, 2], 1)                          # 2 blocks > max_blocks
+    with pytest.raises(pkv.PkvError, match="PKV_E_INVALID"):
+        pkv.Allocator(0, 16)
+    # a CoW with no place to report it is refused without changing anything
+    lib = pkv.lib()
+    slots = np.zeros(1, dtype=np.int64)
+    a.fork(2, 3)
+    st = lib.pkv_seq_append(a._h, 3, 1, slots.ctypes.data_as(_lib.P_i64), None, None, None)
+    assert st == _lib.PKV_E_INVALID and a.info(3) == (21, 2)
+
+
+def test_slots_and_waste_match_oracle(golden):
+    g = golden("worked_example.json")
+    w = pkv.waste_stats(g["lengths"], 16, g["reserve_max_len"])
+    assert (w["paged_slots"], w["naive_slots"], w["used"]) == (2608, 10240, 2581)
+    assert abs(w["waste_paged"] - oracle.waste_fraction(g["lengths"], 2608)) < 1e-15
+    assert round(100 * w["waste_naive"], 1) == 74.8
+    rng = np.random.default_rng(0)
+    for bs in (8, 16, 32):
+        tab = rng.permutation(400)[:120].reshape(6, 20).astype(np.int32)
+        pos = rng.integers(-2, 20 * bs, 6).astype(np.int32)
+        got = pkv.slots_from_tables(tab, pos, bs)
+        assert np.array_equal(got, oracle.slots_for_positions(tab, pos, bs))
+    with pytest.raises(pkv.PkvError):
+        pkv.slots_from_tables(np.array([[3, -1]]), np.array([20]), 16)   # unallocated block
+    with pytest.raises(pkv.PkvError):
+        pkv.slots_from_tables(np.array([[3]]), np.array([16]), 16)       # beyond the table
+
+
+def test_decode_slots_for_workloads_match_oracle():
+    w = W.make("tiny")
+    got = pkv.slots_from_tables(w.block_tables, w.context_lens - 1, w.spec.bs)
+    assert np.array_equal(got, oracle.decode_slots(w.block_tables, w.context_lens, w.spec.bs))
+
+
+# ------------------------------------------------------------------ device argument checks
+FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: every call below fails validation
+
+
+def _attn(**kw):
+    a = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, tab=FAKE, lens=FAKE, S=4, Hq=8, Hkv=2, d=128, bs=16,
+             P=100, maxb=10, maxlen=160, scale=0.1, ks=1.0, vs=1.0, qd=1, cd=1, part=512,
+             ws=FAKE, wsb=0, stream=None)
+    a.update(kw)
+    return pkv.lib().pkv_paged_decode_attn(
+        a["out"], a["q"], a["k"], a["v"], a["tab"], a["lens"], a["S"], a["Hq"], a["Hkv"], a["d"],
+        a["bs"], a["P"], a["maxb"], a["maxlen"], a["scale"], a["ks"], a["vs"], a["qd"], a["cd"],
+        a["part"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw", [
+    dict(Hq=7), dict(Hq=34, Hkv=2), dict(d=96), dict(bs=4), dict(bs=64), dict(P=0),
+    dict(maxb=0), dict(maxlen=161), dict(maxlen=-1), dict(qd=0), dict(qd=1, cd=0),
+    dict(qd=2, cd=2), dict(part=16), dict(part=-32), dict(scale=float("inf")),
+    dict(qd=1, cd=2, ks=float("nan")), dict(out=None), dict(tab=None), dict(S=-1), dict(Hkv=0),
+])
+def test_attn_rejects_invalid_arguments(kw):
+    assert _attn(**kw) == _lib.PKV_E_INVALID
+    assert pkv.last_error()
+
+
+def test_attn_workspace_checks():
+    need = pkv.paged_decode_attn_workspace_size(4, 8, 128, 2000, 512)
+    assert need == 4 * 8 * 4 * 130 * 4
+    assert pkv.paged_decode_attn_workspace_size(4, 8, 128, 512, 512) == 0
+    assert pkv.paged_decode_attn_workspace_size(4, 8, 128, 2000, 0) == 0
+    assert _attn(maxb=200, maxlen=2000, wsb=need - 1) == _lib.PKV_E_WORKSPACE
+    assert _attn(maxb=200, maxlen=2000, ws=None, wsb=need) == _lib.PKV_E_WORKSPACE
+    assert _attn(S=0) == _lib.PKV_OK                 # nothing to do, nothing launched
+
+
+def _write(**kw):
+    a = dict(kn=FAKE, vn=FAKE, kc=FAKE, vc=FAKE, sm=FAKE, T=3, Hkv=2, d=64, bs=16, P=10, sd=1,
+             cd=1, ki=1.0, vi=1.0)
+    a.update(kw)
+    return pkv.lib().pkv_kv_cache_write(a["kn"], a["vn"], a["kc"], a["vc"], a["sm"], a["T"],
+                                        a["Hkv"], a["d"], a["bs"], a["P"], a["sd"], a["cd"],
+                                        a["ki"], a["vi"], None)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(T=-1), dict(Hkv=0), dict(d=32), dict(bs=12), dict(P=0), dict(sd=0, cd=1),
+    dict(sd=2, cd=2), dict(sd=0, cd=2), dict(sd=1, cd=2, ki=0.0), dict(sd=1, cd=2, vi=float("inf")),
+    dict(kn=None), dict(sm=None),
+])
+def test_write_rejects_invalid_arguments(kw):
+    assert _write(**kw) == _lib.PKV_E_INVALID
+
+
+def test_write_zero_tokens_is_a_noop():
+    assert _write(T=0, kn=None, vn=None, kc=None, vc=None, sm=None) == _lib.PKV_OK
