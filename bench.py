@@ -8,7 +8,7 @@ partition kernel and, for split sequences, the merge kernel). Inputs are
 seeded synthetic workloads already resident in HBM.
 
 Timing: W untimed warm-up steps, then K timed steps. Before each timed step
-(outside its event pair) a 1 GiB buffer is written so neither the 256 MB
+(outside its event pair) a 1 GiB buffer is read so neither the 256 MB
 Infinity Cache nor L2 still holds the KV pool; each step is bracketed by HIP
 events on the stream the kernels run on, with a third event between the write
 and the attention call. Bytes are algorithmic: what the method must move (each
@@ -132,6 +132,8 @@ def main():
     ap.add_argument("--no-flush", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (reference for counter scaling)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -146,6 +148,18 @@ def main():
     if not torch.cuda.is_available():
         print(json.dumps({"error": "no GPU visible"}))
         sys.exit(1)
+
+    if args.copy_calibration:
+        # A plain copy of known size: under rocprofv3 --pmc its FETCH_SIZE and
+        # WRITE_SIZE per dispatch give the counters' scale (bytes = MiB * 2^20).
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(max(args.steps, 1)):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "dispatches": max(args.steps, 1)}))
+        return
 
     w = W.make(args.config, bs=args.bs, cache_dtype=args.kv)
     s = w.spec
@@ -173,9 +187,12 @@ def main():
         k_cache, v_cache = dev(w.k_pool), dev(w.v_pool)
     slots = dev(pkv.slots_from_tables(w.block_tables, w.context_lens - 1, s.bs))
     out = torch.empty((s.S, s.Hq, s.d), dtype=torch.float32, device="cuda")
-    need = pkv.paged_decode_attn_workspace_size(s.S, s.Hq, s.d, w.max_context_len, part)
+    need = pkv.paged_decode_attn_workspace_size(s.S, s.Hq, s.Hkv, s.d, w.max_context_len, part)
     ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda") if need else None
-    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    # 1 GiB read between timed steps: the Infinity Cache and L2 then hold only
+    # clean lines of this buffer (a write flush would leave dirty lines whose
+    # write-back the next kernel pays for)
+    flush = torch.ones(1 << 27, dtype=torch.int64, device="cuda")
     stream = torch.cuda.current_stream()
 
     def write():
@@ -199,7 +216,7 @@ def main():
     wall0 = time.perf_counter()
     for k in range(args.steps):
         if not args.no_flush:
-            flush.fill_(k & 0xFF)
+            flush.max()
         a, b, c = ev[k]
         a.record(stream)
         write()

@@ -59,6 +59,9 @@ typedef enum {
     PKV_FP8_E4M3 = 2      /* OCP 8-bit E4M3 ("fn": no inf, NaN = S.1111.111)     */
 } pkv_dtype;
 
+/* partition_size value selecting the balanced split (see pkv_paged_decode_attn). */
+#define PKV_PARTITION_BALANCED (-1)
+
 /* Message for the last non-OK status returned on this thread ("" if none). */
 const char* pkv_last_error(void);
 /* Library version string. */
@@ -97,12 +100,15 @@ pkv_status pkv_kv_cache_write(const void* k_new, const void* v_new,
                               float k_inv_scale, float v_inv_scale, void* stream);
 
 /*
- * Bytes of workspace pkv_paged_decode_attn needs for these sizes: 0 when no
- * sequence can span more than one partition (partition_size == 0 or
- * max_context_len <= partition_size), else
- *   S * Hq * n_part * (d + 2) * 4,   n_part = ceil(max_context_len / partition_size).
+ * Bytes of workspace pkv_paged_decode_attn needs for these sizes:
+ *  - partition_size == PKV_PARTITION_BALANCED: 2 * 4096 * (Hq/Hkv) * (d + 2) * 4
+ *    (two partial records per wave, at most 4096 waves);
+ *  - otherwise 0 when no sequence can span more than one partition
+ *    (partition_size == 0 or max_context_len <= partition_size), else
+ *    S * Hq * n_part * (d + 2) * 4 with n_part = ceil(max_context_len / partition_size).
+ * Returns 0 for invalid sizes.
  */
-size_t pkv_paged_decode_attn_workspace_size(int32_t S, int32_t Hq, int32_t d,
+size_t pkv_paged_decode_attn_workspace_size(int32_t S, int32_t Hq, int32_t Hkv, int32_t d,
                                             int32_t max_context_len,
                                             int32_t partition_size);
 
@@ -136,15 +142,24 @@ size_t pkv_paged_decode_attn_workspace_size(int32_t S, int32_t Hq, int32_t d,
  * bs in {8, 16, 32}, P > 0, max_blocks > 0, 0 <= max_context_len <=
  * max_blocks * bs, softmax_scale finite; for FP8 finite k_scale, v_scale.
  *
- * partition_size: 0 = every (sequence, kv head) in one pass; otherwise a
- * multiple of 32 tokens: a sequence longer than partition_size is split into
- * ceil(L_i / partition_size) partitions whose partial results are merged
- * exactly (max, sum of exponentials, unnormalised output) in a fixed order.
+ * partition_size selects how sequences are split across workgroups (split-K);
+ * partial results are always merged exactly (running max, sum of
+ * exponentials, unnormalised output) in a fixed order:
+ *  - 0: every (sequence, kv head) in one pass, no split;
+ *  - a positive multiple of 32: fixed partitions of that many tokens; a
+ *    sequence longer than partition_size is split into
+ *    ceil(L_i / partition_size) partitions;
+ *  - PKV_PARTITION_BALANCED: every resident wave of the GPU takes an equal
+ *    contiguous share of all (sequence, kv head, 16-token chunk) work, so a
+ *    long sequence is split wherever the shares cut it and every wave
+ *    finishes at about the same time.
  * workspace: device memory of at least
  * pkv_paged_decode_attn_workspace_size(...) bytes (may be NULL when that is 0);
- * its contents on entry do not matter.
+ * its contents on entry do not matter. Calls that overlap in time must not
+ * share a workspace.
  *
- * The result is deterministic: no atomics, fixed reduction order.
+ * The result is deterministic for a given GPU: no atomics, fixed reduction
+ * order (the balanced split depends on the number of resident waves).
  */
 pkv_status pkv_paged_decode_attn(float* out, const void* q,
                                  const void* k_cache, const void* v_cache,

@@ -17,6 +17,7 @@ STATUS_NAMES = {
     PKV_E_STATE: "PKV_E_STATE", PKV_E_HIP: "PKV_E_HIP",
 }
 PKV_F32, PKV_BF16, PKV_FP8_E4M3 = 0, 1, 2
+PKV_PARTITION_BALANCED = -1
 
 c_i32, c_i64, c_f32, c_f64, c_vp, c_sz = (ctypes.c_int32, ctypes.c_int64, ctypes.c_float,
                                           ctypes.c_double, ctypes.c_void_p, ctypes.c_size_t)
@@ -36,7 +37,7 @@ SIGNATURES = {
     "pkv_version": (ctypes.c_char_p, []),
     "pkv_kv_cache_write": (ctypes.c_int, [c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32,
                                           c_i32, ctypes.c_int, ctypes.c_int, c_f32, c_f32, c_vp]),
-    "pkv_paged_decode_attn_workspace_size": (c_sz, [c_i32, c_i32, c_i32, c_i32, c_i32]),
+    "pkv_paged_decode_attn_workspace_size": (c_sz, [c_i32, c_i32, c_i32, c_i32, c_i32, c_i32]),
     "pkv_paged_decode_attn": (ctypes.c_int, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_i32, c_i32,
                                              c_i32, c_i32, c_i32, c_i32, c_i32, c_f32, c_f32, c_f32,
                                              ctypes.c_int, ctypes.c_int, c_i32, c_vp, c_sz, c_vp]),

@@ -11,12 +11,13 @@ import ctypes
 import numpy as np
 
 from ._lib import (lib, check, PkvError, PkvStats, PKV_F32, PKV_BF16, PKV_FP8_E4M3, PKV_OK,
+                   PKV_PARTITION_BALANCED,
                    PKV_E_NO_BLOCKS, P_i32, P_i64, P_f64, c_vp, c_i64, c_i32, c_f64)
 
 __all__ = [
     "kv_cache_write", "paged_decode_attn", "paged_decode_attn_workspace_size", "Allocator",
     "slots_from_tables", "waste_stats", "last_error", "version", "quantise_pool",
-    "PkvError", "NoBlocks",
+    "PkvError", "NoBlocks", "PKV_PARTITION_BALANCED",
 ]
 
 
@@ -77,8 +78,8 @@ def kv_cache_write(k_new, v_new, k_cache, v_cache, slot_mapping, *, k_inv_scale=
         _stream(stream)))
 
 
-def paged_decode_attn_workspace_size(S, Hq, d, max_context_len, partition_size):
-    return int(lib().pkv_paged_decode_attn_workspace_size(S, Hq, d, max_context_len,
+def paged_decode_attn_workspace_size(S, Hq, Hkv, d, max_context_len, partition_size):
+    return int(lib().pkv_paged_decode_attn_workspace_size(S, Hq, Hkv, d, max_context_len,
                                                           partition_size))
 
 
@@ -87,7 +88,8 @@ def paged_decode_attn(out, q, k_cache, v_cache, block_tables, context_lens, *, m
                       workspace=None, stream=None):
     """pkv_paged_decode_attn. out float32 [S][Hq][d]; q [S][Hq][d]; tables int32
     [S][max_blocks]; context_lens int32 [S]; workspace a uint8 device tensor of at
-    least paged_decode_attn_workspace_size(...) bytes (or None when that is 0)."""
+    least paged_decode_attn_workspace_size(...) bytes (or None when that is 0);
+    partition_size 0, a multiple of 32, or PKV_PARTITION_BALANCED."""
     import torch
     S, Hq, d = q.shape
     P, Hkv, bs, _ = k_cache.shape

@@ -19,6 +19,9 @@ HIP_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     # no packed-fp32 instructions anywhere in device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in ordinary VGPRs: the online-softmax rescale of the
+    # output accumulators is then plain VALU work, with no AGPR round trips
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
 
 

@@ -38,6 +38,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 #include <type_traits>
 
 #include "common.h"
@@ -52,8 +53,13 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kWaves = 4;
+#ifndef PKV_WAVES
+#define PKV_WAVES 4
+#endif
+constexpr int kWaves = PKV_WAVES;         // waves per workgroup
 constexpr int kThreads = kWaves * 64;
+constexpr int kMaxCachedLens = 4096;      // sequences whose lengths a workgroup keeps in LDS
+constexpr int kMaxWorkers = 4096;         // waves of the balanced split, at most (sizes its workspace)
 constexpr float kLog2e = 1.4426950408889634f;
 
 enum KvKind { KV_F32 = 0, KV_BF16 = 1, KV_FP8 = 2 };
@@ -172,8 +178,12 @@ struct AttnParams {
     const void* v;
     const int32_t* tables;
     const int32_t* lens;
-    float* ws;             // partials: o [S][Hq][n_part][D], m [...], l [...]
+    float* ws;             // partial records: o [n_rec][G][D], m [n_rec][G], l [n_rec][G]
     int S, Hq, Hkv, G, P, max_blocks, max_len, part_tokens, n_part;
+    int cache_lens;        // workgroups keep all S context lengths in LDS
+    int balanced;          // 1: balanced split over the grid; 0: fixed partitions
+    int n_workers;         // grid size (balanced split)
+    int n_rec;             // partial records in the workspace
     float qk_scale;        // softmax_scale * k_scale * log2(e): scores in the log2 domain
     float v_scale;
 };
@@ -347,57 +357,80 @@ __device__ __forceinline__ void chunk_pv(Frag<KV, D>& f, const float p[4], f32x4
     }
 }
 
+// A work item: sequence i, kv head g, tokens [t0, t1). `rec` < 0: the item is
+// the whole sequence and writes the final output rows; otherwise it writes
+// partial-result record `rec` (m, l and unnormalised o of its G heads).
+struct Item {
+    int i, g, L, t0, t1, n_chunks, rec;
+};
+
+// Block ids of one wave's chunks c_k = wave + kWaves*k for k in [kb, kb+64):
+// lane k - kb holds the physical block of chunk c_k's first token (id0) and,
+// for bs 8, of its token +8 (id1). Only table entries that exist are read.
+// q fragment of this lane (head r16 of kv head g's group, zero for padding
+// heads): the channel map is the K fragment's.
+template <int KV, int D>
+__device__ __forceinline__ void load_q(const AttnParams& p, int i, int g, int r16, int j4,
+                                       typename QFragT<KV>::T* qf) {
+    using QF = typename QFragT<KV>::T;
+    const bool live = r16 < p.G;
+    const size_t qoff = ((size_t)i * p.Hq + g * p.G + (live ? r16 : 0)) * D;
+#pragma unroll
+    for (int x = 0; x < q_loads<KV, D>(); ++x) {
+        int c;
+        if constexpr (KV == KV_F32) c = 16 * x + 4 * j4;
+        else if constexpr (KV == KV_BF16) c = 32 * x + 8 * j4;
+        else c = 64 * (x >> 1) + 16 * j4 + 8 * (x & 1);
+        QF val;
+        if constexpr (KV == KV_F32)
+            val = *reinterpret_cast<const float4*>(static_cast<const float*>(p.q) + qoff + c);
+        else
+            val = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.q) + qoff + c);
+        if (!live) val = QF{};
+        qf[x] = val;
+    }
+}
+
+template <int BS>
+__device__ __forceinline__ void load_ids(const AttnParams& p, const Item& it, int wave, int lane,
+                                         int kb, int& id0, int& id1) {
+    const int nk = it.n_chunks > wave ? (it.n_chunks - wave + kWaves - 1) / kWaves : 0;
+    const int nw = min(64, nk - kb);
+    id0 = 0;
+    id1 = 0;
+    if (lane < nw) {
+        const int32_t* __restrict__ row = p.tables + (size_t)it.i * p.max_blocks;
+        const int tc = it.t0 + 16 * (wave + kWaves * (kb + lane));
+        if constexpr (BS == 8) {
+            id0 = row[tc / 8];
+            id1 = tc + 8 < it.t1 ? row[tc / 8 + 1] : id0;
+        } else {
+            id0 = row[tc / BS];
+        }
+        id0 = min(max(id0, 0), p.P - 1);
+        id1 = min(max(id1, 0), p.P - 1);
+    }
+}
+
+// One work item by the whole workgroup. `cid0/cid1` are this wave's block ids
+// for the item's first 64 chunks (loaded earlier); the next item's ids are
+// fetched at once into `nid0/nid1`, so an item starts with a single memory
+// round trip. LDS `smem` holds m[waves][16], l[waves][16], o[waves][G][D].
 template <int KV, int D, int BS>
-__global__ void __launch_bounds__(kThreads)
-paged_attn_partition_kernel(AttnParams p) {
-    extern __shared__ float smem[];          // m[4][16], l[4][16], o[4][G][D]
+__device__ __forceinline__ void attend_item(const AttnParams& p, float* smem, const Item& it,
+                                            int cid0, int cid1, bool has_next, const Item& nxt,
+                                            int& nid0, int& nid1) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
     const int r16 = lane & 15;               // MFMA row / column index
     const int j4 = lane >> 4;                // token group (scores) / k-group (operands)
-
-    const int per = p.S * p.Hkv;
-    const int part = p.n_part - 1 - (int)(blockIdx.x / per);   // last partitions first
-    const int rem = (int)(blockIdx.x % per);
-    const int i = rem / p.Hkv;
-    const int g = rem - i * p.Hkv;
     const int G = p.G;
-
-    const int L = min(p.lens[i], p.max_len);
-    const int t0 = part * p.part_tokens;
-    if (L <= 0) {                            // empty sequence: zero rows, once
-        if (part == 0)
-            for (int e = threadIdx.x; e < G * D; e += kThreads)
-                p.out[((size_t)i * p.Hq + g * G) * D + e] = 0.f;
-        return;
-    }
-    if (t0 >= L) return;
-    const int t1 = min(L, t0 + p.part_tokens);
-    const int n_chunks = (t1 - t0 + 15) >> 4;
-    const bool split = L > p.part_tokens;
-    const int32_t* __restrict__ row = p.tables + (size_t)i * p.max_blocks;
-
-    // q fragment for head r16 (zero for padding heads), channel map = K's.
+    const int i = it.i, g = it.g, t0 = it.t0, t1 = it.t1;
+    const int n_chunks = it.n_chunks;
+    if (has_next) load_ids<BS>(p, nxt, wave, lane, 0, nid0, nid1);
     using QF = typename QFragT<KV>::T;
     QF qf[q_loads<KV, D>()];
-    {
-        const bool live = r16 < G;
-        const size_t qoff = ((size_t)i * p.Hq + g * G + (live ? r16 : 0)) * D;
-#pragma unroll
-        for (int x = 0; x < q_loads<KV, D>(); ++x) {
-            int c;
-            if constexpr (KV == KV_F32) c = 16 * x + 4 * j4;
-            else if constexpr (KV == KV_BF16) c = 32 * x + 8 * j4;
-            else c = 64 * (x >> 1) + 16 * j4 + 8 * (x & 1);
-            QF val;
-            if constexpr (KV == KV_F32)
-                val = *reinterpret_cast<const float4*>(static_cast<const float*>(p.q) + qoff + c);
-            else
-                val = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.q) + qoff + c);
-            if (!live) val = QF{};
-            qf[x] = val;
-        }
-    }
+    load_q<KV, D>(p, i, g, r16, j4, qf);
 
     f32x4 o[D / 16];
 #pragma unroll
@@ -431,24 +464,13 @@ paged_attn_partition_kernel(AttnParams p) {
         chunk_pv<KV, D>(f, pr, o, tail, first_tok, t1);
     };
 
-    // This wave's chunks are c_k = wave + 4k, k < nk. Their block ids are
-    // fetched once per 64 chunks (lane k holds chunk c_k's ids) and read back
-    // with v_readlane, so no table load sits between a chunk's data loads.
+    // This wave's chunks are c_k = wave + 4k, k < nk, their block ids read
+    // back from a VGPR with v_readlane (one VGPR load per 64 chunks).
     const int nk = n_chunks > wave ? (n_chunks - wave + kWaves - 1) / kWaves : 0;
     for (int kb = 0; kb < nk; kb += 64) {
         const int nw = min(64, nk - kb);
-        int id0 = 0, id1 = 0;
-        if (lane < nw) {
-            const int tc = t0 + 16 * (wave + kWaves * (kb + lane));
-            if constexpr (BS == 8) {
-                id0 = row[tc / 8];
-                id1 = tc + 8 < t1 ? row[tc / 8 + 1] : id0;   // only read entries that exist
-            } else {
-                id0 = row[tc / BS];
-            }
-            id0 = min(max(id0, 0), p.P - 1);
-            id1 = min(max(id1, 0), p.P - 1);
-        }
+        int id0 = cid0, id1 = cid1;
+        if (kb > 0) load_ids<BS>(p, it, wave, lane, kb, id0, id1);
         auto chunk_tc = [&](int k) { return t0 + 16 * (wave + kWaves * (kb + k)); };
         // The scheduling barriers keep each prefetch at its place in program
         // order: nothing of the next chunk's math moves above it (which would
@@ -481,12 +503,11 @@ paged_attn_partition_kernel(AttnParams p) {
             process(fa, wave + kWaves * (kb + k));
         }
     }
-
-    // ---- merge the 4 waves' states (exact rescaling to a common max) ----
+    // ---- merge the waves' states (exact rescaling to a common max) ----
     const float l_tot = head_sum(l_run);
-    float* sm_m = smem;                       // [4][16]
-    float* sm_l = smem + kWaves * 16;         // [4][16]
-    float* sm_o = smem + 2 * kWaves * 16;     // [4][G][D]
+    float* sm_m = smem;                       // [waves][16]
+    float* sm_l = smem + kWaves * 16;         // [waves][16]
+    float* sm_o = smem + 2 * kWaves * 16;     // [waves][G][D]
     if (j4 == 0) {
         sm_m[wave * 16 + r16] = m_run;
         sm_l[wave * 16 + r16] = l_tot;
@@ -498,6 +519,7 @@ paged_attn_partition_kernel(AttnParams p) {
     }
     __syncthreads();
 
+    const size_t nrec = (size_t)p.n_rec;
     for (int e = threadIdx.x; e < G * D; e += kThreads) {
         const int r = e / D;
         const int ch = e - r * D;
@@ -511,41 +533,457 @@ paged_attn_partition_kernel(AttnParams p) {
             num += wt * sm_o[((size_t)w * G + r) * D + ch];
             den += wt * sm_l[w * 16 + r];
         }
-        const size_t h = (size_t)i * p.Hq + g * G + r;
-        if (!split) {
-            p.out[h * D + ch] = num / den * p.v_scale;
+        if (it.rec < 0) {
+            p.out[((size_t)i * p.Hq + g * G + r) * D + ch] = num / den * p.v_scale;
         } else {
-            const size_t slot = h * p.n_part + part;
-            p.ws[slot * D + ch] = num * p.v_scale;
+            const size_t rr = (size_t)it.rec * G + r;
+            p.ws[rr * D + ch] = num * p.v_scale;
             if (ch == 0) {
-                const size_t nrow = (size_t)p.S * p.Hq * p.n_part;
-                p.ws[nrow * D + slot] = M;
-                p.ws[nrow * (D + 1) + slot] = den;
+                p.ws[nrec * G * D + rr] = M;
+                p.ws[nrec * G * (D + 1) + rr] = den;
             }
+        }
+    }
+    __syncthreads();                          // LDS is reused by the next item
+}
+
+// Per-sequence counts over all S sequences, prefix-summed once per workgroup:
+// thread t owns sequences [t*per, t*per + per); pre[t] is the sum over the
+// sequences of threads < t (pre[kThreads] = total). `count(s, L)` is called
+// with the clamped length; the lengths are also stored to `sL` when non-null.
+template <typename F>
+__device__ __forceinline__ void prefix_over_sequences(const AttnParams& p, int* pre, int* wsum,
+                                                      int* sL, F count) {
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int per = (p.S + kThreads - 1) / kThreads;
+    const int s_lo = min(p.S, tid * per);
+    const int s_hi = min(p.S, s_lo + per);
+    int cnt = 0;
+    for (int s = s_lo; s < s_hi; ++s) {
+        const int L = min(p.lens[s], p.max_len);
+        if (sL) sL[s] = L;
+        cnt += count(s, L);
+    }
+    int x = cnt;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(x, off);
+        if (lane >= off) x += y;
+    }
+    if (lane == 63) wsum[wave] = x;
+    __syncthreads();
+    for (int w = 0; w < wave; ++w) x += wsum[w];
+    pre[tid + 1] = x;
+    if (tid == 0) pre[0] = 0;
+    __syncthreads();
+}
+
+// Sequence holding prefix position f (0 <= f < pre[kThreads]) and f's offset in
+// it: binary search over the thread ranges, then a scan of one range.
+template <typename F>
+__device__ __forceinline__ int find_sequence(const AttnParams& p, const int* pre, long long f,
+                                             long long scale, F count, long long& offset) {
+    const int per = (p.S + kThreads - 1) / kThreads;
+    int lo = 0, hi = kThreads;                // pre[lo]*scale <= f < pre[hi]*scale
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if ((long long)pre[mid] * scale <= f) lo = mid; else hi = mid;
+    }
+    long long pos = (long long)pre[lo] * scale;
+    int s = lo * per;
+    for (; s < p.S - 1; ++s) {
+        const long long c = (long long)count(s) * scale;
+        if (f < pos + c) break;
+        pos += c;
+    }
+    offset = f - pos;
+    return s;
+}
+
+// Balanced split: chunk positions c = (sequence-major, then kv head, then
+// 16-token chunk) over all sequences, C in total, cut into W near-equal
+// contiguous ranges (the first C % W ranges one chunk longer).
+__device__ __forceinline__ long long range_start(long long C, long long W, long long w) {
+    const long long q = C / W, r = C % W;
+    return w * q + (w < r ? w : r);
+}
+__device__ __forceinline__ long long range_of(long long C, long long W, long long c) {
+    const long long q = C / W, r = C % W;
+    return c < r * (q + 1) ? c / (q + 1) : r + (c - r * (q + 1)) / q;
+}
+
+// Persistent grid (at most the workgroups the GPU holds at once); the work is
+// enumerated on the device from the context lengths, which each workgroup
+// reads once (kept in LDS when p.cache_lens).
+//  * Fixed partitions (p.balanced == 0): items are (sequence, kv head,
+//    partition); first every full partition of every sequence, then each
+//    sequence's last, ragged one, kv heads fastest; workgroups take items
+//    round-robin in snake order. A sequence with several partitions writes one
+//    partial record per partition.
+//  * Balanced (p.balanced == 1): workgroup w takes the w-th of W equal ranges of
+//    chunk positions, i.e. the pieces of the (sequence, kv head) segments that
+//    fall in it. A piece that is a whole segment writes its output rows;
+//    otherwise (only at the two ends of the range) it writes record 2w (first
+//    piece) or 2w + 1 (last piece), and the merge kernel combines them.
+template <int KV, int D, int BS>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(KV == KV_F32 ? 2 : 3)))
+paged_attn_partition_kernel(AttnParams p) {
+    extern __shared__ float smem[];           // merge area, then the length cache
+    __shared__ int pre[kThreads + 1];
+    __shared__ int wsum[kWaves];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    int* sL = p.cache_lens ? reinterpret_cast<int*>(smem + 2 * kWaves * 16 + kWaves * p.G * D) : nullptr;
+    auto seq_len = [&](int s) { return sL ? sL[s] : min(p.lens[s], p.max_len); };
+    auto n_parts = [&](int L) { return L > 0 ? (L + p.part_tokens - 1) / p.part_tokens : 0; };
+    auto n_chunks_of = [&](int L) { return L > 0 ? (L + 15) >> 4 : 0; };
+    const bool balanced = p.balanced != 0;
+
+    prefix_over_sequences(p, pre, wsum, sL, [&](int, int L) {
+        return balanced ? n_chunks_of(L) : max(n_parts(L) - 1, 0);
+    });
+
+    // Item sources. `fetch` fills the next item of this workgroup, or returns false.
+    long long round = 0;                      // fixed partitions: round-robin round
+    long long c_pos = 0, c_beg = 0, c_end = 0; // balanced: this workgroup's chunk range
+    const long long W = gridDim.x;
+    long long n_items = 0, nA = 0, C = 0;
+    if (balanced) {
+        C = (long long)pre[kThreads] * p.Hkv;
+        c_beg = range_start(C, W, blockIdx.x);
+        c_end = range_start(C, W, (long long)blockIdx.x + 1);
+        c_pos = c_beg;
+        // sequences with no tokens get zero rows (one workgroup each)
+        for (int s = blockIdx.x; s < p.S; s += gridDim.x)
+            if (seq_len(s) <= 0)
+                for (int e = threadIdx.x; e < p.Hq * D; e += kThreads) p.out[(size_t)s * p.Hq * D + e] = 0.f;
+    } else {
+        nA = (long long)pre[kThreads] * p.Hkv;
+        n_items = nA + (long long)p.S * p.Hkv;
+    }
+    auto finish = [&](Item& it) {
+        it.i = __builtin_amdgcn_readfirstlane(it.i);
+        it.g = __builtin_amdgcn_readfirstlane(it.g);
+        it.L = __builtin_amdgcn_readfirstlane(it.L);
+        it.t0 = __builtin_amdgcn_readfirstlane(it.t0);
+        it.t1 = __builtin_amdgcn_readfirstlane(it.t1);
+        it.n_chunks = __builtin_amdgcn_readfirstlane(it.n_chunks);
+        it.rec = __builtin_amdgcn_readfirstlane(it.rec);
+    };
+    auto fetch = [&](Item& it) -> bool {
+        if (balanced) {
+            if (c_pos >= c_end) return false;
+            long long off;
+            const int i = find_sequence(p, pre, c_pos, p.Hkv,
+                                        [&](int s) { return n_chunks_of(seq_len(s)); }, off);
+            const int L = seq_len(i);
+            const int nch = n_chunks_of(L);
+            const int g = (int)(off / nch);
+            const int k0 = (int)(off - (long long)g * nch);
+            const long long left = c_end - c_pos;
+            const int k1 = (int)min<long long>(nch, k0 + left);
+            it.i = i;
+            it.g = g;
+            it.L = L;
+            it.t0 = 16 * k0;
+            it.t1 = min(L, 16 * k1);
+            it.n_chunks = k1 - k0;
+            it.rec = (k0 == 0 && k1 == nch) ? -1 : (int)(2 * (long long)blockIdx.x + (c_pos == c_beg ? 0 : 1));
+            c_pos += k1 - k0;
+        } else {
+            const long long idx = round * W + ((round & 1) ? W - 1 - blockIdx.x : blockIdx.x);
+            if (idx >= n_items) return false;
+            ++round;
+            int part;
+            if (idx < nA) {
+                long long off;
+                it.g = (int)(idx % p.Hkv);
+                it.i = find_sequence(p, pre, idx / p.Hkv, 1,
+                                     [&](int s) { return max(n_parts(seq_len(s)) - 1, 0); }, off);
+                part = (int)off;
+            } else {
+                const long long b = idx - nA;
+                it.i = (int)(b / p.Hkv);
+                it.g = (int)(b - (long long)it.i * p.Hkv);
+                part = max(n_parts(seq_len(it.i)) - 1, 0);
+            }
+            it.L = seq_len(it.i);
+            it.t0 = part * p.part_tokens;
+            it.t1 = min(it.L, it.t0 + p.part_tokens);
+            it.n_chunks = it.L > 0 ? (it.t1 - it.t0 + 15) >> 4 : 0;
+            it.rec = it.L > p.part_tokens ? (it.i * p.Hkv + it.g) * p.n_part + part : -1;
+        }
+        finish(it);
+        return true;
+    };
+
+    Item cur;
+    if (!fetch(cur)) return;
+    int cid0, cid1;
+    load_ids<BS>(p, cur, wave, lane, 0, cid0, cid1);
+    while (true) {
+        Item nxt = cur;
+        const bool has_next = fetch(nxt);
+        int nid0 = 0, nid1 = 0;
+        if (cur.L <= 0) {                     // empty sequence (fixed partitions): zero rows
+            if (has_next) load_ids<BS>(p, nxt, wave, lane, 0, nid0, nid1);
+            for (int e = threadIdx.x; e < p.G * D; e += kThreads)
+                p.out[((size_t)cur.i * p.Hq + cur.g * p.G) * D + e] = 0.f;
+        } else {
+            attend_item<KV, D, BS>(p, smem, cur, cid0, cid1, has_next, nxt, nid0, nid1);
+        }
+        if (!has_next) break;
+        cur = nxt;
+        cid0 = nid0;
+        cid1 = nid1;
+    }
+}
+
+// Balanced split at wave granularity. Chunk positions run sequence-major, then
+// kv head, then 16-token chunk; the W = gridDim.x * kWaves waves each take one of
+// W near-equal contiguous ranges and stream through it with two register
+// buffers, straight across the (sequence, kv head) segment boundaries, so every
+// wave carries the same load and no wave waits for another. A wave finishes a
+// segment at the segment's last chunk or at the end of its range: with the
+// whole segment seen it writes the output rows, otherwise partial record
+// 2w (the segment it started in) or 2w + 1 (the one it ends in), which the
+// merge kernel combines. Per-chunk metadata (block ids, segment, chunk index)
+// sits one chunk per lane in VGPRs, decoded once per 64 chunks.
+template <int KV, int D, int BS>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(KV == KV_F32 ? 2 : 3)))
+paged_attn_stream_kernel(AttnParams p) {
+    extern __shared__ float smem[];           // the length cache (p.cache_lens)
+    __shared__ int pre[kThreads + 1];
+    __shared__ int wsum[kWaves];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int r16 = lane & 15;
+    const int j4 = lane >> 4;
+    const int G = p.G;
+    int* sL = p.cache_lens ? reinterpret_cast<int*>(smem) : nullptr;
+    auto seq_len = [&](int s) { return sL ? sL[s] : min(p.lens[s], p.max_len); };
+    auto n_chunks_of = [&](int L) { return L > 0 ? (L + 15) >> 4 : 0; };
+
+    prefix_over_sequences(p, pre, wsum, sL, [&](int, int L) { return n_chunks_of(L); });
+    for (int s = blockIdx.x; s < p.S; s += gridDim.x)       // sequences with no tokens: zero rows
+        if (seq_len(s) <= 0)
+            for (int e = threadIdx.x; e < p.Hq * D; e += kThreads) p.out[(size_t)s * p.Hq * D + e] = 0.f;
+
+    const long long C = (long long)pre[kThreads] * p.Hkv;
+    const long long W = (long long)gridDim.x * kWaves;
+    const long long w = (long long)blockIdx.x * kWaves + wave;
+    const long long c_beg = range_start(C, W, w);
+    const long long c_end = range_start(C, W, w + 1);
+    if (c_beg >= c_end) return;               // no barriers below: waves are independent
+
+    using QF = typename QFragT<KV>::T;
+    QF qf[q_loads<KV, D>()], qn[q_loads<KV, D>()];
+    f32x4 o[D / 16];
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) o[s] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_run = -INFINITY;
+    float l_run = 0.f;
+    bool seg_from_start = false;              // the current segment began at its chunk 0
+    bool seg_at_range_start = false;          // ... and at this wave's first position
+
+    const long long n_pos = c_end - c_beg;
+    for (long long kb = 0; kb < n_pos; kb += 64) {
+        const int nw = (int)min<long long>(64, n_pos - kb);
+        // lane k: chunk at position c_beg + kb + k
+        int id0 = 0, id1 = 0, mseg = 0, mkc = 0;
+        if (lane < nw) {
+            long long off;
+            const int i = find_sequence(p, pre, c_beg + kb + lane, p.Hkv,
+                                        [&](int s) { return n_chunks_of(seq_len(s)); }, off);
+            const int L = seq_len(i);
+            const int nch = n_chunks_of(L);
+            const int g = (int)(off / nch);
+            const int kc = (int)(off - (long long)g * nch);
+            const int32_t* __restrict__ row = p.tables + (size_t)i * p.max_blocks;
+            const int tok = 16 * kc;
+            if constexpr (BS == 8) {
+                id0 = row[tok / 8];
+                id1 = tok + 8 < L ? row[tok / 8 + 1] : id0;
+            } else {
+                id0 = row[tok / BS];
+            }
+            id0 = min(max(id0, 0), p.P - 1);
+            id1 = min(max(id1, 0), p.P - 1);
+            mseg = i * p.Hkv + g;
+            mkc = kc;
+        }
+        // A chunk that starts a segment also loads that segment's q into qn, so
+        // q arrives with the chunk's K and V rather than one round trip later.
+        // qn holds one pending q (for window chunk qn_k): when the next chunk
+        // starts a segment too before qn is consumed, that chunk loads its q
+        // when it is processed instead.
+        int qn_k = -1;
+        auto issue = [&](Frag<KV, D>& f, int k) {
+            __builtin_amdgcn_sched_barrier(0);
+            const int b0 = __builtin_amdgcn_readlane(id0, k);
+            const int b1 = BS == 8 ? __builtin_amdgcn_readlane(id1, k) : b0;
+            const int seg = __builtin_amdgcn_readlane(mseg, k);
+            const int kc = __builtin_amdgcn_readlane(mkc, k);
+            const int i = seg / p.Hkv;
+            const int g = seg - i * p.Hkv;
+            if ((kc == 0 || c_beg + kb + k == c_beg) && qn_k < 0) {
+                load_q<KV, D>(p, i, g, r16, j4, qn);
+                qn_k = k;
+            }
+            load_chunk<KV, D, BS>(f, p, b0, b1, 16 * kc, g, r16, j4);
+            __builtin_amdgcn_sched_barrier(0);
+        };
+        auto step = [&](Frag<KV, D>& f, int k) {
+            const int seg = __builtin_amdgcn_readlane(mseg, k);
+            const int kc = __builtin_amdgcn_readlane(mkc, k);
+            const int i = seg / p.Hkv;
+            const int g = seg - i * p.Hkv;
+            const int L = __builtin_amdgcn_readfirstlane(seq_len(i));
+            const int nch = n_chunks_of(L);
+            const long long pos = c_beg + kb + k;
+            if (kc == 0 || pos == c_beg) {        // a segment starts
+                if (qn_k == k) {                  // its q came with the chunk
+#pragma unroll
+                    for (int x = 0; x < q_loads<KV, D>(); ++x) qf[x] = qn[x];
+                    qn_k = -1;
+                } else {
+                    load_q<KV, D>(p, i, g, r16, j4, qf);
+                }
+                seg_from_start = kc == 0;
+                seg_at_range_start = pos == c_beg;
+            }
+            const int tc = 16 * kc;
+            const f32x4 sc = chunk_scores<KV, D>(f, qf);
+            const bool tail = tc + 16 > L;
+            const int first_tok = tc + 4 * j4;
+            float x[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                x[e] = sc[e] * p.qk_scale;
+                if (tail && first_tok + e >= L) x[e] = -INFINITY;
+            }
+            const float cm = head_max(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
+            const float m_new = fmaxf(m_run, cm);
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+            float pr[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) pr[e] = __builtin_amdgcn_exp2f(x[e] - m_new);
+            l_run = l_run * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
+            m_run = m_new;
+            if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
+#pragma unroll
+                for (int s = 0; s < D / 16; ++s) o[s] *= alpha;
+            }
+            chunk_pv<KV, D>(f, pr, o, tail, first_tok, L);
+
+            if (kc == nch - 1 || pos == c_end - 1) {   // the segment ends here for this wave
+                const float l_tot = head_sum(l_run);
+                const bool whole = seg_from_start && kc == nch - 1;
+                if (r16 < G) {
+                    if (whole) {
+                        const float sc_o = p.v_scale / l_tot;
+                        float* orow = p.out + ((size_t)i * p.Hq + g * G + r16) * D + 4 * j4;
+#pragma unroll
+                        for (int s = 0; s < D / 16; ++s)
+                            *reinterpret_cast<f32x4*>(orow + 16 * s) = o[s] * sc_o;
+                    } else {
+                        const size_t rr = (size_t)(2 * w + (seg_at_range_start ? 0 : 1)) * G + r16;
+                        const size_t nrec = (size_t)p.n_rec;
+                        float* orec = p.ws + rr * D + 4 * j4;
+#pragma unroll
+                        for (int s = 0; s < D / 16; ++s)
+                            *reinterpret_cast<f32x4*>(orec + 16 * s) = o[s] * p.v_scale;
+                        if (j4 == 0) {
+                            p.ws[nrec * G * D + rr] = m_run;
+                            p.ws[nrec * G * (D + 1) + rr] = l_tot;
+                        }
+                    }
+                }
+#pragma unroll
+                for (int s = 0; s < D / 16; ++s) o[s] = f32x4{0.f, 0.f, 0.f, 0.f};
+                m_run = -INFINITY;
+                l_run = 0.f;
+            }
+        };
+        Frag<KV, D> fa, fb;
+        issue(fa, 0);
+        int k = 0;
+        for (; k + 2 < nw; k += 2) {
+            issue(fb, k + 1);
+            step(fa, k);
+            issue(fa, k + 2);
+            step(fb, k + 1);
+        }
+        if (k + 1 < nw) {
+            issue(fb, k + 1);
+            step(fa, k);
+            step(fb, k + 1);
+        } else {
+            step(fa, k);
         }
     }
 }
 
-// Merge the partitions of every split sequence: one wave per (sequence, head).
-// Lanes hold one partition's (m, l) each (64 partitions per pass); the output
-// loop keeps 8 partitions' loads in flight. Fixed order throughout.
+// Merge partial records into output rows: one wave per (sequence, q head).
+// Fixed partitions: a sequence with n > 1 partitions has records
+// (i*Hkv + g)*n_part + p, p < n. Balanced: a segment split over workgroups
+// w_lo..w_hi has record 2*w_lo + (1 if w_lo's range starts before the
+// segment) and 2*w for the others. Records are combined in that fixed order.
 template <int D>
-__global__ void __launch_bounds__(256)
-paged_attn_reduce_kernel(AttnParams p) {
+__global__ void __launch_bounds__(kThreads)
+paged_attn_merge_kernel(AttnParams p) {
+    __shared__ int pre[kThreads + 1];
+    __shared__ int wsum[kWaves];
+    const bool balanced = p.balanced != 0;
+    if (balanced)
+        prefix_over_sequences(p, pre, wsum, nullptr,
+                              [&](int, int L) { return L > 0 ? (L + 15) >> 4 : 0; });
     const int lane = threadIdx.x & 63;
-    const size_t h = (size_t)blockIdx.x * 4 + (threadIdx.x >> 6);    // (i, head)
-    if (h >= (size_t)p.S * p.Hq) return;
+    const long long h = (long long)blockIdx.x * kWaves + (threadIdx.x >> 6);   // i * Hq + head
+    if (h >= (long long)p.S * p.Hq) return;
     const int i = (int)(h / p.Hq);
+    const int head = (int)(h - (long long)i * p.Hq);
+    const int g = head / p.G;
+    const int r = head - g * p.G;
     const int L = min(p.lens[i], p.max_len);
-    if (L <= p.part_tokens) return;            // written by the partition kernel
-    const int n = (L + p.part_tokens - 1) / p.part_tokens;
-    const size_t nrow = (size_t)p.S * p.Hq * p.n_part;
-    const float* pm = p.ws + nrow * D + h * p.n_part;
-    const float* pl = p.ws + nrow * (D + 1) + h * p.n_part;
-    const float* po = p.ws + h * p.n_part * D;
+    if (L <= 0) return;
+    int n, rec0;                              // records rec0 .. (see below), n of them
+    long long w_lo = 0, seg_off = 0;
+    if (balanced) {
+        const int nch = (L + 15) >> 4;
+        const long long C = (long long)pre[kThreads] * p.Hkv;
+        const long long W = p.n_workers;
+        const int per = (p.S + kThreads - 1) / kThreads;
+        long long cum = pre[i / per];
+        for (int s = (i / per) * per; s < i; ++s) {
+            const int Ls = min(p.lens[s], p.max_len);
+            cum += Ls > 0 ? (Ls + 15) >> 4 : 0;
+        }
+        seg_off = cum * p.Hkv + (long long)g * nch;
+        w_lo = range_of(C, W, seg_off);
+        const long long w_hi = range_of(C, W, seg_off + nch - 1);
+        if (w_lo == w_hi) return;             // one workgroup wrote the rows
+        n = (int)(w_hi - w_lo + 1);
+        rec0 = (int)(2 * w_lo + (range_start(C, W, w_lo) < seg_off ? 1 : 0));
+    } else {
+        if (L <= p.part_tokens) return;       // written by the partition kernel
+        n = (L + p.part_tokens - 1) / p.part_tokens;
+        rec0 = (i * p.Hkv + g) * p.n_part;
+    }
+    // record k of this segment
+    auto rec_of = [&](int k) -> size_t {
+        if (balanced) return k == 0 ? (size_t)rec0 : (size_t)(2 * (w_lo + k));
+        return (size_t)(rec0 + k);
+    };
+    const size_t nrec = (size_t)p.n_rec;
+    const int G = p.G;
+    auto m_at = [&](int k) { return p.ws[nrec * G * D + rec_of(k) * G + r]; };
+    auto l_at = [&](int k) { return p.ws[nrec * G * (D + 1) + rec_of(k) * G + r]; };
     float M = -INFINITY;
     for (int k0 = 0; k0 < n; k0 += 64)
-        if (k0 + lane < n) M = fmaxf(M, pm[k0 + lane]);
+        if (k0 + lane < n) M = fmaxf(M, m_at(k0 + lane));
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
     constexpr int PER = D / 64;
@@ -553,15 +991,15 @@ paged_attn_reduce_kernel(AttnParams p) {
     float den = 0.f;
     for (int k0 = 0; k0 < n; k0 += 64) {
         const int kn = min(64, n - k0);
-        const float wl = k0 + lane < n ? __builtin_amdgcn_exp2f(pm[k0 + lane] - M) : 0.f;
-        den += wl * (k0 + lane < n ? pl[k0 + lane] : 0.f);
+        const float wl = k0 + lane < n ? __builtin_amdgcn_exp2f(m_at(k0 + lane) - M) : 0.f;
+        den += wl * (k0 + lane < n ? l_at(k0 + lane) : 0.f);
         for (int k = 0; k < kn; k += 8) {
             float ov[8][PER];
 #pragma unroll
             for (int u = 0; u < 8; ++u)
 #pragma unroll
                 for (int x = 0; x < PER; ++x)
-                    ov[u][x] = k + u < kn ? po[(size_t)(k0 + k + u) * D + lane + 64 * x] : 0.f;
+                    ov[u][x] = k + u < kn ? p.ws[(rec_of(k0 + k + u) * G + r) * D + lane + 64 * x] : 0.f;
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
                 const float wt = __shfl(wl, (k + u) & 63);
@@ -595,6 +1033,42 @@ AttnKernel pick_bs(int bs) {
 template <int KV>
 AttnKernel pick_d(int d, int bs) {
     return d == 64 ? pick_bs<KV, 64>(bs) : pick_bs<KV, 128>(bs);
+}
+
+template <int KV, int D>
+AttnKernel pick_stream_bs(int bs) {
+    switch (bs) {
+        case 8: return paged_attn_stream_kernel<KV, D, 8>;
+        case 16: return paged_attn_stream_kernel<KV, D, 16>;
+        case 32: return paged_attn_stream_kernel<KV, D, 32>;
+    }
+    return nullptr;
+}
+
+template <int KV>
+AttnKernel pick_stream(int d, int bs) {
+    return d == 64 ? pick_stream_bs<KV, 64>(bs) : pick_stream_bs<KV, 128>(bs);
+}
+
+// Workgroups of `kern` the current device holds at once (cached per kernel,
+// LDS size and device).
+int resident_workgroups(AttnKernel kern, size_t lds) {
+    struct Entry { AttnKernel k; size_t lds; int dev; int n; };
+    static Entry cache[64];
+    static int used = 0;
+    static std::mutex mu;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return -1;
+    std::lock_guard<std::mutex> lock(mu);
+    for (int e = 0; e < used; ++e)
+        if (cache[e].k == kern && cache[e].lds == lds && cache[e].dev == dev) return cache[e].n;
+    int cus = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return -1;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(kern),
+                                                      kThreads, lds) != hipSuccess) return -1;
+    const int n = cus * (per_cu > 0 ? per_cu : 1);
+    if (used < 64) cache[used++] = Entry{kern, lds, dev, n};
+    return n;
 }
 
 int64_t n_partitions(int32_t max_len, int32_t partition_size) {
@@ -644,10 +1118,13 @@ extern "C" pkv_status pkv_kv_cache_write(const void* k_new, const void* v_new, v
     return ok();
 }
 
-extern "C" size_t pkv_paged_decode_attn_workspace_size(int32_t S, int32_t Hq, int32_t d,
+extern "C" size_t pkv_paged_decode_attn_workspace_size(int32_t S, int32_t Hq, int32_t Hkv, int32_t d,
                                                        int32_t max_context_len,
                                                        int32_t partition_size) {
-    if (S <= 0 || Hq <= 0 || d <= 0) return 0;
+    if (S <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || Hq % Hkv != 0) return 0;
+    const size_t G = (size_t)(Hq / Hkv);
+    if (partition_size == PKV_PARTITION_BALANCED)
+        return 2 * (size_t)kMaxWorkers * G * (size_t)(d + 2) * sizeof(float);
     const int64_t n = n_partitions(max_context_len, partition_size);
     if (n <= 1) return 0;
     return (size_t)S * (size_t)Hq * (size_t)n * (size_t)(d + 2) * sizeof(float);
@@ -677,20 +1154,24 @@ extern "C" pkv_status pkv_paged_decode_attn(float* out, const void* q, const voi
     else if (q_dtype == PKV_BF16 && cache_dtype == PKV_BF16) kv = KV_BF16;
     else if (q_dtype == PKV_BF16 && cache_dtype == PKV_FP8_E4M3) kv = KV_FP8;
     else return fail(PKV_E_INVALID, "paged_decode_attn: unsupported q/cache dtypes %d/%d", q_dtype, cache_dtype);
-    if (partition_size < 0 || partition_size % 32 != 0)
-        return fail(PKV_E_INVALID, "paged_decode_attn: partition_size=%d not 0 or a multiple of 32", partition_size);
+    const bool balanced = partition_size == PKV_PARTITION_BALANCED;
+    if (!balanced && (partition_size < 0 || partition_size % 32 != 0))
+        return fail(PKV_E_INVALID, "paged_decode_attn: partition_size=%d not 0, a multiple of 32 or "
+                    "PKV_PARTITION_BALANCED", partition_size);
     if (!std::isfinite(softmax_scale)) return fail(PKV_E_INVALID, "paged_decode_attn: softmax_scale not finite");
     if (kv == KV_FP8 && !(std::isfinite(k_scale) && std::isfinite(v_scale)))
         return fail(PKV_E_INVALID, "paged_decode_attn: fp8 scales not finite");
     if (S == 0) return ok();
     if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
         return fail(PKV_E_INVALID, "paged_decode_attn: NULL pointer");
-    const int64_t n_part = n_partitions(max_context_len, partition_size);
-    const size_t need = pkv_paged_decode_attn_workspace_size(S, Hq, d, max_context_len, partition_size);
+    const int64_t n_part = balanced ? 1 : n_partitions(max_context_len, partition_size);
+    const size_t need = pkv_paged_decode_attn_workspace_size(S, Hq, Hkv, d, max_context_len, partition_size);
     if (need > 0 && (!workspace || workspace_bytes < need))
         return fail(PKV_E_WORKSPACE, "paged_decode_attn: workspace %zu bytes, need %zu", workspace_bytes, need);
-    const int64_t grid = n_part * (int64_t)S * Hkv;
-    if (grid > 0x7FFFFFFFLL) return fail(PKV_E_INVALID, "paged_decode_attn: grid too large");
+    // upper bound on work items (fixed partitions) or chunk positions (balanced)
+    const int64_t n_upper = balanced ? (int64_t)S * Hkv * (((int64_t)max_context_len + 15) / 16)
+                                     : n_part * (int64_t)S * Hkv;
+    if (n_upper > 0x7FFFFFFFLL) return fail(PKV_E_INVALID, "paged_decode_attn: too many work items");
 
     AttnParams prm;
     prm.out = out;
@@ -710,25 +1191,45 @@ extern "C" pkv_status pkv_paged_decode_attn(float* out, const void* q, const voi
     // single pass: one partition long enough for any sequence (whole chunks)
     prm.part_tokens = partition_size > 0 ? partition_size : ((max(max_context_len, 1) + 31) / 32) * 32;
     prm.n_part = (int)n_part;
+    prm.balanced = balanced ? 1 : 0;
     const float ks = kv == KV_FP8 ? k_scale : 1.f;
     prm.qk_scale = softmax_scale * ks * kLog2e;
     prm.v_scale = kv == KV_FP8 ? v_scale : 1.f;
+    prm.cache_lens = S <= kMaxCachedLens;
 
-    AttnKernel kern = kv == KV_F32 ? pick_d<KV_F32>(d, bs)
-                    : kv == KV_BF16 ? pick_d<KV_BF16>(d, bs) : pick_d<KV_FP8>(d, bs);
-    const size_t lds = (size_t)(2 * kWaves * 16 + kWaves * G * d) * sizeof(float);
+    AttnKernel kern;
+    size_t lds;
+    if (balanced) {
+        kern = kv == KV_F32 ? pick_stream<KV_F32>(d, bs)
+             : kv == KV_BF16 ? pick_stream<KV_BF16>(d, bs) : pick_stream<KV_FP8>(d, bs);
+        lds = (size_t)(prm.cache_lens ? S : 0) * sizeof(int);
+    } else {
+        kern = kv == KV_F32 ? pick_d<KV_F32>(d, bs)
+             : kv == KV_BF16 ? pick_d<KV_BF16>(d, bs) : pick_d<KV_FP8>(d, bs);
+        lds = (size_t)(2 * kWaves * 16 + kWaves * G * d + (prm.cache_lens ? S : 0)) * sizeof(float);
+    }
     auto st = static_cast<hipStream_t>(stream);
+    const int resident = resident_workgroups(kern, lds);
+    if (resident <= 0) return fail(PKV_E_HIP, "paged_decode_attn: occupancy query failed");
+    int64_t grid = n_upper < resident ? n_upper : resident;
+    if (balanced) {
+        grid = resident;                      // one wave per share; idle shares exit at once
+        if (grid * kWaves > kMaxWorkers) grid = kMaxWorkers / kWaves;
+    }
+    if (grid < 1) grid = 1;
+    prm.n_workers = (int)(balanced ? grid * kWaves : grid);
+    prm.n_rec = balanced ? 2 * prm.n_workers : (int)(n_part * (int64_t)S * Hkv);
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kThreads), lds, st, prm);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(PKV_E_HIP, "paged_decode_attn: launch failed: %s", hipGetErrorString(e));
-    if (n_part > 1) {
-        const unsigned rgrid = (unsigned)(((int64_t)S * Hq + 3) / 4);
+    if (balanced || n_part > 1) {
+        const unsigned rgrid = (unsigned)(((int64_t)S * Hq + kWaves - 1) / kWaves);
         if (d == 64)
-            hipLaunchKernelGGL(paged_attn_reduce_kernel<64>, dim3(rgrid), dim3(256), 0, st, prm);
+            hipLaunchKernelGGL(paged_attn_merge_kernel<64>, dim3(rgrid), dim3(kThreads), 0, st, prm);
         else
-            hipLaunchKernelGGL(paged_attn_reduce_kernel<128>, dim3(rgrid), dim3(256), 0, st, prm);
+            hipLaunchKernelGGL(paged_attn_merge_kernel<128>, dim3(rgrid), dim3(kThreads), 0, st, prm);
         e = hipGetLastError();
-        if (e != hipSuccess) return fail(PKV_E_HIP, "paged_decode_attn: reduce launch failed: %s", hipGetErrorString(e));
+        if (e != hipSuccess) return fail(PKV_E_HIP, "paged_decode_attn: merge launch failed: %s", hipGetErrorString(e));
     }
     return ok();
 }

@@ -97,7 +97,7 @@ class DeviceStep:
         w = self.w
         s = w.spec
         out = self.out if out is None else out
-        need = pkv.paged_decode_attn_workspace_size(s.S, s.Hq, s.d, w.max_context_len,
+        need = pkv.paged_decode_attn_workspace_size(s.S, s.Hq, s.Hkv, s.d, w.max_context_len,
                                                      partition_size)
         ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda") if need else None
         pkv.paged_decode_attn(out, self.q, self.k_cache, self.v_cache, self.tables, self.lens,

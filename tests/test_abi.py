@@ -204,7 +204,7 @@ def _attn(**kw):
 @pytest.mark.parametrize("kw", [
     dict(Hq=7), dict(Hq=34, Hkv=2), dict(d=96), dict(bs=4), dict(bs=64), dict(P=0),
     dict(maxb=0), dict(maxlen=161), dict(maxlen=-1), dict(qd=0), dict(qd=1, cd=0),
-    dict(qd=2, cd=2), dict(part=16), dict(part=-32), dict(scale=float("inf")),
+    dict(qd=2, cd=2), dict(part=16), dict(part=-32), dict(part=-2), dict(scale=float("inf")),
     dict(qd=1, cd=2, ks=float("nan")), dict(out=None), dict(tab=None), dict(S=-1), dict(Hkv=0),
 ])
 def test_attn_rejects_invalid_arguments(kw):
@@ -213,10 +213,14 @@ def test_attn_rejects_invalid_arguments(kw):
 
 
 def test_attn_workspace_checks():
-    need = pkv.paged_decode_attn_workspace_size(4, 8, 128, 2000, 512)
+    need = pkv.paged_decode_attn_workspace_size(4, 8, 2, 128, 2000, 512)
     assert need == 4 * 8 * 4 * 130 * 4
-    assert pkv.paged_decode_attn_workspace_size(4, 8, 128, 512, 512) == 0
-    assert pkv.paged_decode_attn_workspace_size(4, 8, 128, 2000, 0) == 0
+    assert pkv.paged_decode_attn_workspace_size(4, 8, 2, 128, 512, 512) == 0
+    assert pkv.paged_decode_attn_workspace_size(4, 8, 2, 128, 2000, 0) == 0
+    bal = pkv.paged_decode_attn_workspace_size(4, 8, 2, 128, 2000, pkv.PKV_PARTITION_BALANCED)
+    assert bal == 2 * 4096 * 4 * 130 * 4
+    assert pkv.paged_decode_attn_workspace_size(4, 7, 2, 128, 2000, 512) == 0     # invalid
+    assert _attn(part=pkv.PKV_PARTITION_BALANCED, wsb=bal - 1) == _lib.PKV_E_WORKSPACE
     assert _attn(maxb=200, maxlen=2000, wsb=need - 1) == _lib.PKV_E_WORKSPACE
     assert _attn(maxb=200, maxlen=2000, ws=None, wsb=need) == _lib.PKV_E_WORKSPACE
     assert _attn(S=0) == _lib.PKV_OK                 # nothing to do, nothing launched

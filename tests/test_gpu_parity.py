@@ -19,6 +19,7 @@ from helpers import (TOL, DeviceStep, assert_rows_close, need_gpu, oracle_step, 
                      to_host)
 
 pytestmark = pytest.mark.gpu
+BAL = pkv.PKV_PARTITION_BALANCED
 
 
 @pytest.fixture(autouse=True)
@@ -45,25 +46,25 @@ def _full_case(w, partitions, seqs=None):
 
 
 def test_tiny_fp32():
-    _full_case(W.make("tiny"), [0, 512, 64])
+    _full_case(W.make("tiny"), [0, 512, 64, BAL])
 
 
 def test_small_gqa7():
-    _full_case(W.make("small"), [0, 512])
+    _full_case(W.make("small"), [0, 512, BAL])
 
 
 def test_llama8b():
-    _full_case(W.make("llama8b"), [512, 0, 256])
+    _full_case(W.make("llama8b"), [512, 0, 256, BAL])
 
 
 @pytest.mark.parametrize("bs", [8, 16, 32])
 def test_beam_block_sizes(bs):
-    _full_case(W.make("beam", bs=bs), [0, 512])
+    _full_case(W.make("beam", bs=bs), [0, 512, BAL])
 
 
 def test_long_bf16_sampled():
     # full-size pool and launch; the oracle computes 3 of the 16 sequences
-    _full_case(W.make("long"), [512], seqs=[0, 7, 15])
+    _full_case(W.make("long"), [512, BAL], seqs=[0, 7, 15])
 
 
 def test_long_fp8_sampled():
@@ -96,8 +97,10 @@ def test_long_fp8_sampled():
     ref = oracle.paged_decode_attn(w.q, kc, vc, w.block_tables, w.context_lens, bs=s.bs,
                                    softmax_scale=w.softmax_scale, q_dtype="bf16", cache_dtype="fp8",
                                    k_scale=w.k_scale, v_scale=w.v_scale, seqs=seqs)
-    out = to_host(dev.attend(512))
-    e = assert_rows_close(out[seqs], ref, TOL["fp8"], "long fp8")
+    e = 0.0
+    for part in (512, BAL):
+        out = to_host(dev.attend(part))
+        e = max(e, assert_rows_close(out[seqs], ref, TOL["fp8"], f"long fp8 part={part}"))
     print(f"[case] fp8 max row err {e:.3e}", flush=True)
 
 
@@ -117,7 +120,7 @@ EDGE = [
 def test_edge_shapes(lens, Hq, Hkv, d, bs, dt):
     w = W.make_custom(lens=lens, Hq=Hq, Hkv=Hkv, d=d, bs=bs, q_dtype=dt, cache_dtype=dt,
                       cfg=900 + len(lens) + Hq)
-    dev, out = _full_case(w, [0, 512, 32])
+    dev, out = _full_case(w, [0, 512, 32, BAL])
     for i, L in enumerate(lens):
         if L <= 0:
             assert np.all(out[i] == 0.0)
@@ -195,6 +198,7 @@ def test_block_permutation_bit_identical():
     dev = DeviceStep(w)
     dev.write()
     base = to_host(dev.attend(512)).copy()
+    base_bal = to_host(dev.attend(BAL)).copy()
     pi = np.random.default_rng(77).permutation(w.P)
     k2 = torch.empty_like(dev.k_cache)
     v2 = torch.empty_like(dev.v_cache)
@@ -205,6 +209,7 @@ def test_block_permutation_bit_identical():
     dev.tables = to_dev(np.where(w.block_tables >= 0, pi[np.maximum(w.block_tables, 0)], -1).astype(np.int32))
     out = to_host(dev.attend(512))
     assert np.array_equal(out, base)
+    assert np.array_equal(to_host(dev.attend(BAL)), base_bal)
 
 
 def test_shared_prefix_equals_private_copies_bit_identical():
@@ -213,6 +218,7 @@ def test_shared_prefix_equals_private_copies_bit_identical():
     dev = DeviceStep(w)
     dev.write()
     shared = to_host(dev.attend(512)).copy()
+    shared_bal = to_host(dev.attend(BAL)).copy()
     # give every beam but the first of each group private copies of the prefix
     pre = 1024 // 16
     extra = 96 * pre
@@ -235,6 +241,7 @@ def test_shared_prefix_equals_private_copies_bit_identical():
     dev.k_cache, dev.v_cache, dev.tables = k2, v2, to_dev(tab)
     private = to_host(dev.attend(512))
     assert np.array_equal(private, shared)
+    assert np.array_equal(to_host(dev.attend(BAL)), shared_bal)
 
 
 def test_deterministic_reruns():
@@ -242,6 +249,7 @@ def test_deterministic_reruns():
     w = W.make("small")
     dev = DeviceStep(w)
     dev.write()
-    a = to_host(dev.attend(512)).copy()
-    for _ in range(3):
-        assert np.array_equal(to_host(dev.attend(512)), a)
+    for part in (512, BAL):
+        a = to_host(dev.attend(part)).copy()
+        for _ in range(3):
+            assert np.array_equal(to_host(dev.attend(part)), a)
