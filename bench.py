@@ -33,6 +33,34 @@ HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published peak
 
 ELEM = {"f32": 4, "bf16": 2, "fp8": 1}
 
+DEVICE_SOURCE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "paged_kv_cache_108_amd",
+                             "csrc", "device.hip")
+
+# HBM traffic of one attention call (partition + merge kernels), from
+# rocprofv3 --pmc FETCH_SIZE and --pmc WRITE_SIZE runs of this script's default
+# command, in KiB per call, and the scale that turns each counter into bytes
+# (what the counter reads for a plain copy of known size). Reported only while
+# the kernel source is the one the counters were taken with.
+MEASURED_TRAFFIC = {
+    ("llama8b", "bf16", 16, 512): {
+        "source_sha256": "712f4311347caf3b1092dd2d2aaeb73e87f6684405ac463c4d9ca2ec368e2554",
+        "fetch_kib": 170007.0, "write_kib": 3862.6, "fetch_scale": 2.0, "write_scale": 1.0,
+    },
+}
+
+
+def measured_traffic(name, cache_dtype, bs, part):
+    """Bytes per attention call from the counters, or None when none were taken
+    for this configuration or the kernel source has changed since."""
+    import hashlib
+    m = MEASURED_TRAFFIC.get((name, cache_dtype, bs, part))
+    if m is None:
+        return None
+    with open(DEVICE_SOURCE, "rb") as f:
+        if hashlib.sha256(f.read()).hexdigest() != m["source_sha256"]:
+            return None
+    return int(round(1024 * (m["fetch_kib"] * m["fetch_scale"] + m["write_kib"] * m["write_scale"])))
+
 
 def algorithmic_bytes(w, cache_dtype):
     """(attention bytes, write bytes, logical KV bytes) for one step of workload w."""
@@ -274,7 +302,8 @@ def main():
             "kernel": "paged_decode_attn call (partition kernel"
                       + (" + merge kernel)" if n_part > 1 else ")"),
             "bound": "hbm", "achieved": round(attn_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(attn_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+            "frac": round(attn_gbs / HBM_PEAK_GBS, 4),
+            "traffic": measured_traffic(s.name, cache_dtype, s.bs, part),
         },
         "device": torch.cuda.get_device_name(0),
     }

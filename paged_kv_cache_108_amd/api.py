@@ -15,7 +15,8 @@ from ._lib import (lib, check, PkvError, PkvStats, PKV_F32, PKV_BF16, PKV_FP8_E4
                    PKV_E_NO_BLOCKS, P_i32, P_i64, P_f64, c_vp, c_i64, c_i32, c_f64)
 
 __all__ = [
-    "kv_cache_write", "paged_decode_attn", "paged_decode_attn_workspace_size", "Allocator",
+    "kv_cache_write", "paged_decode_attn", "paged_decode_attn_workspace_size",
+    "paged_decode_attn_workspace", "Allocator",
     "slots_from_tables", "waste_stats", "last_error", "version", "quantise_pool",
     "PkvError", "NoBlocks", "PKV_PARTITION_BALANCED",
 ]
@@ -83,12 +84,22 @@ def paged_decode_attn_workspace_size(S, Hq, Hkv, d, max_context_len, partition_s
                                                           partition_size))
 
 
+def paged_decode_attn_workspace(S, Hq, Hkv, d, max_context_len, partition_size, device="cuda"):
+    """A uint8 device tensor of the size pkv_paged_decode_attn needs (None when
+    it needs none); reusable by any later call with the same or smaller needs."""
+    import torch
+    need = paged_decode_attn_workspace_size(S, Hq, Hkv, d, max_context_len, partition_size)
+    return torch.empty(need, dtype=torch.uint8, device=device) if need else None
+
+
 def paged_decode_attn(out, q, k_cache, v_cache, block_tables, context_lens, *, max_context_len,
                       softmax_scale, k_scale=1.0, v_scale=1.0, partition_size=512,
                       workspace=None, stream=None):
     """pkv_paged_decode_attn. out float32 [S][Hq][d]; q [S][Hq][d]; tables int32
     [S][max_blocks]; context_lens int32 [S]; workspace a uint8 device tensor of at
-    least paged_decode_attn_workspace_size(...) bytes (or None when that is 0);
+    least paged_decode_attn_workspace_size(...) bytes (paged_decode_attn_workspace
+    makes one); None allocates one for this call when one is needed (pass one in
+    loops that must not allocate);
     partition_size 0, a multiple of 32, or PKV_PARTITION_BALANCED."""
     import torch
     S, Hq, d = q.shape
@@ -99,6 +110,9 @@ def paged_decode_attn(out, q, k_cache, v_cache, block_tables, context_lens, *, m
         raise ValueError("paged_decode_attn: tables and lengths must be int32")
     if block_tables.shape[0] != S or context_lens.shape != (S,):
         raise ValueError("paged_decode_attn: tables/lengths shape mismatch")
+    if workspace is None:                     # convenience: a fresh zeroed one for this call
+        workspace = paged_decode_attn_workspace(S, Hq, Hkv, d, int(max_context_len),
+                                                int(partition_size), device=q.device)
     ws_ptr, ws_bytes = ctypes.c_void_p(0), 0
     if workspace is not None:
         ws_ptr, ws_bytes = _dev(workspace, "workspace"), workspace.numel() * workspace.element_size()

@@ -8,10 +8,11 @@
 // the kv head. The pages' own kernel targets other hardware; this one is built
 // for wave64 + MFMA:
 //
-//  * Work item = (sequence i, kv head g, partition p); one 256-thread
-//    workgroup (4 waves) per item. Waves take the item's 16-token chunks
-//    round-robin, each keeping its own online-softmax state; the four states
-//    are merged exactly through LDS at the end.
+//  * Work item = (sequence i, kv head g, partition p). A persistent grid of
+//    256-thread workgroups (4 waves; as many as the GPU holds at once) takes
+//    the items round-robin. Waves take an item's 16-token chunks round-robin,
+//    each keeping its own online-softmax state; the four states are merged
+//    exactly through LDS at the end of the item.
 //  * Scores: S^T[16 tokens][16 heads] = K_chunk . Q^T with one MFMA chain
 //    (bf16 16x16x32, or fp32 16x16x4 for an fp32 cache). The K operand rows
 //    are tokens, so each lane's K fragment is 8 (bf16), 16 (fp8) or 4 (fp32)
@@ -31,8 +32,12 @@
 //    more than one partition writes (m, l, o) partials and a second kernel
 //    merges them in fixed partition order. No atomics anywhere: results are
 //    bit-reproducible.
-//  * Work order: items of the last partition index first, so full-length
-//    items of long sequences start early and short items fill the tail.
+//  * Work order: every full partition of every sequence first, then each
+//    sequence's last, ragged partition, so long items start early and short
+//    ones fill the tail.
+//  * A second decomposition (partition_size = PKV_PARTITION_BALANCED) cuts
+//    the chunks of all (sequence, kv head) segments into one equal range per
+//    wave; pieces of segments write partial records for the merge kernel.
 #include <hip/hip_runtime.h>
 
 #include <cmath>

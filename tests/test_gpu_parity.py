@@ -253,3 +253,4 @@ def test_deterministic_reruns():
         a = to_host(dev.attend(part)).copy()
         for _ in range(3):
             assert np.array_equal(to_host(dev.attend(part)), a)
+
