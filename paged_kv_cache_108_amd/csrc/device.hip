@@ -55,7 +55,6 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 #ifndef PKV_WAVES
@@ -64,7 +63,8 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int kWaves = PKV_WAVES;         // waves per workgroup
 constexpr int kThreads = kWaves * 64;
 constexpr int kMaxCachedLens = 4096;      // sequences whose lengths a workgroup keeps in LDS
-constexpr int kMaxWorkers = 4096;         // waves of the balanced split, at most (sizes its workspace)
+constexpr int kMaxWorkers = 4096;
+constexpr int kSegCost = 1;               // balanced split: positions a segment costs beyond its chunks         // waves of the balanced split, at most (sizes its workspace)
 constexpr float kLog2e = 1.4426950408889634f;
 
 enum KvKind { KV_F32 = 0, KV_BF16 = 1, KV_FP8 = 2 };
@@ -189,6 +189,7 @@ struct AttnParams {
     int balanced;          // 1: balanced split over the grid; 0: fixed partitions
     int n_workers;         // grid size (balanced split)
     int n_rec;             // partial records in the workspace
+    int* desc;             // balanced split: per segment (first record, record count)
     float qk_scale;        // softmax_scale * k_scale * log2(e): scores in the log2 domain
     float v_scale;
 };
@@ -331,12 +332,14 @@ __device__ __forceinline__ void chunk_pv(Frag<KV, D>& f, const float p[4], f32x4
         }
     } else {
         // P = hi + lo, both bf16 (|lo| <= 2^-9 |P|, so the pair carries ~16 bits).
+        // One 16x16x32 MFMA takes both halves: this lane's 8 k-slots are
+        // (hi of its 4 tokens, lo of its 4 tokens) on the P side and the same
+        // 4 V values twice on the V side, so the sum over k is sum_t v_t (hi_t + lo_t).
         const uint32_t h01 = pack_bf16x2(p[0], p[1]);
         const uint32_t h23 = pack_bf16x2(p[2], p[3]);
         const uint32_t l01 = pack_bf16x2(p[0] - bf16_lo_as_f32(h01), p[1] - bf16_hi_as_f32(h01));
         const uint32_t l23 = pack_bf16x2(p[2] - bf16_lo_as_f32(h23), p[3] - bf16_hi_as_f32(h23));
-        const s16x4 phi = __builtin_bit_cast(s16x4, make_uint2(h01, h23));
-        const s16x4 plo = __builtin_bit_cast(s16x4, make_uint2(l01, l23));
+        const bf16x8 php = __builtin_bit_cast(bf16x8, make_uint4(h01, h23, l01, l23));
         // keep-masks for the two bf16 halves of each 32-bit word (tokens +0/+1, +2/+3)
         uint32_t m01 = 0xFFFFFFFFu, m23 = 0xFFFFFFFFu;
         uint32_t m8 = 0xFFFFFFFFu;
@@ -355,9 +358,8 @@ __device__ __forceinline__ void chunk_pv(Frag<KV, D>& f, const float p[4], f32x4
                 const uint32_t w = f.v[s] & m8;   // masked codes become +0
                 vv = make_uint2(fp8x2_to_bf16x2<false>(w), fp8x2_to_bf16x2<true>(w));
             }
-            const s16x4 a = __builtin_bit_cast(s16x4, vv);
-            o[s] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, phi, o[s], 0, 0, 0);
-            o[s] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, plo, o[s], 0, 0, 0);
+            const bf16x8 a = __builtin_bit_cast(bf16x8, make_uint4(vv.x, vv.y, vv.x, vv.y));
+            o[s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, php, o[s], 0, 0, 0);
         }
     }
 }
@@ -619,19 +621,47 @@ __device__ __forceinline__ long long range_of(long long C, long long W, long lon
     return c < r * (q + 1) ? c / (q + 1) : r + (c - r * (q + 1)) / q;
 }
 
+// 32-bit forms for the balanced split (the launcher keeps every position
+// below 2^31). Split: n positions cut into W ranges, range w being
+// [start(w), start(w + 1)) with the first n % W ranges one longer.
+struct Split {
+    unsigned q, r;
+    __device__ Split(unsigned n, unsigned W) : q(n / W), r(n % W) {}
+    __device__ unsigned start(unsigned w) const { return w * q + min(w, r); }
+    __device__ unsigned owner(unsigned c) const {
+        const unsigned big = r * (q + 1);
+        return c < big ? c / (q + 1) : r + (c - big) / q;
+    }
+};
+
+// find_sequence for positions below 2^31.
+template <typename F>
+__device__ __forceinline__ int find_sequence32(const AttnParams& p, const int* pre, unsigned f,
+                                               unsigned scale, F count, unsigned& offset) {
+    const int per = (p.S + kThreads - 1) / kThreads;
+    int lo = 0, hi = kThreads;                // pre[lo]*scale <= f < pre[hi]*scale
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if ((unsigned)pre[mid] * scale <= f) lo = mid; else hi = mid;
+    }
+    unsigned pos = (unsigned)pre[lo] * scale;
+    int s = lo * per;
+    for (; s < p.S - 1; ++s) {
+        const unsigned c = (unsigned)count(s) * scale;
+        if (f < pos + c) break;
+        pos += c;
+    }
+    offset = f - pos;
+    return s;
+}
+
 // Persistent grid (at most the workgroups the GPU holds at once); the work is
 // enumerated on the device from the context lengths, which each workgroup
-// reads once (kept in LDS when p.cache_lens).
-//  * Fixed partitions (p.balanced == 0): items are (sequence, kv head,
-//    partition); first every full partition of every sequence, then each
-//    sequence's last, ragged one, kv heads fastest; workgroups take items
-//    round-robin in snake order. A sequence with several partitions writes one
-//    partial record per partition.
-//  * Balanced (p.balanced == 1): workgroup w takes the w-th of W equal ranges of
-//    chunk positions, i.e. the pieces of the (sequence, kv head) segments that
-//    fall in it. A piece that is a whole segment writes its output rows;
-//    otherwise (only at the two ends of the range) it writes record 2w (first
-//    piece) or 2w + 1 (last piece), and the merge kernel combines them.
+// reads once (kept in LDS when p.cache_lens). Items are (sequence, kv head,
+// partition): first every full partition of every sequence, then each
+// sequence's last, ragged one, kv heads fastest; workgroups take items
+// round-robin in snake order. A sequence with several partitions writes one
+// partial record per partition.
 template <int KV, int D, int BS>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(KV == KV_F32 ? 2 : 3)))
 paged_attn_partition_kernel(AttnParams p) {
@@ -643,31 +673,15 @@ paged_attn_partition_kernel(AttnParams p) {
     int* sL = p.cache_lens ? reinterpret_cast<int*>(smem + 2 * kWaves * 16 + kWaves * p.G * D) : nullptr;
     auto seq_len = [&](int s) { return sL ? sL[s] : min(p.lens[s], p.max_len); };
     auto n_parts = [&](int L) { return L > 0 ? (L + p.part_tokens - 1) / p.part_tokens : 0; };
-    auto n_chunks_of = [&](int L) { return L > 0 ? (L + 15) >> 4 : 0; };
-    const bool balanced = p.balanced != 0;
 
-    prefix_over_sequences(p, pre, wsum, sL, [&](int, int L) {
-        return balanced ? n_chunks_of(L) : max(n_parts(L) - 1, 0);
-    });
+    prefix_over_sequences(p, pre, wsum, sL, [&](int, int L) { return max(n_parts(L) - 1, 0); });
 
-    // Item sources. `fetch` fills the next item of this workgroup, or returns false.
-    long long round = 0;                      // fixed partitions: round-robin round
-    long long c_pos = 0, c_beg = 0, c_end = 0; // balanced: this workgroup's chunk range
+    // `fetch` fills this workgroup's next item (round-robin, snake order), or
+    // returns false.
+    long long round = 0;
     const long long W = gridDim.x;
-    long long n_items = 0, nA = 0, C = 0;
-    if (balanced) {
-        C = (long long)pre[kThreads] * p.Hkv;
-        c_beg = range_start(C, W, blockIdx.x);
-        c_end = range_start(C, W, (long long)blockIdx.x + 1);
-        c_pos = c_beg;
-        // sequences with no tokens get zero rows (one workgroup each)
-        for (int s = blockIdx.x; s < p.S; s += gridDim.x)
-            if (seq_len(s) <= 0)
-                for (int e = threadIdx.x; e < p.Hq * D; e += kThreads) p.out[(size_t)s * p.Hq * D + e] = 0.f;
-    } else {
-        nA = (long long)pre[kThreads] * p.Hkv;
-        n_items = nA + (long long)p.S * p.Hkv;
-    }
+    const long long nA = (long long)pre[kThreads] * p.Hkv;
+    const long long n_items = nA + (long long)p.S * p.Hkv;
     auto finish = [&](Item& it) {
         it.i = __builtin_amdgcn_readfirstlane(it.i);
         it.g = __builtin_amdgcn_readfirstlane(it.g);
@@ -678,48 +692,27 @@ paged_attn_partition_kernel(AttnParams p) {
         it.rec = __builtin_amdgcn_readfirstlane(it.rec);
     };
     auto fetch = [&](Item& it) -> bool {
-        if (balanced) {
-            if (c_pos >= c_end) return false;
+        const long long idx = round * W + ((round & 1) ? W - 1 - blockIdx.x : blockIdx.x);
+        if (idx >= n_items) return false;
+        ++round;
+        int part;
+        if (idx < nA) {
             long long off;
-            const int i = find_sequence(p, pre, c_pos, p.Hkv,
-                                        [&](int s) { return n_chunks_of(seq_len(s)); }, off);
-            const int L = seq_len(i);
-            const int nch = n_chunks_of(L);
-            const int g = (int)(off / nch);
-            const int k0 = (int)(off - (long long)g * nch);
-            const long long left = c_end - c_pos;
-            const int k1 = (int)min<long long>(nch, k0 + left);
-            it.i = i;
-            it.g = g;
-            it.L = L;
-            it.t0 = 16 * k0;
-            it.t1 = min(L, 16 * k1);
-            it.n_chunks = k1 - k0;
-            it.rec = (k0 == 0 && k1 == nch) ? -1 : (int)(2 * (long long)blockIdx.x + (c_pos == c_beg ? 0 : 1));
-            c_pos += k1 - k0;
+            it.g = (int)(idx % p.Hkv);
+            it.i = find_sequence(p, pre, idx / p.Hkv, 1,
+                                 [&](int s) { return max(n_parts(seq_len(s)) - 1, 0); }, off);
+            part = (int)off;
         } else {
-            const long long idx = round * W + ((round & 1) ? W - 1 - blockIdx.x : blockIdx.x);
-            if (idx >= n_items) return false;
-            ++round;
-            int part;
-            if (idx < nA) {
-                long long off;
-                it.g = (int)(idx % p.Hkv);
-                it.i = find_sequence(p, pre, idx / p.Hkv, 1,
-                                     [&](int s) { return max(n_parts(seq_len(s)) - 1, 0); }, off);
-                part = (int)off;
-            } else {
-                const long long b = idx - nA;
-                it.i = (int)(b / p.Hkv);
-                it.g = (int)(b - (long long)it.i * p.Hkv);
-                part = max(n_parts(seq_len(it.i)) - 1, 0);
-            }
-            it.L = seq_len(it.i);
-            it.t0 = part * p.part_tokens;
-            it.t1 = min(it.L, it.t0 + p.part_tokens);
-            it.n_chunks = it.L > 0 ? (it.t1 - it.t0 + 15) >> 4 : 0;
-            it.rec = it.L > p.part_tokens ? (it.i * p.Hkv + it.g) * p.n_part + part : -1;
+            const long long b = idx - nA;
+            it.i = (int)(b / p.Hkv);
+            it.g = (int)(b - (long long)it.i * p.Hkv);
+            part = max(n_parts(seq_len(it.i)) - 1, 0);
         }
+        it.L = seq_len(it.i);
+        it.t0 = part * p.part_tokens;
+        it.t1 = min(it.L, it.t0 + p.part_tokens);
+        it.n_chunks = it.L > 0 ? (it.t1 - it.t0 + 15) >> 4 : 0;
+        it.rec = it.L > p.part_tokens ? (it.i * p.Hkv + it.g) * p.n_part + part : -1;
         finish(it);
         return true;
     };
@@ -746,22 +739,25 @@ paged_attn_partition_kernel(AttnParams p) {
     }
 }
 
-// Balanced split at wave granularity. Chunk positions run sequence-major, then
-// kv head, then 16-token chunk; the W = gridDim.x * kWaves waves each take one of
-// W near-equal contiguous ranges and stream through it with two register
-// buffers, straight across the (sequence, kv head) segment boundaries, so every
-// wave carries the same load and no wave waits for another. A wave finishes a
-// segment at the segment's last chunk or at the end of its range: with the
-// whole segment seen it writes the output rows, otherwise partial record
-// 2w (the segment it started in) or 2w + 1 (the one it ends in), which the
-// merge kernel combines. Per-chunk metadata (block ids, segment, chunk index)
-// sits one chunk per lane in VGPRs, decoded once per 64 chunks.
+// Balanced split at wave granularity. Work positions run sequence-major, then
+// kv head, then position within the (sequence, kv head) segment: a segment of
+// n chunks has kSegCost + n positions, the first kSegCost standing for the
+// fixed cost of starting and finishing a segment (q, the epilogue, the partly
+// filled last chunk). The W = gridDim.x * kWaves waves each take one of W
+// near-equal contiguous ranges of positions and stream the chunks in them
+// without workgroup barriers. A piece of a segment that is the whole segment
+// writes its output rows; otherwise it writes record 2w (the piece that starts
+// wave w's chunks) or 2w + 1 (the piece that ends them). The wave that holds a
+// segment's first chunk writes the segment's descriptor (first record, record
+// count) for the merge kernel. Launched one workgroup per compute unit (one
+// wave per SIMD), so the kernel may use the whole register file.
 template <int KV, int D, int BS>
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(KV == KV_F32 ? 2 : 3)))
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1)))
 paged_attn_stream_kernel(AttnParams p) {
     extern __shared__ float smem[];           // the length cache (p.cache_lens)
     __shared__ int pre[kThreads + 1];
     __shared__ int wsum[kWaves];
+    __shared__ int wmeta[kWaves][4][64];      // per wave: compacted chunk metadata of a window
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int r16 = lane & 15;
@@ -770,94 +766,142 @@ paged_attn_stream_kernel(AttnParams p) {
     int* sL = p.cache_lens ? reinterpret_cast<int*>(smem) : nullptr;
     auto seq_len = [&](int s) { return sL ? sL[s] : min(p.lens[s], p.max_len); };
     auto n_chunks_of = [&](int L) { return L > 0 ? (L + 15) >> 4 : 0; };
+    auto span_of = [&](int L) { return L > 0 ? kSegCost + ((L + 15) >> 4) : 0; };   // positions per segment
+    auto span = [&](int s) { return span_of(seq_len(s)); };
 
-    prefix_over_sequences(p, pre, wsum, sL, [&](int, int L) { return n_chunks_of(L); });
+    prefix_over_sequences(p, pre, wsum, sL, [&](int, int L) { return span_of(L); });
     for (int s = blockIdx.x; s < p.S; s += gridDim.x)       // sequences with no tokens: zero rows
         if (seq_len(s) <= 0)
             for (int e = threadIdx.x; e < p.Hq * D; e += kThreads) p.out[(size_t)s * p.Hq * D + e] = 0.f;
 
-    const long long C = (long long)pre[kThreads] * p.Hkv;
-    const long long W = (long long)gridDim.x * kWaves;
-    const long long w = (long long)blockIdx.x * kWaves + wave;
-    const long long c_beg = range_start(C, W, w);
-    const long long c_end = range_start(C, W, w + 1);
-    if (c_beg >= c_end) return;               // no barriers below: waves are independent
+    const unsigned V = (unsigned)pre[kThreads] * (unsigned)p.Hkv;   // positions in all
+    const unsigned W = gridDim.x * kWaves;
+    const unsigned w = blockIdx.x * kWaves + wave;
+    const Split split(V, W);
+    const unsigned v_beg = split.start(w);
+    const unsigned v_end = split.start(w + 1);
+    const int n_pos = (int)(v_end - v_beg);
+    if (n_pos <= 0) return;                   // no barriers below: waves are independent
+    // position v -> segment (i * Hkv + g) and chunk index (< 0: a cost position)
+    auto locate = [&](unsigned v, int& seg, int& kc, int& L) {
+        unsigned off;
+        const int i = find_sequence32(p, pre, v, (unsigned)p.Hkv, span, off);
+        L = seq_len(i);
+        const unsigned sp = (unsigned)span_of(L);
+        const unsigned g = off / sp;
+        seg = i * p.Hkv + (int)g;
+        kc = (int)(off - g * sp) - kSegCost;
+    };
+
+    // Chunk metadata of window kb (64 positions), compacted to the window's
+    // chunks: lane k holds the block ids, segment, chunk index and window
+    // offset of the window's k-th chunk; nw chunks in all. `fetch_window`
+    // locates the positions and starts the table reads (lane 63, when free,
+    // locates this wave's last position); `compact_window` uses their results.
+    int id0 = 0, id1 = 0, mseg = 0, mkc = 0, mvo = 0, nw = 0;
+    int a0 = 0, a1 = 0, a_seg = 0, a_kc = -1, a_nv = 0;
+    auto fetch_window = [&](int kb) {
+        a_nv = min(64, n_pos - kb);
+        a0 = 0; a1 = 0; a_seg = 0; a_kc = -1;
+        const bool in = lane < a_nv;
+        if (in || (kb == 0 && lane == 63)) {
+            int L;
+            locate(in ? v_beg + kb + lane : v_end - 1, a_seg, a_kc, L);
+            if (in && a_kc >= 0) {
+                const int i = a_seg / p.Hkv;
+                const int32_t* __restrict__ row = p.tables + (size_t)i * p.max_blocks;
+                const int tok = 16 * a_kc;
+                if constexpr (BS == 8) {
+                    a0 = row[tok / 8];
+                    a1 = tok + 8 < L ? row[tok / 8 + 1] : a0;
+                } else {
+                    a0 = row[tok / BS];
+                }
+            }
+        }
+    };
+    auto compact_window = [&]() {
+        const bool real = lane < a_nv && a_kc >= 0;
+        const unsigned long long mask = __builtin_amdgcn_ballot_w64(real);
+        const int dst = __builtin_amdgcn_mbcnt_hi((unsigned)(mask >> 32),
+                                                  __builtin_amdgcn_mbcnt_lo((unsigned)mask, 0u));
+        if (real) {
+            wmeta[wave][0][dst] = min(max(a0, 0), p.P - 1);
+            wmeta[wave][1][dst] = min(max(a1, 0), p.P - 1);
+            wmeta[wave][2][dst] = a_seg;
+            wmeta[wave][3][dst] = a_kc | (lane << 24);
+        }
+        nw = __builtin_popcountll(mask);
+        id0 = wmeta[wave][0][lane];
+        id1 = wmeta[wave][1][lane];
+        mseg = wmeta[wave][2][lane];
+        const int x = wmeta[wave][3][lane];
+        mkc = x & 0xFFFFFF;
+        mvo = x >> 24;
+    };
+    fetch_window(0);
+    // this wave's last chunk: its last position, or the one before a trailing
+    // cost position
+    int last_seg, last_kc;
+    if (n_pos < 64) {
+        last_seg = __builtin_amdgcn_readlane(a_seg, 63);
+        last_kc = __builtin_amdgcn_readlane(a_kc, 63);
+    } else {
+        int L;
+        locate(v_end - 1, last_seg, last_kc, L);
+        last_seg = __builtin_amdgcn_readfirstlane(last_seg);
+        last_kc = __builtin_amdgcn_readfirstlane(last_kc);
+    }
+    const unsigned v_last = last_kc >= 0 ? v_end - 1 : v_end - 2 - (unsigned)(last_kc + kSegCost);
+
+    compact_window();
 
     using QF = typename QFragT<KV>::T;
-    QF qf[q_loads<KV, D>()], qn[q_loads<KV, D>()];
+    QF qf[q_loads<KV, D>()];
     f32x4 o[D / 16];
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) o[s] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m_run = -INFINITY;
     float l_run = 0.f;
+    bool started = false;                     // this wave has begun its first chunk
     bool seg_from_start = false;              // the current segment began at its chunk 0
-    bool seg_at_range_start = false;          // ... and at this wave's first position
+    bool seg_at_range_start = false;          // ... and at this wave's first chunk
 
-    const long long n_pos = c_end - c_beg;
-    for (long long kb = 0; kb < n_pos; kb += 64) {
-        const int nw = (int)min<long long>(64, n_pos - kb);
-        // lane k: chunk at position c_beg + kb + k
-        int id0 = 0, id1 = 0, mseg = 0, mkc = 0;
-        if (lane < nw) {
-            long long off;
-            const int i = find_sequence(p, pre, c_beg + kb + lane, p.Hkv,
-                                        [&](int s) { return n_chunks_of(seq_len(s)); }, off);
-            const int L = seq_len(i);
-            const int nch = n_chunks_of(L);
-            const int g = (int)(off / nch);
-            const int kc = (int)(off - (long long)g * nch);
-            const int32_t* __restrict__ row = p.tables + (size_t)i * p.max_blocks;
-            const int tok = 16 * kc;
-            if constexpr (BS == 8) {
-                id0 = row[tok / 8];
-                id1 = tok + 8 < L ? row[tok / 8 + 1] : id0;
-            } else {
-                id0 = row[tok / BS];
-            }
-            id0 = min(max(id0, 0), p.P - 1);
-            id1 = min(max(id1, 0), p.P - 1);
-            mseg = i * p.Hkv + g;
-            mkc = kc;
+    for (int kb = 0; kb < n_pos; kb += 64) {
+        if (kb > 0) {
+            fetch_window(kb);
+            compact_window();
         }
-        // A chunk that starts a segment also loads that segment's q into qn, so
-        // q arrives with the chunk's K and V rather than one round trip later.
-        // qn holds one pending q (for window chunk qn_k): when the next chunk
-        // starts a segment too before qn is consumed, that chunk loads its q
-        // when it is processed instead.
-        int qn_k = -1;
+        if (nw == 0) continue;
         auto issue = [&](Frag<KV, D>& f, int k) {
             __builtin_amdgcn_sched_barrier(0);
             const int b0 = __builtin_amdgcn_readlane(id0, k);
             const int b1 = BS == 8 ? __builtin_amdgcn_readlane(id1, k) : b0;
             const int seg = __builtin_amdgcn_readlane(mseg, k);
             const int kc = __builtin_amdgcn_readlane(mkc, k);
-            const int i = seg / p.Hkv;
-            const int g = seg - i * p.Hkv;
-            if ((kc == 0 || c_beg + kb + k == c_beg) && qn_k < 0) {
-                load_q<KV, D>(p, i, g, r16, j4, qn);
-                qn_k = k;
-            }
+            const int g = seg % p.Hkv;
             load_chunk<KV, D, BS>(f, p, b0, b1, 16 * kc, g, r16, j4);
             __builtin_amdgcn_sched_barrier(0);
         };
         auto step = [&](Frag<KV, D>& f, int k) {
             const int seg = __builtin_amdgcn_readlane(mseg, k);
             const int kc = __builtin_amdgcn_readlane(mkc, k);
+            const unsigned v = v_beg + kb + __builtin_amdgcn_readlane(mvo, k);
             const int i = seg / p.Hkv;
             const int g = seg - i * p.Hkv;
             const int L = __builtin_amdgcn_readfirstlane(seq_len(i));
             const int nch = n_chunks_of(L);
-            const long long pos = c_beg + kb + k;
-            if (kc == 0 || pos == c_beg) {        // a segment starts
-                if (qn_k == k) {                  // its q came with the chunk
-#pragma unroll
-                    for (int x = 0; x < q_loads<KV, D>(); ++x) qf[x] = qn[x];
-                    qn_k = -1;
-                } else {
-                    load_q<KV, D>(p, i, g, r16, j4, qf);
-                }
+            const bool first = !started;
+            started = true;
+            if (kc == 0 || first) {               // a segment starts
+                load_q<KV, D>(p, i, g, r16, j4, qf);
                 seg_from_start = kc == 0;
-                seg_at_range_start = pos == c_beg;
+                seg_at_range_start = first;
+                if (kc == 0 && lane == 0) {       // descriptor for the merge kernel
+                    const unsigned w_hi = split.owner(v + nch - 1);
+                    p.desc[2 * seg] = (int)(2 * w + (first ? 0 : 1));
+                    p.desc[2 * seg + 1] = (int)(w_hi - w + 1);
+                }
             }
             const int tc = 16 * kc;
             const f32x4 sc = chunk_scores<KV, D>(f, qf);
@@ -883,7 +927,7 @@ paged_attn_stream_kernel(AttnParams p) {
             }
             chunk_pv<KV, D>(f, pr, o, tail, first_tok, L);
 
-            if (kc == nch - 1 || pos == c_end - 1) {   // the segment ends here for this wave
+            if (kc == nch - 1 || v == v_last) {   // the segment ends here for this wave
                 const float l_tot = head_sum(l_run);
                 const bool whole = seg_from_start && kc == nch - 1;
                 if (r16 < G) {
@@ -933,18 +977,15 @@ paged_attn_stream_kernel(AttnParams p) {
 
 // Merge partial records into output rows: one wave per (sequence, q head).
 // Fixed partitions: a sequence with n > 1 partitions has records
-// (i*Hkv + g)*n_part + p, p < n. Balanced: a segment split over workgroups
+// (i*Hkv + g)*n_part + p, p < n. Balanced: a segment split over waves
 // w_lo..w_hi has record 2*w_lo + (1 if w_lo's range starts before the
-// segment) and 2*w for the others. Records are combined in that fixed order.
+// segment) and 2*w for the others; the attention kernel left the first record
+// and the count in the segment's descriptor. Records are combined in that
+// fixed order.
 template <int D>
 __global__ void __launch_bounds__(kThreads)
 paged_attn_merge_kernel(AttnParams p) {
-    __shared__ int pre[kThreads + 1];
-    __shared__ int wsum[kWaves];
     const bool balanced = p.balanced != 0;
-    if (balanced)
-        prefix_over_sequences(p, pre, wsum, nullptr,
-                              [&](int, int L) { return L > 0 ? (L + 15) >> 4 : 0; });
     const int lane = threadIdx.x & 63;
     const long long h = (long long)blockIdx.x * kWaves + (threadIdx.x >> 6);   // i * Hq + head
     if (h >= (long long)p.S * p.Hq) return;
@@ -955,23 +996,13 @@ paged_attn_merge_kernel(AttnParams p) {
     const int L = min(p.lens[i], p.max_len);
     if (L <= 0) return;
     int n, rec0;                              // records rec0 .. (see below), n of them
-    long long w_lo = 0, seg_off = 0;
+    long long w_lo = 0;
     if (balanced) {
-        const int nch = (L + 15) >> 4;
-        const long long C = (long long)pre[kThreads] * p.Hkv;
-        const long long W = p.n_workers;
-        const int per = (p.S + kThreads - 1) / kThreads;
-        long long cum = pre[i / per];
-        for (int s = (i / per) * per; s < i; ++s) {
-            const int Ls = min(p.lens[s], p.max_len);
-            cum += Ls > 0 ? (Ls + 15) >> 4 : 0;
-        }
-        seg_off = cum * p.Hkv + (long long)g * nch;
-        w_lo = range_of(C, W, seg_off);
-        const long long w_hi = range_of(C, W, seg_off + nch - 1);
-        if (w_lo == w_hi) return;             // one workgroup wrote the rows
-        n = (int)(w_hi - w_lo + 1);
-        rec0 = (int)(2 * w_lo + (range_start(C, W, w_lo) < seg_off ? 1 : 0));
+        const int seg = i * p.Hkv + g;
+        rec0 = p.desc[2 * seg];
+        n = p.desc[2 * seg + 1];
+        if (n <= 1) return;                   // one wave wrote the rows
+        w_lo = rec0 >> 1;
     } else {
         if (L <= p.part_tokens) return;       // written by the partition kernel
         n = (L + p.part_tokens - 1) / p.part_tokens;
@@ -1055,6 +1086,20 @@ AttnKernel pick_stream(int d, int bs) {
     return d == 64 ? pick_stream_bs<KV, 64>(bs) : pick_stream_bs<KV, 128>(bs);
 }
 
+// Compute units of the current device (cached per device).
+int compute_units() {
+    static int cache[64] = {};
+    static std::mutex mu;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return -1;
+    std::lock_guard<std::mutex> lock(mu);
+    if (dev < 64 && cache[dev] > 0) return cache[dev];
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return -1;
+    if (dev < 64) cache[dev] = cus;
+    return cus;
+}
+
 // Workgroups of `kern` the current device holds at once (cached per kernel,
 // LDS size and device).
 int resident_workgroups(AttnKernel kern, size_t lds) {
@@ -1074,6 +1119,13 @@ int resident_workgroups(AttnKernel kern, size_t lds) {
     const int n = cus * (per_cu > 0 ? per_cu : 1);
     if (used < 64) cache[used++] = Entry{kern, lds, dev, n};
     return n;
+}
+
+// Balanced split: partial records of up to kMaxWorkers waves, two each
+// (256-byte multiple); the segment descriptors follow them.
+size_t balanced_records_bytes(size_t G, int d) {
+    const size_t b = 2 * (size_t)kMaxWorkers * G * (size_t)(d + 2) * sizeof(float);
+    return (b + 255) / 256 * 256;
 }
 
 int64_t n_partitions(int32_t max_len, int32_t partition_size) {
@@ -1129,7 +1181,7 @@ extern "C" size_t pkv_paged_decode_attn_workspace_size(int32_t S, int32_t Hq, in
     if (S <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || Hq % Hkv != 0) return 0;
     const size_t G = (size_t)(Hq / Hkv);
     if (partition_size == PKV_PARTITION_BALANCED)
-        return 2 * (size_t)kMaxWorkers * G * (size_t)(d + 2) * sizeof(float);
+        return balanced_records_bytes(G, d) + 2 * (size_t)S * (size_t)Hkv * sizeof(int);
     const int64_t n = n_partitions(max_context_len, partition_size);
     if (n <= 1) return 0;
     return (size_t)S * (size_t)Hq * (size_t)n * (size_t)(d + 2) * sizeof(float);
@@ -1174,7 +1226,7 @@ extern "C" pkv_status pkv_paged_decode_attn(float* out, const void* q, const voi
     if (need > 0 && (!workspace || workspace_bytes < need))
         return fail(PKV_E_WORKSPACE, "paged_decode_attn: workspace %zu bytes, need %zu", workspace_bytes, need);
     // upper bound on work items (fixed partitions) or chunk positions (balanced)
-    const int64_t n_upper = balanced ? (int64_t)S * Hkv * (((int64_t)max_context_len + 15) / 16)
+    const int64_t n_upper = balanced ? (int64_t)S * Hkv * (((int64_t)max_context_len + 15) / 16 + kSegCost)
                                      : n_part * (int64_t)S * Hkv;
     if (n_upper > 0x7FFFFFFFLL) return fail(PKV_E_INVALID, "paged_decode_attn: too many work items");
 
@@ -1186,6 +1238,9 @@ extern "C" pkv_status pkv_paged_decode_attn(float* out, const void* q, const voi
     prm.tables = block_tables;
     prm.lens = context_lens;
     prm.ws = static_cast<float*>(workspace);
+    prm.desc = balanced ? reinterpret_cast<int*>(static_cast<char*>(workspace) +
+                                                 balanced_records_bytes((size_t)G, d))
+                        : nullptr;
     prm.S = S;
     prm.Hq = Hq;
     prm.Hkv = Hkv;
@@ -1218,7 +1273,13 @@ extern "C" pkv_status pkv_paged_decode_attn(float* out, const void* q, const voi
     if (resident <= 0) return fail(PKV_E_HIP, "paged_decode_attn: occupancy query failed");
     int64_t grid = n_upper < resident ? n_upper : resident;
     if (balanced) {
-        grid = resident;                      // one wave per share; idle shares exit at once
+        // One workgroup per compute unit: a single wave per SIMD streams at the
+        // same rate as any other (several resident waves per SIMD do not get
+        // equal shares of memory bandwidth, which equal static ranges cannot
+        // absorb). Idle ranges exit at once.
+        const int cus = compute_units();
+        if (cus <= 0) return fail(PKV_E_HIP, "paged_decode_attn: device query failed");
+        grid = cus < resident ? cus : resident;
         if (grid * kWaves > kMaxWorkers) grid = kMaxWorkers / kWaves;
     }
     if (grid < 1) grid = 1;

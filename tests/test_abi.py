@@ -218,7 +218,7 @@ def test_attn_workspace_checks():
     assert pkv.paged_decode_attn_workspace_size(4, 8, 2, 128, 512, 512) == 0
     assert pkv.paged_decode_attn_workspace_size(4, 8, 2, 128, 2000, 0) == 0
     bal = pkv.paged_decode_attn_workspace_size(4, 8, 2, 128, 2000, pkv.PKV_PARTITION_BALANCED)
-    assert bal == 2 * 4096 * 4 * 130 * 4
+    assert bal == 2 * 4096 * 4 * 130 * 4 + 2 * 4 * 2 * 4     # records + segment descriptors
     assert pkv.paged_decode_attn_workspace_size(4, 7, 2, 128, 2000, 512) == 0     # invalid
     assert _attn(part=pkv.PKV_PARTITION_BALANCED, wsb=bal - 1) == _lib.PKV_E_WORKSPACE
     assert _attn(maxb=200, maxlen=2000, wsb=need - 1) == _lib.PKV_E_WORKSPACE
