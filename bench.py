@@ -3,9 +3,10 @@
 
 A step is the whole hot path over one batch: the KV-cache write of each
 sequence's new token (pkv_kv_cache_write), then paged decode attention over
-every sequence's context including that token (pkv_paged_decode_attn: the
-partition kernel and, for split sequences, the merge kernel). Inputs are
-seeded synthetic workloads already resident in HBM.
+every sequence's context including that token (pkv_paged_decode_attn: by
+default the balanced split, i.e. the stream kernel and the merge kernel;
+--partition N selects fixed partitions of N tokens). Inputs are seeded
+synthetic workloads already resident in HBM.
 
 Timing: W untimed warm-up steps, then K timed steps. Before each timed step
 (outside its event pair) a 1 GiB buffer is read so neither the 256 MB
@@ -36,15 +37,15 @@ ELEM = {"f32": 4, "bf16": 2, "fp8": 1}
 DEVICE_SOURCE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "paged_kv_cache_108_amd",
                              "csrc", "device.hip")
 
-# HBM traffic of one attention call (partition + merge kernels), from
+# HBM traffic of one attention call (its two kernels), from
 # rocprofv3 --pmc FETCH_SIZE and --pmc WRITE_SIZE runs of this script's default
 # command, in KiB per call, and the scale that turns each counter into bytes
 # (what the counter reads for a plain copy of known size). Reported only while
 # the kernel source is the one the counters were taken with.
 MEASURED_TRAFFIC = {
-    ("llama8b", "bf16", 16, 512): {
-        "source_sha256": "712f4311347caf3b1092dd2d2aaeb73e87f6684405ac463c4d9ca2ec368e2554",
-        "fetch_kib": 170007.0, "write_kib": 3862.6, "fetch_scale": 2.0, "write_scale": 1.0,
+    ("llama8b", "bf16", 16, -1): {
+        "source_sha256": "e06630c44dcd90da823d443abc97b8e0b85e4a432533276de847169da51bbf60",
+        "fetch_kib": 170031.2, "write_kib": 3844.3, "fetch_scale": 2.0, "write_scale": 1.0,
     },
 }
 
@@ -156,7 +157,9 @@ def main():
                     choices=["tiny", "small", "llama8b", "beam", "long"])
     ap.add_argument("--bs", type=int, default=None)
     ap.add_argument("--kv", default=None, choices=[None, "bf16", "fp8", "f32"])
-    ap.add_argument("--partition", type=int, default=None)
+    ap.add_argument("--partition", type=int, default=-1,
+                    help="partition_size for paged_decode_attn: -1 = balanced split (default), "
+                         "0 = one pass per (sequence, kv head), else tokens per partition")
     ap.add_argument("--no-flush", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
@@ -192,7 +195,7 @@ def main():
     w = W.make(args.config, bs=args.bs, cache_dtype=args.kv)
     s = w.spec
     cache_dtype = s.cache_dtype
-    part = s.partition_size if args.partition is None else args.partition
+    part = args.partition
 
     def dev(a):
         a = np.ascontiguousarray(a)
@@ -264,7 +267,13 @@ def main():
     step_bytes = attn_bytes + write_bytes
     value = step_bytes / (step_mean * 1e-3) / 1e9
     attn_gbs = attn_bytes / (attn_mean * 1e-3) / 1e9
-    n_part = -(-w.max_context_len // part) if part else 1
+    if part == pkv.PKV_PARTITION_BALANCED:
+        kernel_name = "paged_decode_attn call (balanced stream kernel + merge kernel)"
+        split = "balanced: equal cost-weighted chunk ranges, one per wave"
+    else:
+        n_part = -(-w.max_context_len // part) if part else 1
+        kernel_name = "paged_decode_attn call (partition kernel" + (" + merge kernel)" if n_part > 1 else ")")
+        split = f"partitions of {part} tokens" if part else "one pass per (sequence, kv head)"
 
     result = {
         "metric": "paged decode attention: achieved HBM GB/s (% of peak) and seq-steps/sec at 1 GPU",
@@ -284,7 +293,7 @@ def main():
         "config": {
             "workload": f"{s.name}: {s.description}",
             "sequences": s.S, "q_heads": s.Hq, "kv_heads": s.Hkv, "head_dim": s.d,
-            "block_size": s.bs, "kv_dtype": cache_dtype, "partition_size": part,
+            "block_size": s.bs, "kv_dtype": cache_dtype, "partition_size": part, "split": split,
             "context_tokens": int(w.context_lens.sum()), "unique_tokens": int(unique_tokens),
             "max_context_len": w.max_context_len, "pool_blocks": w.P,
             "cache_flush_between_steps": not args.no_flush,
@@ -299,8 +308,7 @@ def main():
         "bytes": {"attn_algorithmic": attn_bytes, "write_algorithmic": write_bytes,
                   "kv_logical": logical_kv},
         "roofline": {
-            "kernel": "paged_decode_attn call (partition kernel"
-                      + (" + merge kernel)" if n_part > 1 else ")"),
+            "kernel": kernel_name,
             "bound": "hbm", "achieved": round(attn_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(attn_gbs / HBM_PEAK_GBS, 4),
             "traffic": measured_traffic(s.name, cache_dtype, s.bs, part),

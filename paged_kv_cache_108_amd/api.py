@@ -93,14 +93,16 @@ def paged_decode_attn_workspace(S, Hq, Hkv, d, max_context_len, partition_size, 
 
 
 def paged_decode_attn(out, q, k_cache, v_cache, block_tables, context_lens, *, max_context_len,
-                      softmax_scale, k_scale=1.0, v_scale=1.0, partition_size=512,
+                      softmax_scale, k_scale=1.0, v_scale=1.0, partition_size=PKV_PARTITION_BALANCED,
                       workspace=None, stream=None):
     """pkv_paged_decode_attn. out float32 [S][Hq][d]; q [S][Hq][d]; tables int32
     [S][max_blocks]; context_lens int32 [S]; workspace a uint8 device tensor of at
     least paged_decode_attn_workspace_size(...) bytes (paged_decode_attn_workspace
     makes one); None allocates one for this call when one is needed (pass one in
     loops that must not allocate);
-    partition_size 0, a multiple of 32, or PKV_PARTITION_BALANCED."""
+    partition_size PKV_PARTITION_BALANCED (default: equal cost-weighted chunk
+    ranges, one per wave), 0 (one pass per sequence and kv head) or a multiple
+    of 32 (fixed partitions of that many tokens)."""
     import torch
     S, Hq, d = q.shape
     P, Hkv, bs, _ = k_cache.shape

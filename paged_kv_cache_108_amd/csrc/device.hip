@@ -1017,14 +1017,42 @@ paged_attn_merge_kernel(AttnParams p) {
     const int G = p.G;
     auto m_at = [&](int k) { return p.ws[nrec * G * D + rec_of(k) * G + r]; };
     auto l_at = [&](int k) { return p.ws[nrec * G * (D + 1) + rec_of(k) * G + r]; };
+    constexpr int PER = D / 64;
+    float num[PER] = {};
+    float den = 0.f;
+    if (n <= 8) {
+        // up to 8 records: every load of the row is issued before any is used
+        float mv[8], lv[8], ov[8][PER];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const bool in = k < n;
+            mv[k] = in ? m_at(k) : -INFINITY;
+            lv[k] = in ? l_at(k) : 0.f;
+#pragma unroll
+            for (int x = 0; x < PER; ++x)
+                ov[k][x] = in ? p.ws[(rec_of(k) * G + r) * D + lane + 64 * x] : 0.f;
+        }
+        float M = -INFINITY;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) M = fmaxf(M, mv[k]);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            if (k < n) {
+                const float wt = __builtin_amdgcn_exp2f(mv[k] - M);
+                den += wt * lv[k];
+#pragma unroll
+                for (int x = 0; x < PER; ++x) num[x] += wt * ov[k][x];
+            }
+        }
+#pragma unroll
+        for (int x = 0; x < PER; ++x) p.out[h * D + lane + 64 * x] = num[x] / den;
+        return;
+    }
     float M = -INFINITY;
     for (int k0 = 0; k0 < n; k0 += 64)
         if (k0 + lane < n) M = fmaxf(M, m_at(k0 + lane));
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-    constexpr int PER = D / 64;
-    float num[PER] = {};
-    float den = 0.f;
     for (int k0 = 0; k0 < n; k0 += 64) {
         const int kn = min(64, n - k0);
         const float wl = k0 + lane < n ? __builtin_amdgcn_exp2f(m_at(k0 + lane) - M) : 0.f;
