@@ -101,8 +101,10 @@ pkv_status pkv_kv_cache_write(const void* k_new, const void* v_new,
 
 /*
  * Bytes of workspace pkv_paged_decode_attn needs for these sizes:
- *  - partition_size == PKV_PARTITION_BALANCED: 2 * 4096 * (Hq/Hkv) * (d + 2) * 4
- *    (two partial records per wave, at most 4096 waves);
+ *  - partition_size == PKV_PARTITION_BALANCED: R + 2 * S * Hkv * 4, where
+ *    R = 2 * 4096 * (Hq/Hkv) * (d + 2) * 4 rounded up to a multiple of 256
+ *    (two partial records per wave, at most 4096 waves) and the rest holds
+ *    one (first record, record count) descriptor per (sequence, kv head);
  *  - otherwise 0 when no sequence can span more than one partition
  *    (partition_size == 0 or max_context_len <= partition_size), else
  *    S * Hq * n_part * (d + 2) * 4 with n_part = ceil(max_context_len / partition_size).
@@ -149,17 +151,18 @@ size_t pkv_paged_decode_attn_workspace_size(int32_t S, int32_t Hq, int32_t Hkv, 
  *  - a positive multiple of 32: fixed partitions of that many tokens; a
  *    sequence longer than partition_size is split into
  *    ceil(L_i / partition_size) partitions;
- *  - PKV_PARTITION_BALANCED: every resident wave of the GPU takes an equal
- *    contiguous share of all (sequence, kv head, 16-token chunk) work, so a
- *    long sequence is split wherever the shares cut it and every wave
- *    finishes at about the same time.
+ *  - PKV_PARTITION_BALANCED: all (sequence, kv head, 16-token chunk) work,
+ *    with each (sequence, kv head) weighted by one extra chunk for its fixed
+ *    costs, is cut into equal contiguous shares, one per wave of a grid of one
+ *    workgroup per compute unit; a long sequence is split wherever the shares
+ *    cut it, and every wave finishes at about the same time.
  * workspace: device memory of at least
  * pkv_paged_decode_attn_workspace_size(...) bytes (may be NULL when that is 0);
  * its contents on entry do not matter. Calls that overlap in time must not
  * share a workspace.
  *
  * The result is deterministic for a given GPU: no atomics, fixed reduction
- * order (the balanced split depends on the number of resident waves).
+ * order (the balanced split depends on the number of compute units).
  */
 pkv_status pkv_paged_decode_attn(float* out, const void* q,
                                  const void* k_cache, const void* v_cache,
@@ -170,6 +173,26 @@ pkv_status pkv_paged_decode_attn(float* out, const void* q,
                                  pkv_dtype q_dtype, pkv_dtype cache_dtype,
                                  int32_t partition_size,
                                  void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Copy whole blocks inside both pools: for each k < n, block dst[k] becomes a
+ * copy of block src[k] (every kv head, K and V). This is the device half of
+ * copy-on-write: pkv_seq_append reports the (src, dst) pair when a sequence
+ * writes into a shared, partly filled last block, and the caller copies it
+ * before writing the new token ("03 · PagedAttention", "Sharing:
+ * copy-on-write"; "PagedAttention" daily term, copy-on-write figure).
+ *
+ * k_cache, v_cache: the pools (layout above) in cache_dtype (any of the three).
+ * src, dst:      int32 [n] device arrays of block ids. A pair with an id
+ *                outside [0, P) is skipped (checked on the device). Within one
+ *                call the copies run concurrently: the dst ids must be distinct
+ *                and no dst may also be a src of the same call.
+ * Requires 0 <= n <= min(P, 2^20) (n == 0 launches nothing), Hkv > 0,
+ * d in {64, 128}, bs in {8, 16, 32}, P > 0.
+ */
+pkv_status pkv_copy_blocks(void* k_cache, void* v_cache, const int32_t* src, const int32_t* dst,
+                           int32_t n, int32_t P, int32_t Hkv, int32_t d, int32_t bs,
+                           pkv_dtype cache_dtype, void* stream);
 
 /* ------------------------------------------------------------------------ */
 /* Host block allocator and builders (CPU only)                              */

@@ -32,7 +32,7 @@ invariants the pages state, a library routine on tiny inputs, brute force.
 from .codecs import (bf16_bits_to_f64, f32_to_f64, e4m3_value_table, e4m3_decode,
                      e4m3_encode)
 from .attention import reassemble, paged_decode_attn, contiguous_decode_attn
-from .cache_write import kv_cache_write, quantise
+from .cache_write import kv_cache_write, quantise, copy_blocks
 from .slots import decode_slots, slots_for_positions
 from .waste import (blocks_for, paged_slots, naive_slots, tail_slots, utilisation,
                     waste_fraction, capacity)
@@ -42,6 +42,7 @@ from .splitk import partition_then_merge
 __all__ = [
     "bf16_bits_to_f64", "f32_to_f64", "e4m3_value_table", "e4m3_decode", "e4m3_encode",
     "reassemble", "paged_decode_attn", "contiguous_decode_attn", "kv_cache_write", "quantise",
+    "copy_blocks",
     "decode_slots", "slots_for_positions", "blocks_for", "paged_slots",
     "naive_slots", "tail_slots", "utilisation", "waste_fraction", "capacity",
     "TwinAllocator", "NoBlocks", "partition_then_merge",

@@ -12,6 +12,12 @@ and channel c
     V[b][h][c][o] = enc(V_new[t][h][c])        (v_cache is [P][Hkv][d][bs])
 Every other element of the pools is left as it was.
 
+Copy-on-write ("03 · PagedAttention", "Sharing: copy-on-write"; the daily
+term's copy-on-write figure): before a sequence writes into a shared, partly
+filled block, the block is duplicated for it. ``copy_blocks`` is that
+duplication: for each (src, dst) pair, every element of block dst (all kv
+heads, K and V) takes the value of block src.
+
 enc is the identity on the stored bits when source and cache dtypes agree
 (f32 -> f32, bf16 -> bf16). For an fp8 cache the source (bf16) value x becomes
 e4m3_encode(float32(x) * float32(inv_scale)): one float32 multiplication rounded
@@ -60,4 +66,25 @@ def kv_cache_write(k_new, v_new, k_cache, v_cache, slot_mapping, *, bs, src_dtyp
             raise ValueError("slot outside the pool")
         k_out[b, :, o, :] = kq[t]
         v_out[b, :, :, o] = vq[t]
+    return k_out, v_out
+
+
+def copy_blocks(k_cache, v_cache, pairs):
+    """Return (k_cache', v_cache'): copies of the pools in which block dst of
+    each (src, dst) pair holds block src's contents. Pairs are applied in
+    order; a dst that is also a src of the same call is rejected (the copies of
+    one call are independent of each other)."""
+    k_out = np.array(k_cache, copy=True)
+    v_out = np.array(v_cache, copy=True)
+    P = k_cache.shape[0]
+    srcs = {int(a) for a, _ in pairs}
+    dsts = [int(b) for _, b in pairs]
+    if len(set(dsts)) != len(dsts) or srcs & set(dsts):
+        raise ValueError("dst blocks must be distinct and not among the sources")
+    for a, b in pairs:
+        a, b = int(a), int(b)
+        if not (0 <= a < P and 0 <= b < P):
+            continue                      # outside the pool: skipped
+        k_out[b] = k_cache[a]
+        v_out[b] = v_cache[a]
     return k_out, v_out

@@ -15,7 +15,7 @@ from ._lib import (lib, check, PkvError, PkvStats, PKV_F32, PKV_BF16, PKV_FP8_E4
                    PKV_E_NO_BLOCKS, P_i32, P_i64, P_f64, c_vp, c_i64, c_i32, c_f64)
 
 __all__ = [
-    "kv_cache_write", "paged_decode_attn", "paged_decode_attn_workspace_size",
+    "kv_cache_write", "copy_blocks", "paged_decode_attn", "paged_decode_attn_workspace_size",
     "paged_decode_attn_workspace", "Allocator",
     "slots_from_tables", "waste_stats", "last_error", "version", "quantise_pool",
     "PkvError", "NoBlocks", "PKV_PARTITION_BALANCED",
@@ -77,6 +77,24 @@ def kv_cache_write(k_new, v_new, k_cache, v_cache, slot_mapping, *, k_inv_scale=
         _dev(v_cache, "v_cache"), _dev(slot_mapping, "slot_mapping"), T, Hkv, d, bs, P,
         _dtype_code(k_new), _dtype_code(k_cache), float(k_inv_scale), float(v_inv_scale),
         _stream(stream)))
+
+
+def copy_blocks(k_cache, v_cache, src, dst, *, stream=None):
+    """pkv_copy_blocks: block dst[k] of both pools becomes a copy of block
+    src[k]. src, dst: int32 device tensors [n]; the dst ids must be distinct
+    and none of them a src of the same call."""
+    import torch
+    P, Hkv, bs, d = k_cache.shape
+    if tuple(v_cache.shape) != (P, Hkv, d, bs) or v_cache.dtype != k_cache.dtype:
+        raise ValueError("copy_blocks: pools disagree")
+    if src.dtype != torch.int32 or dst.dtype != torch.int32 or src.shape != dst.shape or src.dim() != 1:
+        raise ValueError("copy_blocks: src and dst must be int32 [n]")
+    n = src.shape[0]
+    if n == 0:
+        return
+    check(lib().pkv_copy_blocks(_dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dev(src, "src"),
+                                _dev(dst, "dst"), n, P, Hkv, d, bs, _dtype_code(k_cache),
+                                _stream(stream)))
 
 
 def paged_decode_attn_workspace_size(S, Hq, Hkv, d, max_context_len, partition_size):

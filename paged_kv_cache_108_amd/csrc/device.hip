@@ -128,6 +128,26 @@ __device__ __forceinline__ float bf16_lo_as_f32(uint32_t w) { return __uint_as_f
 __device__ __forceinline__ float bf16_hi_as_f32(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
 // ----------------------------------------------------------------------------
+// Block copy (copy-on-write)
+// ----------------------------------------------------------------------------
+
+// blockIdx.x = pair, blockIdx.y = pool (0: K, 1: V); a block of one pool is
+// one contiguous run of `bytes` (a multiple of 16) bytes.
+__global__ void __launch_bounds__(256)
+copy_blocks_kernel(char* __restrict__ k_cache, char* __restrict__ v_cache,
+                   const int32_t* __restrict__ src, const int32_t* __restrict__ dst,
+                   int P, size_t bytes) {
+    const int s = src[blockIdx.x];
+    const int d = dst[blockIdx.x];
+    if (s < 0 || s >= P || d < 0 || d >= P) return;
+    char* pool = blockIdx.y == 0 ? k_cache : v_cache;
+    const uint4* from = reinterpret_cast<const uint4*>(pool + (size_t)s * bytes);
+    uint4* to = reinterpret_cast<uint4*>(pool + (size_t)d * bytes);
+    const size_t n = bytes / 16;
+    for (size_t e = threadIdx.x; e < n; e += blockDim.x) to[e] = from[e];
+}
+
+// ----------------------------------------------------------------------------
 // KV-cache write
 // ----------------------------------------------------------------------------
 
@@ -1200,6 +1220,31 @@ extern "C" pkv_status pkv_kv_cache_write(const void* k_new, const void* v_new, v
                            v_inv_scale);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(PKV_E_HIP, "kv_cache_write: launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+extern "C" pkv_status pkv_copy_blocks(void* k_cache, void* v_cache, const int32_t* src,
+                                      const int32_t* dst, int32_t n, int32_t P, int32_t Hkv,
+                                      int32_t d, int32_t bs, pkv_dtype cache_dtype, void* stream) {
+    if (n < 0) return fail(PKV_E_INVALID, "copy_blocks: n=%d < 0", n);
+    if (Hkv <= 0 || P <= 0) return fail(PKV_E_INVALID, "copy_blocks: Hkv=%d P=%d must be positive", Hkv, P);
+    if (!pkv::is_head_dim(d)) return fail(PKV_E_INVALID, "copy_blocks: d=%d not in {64,128}", d);
+    if (!pkv::is_pow2_block(bs)) return fail(PKV_E_INVALID, "copy_blocks: bs=%d not in {8,16,32}", bs);
+    size_t elem;
+    if (cache_dtype == PKV_F32) elem = 4;
+    else if (cache_dtype == PKV_BF16) elem = 2;
+    else if (cache_dtype == PKV_FP8_E4M3) elem = 1;
+    else return fail(PKV_E_INVALID, "copy_blocks: unsupported cache dtype %d", cache_dtype);
+    if (n == 0) return ok();
+    if (!k_cache || !v_cache || !src || !dst) return fail(PKV_E_INVALID, "copy_blocks: NULL pointer");
+    if (n > P || n > (1 << 20))
+        return fail(PKV_E_INVALID, "copy_blocks: n=%d above min(P=%d, 2^20)", n, P);
+    const size_t bytes = (size_t)Hkv * bs * d * elem;
+    hipLaunchKernelGGL(copy_blocks_kernel, dim3((unsigned)n, 2), dim3(256), 0,
+                       static_cast<hipStream_t>(stream), static_cast<char*>(k_cache),
+                       static_cast<char*>(v_cache), src, dst, P, bytes);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(PKV_E_HIP, "copy_blocks: launch failed: %s", hipGetErrorString(e));
     return ok();
 }
 

@@ -246,3 +246,23 @@ def test_write_rejects_invalid_arguments(kw):
 
 def test_write_zero_tokens_is_a_noop():
     assert _write(T=0, kn=None, vn=None, kc=None, vc=None, sm=None) == _lib.PKV_OK
+
+
+def _copy(**kw):
+    a = dict(kc=FAKE, vc=FAKE, src=FAKE, dst=FAKE, n=3, P=10, Hkv=2, d=64, bs=16, cd=1)
+    a.update(kw)
+    return pkv.lib().pkv_copy_blocks(a["kc"], a["vc"], a["src"], a["dst"], a["n"], a["P"], a["Hkv"],
+                                     a["d"], a["bs"], a["cd"], None)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(n=-1), dict(n=11), dict(P=0), dict(Hkv=0), dict(d=96), dict(bs=4), dict(cd=7),
+    dict(kc=None), dict(dst=None),
+])
+def test_copy_blocks_rejects_invalid_arguments(kw):
+    assert _copy(**kw) == _lib.PKV_E_INVALID
+    assert "copy_blocks" in pkv.last_error()
+
+
+def test_copy_blocks_zero_pairs_is_a_noop():
+    assert _copy(n=0, kc=None, vc=None, src=None, dst=None) == _lib.PKV_OK

@@ -254,3 +254,96 @@ def test_deterministic_reruns():
         for _ in range(3):
             assert np.array_equal(to_host(dev.attend(part)), a)
 
+
+
+# ------------------------------------------------------------------ copy-on-write block copy
+@pytest.mark.parametrize("dt", ["f32", "bf16", "fp8"])
+def test_copy_blocks_matches_oracle(dt):
+    torch = need_gpu()
+    print(f"[case] copy_blocks {dt}", flush=True)
+    rng = np.random.default_rng(31)
+    P, Hkv, bs, d = 64, 4, 16, 128
+    if dt == "fp8":
+        kc = rng.integers(0, 256, (P, Hkv, bs, d), dtype=np.uint8)
+        vc = rng.integers(0, 256, (P, Hkv, d, bs), dtype=np.uint8)
+    elif dt == "bf16":
+        kc = rng.integers(0, 1 << 16, (P, Hkv, bs, d), dtype=np.uint16)
+        vc = rng.integers(0, 1 << 16, (P, Hkv, d, bs), dtype=np.uint16)
+    else:
+        kc = rng.standard_normal((P, Hkv, bs, d)).astype(np.float32)
+        vc = rng.standard_normal((P, Hkv, d, bs)).astype(np.float32)
+    perm = rng.permutation(P)
+    pairs = [(int(perm[k]), int(perm[20 + k])) for k in range(12)]
+    pairs += [(int(perm[40]), P + 5), (-2, int(perm[41]))]         # skipped: outside the pool
+    src = to_dev(np.array([a for a, _ in pairs], dtype=np.int32))
+    dst = to_dev(np.array([b for _, b in pairs], dtype=np.int32))
+    gk, gv = to_dev(kc), to_dev(vc)
+    pkv.copy_blocks(gk, gv, src, dst)
+    torch.cuda.synchronize()
+    ok_, ov = oracle.copy_blocks(kc, vc, pairs)
+    assert same_bits(to_host(gk), ok_) and same_bits(to_host(gv), ov)
+
+
+def test_beam_fork_on_partial_block_copy_on_write():
+    # 8 groups x 4 beams fork from a 1000-token prompt (not a multiple of 16):
+    # each beam's first own token lands in the shared, partly filled last block,
+    # so the library allocator reports copy pairs; the device copies them, then
+    # writes the beams' tokens, then attends. Pools must equal the oracle's
+    # (twin allocator + oracle copy + oracle write) byte for byte, outputs within
+    # the bf16 tolerance of the oracle's attention.
+    torch = need_gpu()
+    print("[case] beam fork on a partial block", flush=True)
+    rng = np.random.default_rng(77)
+    bs, Hkv, Hq, d, L0, groups = 16, 8, 32, 128, 1000, 8
+    P = groups * (L0 // bs + 1) + groups * 4 + 8
+    a, t = pkv.Allocator(P, bs), oracle.TwinAllocator(P, bs)
+
+    def bf16(x):
+        return (np.asarray(x, np.float32).view(np.uint32) + 0x7FFF + ((np.asarray(x, np.float32).view(np.uint32) >> 16) & 1) >> 16).astype(np.uint16)
+
+    kc = np.full((P, Hkv, bs, d), 0x7FC0, np.uint16)          # NaN poison
+    vc = np.full((P, Hkv, d, bs), 0x7FC0, np.uint16)
+    pk = bf16(rng.standard_normal((groups, L0, Hkv, d)))
+    pv = bf16(rng.standard_normal((groups, L0, Hkv, d)))
+    all_slots, kk, vv = [], [], []
+    for gi in range(groups):
+        a.create(4 * gi); t.create(4 * gi)
+        s1, _ = a.append(4 * gi, L0)
+        s2, _ = t.append(4 * gi, L0)
+        assert list(s1) == list(s2)
+        all_slots += list(s1); kk.append(pk[gi]); vv.append(pv[gi])
+    kc, vc = oracle.kv_cache_write(np.concatenate(kk), np.concatenate(vv), kc, vc,
+                                   np.array(all_slots), bs=bs, src_dtype="bf16", cache_dtype="bf16")
+    gk, gv = to_dev(kc), to_dev(vc)
+    for gi in range(groups):
+        for b in (1, 2, 3):
+            a.fork(4 * gi, 4 * gi + b); t.fork(4 * gi, 4 * gi + b)
+    pairs, new_slots = [], []
+    for sid in range(4 * groups):
+        s1, c1 = a.append(sid, 1)
+        s2, c2 = t.append(sid, 1)
+        assert list(s1) == list(s2) and c1 == c2
+        pairs += c1
+        new_slots += list(s1)
+    assert len(pairs) == 3 * groups
+    nk = bf16(rng.standard_normal((4 * groups, Hkv, d)))
+    nv = bf16(rng.standard_normal((4 * groups, Hkv, d)))
+    pkv.copy_blocks(gk, gv, to_dev(np.array([p_[0] for p_ in pairs], np.int32)),
+                    to_dev(np.array([p_[1] for p_ in pairs], np.int32)))
+    pkv.kv_cache_write(to_dev(nk), to_dev(nv), gk, gv, to_dev(np.array(new_slots, np.int64)))
+    okc, ovc = oracle.copy_blocks(kc, vc, pairs)
+    okc, ovc = oracle.kv_cache_write(nk, nv, okc, ovc, np.array(new_slots), bs=bs, src_dtype="bf16",
+                                     cache_dtype="bf16")
+    assert same_bits(to_host(gk), okc) and same_bits(to_host(gv), ovc)
+    ids = list(range(4 * groups))
+    maxb = L0 // bs + 2
+    tab, lens = a.tables(ids, maxb)
+    q = bf16(rng.standard_normal((4 * groups, Hq, d)))
+    ref = oracle.paged_decode_attn(q, okc, ovc, tab, lens, bs=bs, softmax_scale=float(np.float32(d ** -0.5)),
+                                   q_dtype="bf16", cache_dtype="bf16")
+    for part in (BAL, 512):
+        out = torch.empty((4 * groups, Hq, d), dtype=torch.float32, device="cuda")
+        pkv.paged_decode_attn(out, to_dev(q), gk, gv, to_dev(tab), to_dev(lens), max_context_len=int(lens.max()),
+                              softmax_scale=float(np.float32(d ** -0.5)), partition_size=part)
+        torch.cuda.synchronize()
+        assert_rows_close(to_host(out), ref, TOL["bf16"], f"beam CoW part={part}")

@@ -164,6 +164,51 @@ def test_fork_and_copy_on_write():
     assert cow == [] and b.seqs[1][0] == [0, 1, 2]
 
 
+def test_copy_on_write_keeps_every_sequence_equal_to_its_own_tokens():
+    # Beams forked from a prefix that ends inside a block, then each appends
+    # its own token through the allocator: after copying each reported pair and
+    # writing the new tokens, every beam's reassembled K/V must be exactly the
+    # prefix followed by its own token, and the parent's prefix is untouched
+    # (the copy-on-write rule of "Sharing: copy-on-write"). Built against
+    # sequences assembled directly from the token values, not from the pool.
+    from oracle import copy_blocks, kv_cache_write, reassemble
+    rng = np.random.default_rng(5)
+    bs, Hkv, d, P, L0 = 16, 2, 64, 40, 100          # 100 = 6 blocks + 4 tokens
+    prefix_k = rng.standard_normal((L0, Hkv, d)).astype(np.float32)
+    prefix_v = rng.standard_normal((L0, Hkv, d)).astype(np.float32)
+    own_k = rng.standard_normal((4, Hkv, d)).astype(np.float32)
+    own_v = rng.standard_normal((4, Hkv, d)).astype(np.float32)
+    kc = np.full((P, Hkv, bs, d), np.nan, np.float32)
+    vc = np.full((P, Hkv, d, bs), np.nan, np.float32)
+    a = TwinAllocator(P, bs)
+    a.create(0)
+    slots, _ = a.append(0, L0)
+    kc, vc = kv_cache_write(prefix_k, prefix_v, kc, vc, np.array(slots), bs=bs, src_dtype="f32",
+                            cache_dtype="f32")
+    for b in (1, 2, 3):
+        a.fork(0, b)
+    pairs, new_slots = [], []
+    for b in range(4):
+        s_, cow = a.append(b, 1)
+        pairs += cow
+        new_slots += s_
+    assert len(pairs) == 3                          # the last writer owns the block by then
+    kc, vc = copy_blocks(kc, vc, pairs)
+    kc, vc = kv_cache_write(own_k, own_v, kc, vc, np.array(new_slots), bs=bs, src_dtype="f32",
+                            cache_dtype="f32")
+    tabs, lens = a.tables([0, 1, 2, 3], 8)
+    for b in range(4):
+        got_k = reassemble(kc, tabs[b], lens[b], bs, "k")
+        got_v = reassemble(vc, tabs[b], lens[b], bs, "v")
+        assert np.array_equal(got_k, np.concatenate([prefix_k, own_k[b:b + 1]]))
+        assert np.array_equal(got_v, np.concatenate([prefix_v, own_v[b:b + 1]]))
+    # a copy pair with a block outside the pool is skipped; overlapping pairs are refused
+    k2, v2 = copy_blocks(kc, vc, [(0, P + 3)])
+    assert np.array_equal(k2, kc, equal_nan=True) and np.array_equal(v2, vc, equal_nan=True)
+    with pytest.raises(ValueError):
+        copy_blocks(kc, vc, [(1, 2), (2, 3)])
+
+
 def test_exhaustion_is_all_or_nothing():
     a = TwinAllocator(3, 16)
     a.create(0)
