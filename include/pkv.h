@@ -90,7 +90,7 @@ const char* pkv_version(void);
  * k_new, v_new: [T][Hkv][d] in src_dtype. slot_mapping: int64 [T].
  * Two tokens with the same slot race (the result is one of them).
  * T == 0 is a no-op. Requires T >= 0, Hkv > 0, d in {64, 128},
- * bs in {8, 16, 32}, P > 0.
+ * bs in {8, 16, 32, 64, 128}, P > 0.
  */
 pkv_status pkv_kv_cache_write(const void* k_new, const void* v_new,
                               void* k_cache, void* v_cache,
@@ -141,7 +141,7 @@ size_t pkv_paged_decode_attn_workspace_size(int32_t S, int32_t Hq, int32_t Hkv, 
  *                such a sequence is then unspecified.
  * Supported (q_dtype, cache_dtype): (F32, F32), (BF16, BF16), (BF16, FP8_E4M3).
  * Requires S > 0, Hkv > 0, Hq % Hkv == 0, 1 <= Hq/Hkv <= 16, d in {64, 128},
- * bs in {8, 16, 32}, P > 0, max_blocks > 0, 0 <= max_context_len <=
+ * bs in {8, 16, 32, 64, 128}, P > 0, max_blocks > 0, 0 <= max_context_len <=
  * max_blocks * bs, softmax_scale finite; for FP8 finite k_scale, v_scale.
  *
  * partition_size selects how sequences are split across workgroups (split-K);
@@ -188,7 +188,7 @@ pkv_status pkv_paged_decode_attn(float* out, const void* q,
  *                call the copies run concurrently: the dst ids must be distinct
  *                and no dst may also be a src of the same call.
  * Requires 0 <= n <= min(P, 2^20) (n == 0 launches nothing), Hkv > 0,
- * d in {64, 128}, bs in {8, 16, 32}, P > 0.
+ * d in {64, 128}, bs in {8, 16, 32, 64, 128}, P > 0.
  */
 pkv_status pkv_copy_blocks(void* k_cache, void* v_cache, const int32_t* src, const int32_t* dst,
                            int32_t n, int32_t P, int32_t Hkv, int32_t d, int32_t bs,

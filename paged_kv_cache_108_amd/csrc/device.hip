@@ -1110,6 +1110,8 @@ AttnKernel pick_bs(int bs) {
         case 8: return paged_attn_partition_kernel<KV, D, 8>;
         case 16: return paged_attn_partition_kernel<KV, D, 16>;
         case 32: return paged_attn_partition_kernel<KV, D, 32>;
+        case 64: return paged_attn_partition_kernel<KV, D, 64>;
+        case 128: return paged_attn_partition_kernel<KV, D, 128>;
     }
     return nullptr;
 }
@@ -1125,6 +1127,8 @@ AttnKernel pick_stream_bs(int bs) {
         case 8: return paged_attn_stream_kernel<KV, D, 8>;
         case 16: return paged_attn_stream_kernel<KV, D, 16>;
         case 32: return paged_attn_stream_kernel<KV, D, 32>;
+        case 64: return paged_attn_stream_kernel<KV, D, 64>;
+        case 128: return paged_attn_stream_kernel<KV, D, 128>;
     }
     return nullptr;
 }
@@ -1195,7 +1199,7 @@ extern "C" pkv_status pkv_kv_cache_write(const void* k_new, const void* v_new, v
     if (T < 0) return fail(PKV_E_INVALID, "kv_cache_write: T=%d < 0", T);
     if (Hkv <= 0 || P <= 0) return fail(PKV_E_INVALID, "kv_cache_write: Hkv=%d P=%d must be positive", Hkv, P);
     if (!pkv::is_head_dim(d)) return fail(PKV_E_INVALID, "kv_cache_write: d=%d not in {64,128}", d);
-    if (!pkv::is_pow2_block(bs)) return fail(PKV_E_INVALID, "kv_cache_write: bs=%d not in {8,16,32}", bs);
+    if (!pkv::is_pow2_block(bs)) return fail(PKV_E_INVALID, "kv_cache_write: bs=%d not in {8,16,32,64,128}", bs);
     const bool same = src_dtype == cache_dtype && (src_dtype == PKV_F32 || src_dtype == PKV_BF16);
     const bool quant = cache_dtype == PKV_FP8_E4M3 && src_dtype == PKV_BF16;
     if (!same && !quant)
@@ -1229,7 +1233,7 @@ extern "C" pkv_status pkv_copy_blocks(void* k_cache, void* v_cache, const int32_
     if (n < 0) return fail(PKV_E_INVALID, "copy_blocks: n=%d < 0", n);
     if (Hkv <= 0 || P <= 0) return fail(PKV_E_INVALID, "copy_blocks: Hkv=%d P=%d must be positive", Hkv, P);
     if (!pkv::is_head_dim(d)) return fail(PKV_E_INVALID, "copy_blocks: d=%d not in {64,128}", d);
-    if (!pkv::is_pow2_block(bs)) return fail(PKV_E_INVALID, "copy_blocks: bs=%d not in {8,16,32}", bs);
+    if (!pkv::is_pow2_block(bs)) return fail(PKV_E_INVALID, "copy_blocks: bs=%d not in {8,16,32,64,128}", bs);
     size_t elem;
     if (cache_dtype == PKV_F32) elem = 4;
     else if (cache_dtype == PKV_BF16) elem = 2;
@@ -1274,7 +1278,7 @@ extern "C" pkv_status pkv_paged_decode_attn(float* out, const void* q, const voi
     const int32_t G = Hq / Hkv;
     if (G > 16) return fail(PKV_E_INVALID, "paged_decode_attn: Hq/Hkv=%d > 16", G);
     if (!pkv::is_head_dim(d)) return fail(PKV_E_INVALID, "paged_decode_attn: d=%d not in {64,128}", d);
-    if (!pkv::is_pow2_block(bs)) return fail(PKV_E_INVALID, "paged_decode_attn: bs=%d not in {8,16,32}", bs);
+    if (!pkv::is_pow2_block(bs)) return fail(PKV_E_INVALID, "paged_decode_attn: bs=%d not in {8,16,32,64,128}", bs);
     if (P <= 0 || max_blocks <= 0) return fail(PKV_E_INVALID, "paged_decode_attn: P=%d max_blocks=%d", P, max_blocks);
     if (max_context_len < 0 || (int64_t)max_context_len > (int64_t)max_blocks * bs)
         return fail(PKV_E_INVALID, "paged_decode_attn: max_context_len=%d outside [0, max_blocks*bs=%lld]",

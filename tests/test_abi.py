@@ -202,7 +202,7 @@ def _attn(**kw):
 
 
 @pytest.mark.parametrize("kw", [
-    dict(Hq=7), dict(Hq=34, Hkv=2), dict(d=96), dict(bs=4), dict(bs=64), dict(P=0),
+    dict(Hq=7), dict(Hq=34, Hkv=2), dict(d=96), dict(bs=4), dict(bs=48), dict(bs=256), dict(P=0),
     dict(maxb=0), dict(maxlen=161), dict(maxlen=-1), dict(qd=0), dict(qd=1, cd=0),
     dict(qd=2, cd=2), dict(part=16), dict(part=-32), dict(part=-2), dict(scale=float("inf")),
     dict(qd=1, cd=2, ks=float("nan")), dict(out=None), dict(tab=None), dict(S=-1), dict(Hkv=0),

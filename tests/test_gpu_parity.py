@@ -57,6 +57,11 @@ def test_llama8b():
     _full_case(W.make("llama8b"), [512, 0, 256, BAL])
 
 
+@pytest.mark.parametrize("bs", [64, 128])
+def test_llama8b_large_blocks(bs):
+    _full_case(W.make("llama8b", bs=bs), [BAL, 512])
+
+
 @pytest.mark.parametrize("bs", [8, 16, 32])
 def test_beam_block_sizes(bs):
     _full_case(W.make("beam", bs=bs), [0, 512, BAL])
@@ -113,6 +118,9 @@ EDGE = [
     ([1, 513, 1024, 1025, 2049], 8, 8, 64, 16, "f32"),
     ([3, 40, 600], 12, 2, 64, 8, "f32"),
     ([1, 77, 520], 16, 16, 128, 32, "f32"),
+    ([1, 63, 64, 65, 300, 1000], 8, 2, 128, 64, "bf16"),
+    ([5, 127, 128, 129, 700], 4, 4, 64, 128, "f32"),
+    ([2, 130, 1500], 14, 2, 64, 128, "bf16"),
 ]
 
 
