@@ -175,6 +175,49 @@ pkv_status pkv_paged_decode_attn(float* out, const void* q,
                                  void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Bytes of workspace pkv_paged_multi_query_attn needs: R + 2 * S * Hkv * n_qg * 4
+ * with G = Hq/Hkv, qgs = min(n_q, max(1, 16 / G)) queries per pass,
+ * n_qg = ceil(n_q / qgs) passes and R = 2 * 4096 * G * qgs * (d + 2) * 4 rounded
+ * up to a multiple of 256. Returns 0 for invalid sizes.
+ */
+size_t pkv_paged_multi_query_attn_workspace_size(int32_t S, int32_t n_q, int32_t Hq, int32_t Hkv,
+                                                 int32_t d);
+
+/*
+ * Paged attention for a window of n_q consecutive new queries per sequence,
+ * causal inside the window: the chunks of chunked prefill and the candidate
+ * windows of speculative decoding, which reuse the decode gather ("Serving:
+ * vLLM and PagedAttention", sections 2.4 and 2.7). Query j (0-based) of
+ * sequence i sits at position L_i - n_q + j and attends to the cached tokens at
+ * positions 0 .. L_i - n_q + j (the window's own K/V are written beforehand,
+ * e.g. by pkv_kv_cache_write with one slot per query token):
+ *
+ *   out[i][j][h][c] = v_scale * sum_{t <= L_i - n_q + j} exp(s_t - max s) V_i[t][g][c]
+ *                              / sum_{t <= L_i - n_q + j} exp(s_t - max s)
+ *
+ * with s_t, g and the pools as in pkv_paged_decode_attn. n_q = 1 is exactly
+ * decode attention.
+ *
+ * out: float32 [S][n_q][Hq][d]; q: [S][n_q][Hq][d] in q_dtype; the other
+ * arguments as for pkv_paged_decode_attn, which this shares its kernels with:
+ * the balanced split is always used, and workspace must hold
+ * pkv_paged_multi_query_attn_workspace_size(S, n_q, Hq, Hkv, d) bytes.
+ * Requires 1 <= n_q <= 4096 and, per sequence, L_i >= n_q or L_i <= 0 (zero
+ * rows); rows of a query that sees no token are otherwise unspecified.
+ * The G query heads of a kv head and up to 16/G queries of the window share
+ * each pass over the sequence's blocks (one 16-column MFMA tile); a longer
+ * window takes ceil(n_q / qgs) passes.
+ */
+pkv_status pkv_paged_multi_query_attn(float* out, const void* q,
+                                      const void* k_cache, const void* v_cache,
+                                      const int32_t* block_tables, const int32_t* context_lens,
+                                      int32_t S, int32_t n_q, int32_t Hq, int32_t Hkv, int32_t d,
+                                      int32_t bs, int32_t P, int32_t max_blocks,
+                                      int32_t max_context_len, float softmax_scale, float k_scale,
+                                      float v_scale, pkv_dtype q_dtype, pkv_dtype cache_dtype,
+                                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Copy whole blocks inside both pools: for each k < n, block dst[k] becomes a
  * copy of block src[k] (every kv head, K and V). This is the device half of
  * copy-on-write: pkv_seq_append reports the (src, dst) pair when a sequence

@@ -17,7 +17,8 @@ Every function is written from the pages' statement of what is computed:
 * "paged-attention" lesson (tbash.cc): the five-request worked example and the
   statement that the output is identical whatever the layout.
 * "Serving: vLLM and PagedAttention" (henryfzh-note.com): section 2.2 (block
-  table, last-block fill, tail-waste arithmetic).
+  table, last-block fill, tail-waste arithmetic); sections 2.4 and 2.7 (windows
+  of several new queries over the same cache: ``paged_multi_query_attn``).
 
 The attention itself is the textbook definition applied to the sequence's
 K/V reassembled in logical order: the pages state that paging changes only the
@@ -31,7 +32,7 @@ invariants the pages state, a library routine on tiny inputs, brute force.
 
 from .codecs import (bf16_bits_to_f64, f32_to_f64, e4m3_value_table, e4m3_decode,
                      e4m3_encode)
-from .attention import reassemble, paged_decode_attn, contiguous_decode_attn
+from .attention import reassemble, paged_decode_attn, contiguous_decode_attn, paged_multi_query_attn
 from .cache_write import kv_cache_write, quantise, copy_blocks
 from .slots import decode_slots, slots_for_positions
 from .waste import (blocks_for, paged_slots, naive_slots, tail_slots, utilisation,
@@ -41,7 +42,8 @@ from .splitk import partition_then_merge
 
 __all__ = [
     "bf16_bits_to_f64", "f32_to_f64", "e4m3_value_table", "e4m3_decode", "e4m3_encode",
-    "reassemble", "paged_decode_attn", "contiguous_decode_attn", "kv_cache_write", "quantise",
+    "reassemble", "paged_decode_attn", "contiguous_decode_attn", "paged_multi_query_attn",
+    "kv_cache_write", "quantise",
     "copy_blocks",
     "decode_slots", "slots_for_positions", "blocks_for", "paged_slots",
     "naive_slots", "tail_slots", "utilisation", "waste_fraction", "capacity",

@@ -112,3 +112,27 @@ def paged_decode_attn(q, k_cache, v_cache, block_tables, context_lens, *, bs,
         qi = widen(q[i], q_dtype)
         out[r] = contiguous_decode_attn(qi, K, V, sigma)
     return out
+
+
+def paged_multi_query_attn(q, k_cache, v_cache, block_tables, context_lens, *, bs, softmax_scale,
+                           q_dtype, cache_dtype, k_scale=1.0, v_scale=1.0, seqs=None):
+    """Oracle output, float64 [S][n_q][Hq][d], for a window of n_q new queries
+    per sequence ("Serving: vLLM and PagedAttention", sections 2.4 and 2.7:
+    prefill chunks and verification windows reuse the decode gather).
+
+    Query j of sequence i sits at position L_i - n_q + j and is causal: it is the
+    single-query decode attention of ``paged_decode_attn`` over the first
+    L_i - n_q + j + 1 tokens of the same block table. Sequences with L_i <= 0
+    give zero rows.
+    """
+    S, n_q, Hq, d = q.shape
+    rows = list(range(S)) if seqs is None else list(seqs)
+    out = np.zeros((len(rows), n_q, Hq, d))
+    lens = np.asarray(context_lens, dtype=np.int64)
+    for j in range(n_q):
+        lens_j = np.where(lens > 0, lens - n_q + 1 + j, 0)
+        out[:, j] = paged_decode_attn(q[:, j], k_cache, v_cache, block_tables, lens_j, bs=bs,
+                                      softmax_scale=softmax_scale, q_dtype=q_dtype,
+                                      cache_dtype=cache_dtype, k_scale=k_scale, v_scale=v_scale,
+                                      seqs=rows)
+    return out

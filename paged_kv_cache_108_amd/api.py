@@ -16,7 +16,8 @@ from ._lib import (lib, check, PkvError, PkvStats, PKV_F32, PKV_BF16, PKV_FP8_E4
 
 __all__ = [
     "kv_cache_write", "copy_blocks", "paged_decode_attn", "paged_decode_attn_workspace_size",
-    "paged_decode_attn_workspace", "Allocator",
+    "paged_decode_attn_workspace", "paged_multi_query_attn", "paged_multi_query_attn_workspace",
+    "Allocator",
     "slots_from_tables", "waste_stats", "last_error", "version", "quantise_pool",
     "PkvError", "NoBlocks", "PKV_PARTITION_BALANCED",
 ]
@@ -142,6 +143,40 @@ def paged_decode_attn(out, q, k_cache, v_cache, block_tables, context_lens, *, m
         S, Hq, Hkv, d, bs, P, block_tables.shape[1], int(max_context_len),
         float(softmax_scale), float(k_scale), float(v_scale), _dtype_code(q),
         _dtype_code(k_cache), int(partition_size), ws_ptr, ws_bytes, _stream(stream)))
+
+
+def paged_multi_query_attn_workspace(S, n_q, Hq, Hkv, d, device="cuda"):
+    """A uint8 device tensor of the size pkv_paged_multi_query_attn needs."""
+    import torch
+    need = int(lib().pkv_paged_multi_query_attn_workspace_size(S, n_q, Hq, Hkv, d))
+    if need == 0:
+        raise ValueError("paged_multi_query_attn: invalid sizes")
+    return torch.empty(need, dtype=torch.uint8, device=device)
+
+
+def paged_multi_query_attn(out, q, k_cache, v_cache, block_tables, context_lens, *, max_context_len,
+                           softmax_scale, k_scale=1.0, v_scale=1.0, workspace=None, stream=None):
+    """pkv_paged_multi_query_attn. out float32 [S][n_q][Hq][d]; q [S][n_q][Hq][d]:
+    query j of sequence i sits at position L_i - n_q + j and sees the tokens up to
+    it (causal inside the window). workspace as from paged_multi_query_attn_workspace
+    (None allocates one for this call)."""
+    import torch
+    S, n_q, Hq, d = q.shape
+    P, Hkv, bs, _ = k_cache.shape
+    if tuple(out.shape) != (S, n_q, Hq, d) or out.dtype != torch.float32:
+        raise ValueError("paged_multi_query_attn: out must be float32 [S][n_q][Hq][d]")
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise ValueError("paged_multi_query_attn: tables and lengths must be int32")
+    if block_tables.shape[0] != S or context_lens.shape != (S,):
+        raise ValueError("paged_multi_query_attn: tables/lengths shape mismatch")
+    if workspace is None:
+        workspace = paged_multi_query_attn_workspace(S, n_q, Hq, Hkv, d, device=q.device)
+    check(lib().pkv_paged_multi_query_attn(
+        _dev(out, "out"), _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+        _dev(block_tables, "block_tables"), _dev(context_lens, "context_lens"),
+        S, n_q, Hq, Hkv, d, bs, P, block_tables.shape[1], int(max_context_len),
+        float(softmax_scale), float(k_scale), float(v_scale), _dtype_code(q), _dtype_code(k_cache),
+        _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
 def quantise_pool(values_k, values_v, codes_k, codes_v, *, k_inv_scale, v_inv_scale, stream=None):

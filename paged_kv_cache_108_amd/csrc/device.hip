@@ -210,6 +210,10 @@ struct AttnParams {
     int n_workers;         // grid size (balanced split)
     int n_rec;             // partial records in the workspace
     int* desc;             // balanced split: per segment (first record, record count)
+    int n_q;               // queries per sequence (1: decode)
+    int qgs;               // queries per query group (G * qgs <= 16 columns)
+    int n_qg;              // query groups per (sequence, kv head)
+    int cols;              // MFMA columns in use: G * qgs; partial records hold this many rows
     float qk_scale;        // softmax_scale * k_scale * log2(e): scores in the log2 domain
     float v_scale;
 };
@@ -402,6 +406,29 @@ __device__ __forceinline__ void load_q(const AttnParams& p, int i, int g, int r1
     using QF = typename QFragT<KV>::T;
     const bool live = r16 < p.G;
     const size_t qoff = ((size_t)i * p.Hq + g * p.G + (live ? r16 : 0)) * D;
+#pragma unroll
+    for (int x = 0; x < q_loads<KV, D>(); ++x) {
+        int c;
+        if constexpr (KV == KV_F32) c = 16 * x + 4 * j4;
+        else if constexpr (KV == KV_BF16) c = 32 * x + 8 * j4;
+        else c = 64 * (x >> 1) + 16 * j4 + 8 * (x & 1);
+        QF val;
+        if constexpr (KV == KV_F32)
+            val = *reinterpret_cast<const float4*>(static_cast<const float*>(p.q) + qoff + c);
+        else
+            val = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.q) + qoff + c);
+        if (!live) val = QF{};
+        qf[x] = val;
+    }
+}
+
+// The q fragment of one column from an explicit row offset (elements) of q;
+// zero when the column is not live.
+template <int KV, int D>
+__device__ __forceinline__ void load_q_row(const AttnParams& p, size_t row, bool live, int j4,
+                                           typename QFragT<KV>::T* qf) {
+    using QF = typename QFragT<KV>::T;
+    const size_t qoff = live ? row : 0;
 #pragma unroll
     for (int x = 0; x < q_loads<KV, D>(); ++x) {
         int c;
@@ -771,7 +798,7 @@ paged_attn_partition_kernel(AttnParams p) {
 // segment's first chunk writes the segment's descriptor (first record, record
 // count) for the merge kernel. Launched one workgroup per compute unit (one
 // wave per SIMD), so the kernel may use the whole register file.
-template <int KV, int D, int BS>
+template <int KV, int D, int BS, bool MQ>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1)))
 paged_attn_stream_kernel(AttnParams p) {
     extern __shared__ float smem[];           // the length cache (p.cache_lens)
@@ -783,6 +810,10 @@ paged_attn_stream_kernel(AttnParams p) {
     const int r16 = lane & 15;
     const int j4 = lane >> 4;
     const int G = p.G;
+    // segments per sequence: kv heads x query groups (one group when decoding)
+    const int n_qg = MQ ? p.n_qg : 1;
+    const int HS = p.Hkv * n_qg;
+    const int n_q = MQ ? p.n_q : 1;
     int* sL = p.cache_lens ? reinterpret_cast<int*>(smem) : nullptr;
     auto seq_len = [&](int s) { return sL ? sL[s] : min(p.lens[s], p.max_len); };
     auto n_chunks_of = [&](int L) { return L > 0 ? (L + 15) >> 4 : 0; };
@@ -792,9 +823,10 @@ paged_attn_stream_kernel(AttnParams p) {
     prefix_over_sequences(p, pre, wsum, sL, [&](int, int L) { return span_of(L); });
     for (int s = blockIdx.x; s < p.S; s += gridDim.x)       // sequences with no tokens: zero rows
         if (seq_len(s) <= 0)
-            for (int e = threadIdx.x; e < p.Hq * D; e += kThreads) p.out[(size_t)s * p.Hq * D + e] = 0.f;
+            for (int e = threadIdx.x; e < n_q * p.Hq * D; e += kThreads)
+                p.out[(size_t)s * n_q * p.Hq * D + e] = 0.f;
 
-    const unsigned V = (unsigned)pre[kThreads] * (unsigned)p.Hkv;   // positions in all
+    const unsigned V = (unsigned)pre[kThreads] * (unsigned)HS;   // positions in all
     const unsigned W = gridDim.x * kWaves;
     const unsigned w = blockIdx.x * kWaves + wave;
     const Split split(V, W);
@@ -802,14 +834,15 @@ paged_attn_stream_kernel(AttnParams p) {
     const unsigned v_end = split.start(w + 1);
     const int n_pos = (int)(v_end - v_beg);
     if (n_pos <= 0) return;                   // no barriers below: waves are independent
-    // position v -> segment (i * Hkv + g) and chunk index (< 0: a cost position)
+    // position v -> segment (i * HS + kv head * n_qg + query group) and chunk
+    // index (< 0: a cost position)
     auto locate = [&](unsigned v, int& seg, int& kc, int& L) {
         unsigned off;
-        const int i = find_sequence32(p, pre, v, (unsigned)p.Hkv, span, off);
+        const int i = find_sequence32(p, pre, v, (unsigned)HS, span, off);
         L = seq_len(i);
         const unsigned sp = (unsigned)span_of(L);
         const unsigned g = off / sp;
-        seg = i * p.Hkv + (int)g;
+        seg = i * HS + (int)g;
         kc = (int)(off - g * sp) - kSegCost;
     };
 
@@ -828,7 +861,7 @@ paged_attn_stream_kernel(AttnParams p) {
             int L;
             locate(in ? v_beg + kb + lane : v_end - 1, a_seg, a_kc, L);
             if (in && a_kc >= 0) {
-                const int i = a_seg / p.Hkv;
+                const int i = a_seg / HS;
                 const int32_t* __restrict__ row = p.tables + (size_t)i * p.max_blocks;
                 const int tok = 16 * a_kc;
                 if constexpr (BS == 8) {
@@ -899,7 +932,7 @@ paged_attn_stream_kernel(AttnParams p) {
             const int b1 = BS == 8 ? __builtin_amdgcn_readlane(id1, k) : b0;
             const int seg = __builtin_amdgcn_readlane(mseg, k);
             const int kc = __builtin_amdgcn_readlane(mkc, k);
-            const int g = seg % p.Hkv;
+            const int g = (seg % HS) / n_qg;
             load_chunk<KV, D, BS>(f, p, b0, b1, 16 * kc, g, r16, j4);
             __builtin_amdgcn_sched_barrier(0);
         };
@@ -907,14 +940,22 @@ paged_attn_stream_kernel(AttnParams p) {
             const int seg = __builtin_amdgcn_readlane(mseg, k);
             const int kc = __builtin_amdgcn_readlane(mkc, k);
             const unsigned v = v_beg + kb + __builtin_amdgcn_readlane(mvo, k);
-            const int i = seg / p.Hkv;
-            const int g = seg - i * p.Hkv;
+            const int i = seg / HS;
+            const int g2 = seg - i * HS;
+            const int g = g2 / n_qg;
+            const int qg = g2 - g * n_qg;
             const int L = __builtin_amdgcn_readfirstlane(seq_len(i));
             const int nch = n_chunks_of(L);
+            // this lane's column: query j of the window, head g*G + r
+            const int jj = MQ ? r16 / G : 0;
+            const int r = MQ ? r16 - jj * G : r16;
+            const int j = qg * (MQ ? p.qgs : 1) + jj;
+            const bool live = r16 < (MQ ? p.cols : G) && j < n_q;
+            const size_t out_row = (((size_t)i * n_q + j) * p.Hq + g * G + r) * D;
             const bool first = !started;
             started = true;
             if (kc == 0 || first) {               // a segment starts
-                load_q<KV, D>(p, i, g, r16, j4, qf);
+                load_q_row<KV, D>(p, out_row, live, j4, qf);
                 seg_from_start = kc == 0;
                 seg_at_range_start = first;
                 if (kc == 0 && lane == 0) {       // descriptor for the merge kernel
@@ -925,20 +966,26 @@ paged_attn_stream_kernel(AttnParams p) {
             }
             const int tc = 16 * kc;
             const f32x4 sc = chunk_scores<KV, D>(f, qf);
-            const bool tail = tc + 16 > L;
+            const bool tail = tc + 16 > L;        // tokens >= L hold no data
+            // query j sees tokens < L - n_q + 1 + j (causal inside the window)
+            const int lim = MQ ? L - n_q + 1 + j : L;
+            const bool masked = MQ ? tc + 16 > L - n_q + 1 : tail;
             const int first_tok = tc + 4 * j4;
             float x[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 x[e] = sc[e] * p.qk_scale;
-                if (tail && first_tok + e >= L) x[e] = -INFINITY;
+                if (masked && first_tok + e >= lim) x[e] = -INFINITY;
             }
             const float cm = head_max(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
-            const float m_new = fmaxf(m_run, cm);
-            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+            float m_new = fmaxf(m_run, cm);
+            // a column that has seen no visible token yet keeps m = -inf; its
+            // exponentials are taken against 0 so they stay 0, not NaN
+            const float m_ref = MQ && m_new == -INFINITY ? 0.f : m_new;
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_ref);
             float pr[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) pr[e] = __builtin_amdgcn_exp2f(x[e] - m_new);
+            for (int e = 0; e < 4; ++e) pr[e] = __builtin_amdgcn_exp2f(x[e] - m_ref);
             l_run = l_run * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
             m_run = m_new;
             if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
@@ -950,23 +997,24 @@ paged_attn_stream_kernel(AttnParams p) {
             if (kc == nch - 1 || v == v_last) {   // the segment ends here for this wave
                 const float l_tot = head_sum(l_run);
                 const bool whole = seg_from_start && kc == nch - 1;
-                if (r16 < G) {
+                const int C = MQ ? p.cols : G;
+                if (live) {
                     if (whole) {
                         const float sc_o = p.v_scale / l_tot;
-                        float* orow = p.out + ((size_t)i * p.Hq + g * G + r16) * D + 4 * j4;
+                        float* orow = p.out + out_row + 4 * j4;
 #pragma unroll
                         for (int s = 0; s < D / 16; ++s)
                             *reinterpret_cast<f32x4*>(orow + 16 * s) = o[s] * sc_o;
                     } else {
-                        const size_t rr = (size_t)(2 * w + (seg_at_range_start ? 0 : 1)) * G + r16;
+                        const size_t rr = (size_t)(2 * w + (seg_at_range_start ? 0 : 1)) * C + r16;
                         const size_t nrec = (size_t)p.n_rec;
                         float* orec = p.ws + rr * D + 4 * j4;
 #pragma unroll
                         for (int s = 0; s < D / 16; ++s)
                             *reinterpret_cast<f32x4*>(orec + 16 * s) = o[s] * p.v_scale;
                         if (j4 == 0) {
-                            p.ws[nrec * G * D + rr] = m_run;
-                            p.ws[nrec * G * (D + 1) + rr] = l_tot;
+                            p.ws[nrec * C * D + rr] = m_run;
+                            p.ws[nrec * C * (D + 1) + rr] = l_tot;
                         }
                     }
                 }
@@ -1007,18 +1055,22 @@ __global__ void __launch_bounds__(kThreads)
 paged_attn_merge_kernel(AttnParams p) {
     const bool balanced = p.balanced != 0;
     const int lane = threadIdx.x & 63;
-    const long long h = (long long)blockIdx.x * kWaves + (threadIdx.x >> 6);   // i * Hq + head
-    if (h >= (long long)p.S * p.Hq) return;
-    const int i = (int)(h / p.Hq);
-    const int head = (int)(h - (long long)i * p.Hq);
+    // output row h = (i * n_q + j) * Hq + head
+    const long long h = (long long)blockIdx.x * kWaves + (threadIdx.x >> 6);
+    if (h >= (long long)p.S * p.n_q * p.Hq) return;
+    const int i = (int)(h / ((long long)p.n_q * p.Hq));
+    const int jh = (int)(h - (long long)i * p.n_q * p.Hq);
+    const int j = jh / p.Hq;
+    const int head = jh - j * p.Hq;
     const int g = head / p.G;
-    const int r = head - g * p.G;
+    const int qg = j / p.qgs;
+    const int r = (j - qg * p.qgs) * p.G + (head - g * p.G);     // column of this row
     const int L = min(p.lens[i], p.max_len);
     if (L <= 0) return;
     int n, rec0;                              // records rec0 .. (see below), n of them
     long long w_lo = 0;
     if (balanced) {
-        const int seg = i * p.Hkv + g;
+        const int seg = (i * p.Hkv + g) * p.n_qg + qg;
         rec0 = p.desc[2 * seg];
         n = p.desc[2 * seg + 1];
         if (n <= 1) return;                   // one wave wrote the rows
@@ -1034,7 +1086,7 @@ paged_attn_merge_kernel(AttnParams p) {
         return (size_t)(rec0 + k);
     };
     const size_t nrec = (size_t)p.n_rec;
-    const int G = p.G;
+    const int G = p.cols;                     // record rows (columns)
     auto m_at = [&](int k) { return p.ws[nrec * G * D + rec_of(k) * G + r]; };
     auto l_at = [&](int k) { return p.ws[nrec * G * (D + 1) + rec_of(k) * G + r]; };
     constexpr int PER = D / 64;
@@ -1121,21 +1173,22 @@ AttnKernel pick_d(int d, int bs) {
     return d == 64 ? pick_bs<KV, 64>(bs) : pick_bs<KV, 128>(bs);
 }
 
-template <int KV, int D>
+template <int KV, int D, bool MQ>
 AttnKernel pick_stream_bs(int bs) {
     switch (bs) {
-        case 8: return paged_attn_stream_kernel<KV, D, 8>;
-        case 16: return paged_attn_stream_kernel<KV, D, 16>;
-        case 32: return paged_attn_stream_kernel<KV, D, 32>;
-        case 64: return paged_attn_stream_kernel<KV, D, 64>;
-        case 128: return paged_attn_stream_kernel<KV, D, 128>;
+        case 8: return paged_attn_stream_kernel<KV, D, 8, MQ>;
+        case 16: return paged_attn_stream_kernel<KV, D, 16, MQ>;
+        case 32: return paged_attn_stream_kernel<KV, D, 32, MQ>;
+        case 64: return paged_attn_stream_kernel<KV, D, 64, MQ>;
+        case 128: return paged_attn_stream_kernel<KV, D, 128, MQ>;
     }
     return nullptr;
 }
 
 template <int KV>
-AttnKernel pick_stream(int d, int bs) {
-    return d == 64 ? pick_stream_bs<KV, 64>(bs) : pick_stream_bs<KV, 128>(bs);
+AttnKernel pick_stream(int d, int bs, bool mq) {
+    if (mq) return d == 64 ? pick_stream_bs<KV, 64, true>(bs) : pick_stream_bs<KV, 128, true>(bs);
+    return d == 64 ? pick_stream_bs<KV, 64, false>(bs) : pick_stream_bs<KV, 128, false>(bs);
 }
 
 // Compute units of the current device (cached per device).
@@ -1252,60 +1305,79 @@ extern "C" pkv_status pkv_copy_blocks(void* k_cache, void* v_cache, const int32_
     return ok();
 }
 
-extern "C" size_t pkv_paged_decode_attn_workspace_size(int32_t S, int32_t Hq, int32_t Hkv, int32_t d,
-                                                       int32_t max_context_len,
-                                                       int32_t partition_size) {
-    if (S <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || Hq % Hkv != 0) return 0;
-    const size_t G = (size_t)(Hq / Hkv);
-    if (partition_size == PKV_PARTITION_BALANCED)
-        return balanced_records_bytes(G, d) + 2 * (size_t)S * (size_t)Hkv * sizeof(int);
+namespace {
+
+// Query window layout of the balanced split: qgs queries per group (G * qgs
+// MFMA columns, at most 16) and n_qg groups.
+struct QueryGroups {
+    int qgs, n_qg, cols;
+};
+QueryGroups query_groups(int32_t n_q, int32_t G) {
+    QueryGroups r;
+    r.qgs = std::min<int32_t>(n_q, std::max<int32_t>(1, 16 / G));
+    r.n_qg = (n_q + r.qgs - 1) / r.qgs;
+    r.cols = G * r.qgs;
+    return r;
+}
+
+size_t attn_workspace_size(int32_t S, int32_t n_q, int32_t Hq, int32_t Hkv, int32_t d,
+                           int32_t max_context_len, int32_t partition_size) {
+    if (S <= 0 || n_q <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || Hq % Hkv != 0) return 0;
+    const int32_t G = Hq / Hkv;
+    if (partition_size == PKV_PARTITION_BALANCED) {
+        const QueryGroups qg = query_groups(n_q, G);
+        return balanced_records_bytes((size_t)qg.cols, d) +
+               2 * (size_t)S * (size_t)Hkv * (size_t)qg.n_qg * sizeof(int);
+    }
     const int64_t n = n_partitions(max_context_len, partition_size);
     if (n <= 1) return 0;
     return (size_t)S * (size_t)Hq * (size_t)n * (size_t)(d + 2) * sizeof(float);
 }
 
-extern "C" pkv_status pkv_paged_decode_attn(float* out, const void* q, const void* k_cache,
-                                            const void* v_cache, const int32_t* block_tables,
-                                            const int32_t* context_lens, int32_t S, int32_t Hq,
-                                            int32_t Hkv, int32_t d, int32_t bs, int32_t P,
-                                            int32_t max_blocks, int32_t max_context_len,
-                                            float softmax_scale, float k_scale, float v_scale,
-                                            pkv_dtype q_dtype, pkv_dtype cache_dtype,
-                                            int32_t partition_size, void* workspace,
-                                            size_t workspace_bytes, void* stream) {
-    if (S < 0 || Hq <= 0 || Hkv <= 0) return fail(PKV_E_INVALID, "paged_decode_attn: S=%d Hq=%d Hkv=%d", S, Hq, Hkv);
-    if (Hq % Hkv != 0) return fail(PKV_E_INVALID, "paged_decode_attn: Hq=%d not a multiple of Hkv=%d", Hq, Hkv);
+// Validation and launch shared by the single-query and multi-query entry
+// points (n_q > 1 always takes the balanced split).
+pkv_status attn_launch(const char* fn, float* out, const void* q, const void* k_cache,
+                       const void* v_cache, const int32_t* block_tables, const int32_t* context_lens,
+                       int32_t S, int32_t n_q, int32_t Hq, int32_t Hkv, int32_t d, int32_t bs,
+                       int32_t P, int32_t max_blocks, int32_t max_context_len, float softmax_scale,
+                       float k_scale, float v_scale, pkv_dtype q_dtype, pkv_dtype cache_dtype,
+                       int32_t partition_size, void* workspace, size_t workspace_bytes, void* stream) {
+    if (S < 0 || Hq <= 0 || Hkv <= 0) return fail(PKV_E_INVALID, "%s: S=%d Hq=%d Hkv=%d", fn, S, Hq, Hkv);
+    if (n_q < 1 || n_q > 4096) return fail(PKV_E_INVALID, "%s: n_q=%d outside [1, 4096]", fn, n_q);
+    if (Hq % Hkv != 0) return fail(PKV_E_INVALID, "%s: Hq=%d not a multiple of Hkv=%d", fn, Hq, Hkv);
     const int32_t G = Hq / Hkv;
-    if (G > 16) return fail(PKV_E_INVALID, "paged_decode_attn: Hq/Hkv=%d > 16", G);
-    if (!pkv::is_head_dim(d)) return fail(PKV_E_INVALID, "paged_decode_attn: d=%d not in {64,128}", d);
-    if (!pkv::is_pow2_block(bs)) return fail(PKV_E_INVALID, "paged_decode_attn: bs=%d not in {8,16,32,64,128}", bs);
-    if (P <= 0 || max_blocks <= 0) return fail(PKV_E_INVALID, "paged_decode_attn: P=%d max_blocks=%d", P, max_blocks);
+    if (G > 16) return fail(PKV_E_INVALID, "%s: Hq/Hkv=%d > 16", fn, G);
+    if (!pkv::is_head_dim(d)) return fail(PKV_E_INVALID, "%s: d=%d not in {64,128}", fn, d);
+    if (!pkv::is_pow2_block(bs)) return fail(PKV_E_INVALID, "%s: bs=%d not in {8,16,32,64,128}", fn, bs);
+    if (P <= 0 || max_blocks <= 0) return fail(PKV_E_INVALID, "%s: P=%d max_blocks=%d", fn, P, max_blocks);
     if (max_context_len < 0 || (int64_t)max_context_len > (int64_t)max_blocks * bs)
-        return fail(PKV_E_INVALID, "paged_decode_attn: max_context_len=%d outside [0, max_blocks*bs=%lld]",
+        return fail(PKV_E_INVALID, "%s: max_context_len=%d outside [0, max_blocks*bs=%lld]", fn,
                     max_context_len, (long long)max_blocks * bs);
     int kv;
     if (q_dtype == PKV_F32 && cache_dtype == PKV_F32) kv = KV_F32;
     else if (q_dtype == PKV_BF16 && cache_dtype == PKV_BF16) kv = KV_BF16;
     else if (q_dtype == PKV_BF16 && cache_dtype == PKV_FP8_E4M3) kv = KV_FP8;
-    else return fail(PKV_E_INVALID, "paged_decode_attn: unsupported q/cache dtypes %d/%d", q_dtype, cache_dtype);
+    else return fail(PKV_E_INVALID, "%s: unsupported q/cache dtypes %d/%d", fn, q_dtype, cache_dtype);
     const bool balanced = partition_size == PKV_PARTITION_BALANCED;
     if (!balanced && (partition_size < 0 || partition_size % 32 != 0))
-        return fail(PKV_E_INVALID, "paged_decode_attn: partition_size=%d not 0, a multiple of 32 or "
-                    "PKV_PARTITION_BALANCED", partition_size);
-    if (!std::isfinite(softmax_scale)) return fail(PKV_E_INVALID, "paged_decode_attn: softmax_scale not finite");
+        return fail(PKV_E_INVALID, "%s: partition_size=%d not 0, a multiple of 32 or "
+                    "PKV_PARTITION_BALANCED", fn, partition_size);
+    if (!std::isfinite(softmax_scale)) return fail(PKV_E_INVALID, "%s: softmax_scale not finite", fn);
     if (kv == KV_FP8 && !(std::isfinite(k_scale) && std::isfinite(v_scale)))
-        return fail(PKV_E_INVALID, "paged_decode_attn: fp8 scales not finite");
+        return fail(PKV_E_INVALID, "%s: fp8 scales not finite", fn);
     if (S == 0) return ok();
     if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
-        return fail(PKV_E_INVALID, "paged_decode_attn: NULL pointer");
+        return fail(PKV_E_INVALID, "%s: NULL pointer", fn);
+    const QueryGroups qgr = query_groups(n_q, G);
     const int64_t n_part = balanced ? 1 : n_partitions(max_context_len, partition_size);
-    const size_t need = pkv_paged_decode_attn_workspace_size(S, Hq, Hkv, d, max_context_len, partition_size);
+    const size_t need = attn_workspace_size(S, n_q, Hq, Hkv, d, max_context_len, partition_size);
     if (need > 0 && (!workspace || workspace_bytes < need))
-        return fail(PKV_E_WORKSPACE, "paged_decode_attn: workspace %zu bytes, need %zu", workspace_bytes, need);
-    // upper bound on work items (fixed partitions) or chunk positions (balanced)
-    const int64_t n_upper = balanced ? (int64_t)S * Hkv * (((int64_t)max_context_len + 15) / 16 + kSegCost)
+        return fail(PKV_E_WORKSPACE, "%s: workspace %zu bytes, need %zu", fn, workspace_bytes, need);
+    // upper bound on work items (fixed partitions) or positions (balanced)
+    const int64_t n_upper = balanced ? (int64_t)S * Hkv * qgr.n_qg *
+                                           (((int64_t)max_context_len + 15) / 16 + kSegCost)
                                      : n_part * (int64_t)S * Hkv;
-    if (n_upper > 0x7FFFFFFFLL) return fail(PKV_E_INVALID, "paged_decode_attn: too many work items");
+    if (n_upper > 0x7FFFFFFFLL) return fail(PKV_E_INVALID, "%s: too many work items", fn);
 
     AttnParams prm;
     prm.out = out;
@@ -1316,7 +1388,7 @@ extern "C" pkv_status pkv_paged_decode_attn(float* out, const void* q, const voi
     prm.lens = context_lens;
     prm.ws = static_cast<float*>(workspace);
     prm.desc = balanced ? reinterpret_cast<int*>(static_cast<char*>(workspace) +
-                                                 balanced_records_bytes((size_t)G, d))
+                                                 balanced_records_bytes((size_t)qgr.cols, d))
                         : nullptr;
     prm.S = S;
     prm.Hq = Hq;
@@ -1325,6 +1397,10 @@ extern "C" pkv_status pkv_paged_decode_attn(float* out, const void* q, const voi
     prm.P = P;
     prm.max_blocks = max_blocks;
     prm.max_len = max_context_len;
+    prm.n_q = n_q;
+    prm.qgs = qgr.qgs;
+    prm.n_qg = qgr.n_qg;
+    prm.cols = qgr.cols;
     // single pass: one partition long enough for any sequence (whole chunks)
     prm.part_tokens = partition_size > 0 ? partition_size : ((max(max_context_len, 1) + 31) / 32) * 32;
     prm.n_part = (int)n_part;
@@ -1337,8 +1413,9 @@ extern "C" pkv_status pkv_paged_decode_attn(float* out, const void* q, const voi
     AttnKernel kern;
     size_t lds;
     if (balanced) {
-        kern = kv == KV_F32 ? pick_stream<KV_F32>(d, bs)
-             : kv == KV_BF16 ? pick_stream<KV_BF16>(d, bs) : pick_stream<KV_FP8>(d, bs);
+        const bool mq = n_q > 1;
+        kern = kv == KV_F32 ? pick_stream<KV_F32>(d, bs, mq)
+             : kv == KV_BF16 ? pick_stream<KV_BF16>(d, bs, mq) : pick_stream<KV_FP8>(d, bs, mq);
         lds = (size_t)(prm.cache_lens ? S : 0) * sizeof(int);
     } else {
         kern = kv == KV_F32 ? pick_d<KV_F32>(d, bs)
@@ -1347,7 +1424,7 @@ extern "C" pkv_status pkv_paged_decode_attn(float* out, const void* q, const voi
     }
     auto st = static_cast<hipStream_t>(stream);
     const int resident = resident_workgroups(kern, lds);
-    if (resident <= 0) return fail(PKV_E_HIP, "paged_decode_attn: occupancy query failed");
+    if (resident <= 0) return fail(PKV_E_HIP, "%s: occupancy query failed", fn);
     int64_t grid = n_upper < resident ? n_upper : resident;
     if (balanced) {
         // One workgroup per compute unit: a single wave per SIMD streams at the
@@ -1355,7 +1432,7 @@ extern "C" pkv_status pkv_paged_decode_attn(float* out, const void* q, const voi
         // equal shares of memory bandwidth, which equal static ranges cannot
         // absorb). Idle ranges exit at once.
         const int cus = compute_units();
-        if (cus <= 0) return fail(PKV_E_HIP, "paged_decode_attn: device query failed");
+        if (cus <= 0) return fail(PKV_E_HIP, "%s: device query failed", fn);
         grid = cus < resident ? cus : resident;
         if (grid * kWaves > kMaxWorkers) grid = kMaxWorkers / kWaves;
     }
@@ -1364,15 +1441,57 @@ extern "C" pkv_status pkv_paged_decode_attn(float* out, const void* q, const voi
     prm.n_rec = balanced ? 2 * prm.n_workers : (int)(n_part * (int64_t)S * Hkv);
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kThreads), lds, st, prm);
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return fail(PKV_E_HIP, "paged_decode_attn: launch failed: %s", hipGetErrorString(e));
+    if (e != hipSuccess) return fail(PKV_E_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
     if (balanced || n_part > 1) {
-        const unsigned rgrid = (unsigned)(((int64_t)S * Hq + kWaves - 1) / kWaves);
+        const unsigned rgrid = (unsigned)(((int64_t)S * n_q * Hq + kWaves - 1) / kWaves);
         if (d == 64)
             hipLaunchKernelGGL(paged_attn_merge_kernel<64>, dim3(rgrid), dim3(kThreads), 0, st, prm);
         else
             hipLaunchKernelGGL(paged_attn_merge_kernel<128>, dim3(rgrid), dim3(kThreads), 0, st, prm);
         e = hipGetLastError();
-        if (e != hipSuccess) return fail(PKV_E_HIP, "paged_decode_attn: merge launch failed: %s", hipGetErrorString(e));
+        if (e != hipSuccess) return fail(PKV_E_HIP, "%s: merge launch failed: %s", fn, hipGetErrorString(e));
     }
     return ok();
+}
+
+}  // namespace
+
+extern "C" size_t pkv_paged_decode_attn_workspace_size(int32_t S, int32_t Hq, int32_t Hkv, int32_t d,
+                                                       int32_t max_context_len,
+                                                       int32_t partition_size) {
+    return attn_workspace_size(S, 1, Hq, Hkv, d, max_context_len, partition_size);
+}
+
+extern "C" pkv_status pkv_paged_decode_attn(float* out, const void* q, const void* k_cache,
+                                            const void* v_cache, const int32_t* block_tables,
+                                            const int32_t* context_lens, int32_t S, int32_t Hq,
+                                            int32_t Hkv, int32_t d, int32_t bs, int32_t P,
+                                            int32_t max_blocks, int32_t max_context_len,
+                                            float softmax_scale, float k_scale, float v_scale,
+                                            pkv_dtype q_dtype, pkv_dtype cache_dtype,
+                                            int32_t partition_size, void* workspace,
+                                            size_t workspace_bytes, void* stream) {
+    return attn_launch("paged_decode_attn", out, q, k_cache, v_cache, block_tables, context_lens, S, 1,
+                       Hq, Hkv, d, bs, P, max_blocks, max_context_len, softmax_scale, k_scale, v_scale,
+                       q_dtype, cache_dtype, partition_size, workspace, workspace_bytes, stream);
+}
+
+extern "C" size_t pkv_paged_multi_query_attn_workspace_size(int32_t S, int32_t n_q, int32_t Hq,
+                                                            int32_t Hkv, int32_t d) {
+    return attn_workspace_size(S, n_q, Hq, Hkv, d, 0, PKV_PARTITION_BALANCED);
+}
+
+extern "C" pkv_status pkv_paged_multi_query_attn(float* out, const void* q, const void* k_cache,
+                                                 const void* v_cache, const int32_t* block_tables,
+                                                 const int32_t* context_lens, int32_t S, int32_t n_q,
+                                                 int32_t Hq, int32_t Hkv, int32_t d, int32_t bs,
+                                                 int32_t P, int32_t max_blocks,
+                                                 int32_t max_context_len, float softmax_scale,
+                                                 float k_scale, float v_scale, pkv_dtype q_dtype,
+                                                 pkv_dtype cache_dtype, void* workspace,
+                                                 size_t workspace_bytes, void* stream) {
+    return attn_launch("paged_multi_query_attn", out, q, k_cache, v_cache, block_tables, context_lens, S,
+                       n_q, Hq, Hkv, d, bs, P, max_blocks, max_context_len, softmax_scale, k_scale,
+                       v_scale, q_dtype, cache_dtype, PKV_PARTITION_BALANCED, workspace, workspace_bytes,
+                       stream);
 }

@@ -118,3 +118,24 @@ def oracle_step(w, seqs=None):
                                    softmax_scale=w.softmax_scale, q_dtype=s.q_dtype,
                                    cache_dtype=s.cache_dtype, seqs=seqs)
     return slots, kc, vc, out
+
+
+def oracle_pools(w, seqs=None):
+    """The oracle's pools after this step's write. fp8: the oracle quantises the
+    blocks that the listed sequences read (all blocks when seqs is None) from the
+    bf16 values itself; other blocks stay zero."""
+    s = w.spec
+    slots = oracle.decode_slots(w.block_tables, w.context_lens, s.bs)
+    if s.cache_dtype != "fp8":
+        return oracle.kv_cache_write(w.k_new, w.v_new, w.k_pool, w.v_pool, slots, bs=s.bs,
+                                     src_dtype=s.src_dtype, cache_dtype=s.cache_dtype)
+    rows = range(s.S) if seqs is None else seqs
+    blocks = np.unique(w.block_tables[list(rows)].reshape(-1))
+    blocks = blocks[blocks >= 0]
+    kq = np.zeros(w.k_pool.shape, dtype=np.uint8)
+    vq = np.zeros(w.v_pool.shape, dtype=np.uint8)
+    kq[blocks] = oracle.quantise(w.k_pool[blocks], "bf16", w.k_inv_scale)
+    vq[blocks] = oracle.quantise(w.v_pool[blocks], "bf16", w.v_inv_scale)
+    return oracle.kv_cache_write(w.k_new, w.v_new, kq, vq, slots, bs=s.bs, src_dtype="bf16",
+                                 cache_dtype="fp8", k_inv_scale=w.k_inv_scale,
+                                 v_inv_scale=w.v_inv_scale)

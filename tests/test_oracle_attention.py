@@ -298,3 +298,73 @@ def test_planted_bf16_truncation_mistake_is_caught(monkeypatch):
     monkeypatch.setattr(oatt, "bf16_bits_to_f64", wrong)
     assert not _pins_pass()
     assert codecs.bf16_bits_to_f64 is not wrong
+
+
+# ------------------------------------------------------------------ query windows
+def _sdpa_window(q_w, K, V, sigma):
+    """All n_q queries of a window at once through torch SDPA with an explicit
+    boolean mask: query j (position L - n_q + j) may see token t iff t <= that
+    position. float64; kv head h // G serves q head h."""
+    n_q, Hq, d = q_w.shape
+    L, Hkv, _ = K.shape
+    G = Hq // Hkv
+    q = torch.from_numpy(q_w).permute(1, 0, 2).unsqueeze(0).contiguous()          # [1][Hq][n_q][d]
+    k = torch.from_numpy(K).permute(1, 0, 2).repeat_interleave(G, dim=0).unsqueeze(0).contiguous()
+    v = torch.from_numpy(V).permute(1, 0, 2).repeat_interleave(G, dim=0).unsqueeze(0).contiguous()
+    pos = torch.arange(L - n_q, L).unsqueeze(1)                                   # [n_q][1]
+    mask = torch.arange(L).unsqueeze(0) <= pos                                    # [n_q][L]
+    o = torch.nn.functional.scaled_dot_product_attention(q, k, v, attn_mask=mask, scale=float(sigma))
+    return o[0].permute(1, 0, 2).numpy()                                          # [n_q][Hq][d]
+
+
+WINDOWS = [
+    (21, [5, 17, 33], 4, 4, 8, 4, 3),
+    (22, [16, 40, 9], 8, 2, 16, 8, 5),
+    (23, [64, 30], 6, 3, 8, 16, 1),
+    (24, [20, 20], 16, 2, 32, 16, 20),        # the window is the whole sequence
+]
+
+
+@pytest.mark.parametrize("seed,lens,Hq,Hkv,d,bs,n_q", WINDOWS)
+def test_multi_query_against_masked_sdpa(seed, lens, Hq, Hkv, d, bs, n_q):
+    rng = np.random.default_rng(seed)
+    _, Kc, Vc, kp, vp, tab = _case(seed, lens, Hq, Hkv, d, bs)
+    q = rng.standard_normal((len(lens), n_q, Hq, d)).astype(np.float32)
+    sigma = np.float32(1 / math.sqrt(d))
+    out = oracle.paged_multi_query_attn(q, kp, vp, tab, np.array(lens), bs=bs, softmax_scale=sigma,
+                                        q_dtype="f32", cache_dtype="f32")
+    for i in range(len(lens)):
+        ref = _sdpa_window(q[i].astype(np.float64), Kc[i].astype(np.float64), Vc[i].astype(np.float64),
+                           np.float64(sigma))
+        np.testing.assert_allclose(out[i], ref, rtol=1e-12, atol=1e-12)
+
+
+def test_multi_query_last_query_is_decode_and_empty_rows():
+    _, Kc, Vc, kp, vp, tab = _case(25, [30, 0, 12], 4, 2, 8, 4)
+    q = np.random.default_rng(26).standard_normal((3, 4, 4, 8)).astype(np.float32)
+    lens = np.array([30, 0, 12])
+    mq = oracle.paged_multi_query_attn(q, kp, vp, tab, lens, bs=4, softmax_scale=0.3,
+                                       q_dtype="f32", cache_dtype="f32")
+    dec = oracle.paged_decode_attn(q[:, -1], kp, vp, tab, lens, bs=4, softmax_scale=0.3,
+                                   q_dtype="f32", cache_dtype="f32")
+    assert np.array_equal(mq[:, -1], dec)
+    assert np.all(mq[1] == 0.0)
+
+
+def test_planted_causal_offset_mistake_is_caught(monkeypatch):
+    # a window whose queries saw one token too many would disagree with SDPA
+    real = oatt.paged_decode_attn
+
+    def shifted(q, kc, vc, tab, lens, **kw):
+        return real(q, kc, vc, tab, np.where(np.asarray(lens) > 0, np.asarray(lens) + 1, 0), **kw)
+
+    seed, lens, Hq, Hkv, d, bs, n_q = WINDOWS[0]
+    rng = np.random.default_rng(seed)
+    _, Kc, Vc, kp, vp, tab = _case(seed, lens, Hq, Hkv, d, bs)
+    q = rng.standard_normal((len(lens), n_q, Hq, d)).astype(np.float32)
+    monkeypatch.setattr(oatt, "paged_decode_attn", shifted)
+    out = oatt.paged_multi_query_attn(q, kp, vp, tab, np.array(lens), bs=bs, softmax_scale=0.35,
+                                      q_dtype="f32", cache_dtype="f32")
+    ref = _sdpa_window(q[0].astype(np.float64), Kc[0].astype(np.float64), Vc[0].astype(np.float64),
+                       np.float64(np.float32(0.35)))
+    assert not np.allclose(out[0], ref, rtol=1e-6, atol=1e-6)
