@@ -322,6 +322,46 @@ pkv_status pkv_slots_from_tables(const int32_t* tables, const int32_t* positions
                                  int32_t S, int32_t max_blocks, int32_t bs,
                                  int64_t* slots_out);
 
+/*
+ * Prefix caching ("PagedAttention" daily term, the prefix-caching paragraph
+ * after the copy-on-write figure; "Serving: vLLM and PagedAttention",
+ * section 2.6): a full block is named by a hash of its tokens and of the
+ * prefix before it, so a later request whose prompt starts the same way reuses
+ * the cached blocks instead of recomputing them.
+ *
+ * Block hash k of a token sequence (reading of the pages' components: parent
+ * hash, block token ids, extra keys) is
+ *   SHA-256( hash_{k-1} || tokens[k*bs .. k*bs+bs) as little-endian int32 || extra )
+ * with hash_{-1} = 32 zero bytes; extra is any caller key (adapter id, tenant
+ * salt, ...) and may be empty. Only full blocks have hashes.
+ *
+ * pkv_block_hashes writes the n_tokens / bs hashes of a sequence to
+ * hashes_out[n_tokens / bs][32].
+ */
+pkv_status pkv_block_hashes(const int32_t* tokens, int32_t n_tokens, int32_t bs,
+                            const uint8_t* extra, int32_t extra_len, uint8_t* hashes_out);
+
+/*
+ * Create sequence seq_id holding a prompt of n_tokens tokens. The longest run
+ * of leading full blocks whose hashes are cached is shared (reference count + 1;
+ * a cached block that is free again is taken back off the free list); the rest
+ * of the prompt gets fresh blocks, and each fresh full block is registered
+ * under its hash. slots_out[n_tokens] receives every position's slot;
+ * *n_cached_out the number of leading tokens whose K/V are already in the
+ * cache (a multiple of bs) -- the caller writes only the others.
+ * A block keeps its hash while in use and after it is freed, until the free
+ * list hands it out again. All or nothing: PKV_E_NO_BLOCKS changes nothing;
+ * PKV_E_STATE if seq_id exists.
+ */
+pkv_status pkv_seq_create_prefixed(pkv_allocator* a, int64_t seq_id, const int32_t* tokens,
+                                   int32_t n_tokens, const uint8_t* extra, int32_t extra_len,
+                                   int64_t* slots_out, int32_t* n_cached_out);
+
+/* Prefix-cache counters: leading blocks found and not found by
+ * pkv_seq_create_prefixed, and blocks holding a hash now. */
+pkv_status pkv_prefix_cache_stats(const pkv_allocator* a, int64_t* hit_blocks,
+                                  int64_t* miss_blocks, int32_t* cached_blocks);
+
 /* Pool-wide statistics ("03 · PagedAttention", "In Production": the block
  * pool's fill is the capacity signal). */
 pkv_status pkv_allocator_stats(const pkv_allocator* a, pkv_stats* out);

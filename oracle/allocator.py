@@ -27,7 +27,19 @@ What the pages fix, and the readings taken where they leave a choice:
   needs more blocks than are free changes nothing and reports NoBlocks.
 * Freeing lowers every block's count, last logical block first, and returns a
   block to the free list when its count reaches zero.
+* Prefix caching ("PagedAttention" daily term, the prefix-caching paragraph
+  after the copy-on-write figure; "Serving: vLLM and PagedAttention", section
+  2.6): a full block is named by a hash chaining the parent block's hash, the
+  block's token ids and extra keys, and a later request with the same prefix
+  points at the cached blocks. Readings: the hash is SHA-256 over parent (32
+  zero bytes for the first block) || token ids as little-endian int32 ||
+  extra; the longest run of leading cached blocks is reused; a freed block
+  keeps its hash until the free list hands it out again, and reusing such a
+  block takes it back off the free list.
 """
+
+import hashlib
+import struct
 
 
 class NoBlocks(Exception):
@@ -40,9 +52,30 @@ class TwinAllocator:
             raise ValueError("pool and block size must be positive")
         self.P = num_blocks
         self.bs = block_size
-        self.free = list(range(num_blocks - 1, -1, -1))   # pop() -> 0 first
         self.ref = [0] * num_blocks
         self.seqs = {}                                    # id -> [blocks, length]
+        # free list: a stack of (block, stamp); an entry counts only while the
+        # block is free and the stamp is the block's latest (a cached block
+        # taken back leaves a stale entry behind)
+        self.stamp = [0] * num_blocks
+        self.stack = []
+        self.n_free = 0
+        for b in range(num_blocks - 1, -1, -1):           # first pop -> 0
+            self._push(b)
+        self.cached = {}                                  # hash -> block
+        self.hash_of = {}                                 # block -> hash
+        self.hits = 0
+        self.misses = 0
+
+    @property
+    def free(self):
+        """The free blocks, in pop order reversed (last element pops first)."""
+        return [b for b, st in self.stack if self.ref[b] == 0 and st == self.stamp[b]]
+
+    def _push(self, b):
+        self.stamp[b] += 1
+        self.stack.append((b, self.stamp[b]))
+        self.n_free += 1
 
     # -- sequence operations -------------------------------------------------
     def create(self, seq_id):
@@ -51,9 +84,26 @@ class TwinAllocator:
         self.seqs[seq_id] = [[], 0]
 
     def _pop(self):
-        b = self.free.pop()
+        while True:
+            b, st = self.stack.pop()
+            if self.ref[b] == 0 and st == self.stamp[b]:
+                break
         self.ref[b] = 1
+        self.n_free -= 1
+        self._forget(b)                                   # its contents are about to change
         return b
+
+    def _forget(self, b):
+        h = self.hash_of.pop(b, None)
+        if h is not None and self.cached.get(h) == b:
+            del self.cached[h]
+
+    def _remember(self, b, h):
+        old = self.cached.get(h)
+        if old is not None and old != b:
+            self.hash_of.pop(old, None)
+        self.cached[h] = b
+        self.hash_of[b] = h
 
     def append(self, seq_id, n):
         """Append n token positions; returns (slots, cow_pairs)."""
@@ -64,8 +114,8 @@ class TwinAllocator:
         cow = n > 0 and length % bs != 0 and self.ref[blocks[-1]] > 1
         have = -(-length // bs)
         need = -(-(length + n) // bs) - have + (1 if cow else 0)
-        if need > len(self.free):
-            raise NoBlocks(f"need {need} blocks, {len(self.free)} free")
+        if need > self.n_free:
+            raise NoBlocks(f"need {need} blocks, {self.n_free} free")
         pairs = []
         if cow:
             src = blocks[-1]
@@ -97,7 +147,56 @@ class TwinAllocator:
         for b in reversed(blocks):
             self.ref[b] -= 1
             if self.ref[b] == 0:
-                self.free.append(b)
+                self._push(b)
+
+    # -- prefix caching ----------------------------------------------------------
+    @staticmethod
+    def block_hashes(tokens, bs, extra=b""):
+        """Chained hashes of the full blocks of a token sequence (list of 32-byte
+        digests)."""
+        out, parent = [], bytes(32)
+        for k in range(len(tokens) // bs):
+            block = tokens[k * bs:(k + 1) * bs]
+            data = parent + struct.pack("<%di" % bs, *[int(t) for t in block]) + bytes(extra)
+            parent = hashlib.sha256(data).digest()
+            out.append(parent)
+        return out
+
+    def create_prefixed(self, seq_id, tokens, extra=b""):
+        """New sequence holding a prompt; reuses the longest run of leading cached
+        full blocks. Returns (slots, n_cached_tokens)."""
+        if seq_id in self.seqs:
+            raise KeyError(f"sequence {seq_id} exists")
+        bs, n = self.bs, len(tokens)
+        hs = self.block_hashes(tokens, bs, extra)
+        hit_ids = []
+        for h in hs:
+            if h not in self.cached:
+                break
+            hit_ids.append(self.cached[h])
+        hit = len(hit_ids)
+        revive = sum(1 for b in hit_ids if self.ref[b] == 0)
+        fresh = -(-n // bs) - hit
+        if revive + fresh > self.n_free:
+            raise NoBlocks(f"need {revive + fresh} blocks, {self.n_free} free")
+        blocks = []
+        for b in hit_ids:
+            if self.ref[b] == 0:
+                self.n_free -= 1                          # its stack entry goes stale
+            self.ref[b] += 1
+            blocks.append(b)
+        for j in range(hit, -(-n // bs)):
+            b = self._pop()
+            if j < len(hs):
+                self._remember(b, hs[j])
+            blocks.append(b)
+        self.seqs[seq_id] = [blocks, n]
+        self.hits += hit
+        self.misses += len(hs) - hit
+        return [blocks[p // bs] * bs + p % bs for p in range(n)], hit * bs
+
+    def prefix_stats(self):
+        return {"hit_blocks": self.hits, "miss_blocks": self.misses, "cached_blocks": len(self.cached)}
 
     # -- views -----------------------------------------------------------------
     def tables(self, seq_ids, max_blocks):
@@ -122,11 +221,11 @@ class TwinAllocator:
             for j, b in enumerate(blocks):
                 f = min(self.bs, length - j * self.bs)
                 fill[b] = max(fill.get(b, 0), f)
-        used = self.P - len(self.free)
+        used = self.P - self.n_free
         slots = used * self.bs
         tokens = sum(fill.values())
         return {
-            "num_blocks": self.P, "free_blocks": len(self.free), "used_blocks": used,
+            "num_blocks": self.P, "free_blocks": self.n_free, "used_blocks": used,
             "slots_allocated": slots, "tokens_stored": tokens,
             "waste": (1.0 - tokens / slots) if slots else 0.0,
         }

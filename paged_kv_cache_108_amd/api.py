@@ -18,7 +18,7 @@ __all__ = [
     "kv_cache_write", "copy_blocks", "paged_decode_attn", "paged_decode_attn_workspace_size",
     "paged_decode_attn_workspace", "paged_multi_query_attn", "paged_multi_query_attn_workspace",
     "Allocator",
-    "slots_from_tables", "waste_stats", "last_error", "version", "quantise_pool",
+    "slots_from_tables", "waste_stats", "block_hashes", "last_error", "version", "quantise_pool",
     "PkvError", "NoBlocks", "PKV_PARTITION_BALANCED",
 ]
 
@@ -223,6 +223,17 @@ def waste_stats(lens, bs, max_len):
             "waste_paged": wp.value, "waste_naive": wn.value}
 
 
+def block_hashes(tokens, bs, extra=b""):
+    """pkv_block_hashes -> uint8 [n_tokens // bs][32]."""
+    tokens = _i32(tokens)
+    m = len(tokens) // bs
+    out = np.zeros((max(m, 1), 32), dtype=np.uint8)
+    ex = bytes(extra)
+    check(lib().pkv_block_hashes(_ptr(tokens, P_i32), len(tokens), bs, ex if ex else None, len(ex),
+                                 out.ctypes.data_as(c_vp)))
+    return out[:m]
+
+
 class Allocator:
     """The library's host block allocator (pkv_allocator_*)."""
 
@@ -277,6 +288,25 @@ class Allocator:
         check(lib().pkv_build_block_tables(self._h, _ptr(ids, P_i64), S, max_blocks,
                                            _ptr(tab, P_i32), _ptr(lens, P_i32)))
         return tab, lens
+
+    def create_prefixed(self, seq_id, tokens, extra=b""):
+        """pkv_seq_create_prefixed -> (slots int64[n], n_cached)."""
+        tokens = _i32(tokens)
+        n = len(tokens)
+        slots = np.empty(max(n, 1), dtype=np.int64)
+        n_cached = c_i32()
+        ex = bytes(extra)
+        st = lib().pkv_seq_create_prefixed(self._h, seq_id, _ptr(tokens, P_i32), n, ex if ex else None,
+                                           len(ex), _ptr(slots, P_i64), ctypes.byref(n_cached))
+        if st == PKV_E_NO_BLOCKS:
+            raise NoBlocks(st, last_error())
+        check(st)
+        return slots[:n], n_cached.value
+
+    def prefix_stats(self):
+        h, m, c = c_i64(), c_i64(), c_i32()
+        check(lib().pkv_prefix_cache_stats(self._h, ctypes.byref(h), ctypes.byref(m), ctypes.byref(c)))
+        return {"hit_blocks": h.value, "miss_blocks": m.value, "cached_blocks": c.value}
 
     def stats(self):
         s = PkvStats()

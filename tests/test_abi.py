@@ -266,3 +266,80 @@ def test_copy_blocks_rejects_invalid_arguments(kw):
 
 def test_copy_blocks_zero_pairs_is_a_noop():
     assert _copy(n=0, kc=None, vc=None, src=None, dst=None) == _lib.PKV_OK
+
+
+# ------------------------------------------------------------------ prefix caching
+def test_block_hashes_match_sha256_of_the_chain():
+    # lengths of parent + tokens + extra cross every SHA-256 padding boundary
+    rng = np.random.default_rng(3)
+    for bs in (1, 2, 8, 16):
+        for extra_len in (0, 1, 3, 7, 8, 19, 20, 23, 24, 55, 56, 64, 120):
+            toks = rng.integers(-2**31, 2**31, 3 * bs + 1).astype(np.int32)
+            extra = bytes(rng.integers(0, 256, extra_len, dtype=np.uint8))
+            got = pkv.block_hashes(toks, bs, extra)
+            want = oracle.TwinAllocator.block_hashes(list(toks), bs, extra)
+            assert [bytes(r) for r in got] == want, (bs, extra_len)
+    assert pkv.block_hashes(np.arange(5, dtype=np.int32), 16).shape == (0, 32)
+
+
+def _prefixed_ops(seed, n=600):
+    rng = np.random.default_rng(seed)
+    prefixes = [list(rng.integers(0, 1000, 80)) for _ in range(4)]
+    ops, live, nxt = [], [], 0
+    for _ in range(n):
+        k = rng.integers(6)
+        if k <= 1 or not live:
+            base = prefixes[rng.integers(4)]
+            cut = int(rng.integers(0, 81))
+            toks = base[:cut] + list(rng.integers(0, 1000, rng.integers(0, 40)))
+            extra = b"" if rng.integers(4) else b"salt"
+            ops.append(("prefixed", nxt, toks, extra)); live.append(nxt); nxt += 1
+        elif k == 2:
+            ops.append(("append", int(live[rng.integers(len(live))]), int(rng.integers(0, 20))))
+        elif k == 3:
+            ops.append(("fork", int(live[rng.integers(len(live))]), nxt)); live.append(nxt); nxt += 1
+        else:
+            ops.append(("free", int(live.pop(int(rng.integers(len(live)))))))
+    return ops
+
+
+@pytest.mark.parametrize("seed,P,bs", [(0, 48, 8), (1, 120, 16), (2, 30, 4)])
+def test_prefix_allocator_matches_twin(seed, P, bs):
+    a, t = pkv.Allocator(P, bs), oracle.TwinAllocator(P, bs)
+    for op in _prefixed_ops(seed):
+        if op[0] == "prefixed":
+            try:
+                s_, c = a.create_prefixed(op[1], op[2], op[3])
+                got = (list(s_), c)
+            except pkv.NoBlocks:
+                got = "noblocks"
+            try:
+                want = t.create_prefixed(op[1], op[2], op[3])
+            except oracle.NoBlocks:
+                want = "noblocks"
+            assert got == want, op[:2]
+            if got == "noblocks":
+                a.create(op[1]); t.create(op[1])
+        elif op[0] == "append":
+            try:
+                g = a.append(op[1], op[2]); g = (list(g[0]), g[1])
+            except pkv.NoBlocks:
+                g = "noblocks"
+            try:
+                wnt = t.append(op[1], op[2])
+            except oracle.NoBlocks:
+                wnt = "noblocks"
+            assert g == wnt
+        elif op[0] == "fork":
+            a.fork(op[1], op[2]); t.fork(op[1], op[2])
+        else:
+            a.release(op[1]); t.release(op[1])
+    ids = sorted(t.seqs)
+    maxb = max([len(t.seqs[s][0]) for s in ids] + [1])
+    tab, lens = a.tables(ids, maxb)
+    ttab, tlens = t.tables(ids, maxb)
+    assert np.array_equal(tab, np.array(ttab, dtype=np.int32).reshape(len(ids), maxb))
+    assert a.prefix_stats() == t.prefix_stats()
+    assert a.prefix_stats()["hit_blocks"] > 0
+    sa, st = a.stats(), t.stats()
+    assert sa["free_blocks"] == st["free_blocks"] and sa["tokens_stored"] == st["tokens_stored"]

@@ -425,3 +425,49 @@ def test_window_edge_shapes(lens, Hq, Hkv, d, bs, dt, n_q):
 
 def test_window_long_fp8_sampled():
     _window_case(W.make("long", cache_dtype="fp8"), 3, seqs=[0, 11])
+
+
+# ------------------------------------------------------------------ prefix caching end to end
+def test_prefix_cache_second_request_writes_only_its_new_tokens():
+    # Request A's prompt is written in full. Request B shares A's first 1000
+    # tokens: the allocator hands B A's cached full blocks, B writes only the
+    # tokens after them, and B's attention must equal the oracle's on a pool
+    # where B's whole sequence was written privately.
+    torch = need_gpu()
+    print("[case] prefix cache", flush=True)
+    rng = np.random.default_rng(91)
+    bs, Hkv, Hq, d, P = 16, 8, 32, 128, 400
+    vocab = rng.integers(0, 32000, 2000)
+    tok_a = list(vocab[:1000]) + list(rng.integers(0, 32000, 37))
+    tok_b = list(vocab[:1000]) + list(rng.integers(0, 32000, 300))
+
+    def kv_of(tokens):     # K/V are a function of (token, position), as a model's would be
+        k = np.stack([np.random.default_rng([int(t), p]).standard_normal((Hkv, d)) for p, t in enumerate(tokens)])
+        v = np.stack([np.random.default_rng([int(t), p, 1]).standard_normal((Hkv, d)) for p, t in enumerate(tokens)])
+        return W.to_bf16_bits(k.astype(np.float32)), W.to_bf16_bits(v.astype(np.float32))
+
+    ka, va = kv_of(tok_a)
+    kb, vb = kv_of(tok_b)
+    alloc = pkv.Allocator(P, bs)
+    sa, ca = alloc.create_prefixed(0, tok_a)
+    sb, cb = alloc.create_prefixed(1, tok_b)
+    assert ca == 0 and cb == 992                        # 62 full blocks of the shared 1000 tokens
+    kc = np.full((P, Hkv, bs, d), 0x7FC0, np.uint16)
+    vc = np.full((P, Hkv, d, bs), 0x7FC0, np.uint16)
+    gk, gv = to_dev(kc), to_dev(vc)
+    pkv.kv_cache_write(to_dev(ka), to_dev(va), gk, gv, to_dev(np.asarray(sa, np.int64)))
+    pkv.kv_cache_write(to_dev(kb[cb:]), to_dev(vb[cb:]), gk, gv, to_dev(np.asarray(sb[cb:], np.int64)))
+    tab, lens = alloc.tables([0, 1], 128)
+    # the oracle: B written privately through its own table into a fresh pool
+    okc, ovc = oracle.kv_cache_write(kb, vb, kc, vc, np.asarray(sb), bs=bs, src_dtype="bf16",
+                                     cache_dtype="bf16")
+    q = W.to_bf16_bits(rng.standard_normal((2, Hq, d)).astype(np.float32))
+    ref = oracle.paged_decode_attn(q[1:], okc, ovc, tab[1:], lens[1:], bs=bs,
+                                   softmax_scale=float(np.float32(d ** -0.5)), q_dtype="bf16",
+                                   cache_dtype="bf16")
+    out = torch.empty((2, Hq, d), dtype=torch.float32, device="cuda")
+    pkv.paged_decode_attn(out, to_dev(q), gk, gv, to_dev(tab), to_dev(lens), max_context_len=int(lens.max()),
+                          softmax_scale=float(np.float32(d ** -0.5)))
+    torch.cuda.synchronize()
+    assert_rows_close(to_host(out)[1:], ref, TOL["bf16"], "prefix-cached request")
+    assert alloc.prefix_stats()["hit_blocks"] == 62

@@ -260,3 +260,63 @@ def test_random_op_invariants():
         except NoBlocks:
             pass
         _check_invariants(a)
+
+
+def test_prefix_cache_reuses_the_longest_cached_prefix():
+    # A later request with the same prefix points at the blocks already holding
+    # it (the daily term's prefix-caching paragraph; "Serving", section 2.6):
+    # only full blocks, only a run of leading ones, only with the same extra key.
+    rng = np.random.default_rng(8)
+    prompt = list(rng.integers(0, 50000, 100))          # 6 full blocks of 16 + 4 tokens
+    a = TwinAllocator(64, 16)
+    s1, c1 = a.create_prefixed("r1", prompt)
+    assert c1 == 0 and len(s1) == 100
+    s2, c2 = a.create_prefixed("r2", prompt[:96] + list(rng.integers(0, 50000, 30)))
+    assert c2 == 96                                     # 6 shared blocks, not the partial 7th
+    t1, t2 = a.seqs["r1"][0], a.seqs["r2"][0]
+    assert t2[:6] == t1[:6] and t2[6] != t1[6]
+    assert all(a.ref[b] == 2 for b in t1[:6]) and a.ref[t1[6]] == 1
+    # differing in block 3 keeps blocks 0-2 only (the hashes chain)
+    p3 = list(prompt)
+    p3[50] += 1
+    _, c3 = a.create_prefixed("r3", p3)
+    assert c3 == 48 and a.seqs["r3"][0][:3] == t1[:3] and a.seqs["r3"][0][3] != t1[3]
+    # another extra key (tenant salt, adapter id) shares nothing
+    _, c4 = a.create_prefixed("r4", prompt, extra=b"tenant-b")
+    assert c4 == 0
+    # freed blocks stay cached: a new request takes them back off the free list
+    a.release("r1"); a.release("r2"); a.release("r3")
+    free_before = a.n_free
+    _, c5 = a.create_prefixed("r5", prompt)
+    assert c5 == 96 and a.seqs["r5"][0][:6] == t1[:6]
+    assert a.n_free == free_before - 7                  # 6 taken back + 1 fresh for the tail
+    assert not set(a.seqs["r5"][0]) & set(a.free)
+    _check_invariants(a)
+
+
+def test_prefix_cache_forgets_reused_blocks_and_is_all_or_nothing():
+    a = TwinAllocator(10, 4)
+    p = list(range(16))                                 # 4 full blocks
+    a.create_prefixed(0, p)
+    a.release(0)                                        # blocks free but still cached
+    assert sorted(a.cached.values()) == [0, 1, 2, 3]
+    a.create(1)
+    a.append(1, 20)                                     # pops 0..4: the cached blocks are reused
+    assert a.cached == {}                               # ... and no longer named
+    _, c = a.create_prefixed(2, p)
+    assert c == 0
+    before = (list(a.free), list(a.ref), dict(a.cached))
+    with pytest.raises(NoBlocks):
+        a.create_prefixed(3, list(range(100, 140)))
+    assert (list(a.free), list(a.ref), dict(a.cached)) == before
+    _check_invariants(a)
+
+
+def test_twin_block_hash_is_chained_sha256():
+    # the hash of block k covers its parent's hash, its tokens and the extra key
+    import hashlib, struct
+    toks = [7, 8, 9, 10, 11, 12, 13, 14]
+    h0 = hashlib.sha256(bytes(32) + struct.pack("<4i", 7, 8, 9, 10) + b"x").digest()
+    h1 = hashlib.sha256(h0 + struct.pack("<4i", 11, 12, 13, 14) + b"x").digest()
+    assert TwinAllocator.block_hashes(toks, 4, b"x") == [h0, h1]
+    assert len(TwinAllocator.block_hashes(toks[:7], 4)) == 1      # only full blocks
