@@ -44,8 +44,8 @@ DEVICE_SOURCE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "paged_
 # the kernel source is the one the counters were taken with.
 MEASURED_TRAFFIC = {
     ("llama8b", "bf16", 16, -1): {
-        "source_sha256": "e06630c44dcd90da823d443abc97b8e0b85e4a432533276de847169da51bbf60",
-        "fetch_kib": 170031.2, "write_kib": 3844.3, "fetch_scale": 2.0, "write_scale": 1.0,
+        "source_sha256": "85088587daf8b838fbf6fcda10f5c30b7f43555cebb640b2732dfff2902c5d57",
+        "fetch_kib": 170028.6, "write_kib": 3844.4, "fetch_scale": 2.0, "write_scale": 1.0,
     },
 }
 
