@@ -2,17 +2,18 @@
 """Benchmark one decode step of paged attention on one MI355X.
 
 A step is the whole hot path over one batch: the KV-cache write of each
-sequence's new token (pkv_kv_cache_write), then paged decode attention over
-every sequence's context including that token (pkv_paged_decode_attn: by
-default the balanced split, i.e. the stream kernel and the merge kernel;
---partition N selects fixed partitions of N tokens). Inputs are seeded
-synthetic workloads already resident in HBM.
+sequence's new token and paged decode attention over every sequence's context
+including that token. By default one pkv_paged_decode_step call does both
+(the stream kernel with the write fused in, then the merge kernel);
+--step split times pkv_kv_cache_write, then pkv_paged_decode_attn (balanced
+split by default; --partition N selects fixed partitions of N tokens). Inputs
+are seeded synthetic workloads already resident in HBM.
 
 Timing: W untimed warm-up steps, then K timed steps. Before each timed step
 (outside its event pair) a 1 GiB buffer is read so neither the 256 MB
 Infinity Cache nor L2 still holds the KV pool; each step is bracketed by HIP
-events on the stream the kernels run on, with a third event between the write
-and the attention call. Bytes are algorithmic: what the method must move (each
+events on the stream the kernels run on (with --step split, a third event
+between the write and the attention call). Bytes are algorithmic: what the method must move (each
 valid token's K and V once, shared blocks once, q, the fp32 output, the table
 entries and lengths; for the write, the new tokens read and stored and the slot
 mapping).
@@ -37,24 +38,24 @@ ELEM = {"f32": 4, "bf16": 2, "fp8": 1}
 DEVICE_SOURCE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "paged_kv_cache_108_amd",
                              "csrc", "device.hip")
 
-# HBM traffic of one attention call (its two kernels), from
+# HBM traffic of one measured call (its two kernels), from
 # rocprofv3 --pmc FETCH_SIZE and --pmc WRITE_SIZE runs of this script's default
 # command, in KiB per call, and the scale that turns each counter into bytes
 # (what the counter reads for a plain copy of known size). Reported only while
 # the kernel source is the one the counters were taken with.
 MEASURED_TRAFFIC = {
-    ("llama8b", "bf16", 16, -1): {
-        "source_sha256": "85088587daf8b838fbf6fcda10f5c30b7f43555cebb640b2732dfff2902c5d57",
-        "fetch_kib": 170028.6, "write_kib": 3844.4, "fetch_scale": 2.0, "write_scale": 1.0,
+    ("llama8b", "bf16", 16, -1, "fused"): {
+        "source_sha256": "c988ddd16875570500f5f42fc563ccab00a34d9f382498244fb25a1ae61da740",
+        "fetch_kib": 170457.7, "write_kib": 6020.0, "fetch_scale": 2.0, "write_scale": 1.0,
     },
 }
 
 
-def measured_traffic(name, cache_dtype, bs, part):
+def measured_traffic(name, cache_dtype, bs, part, step="split"):
     """Bytes per attention call from the counters, or None when none were taken
     for this configuration or the kernel source has changed since."""
     import hashlib
-    m = MEASURED_TRAFFIC.get((name, cache_dtype, bs, part))
+    m = MEASURED_TRAFFIC.get((name, cache_dtype, bs, part, step))
     if m is None:
         return None
     with open(DEVICE_SOURCE, "rb") as f:
@@ -160,6 +161,9 @@ def main():
     ap.add_argument("--partition", type=int, default=-1,
                     help="partition_size for paged_decode_attn: -1 = balanced split (default), "
                          "0 = one pass per (sequence, kv head), else tokens per partition")
+    ap.add_argument("--step", choices=["fused", "split"], default="fused",
+                    help="fused: one pkv_paged_decode_step call writes the new tokens and attends "
+                         "(balanced split only); split: pkv_kv_cache_write, then pkv_paged_decode_attn")
     ap.add_argument("--no-flush", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
@@ -196,6 +200,10 @@ def main():
     s = w.spec
     cache_dtype = s.cache_dtype
     part = args.partition
+    fused = args.step == "fused"
+    if fused and part != pkv.PKV_PARTITION_BALANCED:
+        print(json.dumps({"error": "--step fused takes the balanced split (--partition -1)"}))
+        sys.exit(2)
 
     def dev(a):
         a = np.ascontiguousarray(a)
@@ -236,9 +244,18 @@ def main():
                               k_scale=w.k_scale, v_scale=w.v_scale, partition_size=part,
                               workspace=ws, stream=stream)
 
+    def fused_step():
+        pkv.paged_decode_step(out, q, k_new, v_new, k_cache, v_cache, tables, lens,
+                              max_context_len=w.max_context_len, softmax_scale=w.softmax_scale,
+                              k_scale=w.k_scale, v_scale=w.v_scale, k_inv_scale=w.k_inv_scale,
+                              v_inv_scale=w.v_inv_scale, workspace=ws, stream=stream)
+
     for _ in range(args.warmup):
-        write()
-        attend()
+        if fused:
+            fused_step()
+        else:
+            write()
+            attend()
     torch.cuda.synchronize()
 
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
@@ -250,16 +267,22 @@ def main():
             flush.max()
         a, b, c = ev[k]
         a.record(stream)
-        write()
-        b.record(stream)
-        attend()
+        if fused:
+            fused_step()
+        else:
+            write()
+            b.record(stream)
+            attend()
         c.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
 
     step_ms = [a.elapsed_time(c) for a, b, c in ev]
-    write_ms = [a.elapsed_time(b) for a, b, c in ev]
-    attn_ms = [b.elapsed_time(c) for a, b, c in ev]
+    if fused:                                  # one call does both
+        write_ms, attn_ms = None, step_ms
+    else:
+        write_ms = [a.elapsed_time(b) for a, b, c in ev]
+        attn_ms = [b.elapsed_time(c) for a, b, c in ev]
     step_mean = statistics.mean(step_ms)
     attn_mean = statistics.mean(attn_ms)
 
@@ -267,7 +290,11 @@ def main():
     step_bytes = attn_bytes + write_bytes
     value = step_bytes / (step_mean * 1e-3) / 1e9
     attn_gbs = attn_bytes / (attn_mean * 1e-3) / 1e9
-    if part == pkv.PKV_PARTITION_BALANCED:
+    if fused:
+        kernel_name = "paged_decode_step call (stream kernel with the write fused in + merge kernel)"
+        split = "balanced: equal cost-weighted chunk ranges, one per wave"
+        attn_gbs = step_bytes / (step_mean * 1e-3) / 1e9     # the call moves the write's bytes too
+    elif part == pkv.PKV_PARTITION_BALANCED:
         kernel_name = "paged_decode_attn call (balanced stream kernel + merge kernel)"
         split = "balanced: equal cost-weighted chunk ranges, one per wave"
     else:
@@ -294,13 +321,14 @@ def main():
             "workload": f"{s.name}: {s.description}",
             "sequences": s.S, "q_heads": s.Hq, "kv_heads": s.Hkv, "head_dim": s.d,
             "block_size": s.bs, "kv_dtype": cache_dtype, "partition_size": part, "split": split,
+            "step": "one fused call (write + attention)" if fused else "write call, then attention call",
             "context_tokens": int(w.context_lens.sum()), "unique_tokens": int(unique_tokens),
             "max_context_len": w.max_context_len, "pool_blocks": w.P,
             "cache_flush_between_steps": not args.no_flush,
         },
         "timing": {
             "step_ms_mean": round(step_mean, 5), "step_ms_median": round(statistics.median(step_ms), 5),
-            "write_ms_mean": round(statistics.mean(write_ms), 5),
+            "write_ms_mean": None if write_ms is None else round(statistics.mean(write_ms), 5),
             "attn_ms_mean": round(attn_mean, 5), "attn_ms_median": round(statistics.median(attn_ms), 5),
             "attn_ms_min": round(min(attn_ms), 5),
             "wall_s_timed_region": round(wall, 4),
@@ -311,7 +339,7 @@ def main():
             "kernel": kernel_name,
             "bound": "hbm", "achieved": round(attn_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(attn_gbs / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic(s.name, cache_dtype, s.bs, part),
+            "traffic": measured_traffic(s.name, cache_dtype, s.bs, part, args.step),
         },
         "device": torch.cuda.get_device_name(0),
     }

@@ -175,6 +175,35 @@ pkv_status pkv_paged_decode_attn(float* out, const void* q,
                                  void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * One decode step in one call: write each sequence's new token and attend
+ * over the context including it, as a single launch of the attention kernel
+ * ("PagedAttention" daily term, decode-step figure: gather, score and the
+ * write of the new K/V in one launch for the batch). The result equals
+ * pkv_kv_cache_write of token i at position L_i - 1 of sequence i (its slot
+ * taken from block_tables) followed by pkv_paged_decode_attn with
+ * PKV_PARTITION_BALANCED. The new token's slot may hold anything on entry:
+ * the kernel takes that token's K/V from k_new/v_new (encoded as the write
+ * encodes them) and writes the slot concurrently.
+ *
+ * k_new, v_new:  [S][Hkv][d], F32 for an F32 cache, BF16 for BF16 and
+ *                FP8_E4M3 caches; k_inv_scale / v_inv_scale are the fp8
+ *                write's inverse scales (ignored otherwise).
+ * Other arguments and the workspace as for pkv_paged_decode_attn with
+ * partition_size = PKV_PARTITION_BALANCED (same workspace size). Sequences with
+ * L_i <= 0 get zero rows and no write. The new token's block must not be
+ * shared with another sequence (copy-on-write first: pkv_copy_blocks).
+ */
+pkv_status pkv_paged_decode_step(float* out, const void* q, const void* k_new, const void* v_new,
+                                 void* k_cache, void* v_cache,
+                                 const int32_t* block_tables, const int32_t* context_lens,
+                                 int32_t S, int32_t Hq, int32_t Hkv, int32_t d, int32_t bs,
+                                 int32_t P, int32_t max_blocks, int32_t max_context_len,
+                                 float softmax_scale, float k_scale, float v_scale,
+                                 float k_inv_scale, float v_inv_scale,
+                                 pkv_dtype q_dtype, pkv_dtype cache_dtype,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Bytes of workspace pkv_paged_multi_query_attn needs: R + 2 * S * Hkv * n_qg * 4
  * with G = Hq/Hkv, qgs = min(n_q, max(1, 16 / G)) queries per pass,
  * n_qg = ceil(n_q / qgs) passes and R = 2 * 4096 * G * qgs * (d + 2) * 4 rounded

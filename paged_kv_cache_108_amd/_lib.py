@@ -37,6 +37,9 @@ SIGNATURES = {
     "pkv_version": (ctypes.c_char_p, []),
     "pkv_kv_cache_write": (ctypes.c_int, [c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32,
                                           c_i32, ctypes.c_int, ctypes.c_int, c_f32, c_f32, c_vp]),
+    "pkv_paged_decode_step": (ctypes.c_int, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_i32,
+                                             c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_f32, c_f32, c_f32,
+                                             c_f32, c_f32, ctypes.c_int, ctypes.c_int, c_vp, c_sz, c_vp]),
     "pkv_paged_multi_query_attn_workspace_size": (c_sz, [c_i32, c_i32, c_i32, c_i32, c_i32]),
     "pkv_paged_multi_query_attn": (ctypes.c_int, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_i32, c_i32,
                                                   c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_f32, c_f32,

@@ -15,7 +15,8 @@ from ._lib import (lib, check, PkvError, PkvStats, PKV_F32, PKV_BF16, PKV_FP8_E4
                    PKV_E_NO_BLOCKS, P_i32, P_i64, P_f64, c_vp, c_i64, c_i32, c_f64)
 
 __all__ = [
-    "kv_cache_write", "copy_blocks", "paged_decode_attn", "paged_decode_attn_workspace_size",
+    "kv_cache_write", "copy_blocks", "paged_decode_attn", "paged_decode_step",
+    "paged_decode_attn_workspace_size",
     "paged_decode_attn_workspace", "paged_multi_query_attn", "paged_multi_query_attn_workspace",
     "Allocator",
     "slots_from_tables", "waste_stats", "block_hashes", "last_error", "version", "quantise_pool",
@@ -143,6 +144,37 @@ def paged_decode_attn(out, q, k_cache, v_cache, block_tables, context_lens, *, m
         S, Hq, Hkv, d, bs, P, block_tables.shape[1], int(max_context_len),
         float(softmax_scale), float(k_scale), float(v_scale), _dtype_code(q),
         _dtype_code(k_cache), int(partition_size), ws_ptr, ws_bytes, _stream(stream)))
+
+
+def paged_decode_step(out, q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, *,
+                      max_context_len, softmax_scale, k_scale=1.0, v_scale=1.0, k_inv_scale=1.0,
+                      v_inv_scale=1.0, workspace=None, stream=None):
+    """pkv_paged_decode_step: write each sequence's new token (k_new, v_new
+    [S][Hkv][d]) at position L_i - 1 and attend, in one launch. Same result as
+    kv_cache_write followed by paged_decode_attn with the balanced split."""
+    import torch
+    S, Hq, d = q.shape
+    P, Hkv, bs, _ = k_cache.shape
+    if tuple(out.shape) != (S, Hq, d) or out.dtype != torch.float32:
+        raise ValueError("paged_decode_step: out must be float32 [S][Hq][d]")
+    if tuple(k_new.shape) != (S, Hkv, d) or tuple(v_new.shape) != (S, Hkv, d):
+        raise ValueError("paged_decode_step: k_new/v_new must be [S][Hkv][d]")
+    if tuple(v_cache.shape) != (P, Hkv, d, bs):
+        raise ValueError("paged_decode_step: v_cache shape")
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise ValueError("paged_decode_step: tables and lengths must be int32")
+    if block_tables.shape[0] != S or context_lens.shape != (S,):
+        raise ValueError("paged_decode_step: tables/lengths shape mismatch")
+    if workspace is None:
+        workspace = paged_decode_attn_workspace(S, Hq, Hkv, d, int(max_context_len),
+                                                PKV_PARTITION_BALANCED, device=q.device)
+    check(lib().pkv_paged_decode_step(
+        _dev(out, "out"), _dev(q, "q"), _dev(k_new, "k_new"), _dev(v_new, "v_new"),
+        _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dev(block_tables, "block_tables"),
+        _dev(context_lens, "context_lens"), S, Hq, Hkv, d, bs, P, block_tables.shape[1],
+        int(max_context_len), float(softmax_scale), float(k_scale), float(v_scale),
+        float(k_inv_scale), float(v_inv_scale), _dtype_code(q), _dtype_code(k_cache),
+        _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
 def paged_multi_query_attn_workspace(S, n_q, Hq, Hkv, d, device="cuda"):

@@ -214,6 +214,9 @@ struct AttnParams {
     int qgs;               // queries per query group (G * qgs <= 16 columns)
     int n_qg;              // query groups per (sequence, kv head)
     int cols;              // MFMA columns in use: G * qgs; partial records hold this many rows
+    const void* k_new;     // decode step: sequence i's new token [S][Hkv][D] (src dtype)
+    const void* v_new;
+    float k_inv, v_inv;    // decode step, fp8 cache: inverse scales of the write
     float qk_scale;        // softmax_scale * k_scale * log2(e): scores in the log2 domain
     float v_scale;
 };
@@ -442,6 +445,81 @@ __device__ __forceinline__ void load_q_row(const AttnParams& p, size_t row, bool
             val = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.q) + qoff + c);
         if (!live) val = QF{};
         qf[x] = val;
+    }
+}
+
+// The new token's K row and V values of one (sequence, kv head), in the
+// chunk fragments' register layout and already in the cache's encoding
+// (the write's): nk like Frag::k for the lane's channels, nv[s] the value of
+// channel 16s + r16 (bits of an f32, a bf16 or an E4M3 code).
+template <int KV, int D> struct NewTok;
+template <int D> struct NewTok<KV_F32, D> { float4 k[D / 16]; uint32_t v[D / 16]; };
+template <int D> struct NewTok<KV_BF16, D> { uint4 k[D / 32]; uint32_t v[D / 16]; };
+template <int D> struct NewTok<KV_FP8, D> { uint4 k[D / 64]; uint32_t v[D / 16]; };
+
+template <int KV, int D>
+__device__ __forceinline__ void load_new_token(const AttnParams& p, size_t row, int r16, int j4,
+                                               NewTok<KV, D>& nt) {
+    if constexpr (KV == KV_F32) {
+        const float* kn = static_cast<const float*>(p.k_new) + row;
+        const float* vn = static_cast<const float*>(p.v_new) + row;
+#pragma unroll
+        for (int x = 0; x < D / 16; ++x) nt.k[x] = *reinterpret_cast<const float4*>(kn + 16 * x + 4 * j4);
+#pragma unroll
+        for (int s = 0; s < D / 16; ++s) nt.v[s] = __float_as_uint(vn[16 * s + r16]);
+    } else if constexpr (KV == KV_BF16) {
+        const uint16_t* kn = static_cast<const uint16_t*>(p.k_new) + row;
+        const uint16_t* vn = static_cast<const uint16_t*>(p.v_new) + row;
+#pragma unroll
+        for (int x = 0; x < D / 32; ++x) nt.k[x] = *reinterpret_cast<const uint4*>(kn + 32 * x + 8 * j4);
+#pragma unroll
+        for (int s = 0; s < D / 16; ++s) nt.v[s] = vn[16 * s + r16];
+    } else {
+        const uint16_t* kn = static_cast<const uint16_t*>(p.k_new) + row;
+        const uint16_t* vn = static_cast<const uint16_t*>(p.v_new) + row;
+#pragma unroll
+        for (int x = 0; x < D / 64; ++x) {
+            const uint4 lo = *reinterpret_cast<const uint4*>(kn + 64 * x + 16 * j4);
+            const uint4 hi = *reinterpret_cast<const uint4*>(kn + 64 * x + 16 * j4 + 8);
+            const uint32_t w[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+            uint32_t c[4] = {0, 0, 0, 0};
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const uint16_t b = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+                c[e >> 2] |= e4m3_encode(bf16_bits_to_f32(b) * p.k_inv) << (8 * (e & 3));
+            }
+            nt.k[x] = make_uint4(c[0], c[1], c[2], c[3]);
+        }
+#pragma unroll
+        for (int s = 0; s < D / 16; ++s) nt.v[s] = e4m3_encode(bf16_bits_to_f32(vn[16 * s + r16]) * p.v_inv);
+    }
+}
+
+// Put the new token (chunk row rr) into a loaded chunk fragment.
+template <int KV, int D>
+__device__ __forceinline__ void patch_new_token(Frag<KV, D>& f, const NewTok<KV, D>& nt, int rr,
+                                                int r16, int j4) {
+    if (r16 == rr) {
+#pragma unroll
+        for (int x = 0; x < (int)(sizeof(nt.k) / sizeof(nt.k[0])); ++x) f.k[x] = nt.k[x];
+    }
+    if (j4 == (rr >> 2)) {
+        const int e = rr & 3;
+#pragma unroll
+        for (int s = 0; s < D / 16; ++s) {
+            if constexpr (KV == KV_F32) {
+                const float v = __uint_as_float(nt.v[s]);
+                if (e == 0) f.v[s].x = v; else if (e == 1) f.v[s].y = v;
+                else if (e == 2) f.v[s].z = v; else f.v[s].w = v;
+            } else if constexpr (KV == KV_BF16) {
+                uint32_t& word = (e >> 1) ? f.v[s].y : f.v[s].x;
+                const int sh = 16 * (e & 1);
+                word = (word & ~(0xFFFFu << sh)) | (nt.v[s] << sh);
+            } else {
+                const int sh = 8 * e;
+                f.v[s] = (f.v[s] & ~(0xFFu << sh)) | (nt.v[s] << sh);
+            }
+        }
     }
 }
 
@@ -798,9 +876,13 @@ paged_attn_partition_kernel(AttnParams p) {
 // segment's first chunk writes the segment's descriptor (first record, record
 // count) for the merge kernel. Launched one workgroup per compute unit (one
 // wave per SIMD), so the kernel may use the whole register file.
-template <int KV, int D, int BS, bool MQ>
+enum StreamMode { SM_DECODE = 0, SM_WINDOW = 1, SM_STEP = 2 };
+
+template <int KV, int D, int BS, int MODE>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1)))
 paged_attn_stream_kernel(AttnParams p) {
+    constexpr bool MQ = MODE == SM_WINDOW;     // a window of queries per sequence
+    constexpr bool STEP = MODE == SM_STEP;     // decode with this step's write fused in
     extern __shared__ float smem[];           // the length cache (p.cache_lens)
     __shared__ int pre[kThreads + 1];
     __shared__ int wsum[kWaves];
@@ -833,7 +915,52 @@ paged_attn_stream_kernel(AttnParams p) {
     const unsigned v_beg = split.start(w);
     const unsigned v_end = split.start(w + 1);
     const int n_pos = (int)(v_end - v_beg);
-    if (n_pos <= 0) return;                   // no barriers below: waves are independent
+
+    // Decode step: this wave's share of the write of every sequence's new token
+    // (position L - 1): part q = (sequence, kv head, K or V), parts w, w + W, ...
+    // Lane l handles channels l and l + 64. The reads are issued here and the
+    // stores after the first window's table reads have returned.
+    auto write_parts = [&](auto&& between) {
+        constexpr int NCH = D / 64;
+        const int n_parts = STEP ? p.S * p.Hkv * 2 : 0;
+        for (int q0 = (int)w; q0 < n_parts; q0 += (int)W) {
+            const int i = q0 / (2 * p.Hkv);
+            const int rem = q0 - i * 2 * p.Hkv;
+            const int g = rem >> 1;
+            const bool is_v = rem & 1;
+            const int L = seq_len(i);
+            if (L <= 0) continue;
+            const int pos = L - 1;
+            const int b = min(max(p.tables[(size_t)i * p.max_blocks + pos / BS], 0), p.P - 1);
+            const int o = pos % BS;
+            const size_t src_row = ((size_t)i * p.Hkv + g) * D;
+            uint32_t val[NCH];
+#pragma unroll
+            for (int u = 0; u < NCH; ++u) {
+                const int c = lane + 64 * u;
+                if constexpr (KV == KV_F32)
+                    val[u] = __float_as_uint(static_cast<const float*>(is_v ? p.v_new : p.k_new)[src_row + c]);
+                else
+                    val[u] = static_cast<const uint16_t*>(is_v ? p.v_new : p.k_new)[src_row + c];
+            }
+            if (q0 == (int)w) between();
+#pragma unroll
+            for (int u = 0; u < NCH; ++u) {
+                const int c = lane + 64 * u;
+                const size_t dst = is_v ? (((size_t)b * p.Hkv + g) * D + c) * BS + o
+                                        : (((size_t)b * p.Hkv + g) * BS + o) * D + c;
+                void* pool = const_cast<void*>(is_v ? p.v : p.k);
+                if constexpr (KV == KV_F32) static_cast<float*>(pool)[dst] = __uint_as_float(val[u]);
+                else if constexpr (KV == KV_BF16) static_cast<uint16_t*>(pool)[dst] = (uint16_t)val[u];
+                else static_cast<uint8_t*>(pool)[dst] =
+                         (uint8_t)e4m3_encode(bf16_bits_to_f32((uint16_t)val[u]) * (is_v ? p.v_inv : p.k_inv));
+            }
+        }
+    };
+    if (n_pos <= 0) {                         // no barriers below: waves are independent
+        if constexpr (STEP) write_parts([] {});
+        return;
+    }
     // position v -> segment (i * HS + kv head * n_qg + query group) and chunk
     // index (< 0: a cost position)
     auto locate = [&](unsigned v, int& seg, int& kc, int& L) {
@@ -893,6 +1020,8 @@ paged_attn_stream_kernel(AttnParams p) {
         mvo = x >> 24;
     };
     fetch_window(0);
+    bool window_done = false;
+    if constexpr (STEP) write_parts([&] { compact_window(); window_done = true; });
     // this wave's last chunk: its last position, or the one before a trailing
     // cost position
     int last_seg, last_kc;
@@ -907,10 +1036,11 @@ paged_attn_stream_kernel(AttnParams p) {
     }
     const unsigned v_last = last_kc >= 0 ? v_end - 1 : v_end - 2 - (unsigned)(last_kc + kSegCost);
 
-    compact_window();
+    if (!window_done) compact_window();
 
     using QF = typename QFragT<KV>::T;
     QF qf[q_loads<KV, D>()];
+    NewTok<KV, D> nt;                         // decode step: the segment's new token
     f32x4 o[D / 16];
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) o[s] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -956,6 +1086,7 @@ paged_attn_stream_kernel(AttnParams p) {
             started = true;
             if (kc == 0 || first) {               // a segment starts
                 load_q_row<KV, D>(p, out_row, live, j4, qf);
+                if constexpr (STEP) load_new_token<KV, D>(p, ((size_t)i * p.Hkv + g) * D, r16, j4, nt);
                 seg_from_start = kc == 0;
                 seg_at_range_start = first;
                 if (kc == 0 && lane == 0) {       // descriptor for the merge kernel
@@ -965,6 +1096,10 @@ paged_attn_stream_kernel(AttnParams p) {
                 }
             }
             const int tc = 16 * kc;
+            // the write of position L - 1 runs concurrently: take its value
+            // from the new token instead of the pool
+            if constexpr (STEP)
+                if (kc == nch - 1) patch_new_token<KV, D>(f, nt, L - 1 - tc, r16, j4);
             const f32x4 sc = chunk_scores<KV, D>(f, qf);
             const bool tail = tc + 16 > L;        // tokens >= L hold no data
             // query j sees tokens < L - n_q + 1 + j (causal inside the window)
@@ -1173,7 +1308,7 @@ AttnKernel pick_d(int d, int bs) {
     return d == 64 ? pick_bs<KV, 64>(bs) : pick_bs<KV, 128>(bs);
 }
 
-template <int KV, int D, bool MQ>
+template <int KV, int D, int MQ>
 AttnKernel pick_stream_bs(int bs) {
     switch (bs) {
         case 8: return paged_attn_stream_kernel<KV, D, 8, MQ>;
@@ -1186,9 +1321,10 @@ AttnKernel pick_stream_bs(int bs) {
 }
 
 template <int KV>
-AttnKernel pick_stream(int d, int bs, bool mq) {
-    if (mq) return d == 64 ? pick_stream_bs<KV, 64, true>(bs) : pick_stream_bs<KV, 128, true>(bs);
-    return d == 64 ? pick_stream_bs<KV, 64, false>(bs) : pick_stream_bs<KV, 128, false>(bs);
+AttnKernel pick_stream(int d, int bs, int mode) {
+    if (mode == SM_WINDOW) return d == 64 ? pick_stream_bs<KV, 64, SM_WINDOW>(bs) : pick_stream_bs<KV, 128, SM_WINDOW>(bs);
+    if (mode == SM_STEP) return d == 64 ? pick_stream_bs<KV, 64, SM_STEP>(bs) : pick_stream_bs<KV, 128, SM_STEP>(bs);
+    return d == 64 ? pick_stream_bs<KV, 64, SM_DECODE>(bs) : pick_stream_bs<KV, 128, SM_DECODE>(bs);
 }
 
 // Compute units of the current device (cached per device).
@@ -1336,12 +1472,21 @@ size_t attn_workspace_size(int32_t S, int32_t n_q, int32_t Hq, int32_t Hkv, int3
 
 // Validation and launch shared by the single-query and multi-query entry
 // points (n_q > 1 always takes the balanced split).
+// The new tokens a decode step writes (k_new == nullptr: no write).
+struct StepWrite {
+    const void* k_new = nullptr;
+    const void* v_new = nullptr;
+    float k_inv = 1.f, v_inv = 1.f;
+};
+
 pkv_status attn_launch(const char* fn, float* out, const void* q, const void* k_cache,
                        const void* v_cache, const int32_t* block_tables, const int32_t* context_lens,
                        int32_t S, int32_t n_q, int32_t Hq, int32_t Hkv, int32_t d, int32_t bs,
                        int32_t P, int32_t max_blocks, int32_t max_context_len, float softmax_scale,
                        float k_scale, float v_scale, pkv_dtype q_dtype, pkv_dtype cache_dtype,
-                       int32_t partition_size, void* workspace, size_t workspace_bytes, void* stream) {
+                       int32_t partition_size, void* workspace, size_t workspace_bytes, void* stream,
+                       const StepWrite& step = StepWrite()) {
+    const bool is_step = step.k_new != nullptr || step.v_new != nullptr;
     if (S < 0 || Hq <= 0 || Hkv <= 0) return fail(PKV_E_INVALID, "%s: S=%d Hq=%d Hkv=%d", fn, S, Hq, Hkv);
     if (n_q < 1 || n_q > 4096) return fail(PKV_E_INVALID, "%s: n_q=%d outside [1, 4096]", fn, n_q);
     if (Hq % Hkv != 0) return fail(PKV_E_INVALID, "%s: Hq=%d not a multiple of Hkv=%d", fn, Hq, Hkv);
@@ -1365,7 +1510,11 @@ pkv_status attn_launch(const char* fn, float* out, const void* q, const void* k_
     if (!std::isfinite(softmax_scale)) return fail(PKV_E_INVALID, "%s: softmax_scale not finite", fn);
     if (kv == KV_FP8 && !(std::isfinite(k_scale) && std::isfinite(v_scale)))
         return fail(PKV_E_INVALID, "%s: fp8 scales not finite", fn);
+    if (is_step && kv == KV_FP8 && !(std::isfinite(step.k_inv) && std::isfinite(step.v_inv) &&
+                                     step.k_inv > 0.f && step.v_inv > 0.f))
+        return fail(PKV_E_INVALID, "%s: fp8 inverse scales must be finite and > 0", fn);
     if (S == 0) return ok();
+    if (is_step && (!step.k_new || !step.v_new)) return fail(PKV_E_INVALID, "%s: NULL pointer", fn);
     if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
         return fail(PKV_E_INVALID, "%s: NULL pointer", fn);
     const QueryGroups qgr = query_groups(n_q, G);
@@ -1405,6 +1554,10 @@ pkv_status attn_launch(const char* fn, float* out, const void* q, const void* k_
     prm.part_tokens = partition_size > 0 ? partition_size : ((max(max_context_len, 1) + 31) / 32) * 32;
     prm.n_part = (int)n_part;
     prm.balanced = balanced ? 1 : 0;
+    prm.k_new = step.k_new;
+    prm.v_new = step.v_new;
+    prm.k_inv = step.k_inv;
+    prm.v_inv = step.v_inv;
     const float ks = kv == KV_FP8 ? k_scale : 1.f;
     prm.qk_scale = softmax_scale * ks * kLog2e;
     prm.v_scale = kv == KV_FP8 ? v_scale : 1.f;
@@ -1413,9 +1566,9 @@ pkv_status attn_launch(const char* fn, float* out, const void* q, const void* k_
     AttnKernel kern;
     size_t lds;
     if (balanced) {
-        const bool mq = n_q > 1;
-        kern = kv == KV_F32 ? pick_stream<KV_F32>(d, bs, mq)
-             : kv == KV_BF16 ? pick_stream<KV_BF16>(d, bs, mq) : pick_stream<KV_FP8>(d, bs, mq);
+        const int mode = is_step ? SM_STEP : n_q > 1 ? SM_WINDOW : SM_DECODE;
+        kern = kv == KV_F32 ? pick_stream<KV_F32>(d, bs, mode)
+             : kv == KV_BF16 ? pick_stream<KV_BF16>(d, bs, mode) : pick_stream<KV_FP8>(d, bs, mode);
         lds = (size_t)(prm.cache_lens ? S : 0) * sizeof(int);
     } else {
         kern = kv == KV_F32 ? pick_d<KV_F32>(d, bs)
@@ -1494,4 +1647,24 @@ extern "C" pkv_status pkv_paged_multi_query_attn(float* out, const void* q, cons
                        n_q, Hq, Hkv, d, bs, P, max_blocks, max_context_len, softmax_scale, k_scale,
                        v_scale, q_dtype, cache_dtype, PKV_PARTITION_BALANCED, workspace, workspace_bytes,
                        stream);
+}
+
+extern "C" pkv_status pkv_paged_decode_step(float* out, const void* q, const void* k_new,
+                                            const void* v_new, void* k_cache, void* v_cache,
+                                            const int32_t* block_tables, const int32_t* context_lens,
+                                            int32_t S, int32_t Hq, int32_t Hkv, int32_t d, int32_t bs,
+                                            int32_t P, int32_t max_blocks, int32_t max_context_len,
+                                            float softmax_scale, float k_scale, float v_scale,
+                                            float k_inv_scale, float v_inv_scale, pkv_dtype q_dtype,
+                                            pkv_dtype cache_dtype, void* workspace,
+                                            size_t workspace_bytes, void* stream) {
+    StepWrite w;
+    w.k_new = k_new;
+    w.v_new = v_new;
+    w.k_inv = cache_dtype == PKV_FP8_E4M3 ? k_inv_scale : 1.f;
+    w.v_inv = cache_dtype == PKV_FP8_E4M3 ? v_inv_scale : 1.f;
+    if (S > 0 && (!k_new || !v_new)) return fail(PKV_E_INVALID, "paged_decode_step: NULL pointer");
+    return attn_launch("paged_decode_step", out, q, k_cache, v_cache, block_tables, context_lens, S, 1,
+                       Hq, Hkv, d, bs, P, max_blocks, max_context_len, softmax_scale, k_scale, v_scale,
+                       q_dtype, cache_dtype, PKV_PARTITION_BALANCED, workspace, workspace_bytes, stream, w);
 }

@@ -108,6 +108,22 @@ class DeviceStep:
         return out
 
 
+def device_decode_step(dev, out=None):
+    """One fused pkv_paged_decode_step on a DeviceStep's buffers (write + attend)."""
+    import torch
+    w = dev.w
+    s = w.spec
+    out = dev.out if out is None else out
+    ws = pkv.paged_decode_attn_workspace(s.S, s.Hq, s.Hkv, s.d, w.max_context_len,
+                                         pkv.PKV_PARTITION_BALANCED)
+    pkv.paged_decode_step(out, dev.q, dev.k_new, dev.v_new, dev.k_cache, dev.v_cache, dev.tables,
+                          dev.lens, max_context_len=w.max_context_len, softmax_scale=w.softmax_scale,
+                          k_scale=w.k_scale, v_scale=w.v_scale, k_inv_scale=w.k_inv_scale,
+                          v_inv_scale=w.v_inv_scale, workspace=ws)
+    torch.cuda.synchronize()
+    return out
+
+
 def oracle_step(w, seqs=None):
     """The oracle's write then attention for a workload (non-fp8 caches)."""
     s = w.spec

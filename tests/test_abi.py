@@ -343,3 +343,19 @@ def test_prefix_allocator_matches_twin(seed, P, bs):
     assert a.prefix_stats()["hit_blocks"] > 0
     sa, st = a.stats(), t.stats()
     assert sa["free_blocks"] == st["free_blocks"] and sa["tokens_stored"] == st["tokens_stored"]
+
+
+def test_decode_step_rejects_invalid_arguments():
+    lib = pkv.lib()
+
+    def step(**kw):
+        a = dict(kn=FAKE, vn=FAKE, cd=1, qd=1, ki=1.0, vi=1.0, wsb=1 << 30)
+        a.update(kw)
+        return lib.pkv_paged_decode_step(FAKE, FAKE, a["kn"], a["vn"], FAKE, FAKE, FAKE, FAKE, 4, 8, 2,
+                                         128, 16, 100, 10, 160, 0.1, 1.0, 1.0, a["ki"], a["vi"],
+                                         a["qd"], a["cd"], FAKE, a["wsb"], None)
+    assert step(kn=None) == _lib.PKV_E_INVALID
+    assert step(vn=None) == _lib.PKV_E_INVALID
+    assert step(cd=2, ki=0.0) == _lib.PKV_E_INVALID
+    assert step(cd=2, vi=float("inf")) == _lib.PKV_E_INVALID
+    assert step(wsb=16) == _lib.PKV_E_WORKSPACE
