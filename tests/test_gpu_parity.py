@@ -515,3 +515,26 @@ def test_decode_step_edge_shapes():
                                      ([1, 64, 65, 300], 8, 2, 128, 64, "bf16")]:
         _step_case(W.make_custom(lens=lens, Hq=Hq, Hkv=Hkv, d=d, bs=bs, q_dtype=dt, cache_dtype=dt,
                                  cfg=970 + len(lens) + Hq))
+
+
+
+def test_balanced_workspace_reuse_any_contents():
+    # One workspace serves calls of any shapes in any order, whatever it held
+    # before: here it starts filled with random bytes and the calls change
+    # shape, so each call's records and descriptors land on the previous
+    # call's data.
+    torch = need_gpu()
+    ws = torch.randint(0, 256, (96 << 20,), dtype=torch.uint8, device="cuda")
+    for name, kw in [("small", {}), ("llama8b", {}), ("tiny", {}), ("beam", {"bs": 8}), ("small", {})]:
+        w = W.make(name, **kw)
+        print(f"[case] reuse {name}", flush=True)
+        dev = DeviceStep(w)
+        dev.write()
+        want = to_host(dev.attend(BAL)).copy()
+        for _ in range(2):
+            out = torch.empty_like(dev.out)
+            pkv.paged_decode_attn(out, dev.q, dev.k_cache, dev.v_cache, dev.tables, dev.lens,
+                                  max_context_len=w.max_context_len, softmax_scale=w.softmax_scale,
+                                  partition_size=BAL, workspace=ws)
+            torch.cuda.synchronize()
+            assert np.array_equal(to_host(out), want)
