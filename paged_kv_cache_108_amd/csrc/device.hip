@@ -1200,14 +1200,18 @@ paged_attn_merge_kernel(AttnParams p) {
     const int g = head / p.G;
     const int qg = j / p.qgs;
     const int r = (j - qg * p.qgs) * p.G + (head - g * p.G);     // column of this row
+    // the length and (balanced) the segment's descriptor are read together:
+    // one memory round trip before the records
+    const int seg = (i * p.Hkv + g) * p.n_qg + qg;
+    int2 dsc = make_int2(0, 0);
+    if (balanced) dsc = *reinterpret_cast<const int2*>(p.desc + 2 * seg);
     const int L = min(p.lens[i], p.max_len);
     if (L <= 0) return;
     int n, rec0;                              // records rec0 .. (see below), n of them
     long long w_lo = 0;
     if (balanced) {
-        const int seg = (i * p.Hkv + g) * p.n_qg + qg;
-        rec0 = p.desc[2 * seg];
-        n = p.desc[2 * seg + 1];
+        rec0 = dsc.x;
+        n = dsc.y;
         if (n <= 1) return;                   // one wave wrote the rows
         w_lo = rec0 >> 1;
     } else {
