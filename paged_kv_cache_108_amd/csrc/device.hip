@@ -75,22 +75,20 @@ enum KvKind { KV_F32 = 0, KV_BF16 = 1, KV_FP8 = 2 };
 
 // OCP E4M3 encoder written from the format definition: round to nearest,
 // ties to even mantissa, |y| > 448 (and infinities) saturate to 448, NaN keeps
-// its sign with the all-ones code, zero keeps its sign.
+// its sign with the all-ones code, zero keeps its sign. Both candidate codes
+// (subnormal and normal) are formed and one is selected, so the encoder has
+// no branches.
 __device__ __forceinline__ uint32_t e4m3_encode(float y) {
-    const uint32_t u = __float_as_uint(y);
-    const uint32_t sign = (u >> 24) & 0x80u;
-    const float a = fabsf(y);
-    if (!(a == a)) return sign | 0x7Fu;
-    if (a > 448.0f) return sign | 0x7Eu;
-    if (a < 0.015625f) {                        // below 2^-6: subnormal quantum 2^-9
-        const float q = rintf(a * 512.0f);      // exact scaling, round half to even
-        return sign | (uint32_t)q;              // q == 8 is the smallest normal, code 0x08
-    }
+    const uint32_t sign = (__float_as_uint(y) >> 24) & 0x80u;
+    const float a = fminf(fabsf(y), 448.0f);    // saturate first: 448 is code 0x7E
+    // below 2^-6 the quantum is 2^-9: exact scaling, round half to even; the
+    // count 8 is the smallest normal, code 0x08
+    const uint32_t sub = (uint32_t)rintf(a * 512.0f);
     uint32_t ua = __float_as_uint(a);
     ua += 0x7FFFFu + ((ua >> 20) & 1u);         // round the 23-bit mantissa to 3 bits, RNE
-    const uint32_t e = (ua >> 23) - 120u;       // rebias 127 -> 7
-    const uint32_t m = (ua >> 20) & 7u;
-    return sign | (e << 3) | m;
+    const uint32_t nrm = (((ua >> 23) - 120u) << 3) | ((ua >> 20) & 7u);   // rebias 127 -> 7
+    const uint32_t code = a < 0.015625f ? sub : nrm;
+    return sign | (y != y ? 0x7Fu : code);
 }
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
@@ -451,7 +449,8 @@ __device__ __forceinline__ void load_q_row(const AttnParams& p, size_t row, bool
 // The new token's K row and V values of one (sequence, kv head), in the
 // chunk fragments' register layout and already in the cache's encoding
 // (the write's): nk like Frag::k for the lane's channels, nv[s] the value of
-// channel 16s + r16 (bits of an f32, a bf16 or an E4M3 code).
+// channel 16s + r16 (bits of an f32, a bf16 or an E4M3 code). `stage` is the
+// wave's LDS staging area of D/2 words, used by the fp8 encoding.
 template <int KV, int D> struct NewTok;
 template <int D> struct NewTok<KV_F32, D> { float4 k[D / 16]; uint32_t v[D / 16]; };
 template <int D> struct NewTok<KV_BF16, D> { uint4 k[D / 32]; uint32_t v[D / 16]; };
@@ -459,7 +458,7 @@ template <int D> struct NewTok<KV_FP8, D> { uint4 k[D / 64]; uint32_t v[D / 16];
 
 template <int KV, int D>
 __device__ __forceinline__ void load_new_token(const AttnParams& p, size_t row, int r16, int j4,
-                                               NewTok<KV, D>& nt) {
+                                               uint32_t* stage, NewTok<KV, D>& nt) {
     if constexpr (KV == KV_F32) {
         const float* kn = static_cast<const float*>(p.k_new) + row;
         const float* vn = static_cast<const float*>(p.v_new) + row;
@@ -475,23 +474,30 @@ __device__ __forceinline__ void load_new_token(const AttnParams& p, size_t row, 
 #pragma unroll
         for (int s = 0; s < D / 16; ++s) nt.v[s] = vn[16 * s + r16];
     } else {
-        const uint16_t* kn = static_cast<const uint16_t*>(p.k_new) + row;
-        const uint16_t* vn = static_cast<const uint16_t*>(p.v_new) + row;
-#pragma unroll
-        for (int x = 0; x < D / 64; ++x) {
-            const uint4 lo = *reinterpret_cast<const uint4*>(kn + 64 * x + 16 * j4);
-            const uint4 hi = *reinterpret_cast<const uint4*>(kn + 64 * x + 16 * j4 + 8);
-            const uint32_t w[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-            uint32_t c[4] = {0, 0, 0, 0};
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const uint16_t b = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
-                c[e >> 2] |= e4m3_encode(bf16_bits_to_f32(b) * p.k_inv) << (8 * (e & 3));
-            }
-            nt.k[x] = make_uint4(c[0], c[1], c[2], c[3]);
+        // encode cooperatively: lane l turns channels 4l..4l+3 of the row
+        // [K | V] (2D codes) into one word of the wave's staging area, then
+        // every lane reads back what its fragment layout needs
+        const int lane = 16 * j4 + r16;
+        if (lane < D / 2) {
+            const int c0 = 4 * lane;
+            const bool is_v = c0 >= D;
+            const uint16_t* src = static_cast<const uint16_t*>(is_v ? p.v_new : p.k_new) + row +
+                                  (is_v ? c0 - D : c0);
+            const uint2 w = *reinterpret_cast<const uint2*>(src);
+            const float inv = is_v ? p.v_inv : p.k_inv;
+            stage[lane] = e4m3_encode(bf16_bits_to_f32((uint16_t)w.x) * inv) |
+                          e4m3_encode(bf16_bits_to_f32((uint16_t)(w.x >> 16)) * inv) << 8 |
+                          e4m3_encode(bf16_bits_to_f32((uint16_t)w.y) * inv) << 16 |
+                          e4m3_encode(bf16_bits_to_f32((uint16_t)(w.y >> 16)) * inv) << 24;
         }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
-        for (int s = 0; s < D / 16; ++s) nt.v[s] = e4m3_encode(bf16_bits_to_f32(vn[16 * s + r16]) * p.v_inv);
+        for (int x = 0; x < D / 64; ++x) nt.k[x] = *reinterpret_cast<const uint4*>(stage + 16 * x + 4 * j4);
+#pragma unroll
+        for (int s = 0; s < D / 16; ++s)
+            nt.v[s] = (stage[D / 4 + 4 * s + (r16 >> 2)] >> (8 * (r16 & 3))) & 0xFFu;
     }
 }
 
@@ -887,6 +893,7 @@ paged_attn_stream_kernel(AttnParams p) {
     __shared__ int pre[kThreads + 1];
     __shared__ int wsum[kWaves];
     __shared__ int wmeta[kWaves][4][64];      // per wave: compacted chunk metadata of a window
+    __shared__ __align__(16) uint32_t ntstage[kWaves][D / 2];   // per wave: fp8 new-token codes
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int r16 = lane & 15;
@@ -1086,7 +1093,7 @@ paged_attn_stream_kernel(AttnParams p) {
             started = true;
             if (kc == 0 || first) {               // a segment starts
                 load_q_row<KV, D>(p, out_row, live, j4, qf);
-                if constexpr (STEP) load_new_token<KV, D>(p, ((size_t)i * p.Hkv + g) * D, r16, j4, nt);
+                if constexpr (STEP) load_new_token<KV, D>(p, ((size_t)i * p.Hkv + g) * D, r16, j4, ntstage[wave], nt);
                 seg_from_start = kc == 0;
                 seg_at_range_start = first;
                 if (kc == 0 && lane == 0) {       // descriptor for the merge kernel
