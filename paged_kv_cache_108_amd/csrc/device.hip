@@ -63,11 +63,20 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int kWaves = PKV_WAVES;         // waves per workgroup
 constexpr int kThreads = kWaves * 64;
 constexpr int kMaxCachedLens = 4096;      // sequences whose lengths a workgroup keeps in LDS
-constexpr int kMaxWorkers = 4096;
-constexpr int kSegCost = 1;               // balanced split: positions a segment costs beyond its chunks         // waves of the balanced split, at most (sizes its workspace)
+constexpr int kMaxWorkers = 4096;         // waves of the balanced split, at most (sizes its workspace)
 constexpr float kLog2e = 1.4426950408889634f;
 
 enum KvKind { KV_F32 = 0, KV_BF16 = 1, KV_FP8 = 2 };
+
+// Balanced split: positions a segment costs beyond its chunks. Starting and
+// finishing a segment costs about one memory round trip, which is one chunk
+// time for 8 KiB chunks (bf16 at d 128) and proportionally more chunks for
+// smaller ones.
+__host__ __device__ constexpr int seg_cost(int kv, int d) {
+    const int chunk_bytes = 16 * 2 * d * (kv == KV_F32 ? 4 : kv == KV_BF16 ? 2 : 1);
+    return chunk_bytes >= 8192 ? 1 : 8192 / chunk_bytes;
+}
+constexpr int kSegCostMax = seg_cost(KV_FP8, 64);
 
 // ----------------------------------------------------------------------------
 // Small device helpers
@@ -503,7 +512,11 @@ __device__ __forceinline__ void load_new_token(const AttnParams& p, size_t row, 
             const uint16_t* src = static_cast<const uint16_t*>(is_v ? p.v_new : p.k_new) + row +
                                   (is_v ? c0 - D : c0);
             const uint2 w = *reinterpret_cast<const uint2*>(src);
-            const float inv = is_v ? p.v_inv : p.k_inv;
+            // both scales as scalars first: a lane-dependent choice between
+            // the two parameters would otherwise become a per-lane load
+            float k_inv = p.k_inv, v_inv = p.v_inv;
+            asm volatile("" : "+s"(k_inv), "+s"(v_inv));
+            const float inv = is_v ? v_inv : k_inv;
             stage[lane] = e4m3_encode(bf16_bits_to_f32((uint16_t)w.x) * inv) |
                           e4m3_encode(bf16_bits_to_f32((uint16_t)(w.x >> 16)) * inv) << 8 |
                           e4m3_encode(bf16_bits_to_f32((uint16_t)w.y) * inv) << 16 |
@@ -891,7 +904,7 @@ paged_attn_partition_kernel(AttnParams p) {
 
 // Balanced split at wave granularity. Work positions run sequence-major, then
 // kv head, then position within the (sequence, kv head) segment: a segment of
-// n chunks has kSegCost + n positions, the first kSegCost standing for the
+// n chunks has seg_cost + n positions, the first seg_cost standing for the
 // fixed cost of starting and finishing a segment (q, the epilogue, the partly
 // filled last chunk). The W = gridDim.x * kWaves waves each take one of W
 // near-equal contiguous ranges of positions and stream the chunks in them
@@ -908,6 +921,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1
 paged_attn_stream_kernel(AttnParams p) {
     constexpr bool MQ = MODE == SM_WINDOW;     // a window of queries per sequence
     constexpr bool STEP = MODE == SM_STEP;     // decode with this step's write fused in
+    constexpr int kSegCost = seg_cost(KV, D);
     extern __shared__ float smem[];           // the length cache (p.cache_lens)
     __shared__ int pre[kThreads + 1];
     __shared__ int wsum[kWaves];
@@ -1554,7 +1568,7 @@ pkv_status attn_launch(const char* fn, float* out, const void* q, const void* k_
         return fail(PKV_E_WORKSPACE, "%s: workspace %zu bytes, need %zu", fn, workspace_bytes, need);
     // upper bound on work items (fixed partitions) or positions (balanced)
     const int64_t n_upper = balanced ? (int64_t)S * Hkv * qgr.n_qg *
-                                           (((int64_t)max_context_len + 15) / 16 + kSegCost)
+                                           (((int64_t)max_context_len + 15) / 16 + kSegCostMax)
                                      : n_part * (int64_t)S * Hkv;
     if (n_upper > 0x7FFFFFFFLL) return fail(PKV_E_INVALID, "%s: too many work items", fn);
 
