@@ -258,7 +258,12 @@ __device__ __forceinline__ int clamp_block(int b, int P) { return min(max(b, 0),
 // Load the K and V fragments of the chunk starting at token `tc` (absolute).
 // b0 is the physical block holding token tc; for bs 8, b1 holds token tc + 8.
 // Streaming loads of the cache: the nontemporal hint marks the lines
-// evict-first, since each K/V byte is read once per call.
+// evict-first, since each K/V byte is read once per call. load_chunk uses it
+// for blocks of at most 16 tokens, where a 16-token chunk reads its blocks
+// whole. With larger blocks a chunk reads part of each V channel row
+// (channel-major [d][bs] tiles) and a later chunk the rest of the line, which
+// must still be cached then; measured on MI355X, hinted loads slow bs 32 and
+// 64 down by 5-30% (K loads included), so those take plain loads.
 __device__ __forceinline__ uint4 ld_stream(const uint4* a) {
     typedef unsigned v4u __attribute__((ext_vector_type(4)));
     const v4u t = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(a));
@@ -275,6 +280,11 @@ __device__ __forceinline__ uint2 ld_stream(const uint2* a) {
     return make_uint2(t.x, t.y);
 }
 __device__ __forceinline__ uint32_t ld_stream(const uint32_t* a) { return __builtin_nontemporal_load(a); }
+template <int BS, typename T>
+__device__ __forceinline__ T ld_kv(const T* a) {
+    if constexpr (BS <= 16) return ld_stream(a);
+    else return *a;
+}
 
 template <int KV, int D, int BS>
 __device__ __forceinline__ void load_chunk(Frag<KV, D>& f, const AttnParams& p, int b0, int b1,
@@ -302,24 +312,24 @@ __device__ __forceinline__ void load_chunk(Frag<KV, D>& f, const AttnParams& p, 
     if constexpr (KV == KV_F32) {
 #pragma unroll
         for (int x = 0; x < D / 16; ++x)
-            f.k[x] = ld_stream(reinterpret_cast<const float4*>(krow + 16 * x + 4 * j4));
+            f.k[x] = ld_kv<BS>(reinterpret_cast<const float4*>(krow + 16 * x + 4 * j4));
 #pragma unroll
         for (int s = 0; s < D / 16; ++s)
-            f.v[s] = ld_stream(reinterpret_cast<const float4*>(vt + (size_t)(16 * s + r16) * BS));
+            f.v[s] = ld_kv<BS>(reinterpret_cast<const float4*>(vt + (size_t)(16 * s + r16) * BS));
     } else if constexpr (KV == KV_BF16) {
 #pragma unroll
         for (int s = 0; s < D / 32; ++s)
-            f.k[s] = ld_stream(reinterpret_cast<const uint4*>(krow + 32 * s + 8 * j4));
+            f.k[s] = ld_kv<BS>(reinterpret_cast<const uint4*>(krow + 32 * s + 8 * j4));
 #pragma unroll
         for (int s = 0; s < D / 16; ++s)
-            f.v[s] = ld_stream(reinterpret_cast<const uint2*>(vt + (size_t)(16 * s + r16) * BS));
+            f.v[s] = ld_kv<BS>(reinterpret_cast<const uint2*>(vt + (size_t)(16 * s + r16) * BS));
     } else {
 #pragma unroll
         for (int x = 0; x < D / 64; ++x)
-            f.k[x] = ld_stream(reinterpret_cast<const uint4*>(krow + 64 * x + 16 * j4));
+            f.k[x] = ld_kv<BS>(reinterpret_cast<const uint4*>(krow + 64 * x + 16 * j4));
 #pragma unroll
         for (int s = 0; s < D / 16; ++s)
-            f.v[s] = ld_stream(reinterpret_cast<const uint32_t*>(vt + (size_t)(16 * s + r16) * BS));
+            f.v[s] = ld_kv<BS>(reinterpret_cast<const uint32_t*>(vt + (size_t)(16 * s + r16) * BS));
     }
 }
 
