@@ -149,6 +149,113 @@ def cpu_baseline(w, cache_dtype, budget_s=12.0):
     }
 
 
+def _timed(args, torch, fn, flush, stream):
+    """Mean and median event time in ms of fn over args.steps calls (after
+    args.warmup), each preceded by the flush read outside the events."""
+    for _ in range(args.warmup):
+        fn()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    for a, b in ev:
+        if not args.no_flush:
+            flush.max()
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms = [a.elapsed_time(b) for a, b in ev]
+    return statistics.mean(ms), statistics.median(ms), min(ms), wall
+
+
+def run_other_op(args, w, torch, pkv):
+    """--op window / --op copy: one JSON line for that call on workload w."""
+    from paged_kv_cache_108_amd import workloads as W
+    s = w.spec
+    cache_dtype = s.cache_dtype
+
+    def dev(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(a).cuda()
+
+    if cache_dtype == "fp8":
+        vk, vv = dev(w.k_pool), dev(w.v_pool)
+        k_cache = torch.empty(vk.shape, dtype=torch.uint8, device="cuda")
+        v_cache = torch.empty(vv.shape, dtype=torch.uint8, device="cuda")
+        pkv.quantise_pool(vk, vv, k_cache, v_cache, k_inv_scale=w.k_inv_scale,
+                          v_inv_scale=w.v_inv_scale)
+        del vk, vv
+    else:
+        k_cache, v_cache = dev(w.k_pool), dev(w.v_pool)
+    flush = torch.ones(1 << 27, dtype=torch.int64, device="cuda")
+    stream = torch.cuda.current_stream()
+    kv_elem = ELEM[cache_dtype]
+    if args.op == "window":
+        n_q = args.window
+        G = s.Hq // s.Hkv
+        qgs = min(n_q, max(16 // G, 1))
+        n_qg = -(-n_q // qgs)
+        rng = np.random.default_rng([108, 951, n_q])
+        qf = rng.standard_normal((s.S, n_q, s.Hq, s.d)).astype(np.float32)
+        q = dev(qf if s.q_dtype == "f32" else W.to_bf16_bits(qf))
+        tables, lens = dev(w.block_tables), dev(w.context_lens)
+        out = torch.empty((s.S, n_q, s.Hq, s.d), dtype=torch.float32, device="cuda")
+        ws = pkv.paged_multi_query_attn_workspace(s.S, n_q, s.Hq, s.Hkv, s.d)
+
+        def fn():
+            pkv.paged_multi_query_attn(out, q, k_cache, v_cache, tables, lens,
+                                       max_context_len=w.max_context_len,
+                                       softmax_scale=w.softmax_scale, k_scale=w.k_scale,
+                                       v_scale=w.v_scale, workspace=ws, stream=stream)
+        attn, _, _, unique_tokens = algorithmic_bytes(w, cache_dtype)
+        dec_q = s.S * s.Hq * s.d * ELEM[s.q_dtype]
+        dec_out = s.S * s.Hq * s.d * 4
+        once = attn - dec_q - dec_out                 # K/V, tables, lengths: read once
+        byts = once + n_q * (dec_q + dec_out)
+        passes = once * n_qg + n_q * (dec_q + dec_out)
+        metric = "paged multi-query (window) attention: achieved HBM GB/s at 1 GPU"
+        kernel = "paged_multi_query_attn call (stream kernel, window instantiation + merge kernel)"
+        cfg = {"window": n_q, "query_groups_per_pass": qgs, "passes": n_qg,
+               "bytes_with_passes": passes,
+               "note": "value counts K/V once; a window needing several passes reads K/V once per pass "
+                       "(bytes_with_passes)"}
+    else:
+        per_pool = s.Hkv * s.bs * s.d * kv_elem           # one block of one pool
+        n = min(args.pairs, w.P // 2)
+        perm = np.random.default_rng([108, 952]).permutation(w.P)
+        src = torch.from_numpy(perm[:n].astype(np.int32)).cuda()
+        dst = torch.from_numpy(perm[n:2 * n].astype(np.int32)).cuda()
+
+        def fn():
+            pkv.copy_blocks(k_cache, v_cache, src, dst, stream=stream)
+        byts = n * 2 * 2 * per_pool                        # both pools, read + write
+        metric = "copy-on-write block copies: achieved HBM GB/s at 1 GPU"
+        kernel = "copy_blocks call (copy_blocks_kernel)"
+        cfg = {"pairs": n, "bytes_per_pair": 4 * per_pool}
+    mean, med, mn, wall = _timed(args, torch, fn, flush, stream)
+    gbs = byts / (mean * 1e-3) / 1e9
+    print(json.dumps({
+        "metric": metric, "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(mean, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": {"f32": "f32", "bf16": "bf16", "fp8": "fp8-e4m3 KV, bf16 q"}[cache_dtype],
+        "data": "synthetic (seeded)",
+        "config": dict({"workload": f"{s.name}: {s.description}", "block_size": s.bs,
+                        "kv_dtype": cache_dtype, "cache_flush_between_steps": not args.no_flush}, **cfg),
+        "timing": {"ms_mean": round(mean, 5), "ms_median": round(med, 5), "ms_min": round(mn, 5),
+                   "wall_s_timed_region": round(wall, 4)},
+        "bytes": {"algorithmic": int(byts)},
+        "roofline": {"kernel": kernel, "bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None},
+        "device": torch.cuda.get_device_name(0),
+    }), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -167,6 +274,12 @@ def main():
     ap.add_argument("--no-flush", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--op", choices=["step", "window", "copy"], default="step",
+                    help="step: the decode step (default); window: pkv_paged_multi_query_attn over "
+                         "windows of --window queries per sequence; copy: pkv_copy_blocks of --pairs "
+                         "(src, dst) block pairs")
+    ap.add_argument("--window", type=int, default=4, help="queries per sequence for --op window")
+    ap.add_argument("--pairs", type=int, default=1024, help="block pairs for --op copy")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (reference for counter scaling)")
     args = ap.parse_args()
@@ -198,6 +311,9 @@ def main():
 
     w = W.make(args.config, bs=args.bs, cache_dtype=args.kv)
     s = w.spec
+    if args.op != "step":
+        run_other_op(args, w, torch, pkv)
+        return
     cache_dtype = s.cache_dtype
     part = args.partition
     fused = args.step == "fused"
