@@ -198,7 +198,8 @@ def run_other_op(args, w, torch, pkv):
     if args.op == "window":
         n_q = args.window
         G = s.Hq // s.Hkv
-        qgs = min(n_q, max(16 // G, 1))
+        tiles = 1 if n_q * G <= 16 else 2             # 16-column tiles per pass (as the library)
+        qgs = min(n_q, max(16 * tiles // G, 1))
         n_qg = -(-n_q // qgs)
         rng = np.random.default_rng([108, 951, n_q])
         qf = rng.standard_normal((s.S, n_q, s.Hq, s.d)).astype(np.float32)
@@ -220,7 +221,7 @@ def run_other_op(args, w, torch, pkv):
         passes = once * n_qg + n_q * (dec_q + dec_out)
         metric = "paged multi-query (window) attention: achieved HBM GB/s at 1 GPU"
         kernel = "paged_multi_query_attn call (stream kernel, window instantiation + merge kernel)"
-        cfg = {"window": n_q, "query_groups_per_pass": qgs, "passes": n_qg,
+        cfg = {"window": n_q, "column_tiles": tiles, "queries_per_pass": qgs, "passes": n_qg,
                "bytes_with_passes": passes,
                "note": "value counts K/V once; a window needing several passes reads K/V once per pass "
                        "(bytes_with_passes)"}

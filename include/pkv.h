@@ -205,9 +205,10 @@ pkv_status pkv_paged_decode_step(float* out, const void* q, const void* k_new, c
 
 /*
  * Bytes of workspace pkv_paged_multi_query_attn needs: R + 2 * S * Hkv * n_qg * 4
- * with G = Hq/Hkv, qgs = min(n_q, max(1, 16 / G)) queries per pass,
- * n_qg = ceil(n_q / qgs) passes and R = 2 * 4096 * G * qgs * (d + 2) * 4 rounded
- * up to a multiple of 256. Returns 0 for invalid sizes.
+ * with G = Hq/Hkv, T = 1 column tile when n_q * G <= 16 and otherwise T = 2,
+ * qgs = min(n_q, max(1, 16 * T / G)) queries per
+ * pass, n_qg = ceil(n_q / qgs) passes and R = 2 * 4096 * G * qgs * (d + 2) * 4
+ * rounded up to a multiple of 256. Returns 0 for invalid sizes.
  */
 size_t pkv_paged_multi_query_attn_workspace_size(int32_t S, int32_t n_q, int32_t Hq, int32_t Hkv,
                                                  int32_t d);
@@ -233,9 +234,10 @@ size_t pkv_paged_multi_query_attn_workspace_size(int32_t S, int32_t n_q, int32_t
  * pkv_paged_multi_query_attn_workspace_size(S, n_q, Hq, Hkv, d) bytes.
  * Requires 1 <= n_q <= 4096 and, per sequence, L_i >= n_q or L_i <= 0 (zero
  * rows); rows of a query that sees no token are otherwise unspecified.
- * The G query heads of a kv head and up to 16/G queries of the window share
- * each pass over the sequence's blocks (one 16-column MFMA tile); a longer
- * window takes ceil(n_q / qgs) passes.
+ * The G query heads of a kv head and up to qgs queries of the window share
+ * each pass over the sequence's blocks, as T tiles of 16 MFMA columns (T and
+ * qgs as for the workspace size); a longer window takes ceil(n_q / qgs)
+ * passes.
  */
 pkv_status pkv_paged_multi_query_attn(float* out, const void* q,
                                       const void* k_cache, const void* v_cache,

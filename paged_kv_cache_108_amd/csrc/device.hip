@@ -64,6 +64,10 @@ constexpr int kWaves = PKV_WAVES;         // waves per workgroup
 constexpr int kThreads = kWaves * 64;
 constexpr int kMaxCachedLens = 4096;      // sequences whose lengths a workgroup keeps in LDS
 constexpr int kMaxWorkers = 4096;         // waves of the balanced split, at most (sizes its workspace)
+// 16-column tiles per pass for wide query windows. Each tile adds its own
+// q fragment, accumulator and softmax to every chunk: four tiles at d 128
+// spill registers, and four at d 64 made a chunk's compute outlast its load.
+constexpr int wide_tiles(int) { return 2; }
 constexpr float kLog2e = 1.4426950408889634f;
 
 enum KvKind { KV_F32 = 0, KV_BF16 = 1, KV_FP8 = 2 };
@@ -926,10 +930,11 @@ paged_attn_partition_kernel(AttnParams p) {
 // wave per SIMD), so the kernel may use the whole register file.
 enum StreamMode { SM_DECODE = 0, SM_WINDOW = 1, SM_STEP = 2 };
 
-template <int KV, int D, int BS, int MODE>
+template <int KV, int D, int BS, int MODE, int NT>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1)))
 paged_attn_stream_kernel(AttnParams p) {
     constexpr bool MQ = MODE == SM_WINDOW;     // a window of queries per sequence
+    static_assert(NT == 1 || MQ, "several column tiles only for query windows");
     constexpr bool STEP = MODE == SM_STEP;     // decode with this step's write fused in
     constexpr int kSegCost = seg_cost(KV, D);
     extern __shared__ float smem[];           // the length cache (p.cache_lens)
@@ -1088,14 +1093,20 @@ paged_attn_stream_kernel(AttnParams p) {
 
     if (!window_done) compact_window();
 
+    // NT tiles of 16 MFMA columns share every loaded chunk (query windows:
+    // column c = 16t + r16 of tile t is query c / G of the group, head c % G)
     using QF = typename QFragT<KV>::T;
-    QF qf[q_loads<KV, D>()];
+    QF qf[NT][q_loads<KV, D>()];
     NewTok<KV, D> nt;                         // decode step: the segment's new token
-    f32x4 o[D / 16];
+    f32x4 o[NT][D / 16];
+    float m_run[NT], l_run[NT];
 #pragma unroll
-    for (int s = 0; s < D / 16; ++s) o[s] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m_run = -INFINITY;
-    float l_run = 0.f;
+    for (int t = 0; t < NT; ++t) {
+#pragma unroll
+        for (int s = 0; s < D / 16; ++s) o[t][s] = f32x4{0.f, 0.f, 0.f, 0.f};
+        m_run[t] = -INFINITY;
+        l_run[t] = 0.f;
+    }
     bool started = false;                     // this wave has begun its first chunk
     bool seg_from_start = false;              // the current segment began at its chunk 0
     bool seg_at_range_start = false;          // ... and at this wave's first chunk
@@ -1126,16 +1137,24 @@ paged_attn_stream_kernel(AttnParams p) {
             const int qg = g2 - g * n_qg;
             const int L = __builtin_amdgcn_readfirstlane(seq_len(i));
             const int nch = n_chunks_of(L);
-            // this lane's column: query j of the window, head g*G + r
-            const int jj = MQ ? r16 / G : 0;
-            const int r = MQ ? r16 - jj * G : r16;
-            const int j = qg * (MQ ? p.qgs : 1) + jj;
-            const bool live = r16 < (MQ ? p.cols : G) && j < n_q;
-            const size_t out_row = (((size_t)i * n_q + j) * p.Hq + g * G + r) * D;
+            // this lane's column in tile t: query j[t] of the window, head g*G + r
+            int j[NT];
+            bool live[NT];
+            size_t out_row[NT];
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                const int c = 16 * t + r16;
+                const int jj = MQ ? c / G : 0;
+                const int r = MQ ? c - jj * G : r16;
+                j[t] = qg * (MQ ? p.qgs : 1) + jj;
+                live[t] = c < (MQ ? p.cols : G) && j[t] < n_q;
+                out_row[t] = (((size_t)i * n_q + j[t]) * p.Hq + g * G + r) * D;
+            }
             const bool first = !started;
             started = true;
             if (kc == 0 || first) {               // a segment starts
-                load_q_row<KV, D>(p, out_row, live, j4, qf);
+#pragma unroll
+                for (int t = 0; t < NT; ++t) load_q_row<KV, D>(p, out_row[t], live[t], j4, qf[t]);
                 if constexpr (STEP) load_new_token<KV, D>(p, ((size_t)i * p.Hkv + g) * D, r16, j4, ntstage[wave], nt);
                 seg_from_start = kc == 0;
                 seg_at_range_start = first;
@@ -1150,63 +1169,69 @@ paged_attn_stream_kernel(AttnParams p) {
             // from the new token instead of the pool
             if constexpr (STEP)
                 if (kc == nch - 1) patch_new_token<KV, D>(f, nt, L - 1 - tc, r16, j4);
-            const f32x4 sc = chunk_scores<KV, D>(f, qf);
             const bool tail = tc + 16 > L;        // tokens >= L hold no data
             // query j sees tokens < L - n_q + 1 + j (causal inside the window)
-            const int lim = MQ ? L - n_q + 1 + j : L;
             const bool masked = MQ ? tc + 16 > L - n_q + 1 : tail;
             const int first_tok = tc + 4 * j4;
-            float x[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                x[e] = sc[e] * p.qk_scale;
-                if (masked && first_tok + e >= lim) x[e] = -INFINITY;
+            for (int t = 0; t < NT; ++t) {
+                const f32x4 sc = chunk_scores<KV, D>(f, qf[t]);
+                const int lim = MQ ? L - n_q + 1 + j[t] : L;
+                float x[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    x[e] = sc[e] * p.qk_scale;
+                    if (masked && first_tok + e >= lim) x[e] = -INFINITY;
+                }
+                const float cm = head_max(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
+                float m_new = fmaxf(m_run[t], cm);
+                // a column that has seen no visible token yet keeps m = -inf;
+                // its exponentials are taken against 0 so they stay 0, not NaN
+                const float m_ref = MQ && m_new == -INFINITY ? 0.f : m_new;
+                const float alpha = __builtin_amdgcn_exp2f(m_run[t] - m_ref);
+                float pr[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) pr[e] = __builtin_amdgcn_exp2f(x[e] - m_ref);
+                l_run[t] = l_run[t] * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
+                m_run[t] = m_new;
+                if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
+#pragma unroll
+                    for (int s = 0; s < D / 16; ++s) o[t][s] *= alpha;
+                }
+                chunk_pv<KV, D>(f, pr, o[t], tail, first_tok, L);
             }
-            const float cm = head_max(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
-            float m_new = fmaxf(m_run, cm);
-            // a column that has seen no visible token yet keeps m = -inf; its
-            // exponentials are taken against 0 so they stay 0, not NaN
-            const float m_ref = MQ && m_new == -INFINITY ? 0.f : m_new;
-            const float alpha = __builtin_amdgcn_exp2f(m_run - m_ref);
-            float pr[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) pr[e] = __builtin_amdgcn_exp2f(x[e] - m_ref);
-            l_run = l_run * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
-            m_run = m_new;
-            if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
-#pragma unroll
-                for (int s = 0; s < D / 16; ++s) o[s] *= alpha;
-            }
-            chunk_pv<KV, D>(f, pr, o, tail, first_tok, L);
 
             if (kc == nch - 1 || v == v_last) {   // the segment ends here for this wave
-                const float l_tot = head_sum(l_run);
                 const bool whole = seg_from_start && kc == nch - 1;
                 const int C = MQ ? p.cols : G;
-                if (live) {
-                    if (whole) {
-                        const float sc_o = p.v_scale / l_tot;
-                        float* orow = p.out + out_row + 4 * j4;
 #pragma unroll
-                        for (int s = 0; s < D / 16; ++s)
-                            *reinterpret_cast<f32x4*>(orow + 16 * s) = o[s] * sc_o;
-                    } else {
-                        const size_t rr = (size_t)(2 * w + (seg_at_range_start ? 0 : 1)) * C + r16;
-                        const size_t nrec = (size_t)p.n_rec;
-                        float* orec = p.ws + rr * D + 4 * j4;
+                for (int t = 0; t < NT; ++t) {
+                    const float l_tot = head_sum(l_run[t]);
+                    if (live[t]) {
+                        if (whole) {
+                            const float sc_o = p.v_scale / l_tot;
+                            float* orow = p.out + out_row[t] + 4 * j4;
 #pragma unroll
-                        for (int s = 0; s < D / 16; ++s)
-                            *reinterpret_cast<f32x4*>(orec + 16 * s) = o[s] * p.v_scale;
-                        if (j4 == 0) {
-                            p.ws[nrec * C * D + rr] = m_run;
-                            p.ws[nrec * C * (D + 1) + rr] = l_tot;
+                            for (int s = 0; s < D / 16; ++s)
+                                *reinterpret_cast<f32x4*>(orow + 16 * s) = o[t][s] * sc_o;
+                        } else {
+                            const size_t rr = (size_t)(2 * w + (seg_at_range_start ? 0 : 1)) * C + 16 * t + r16;
+                            const size_t nrec = (size_t)p.n_rec;
+                            float* orec = p.ws + rr * D + 4 * j4;
+#pragma unroll
+                            for (int s = 0; s < D / 16; ++s)
+                                *reinterpret_cast<f32x4*>(orec + 16 * s) = o[t][s] * p.v_scale;
+                            if (j4 == 0) {
+                                p.ws[nrec * C * D + rr] = m_run[t];
+                                p.ws[nrec * C * (D + 1) + rr] = l_tot;
+                            }
                         }
                     }
-                }
 #pragma unroll
-                for (int s = 0; s < D / 16; ++s) o[s] = f32x4{0.f, 0.f, 0.f, 0.f};
-                m_run = -INFINITY;
-                l_run = 0.f;
+                    for (int s = 0; s < D / 16; ++s) o[t][s] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    m_run[t] = -INFINITY;
+                    l_run[t] = 0.f;
+                }
             }
         };
         Frag<KV, D> fa, fb;
@@ -1362,23 +1387,30 @@ AttnKernel pick_d(int d, int bs) {
     return d == 64 ? pick_bs<KV, 64>(bs) : pick_bs<KV, 128>(bs);
 }
 
-template <int KV, int D, int MQ>
+template <int KV, int D, int MODE, int NT>
 AttnKernel pick_stream_bs(int bs) {
     switch (bs) {
-        case 8: return paged_attn_stream_kernel<KV, D, 8, MQ>;
-        case 16: return paged_attn_stream_kernel<KV, D, 16, MQ>;
-        case 32: return paged_attn_stream_kernel<KV, D, 32, MQ>;
-        case 64: return paged_attn_stream_kernel<KV, D, 64, MQ>;
-        case 128: return paged_attn_stream_kernel<KV, D, 128, MQ>;
+        case 8: return paged_attn_stream_kernel<KV, D, 8, MODE, NT>;
+        case 16: return paged_attn_stream_kernel<KV, D, 16, MODE, NT>;
+        case 32: return paged_attn_stream_kernel<KV, D, 32, MODE, NT>;
+        case 64: return paged_attn_stream_kernel<KV, D, 64, MODE, NT>;
+        case 128: return paged_attn_stream_kernel<KV, D, 128, MODE, NT>;
     }
     return nullptr;
 }
 
+// tiles: 16-column MFMA tiles per pass (query windows: 1 or wide_tiles(d))
 template <int KV>
-AttnKernel pick_stream(int d, int bs, int mode) {
-    if (mode == SM_WINDOW) return d == 64 ? pick_stream_bs<KV, 64, SM_WINDOW>(bs) : pick_stream_bs<KV, 128, SM_WINDOW>(bs);
-    if (mode == SM_STEP) return d == 64 ? pick_stream_bs<KV, 64, SM_STEP>(bs) : pick_stream_bs<KV, 128, SM_STEP>(bs);
-    return d == 64 ? pick_stream_bs<KV, 64, SM_DECODE>(bs) : pick_stream_bs<KV, 128, SM_DECODE>(bs);
+AttnKernel pick_stream(int d, int bs, int mode, int tiles) {
+    if (mode == SM_WINDOW) {
+        if (tiles == 1)
+            return d == 64 ? pick_stream_bs<KV, 64, SM_WINDOW, 1>(bs) : pick_stream_bs<KV, 128, SM_WINDOW, 1>(bs);
+        return d == 64 ? pick_stream_bs<KV, 64, SM_WINDOW, wide_tiles(64)>(bs)
+                       : pick_stream_bs<KV, 128, SM_WINDOW, wide_tiles(128)>(bs);
+    }
+    if (mode == SM_STEP)
+        return d == 64 ? pick_stream_bs<KV, 64, SM_STEP, 1>(bs) : pick_stream_bs<KV, 128, SM_STEP, 1>(bs);
+    return d == 64 ? pick_stream_bs<KV, 64, SM_DECODE, 1>(bs) : pick_stream_bs<KV, 128, SM_DECODE, 1>(bs);
 }
 
 // Compute units of the current device (cached per device).
@@ -1498,13 +1530,16 @@ extern "C" pkv_status pkv_copy_blocks(void* k_cache, void* v_cache, const int32_
 namespace {
 
 // Query window layout of the balanced split: qgs queries per group (G * qgs
-// MFMA columns, at most 16) and n_qg groups.
+// MFMA columns in `tiles` tiles of 16) and n_qg groups, each one pass over
+// the sequence's blocks. A window that fits one 16-column tile takes one
+// tile; a larger one takes wide_tiles(d) tiles (32 columns) per pass.
 struct QueryGroups {
-    int qgs, n_qg, cols;
+    int qgs, n_qg, cols, tiles;
 };
-QueryGroups query_groups(int32_t n_q, int32_t G) {
+QueryGroups query_groups(int32_t n_q, int32_t G, int32_t d) {
     QueryGroups r;
-    r.qgs = std::min<int32_t>(n_q, std::max<int32_t>(1, 16 / G));
+    r.tiles = (int64_t)n_q * G <= 16 ? 1 : wide_tiles(d);
+    r.qgs = std::min<int32_t>(n_q, std::max<int32_t>(1, 16 * r.tiles / G));
     r.n_qg = (n_q + r.qgs - 1) / r.qgs;
     r.cols = G * r.qgs;
     return r;
@@ -1515,7 +1550,7 @@ size_t attn_workspace_size(int32_t S, int32_t n_q, int32_t Hq, int32_t Hkv, int3
     if (S <= 0 || n_q <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || Hq % Hkv != 0) return 0;
     const int32_t G = Hq / Hkv;
     if (partition_size == PKV_PARTITION_BALANCED) {
-        const QueryGroups qg = query_groups(n_q, G);
+        const QueryGroups qg = query_groups(n_q, G, d);
         return balanced_records_bytes((size_t)qg.cols, d) +
                2 * (size_t)S * (size_t)Hkv * (size_t)qg.n_qg * sizeof(int);
     }
@@ -1571,7 +1606,7 @@ pkv_status attn_launch(const char* fn, float* out, const void* q, const void* k_
     if (is_step && (!step.k_new || !step.v_new)) return fail(PKV_E_INVALID, "%s: NULL pointer", fn);
     if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
         return fail(PKV_E_INVALID, "%s: NULL pointer", fn);
-    const QueryGroups qgr = query_groups(n_q, G);
+    const QueryGroups qgr = query_groups(n_q, G, d);
     const int64_t n_part = balanced ? 1 : n_partitions(max_context_len, partition_size);
     const size_t need = attn_workspace_size(S, n_q, Hq, Hkv, d, max_context_len, partition_size);
     if (need > 0 && (!workspace || workspace_bytes < need))
@@ -1621,8 +1656,9 @@ pkv_status attn_launch(const char* fn, float* out, const void* q, const void* k_
     size_t lds;
     if (balanced) {
         const int mode = is_step ? SM_STEP : n_q > 1 ? SM_WINDOW : SM_DECODE;
-        kern = kv == KV_F32 ? pick_stream<KV_F32>(d, bs, mode)
-             : kv == KV_BF16 ? pick_stream<KV_BF16>(d, bs, mode) : pick_stream<KV_FP8>(d, bs, mode);
+        const int tiles = mode == SM_WINDOW ? qgr.tiles : 1;
+        kern = kv == KV_F32 ? pick_stream<KV_F32>(d, bs, mode, tiles)
+             : kv == KV_BF16 ? pick_stream<KV_BF16>(d, bs, mode, tiles) : pick_stream<KV_FP8>(d, bs, mode, tiles);
         lds = (size_t)(prm.cache_lens ? S : 0) * sizeof(int);
     } else {
         kern = kv == KV_F32 ? pick_d<KV_F32>(d, bs)

@@ -385,12 +385,16 @@ def _window_case(w, n_q, seqs=None):
     return got
 
 
-@pytest.mark.parametrize("n_q", [2, 5])
+# small (G 7, d 64): 2 -> one 16-column tile; 5 -> two passes of 2 tiles (4 + 1
+# queries); 12 -> three passes of 2 tiles (4 + 4 + 4 queries)
+@pytest.mark.parametrize("n_q", [2, 5, 12])
 def test_window_small_gqa7(n_q):
     _window_case(W.make("small"), n_q)
 
 
-@pytest.mark.parametrize("n_q", [1, 4, 6])
+# llama8b (G 4, d 128): 1 and 4 -> one tile; 6 -> 24 columns in one pass of 2
+# tiles; 20 -> three passes of 2 tiles (8 + 8 + 4 queries)
+@pytest.mark.parametrize("n_q", [1, 4, 6, 20])
 def test_window_llama8b(n_q):
     _window_case(W.make("llama8b"), n_q)
 
@@ -413,7 +417,7 @@ def test_window_of_one_equals_decode():
     ([16, 17, 40, 300, 0, 20], 4, 4, 64, 16, "f32", 16),      # G 1: the whole window in one pass
     ([20, 21, 100, 600], 2, 2, 64, 8, "f32", 20),             # G 1, two passes
     ([4, 5, 17, 33, 1000, 0], 32, 8, 128, 16, "bf16", 4),     # L = n_q exactly
-    ([9, 64, 65, 700], 14, 2, 64, 32, "bf16", 9),             # G 7, five passes
+    ([9, 64, 65, 700], 14, 2, 64, 32, "bf16", 9),             # G 7: three passes of 2 tiles
 ])
 def test_window_edge_shapes(lens, Hq, Hkv, d, bs, dt, n_q):
     w = W.make_custom(lens=lens, Hq=Hq, Hkv=Hkv, d=d, bs=bs, q_dtype=dt, cache_dtype=dt,
