@@ -257,6 +257,43 @@ def run_other_op(args, w, torch, pkv):
     }), flush=True)
 
 
+def run_prefix(args):
+    """--op prefix: admission of requests that share a system prompt through the
+    host allocator's prefix cache (chained block hashes, cached full blocks).
+    Host code only; one JSON line."""
+    import paged_kv_cache_108_amd as pkv
+    bs, n_req, shared = 16, 64, 1024
+    rng = np.random.default_rng([108, 953])
+    system = rng.integers(0, 32000, shared)
+    private = np.clip(np.floor(np.exp(rng.normal(np.log(500), 1.0, n_req))), 1, 4096).astype(int)
+    prompts = [np.concatenate([system, rng.integers(0, 32000, int(n))]).astype(np.int32) for n in private]
+    blocks_needed = sum(-(-len(t) // bs) for t in prompts) + 64
+    reps = max(args.steps, 1)
+    times, hits, misses, hashed = [], 0, 0, 0
+    for _ in range(reps):
+        alloc = pkv.Allocator(blocks_needed, bs)
+        t0 = time.perf_counter()
+        for k, t in enumerate(prompts):
+            alloc.create_prefixed(k, t)
+        times.append(time.perf_counter() - t0)
+        st = alloc.prefix_stats()
+        hits, misses = st["hit_blocks"], st["miss_blocks"]
+        alloc.close()
+    hashed = sum(len(t) // bs for t in prompts)
+    mean = statistics.mean(times)
+    print(json.dumps({
+        "metric": "prefix-cache admission (host): requests/s and hashed blocks/s", "value": round(n_req / mean, 1),
+        "unit": "requests/s", "n_gpus": 0, "steps": reps, "warmup": 0, "ms_per_step": round(1e3 * mean, 4),
+        "higher_is_better": True, "scaling": "none", "vs_baseline": None, "dtype": "int32 tokens",
+        "data": "synthetic (seeded)",
+        "config": {"workload": f"{n_req} requests sharing a {shared}-token system prompt, lognormal(500, 1.0) "
+                               f"private tokens, bs {bs}", "tokens": int(sum(len(t) for t in prompts)),
+                   "full_blocks_hashed": hashed, "hit_blocks": hits, "miss_blocks": misses},
+        "timing": {"s_mean": round(mean, 6), "s_min": round(min(times), 6),
+                   "us_per_hashed_block": round(1e6 * mean / hashed, 3)},
+    }), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -275,10 +312,11 @@ def main():
     ap.add_argument("--no-flush", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
-    ap.add_argument("--op", choices=["step", "window", "copy"], default="step",
+    ap.add_argument("--op", choices=["step", "window", "copy", "prefix"], default="step",
                     help="step: the decode step (default); window: pkv_paged_multi_query_attn over "
                          "windows of --window queries per sequence; copy: pkv_copy_blocks of --pairs "
-                         "(src, dst) block pairs")
+                         "(src, dst) block pairs; prefix: host-side prefix-cache admission "
+                         "(pkv_seq_create_prefixed), no GPU")
     ap.add_argument("--window", type=int, default=4, help="queries per sequence for --op window")
     ap.add_argument("--pairs", type=int, default=1024, help="block pairs for --op copy")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -289,6 +327,10 @@ def main():
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
                           "n_gpus_requested": args.gpus}))
         sys.exit(2)
+
+    if args.op == "prefix":
+        run_prefix(args)
+        return
 
     import torch
     import paged_kv_cache_108_amd as pkv
