@@ -542,3 +542,27 @@ def test_balanced_workspace_reuse_any_contents():
                                   partition_size=BAL, workspace=ws)
             torch.cuda.synchronize()
             assert np.array_equal(to_host(out), want)
+
+
+# ------------------------------------------------------------------ more sequences than cached lengths
+def _many_lens(min_len):
+    # 4100 sequences: more than the 4096 context lengths a workgroup keeps in
+    # LDS, so every kernel reads the lengths from memory instead
+    rng = np.random.default_rng(4100 + min_len)
+    lens = rng.integers(min_len, 41, 4100)
+    lens[::97] = 0
+    return [int(L) for L in lens]
+
+
+def test_many_sequences_lengths_read_from_memory():
+    lens = _many_lens(1)
+    w = W.make_custom(lens=lens, Hq=4, Hkv=2, d=64, bs=16, cfg=4100)
+    dev, out = _full_case(w, [0, 512, BAL])
+    for i, L in enumerate(lens):
+        if L <= 0:
+            assert np.all(out[i] == 0.0)
+    _step_case(W.make_custom(lens=lens, Hq=4, Hkv=2, d=64, bs=16, cfg=4101))
+
+
+def test_many_sequences_window():
+    _window_case(W.make_custom(lens=_many_lens(5), Hq=8, Hkv=2, d=64, bs=16, cfg=4102), 5)
