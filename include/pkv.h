@@ -30,8 +30,12 @@
  * blocks in the pool, L_i the context length of sequence i.
  *
  * Pool layout (the pages fix none; tokens of a block are contiguous in both):
- *   k_cache[P][Hkv][bs][d]   each (block, kv head) tile token-major
- *   v_cache[P][Hkv][d][bs]   each (block, kv head) tile channel-major
+ *   k_cache[P][Hkv][bs][d]           each (block, kv head) tile token-major
+ *   v_cache[P][Hkv][bs/vs][d][vs]    each (block, kv head) tile in sub-tiles of
+ *                                    vs = min(bs, 16) tokens, each channel-major
+ *                                    (for bs <= 16: v_cache[P][Hkv][d][bs])
+ * A 16-token chunk of a block then reads whole rows of K and one whole V
+ * sub-tile, whatever the block size.
  */
 #ifndef PKV_H
 #define PKV_H

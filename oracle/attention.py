@@ -21,8 +21,10 @@ g = h // G (grouped-query attention, consecutive grouping), over the L_i tokens
 of sequence i; a row with L_i <= 0 is zero.
 
 Storage layout of the pools (the pages fix none; the reading taken):
-  k_cache[P][Hkv][bs][d]   token-major within each (block, kv-head) tile
-  v_cache[P][Hkv][d][bs]   channel-major within each (block, kv-head) tile
+  k_cache[P][Hkv][bs][d]          token-major within each (block, kv-head) tile
+  v_cache[P][Hkv][bs/vs][d][vs]   channel-major within each sub-tile of vs =
+                                  min(bs, 16) tokens; for bs <= 16 that is
+                                  [P][Hkv][d][bs], and may be given so
 Both tiles are contiguous, and the bs tokens of a block sit together in each.
 
 Element storage: "f32" float32, "bf16" uint16 bit patterns, "fp8" uint8 OCP
@@ -32,6 +34,7 @@ E4M3 codes whose value is decode(code) * scale (one float32 scale per tensor).
 import numpy as np
 
 from .codecs import bf16_bits_to_f64, f32_to_f64, e4m3_decode
+from .layout import v_view5
 
 
 def widen(arr, dtype, scale=1.0):
@@ -51,9 +54,12 @@ def reassemble(pool, table_row, L, bs, which):
     """Gather one sequence's K or V into logical order: [L][Hkv][d] (storage dtype).
 
     ``which`` is "k" for the [P][Hkv][bs][d] pool and "v" for the
-    [P][Hkv][d][bs] pool. Position p lives in logical block p // bs at offset
-    p % bs (0-based positions).
+    [P][Hkv][bs/vs][d][vs] pool (or [P][Hkv][d][bs] when bs <= 16). Position p
+    lives in logical block p // bs at offset p % bs (0-based positions); in V
+    that is sub-tile (p % bs) // vs, column (p % bs) % vs.
     """
+    if which == "v":
+        pool = v_view5(pool, bs)
     P = pool.shape[0]
     n = -(-L // bs)
     ids = np.asarray(table_row[:n], dtype=np.int64)
@@ -62,11 +68,11 @@ def reassemble(pool, table_row, L, bs, which):
     tiles = pool[ids]
     if which == "k":            # [n][Hkv][bs][d] -> [n][bs][Hkv][d]
         tiles = tiles.transpose(0, 2, 1, 3)
-    elif which == "v":          # [n][Hkv][d][bs] -> [n][bs][Hkv][d]
-        tiles = tiles.transpose(0, 3, 1, 2)
+    elif which == "v":          # [n][Hkv][bs/vs][d][vs] -> [n][bs/vs][vs][Hkv][d]
+        tiles = tiles.transpose(0, 2, 4, 1, 3)
     else:
         raise ValueError(which)
-    flat = tiles.reshape(n * bs, tiles.shape[2], tiles.shape[3])
+    flat = tiles.reshape(n * bs, tiles.shape[-2], tiles.shape[-1])
     return flat[:L]
 
 

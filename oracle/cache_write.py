@@ -8,9 +8,11 @@ is the flat index block * bs + offset; slot -1 means "skip this token" (padding)
 
 Per token t with slot >= 0: (b, o) = divmod(slot, bs), then for every kv head h
 and channel c
-    K[b][h][o][c] = enc(K_new[t][h][c])        (k_cache is [P][Hkv][bs][d])
-    V[b][h][c][o] = enc(V_new[t][h][c])        (v_cache is [P][Hkv][d][bs])
-Every other element of the pools is left as it was.
+    K[b][h][o][c] = enc(K_new[t][h][c])                  (k_cache [P][Hkv][bs][d])
+    V[b][h][o // vs][c][o % vs] = enc(V_new[t][h][c])    (v_cache [P][Hkv][bs/vs][d][vs])
+with vs = min(bs, 16); for bs <= 16 the V pool may also be given as
+[P][Hkv][d][bs], the same memory. Every other element of the pools is left as
+it was.
 
 Copy-on-write ("03 · PagedAttention", "Sharing: copy-on-write"; the daily
 term's copy-on-write figure): before a sequence writes into a shared, partly
@@ -27,6 +29,7 @@ to nearest-even, then the codec of ``codecs.py``.
 import numpy as np
 
 from .codecs import bf16_bits_to_f64, e4m3_encode
+from .layout import v_view5
 
 
 def quantise(x_bits, src_dtype, inv_scale):
@@ -49,6 +52,7 @@ def kv_cache_write(k_new, v_new, k_cache, v_cache, slot_mapping, *, bs, src_dtyp
     """
     k_out = np.array(k_cache, copy=True)
     v_out = np.array(v_cache, copy=True)
+    v5 = v_view5(v_out, bs)                                # a view: writes land in v_out
     if cache_dtype == "fp8":
         kq = quantise(k_new, src_dtype, k_inv_scale)
         vq = quantise(v_new, src_dtype, v_inv_scale)
@@ -65,7 +69,7 @@ def kv_cache_write(k_new, v_new, k_cache, v_cache, slot_mapping, *, bs, src_dtyp
         if b >= P:
             raise ValueError("slot outside the pool")
         k_out[b, :, o, :] = kq[t]
-        v_out[b, :, :, o] = vq[t]
+        v5[b, :, o // v5.shape[4], :, o % v5.shape[4]] = vq[t]
     return k_out, v_out
 
 

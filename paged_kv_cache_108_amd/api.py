@@ -62,14 +62,25 @@ def _stream(stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def v_shape_ok(v_cache, P, Hkv, d, bs):
+    """The V pool holds one tile per (block, kv head) in sub-tiles of
+    vs = min(bs, 16) tokens, each [d][vs]: shape [P][Hkv][bs/vs][d][vs], or
+    [P][Hkv][d][bs] when bs <= 16 (the same memory)."""
+    shp = tuple(v_cache.shape)
+    vs = min(bs, 16)
+    if shp == (P, Hkv, bs // vs, d, vs):
+        return True
+    return bs <= 16 and shp == (P, Hkv, d, bs)
+
+
 def kv_cache_write(k_new, v_new, k_cache, v_cache, slot_mapping, *, k_inv_scale=1.0,
                    v_inv_scale=1.0, stream=None):
     """pkv_kv_cache_write. k_new/v_new [T][Hkv][d]; k_cache [P][Hkv][bs][d];
-    v_cache [P][Hkv][d][bs]; slot_mapping int64 [T]."""
+    v_cache as v_shape_ok describes; slot_mapping int64 [T]."""
     import torch
     T, Hkv, d = k_new.shape
     P, _, bs, _ = k_cache.shape
-    if v_new.shape != k_new.shape or tuple(v_cache.shape) != (P, Hkv, d, bs) \
+    if v_new.shape != k_new.shape or not v_shape_ok(v_cache, P, Hkv, d, bs) \
             or tuple(k_cache.shape) != (P, Hkv, bs, d):
         raise ValueError("kv_cache_write: shape mismatch")
     if slot_mapping.dtype != torch.int64 or slot_mapping.shape != (T,):
@@ -87,7 +98,7 @@ def copy_blocks(k_cache, v_cache, src, dst, *, stream=None):
     and none of them a src of the same call."""
     import torch
     P, Hkv, bs, d = k_cache.shape
-    if tuple(v_cache.shape) != (P, Hkv, d, bs) or v_cache.dtype != k_cache.dtype:
+    if not v_shape_ok(v_cache, P, Hkv, d, bs) or v_cache.dtype != k_cache.dtype:
         raise ValueError("copy_blocks: pools disagree")
     if src.dtype != torch.int32 or dst.dtype != torch.int32 or src.shape != dst.shape or src.dim() != 1:
         raise ValueError("copy_blocks: src and dst must be int32 [n]")
@@ -159,7 +170,7 @@ def paged_decode_step(out, q, k_new, v_new, k_cache, v_cache, block_tables, cont
         raise ValueError("paged_decode_step: out must be float32 [S][Hq][d]")
     if tuple(k_new.shape) != (S, Hkv, d) or tuple(v_new.shape) != (S, Hkv, d):
         raise ValueError("paged_decode_step: k_new/v_new must be [S][Hkv][d]")
-    if tuple(v_cache.shape) != (P, Hkv, d, bs):
+    if not v_shape_ok(v_cache, P, Hkv, d, bs):
         raise ValueError("paged_decode_step: v_cache shape")
     if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
         raise ValueError("paged_decode_step: tables and lengths must be int32")
@@ -217,7 +228,11 @@ def quantise_pool(values_k, values_v, codes_k, codes_v, *, k_inv_scale, v_inv_sc
     import torch
     P, Hkv, bs, d = values_k.shape
     tok_k = values_k.permute(0, 2, 1, 3).reshape(P * bs, Hkv, d).contiguous()
-    tok_v = values_v.permute(0, 3, 1, 2).reshape(P * bs, Hkv, d).contiguous()
+    if values_v.dim() == 4:                    # [P][Hkv][d][bs] (bs <= 16)
+        tok_v = values_v.permute(0, 3, 1, 2)
+    else:                                      # [P][Hkv][bs/vs][d][vs]
+        tok_v = values_v.permute(0, 2, 4, 1, 3)
+    tok_v = tok_v.reshape(P * bs, Hkv, d).contiguous()
     slots = torch.arange(P * bs, dtype=torch.int64, device=values_k.device)
     kv_cache_write(tok_k, tok_v, codes_k, codes_v, slots, k_inv_scale=k_inv_scale,
                    v_inv_scale=v_inv_scale, stream=stream)

@@ -181,7 +181,9 @@ kv_cache_write_kernel(const void* __restrict__ k_new, const void* __restrict__ v
         const int c = e - h * d;
         const size_t src = (size_t)t * n + e;
         const size_t kd = (((size_t)b * Hkv + h) * bs + o) * d + c;
-        const size_t vd = (((size_t)b * Hkv + h) * d + c) * bs + o;
+        // V tile: [bs / vs][d][vs] with vs = min(bs, 16) tokens per sub-tile
+        const int vs = bs < 16 ? bs : 16;
+        const size_t vd = ((size_t)b * Hkv + h) * bs * d + (size_t)(o / vs) * vs * d + (size_t)c * vs + o % vs;
         if constexpr (CACHE == KV_F32) {
             static_cast<float*>(k_cache)[kd] = static_cast<const float*>(k_new)[src];
             static_cast<float*>(v_cache)[vd] = static_cast<const float*>(v_new)[src];
@@ -262,12 +264,8 @@ __device__ __forceinline__ int clamp_block(int b, int P) { return min(max(b, 0),
 // Load the K and V fragments of the chunk starting at token `tc` (absolute).
 // b0 is the physical block holding token tc; for bs 8, b1 holds token tc + 8.
 // Streaming loads of the cache: the nontemporal hint marks the lines
-// evict-first, since each K/V byte is read once per call. load_chunk uses it
-// for blocks of at most 16 tokens, where a 16-token chunk reads its blocks
-// whole. With larger blocks a chunk reads part of each V channel row
-// (channel-major [d][bs] tiles) and a later chunk the rest of the line, which
-// must still be cached then; measured on MI355X, hinted loads slow bs 32 and
-// 64 down by 5-30% (K loads included), so those take plain loads.
+// evict-first, since each K/V byte is read once per call: a 16-token chunk
+// reads 16 whole K rows and one whole V sub-tile of its block.
 __device__ __forceinline__ uint4 ld_stream(const uint4* a) {
     typedef unsigned v4u __attribute__((ext_vector_type(4)));
     const v4u t = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(a));
@@ -286,8 +284,7 @@ __device__ __forceinline__ uint2 ld_stream(const uint2* a) {
 __device__ __forceinline__ uint32_t ld_stream(const uint32_t* a) { return __builtin_nontemporal_load(a); }
 template <int BS, typename T>
 __device__ __forceinline__ T ld_kv(const T* a) {
-    if constexpr (BS <= 16) return ld_stream(a);
-    else return *a;
+    return ld_stream(a);
 }
 
 template <int KV, int D, int BS>
@@ -308,8 +305,9 @@ __device__ __forceinline__ void load_chunk(Frag<KV, D>& f, const AttnParams& p, 
         bk = b0;
         bv = b0;
         ok_ = (tc % BS) + r16;
-        ov = (tc % BS) + 4 * j4;
+        ov = ((tc % BS) / 16) * 16 * D + 4 * j4;    // the chunk's 16-token V sub-tile
     }
+    constexpr int VS = BS < 16 ? BS : 16;           // tokens per V sub-tile row
     const size_t tile = (size_t)BS * D;
     const E* krow = kbase + ((size_t)bk * p.Hkv + g) * tile + (size_t)ok_ * D;
     const E* vt = vbase + ((size_t)bv * p.Hkv + g) * tile + ov;
@@ -319,21 +317,21 @@ __device__ __forceinline__ void load_chunk(Frag<KV, D>& f, const AttnParams& p, 
             f.k[x] = ld_kv<BS>(reinterpret_cast<const float4*>(krow + 16 * x + 4 * j4));
 #pragma unroll
         for (int s = 0; s < D / 16; ++s)
-            f.v[s] = ld_kv<BS>(reinterpret_cast<const float4*>(vt + (size_t)(16 * s + r16) * BS));
+            f.v[s] = ld_kv<BS>(reinterpret_cast<const float4*>(vt + (size_t)(16 * s + r16) * VS));
     } else if constexpr (KV == KV_BF16) {
 #pragma unroll
         for (int s = 0; s < D / 32; ++s)
             f.k[s] = ld_kv<BS>(reinterpret_cast<const uint4*>(krow + 32 * s + 8 * j4));
 #pragma unroll
         for (int s = 0; s < D / 16; ++s)
-            f.v[s] = ld_kv<BS>(reinterpret_cast<const uint2*>(vt + (size_t)(16 * s + r16) * BS));
+            f.v[s] = ld_kv<BS>(reinterpret_cast<const uint2*>(vt + (size_t)(16 * s + r16) * VS));
     } else {
 #pragma unroll
         for (int x = 0; x < D / 64; ++x)
             f.k[x] = ld_kv<BS>(reinterpret_cast<const uint4*>(krow + 64 * x + 16 * j4));
 #pragma unroll
         for (int s = 0; s < D / 16; ++s)
-            f.v[s] = ld_kv<BS>(reinterpret_cast<const uint32_t*>(vt + (size_t)(16 * s + r16) * BS));
+            f.v[s] = ld_kv<BS>(reinterpret_cast<const uint32_t*>(vt + (size_t)(16 * s + r16) * VS));
     }
 }
 
@@ -1002,7 +1000,9 @@ paged_attn_stream_kernel(AttnParams p) {
 #pragma unroll
             for (int u = 0; u < NCH; ++u) {
                 const int c = lane + 64 * u;
-                const size_t dst = is_v ? (((size_t)b * p.Hkv + g) * D + c) * BS + o
+                constexpr int VS = BS < 16 ? BS : 16;      // V sub-tiles of VS tokens
+                const size_t dst = is_v ? ((size_t)b * p.Hkv + g) * BS * D + (size_t)(o / VS) * VS * D +
+                                              (size_t)c * VS + o % VS
                                         : (((size_t)b * p.Hkv + g) * BS + o) * D + c;
                 void* pool = const_cast<void*>(is_v ? p.v : p.k);
                 if constexpr (KV == KV_F32) static_cast<float*>(pool)[dst] = __uint_as_float(val[u]);

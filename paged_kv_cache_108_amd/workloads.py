@@ -211,7 +211,7 @@ class Workload:
     P: int
     q: np.ndarray              # [S][Hq][d]      f32 or bf16 bits
     k_pool: np.ndarray         # [P][Hkv][bs][d] f32 or bf16 bits (fp8: values to quantise)
-    v_pool: np.ndarray         # [P][Hkv][d][bs]
+    v_pool: np.ndarray         # [P][Hkv][d][bs] for bs <= 16, else [P][Hkv][bs/16][d][16]
     block_tables: np.ndarray   # int32 [S][maxB], -1 padded
     context_lens: np.ndarray   # int32 [S], includes this step's new token
     k_new: np.ndarray          # [S][Hkv][d] source dtype
@@ -246,12 +246,21 @@ def _valid_mask(tables, lens, bs, P):
     return valid
 
 
+def v_pool_shape(P, Hkv, d, bs):
+    """V pool shape: one channel-major tile per (block, kv head), in sub-tiles of
+    16 tokens when bs > 16 (the library's layout)."""
+    return (P, Hkv, d, bs) if bs <= 16 else (P, Hkv, bs // 16, d, 16)
+
+
 def _poison(pool_k, pool_v, valid, dtype):
     nan = np.float32(np.nan) if dtype == F32 else BF16_NAN
     inv = ~valid                                   # [P][bs]
     b_idx, o_idx = np.nonzero(inv)
     pool_k[b_idx, :, o_idx, :] = nan
-    pool_v[b_idx, :, :, o_idx] = nan
+    if pool_v.ndim == 4:
+        pool_v[b_idx, :, :, o_idx] = nan
+    else:
+        pool_v[b_idx, :, o_idx // 16, :, o_idx % 16] = nan
 
 
 def generate(s, tables, lens, P, *, extra=None, poison_new=True):
@@ -260,7 +269,7 @@ def generate(s, tables, lens, P, *, extra=None, poison_new=True):
     assert tables.shape[0] == S and len(lens) == S
     q32 = _rng(cfg, 2).standard_normal((S, Hq, d), dtype=np.float32)
     k32 = _rng(cfg, 3).standard_normal((P, Hkv, bs, d), dtype=np.float32)
-    v32 = _rng(cfg, 4).standard_normal((P, Hkv, d, bs), dtype=np.float32)
+    v32 = _rng(cfg, 4).standard_normal(v_pool_shape(P, Hkv, d, bs), dtype=np.float32)
     kn32 = _rng(cfg, 5).standard_normal((S, Hkv, d), dtype=np.float32)
     vn32 = _rng(cfg, 6).standard_normal((S, Hkv, d), dtype=np.float32)
     pool_dtype = F32 if s.cache_dtype == F32 else BF16

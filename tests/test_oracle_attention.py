@@ -32,7 +32,9 @@ def _scatter(Kc, Vc, bs, P, rng, shared_prefix=None):
     maxb = max(max(nb), 1)
     perm = list(rng.permutation(P))
     kpool = np.full((P, Hkv, bs, d), np.nan, dtype=np.float32)
-    vpool = np.full((P, Hkv, d, bs), np.nan, dtype=np.float32)
+    # V: sub-tiles of vs = min(bs, 16) tokens, channel-major; [P][Hkv][d][bs] for bs <= 16
+    vs = min(bs, 16)
+    vpool = np.full((P, Hkv, bs // vs, d, vs), np.nan, dtype=np.float32)
     tables = np.full((S, maxb), -1, dtype=np.int32)
     for i in range(S):
         for j in range(nb[i]):
@@ -42,7 +44,9 @@ def _scatter(Kc, Vc, bs, P, rng, shared_prefix=None):
             for h in range(Hkv):
                 for c in range(d):
                     kpool[b, h, o, c] = Kc[i][t, h, c]
-                    vpool[b, h, c, o] = Vc[i][t, h, c]
+                    vpool[b, h, o // vs, c, o % vs] = Vc[i][t, h, c]
+    if bs <= 16:
+        vpool = vpool.reshape(P, Hkv, d, bs)
     return kpool, vpool, tables
 
 

@@ -71,6 +71,28 @@ def test_write_bf16_is_a_bit_copy():
     assert np.sum(k2 != kc) == Hkv * d and np.sum(v2 != vc) == Hkv * d
 
 
+def test_write_large_block_lands_in_its_v_sub_tile():
+    # bs 64: V tiles are 4 sub-tiles of 16 tokens, each [d][16]; token offset
+    # 37 of block 2 is sub-tile 2, column 5
+    P, Hkv, bs, d = 3, 2, 64, 8
+    kc = np.zeros((P, Hkv, bs, d), dtype=np.uint16)
+    vc = np.zeros((P, Hkv, bs // 16, d, 16), dtype=np.uint16)
+    kn = np.arange(1, Hkv * d + 1, dtype=np.uint16).reshape(1, Hkv, d)
+    vn = kn + 1000
+    k2, v2 = oracle.kv_cache_write(kn, vn, kc, vc, np.array([2 * bs + 37]), bs=bs, src_dtype="bf16",
+                                   cache_dtype="bf16")
+    assert np.array_equal(k2[2, :, 37, :], kn[0]) and np.sum(k2 != 0) == Hkv * d
+    assert np.array_equal(v2[2, :, 2, :, 5], vn[0]) and np.sum(v2 != 0) == Hkv * d
+    flat = v2.reshape(P, Hkv, bs * d)                     # tile memory order
+    for h in range(Hkv):
+        for c in range(d):
+            assert flat[2, h, 2 * 16 * d + c * 16 + 5] == vn[0, h, c]
+    # a [P][Hkv][d][bs] pool does not describe bs > 16
+    with pytest.raises(ValueError):
+        oracle.kv_cache_write(kn, vn, kc, np.zeros((P, Hkv, d, bs), np.uint16), np.array([0]), bs=bs,
+                              src_dtype="bf16", cache_dtype="bf16")
+
+
 def test_write_fp8_quantises_with_one_float32_product():
     P, Hkv, bs, d = 3, 2, 16, 64
     kc = np.zeros((P, Hkv, bs, d), dtype=np.uint8)
