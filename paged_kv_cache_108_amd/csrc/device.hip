@@ -258,9 +258,6 @@ template <> struct QFragT<KV_FP8> { using T = uint4; };
 // Number of 16-byte q loads per lane, matching the K fragment's channel map.
 template <int KV, int D> constexpr int q_loads() { return KV == KV_F32 ? D / 16 : D / 32; }
 
-template <int BS>
-__device__ __forceinline__ int clamp_block(int b, int P) { return min(max(b, 0), P - 1); }
-
 // Load the K and V fragments of the chunk starting at token `tc` (absolute).
 // b0 is the physical block holding token tc; for bs 8, b1 holds token tc + 8.
 // Streaming loads of the cache: the nontemporal hint marks the lines
@@ -784,20 +781,8 @@ __device__ __forceinline__ int find_sequence(const AttnParams& p, const int* pre
     return s;
 }
 
-// Balanced split: chunk positions c = (sequence-major, then kv head, then
-// 16-token chunk) over all sequences, C in total, cut into W near-equal
-// contiguous ranges (the first C % W ranges one chunk longer).
-__device__ __forceinline__ long long range_start(long long C, long long W, long long w) {
-    const long long q = C / W, r = C % W;
-    return w * q + (w < r ? w : r);
-}
-__device__ __forceinline__ long long range_of(long long C, long long W, long long c) {
-    const long long q = C / W, r = C % W;
-    return c < r * (q + 1) ? c / (q + 1) : r + (c - r * (q + 1)) / q;
-}
-
-// 32-bit forms for the balanced split (the launcher keeps every position
-// below 2^31). Split: n positions cut into W ranges, range w being
+// Balanced split, in 32-bit arithmetic (the launcher keeps every position
+// below 2^31): n positions cut into W ranges, range w being
 // [start(w), start(w + 1)) with the first n % W ranges one longer.
 struct Split {
     unsigned q, r;
