@@ -64,6 +64,7 @@ constexpr int kWaves = PKV_WAVES;         // waves per workgroup
 constexpr int kThreads = kWaves * 64;
 constexpr int kMaxCachedLens = 4096;      // sequences whose lengths a workgroup keeps in LDS
 constexpr int kMaxWorkers = 4096;         // waves of the balanced split, at most (sizes its workspace)
+constexpr int kMergeBatch = 32;           // records per round trip for rows that merge 32 or more
 // 16-column tiles per pass for wide query windows. Each tile adds its own
 // q fragment, accumulator and softmax to every chunk: four tiles at d 128
 // spill registers, and four at d 64 made a chunk's compute outlast its load.
@@ -1328,7 +1329,23 @@ paged_attn_merge_kernel(AttnParams p) {
         const int kn = min(64, n - k0);
         const float wl = k0 + lane < n ? __builtin_amdgcn_exp2f(m_at(k0 + lane) - M) : 0.f;
         den += wl * (k0 + lane < n ? l_at(k0 + lane) : 0.f);
-        for (int k = 0; k < kn; k += 8) {
+        int k = 0;
+        for (; k + kMergeBatch <= kn; k += kMergeBatch) {
+            // long rows: kMergeBatch records per memory round trip
+            float ov[kMergeBatch][PER];
+#pragma unroll
+            for (int u = 0; u < kMergeBatch; ++u)
+#pragma unroll
+                for (int x = 0; x < PER; ++x)
+                    ov[u][x] = p.ws[(rec_of(k0 + k + u) * G + r) * D + lane + 64 * x];
+#pragma unroll
+            for (int u = 0; u < kMergeBatch; ++u) {
+                const float wt = __shfl(wl, (k + u) & 63);
+#pragma unroll
+                for (int x = 0; x < PER; ++x) num[x] += wt * ov[u][x];
+            }
+        }
+        for (; k < kn; k += 8) {
             float ov[8][PER];
 #pragma unroll
             for (int u = 0; u < 8; ++u)
