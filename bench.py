@@ -225,6 +225,21 @@ def run_other_op(args, w, torch, pkv):
                "bytes_with_passes": passes,
                "note": "value counts K/V once; a window needing several passes reads K/V once per pass "
                        "(bytes_with_passes)"}
+    elif args.op == "shared":
+        q = dev(w.q)
+        run = pkv.SharedPrefixDecode(w.block_tables, w.context_lens, args.group, s.bs, s.Hq, s.Hkv, s.d)
+        out = torch.empty((s.S, s.Hq, s.d), dtype=torch.float32, device="cuda")
+
+        def fn():
+            run(out, q, k_cache, v_cache, softmax_scale=w.softmax_scale, k_scale=w.k_scale,
+                v_scale=w.v_scale, stream=stream)
+        attn, _, logical, unique_tokens = algorithmic_bytes(w, cache_dtype)
+        byts = attn                                        # unique K/V once, q, out, tables, lengths
+        metric = "shared-prefix decode attention: achieved HBM GB/s at 1 GPU"
+        kernel = ("SharedPrefixDecode (shared-prefix window kernel + merge, suffix stream kernel + merge, "
+                  "state merge)")
+        cfg = {"group": args.group, "prefix_tokens": run.prefix_tokens, "unique_tokens": int(unique_tokens),
+               "context_tokens": int(w.context_lens.sum()), "kv_bytes_logical": int(logical)}
     else:
         per_pool = s.Hkv * s.bs * s.d * kv_elem           # one block of one pool
         n = min(args.pairs, w.P // 2)
@@ -312,13 +327,15 @@ def main():
     ap.add_argument("--no-flush", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
-    ap.add_argument("--op", choices=["step", "window", "copy", "prefix"], default="step",
+    ap.add_argument("--op", choices=["step", "window", "copy", "prefix", "shared"], default="step",
                     help="step: the decode step (default); window: pkv_paged_multi_query_attn over "
                          "windows of --window queries per sequence; copy: pkv_copy_blocks of --pairs "
                          "(src, dst) block pairs; prefix: host-side prefix-cache admission "
-                         "(pkv_seq_create_prefixed), no GPU")
+                         "(pkv_seq_create_prefixed), no GPU; shared: shared-prefix decode attention "
+                         "(prefix pass + suffix pass + merge) for groups of --group sequences")
     ap.add_argument("--window", type=int, default=4, help="queries per sequence for --op window")
     ap.add_argument("--pairs", type=int, default=1024, help="block pairs for --op copy")
+    ap.add_argument("--group", type=int, default=4, help="sequences per group for --op shared")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (reference for counter scaling)")
     args = ap.parse_args()

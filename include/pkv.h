@@ -253,6 +253,65 @@ pkv_status pkv_paged_multi_query_attn(float* out, const void* q,
                                       void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Decode attention over sequences that share leading blocks (beams, parallel
+ * samples: several block tables list the same physical blocks for a common
+ * prefix, "03 · PagedAttention", "Sharing: copy-on-write"; "PagedAttention"
+ * daily term, "Pros"). The pages share such blocks in memory; these three
+ * calls also read them once per step instead of once per sequence:
+ *
+ *   1. pkv_paged_shared_prefix_attn: for each group of M sequences, attention of
+ *      all M queries over the group's shared prefix, every query seeing every
+ *      prefix token (one pass over the prefix blocks serves G*M columns);
+ *   2. pkv_paged_decode_attn_lse: each sequence's attention over its own
+ *      tokens after the prefix (tables and lengths of the suffixes);
+ *   3. pkv_merge_attn_states: the exact combination of the two states.
+ *
+ * For a row (sequence i, head h) the result is the decode attention of
+ * pkv_paged_decode_attn over all L_i tokens: with A = the prefix tokens and
+ * B = the suffix tokens, out = (2^la o_A + 2^lb o_B) / (2^la + 2^lb), where
+ * o_X and lx = log2 sum_{t in X} exp(s_t) (the scores s_t as in
+ * pkv_paged_decode_attn, including k_scale) are what calls 1 and 2 return.
+ */
+
+/* Call 2: pkv_paged_decode_attn with the balanced split (same workspace size,
+ * partition_size PKV_PARTITION_BALANCED) that also writes lse[S][Hq] (float32,
+ * device): log2 of each row's sum of exp(s_t) over its tokens; -inf for a
+ * sequence with L_i <= 0 (whose row is zero). */
+pkv_status pkv_paged_decode_attn_lse(float* out, float* lse, const void* q, const void* k_cache,
+                                     const void* v_cache, const int32_t* block_tables,
+                                     const int32_t* context_lens, int32_t S, int32_t Hq,
+                                     int32_t Hkv, int32_t d, int32_t bs, int32_t P,
+                                     int32_t max_blocks, int32_t max_context_len,
+                                     float softmax_scale, float k_scale, float v_scale,
+                                     pkv_dtype q_dtype, pkv_dtype cache_dtype, void* workspace,
+                                     size_t workspace_bytes, void* stream);
+
+/* Call 1: n_groups groups of M queries each. q: [n_groups][M][Hq][d] (query m
+ * of group g is the g*M + m-th sequence's q); prefix_tables [n_groups]
+ * [max_blocks] and prefix_lens [n_groups] describe each group's shared prefix
+ * (a whole number of blocks). out: float32 [n_groups][M][Hq][d]; lse:
+ * float32 [n_groups][M][Hq] as for call 2. Every query attends to all
+ * prefix_lens[g] tokens (no causal mask). workspace as
+ * pkv_paged_multi_query_attn_workspace_size(n_groups, M, Hq, Hkv, d); other
+ * arguments and limits as for pkv_paged_multi_query_attn (1 <= M <= 4096). */
+pkv_status pkv_paged_shared_prefix_attn(float* out, float* lse, const void* q, const void* k_cache,
+                                        const void* v_cache, const int32_t* prefix_tables,
+                                        const int32_t* prefix_lens, int32_t n_groups, int32_t M,
+                                        int32_t Hq, int32_t Hkv, int32_t d, int32_t bs, int32_t P,
+                                        int32_t max_blocks, int32_t max_prefix_len,
+                                        float softmax_scale, float k_scale, float v_scale,
+                                        pkv_dtype q_dtype, pkv_dtype cache_dtype, void* workspace,
+                                        size_t workspace_bytes, void* stream);
+
+/* Call 3: out[r] = (2^la[r] a[r] + 2^lb[r] b[r]) / (2^la[r] + 2^lb[r]) for rows
+ * r < rows of d floats (device, float32); a side with lse -inf has weight 0
+ * and a row with both -inf is zero. lse_out (optional, may be NULL) receives
+ * log2(2^la + 2^lb). out may alias a or b. d in {64, 128}. */
+pkv_status pkv_merge_attn_states(float* out, float* lse_out, const float* a, const float* lse_a,
+                                 const float* b, const float* lse_b, int64_t rows, int32_t d,
+                                 void* stream);
+
+/*
  * Copy whole blocks inside both pools: for each k < n, block dst[k] becomes a
  * copy of block src[k] (every kv head, K and V). This is the device half of
  * copy-on-write: pkv_seq_append reports the (src, dst) pair when a sequence

@@ -9,7 +9,8 @@ from .api import (kv_cache_write, copy_blocks, paged_decode_attn, paged_decode_s
                   paged_decode_attn_workspace, paged_multi_query_attn,
                   paged_multi_query_attn_workspace, Allocator,
                   slots_from_tables, waste_stats, block_hashes, last_error, version, quantise_pool, PkvError,
-                  NoBlocks, PKV_PARTITION_BALANCED)
+                  NoBlocks, PKV_PARTITION_BALANCED, paged_decode_attn_lse, paged_shared_prefix_attn,
+                  merge_attn_states, shared_prefix_plan, SharedPrefixDecode, v_shape_ok)
 from ._lib import lib, LIB_PATH, SIGNATURES, PKV_F32, PKV_BF16, PKV_FP8_E4M3
 
 __all__ = [
@@ -18,5 +19,6 @@ __all__ = [
     "paged_decode_attn_workspace", "paged_multi_query_attn", "paged_multi_query_attn_workspace",
     "Allocator",
     "slots_from_tables", "waste_stats", "block_hashes", "last_error", "version", "quantise_pool", "PkvError",
-    "NoBlocks", "PKV_PARTITION_BALANCED", "lib", "LIB_PATH", "SIGNATURES", "PKV_F32", "PKV_BF16", "PKV_FP8_E4M3",
+    "NoBlocks", "PKV_PARTITION_BALANCED", "paged_decode_attn_lse", "paged_shared_prefix_attn",
+    "merge_attn_states", "shared_prefix_plan", "SharedPrefixDecode", "v_shape_ok", "lib", "LIB_PATH", "SIGNATURES", "PKV_F32", "PKV_BF16", "PKV_FP8_E4M3",
 ]

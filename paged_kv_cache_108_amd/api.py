@@ -222,6 +222,153 @@ def paged_multi_query_attn(out, q, k_cache, v_cache, block_tables, context_lens,
         _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
+def paged_decode_attn_lse(out, lse, q, k_cache, v_cache, block_tables, context_lens, *,
+                          max_context_len, softmax_scale, k_scale=1.0, v_scale=1.0, workspace=None,
+                          stream=None):
+    """pkv_paged_decode_attn_lse: balanced decode attention that also writes
+    lse float32 [S][Hq], the base-2 log of each row's softmax sum."""
+    import torch
+    S, Hq, d = q.shape
+    P, Hkv, bs, _ = k_cache.shape
+    if tuple(out.shape) != (S, Hq, d) or out.dtype != torch.float32:
+        raise ValueError("paged_decode_attn_lse: out must be float32 [S][Hq][d]")
+    if tuple(lse.shape) != (S, Hq) or lse.dtype != torch.float32:
+        raise ValueError("paged_decode_attn_lse: lse must be float32 [S][Hq]")
+    if not v_shape_ok(v_cache, P, Hkv, d, bs):
+        raise ValueError("paged_decode_attn_lse: v_cache shape")
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise ValueError("paged_decode_attn_lse: tables and lengths must be int32")
+    if block_tables.shape[0] != S or context_lens.shape != (S,):
+        raise ValueError("paged_decode_attn_lse: tables/lengths shape mismatch")
+    if workspace is None:
+        workspace = paged_decode_attn_workspace(S, Hq, Hkv, d, int(max_context_len),
+                                                PKV_PARTITION_BALANCED, device=q.device)
+    check(lib().pkv_paged_decode_attn_lse(
+        _dev(out, "out"), _dev(lse, "lse"), _dev(q, "q"), _dev(k_cache, "k_cache"),
+        _dev(v_cache, "v_cache"), _dev(block_tables, "block_tables"), _dev(context_lens, "context_lens"),
+        S, Hq, Hkv, d, bs, P, block_tables.shape[1], int(max_context_len), float(softmax_scale),
+        float(k_scale), float(v_scale), _dtype_code(q), _dtype_code(k_cache), _dev(workspace, "workspace"),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def paged_shared_prefix_attn(out, lse, q, k_cache, v_cache, prefix_tables, prefix_lens, *,
+                             max_prefix_len, softmax_scale, k_scale=1.0, v_scale=1.0, workspace=None,
+                             stream=None):
+    """pkv_paged_shared_prefix_attn: q [n_groups][M][Hq][d]; every query of a
+    group attends to all of the group's prefix tokens. out float32
+    [n_groups][M][Hq][d], lse float32 [n_groups][M][Hq]."""
+    import torch
+    n_groups, M, Hq, d = q.shape
+    P, Hkv, bs, _ = k_cache.shape
+    if tuple(out.shape) != (n_groups, M, Hq, d) or out.dtype != torch.float32:
+        raise ValueError("paged_shared_prefix_attn: out must be float32 [n_groups][M][Hq][d]")
+    if tuple(lse.shape) != (n_groups, M, Hq) or lse.dtype != torch.float32:
+        raise ValueError("paged_shared_prefix_attn: lse must be float32 [n_groups][M][Hq]")
+    if not v_shape_ok(v_cache, P, Hkv, d, bs):
+        raise ValueError("paged_shared_prefix_attn: v_cache shape")
+    if prefix_tables.dtype != torch.int32 or prefix_lens.dtype != torch.int32:
+        raise ValueError("paged_shared_prefix_attn: tables and lengths must be int32")
+    if prefix_tables.shape[0] != n_groups or prefix_lens.shape != (n_groups,):
+        raise ValueError("paged_shared_prefix_attn: tables/lengths shape mismatch")
+    if workspace is None:
+        workspace = paged_multi_query_attn_workspace(n_groups, M, Hq, Hkv, d, device=q.device)
+    check(lib().pkv_paged_shared_prefix_attn(
+        _dev(out, "out"), _dev(lse, "lse"), _dev(q, "q"), _dev(k_cache, "k_cache"),
+        _dev(v_cache, "v_cache"), _dev(prefix_tables, "prefix_tables"), _dev(prefix_lens, "prefix_lens"),
+        n_groups, M, Hq, Hkv, d, bs, P, prefix_tables.shape[1], int(max_prefix_len), float(softmax_scale),
+        float(k_scale), float(v_scale), _dtype_code(q), _dtype_code(k_cache), _dev(workspace, "workspace"),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def merge_attn_states(out, a, lse_a, b, lse_b, *, lse_out=None, stream=None):
+    """pkv_merge_attn_states over rows of d floats: a, b, out float32 [..., d];
+    lse_a, lse_b (and lse_out) float32 with one value per row."""
+    import torch
+    d = a.shape[-1]
+    rows = a.numel() // d
+    for t, name in ((out, "out"), (a, "a"), (b, "b")):
+        if t.dtype != torch.float32 or t.numel() != rows * d:
+            raise ValueError(f"merge_attn_states: {name} must be float32 with {rows} rows of {d}")
+    for t, name in ((lse_a, "lse_a"), (lse_b, "lse_b")) + (((lse_out, "lse_out"),) if lse_out is not None else ()):
+        if t.dtype != torch.float32 or t.numel() != rows:
+            raise ValueError(f"merge_attn_states: {name} must be float32 with {rows} values")
+    check(lib().pkv_merge_attn_states(
+        _dev(out, "out"), _dev(lse_out, "lse_out") if lse_out is not None else None, _dev(a, "a"),
+        _dev(lse_a, "lse_a"), _dev(b, "b"), _dev(lse_b, "lse_b"), rows, d, _stream(stream)))
+
+
+def shared_prefix_plan(block_tables, context_lens, group_size, bs):
+    """Host side of shared-prefix decode for groups of group_size consecutive
+    sequences (beams, parallel samples): per group, the leading blocks that
+    every member lists with the same id and fills completely, as (prefix
+    tables [n_groups][max_blocks], prefix lengths [n_groups], suffix tables
+    [S][max_blocks], suffix lengths [S]) int32 numpy arrays. A group that
+    shares nothing gets a prefix of length 0."""
+    tables = np.asarray(block_tables, dtype=np.int32)
+    lens = np.asarray(context_lens, dtype=np.int64)
+    S, max_blocks = tables.shape
+    if group_size < 1 or S % group_size:
+        raise ValueError("shared_prefix_plan: S must be a multiple of group_size")
+    n_groups = S // group_size
+    pre_tab = np.full((n_groups, max_blocks), -1, dtype=np.int32)
+    pre_len = np.zeros(n_groups, dtype=np.int32)
+    suf_tab = np.full((S, max_blocks), -1, dtype=np.int32)
+    suf_len = np.zeros(S, dtype=np.int32)
+    for g in range(n_groups):
+        members = range(g * group_size, (g + 1) * group_size)
+        full = min(max(int(lens[i]), 0) // bs for i in members)
+        k = 0
+        while k < full and all(tables[i, k] == tables[g * group_size, k] for i in members):
+            k += 1
+        pre_tab[g, :k] = tables[g * group_size, :k]
+        pre_len[g] = k * bs
+        for i in members:
+            n = max(int(lens[i]), 0)
+            nb = -(-n // bs)
+            suf_tab[i, :nb - k] = tables[i, k:nb]
+            suf_len[i] = n - k * bs if n > 0 else n
+    return pre_tab, pre_len, suf_tab, suf_len
+
+
+class SharedPrefixDecode:
+    """Decode attention for groups of group_size consecutive sequences that share
+    leading blocks, reading the shared blocks once per group: one
+    pkv_paged_shared_prefix_attn over the prefixes, one
+    pkv_paged_decode_attn_lse over the suffixes and one pkv_merge_attn_states.
+    The plan (host tables, see shared_prefix_plan) is built once here and
+    uploaded; __call__ runs the three device calls."""
+
+    def __init__(self, block_tables, context_lens, group_size, bs, Hq, Hkv, d, device="cuda"):
+        import torch
+        pre_tab, pre_len, suf_tab, suf_len = shared_prefix_plan(block_tables, context_lens, group_size, bs)
+        S = len(suf_len)
+        self.M, self.n_groups, self.S, self.Hq, self.d = group_size, S // group_size, S, Hq, d
+        self.max_prefix = int(pre_len.max()) if len(pre_len) else 0
+        self.max_suffix = int(suf_len.max()) if len(suf_len) else 0
+        self.prefix_tokens = int(pre_len.sum())
+        self.pre_tab = torch.from_numpy(pre_tab).to(device)
+        self.pre_len = torch.from_numpy(pre_len).to(device)
+        self.suf_tab = torch.from_numpy(suf_tab).to(device)
+        self.suf_len = torch.from_numpy(suf_len).to(device)
+        f32 = dict(dtype=torch.float32, device=device)
+        self.out_p = torch.empty((self.n_groups, group_size, Hq, d), **f32)
+        self.lse_p = torch.empty((self.n_groups, group_size, Hq), **f32)
+        self.out_s = torch.empty((S, Hq, d), **f32)
+        self.lse_s = torch.empty((S, Hq), **f32)
+        self.ws_p = paged_multi_query_attn_workspace(self.n_groups, group_size, Hq, Hkv, d, device=device)
+        self.ws_s = paged_decode_attn_workspace(S, Hq, Hkv, d, max(self.max_suffix, 1), PKV_PARTITION_BALANCED,
+                                                device=device)
+
+    def __call__(self, out, q, k_cache, v_cache, *, softmax_scale, k_scale=1.0, v_scale=1.0, stream=None):
+        kw = dict(softmax_scale=softmax_scale, k_scale=k_scale, v_scale=v_scale, stream=stream)
+        qg = q.view(self.n_groups, self.M, self.Hq, self.d)
+        paged_shared_prefix_attn(self.out_p, self.lse_p, qg, k_cache, v_cache, self.pre_tab, self.pre_len,
+                                 max_prefix_len=self.max_prefix, workspace=self.ws_p, **kw)
+        paged_decode_attn_lse(self.out_s, self.lse_s, q, k_cache, v_cache, self.suf_tab, self.suf_len,
+                              max_context_len=self.max_suffix, workspace=self.ws_s, **kw)
+        merge_attn_states(out, self.out_p, self.lse_p, self.out_s, self.lse_s, stream=stream)
+
+
 def quantise_pool(values_k, values_v, codes_k, codes_v, *, k_inv_scale, v_inv_scale, stream=None):
     """Fill whole fp8 pools from bf16 pools of the same layout, through the
     library's cache write (every slot written once, in order)."""

@@ -233,6 +233,8 @@ struct AttnParams {
     float k_inv, v_inv;    // decode step, fp8 cache: inverse scales of the write
     float qk_scale;        // softmax_scale * k_scale * log2(e): scores in the log2 domain
     float v_scale;
+    float* lse;            // optional [rows]: base-2 log of each output row's softmax sum
+    int causal;            // query windows: 1 causal inside the window, 0 every query sees all L
 };
 
 // Per-cache-type register fragments of one 16-token chunk.
@@ -943,9 +945,13 @@ paged_attn_stream_kernel(AttnParams p) {
 
     prefix_over_sequences(p, pre, wsum, sL, [&](int, int L) { return span_of(L); });
     for (int s = blockIdx.x; s < p.S; s += gridDim.x)       // sequences with no tokens: zero rows
-        if (seq_len(s) <= 0)
+        if (seq_len(s) <= 0) {
             for (int e = threadIdx.x; e < n_q * p.Hq * D; e += kThreads)
                 p.out[(size_t)s * n_q * p.Hq * D + e] = 0.f;
+            if (p.lse)
+                for (int e = threadIdx.x; e < n_q * p.Hq; e += kThreads)
+                    p.lse[(size_t)s * n_q * p.Hq + e] = -INFINITY;
+        }
 
     const unsigned V = (unsigned)pre[kThreads] * (unsigned)HS;   // positions in all
     const unsigned W = gridDim.x * kWaves;
@@ -1157,12 +1163,12 @@ paged_attn_stream_kernel(AttnParams p) {
                 if (kc == nch - 1) patch_new_token<KV, D>(f, nt, L - 1 - tc, r16, j4);
             const bool tail = tc + 16 > L;        // tokens >= L hold no data
             // query j sees tokens < L - n_q + 1 + j (causal inside the window)
-            const bool masked = MQ ? tc + 16 > L - n_q + 1 : tail;
+            const bool masked = MQ && p.causal ? tc + 16 > L - n_q + 1 : tail;
             const int first_tok = tc + 4 * j4;
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
                 const f32x4 sc = chunk_scores<KV, D>(f, qf[t]);
-                const int lim = MQ ? L - n_q + 1 + j[t] : L;
+                const int lim = MQ && p.causal ? L - n_q + 1 + j[t] : L;
                 float x[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
@@ -1200,6 +1206,7 @@ paged_attn_stream_kernel(AttnParams p) {
 #pragma unroll
                             for (int s = 0; s < D / 16; ++s)
                                 *reinterpret_cast<f32x4*>(orow + 16 * s) = o[t][s] * sc_o;
+                            if (p.lse && j4 == 0) p.lse[out_row[t] / D] = m_run[t] + __log2f(l_tot);
                         } else {
                             const size_t rr = (size_t)(2 * w + (seg_at_range_start ? 0 : 1)) * C + 16 * t + r16;
                             const size_t nrec = (size_t)p.n_rec;
@@ -1318,6 +1325,7 @@ paged_attn_merge_kernel(AttnParams p) {
         }
 #pragma unroll
         for (int x = 0; x < PER; ++x) p.out[h * D + lane + 64 * x] = num[x] / den;
+        if (p.lse && lane == 0) p.lse[h] = M + __log2f(den);
         return;
     }
     float M = -INFINITY;
@@ -1364,6 +1372,39 @@ paged_attn_merge_kernel(AttnParams p) {
     for (int off = 32; off > 0; off >>= 1) den += __shfl_xor(den, off);
 #pragma unroll
     for (int x = 0; x < PER; ++x) p.out[h * D + lane + 64 * x] = num[x] / den;
+    if (p.lse && lane == 0) p.lse[h] = M + __log2f(den);
+}
+
+// Two attention states of the same rows over disjoint token sets (a shared
+// prefix and a private suffix): out = (2^la a + 2^lb b) / (2^la + 2^lb) per
+// row, with la, lb the rows' base-2 log softmax sums. A side with lse = -inf
+// saw no token and gets weight 0; a row with both -inf is 0. One wave per row.
+template <int D>
+__global__ void __launch_bounds__(kThreads)
+merge_states_kernel(float* __restrict__ out, float* __restrict__ lse_out, const float* __restrict__ a,
+                    const float* __restrict__ lse_a, const float* __restrict__ b,
+                    const float* __restrict__ lse_b, long long rows) {
+    const long long r = (long long)blockIdx.x * kWaves + (threadIdx.x >> 6);
+    if (r >= rows) return;
+    const int lane = threadIdx.x & 63;
+    const float la = lse_a[r], lb = lse_b[r];
+    const float M = fmaxf(la, lb);
+    constexpr int PER = D / 64;
+    if (M == -INFINITY) {
+#pragma unroll
+        for (int x = 0; x < PER; ++x) out[r * D + lane + 64 * x] = 0.f;
+        if (lse_out && lane == 0) lse_out[r] = -INFINITY;
+        return;
+    }
+    const float wa = __builtin_amdgcn_exp2f(la - M);
+    const float wb = __builtin_amdgcn_exp2f(lb - M);
+    const float den = wa + wb;
+#pragma unroll
+    for (int x = 0; x < PER; ++x) {
+        const size_t e = r * D + lane + 64 * x;
+        out[e] = (wa * a[e] + wb * b[e]) / den;
+    }
+    if (lse_out && lane == 0) lse_out[r] = M + __log2f(den);
 }
 
 // ----------------------------------------------------------------------------
@@ -1576,7 +1617,8 @@ pkv_status attn_launch(const char* fn, float* out, const void* q, const void* k_
                        int32_t P, int32_t max_blocks, int32_t max_context_len, float softmax_scale,
                        float k_scale, float v_scale, pkv_dtype q_dtype, pkv_dtype cache_dtype,
                        int32_t partition_size, void* workspace, size_t workspace_bytes, void* stream,
-                       const StepWrite& step = StepWrite()) {
+                       const StepWrite& step = StepWrite(), float* lse = nullptr,
+                       bool causal = true) {
     const bool is_step = step.k_new != nullptr || step.v_new != nullptr;
     if (S < 0 || Hq <= 0 || Hkv <= 0) return fail(PKV_E_INVALID, "%s: S=%d Hq=%d Hkv=%d", fn, S, Hq, Hkv);
     if (n_q < 1 || n_q > 4096) return fail(PKV_E_INVALID, "%s: n_q=%d outside [1, 4096]", fn, n_q);
@@ -1652,6 +1694,8 @@ pkv_status attn_launch(const char* fn, float* out, const void* q, const void* k_
     const float ks = kv == KV_FP8 ? k_scale : 1.f;
     prm.qk_scale = softmax_scale * ks * kLog2e;
     prm.v_scale = kv == KV_FP8 ? v_scale : 1.f;
+    prm.lse = lse;
+    prm.causal = causal ? 1 : 0;
     prm.cache_lens = S <= kMaxCachedLens;
 
     AttnKernel kern;
@@ -1759,4 +1803,59 @@ extern "C" pkv_status pkv_paged_decode_step(float* out, const void* q, const voi
     return attn_launch("paged_decode_step", out, q, k_cache, v_cache, block_tables, context_lens, S, 1,
                        Hq, Hkv, d, bs, P, max_blocks, max_context_len, softmax_scale, k_scale, v_scale,
                        q_dtype, cache_dtype, PKV_PARTITION_BALANCED, workspace, workspace_bytes, stream, w);
+}
+
+extern "C" pkv_status pkv_paged_decode_attn_lse(float* out, float* lse, const void* q,
+                                                const void* k_cache, const void* v_cache,
+                                                const int32_t* block_tables,
+                                                const int32_t* context_lens, int32_t S, int32_t Hq,
+                                                int32_t Hkv, int32_t d, int32_t bs, int32_t P,
+                                                int32_t max_blocks, int32_t max_context_len,
+                                                float softmax_scale, float k_scale, float v_scale,
+                                                pkv_dtype q_dtype, pkv_dtype cache_dtype,
+                                                void* workspace, size_t workspace_bytes,
+                                                void* stream) {
+    if (S > 0 && !lse) return fail(PKV_E_INVALID, "paged_decode_attn_lse: NULL pointer");
+    return attn_launch("paged_decode_attn_lse", out, q, k_cache, v_cache, block_tables, context_lens, S,
+                       1, Hq, Hkv, d, bs, P, max_blocks, max_context_len, softmax_scale, k_scale,
+                       v_scale, q_dtype, cache_dtype, PKV_PARTITION_BALANCED, workspace,
+                       workspace_bytes, stream, StepWrite(), lse, true);
+}
+
+extern "C" pkv_status pkv_paged_shared_prefix_attn(float* out, float* lse, const void* q,
+                                                   const void* k_cache, const void* v_cache,
+                                                   const int32_t* prefix_tables,
+                                                   const int32_t* prefix_lens, int32_t n_groups,
+                                                   int32_t M, int32_t Hq, int32_t Hkv, int32_t d,
+                                                   int32_t bs, int32_t P, int32_t max_blocks,
+                                                   int32_t max_prefix_len, float softmax_scale,
+                                                   float k_scale, float v_scale, pkv_dtype q_dtype,
+                                                   pkv_dtype cache_dtype, void* workspace,
+                                                   size_t workspace_bytes, void* stream) {
+    if (n_groups > 0 && !lse) return fail(PKV_E_INVALID, "paged_shared_prefix_attn: NULL pointer");
+    return attn_launch("paged_shared_prefix_attn", out, q, k_cache, v_cache, prefix_tables, prefix_lens,
+                       n_groups, M, Hq, Hkv, d, bs, P, max_blocks, max_prefix_len, softmax_scale,
+                       k_scale, v_scale, q_dtype, cache_dtype, PKV_PARTITION_BALANCED, workspace,
+                       workspace_bytes, stream, StepWrite(), lse, false);
+}
+
+extern "C" pkv_status pkv_merge_attn_states(float* out, float* lse_out, const float* a,
+                                            const float* lse_a, const float* b, const float* lse_b,
+                                            int64_t rows, int32_t d, void* stream) {
+    if (rows < 0) return fail(PKV_E_INVALID, "merge_attn_states: rows=%lld < 0", (long long)rows);
+    if (!pkv::is_head_dim(d)) return fail(PKV_E_INVALID, "merge_attn_states: d=%d not in {64,128}", d);
+    if (rows == 0) return ok();
+    if (!out || !a || !lse_a || !b || !lse_b) return fail(PKV_E_INVALID, "merge_attn_states: NULL pointer");
+    if (rows > (int64_t)0x7FFFFFFF * kWaves) return fail(PKV_E_INVALID, "merge_attn_states: too many rows");
+    const unsigned grid = (unsigned)((rows + kWaves - 1) / kWaves);
+    auto st = static_cast<hipStream_t>(stream);
+    if (d == 64)
+        hipLaunchKernelGGL(merge_states_kernel<64>, dim3(grid), dim3(kThreads), 0, st, out, lse_out, a,
+                           lse_a, b, lse_b, (long long)rows);
+    else
+        hipLaunchKernelGGL(merge_states_kernel<128>, dim3(grid), dim3(kThreads), 0, st, out, lse_out, a,
+                           lse_a, b, lse_b, (long long)rows);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(PKV_E_HIP, "merge_attn_states: launch failed: %s", hipGetErrorString(e));
+    return ok();
 }

@@ -566,3 +566,72 @@ def test_many_sequences_lengths_read_from_memory():
 
 def test_many_sequences_window():
     _window_case(W.make_custom(lens=_many_lens(5), Hq=8, Hkv=2, d=64, bs=16, cfg=4102), 5)
+
+
+# ------------------------------------------------------------------ shared-prefix decode (beams)
+def _shared_prefix_case(w, group_size):
+    torch = need_gpu()
+    s = w.spec
+    print(f"[case] shared prefix {s.name} bs={s.bs} cache={s.cache_dtype} M={group_size}", flush=True)
+    dev = DeviceStep(w)
+    dev.write()
+    slots, kc, vc, ref = oracle_step(w)
+    run = pkv.SharedPrefixDecode(w.block_tables, w.context_lens, group_size, s.bs, s.Hq, s.Hkv, s.d)
+    out = torch.empty((s.S, s.Hq, s.d), dtype=torch.float32, device="cuda")
+    for _ in range(2):                          # the second call reuses the plan's buffers
+        run(out, dev.q, dev.k_cache, dev.v_cache, softmax_scale=w.softmax_scale, k_scale=w.k_scale,
+            v_scale=w.v_scale)
+    torch.cuda.synchronize()
+    e = assert_rows_close(to_host(out), ref, TOL[s.cache_dtype], f"shared prefix {s.name}")
+    print(f"[case] max row err {e:.3e}; prefix tokens {run.prefix_tokens}", flush=True)
+    return run
+
+
+@pytest.mark.parametrize("bs", [8, 16, 32])
+def test_shared_prefix_beam(bs):
+    run = _shared_prefix_case(W.make("beam", bs=bs), 4)
+    assert run.prefix_tokens == 32 * 1024          # every group shares its 1024-token prompt
+
+
+def test_shared_prefix_edge_groups():
+    # groups of 3: group 0 shares 4 full blocks and one member has no token
+    # after them (empty suffix); group 1 shares nothing (its tables differ from
+    # the first block); group 2 has a member with no tokens at all
+    bs, Hq, Hkv, d = 16, 8, 2, 64
+    lens = [64, 70, 90, 20, 33, 5, 0, 40, 41]
+    w = W.make_custom(lens=lens, Hq=Hq, Hkv=Hkv, d=d, bs=bs, cfg=991, pool_factor=3.0)
+    tab = w.block_tables.copy()
+    tab[1, :4] = tab[0, :4]
+    tab[2, :4] = tab[0, :4]
+    tab[7, :2] = tab[8, :2]                        # group 2: the zero-length member lists nothing
+    w.block_tables[:] = tab
+    pre_tab, pre_len, suf_tab, suf_len = pkv.shared_prefix_plan(tab, lens, 3, bs)
+    assert list(pre_len) == [64, 0, 0] and list(suf_len[:3]) == [0, 6, 26]
+    _shared_prefix_case(w, 3)
+
+
+def test_merge_attn_states_edges():
+    torch = need_gpu()
+    rng = np.random.default_rng(5)
+    rows, d = 37, 128
+    a = rng.standard_normal((rows, d)).astype(np.float32)
+    b = rng.standard_normal((rows, d)).astype(np.float32)
+    la = rng.normal(0, 3, rows).astype(np.float32)
+    lb = rng.normal(0, 3, rows).astype(np.float32)
+    la[3] = -np.inf
+    lb[4] = -np.inf
+    la[5] = lb[5] = -np.inf
+    out = torch.empty((rows, d), dtype=torch.float32, device="cuda")
+    lo = torch.empty(rows, dtype=torch.float32, device="cuda")
+    pkv.merge_attn_states(out, to_dev(a), to_dev(la), to_dev(b), to_dev(lb), lse_out=lo)
+    torch.cuda.synchronize()
+    got, glo = to_host(out), to_host(lo)
+    m = np.maximum(la.astype(np.float64), lb)
+    for r in range(rows):
+        if m[r] == -np.inf:
+            assert np.all(got[r] == 0) and glo[r] == -np.inf
+            continue
+        wa, wb = 2.0 ** (la[r] - m[r]), 2.0 ** (lb[r] - m[r])
+        want = (wa * a[r] + wb * b[r]) / (wa + wb)
+        assert np.max(np.abs(got[r] - want)) <= 1e-5 * max(1.0, np.max(np.abs(want)))
+        assert abs(glo[r] - (m[r] + np.log2(wa + wb))) <= 1e-5 * max(1.0, abs(glo[r]))
