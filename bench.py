@@ -226,18 +226,19 @@ def run_other_op(args, w, torch, pkv):
                "note": "value counts K/V once; a window needing several passes reads K/V once per pass "
                        "(bytes_with_passes)"}
     elif args.op == "shared":
-        q = dev(w.q)
+        q, k_new, v_new = dev(w.q), dev(w.k_new), dev(w.v_new)
         run = pkv.SharedPrefixDecode(w.block_tables, w.context_lens, args.group, s.bs, s.Hq, s.Hkv, s.d)
         out = torch.empty((s.S, s.Hq, s.d), dtype=torch.float32, device="cuda")
 
         def fn():
             run(out, q, k_cache, v_cache, softmax_scale=w.softmax_scale, k_scale=w.k_scale,
-                v_scale=w.v_scale, stream=stream)
-        attn, _, logical, unique_tokens = algorithmic_bytes(w, cache_dtype)
-        byts = attn                                        # unique K/V once, q, out, tables, lengths
-        metric = "shared-prefix decode attention: achieved HBM GB/s at 1 GPU"
-        kernel = ("SharedPrefixDecode (shared-prefix window kernel + merge, suffix stream kernel + merge, "
-                  "state merge)")
+                v_scale=w.v_scale, k_new=k_new, v_new=v_new, k_inv_scale=w.k_inv_scale,
+                v_inv_scale=w.v_inv_scale, stream=stream)
+        attn, write, logical, unique_tokens = algorithmic_bytes(w, cache_dtype)
+        byts = attn + write                  # unique K/V once, q, out, tables, lengths; the write
+        metric = "shared-prefix decode step (write + attention): achieved HBM GB/s at 1 GPU"
+        kernel = ("pkv_paged_shared_prefix_decode call (suffix stream kernel with the write, prefix "
+                  "window kernel, shared-prefix merge kernel)")
         cfg = {"group": args.group, "prefix_tokens": run.prefix_tokens, "unique_tokens": int(unique_tokens),
                "context_tokens": int(w.context_lens.sum()), "kv_bytes_logical": int(logical)}
     else:
@@ -331,8 +332,8 @@ def main():
                     help="step: the decode step (default); window: pkv_paged_multi_query_attn over "
                          "windows of --window queries per sequence; copy: pkv_copy_blocks of --pairs "
                          "(src, dst) block pairs; prefix: host-side prefix-cache admission "
-                         "(pkv_seq_create_prefixed), no GPU; shared: shared-prefix decode attention "
-                         "(prefix pass + suffix pass + merge) for groups of --group sequences")
+                         "(pkv_seq_create_prefixed), no GPU; shared: shared-prefix decode step "
+                         "(pkv_paged_shared_prefix_decode) for groups of --group sequences")
     ap.add_argument("--window", type=int, default=4, help="queries per sequence for --op window")
     ap.add_argument("--pairs", type=int, default=1024, help="block pairs for --op copy")
     ap.add_argument("--group", type=int, default=4, help="sequences per group for --op shared")

@@ -312,6 +312,42 @@ pkv_status pkv_merge_attn_states(float* out, float* lse_out, const float* a, con
                                  void* stream);
 
 /*
+ * The three calls above in one, plus the decode step's write, with a single
+ * merge: groups of M consecutive sequences (sequence g*M + m is member m of
+ * group g) whose tables start with the same blocks. prefix_tables/prefix_lens
+ * ([n_groups][prefix_max_blocks], [n_groups]) list each group's shared
+ * blocks; suffix_tables/suffix_lens ([S][suffix_max_blocks], [S], S =
+ * n_groups*M) list each sequence's blocks after them. A sequence's context is
+ * its group's prefix followed by its suffix; out[S][Hq][d] (float32) is the
+ * decode attention of pkv_paged_decode_attn over that whole context.
+ *
+ * k_new/v_new ([S][Hkv][d], as for pkv_kv_cache_write; both NULL: no write)
+ * are each sequence's new token: it is written at the suffix's last position
+ * (suffix_lens[i] - 1; sequences with an empty suffix write nothing), before
+ * any attention reads the pools, and attended to. So a plan whose suffixes
+ * keep each sequence's last block (the one that takes the new token) makes
+ * this one decode step, like pkv_paged_decode_step.
+ *
+ * Order on `stream`: the suffix pass (with the write), the prefix pass (every
+ * query of a group sees every prefix token), then one merge kernel over the
+ * partial states of both. workspace: pkv_paged_shared_prefix_decode_workspace_size
+ * bytes (device, caller-owned, any contents). Limits and dtypes as for
+ * pkv_paged_decode_step and pkv_paged_multi_query_attn (1 <= M <= 4096);
+ * k_inv_scale/v_inv_scale are used only for an fp8 cache with a write.
+ */
+size_t pkv_paged_shared_prefix_decode_workspace_size(int32_t n_groups, int32_t M, int32_t Hq,
+                                                     int32_t Hkv, int32_t d);
+
+pkv_status pkv_paged_shared_prefix_decode(
+    float* out, const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+    const int32_t* prefix_tables, const int32_t* prefix_lens, int32_t prefix_max_blocks,
+    int32_t max_prefix_len, const int32_t* suffix_tables, const int32_t* suffix_lens,
+    int32_t suffix_max_blocks, int32_t max_suffix_len, int32_t n_groups, int32_t M, int32_t Hq,
+    int32_t Hkv, int32_t d, int32_t bs, int32_t P, float softmax_scale, float k_scale, float v_scale,
+    float k_inv_scale, float v_inv_scale, pkv_dtype q_dtype, pkv_dtype cache_dtype, void* workspace,
+    size_t workspace_bytes, void* stream);
+
+/*
  * Copy whole blocks inside both pools: for each k < n, block dst[k] becomes a
  * copy of block src[k] (every kv head, K and V). This is the device half of
  * copy-on-write: pkv_seq_append reports the (src, dst) pair when a sequence

@@ -19,6 +19,9 @@ Every function is written from the pages' statement of what is computed:
 * "Serving: vLLM and PagedAttention" (henryfzh-note.com): section 2.2 (block
   table, last-block fill, tail-waste arithmetic); sections 2.4 and 2.7 (windows
   of several new queries over the same cache: ``paged_multi_query_attn``).
+* Shared prefix blocks ("03 · PagedAttention", "Sharing: copy-on-write"):
+  ``paged_decode_lse`` and ``merge_attn_states`` give the state of an attention
+  over part of a sequence and the exact combination of two such parts.
 
 The attention itself is the textbook definition applied to the sequence's
 K/V reassembled in logical order: the pages state that paging changes only the
@@ -32,7 +35,8 @@ invariants the pages state, a library routine on tiny inputs, brute force.
 
 from .codecs import (bf16_bits_to_f64, f32_to_f64, e4m3_value_table, e4m3_decode,
                      e4m3_encode)
-from .attention import reassemble, paged_decode_attn, contiguous_decode_attn, paged_multi_query_attn
+from .attention import (reassemble, paged_decode_attn, contiguous_decode_attn, paged_multi_query_attn,
+                        contiguous_decode_lse, paged_decode_lse, merge_attn_states)
 from .cache_write import kv_cache_write, quantise, copy_blocks
 from .slots import decode_slots, slots_for_positions
 from .waste import (blocks_for, paged_slots, naive_slots, tail_slots, utilisation,
@@ -43,6 +47,7 @@ from .splitk import partition_then_merge
 __all__ = [
     "bf16_bits_to_f64", "f32_to_f64", "e4m3_value_table", "e4m3_decode", "e4m3_encode",
     "reassemble", "paged_decode_attn", "contiguous_decode_attn", "paged_multi_query_attn",
+    "contiguous_decode_lse", "paged_decode_lse", "merge_attn_states",
     "kv_cache_write", "quantise",
     "copy_blocks",
     "decode_slots", "slots_for_positions", "blocks_for", "paged_slots",

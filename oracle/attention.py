@@ -142,3 +142,64 @@ def paged_multi_query_attn(q, k_cache, v_cache, block_tables, context_lens, *, b
                                       cache_dtype=cache_dtype, k_scale=k_scale, v_scale=v_scale,
                                       seqs=rows)
     return out
+
+
+def contiguous_decode_lse(q_i, K, sigma):
+    """[Hq]: log2 of each head's softmax denominator, log2 sum_t exp(s_t), over
+    contiguous float64 K ([L][Hkv][d]) with s_t = sigma * q . K_t; -inf when
+    L <= 0. This is the state that lets two attentions over disjoint token sets
+    be combined exactly (``merge_attn_states``)."""
+    Hq, d = q_i.shape
+    L, Hkv, _ = K.shape
+    if L <= 0:
+        return np.full(Hq, -np.inf)
+    G = Hq // Hkv
+    s = sigma * (q_i.reshape(Hkv, G, d) @ K.transpose(1, 2, 0))   # [Hkv][G][L]
+    m = s.max(axis=-1)
+    return ((m + np.log(np.exp(s - m[..., None]).sum(axis=-1))) / np.log(2.0)).reshape(Hq)
+
+
+def paged_decode_lse(q, k_cache, block_tables, context_lens, *, bs, softmax_scale, q_dtype,
+                     cache_dtype, k_scale=1.0, seqs=None):
+    """Oracle [S][Hq] (or the rows in ``seqs``): ``contiguous_decode_lse`` of each
+    sequence's reassembled K, scores as in ``paged_decode_attn`` (k_scale
+    included for fp8 caches)."""
+    S, Hq, d = q.shape
+    sigma = np.float64(np.float32(softmax_scale))
+    ks = k_scale if cache_dtype == "fp8" else 1.0
+    rows = list(range(S)) if seqs is None else list(seqs)
+    out = np.full((len(rows), Hq), -np.inf)
+    for r, i in enumerate(rows):
+        L = int(context_lens[i])
+        if L <= 0:
+            continue
+        K = widen(reassemble(k_cache, block_tables[i], L, bs, "k"), cache_dtype, ks)
+        out[r] = contiguous_decode_lse(widen(q[i], q_dtype), K, sigma)
+    return out
+
+
+def merge_attn_states(o_a, lse_a, o_b, lse_b):
+    """Combine the attentions of one query over two disjoint token sets A and B
+    into its attention over A and B together. With Z_X = sum_{t in X} exp(s_t)
+    = 2^lse_X, the softmax over A and B weighs o_A by Z_A / (Z_A + Z_B) and o_B
+    by Z_B / (Z_A + Z_B); the new lse is log2(Z_A + Z_B). A side with lse -inf
+    (no tokens) has weight 0; a row with no tokens on either side is zero.
+    o_*: [..., d]; lse_*: [...]. Returns (o, lse) in float64.
+
+    This is how shared prefix blocks ("03 · PagedAttention", "Sharing:
+    copy-on-write") are attended once for all sequences that list them.
+    """
+    la = np.asarray(lse_a, dtype=np.float64)
+    lb = np.asarray(lse_b, dtype=np.float64)
+    m = np.maximum(la, lb)
+    empty = m == -np.inf
+    m_safe = np.where(empty, 0.0, m)
+    wa = np.where(la == -np.inf, 0.0, np.exp2(la - m_safe))
+    wb = np.where(lb == -np.inf, 0.0, np.exp2(lb - m_safe))
+    den = wa + wb
+    den_safe = np.where(empty, 1.0, den)
+    o = (wa[..., None] * np.asarray(o_a, dtype=np.float64)
+         + wb[..., None] * np.asarray(o_b, dtype=np.float64)) / den_safe[..., None]
+    o = np.where(empty[..., None], 0.0, o)
+    lse = np.where(empty, -np.inf, m_safe + np.log2(den_safe))
+    return o, lse

@@ -10,7 +10,8 @@ from .api import (kv_cache_write, copy_blocks, paged_decode_attn, paged_decode_s
                   paged_multi_query_attn_workspace, Allocator,
                   slots_from_tables, waste_stats, block_hashes, last_error, version, quantise_pool, PkvError,
                   NoBlocks, PKV_PARTITION_BALANCED, paged_decode_attn_lse, paged_shared_prefix_attn,
-                  merge_attn_states, shared_prefix_plan, SharedPrefixDecode, v_shape_ok)
+                  merge_attn_states, shared_prefix_plan, SharedPrefixDecode, v_shape_ok,
+                  paged_shared_prefix_decode, paged_shared_prefix_decode_workspace)
 from ._lib import lib, LIB_PATH, SIGNATURES, PKV_F32, PKV_BF16, PKV_FP8_E4M3
 
 __all__ = [
@@ -20,5 +21,6 @@ __all__ = [
     "Allocator",
     "slots_from_tables", "waste_stats", "block_hashes", "last_error", "version", "quantise_pool", "PkvError",
     "NoBlocks", "PKV_PARTITION_BALANCED", "paged_decode_attn_lse", "paged_shared_prefix_attn",
-    "merge_attn_states", "shared_prefix_plan", "SharedPrefixDecode", "v_shape_ok", "lib", "LIB_PATH", "SIGNATURES", "PKV_F32", "PKV_BF16", "PKV_FP8_E4M3",
+    "merge_attn_states", "shared_prefix_plan", "SharedPrefixDecode",
+    "paged_shared_prefix_decode", "paged_shared_prefix_decode_workspace", "v_shape_ok", "lib", "LIB_PATH", "SIGNATURES", "PKV_F32", "PKV_BF16", "PKV_FP8_E4M3",
 ]

@@ -54,6 +54,11 @@ SIGNATURES = {
                                                     c_i32, c_f32, c_f32, c_f32, ctypes.c_int,
                                                     ctypes.c_int, c_vp, c_sz, c_vp]),
     "pkv_merge_attn_states": (ctypes.c_int, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_i32, c_vp]),
+    "pkv_paged_shared_prefix_decode_workspace_size": (c_sz, [c_i32, c_i32, c_i32, c_i32, c_i32]),
+    "pkv_paged_shared_prefix_decode": (ctypes.c_int, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32,
+                                                      c_i32, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_i32,
+                                                      c_i32, c_i32, c_i32, c_i32, c_f32, c_f32, c_f32, c_f32,
+                                                      c_f32, ctypes.c_int, ctypes.c_int, c_vp, c_sz, c_vp]),
     "pkv_paged_decode_attn_workspace_size": (c_sz, [c_i32, c_i32, c_i32, c_i32, c_i32, c_i32]),
     "pkv_paged_decode_attn": (ctypes.c_int, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_i32, c_i32,
                                              c_i32, c_i32, c_i32, c_i32, c_i32, c_f32, c_f32, c_f32,

@@ -300,10 +300,11 @@ def merge_attn_states(out, a, lse_a, b, lse_b, *, lse_out=None, stream=None):
 def shared_prefix_plan(block_tables, context_lens, group_size, bs):
     """Host side of shared-prefix decode for groups of group_size consecutive
     sequences (beams, parallel samples): per group, the leading blocks that
-    every member lists with the same id and fills completely, as (prefix
-    tables [n_groups][max_blocks], prefix lengths [n_groups], suffix tables
-    [S][max_blocks], suffix lengths [S]) int32 numpy arrays. A group that
-    shares nothing gets a prefix of length 0."""
+    every member lists with the same id, not counting any member's last block
+    (it takes this step's new token, and after copy-on-write it is never
+    shared). Returns (prefix tables [n_groups][max_blocks], prefix lengths
+    [n_groups], suffix tables [S][max_blocks], suffix lengths [S]) as int32
+    numpy arrays; a group that shares nothing gets a prefix of length 0."""
     tables = np.asarray(block_tables, dtype=np.int32)
     lens = np.asarray(context_lens, dtype=np.int64)
     S, max_blocks = tables.shape
@@ -316,7 +317,8 @@ def shared_prefix_plan(block_tables, context_lens, group_size, bs):
     suf_len = np.zeros(S, dtype=np.int32)
     for g in range(n_groups):
         members = range(g * group_size, (g + 1) * group_size)
-        full = min(max(int(lens[i]), 0) // bs for i in members)
+        # blocks before each member's last one
+        full = min((int(lens[i]) - 1) // bs if lens[i] > 0 else 0 for i in members)
         k = 0
         while k < full and all(tables[i, k] == tables[g * group_size, k] for i in members):
             k += 1
@@ -326,17 +328,68 @@ def shared_prefix_plan(block_tables, context_lens, group_size, bs):
             n = max(int(lens[i]), 0)
             nb = -(-n // bs)
             suf_tab[i, :nb - k] = tables[i, k:nb]
-            suf_len[i] = n - k * bs if n > 0 else n
+            suf_len[i] = n - k * bs
     return pre_tab, pre_len, suf_tab, suf_len
 
 
+def paged_shared_prefix_decode_workspace(n_groups, M, Hq, Hkv, d, device="cuda"):
+    import torch
+    n = lib().pkv_paged_shared_prefix_decode_workspace_size(n_groups, M, Hq, Hkv, d)
+    return torch.empty(max(n, 1), dtype=torch.uint8, device=device)
+
+
+def paged_shared_prefix_decode(out, q, k_cache, v_cache, prefix_tables, prefix_lens, suffix_tables,
+                               suffix_lens, group_size, *, max_prefix_len, max_suffix_len, softmax_scale,
+                               k_scale=1.0, v_scale=1.0, k_new=None, v_new=None, k_inv_scale=1.0,
+                               v_inv_scale=1.0, workspace=None, stream=None):
+    """pkv_paged_shared_prefix_decode: decode attention (and, with k_new/v_new,
+    the step's write) for groups of group_size sequences over their group's
+    prefix blocks followed by their own suffix blocks. out float32 [S][Hq][d]."""
+    import torch
+    S, Hq, d = q.shape
+    P, Hkv, bs, _ = k_cache.shape
+    M = int(group_size)
+    if M < 1 or S % M:
+        raise ValueError("paged_shared_prefix_decode: S must be a multiple of group_size")
+    n_groups = S // M
+    if tuple(out.shape) != (S, Hq, d) or out.dtype != torch.float32:
+        raise ValueError("paged_shared_prefix_decode: out must be float32 [S][Hq][d]")
+    if not v_shape_ok(v_cache, P, Hkv, d, bs):
+        raise ValueError("paged_shared_prefix_decode: v_cache shape")
+    for t, name in ((prefix_tables, "prefix_tables"), (prefix_lens, "prefix_lens"),
+                    (suffix_tables, "suffix_tables"), (suffix_lens, "suffix_lens")):
+        if t.dtype != torch.int32:
+            raise ValueError(f"paged_shared_prefix_decode: {name} must be int32")
+    if prefix_tables.shape[0] != n_groups or prefix_lens.shape != (n_groups,):
+        raise ValueError("paged_shared_prefix_decode: prefix tables/lengths shape mismatch")
+    if suffix_tables.shape[0] != S or suffix_lens.shape != (S,):
+        raise ValueError("paged_shared_prefix_decode: suffix tables/lengths shape mismatch")
+    if (k_new is None) != (v_new is None):
+        raise ValueError("paged_shared_prefix_decode: give both k_new and v_new, or neither")
+    if k_new is not None:
+        for t, name in ((k_new, "k_new"), (v_new, "v_new")):
+            if tuple(t.shape) != (S, Hkv, d):
+                raise ValueError(f"paged_shared_prefix_decode: {name} must be [S][Hkv][d]")
+    if workspace is None:
+        workspace = paged_shared_prefix_decode_workspace(n_groups, M, Hq, Hkv, d, device=q.device)
+    check(lib().pkv_paged_shared_prefix_decode(
+        _dev(out, "out"), _dev(q, "q"), _dev(k_new, "k_new") if k_new is not None else None,
+        _dev(v_new, "v_new") if v_new is not None else None, _dev(k_cache, "k_cache"),
+        _dev(v_cache, "v_cache"), _dev(prefix_tables, "prefix_tables"), _dev(prefix_lens, "prefix_lens"),
+        prefix_tables.shape[1], int(max_prefix_len), _dev(suffix_tables, "suffix_tables"),
+        _dev(suffix_lens, "suffix_lens"), suffix_tables.shape[1], int(max_suffix_len), n_groups, M, Hq,
+        Hkv, d, bs, P, float(softmax_scale), float(k_scale), float(v_scale), float(k_inv_scale),
+        float(v_inv_scale), _dtype_code(q), _dtype_code(k_cache), _dev(workspace, "workspace"),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
 class SharedPrefixDecode:
-    """Decode attention for groups of group_size consecutive sequences that share
-    leading blocks, reading the shared blocks once per group: one
-    pkv_paged_shared_prefix_attn over the prefixes, one
-    pkv_paged_decode_attn_lse over the suffixes and one pkv_merge_attn_states.
-    The plan (host tables, see shared_prefix_plan) is built once here and
-    uploaded; __call__ runs the three device calls."""
+    """Decode steps for groups of group_size consecutive sequences that share
+    leading blocks, reading the shared blocks once per group
+    (pkv_paged_shared_prefix_decode). The plan (host tables, see
+    shared_prefix_plan) is built and uploaded once here, with the workspace;
+    __call__ runs one step: with k_new/v_new the write of each sequence's new
+    token and the attention, without them the attention alone."""
 
     def __init__(self, block_tables, context_lens, group_size, bs, Hq, Hkv, d, device="cuda"):
         import torch
@@ -350,23 +403,16 @@ class SharedPrefixDecode:
         self.pre_len = torch.from_numpy(pre_len).to(device)
         self.suf_tab = torch.from_numpy(suf_tab).to(device)
         self.suf_len = torch.from_numpy(suf_len).to(device)
-        f32 = dict(dtype=torch.float32, device=device)
-        self.out_p = torch.empty((self.n_groups, group_size, Hq, d), **f32)
-        self.lse_p = torch.empty((self.n_groups, group_size, Hq), **f32)
-        self.out_s = torch.empty((S, Hq, d), **f32)
-        self.lse_s = torch.empty((S, Hq), **f32)
-        self.ws_p = paged_multi_query_attn_workspace(self.n_groups, group_size, Hq, Hkv, d, device=device)
-        self.ws_s = paged_decode_attn_workspace(S, Hq, Hkv, d, max(self.max_suffix, 1), PKV_PARTITION_BALANCED,
-                                                device=device)
+        self.ws = paged_shared_prefix_decode_workspace(self.n_groups, group_size, Hq, Hkv, d, device=device)
 
-    def __call__(self, out, q, k_cache, v_cache, *, softmax_scale, k_scale=1.0, v_scale=1.0, stream=None):
-        kw = dict(softmax_scale=softmax_scale, k_scale=k_scale, v_scale=v_scale, stream=stream)
-        qg = q.view(self.n_groups, self.M, self.Hq, self.d)
-        paged_shared_prefix_attn(self.out_p, self.lse_p, qg, k_cache, v_cache, self.pre_tab, self.pre_len,
-                                 max_prefix_len=self.max_prefix, workspace=self.ws_p, **kw)
-        paged_decode_attn_lse(self.out_s, self.lse_s, q, k_cache, v_cache, self.suf_tab, self.suf_len,
-                              max_context_len=self.max_suffix, workspace=self.ws_s, **kw)
-        merge_attn_states(out, self.out_p, self.lse_p, self.out_s, self.lse_s, stream=stream)
+    def __call__(self, out, q, k_cache, v_cache, *, softmax_scale, k_scale=1.0, v_scale=1.0, k_new=None,
+                 v_new=None, k_inv_scale=1.0, v_inv_scale=1.0, stream=None):
+        paged_shared_prefix_decode(out, q, k_cache, v_cache, self.pre_tab, self.pre_len, self.suf_tab,
+                                   self.suf_len, self.M, max_prefix_len=self.max_prefix,
+                                   max_suffix_len=self.max_suffix, softmax_scale=softmax_scale,
+                                   k_scale=k_scale, v_scale=v_scale, k_new=k_new, v_new=v_new,
+                                   k_inv_scale=k_inv_scale, v_inv_scale=v_inv_scale, workspace=self.ws,
+                                   stream=stream)
 
 
 def quantise_pool(values_k, values_v, codes_k, codes_v, *, k_inv_scale, v_inv_scale, stream=None):

@@ -1407,6 +1407,125 @@ merge_states_kernel(float* __restrict__ out, float* __restrict__ lse_out, const 
     if (lse_out && lane == 0) lse_out[r] = M + __log2f(den);
 }
 
+// One side of a shared-prefix merge: where the attention state of an output
+// row over one token set lies after a stream pass whose merge was not run.
+// A segment one wave processed whole left the normalised row and its lse; a
+// split segment left n partial records (see paged_attn_merge_kernel).
+struct SideState {
+    const float* rows;   // normalised rows [.][D] (whole segments)
+    const float* lse;    // their base-2 log softmax sums
+    const float* ws;     // partial records
+    size_t nrec;         // record slots in ws
+    int C;               // columns (rows) per record
+    int col;             // this row's column
+    int n;               // 0: no tokens; 1: whole; > 1: records
+    int rec0;            // first record (descriptor)
+};
+
+template <int D>
+__device__ __forceinline__ size_t side_rec(const SideState& x, int k) {
+    return k == 0 ? (size_t)x.rec0 : (size_t)(2 * ((x.rec0 >> 1) + k));
+}
+
+// Source k of a side as a record (m, l, o): a whole row is (lse, 1, row).
+template <int D>
+__device__ __forceinline__ void side_source(const SideState& x, long long h, int k, int lane, float& m,
+                                            float& l, float (&o)[D / 64]) {
+    if (x.n == 1) {
+        m = x.lse[h];
+        l = 1.f;
+#pragma unroll
+        for (int u = 0; u < D / 64; ++u) o[u] = x.rows[h * D + lane + 64 * u];
+        return;
+    }
+    const size_t rr = side_rec<D>(x, k) * x.C + x.col;
+    m = x.ws[x.nrec * x.C * D + rr];
+    l = x.ws[x.nrec * x.C * (D + 1) + rr];
+#pragma unroll
+    for (int u = 0; u < D / 64; ++u) o[u] = x.ws[rr * D + lane + 64 * u];
+}
+
+// Shared-prefix decode, final step: each output row (sequence i = group g,
+// member m; head) combines its state over the group's shared prefix (window
+// pass a, column m's head) with its state over its own suffix (decode pass b).
+// Both passes ran without their merge; this kernel merges the records of
+// both in one go: out = sum_k 2^(m_k - M) o_k / sum_k 2^(m_k - M) l_k over
+// every source k of either side. One wave per row.
+template <int D>
+__global__ void __launch_bounds__(kThreads)
+shared_prefix_merge_kernel(AttnParams a, AttnParams b, float* __restrict__ out, int M) {
+    const long long h = (long long)blockIdx.x * kWaves + (threadIdx.x >> 6);
+    if (h >= (long long)b.S * b.Hq) return;
+    const int lane = threadIdx.x & 63;
+    const int i = (int)(h / b.Hq);
+    const int head = (int)(h - (long long)i * b.Hq);
+    const int G = b.G;
+    const int kvh = head / G;
+    const int r = head - kvh * G;
+    const int g = i / M;
+    const int mm = i - g * M;
+    const int qg = mm / a.qgs;
+    const int seg_a = (g * a.Hkv + kvh) * a.n_qg + qg;
+    const int seg_b = i * b.Hkv + kvh;
+    // one round trip: both lengths and both descriptors
+    const int La = min(a.lens[g], a.max_len);
+    const int Lb = min(b.lens[i], b.max_len);
+    const int2 da = *reinterpret_cast<const int2*>(a.desc + 2 * seg_a);
+    const int2 db = *reinterpret_cast<const int2*>(b.desc + 2 * seg_b);
+    SideState x[2];
+    x[0] = SideState{a.out, a.lse, a.ws, (size_t)a.n_rec, a.cols, (mm - qg * a.qgs) * G + r,
+                     La > 0 ? max(da.y, 1) : 0, da.x};
+    x[1] = SideState{b.out, b.lse, b.ws, (size_t)b.n_rec, b.cols, r, Lb > 0 ? max(db.y, 1) : 0, db.x};
+    constexpr int PER = D / 64;
+    float num[PER] = {};
+    float den = 0.f, Mx = -INFINITY;
+    if (x[0].n <= 8 && x[1].n <= 8) {
+        // every load of both sides is issued before any is used
+        float mv[16], lv[16], ov[16][PER];
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const int e = 8 * s + k;
+                mv[e] = -INFINITY;
+                lv[e] = 0.f;
+#pragma unroll
+                for (int u = 0; u < PER; ++u) ov[e][u] = 0.f;
+                if (k < x[s].n) side_source<D>(x[s], h, k, lane, mv[e], lv[e], ov[e]);
+            }
+#pragma unroll
+        for (int e = 0; e < 16; ++e) Mx = fmaxf(Mx, mv[e]);
+        if (Mx != -INFINITY) {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                if (mv[e] != -INFINITY) {
+                    const float wt = __builtin_amdgcn_exp2f(mv[e] - Mx);
+                    den += wt * lv[e];
+#pragma unroll
+                    for (int u = 0; u < PER; ++u) num[u] += wt * ov[e][u];
+                }
+            }
+        }
+    } else {
+        // long sides: sources one at a time with a running maximum
+        for (int s = 0; s < 2; ++s)
+            for (int k = 0; k < x[s].n; ++k) {
+                float m, l, o[PER];
+                side_source<D>(x[s], h, k, lane, m, l, o);
+                if (m == -INFINITY) continue;
+                const float m_new = fmaxf(Mx, m);
+                const float alpha = __builtin_amdgcn_exp2f(Mx - m_new);
+                const float wt = __builtin_amdgcn_exp2f(m - m_new);
+                den = den * alpha + wt * l;
+#pragma unroll
+                for (int u = 0; u < PER; ++u) num[u] = num[u] * alpha + wt * o[u];
+                Mx = m_new;
+            }
+    }
+#pragma unroll
+    for (int u = 0; u < PER; ++u) out[h * D + lane + 64 * u] = den > 0.f ? num[u] / den : 0.f;
+}
+
 // ----------------------------------------------------------------------------
 // Dispatch
 // ----------------------------------------------------------------------------
@@ -1618,7 +1737,7 @@ pkv_status attn_launch(const char* fn, float* out, const void* q, const void* k_
                        float k_scale, float v_scale, pkv_dtype q_dtype, pkv_dtype cache_dtype,
                        int32_t partition_size, void* workspace, size_t workspace_bytes, void* stream,
                        const StepWrite& step = StepWrite(), float* lse = nullptr,
-                       bool causal = true) {
+                       bool causal = true, bool run_merge = true, AttnParams* used = nullptr) {
     const bool is_step = step.k_new != nullptr || step.v_new != nullptr;
     if (S < 0 || Hq <= 0 || Hkv <= 0) return fail(PKV_E_INVALID, "%s: S=%d Hq=%d Hkv=%d", fn, S, Hq, Hkv);
     if (n_q < 1 || n_q > 4096) return fail(PKV_E_INVALID, "%s: n_q=%d outside [1, 4096]", fn, n_q);
@@ -1728,10 +1847,11 @@ pkv_status attn_launch(const char* fn, float* out, const void* q, const void* k_
     if (grid < 1) grid = 1;
     prm.n_workers = (int)(balanced ? grid * kWaves : grid);
     prm.n_rec = balanced ? 2 * prm.n_workers : (int)(n_part * (int64_t)S * Hkv);
+    if (used) *used = prm;
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kThreads), lds, st, prm);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(PKV_E_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
-    if (balanced || n_part > 1) {
+    if (run_merge && (balanced || n_part > 1)) {
         const unsigned rgrid = (unsigned)(((int64_t)S * n_q * Hq + kWaves - 1) / kWaves);
         if (d == 64)
             hipLaunchKernelGGL(paged_attn_merge_kernel<64>, dim3(rgrid), dim3(kThreads), 0, st, prm);
@@ -1857,5 +1977,94 @@ extern "C" pkv_status pkv_merge_attn_states(float* out, float* lse_out, const fl
                            lse_a, b, lse_b, (long long)rows);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(PKV_E_HIP, "merge_attn_states: launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+namespace {
+
+// Workspace of pkv_paged_shared_prefix_decode: the prefix pass's balanced
+// workspace, the suffix pass's, then both passes' rows and lse values.
+struct SharedPrefixLayout {
+    size_t a, b, out_a, lse_a, out_b, lse_b, total;
+};
+SharedPrefixLayout shared_prefix_layout(int32_t n_groups, int32_t M, int32_t Hq, int32_t Hkv, int32_t d) {
+    auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+    SharedPrefixLayout L{};
+    const size_t S = (size_t)n_groups * (size_t)M;
+    const size_t rows = S * (size_t)Hq;
+    L.a = 0;
+    L.b = L.a + up(attn_workspace_size(n_groups, M, Hq, Hkv, d, 0, PKV_PARTITION_BALANCED));
+    L.out_a = L.b + up(attn_workspace_size((int32_t)S, 1, Hq, Hkv, d, 0, PKV_PARTITION_BALANCED));
+    L.lse_a = L.out_a + up(rows * d * sizeof(float));
+    L.out_b = L.lse_a + up(rows * sizeof(float));
+    L.lse_b = L.out_b + up(rows * d * sizeof(float));
+    L.total = L.lse_b + up(rows * sizeof(float));
+    return L;
+}
+
+}  // namespace
+
+extern "C" size_t pkv_paged_shared_prefix_decode_workspace_size(int32_t n_groups, int32_t M, int32_t Hq,
+                                                                int32_t Hkv, int32_t d) {
+    if (n_groups <= 0 || M <= 0 || M > 4096 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 ||
+        !pkv::is_head_dim(d) || (int64_t)n_groups * M > 0x7FFFFFFF)
+        return 0;
+    return shared_prefix_layout(n_groups, M, Hq, Hkv, d).total;
+}
+
+extern "C" pkv_status pkv_paged_shared_prefix_decode(
+    float* out, const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+    const int32_t* prefix_tables, const int32_t* prefix_lens, int32_t prefix_max_blocks,
+    int32_t max_prefix_len, const int32_t* suffix_tables, const int32_t* suffix_lens,
+    int32_t suffix_max_blocks, int32_t max_suffix_len, int32_t n_groups, int32_t M, int32_t Hq,
+    int32_t Hkv, int32_t d, int32_t bs, int32_t P, float softmax_scale, float k_scale, float v_scale,
+    float k_inv_scale, float v_inv_scale, pkv_dtype q_dtype, pkv_dtype cache_dtype, void* workspace,
+    size_t workspace_bytes, void* stream) {
+    const char* fn = "paged_shared_prefix_decode";
+    if (n_groups < 0 || M < 1 || M > 4096)
+        return fail(PKV_E_INVALID, "%s: n_groups=%d M=%d (need n_groups >= 0, 1 <= M <= 4096)", fn, n_groups, M);
+    if ((int64_t)n_groups * M > 0x7FFFFFFF) return fail(PKV_E_INVALID, "%s: too many sequences", fn);
+    if ((k_new == nullptr) != (v_new == nullptr))
+        return fail(PKV_E_INVALID, "%s: k_new and v_new must both be given or both be NULL", fn);
+    if (Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || !pkv::is_head_dim(d))
+        return fail(PKV_E_INVALID, "%s: Hq=%d Hkv=%d d=%d", fn, Hq, Hkv, d);
+    if (n_groups == 0) return ok();
+    if (!out || !q || !k_cache || !v_cache || !prefix_tables || !prefix_lens || !suffix_tables || !suffix_lens)
+        return fail(PKV_E_INVALID, "%s: NULL pointer", fn);
+    const SharedPrefixLayout lay = shared_prefix_layout(n_groups, M, Hq, Hkv, d);
+    if (!workspace || workspace_bytes < lay.total)
+        return fail(PKV_E_WORKSPACE, "%s: workspace %zu bytes, need %zu", fn, workspace_bytes, lay.total);
+    char* ws = static_cast<char*>(workspace);
+    float* out_a = reinterpret_cast<float*>(ws + lay.out_a);
+    float* lse_a = reinterpret_cast<float*>(ws + lay.lse_a);
+    float* out_b = reinterpret_cast<float*>(ws + lay.out_b);
+    float* lse_b = reinterpret_cast<float*>(ws + lay.lse_b);
+    const int32_t S = n_groups * M;
+    // the suffixes first: they hold each sequence's last block, so this pass
+    // also writes the step's new tokens (when given) before the prefix pass
+    StepWrite step;
+    step.k_new = k_new;
+    step.v_new = v_new;
+    step.k_inv = cache_dtype == PKV_FP8_E4M3 ? k_inv_scale : 1.f;
+    step.v_inv = cache_dtype == PKV_FP8_E4M3 ? v_inv_scale : 1.f;
+    AttnParams pb, pa;
+    pkv_status rc = attn_launch(fn, out_b, q, k_cache, v_cache, suffix_tables, suffix_lens, S, 1, Hq, Hkv, d,
+                                bs, P, suffix_max_blocks, max_suffix_len, softmax_scale, k_scale, v_scale,
+                                q_dtype, cache_dtype, PKV_PARTITION_BALANCED, ws + lay.b, lay.out_a - lay.b,
+                                stream, step, lse_b, true, false, &pb);
+    if (rc != PKV_OK) return rc;
+    rc = attn_launch(fn, out_a, q, k_cache, v_cache, prefix_tables, prefix_lens, n_groups, M, Hq, Hkv, d, bs,
+                     P, prefix_max_blocks, max_prefix_len, softmax_scale, k_scale, v_scale, q_dtype,
+                     cache_dtype, PKV_PARTITION_BALANCED, ws + lay.a, lay.b - lay.a, stream, StepWrite(),
+                     lse_a, false, false, &pa);
+    if (rc != PKV_OK) return rc;
+    const unsigned grid = (unsigned)(((int64_t)S * Hq + kWaves - 1) / kWaves);
+    auto st = static_cast<hipStream_t>(stream);
+    if (d == 64)
+        hipLaunchKernelGGL(shared_prefix_merge_kernel<64>, dim3(grid), dim3(kThreads), 0, st, pa, pb, out, M);
+    else
+        hipLaunchKernelGGL(shared_prefix_merge_kernel<128>, dim3(grid), dim3(kThreads), 0, st, pa, pb, out, M);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(PKV_E_HIP, "%s: merge launch failed: %s", fn, hipGetErrorString(e));
     return ok();
 }

@@ -569,34 +569,57 @@ def test_many_sequences_window():
 
 
 # ------------------------------------------------------------------ shared-prefix decode (beams)
-def _shared_prefix_case(w, group_size):
+def _shared_prefix_case(w, group_size, step=False):
     torch = need_gpu()
     s = w.spec
-    print(f"[case] shared prefix {s.name} bs={s.bs} cache={s.cache_dtype} M={group_size}", flush=True)
+    print(f"[case] shared prefix {s.name} bs={s.bs} cache={s.cache_dtype} M={group_size} step={step}",
+          flush=True)
     dev = DeviceStep(w)
-    dev.write()
-    slots, kc, vc, ref = oracle_step(w)
+    if not step:
+        dev.write()
+    kc, vc = oracle_pools(w)
+    ref = oracle.paged_decode_attn(w.q, kc, vc, w.block_tables, w.context_lens, bs=s.bs,
+                                   softmax_scale=w.softmax_scale, q_dtype=s.q_dtype,
+                                   cache_dtype=s.cache_dtype, k_scale=w.k_scale, v_scale=w.v_scale)
     run = pkv.SharedPrefixDecode(w.block_tables, w.context_lens, group_size, s.bs, s.Hq, s.Hkv, s.d)
     out = torch.empty((s.S, s.Hq, s.d), dtype=torch.float32, device="cuda")
+    wr = dict(k_new=dev.k_new, v_new=dev.v_new, k_inv_scale=w.k_inv_scale,
+              v_inv_scale=w.v_inv_scale) if step else {}
     for _ in range(2):                          # the second call reuses the plan's buffers
         run(out, dev.q, dev.k_cache, dev.v_cache, softmax_scale=w.softmax_scale, k_scale=w.k_scale,
-            v_scale=w.v_scale)
+            v_scale=w.v_scale, **wr)
     torch.cuda.synchronize()
+    if step:                                    # the write landed in every listed block
+        blocks = np.unique(w.block_tables.reshape(-1))
+        blocks = blocks[blocks >= 0]
+        assert same_bits(to_host(dev.k_cache)[blocks], kc[blocks]), "K pool differs after the step"
+        assert same_bits(to_host(dev.v_cache)[blocks], vc[blocks]), "V pool differs after the step"
     e = assert_rows_close(to_host(out), ref, TOL[s.cache_dtype], f"shared prefix {s.name}")
     print(f"[case] max row err {e:.3e}; prefix tokens {run.prefix_tokens}", flush=True)
     return run
 
 
-@pytest.mark.parametrize("bs", [8, 16, 32])
-def test_shared_prefix_beam(bs):
-    run = _shared_prefix_case(W.make("beam", bs=bs), 4)
+@pytest.mark.parametrize("bs,cache", [(8, None), (16, None), (32, None), (16, "fp8")])
+def test_shared_prefix_beam(bs, cache):
+    run = _shared_prefix_case(W.make("beam", bs=bs, cache_dtype=cache), 4)
     assert run.prefix_tokens == 32 * 1024          # every group shares its 1024-token prompt
 
 
+@pytest.mark.parametrize("bs,cache", [(16, None), (16, "fp8")])
+def test_shared_prefix_beam_decode_step(bs, cache):
+    # the write of each beam's new token and the attention in one call
+    _shared_prefix_case(W.make("beam", bs=bs, cache_dtype=cache), 4, step=True)
+
+
+def test_shared_prefix_groups_of_one_step():
+    # groups of one: every block before the last is the "prefix" (a decode pass)
+    _shared_prefix_case(W.make("tiny"), 1, step=True)
+
+
 def test_shared_prefix_edge_groups():
-    # groups of 3: group 0 shares 4 full blocks and one member has no token
-    # after them (empty suffix); group 1 shares nothing (its tables differ from
-    # the first block); group 2 has a member with no tokens at all
+    # groups of 3: group 0 shares 4 blocks (3 of them before every member's
+    # last block); group 1 shares nothing (its tables differ from the first
+    # block); group 2 has a member with no tokens at all
     bs, Hq, Hkv, d = 16, 8, 2, 64
     lens = [64, 70, 90, 20, 33, 5, 0, 40, 41]
     w = W.make_custom(lens=lens, Hq=Hq, Hkv=Hkv, d=d, bs=bs, cfg=991, pool_factor=3.0)
@@ -604,10 +627,51 @@ def test_shared_prefix_edge_groups():
     tab[1, :4] = tab[0, :4]
     tab[2, :4] = tab[0, :4]
     tab[7, :2] = tab[8, :2]                        # group 2: the zero-length member lists nothing
-    w.block_tables[:] = tab
     pre_tab, pre_len, suf_tab, suf_len = pkv.shared_prefix_plan(tab, lens, 3, bs)
-    assert list(pre_len) == [64, 0, 0] and list(suf_len[:3]) == [0, 6, 26]
+    assert list(pre_len) == [48, 0, 0] and list(suf_len[:3]) == [16, 22, 42]
+    # on the device, member 0's last block (block 3, where its new token goes)
+    # stays private, as copy-on-write leaves it: the others share blocks 0-2
+    tab[1, 3] = w.block_tables[1, 3]
+    tab[2, 3] = w.block_tables[2, 3]
+    w.block_tables[:] = tab
+    assert list(pkv.shared_prefix_plan(tab, lens, 3, bs)[1]) == [48, 0, 0]
     _shared_prefix_case(w, 3)
+    _shared_prefix_case(w, 3, step=True)
+
+
+def test_shared_prefix_decode_empty_suffix_plan():
+    # a hand-made plan: group 0's members list the same 4 blocks and keep no
+    # suffix; group 1 shares one block and keeps suffixes of 14 and 34 tokens
+    torch = need_gpu()
+    bs, Hq, Hkv, d = 16, 8, 2, 128
+    lens = [64, 64, 30, 50]
+    w = W.make_custom(lens=lens, Hq=Hq, Hkv=Hkv, d=d, bs=bs, cfg=992, pool_factor=3.0)
+    tab = w.block_tables.copy()
+    tab[1] = tab[0]
+    tab[3, :1] = tab[2, :1]
+    w.block_tables[:] = tab
+    w.k_new[1] = w.k_new[0]                        # sequences 0 and 1 write the same slot
+    w.v_new[1] = w.v_new[0]
+    dev = DeviceStep(w)
+    dev.write()
+    kc, vc = oracle_pools(w)
+    ref = oracle.paged_decode_attn(w.q, kc, vc, tab, w.context_lens, bs=bs, softmax_scale=w.softmax_scale,
+                                   q_dtype=w.spec.q_dtype, cache_dtype=w.spec.cache_dtype)
+    mb = tab.shape[1]
+    pre_tab = np.full((2, mb), -1, dtype=np.int32)
+    pre_tab[0, :4] = tab[0, :4]
+    pre_tab[1, :1] = tab[2, :1]
+    pre_len = np.array([64, 16], dtype=np.int32)
+    suf_tab = np.full((4, mb), -1, dtype=np.int32)
+    suf_tab[2, :1] = tab[2, 1:2]
+    suf_tab[3, :3] = tab[3, 1:4]
+    suf_len = np.array([0, 0, 14, 34], dtype=np.int32)
+    out = torch.empty((4, Hq, d), dtype=torch.float32, device="cuda")
+    pkv.paged_shared_prefix_decode(out, dev.q, dev.k_cache, dev.v_cache, to_dev(pre_tab), to_dev(pre_len),
+                                   to_dev(suf_tab), to_dev(suf_len), 2, max_prefix_len=64, max_suffix_len=34,
+                                   softmax_scale=w.softmax_scale)
+    torch.cuda.synchronize()
+    assert_rows_close(to_host(out), ref, TOL[w.spec.cache_dtype], "empty suffix plan")
 
 
 def test_merge_attn_states_edges():
@@ -635,3 +699,33 @@ def test_merge_attn_states_edges():
         want = (wa * a[r] + wb * b[r]) / (wa + wb)
         assert np.max(np.abs(got[r] - want)) <= 1e-5 * max(1.0, np.max(np.abs(want)))
         assert abs(glo[r] - (m[r] + np.log2(wa + wb))) <= 1e-5 * max(1.0, abs(glo[r]))
+
+
+@pytest.mark.parametrize("name,cache,seqs", [("tiny", None, None), ("small", None, None),
+                                             ("small", "fp8", list(range(0, 256, 17))),
+                                             ("llama8b", None, [0, 5, 17, 40, 63])])
+def test_decode_lse_matches_oracle(name, cache, seqs):
+    torch = need_gpu()
+    w = W.make(name, cache_dtype=cache)
+    s = w.spec
+    print(f"[case] decode lse {name} cache={s.cache_dtype}", flush=True)
+    dev = DeviceStep(w)
+    dev.write()
+    out = torch.empty((s.S, s.Hq, s.d), dtype=torch.float32, device="cuda")
+    lse = torch.empty((s.S, s.Hq), dtype=torch.float32, device="cuda")
+    pkv.paged_decode_attn_lse(out, lse, dev.q, dev.k_cache, dev.v_cache, dev.tables, dev.lens,
+                              max_context_len=w.max_context_len, softmax_scale=w.softmax_scale,
+                              k_scale=w.k_scale, v_scale=w.v_scale)
+    torch.cuda.synchronize()
+    got, glse = to_host(out), to_host(lse)
+    # the output is the balanced decode attention's, bit for bit
+    assert np.array_equal(got, to_host(dev.attend(BAL)))
+    kc, vc = oracle_pools(w, seqs)
+    kw = dict(bs=s.bs, softmax_scale=w.softmax_scale, q_dtype=s.q_dtype, cache_dtype=s.cache_dtype,
+              k_scale=w.k_scale, seqs=seqs)
+    want = oracle.paged_decode_lse(w.q, kc, w.block_tables, w.context_lens, **kw)
+    g = glse if seqs is None else glse[seqs]
+    # fp32 scores of exactly widened inputs: the log2 sum is good to a few ulps of its terms
+    err = np.abs(g.astype(np.float64) - want)
+    assert np.all(err <= 1e-4 + 1e-5 * np.abs(want)), float(err.max())
+    print(f"[case] max lse err {err.max():.3e}", flush=True)

@@ -8,7 +8,10 @@ The pages print no attention outputs. What they fix, and what pins the oracle:
 * the output does not change when physical block ids are permuted or when
   sequences share prefix blocks instead of holding private copies;
 * closed forms (one token, constant V, equal keys, zero query, empty sequence);
-* the split-K merge equals the single pass.
+* the split-K merge equals the single pass;
+* the log-sum-exp state: closed forms and brute force; merging the states of a
+  prefix and a suffix (found through their own tables) gives the whole
+  sequence's attention.
 Mutation checks at the end plant plausible mistakes in the oracle and confirm
 that one of these pins catches each.
 """
@@ -372,3 +375,108 @@ def test_planted_causal_offset_mistake_is_caught(monkeypatch):
     ref = _sdpa_window(q[0].astype(np.float64), Kc[0].astype(np.float64), Vc[0].astype(np.float64),
                        np.float64(np.float32(0.35)))
     assert not np.allclose(out[0], ref, rtol=1e-6, atol=1e-6)
+
+
+# ------------------------------------------------ log-sum-exp states and their merge (shared prefixes)
+def _lse_loops(q_i, K, sigma):
+    """Pure-Python log2 sum_t exp(s_t) per head."""
+    Hq, d = q_i.shape
+    L, Hkv, _ = K.shape
+    G = Hq // Hkv
+    out = []
+    for h in range(Hq):
+        s = [sigma * sum(float(q_i[h, c]) * float(K[t, h // G, c]) for c in range(d)) for t in range(L)]
+        out.append(math.log2(sum(math.exp(x) for x in s)) if s else -math.inf)
+    return np.array(out)
+
+
+def _lse_closed_forms_hold():
+    rng = np.random.default_rng(41)
+    ok = True
+    for L in (1, 2, 7, 100):
+        K = rng.standard_normal((L, 2, 8))
+        # q = 0: every score is 0, the sum of exponentials is L
+        ok &= bool(np.allclose(oatt.contiguous_decode_lse(np.zeros((4, 8)), K, 0.5), math.log2(L),
+                               rtol=0, atol=1e-13))
+    # one token: the sum is exp(s_0), so lse = s_0 / ln 2
+    q = rng.standard_normal((4, 8))
+    K = rng.standard_normal((1, 2, 8))
+    want = [0.3 * float(q[h] @ K[0, h // 2]) / math.log(2) for h in range(4)]
+    ok &= bool(np.allclose(oatt.contiguous_decode_lse(q, K, 0.3), want, rtol=0, atol=1e-13))
+    ok &= bool(np.all(oatt.contiguous_decode_lse(q, K[:0], 0.3) == -np.inf))
+    return ok
+
+
+def test_lse_closed_forms():
+    assert _lse_closed_forms_hold()
+
+
+@pytest.mark.parametrize("seed,lens,Hq,Hkv,d,bs", CASES)
+def test_lse_against_loops(seed, lens, Hq, Hkv, d, bs):
+    q, Kc, _, kp, _, tab = _case(seed, lens, Hq, Hkv, d, bs)
+    sigma = np.float32(1 / math.sqrt(d))
+    got = oracle.paged_decode_lse(q, kp, tab, np.array(lens), bs=bs, softmax_scale=sigma,
+                                  q_dtype="f32", cache_dtype="f32")
+    for i, L in enumerate(lens):
+        want = _lse_loops(q[i].astype(np.float64), Kc[i].astype(np.float64), float(sigma))
+        np.testing.assert_allclose(got[i], want, rtol=1e-12, atol=1e-12)
+
+
+def _split_error(seed=51, lens=(40, 17, 64, 8), Hq=6, Hkv=2, d=16, bs=8, cut_blocks=(2, 1, 5, 1)):
+    """Largest difference between the whole-sequence oracle attention and the
+    merge of its states over the first cut_blocks[i] blocks and over the rest,
+    both found through block tables (the rest through a table that starts at
+    the cut). Returns (output error, lse error)."""
+    q, _, _, kp, vp, tab = _case(seed, list(lens), Hq, Hkv, d, bs)
+    lens = np.array(lens)
+    kw = dict(bs=bs, softmax_scale=0.31, q_dtype="f32", cache_dtype="f32")
+    cut = np.minimum(np.array(cut_blocks) * bs, lens)
+    pre_tab = tab.copy()
+    suf_tab = np.full_like(tab, -1)
+    for i in range(len(lens)):
+        nb = -(-int(lens[i]) // bs)
+        k = int(cut[i]) // bs
+        suf_tab[i, :nb - k] = tab[i, k:nb]
+    o_a = oracle.paged_decode_attn(q, kp, vp, pre_tab, cut, **kw)
+    o_b = oracle.paged_decode_attn(q, kp, vp, suf_tab, lens - cut, **kw)
+    la = oracle.paged_decode_lse(q, kp, pre_tab, cut, **kw)
+    lb = oracle.paged_decode_lse(q, kp, suf_tab, lens - cut, **kw)
+    o, lse = oracle.merge_attn_states(o_a, la, o_b, lb)
+    whole = oracle.paged_decode_attn(q, kp, vp, tab, lens, **kw)
+    lse_whole = oracle.paged_decode_lse(q, kp, tab, lens, **kw)
+    return float(np.max(np.abs(o - whole))), float(np.max(np.abs(lse - lse_whole)))
+
+
+def test_merge_of_prefix_and_suffix_states_is_the_whole_attention():
+    # cuts inside, at the end of (nothing after) and past nothing (all after)
+    eo, el = _split_error()
+    assert eo < 1e-12 and el < 1e-12
+    eo, el = _split_error(cut_blocks=(0, 3, 8, 1))
+    assert eo < 1e-12 and el < 1e-12
+
+
+def test_merge_attn_states_empty_sides():
+    o_a = np.arange(6.0).reshape(3, 2)
+    o_b = -np.arange(6.0).reshape(3, 2)
+    la = np.array([1.5, -np.inf, -np.inf])
+    lb = np.array([-np.inf, 0.25, -np.inf])
+    o, lse = oracle.merge_attn_states(o_a, la, o_b, lb)
+    assert np.array_equal(o[0], o_a[0]) and lse[0] == 1.5
+    assert np.array_equal(o[1], o_b[1]) and lse[1] == 0.25
+    assert np.all(o[2] == 0) and lse[2] == -np.inf
+    # equal weights: the mean, and lse grows by exactly one (a doubled sum)
+    o, lse = oracle.merge_attn_states(o_a[:1], np.array([3.0]), o_b[:1], np.array([3.0]))
+    assert np.array_equal(o[0], (o_a[0] + o_b[0]) / 2) and lse[0] == 4.0
+
+
+def test_planted_natural_log_lse_is_caught(monkeypatch):
+    real = oatt.contiguous_decode_lse
+    monkeypatch.setattr(oatt, "contiguous_decode_lse", lambda q, K, s: real(q, K, s) * math.log(2))
+    assert not _lse_closed_forms_hold()
+
+
+def test_planted_swapped_merge_weights_are_caught(monkeypatch):
+    real = oatt.merge_attn_states
+    monkeypatch.setattr(oracle, "merge_attn_states", lambda a, la, b, lb: real(a, lb, b, la))
+    eo, _ = _split_error()
+    assert eo > 1e-6
