@@ -1328,6 +1328,44 @@ paged_attn_merge_kernel(AttnParams p) {
         if (p.lse && lane == 0) p.lse[h] = M + __log2f(den);
         return;
     }
+    if (n <= 32) {
+        // up to 32 records, also in one round trip: lane k reads record k's
+        // m and l, and every lane its PER adjacent columns of every record
+        using VT = typename std::conditional<PER == 2, float2, float>::type;
+        const float mk = lane < n ? m_at(lane) : -INFINITY;
+        const float lk = lane < n ? l_at(lane) : 0.f;
+        VT ov[32];
+#pragma unroll
+        for (int u = 0; u < 32; ++u) {
+            if (u < n) ov[u] = *reinterpret_cast<const VT*>(p.ws + (rec_of(u) * G + r) * D + PER * lane);
+            else ov[u] = VT{};
+        }
+        float M = mk;
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+        const float wl = lane < n ? __builtin_amdgcn_exp2f(mk - M) : 0.f;
+        float dn = wl * lk;
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) dn += __shfl_xor(dn, off);
+        float acc[PER] = {};
+#pragma unroll
+        for (int u = 0; u < 32; ++u) {
+            if (u < n) {
+                const float wt = __shfl(wl, u);
+                if constexpr (PER == 2) {
+                    acc[0] += wt * ov[u].x;
+                    acc[1] += wt * ov[u].y;
+                } else {
+                    acc[0] += wt * ov[u];
+                }
+            }
+        }
+        float* orow = p.out + h * D + PER * lane;
+        if constexpr (PER == 2) *reinterpret_cast<float2*>(orow) = make_float2(acc[0] / dn, acc[1] / dn);
+        else orow[0] = acc[0] / dn;
+        if (p.lse && lane == 0) p.lse[h] = M + __log2f(dn);
+        return;
+    }
     float M = -INFINITY;
     for (int k0 = 0; k0 < n; k0 += 64)
         if (k0 + lane < n) M = fmaxf(M, m_at(k0 + lane));
