@@ -1775,7 +1775,8 @@ pkv_status attn_launch(const char* fn, float* out, const void* q, const void* k_
                        float k_scale, float v_scale, pkv_dtype q_dtype, pkv_dtype cache_dtype,
                        int32_t partition_size, void* workspace, size_t workspace_bytes, void* stream,
                        const StepWrite& step = StepWrite(), float* lse = nullptr,
-                       bool causal = true, bool run_merge = true, AttnParams* used = nullptr) {
+                       bool causal = true, bool run_merge = true, AttnParams* used = nullptr,
+                       bool validate_only = false) {
     const bool is_step = step.k_new != nullptr || step.v_new != nullptr;
     if (S < 0 || Hq <= 0 || Hkv <= 0) return fail(PKV_E_INVALID, "%s: S=%d Hq=%d Hkv=%d", fn, S, Hq, Hkv);
     if (n_q < 1 || n_q > 4096) return fail(PKV_E_INVALID, "%s: n_q=%d outside [1, 4096]", fn, n_q);
@@ -1817,6 +1818,7 @@ pkv_status attn_launch(const char* fn, float* out, const void* q, const void* k_
                                            (((int64_t)max_context_len + 15) / 16 + kSegCostMax)
                                      : n_part * (int64_t)S * Hkv;
     if (n_upper > 0x7FFFFFFFLL) return fail(PKV_E_INVALID, "%s: too many work items", fn);
+    if (validate_only) return ok();
 
     AttnParams prm;
     prm.out = out;
@@ -2086,16 +2088,19 @@ extern "C" pkv_status pkv_paged_shared_prefix_decode(
     step.k_inv = cache_dtype == PKV_FP8_E4M3 ? k_inv_scale : 1.f;
     step.v_inv = cache_dtype == PKV_FP8_E4M3 ? v_inv_scale : 1.f;
     AttnParams pb, pa;
-    pkv_status rc = attn_launch(fn, out_b, q, k_cache, v_cache, suffix_tables, suffix_lens, S, 1, Hq, Hkv, d,
-                                bs, P, suffix_max_blocks, max_suffix_len, softmax_scale, k_scale, v_scale,
-                                q_dtype, cache_dtype, PKV_PARTITION_BALANCED, ws + lay.b, lay.out_a - lay.b,
-                                stream, step, lse_b, true, false, &pb);
-    if (rc != PKV_OK) return rc;
-    rc = attn_launch(fn, out_a, q, k_cache, v_cache, prefix_tables, prefix_lens, n_groups, M, Hq, Hkv, d, bs,
-                     P, prefix_max_blocks, max_prefix_len, softmax_scale, k_scale, v_scale, q_dtype,
-                     cache_dtype, PKV_PARTITION_BALANCED, ws + lay.a, lay.b - lay.a, stream, StepWrite(),
-                     lse_a, false, false, &pa);
-    if (rc != PKV_OK) return rc;
+    // both passes' arguments are checked before either is launched
+    for (int launch = 0; launch < 2; ++launch) {
+        pkv_status rc = attn_launch(fn, out_b, q, k_cache, v_cache, suffix_tables, suffix_lens, S, 1, Hq, Hkv,
+                                    d, bs, P, suffix_max_blocks, max_suffix_len, softmax_scale, k_scale,
+                                    v_scale, q_dtype, cache_dtype, PKV_PARTITION_BALANCED, ws + lay.b,
+                                    lay.out_a - lay.b, stream, step, lse_b, true, false, &pb, launch == 0);
+        if (rc != PKV_OK) return rc;
+        rc = attn_launch(fn, out_a, q, k_cache, v_cache, prefix_tables, prefix_lens, n_groups, M, Hq, Hkv, d,
+                         bs, P, prefix_max_blocks, max_prefix_len, softmax_scale, k_scale, v_scale, q_dtype,
+                         cache_dtype, PKV_PARTITION_BALANCED, ws + lay.a, lay.b - lay.a, stream, StepWrite(),
+                         lse_a, false, false, &pa, launch == 0);
+        if (rc != PKV_OK) return rc;
+    }
     const unsigned grid = (unsigned)(((int64_t)S * Hq + kWaves - 1) / kWaves);
     auto st = static_cast<hipStream_t>(stream);
     if (d == 64)

@@ -359,3 +359,60 @@ def test_decode_step_rejects_invalid_arguments():
     assert step(cd=2, ki=0.0) == _lib.PKV_E_INVALID
     assert step(cd=2, vi=float("inf")) == _lib.PKV_E_INVALID
     assert step(wsb=16) == _lib.PKV_E_WORKSPACE
+
+
+def _shared(**kw):
+    a = dict(out=FAKE, q=FAKE, kn=FAKE, vn=FAKE, kc=FAKE, vc=FAKE, ptab=FAKE, plen=FAKE, pmaxb=64,
+             pmax=1024, stab=FAKE, slen=FAKE, smaxb=16, smax=200, ng=8, M=4, Hq=32, Hkv=8, d=128, bs=16,
+             P=4000, scale=0.1, ks=1.0, vs=1.0, ki=1.0, vi=1.0, qd=1, cd=1, ws=FAKE, wsb=1 << 40)
+    a.update(kw)
+    return pkv.lib().pkv_paged_shared_prefix_decode(
+        a["out"], a["q"], a["kn"], a["vn"], a["kc"], a["vc"], a["ptab"], a["plen"], a["pmaxb"], a["pmax"],
+        a["stab"], a["slen"], a["smaxb"], a["smax"], a["ng"], a["M"], a["Hq"], a["Hkv"], a["d"], a["bs"],
+        a["P"], a["scale"], a["ks"], a["vs"], a["ki"], a["vi"], a["qd"], a["cd"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(M=0), _lib.PKV_E_INVALID), (dict(M=4097), _lib.PKV_E_INVALID), (dict(ng=-1), _lib.PKV_E_INVALID),
+    (dict(kn=None), _lib.PKV_E_INVALID), (dict(vn=None), _lib.PKV_E_INVALID),
+    (dict(Hq=30), _lib.PKV_E_INVALID), (dict(d=96), _lib.PKV_E_INVALID), (dict(bs=12), _lib.PKV_E_INVALID),
+    (dict(pmaxb=0), _lib.PKV_E_INVALID), (dict(pmax=1025), _lib.PKV_E_INVALID),
+    (dict(smax=257), _lib.PKV_E_INVALID), (dict(qd=0), _lib.PKV_E_INVALID),
+    (dict(cd=2, ki=0.0), _lib.PKV_E_INVALID), (dict(scale=float("nan")), _lib.PKV_E_INVALID),
+    (dict(ptab=None), _lib.PKV_E_INVALID), (dict(slen=None), _lib.PKV_E_INVALID),
+    (dict(wsb=1024), _lib.PKV_E_WORKSPACE), (dict(ws=None), _lib.PKV_E_WORKSPACE),
+])
+def test_shared_prefix_decode_rejects_invalid_arguments(kw, status):
+    # every check, of both passes, runs before any launch
+    assert _shared(**kw) == status
+    assert "shared_prefix_decode" in pkv.last_error()
+
+
+def test_shared_prefix_decode_workspace_and_empty_call():
+    lib = pkv.lib()
+    n = lib.pkv_paged_shared_prefix_decode_workspace_size(32, 4, 32, 8, 128)
+    pre = lib.pkv_paged_multi_query_attn_workspace_size(32, 4, 32, 8, 128)
+    suf = lib.pkv_paged_decode_attn_workspace_size(128, 32, 8, 128, 0, pkv.PKV_PARTITION_BALANCED)
+    rows = 128 * 32
+    up = lambda x: -(-x // 256) * 256  # noqa: E731
+    assert n == up(pre) + up(suf) + 2 * (up(rows * 128 * 4) + up(rows * 4))
+    assert lib.pkv_paged_shared_prefix_decode_workspace_size(0, 4, 32, 8, 128) == 0
+    assert lib.pkv_paged_shared_prefix_decode_workspace_size(4, 4, 30, 8, 128) == 0
+    assert _shared(ng=0, out=None, q=None, ws=None, wsb=0) == _lib.PKV_OK     # nothing to do
+
+
+def test_lse_and_merge_entry_points_reject_invalid_arguments():
+    lib = pkv.lib()
+    rc = lib.pkv_paged_decode_attn_lse(FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 8, 2, 128, 16, 100, 10,
+                                       160, 0.1, 1.0, 1.0, 1, 1, FAKE, 1 << 30, None)
+    assert rc == _lib.PKV_E_INVALID                                   # lse is required
+    rc = lib.pkv_paged_shared_prefix_attn(FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 2, 8, 2, 128, 16, 100,
+                                          10, 160, 0.1, 1.0, 1.0, 1, 1, FAKE, 1 << 30, None)
+    assert rc == _lib.PKV_E_INVALID
+    rc = lib.pkv_merge_attn_states(FAKE, None, FAKE, FAKE, FAKE, FAKE, -1, 128, None)
+    assert rc == _lib.PKV_E_INVALID
+    rc = lib.pkv_merge_attn_states(FAKE, None, FAKE, FAKE, FAKE, FAKE, 10, 96, None)
+    assert rc == _lib.PKV_E_INVALID
+    rc = lib.pkv_merge_attn_states(FAKE, None, None, FAKE, FAKE, FAKE, 10, 128, None)
+    assert rc == _lib.PKV_E_INVALID
+    assert lib.pkv_merge_attn_states(None, None, None, None, None, None, 0, 128, None) == _lib.PKV_OK
