@@ -453,6 +453,26 @@ pkv_status pkv_slots_from_tables(const int32_t* tables, const int32_t* positions
                                  int64_t* slots_out);
 
 /*
+ * Host plan for pkv_paged_shared_prefix_decode (shared blocks, "03 ·
+ * PagedAttention", "Sharing: copy-on-write"): rows g*group_size ..
+ * (g+1)*group_size - 1 of tables [S][max_blocks] (lengths lens[S]) form group
+ * g. Its prefix is the longest run of leading blocks that every member lists
+ * with the same id (>= 0), not counting any member's last block (the one that
+ * takes the step's new token; copy-on-write keeps it private):
+ * prefix_tables[g][0..k) = those ids, prefix_lens[g] = k*bs. Member i's suffix
+ * is the rest of its row: suffix_tables[i][j] = tables[i][k + j] for
+ * k + j < ceil(L_i/bs), suffix_lens[i] = L_i - k*bs (L_i <= 0: 0). Unused
+ * entries are -1. All arrays are caller-owned host memory: prefix_tables
+ * [S/group_size][max_blocks], prefix_lens [S/group_size], suffix_tables
+ * [S][max_blocks], suffix_lens [S]. PKV_E_INVALID if S is not a multiple of
+ * group_size or a length exceeds max_blocks*bs (nothing written then).
+ */
+pkv_status pkv_shared_prefix_plan(const int32_t* tables, const int32_t* lens, int32_t S,
+                                  int32_t max_blocks, int32_t group_size, int32_t bs,
+                                  int32_t* prefix_tables, int32_t* prefix_lens,
+                                  int32_t* suffix_tables, int32_t* suffix_lens);
+
+/*
  * Prefix caching ("PagedAttention" daily term, the prefix-caching paragraph
  * after the copy-on-write figure; "Serving: vLLM and PagedAttention",
  * section 2.6): a full block is named by a hash of its tokens and of the

@@ -72,6 +72,8 @@ SIGNATURES = {
     "pkv_seq_info": (ctypes.c_int, [c_vp, c_i64, P_i64, P_i32]),
     "pkv_build_block_tables": (ctypes.c_int, [c_vp, P_i64, c_i32, c_i32, P_i32, P_i32]),
     "pkv_slots_from_tables": (ctypes.c_int, [P_i32, P_i32, c_i32, c_i32, c_i32, P_i64]),
+    "pkv_shared_prefix_plan": (ctypes.c_int, [P_i32, P_i32, c_i32, c_i32, c_i32, c_i32, P_i32, P_i32, P_i32,
+                                              P_i32]),
     "pkv_allocator_stats": (ctypes.c_int, [c_vp, ctypes.POINTER(PkvStats)]),
     "pkv_block_hashes": (ctypes.c_int, [P_i32, c_i32, c_i32, c_vp, c_i32, c_vp]),
     "pkv_seq_create_prefixed": (ctypes.c_int, [c_vp, c_i64, P_i32, c_i32, c_vp, c_i32, P_i64, P_i32]),

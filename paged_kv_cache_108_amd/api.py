@@ -298,37 +298,26 @@ def merge_attn_states(out, a, lse_a, b, lse_b, *, lse_out=None, stream=None):
 
 
 def shared_prefix_plan(block_tables, context_lens, group_size, bs):
-    """Host side of shared-prefix decode for groups of group_size consecutive
-    sequences (beams, parallel samples): per group, the leading blocks that
-    every member lists with the same id, not counting any member's last block
-    (it takes this step's new token, and after copy-on-write it is never
-    shared). Returns (prefix tables [n_groups][max_blocks], prefix lengths
-    [n_groups], suffix tables [S][max_blocks], suffix lengths [S]) as int32
-    numpy arrays; a group that shares nothing gets a prefix of length 0."""
-    tables = np.asarray(block_tables, dtype=np.int32)
-    lens = np.asarray(context_lens, dtype=np.int64)
+    """pkv_shared_prefix_plan (host): for groups of group_size consecutive
+    sequences (beams, parallel samples), the leading blocks that every member
+    lists with the same id, not counting any member's last block (it takes this
+    step's new token, and copy-on-write keeps it private). Returns (prefix
+    tables [n_groups][max_blocks], prefix lengths [n_groups], suffix tables
+    [S][max_blocks], suffix lengths [S]) as int32 numpy arrays; a group that
+    shares nothing gets a prefix of length 0."""
+    tables = _i32(block_tables)
+    lens = _i32(context_lens)
     S, max_blocks = tables.shape
     if group_size < 1 or S % group_size:
         raise ValueError("shared_prefix_plan: S must be a multiple of group_size")
     n_groups = S // group_size
-    pre_tab = np.full((n_groups, max_blocks), -1, dtype=np.int32)
-    pre_len = np.zeros(n_groups, dtype=np.int32)
-    suf_tab = np.full((S, max_blocks), -1, dtype=np.int32)
-    suf_len = np.zeros(S, dtype=np.int32)
-    for g in range(n_groups):
-        members = range(g * group_size, (g + 1) * group_size)
-        # blocks before each member's last one
-        full = min((int(lens[i]) - 1) // bs if lens[i] > 0 else 0 for i in members)
-        k = 0
-        while k < full and all(tables[i, k] == tables[g * group_size, k] for i in members):
-            k += 1
-        pre_tab[g, :k] = tables[g * group_size, :k]
-        pre_len[g] = k * bs
-        for i in members:
-            n = max(int(lens[i]), 0)
-            nb = -(-n // bs)
-            suf_tab[i, :nb - k] = tables[i, k:nb]
-            suf_len[i] = n - k * bs
+    pre_tab = np.empty((n_groups, max_blocks), dtype=np.int32)
+    pre_len = np.empty(n_groups, dtype=np.int32)
+    suf_tab = np.empty((S, max_blocks), dtype=np.int32)
+    suf_len = np.empty(S, dtype=np.int32)
+    check(lib().pkv_shared_prefix_plan(_ptr(tables, P_i32), _ptr(lens, P_i32), S, max_blocks, group_size, bs,
+                                       _ptr(pre_tab, P_i32), _ptr(pre_len, P_i32), _ptr(suf_tab, P_i32),
+                                       _ptr(suf_len, P_i32)))
     return pre_tab, pre_len, suf_tab, suf_len
 
 
@@ -387,9 +376,10 @@ class SharedPrefixDecode:
     """Decode steps for groups of group_size consecutive sequences that share
     leading blocks, reading the shared blocks once per group
     (pkv_paged_shared_prefix_decode). The plan (host tables, see
-    shared_prefix_plan) is built and uploaded once here, with the workspace;
-    __call__ runs one step: with k_new/v_new the write of each sequence's new
-    token and the attention, without them the attention alone."""
+    shared_prefix_plan) is built and uploaded once here, with the workspace,
+    and holds while the tables and lengths do: a step that changes them needs
+    a new plan. __call__ runs one step: with k_new/v_new the write of each
+    sequence's new token and the attention, without them the attention alone."""
 
     def __init__(self, block_tables, context_lens, group_size, bs, Hq, Hkv, d, device="cuda"):
         import torch

@@ -382,6 +382,51 @@ extern "C" pkv_status pkv_slots_from_tables(const int32_t* tables, const int32_t
     return ok();
 }
 
+extern "C" pkv_status pkv_shared_prefix_plan(const int32_t* tables, const int32_t* lens, int32_t S,
+                                             int32_t max_blocks, int32_t group_size, int32_t bs,
+                                             int32_t* prefix_tables, int32_t* prefix_lens,
+                                             int32_t* suffix_tables, int32_t* suffix_lens) {
+    if (S < 0 || max_blocks <= 0 || bs <= 0 || group_size < 1 || S % group_size != 0)
+        return fail(PKV_E_INVALID, "shared_prefix_plan: S=%d max_blocks=%d bs=%d group_size=%d", S,
+                    max_blocks, bs, group_size);
+    if (S > 0 && (!tables || !lens || !prefix_tables || !prefix_lens || !suffix_tables || !suffix_lens))
+        return fail(PKV_E_INVALID, "shared_prefix_plan: NULL pointer");
+    for (int32_t i = 0; i < S; ++i)
+        if ((int64_t)lens[i] > (int64_t)max_blocks * bs)
+            return fail(PKV_E_INVALID, "shared_prefix_plan: length %d of row %d beyond the table", lens[i], i);
+    const int32_t n_groups = S / group_size;
+    for (int32_t g = 0; g < n_groups; ++g) {
+        const int32_t first = g * group_size;
+        // blocks before every member's last one, listed with the same id by all
+        int32_t full = max_blocks;
+        for (int32_t m = 0; m < group_size; ++m) {
+            const int32_t L = lens[first + m];
+            full = std::min(full, L > 0 ? (L - 1) / bs : 0);
+        }
+        int32_t k = 0;
+        for (; k < full; ++k) {
+            const int32_t id = tables[(size_t)first * max_blocks + k];
+            bool same = id >= 0;
+            for (int32_t m = 1; m < group_size && same; ++m)
+                same = tables[(size_t)(first + m) * max_blocks + k] == id;
+            if (!same) break;
+        }
+        int32_t* pre = prefix_tables + (size_t)g * max_blocks;
+        for (int32_t j = 0; j < max_blocks; ++j) pre[j] = j < k ? tables[(size_t)first * max_blocks + j] : -1;
+        prefix_lens[g] = k * bs;
+        for (int32_t m = 0; m < group_size; ++m) {
+            const int32_t i = first + m;
+            const int32_t L = std::max(lens[i], 0);
+            const int32_t nb = (L + bs - 1) / bs;
+            int32_t* suf = suffix_tables + (size_t)i * max_blocks;
+            for (int32_t j = 0; j < max_blocks; ++j)
+                suf[j] = k + j < nb ? tables[(size_t)i * max_blocks + k + j] : -1;
+            suffix_lens[i] = L - k * bs;
+        }
+    }
+    return ok();
+}
+
 extern "C" pkv_status pkv_allocator_stats(const pkv_allocator* a, pkv_stats* out) {
     if (!a || !out) return fail(PKV_E_INVALID, "allocator_stats: NULL pointer");
     std::vector<int32_t> fill(a->P, 0);   // a shared block holds the same prefix in every table

@@ -416,3 +416,62 @@ def test_lse_and_merge_entry_points_reject_invalid_arguments():
     rc = lib.pkv_merge_attn_states(FAKE, None, None, FAKE, FAKE, FAKE, 10, 128, None)
     assert rc == _lib.PKV_E_INVALID
     assert lib.pkv_merge_attn_states(None, None, None, None, None, None, 0, 128, None) == _lib.PKV_OK
+
+
+def _plan_properties_hold(tab, lens, M, bs):
+    """Every member's prefix blocks followed by its suffix blocks are exactly its
+    own first ceil(L/bs) table entries; the prefix never holds a member's last
+    block; prefixes are whole blocks."""
+    pre_tab, pre_len, suf_tab, suf_len = pkv.shared_prefix_plan(tab, lens, M, bs)
+    for g in range(len(pre_len)):
+        assert pre_len[g] % bs == 0
+        k = pre_len[g] // bs
+        for i in range(g * M, (g + 1) * M):
+            L = max(int(lens[i]), 0)
+            nb = -(-L // bs)
+            assert k <= max(nb - 1, 0)
+            assert pre_len[g] + suf_len[i] == L
+            joined = list(pre_tab[g, :k]) + list(suf_tab[i, :nb - k])
+            assert joined == list(tab[i, :nb])
+            assert np.all(suf_tab[i, nb - k:] == -1)
+        assert np.all(pre_tab[g, k:] == -1)
+    return pre_tab, pre_len, suf_tab, suf_len
+
+
+def test_shared_prefix_plan_on_the_beam_layout():
+    for bs in (8, 16, 32):
+        w = W.make("beam", bs=bs)
+        pre_tab, pre_len, suf_tab, suf_len = _plan_properties_hold(w.block_tables, w.context_lens, 4, bs)
+        assert np.all(pre_len == 1024)                  # each group's whole prompt, every block size
+        assert np.array_equal(suf_len, w.context_lens - 1024)
+        assert np.array_equal(pre_tab[:, :1024 // bs], w.block_tables[::4, :1024 // bs])
+
+
+def test_shared_prefix_plan_edges():
+    bs = 4
+    tab = np.full((6, 8), -1, dtype=np.int32)
+    tab[0, :4] = [10, 11, 12, 13]        # group 0 (M = 3): members share blocks 10, 11, 12
+    tab[1, :5] = [10, 11, 12, 20, 21]
+    tab[2, :4] = [10, 11, 12, 30]
+    tab[3, :2] = [40, 41]                # group 1: differs at block 0 -> nothing shared
+    tab[4, :2] = [50, 41]
+    lens = np.array([16, 18, 13, 8, 6, 0])
+    pre_tab, pre_len, suf_tab, suf_len = _plan_properties_hold(tab, lens, 3, bs)
+    # member 0 fills block 13 exactly (L = 16): its last block is 13, so the
+    # prefix stops before it, at 3 blocks
+    assert list(pre_len) == [12, 0]
+    assert list(suf_len) == [4, 6, 1, 8, 6, 0]
+    # groups of one: everything before the last block is "shared"
+    _, pre1, _, suf1 = _plan_properties_hold(tab, lens, 1, bs)
+    assert list(pre1) == [12, 16, 12, 4, 4, 0] and list(suf1) == [4, 2, 1, 4, 2, 0]
+    # groups of two: rows 0/1 share 3 blocks, rows 2/3 none, rows 4/5 none (row 5 is empty)
+    _, pre2, _, _ = _plan_properties_hold(tab, lens, 2, bs)
+    assert list(pre2) == [12, 0, 0]
+    with pytest.raises(ValueError):
+        pkv.shared_prefix_plan(tab, lens, 4, bs)         # 6 rows are not groups of 4
+    out = [np.empty(48, dtype=np.int32), np.empty(6, dtype=np.int32)] * 2
+    ptr = lambda a: a.ctypes.data_as(_lib.P_i32)          # noqa: E731
+    t32, l32 = np.ascontiguousarray(tab), lens.astype(np.int32)
+    assert pkv.lib().pkv_shared_prefix_plan(ptr(t32), ptr(l32), 6, 8, 4, bs, *map(ptr, out)) == _lib.PKV_E_INVALID
+    with pytest.raises(pkv.PkvError):
+        pkv.shared_prefix_plan(tab, np.array([33, 0, 0, 0, 0, 0]), 3, bs)   # beyond 8 blocks of 4
