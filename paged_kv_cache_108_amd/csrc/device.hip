@@ -64,6 +64,10 @@ constexpr int kWaves = PKV_WAVES;         // waves per workgroup
 constexpr int kThreads = kWaves * 64;
 constexpr int kMaxCachedLens = 4096;      // sequences whose lengths a workgroup keeps in LDS
 constexpr int kMaxWorkers = 4096;         // waves of the balanced split, at most (sizes its workspace)
+#ifndef PKV_MIN_POS
+#define PKV_MIN_POS 4
+#endif
+constexpr unsigned kMinPositions = PKV_MIN_POS;   // balanced split: positions per wave, at least
 constexpr int kMergeBatch = 32;           // records per round trip for rows that merge 32 or more
 // 16-column tiles per pass for wide query windows. Each tile adds its own
 // q fragment, accumulator and softmax to every chunk: four tiles at d 128
@@ -954,21 +958,25 @@ paged_attn_stream_kernel(AttnParams p) {
         }
 
     const unsigned V = (unsigned)pre[kThreads] * (unsigned)HS;   // positions in all
-    const unsigned W = gridDim.x * kWaves;
+    const unsigned W_all = gridDim.x * kWaves;
     const unsigned w = blockIdx.x * kWaves + wave;
+    // A short input is cut into fewer, longer ranges (at least kMinPositions
+    // positions each), so that a merged row has fewer records; the waves past
+    // the last range only take part in the write.
+    const unsigned W = min(W_all, max(1u, (V + kMinPositions - 1) / kMinPositions));
     const Split split(V, W);
-    const unsigned v_beg = split.start(w);
-    const unsigned v_end = split.start(w + 1);
+    const unsigned v_beg = w < W ? split.start(w) : V;
+    const unsigned v_end = w < W ? split.start(w + 1) : V;
     const int n_pos = (int)(v_end - v_beg);
 
     // Decode step: this wave's share of the write of every sequence's new token
-    // (position L - 1): part q = (sequence, kv head, K or V), parts w, w + W, ...
+    // (position L - 1): part q = (sequence, kv head, K or V), parts w, w + W_all, ...
     // Lane l handles channels l and l + 64. The reads are issued here and the
     // stores after the first window's table reads have returned.
     auto write_parts = [&](auto&& between) {
         constexpr int NCH = D / 64;
         const int n_parts = STEP ? p.S * p.Hkv * 2 : 0;
-        for (int q0 = (int)w; q0 < n_parts; q0 += (int)W) {
+        for (int q0 = (int)w; q0 < n_parts; q0 += (int)W_all) {
             const int i = q0 / (2 * p.Hkv);
             const int rem = q0 - i * 2 * p.Hkv;
             const int g = rem >> 1;
