@@ -8,36 +8,38 @@
 // the kv head. The pages' own kernel targets other hardware; this one is built
 // for wave64 + MFMA:
 //
-//  * Work item = (sequence i, kv head g, partition p). A persistent grid of
-//    256-thread workgroups (4 waves; as many as the GPU holds at once) takes
-//    the items round-robin. Waves take an item's 16-token chunks round-robin,
-//    each keeping its own online-softmax state; the four states are merged
-//    exactly through LDS at the end of the item.
-//  * Scores: S^T[16 tokens][16 heads] = K_chunk . Q^T with one MFMA chain
-//    (bf16 16x16x32, or fp32 16x16x4 for an fp32 cache). The K operand rows
-//    are tokens, so each lane's K fragment is 8 (bf16), 16 (fp8) or 4 (fp32)
-//    consecutive channels of one token: 16-byte global loads, 64 contiguous
-//    bytes per token row per instruction. Heads G..15 of the MFMA are padding.
-//  * The MFMA result layout (lane = head + 16*token_group, 4 tokens per lane)
-//    is exactly the B-operand layout of the P.V MFMA
-//    (O^T[dims][heads] += V^T[dims][tokens] . P^T[tokens][heads]), so P never
-//    leaves registers. V tiles are stored channel-major ([d][bs] per block and
-//    head) so the V^T operand is 4 consecutive tokens of one channel.
-//  * P stays float32 to the accuracy of the product: for bf16/fp8 caches it is
-//    split into hi + lo bf16 parts and both are multiplied (two MFMAs), since
-//    rounding P alone to bf16 costs ~2e-3 relative error.
-//  * Softmax max and sum across the 4 token groups of a head use gfx950's
-//    v_permlane16_swap / v_permlane32_swap (no LDS traffic).
-//  * Split-K: partition p covers tokens [p*part, (p+1)*part); a sequence with
-//    more than one partition writes (m, l, o) partials and a second kernel
-//    merges them in fixed partition order. No atomics anywhere: results are
-//    bit-reproducible.
-//  * Work order: every full partition of every sequence first, then each
-//    sequence's last, ragged partition, so long items start early and short
-//    ones fill the tail.
-//  * A second decomposition (partition_size = PKV_PARTITION_BALANCED) cuts
-//    the chunks of all (sequence, kv head) segments into one equal range per
-//    wave; pieces of segments write partial records for the merge kernel.
+//  * The unit of work is a 16-token chunk of one (sequence, kv head): one MFMA
+//    tile of scores S^T[16 tokens][16 columns] = K_chunk . Q^T (bf16 16x16x32,
+//    or fp32 16x16x4 for an fp32 cache; fp8 codes are converted exactly to
+//    bf16). Columns are the G query heads (padded to 16), or (query, head)
+//    pairs for windows of several queries. The K operand rows are tokens, so a
+//    lane's K fragment is consecutive channels of one token: 16-byte loads.
+//  * The MFMA result layout is exactly the B operand of the P.V MFMA
+//    (O^T[dims][columns] += V^T[dims][tokens] . P^T[tokens][columns]), so P
+//    never leaves registers. V tiles are channel-major inside sub-tiles of
+//    min(bs, 16) tokens, so the V^T operand is 4 consecutive tokens of one
+//    channel and a chunk reads one whole sub-tile.
+//  * P keeps float32 accuracy: for bf16/fp8 caches it is split into hi + lo
+//    bf16 parts that one MFMA takes together (rounding P to bf16 alone costs
+//    about 2e-3 relative error).
+//  * Softmax max and sum across the 4 token groups of a column use gfx950's
+//    v_permlane16_swap / v_permlane32_swap.
+//  * Default split (paged_attn_stream_kernel, partition_size =
+//    PKV_PARTITION_BALANCED): the chunks of all segments, plus a fixed cost per
+//    segment, are cut into one equal contiguous range per wave, with one
+//    4-wave workgroup per CU. Each wave streams its chunks through a two-stage
+//    register pipeline with nontemporal loads; pieces of split segments write
+//    partial records that paged_attn_merge_kernel combines in fixed order.
+//    Instantiations: decode, query windows, and the decode step with the write
+//    of the new tokens fused in.
+//  * Fixed partitions (paged_attn_partition_kernel): partition p covers tokens
+//    [p*part, (p+1)*part), items (sequence, kv head, partition) over a
+//    persistent grid, merged by the same merge kernel.
+//  * Shared prefixes: a window pass over a group's shared blocks and a decode
+//    pass over each sequence's own blocks, combined exactly by log-sum-exp
+//    (shared_prefix_merge_kernel, merge_states_kernel).
+//  * No atomics anywhere: every split depends only on the lengths and every
+//    record has a fixed slot, so results are bit-reproducible.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
