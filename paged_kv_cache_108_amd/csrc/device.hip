@@ -241,7 +241,23 @@ struct AttnParams {
     float v_scale;
     float* lse;            // optional [rows]: base-2 log of each output row's softmax sum
     int causal;            // query windows: 1 causal inside the window, 0 every query sees all L
+    // Shared-prefix launches: sequences 0 .. n_pre-1 are group prefixes (n_q
+    // queries each, tables/lens/max_blocks/max_len, rows in out/lse) and
+    // sequences n_pre .. S-1 are member suffixes (one query each, the
+    // arrays below, rows in out2/lse2; member m's query is q row m).
+    int n_pre;             // 0 for every other launch
+    const int32_t* tables2;
+    const int32_t* lens2;
+    int max_blocks2, max_len2;
+    float* out2;
+    float* lse2;
 };
+
+// Clamped context length of sequence s (of either table set).
+__device__ __forceinline__ int clamped_len(const AttnParams& p, int s) {
+    if (p.n_pre > 0 && s >= p.n_pre) return min(p.lens2[s - p.n_pre], p.max_len2);
+    return min(p.lens[s], p.max_len);
+}
 
 // Per-cache-type register fragments of one 16-token chunk.
 template <int KV, int D> struct Frag;
@@ -750,7 +766,7 @@ __device__ __forceinline__ void prefix_over_sequences(const AttnParams& p, int* 
     const int s_hi = min(p.S, s_lo + per);
     int cnt = 0;
     for (int s = s_lo; s < s_hi; ++s) {
-        const int L = min(p.lens[s], p.max_len);
+        const int L = clamped_len(p, s);
         if (sL) sL[s] = L;
         cnt += count(s, L);
     }
@@ -920,14 +936,17 @@ paged_attn_partition_kernel(AttnParams p) {
 // segment's first chunk writes the segment's descriptor (first record, record
 // count) for the merge kernel. Launched one workgroup per compute unit (one
 // wave per SIMD), so the kernel may use the whole register file.
-enum StreamMode { SM_DECODE = 0, SM_WINDOW = 1, SM_STEP = 2 };
+enum StreamMode { SM_DECODE = 0, SM_WINDOW = 1, SM_STEP = 2, SM_SHARED = 3 };
 
 template <int KV, int D, int BS, int MODE, int NT>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1)))
 paged_attn_stream_kernel(AttnParams p) {
-    constexpr bool MQ = MODE == SM_WINDOW;     // a window of queries per sequence
-    static_assert(NT == 1 || MQ, "several column tiles only for query windows");
-    constexpr bool STEP = MODE == SM_STEP;     // decode with this step's write fused in
+    // SM_SHARED: group prefixes (a window of the group's queries, no causal
+    // mask) and member suffixes (decode, with the step's write) in one launch
+    constexpr bool SH = MODE == SM_SHARED;
+    constexpr bool MQ = MODE == SM_WINDOW || SH;   // several queries per sequence
+    static_assert(NT == 1 || MODE == SM_WINDOW, "several column tiles only for query windows");
+    constexpr bool STEP = MODE == SM_STEP || SH;   // this step's write fused in
     constexpr int kSegCost = seg_cost(KV, D);
     extern __shared__ float smem[];           // the length cache (p.cache_lens)
     __shared__ int pre[kThreads + 1];
@@ -944,7 +963,12 @@ paged_attn_stream_kernel(AttnParams p) {
     const int HS = p.Hkv * n_qg;
     const int n_q = MQ ? p.n_q : 1;
     int* sL = p.cache_lens ? reinterpret_cast<int*>(smem) : nullptr;
-    auto seq_len = [&](int s) { return sL ? sL[s] : min(p.lens[s], p.max_len); };
+    auto seq_len = [&](int s) { return sL ? sL[s] : clamped_len(p, s); };
+    auto is_sfx = [&](int s) { return SH && s >= p.n_pre; };      // a member suffix
+    auto table_row = [&](int s) -> const int32_t* {
+        if (is_sfx(s)) return p.tables2 + (size_t)(s - p.n_pre) * p.max_blocks2;
+        return p.tables + (size_t)s * p.max_blocks;
+    };
     auto n_chunks_of = [&](int L) { return L > 0 ? (L + 15) >> 4 : 0; };
     auto span_of = [&](int L) { return L > 0 ? kSegCost + ((L + 15) >> 4) : 0; };   // positions per segment
     auto span = [&](int s) { return span_of(seq_len(s)); };
@@ -952,11 +976,13 @@ paged_attn_stream_kernel(AttnParams p) {
     prefix_over_sequences(p, pre, wsum, sL, [&](int, int L) { return span_of(L); });
     for (int s = blockIdx.x; s < p.S; s += gridDim.x)       // sequences with no tokens: zero rows
         if (seq_len(s) <= 0) {
-            for (int e = threadIdx.x; e < n_q * p.Hq * D; e += kThreads)
-                p.out[(size_t)s * n_q * p.Hq * D + e] = 0.f;
-            if (p.lse)
-                for (int e = threadIdx.x; e < n_q * p.Hq; e += kThreads)
-                    p.lse[(size_t)s * n_q * p.Hq + e] = -INFINITY;
+            const bool sf = is_sfx(s);
+            const int rows = sf ? 1 : n_q;
+            float* ob = sf ? p.out2 + (size_t)(s - p.n_pre) * p.Hq * D : p.out + (size_t)s * n_q * p.Hq * D;
+            float* lb = sf ? p.lse2 + (size_t)(s - p.n_pre) * p.Hq : p.lse ? p.lse + (size_t)s * n_q * p.Hq : nullptr;
+            for (int e = threadIdx.x; e < rows * p.Hq * D; e += kThreads) ob[e] = 0.f;
+            if (lb)
+                for (int e = threadIdx.x; e < rows * p.Hq; e += kThreads) lb[e] = -INFINITY;
         }
 
     const unsigned V = (unsigned)pre[kThreads] * (unsigned)HS;   // positions in all
@@ -977,16 +1003,18 @@ paged_attn_stream_kernel(AttnParams p) {
     // stores after the first window's table reads have returned.
     auto write_parts = [&](auto&& between) {
         constexpr int NCH = D / 64;
-        const int n_parts = STEP ? p.S * p.Hkv * 2 : 0;
+        const int n_tok = SH ? p.S - p.n_pre : p.S;  // sequences with a new token
+        const int n_parts = STEP && (!SH || p.k_new) ? n_tok * p.Hkv * 2 : 0;
         for (int q0 = (int)w; q0 < n_parts; q0 += (int)W_all) {
-            const int i = q0 / (2 * p.Hkv);
+            const int i = q0 / (2 * p.Hkv);        // new token i (k_new/v_new row)
             const int rem = q0 - i * 2 * p.Hkv;
             const int g = rem >> 1;
             const bool is_v = rem & 1;
-            const int L = seq_len(i);
+            const int sq = SH ? p.n_pre + i : i;     // its sequence
+            const int L = seq_len(sq);
             if (L <= 0) continue;
             const int pos = L - 1;
-            const int b = min(max(p.tables[(size_t)i * p.max_blocks + pos / BS], 0), p.P - 1);
+            const int b = min(max(table_row(sq)[pos / BS], 0), p.P - 1);
             const int o = pos % BS;
             const size_t src_row = ((size_t)i * p.Hkv + g) * D;
             uint32_t val[NCH];
@@ -1046,7 +1074,7 @@ paged_attn_stream_kernel(AttnParams p) {
             locate(in ? v_beg + kb + lane : v_end - 1, a_seg, a_kc, L);
             if (in && a_kc >= 0) {
                 const int i = a_seg / HS;
-                const int32_t* __restrict__ row = p.tables + (size_t)i * p.max_blocks;
+                const int32_t* __restrict__ row = table_row(i);
                 const int tok = 16 * a_kc;
                 if constexpr (BS == 8) {
                     a0 = row[tok / 8];
@@ -1139,7 +1167,9 @@ paged_attn_stream_kernel(AttnParams p) {
             const int qg = g2 - g * n_qg;
             const int L = __builtin_amdgcn_readfirstlane(seq_len(i));
             const int nch = n_chunks_of(L);
-            // this lane's column in tile t: query j[t] of the window, head g*G + r
+            const bool sfx = is_sfx(i);
+            // this lane's column in tile t: query j[t] of the window, head g*G + r;
+            // out_row[t] is also the q row's offset (q and out share their row order)
             int j[NT];
             bool live[NT];
             size_t out_row[NT];
@@ -1149,15 +1179,21 @@ paged_attn_stream_kernel(AttnParams p) {
                 const int jj = MQ ? c / G : 0;
                 const int r = MQ ? c - jj * G : r16;
                 j[t] = qg * (MQ ? p.qgs : 1) + jj;
-                live[t] = c < (MQ ? p.cols : G) && j[t] < n_q;
-                out_row[t] = (((size_t)i * n_q + j[t]) * p.Hq + g * G + r) * D;
+                live[t] = c < (MQ ? p.cols : G) && j[t] < (sfx ? 1 : n_q);
+                const size_t row = sfx ? (size_t)(i - p.n_pre) : (size_t)i * n_q + j[t];
+                out_row[t] = (row * p.Hq + g * G + r) * D;
             }
+            float* const obase = sfx ? p.out2 : p.out;
+            float* const lbase = sfx ? p.lse2 : p.lse;
             const bool first = !started;
             started = true;
             if (kc == 0 || first) {               // a segment starts
 #pragma unroll
                 for (int t = 0; t < NT; ++t) load_q_row<KV, D>(p, out_row[t], live[t], j4, qf[t]);
-                if constexpr (STEP) load_new_token<KV, D>(p, ((size_t)i * p.Hkv + g) * D, r16, j4, ntstage[wave], nt);
+                if constexpr (STEP)
+                    if (!SH || (sfx && p.k_new))
+                        load_new_token<KV, D>(p, ((size_t)(SH ? i - p.n_pre : i) * p.Hkv + g) * D, r16, j4,
+                                              ntstage[wave], nt);
                 seg_from_start = kc == 0;
                 seg_at_range_start = first;
                 if (kc == 0 && lane == 0) {       // descriptor for the merge kernel
@@ -1170,7 +1206,7 @@ paged_attn_stream_kernel(AttnParams p) {
             // the write of position L - 1 runs concurrently: take its value
             // from the new token instead of the pool
             if constexpr (STEP)
-                if (kc == nch - 1) patch_new_token<KV, D>(f, nt, L - 1 - tc, r16, j4);
+                if (kc == nch - 1 && (!SH || (sfx && p.k_new))) patch_new_token<KV, D>(f, nt, L - 1 - tc, r16, j4);
             const bool tail = tc + 16 > L;        // tokens >= L hold no data
             // query j sees tokens < L - n_q + 1 + j (causal inside the window)
             const bool masked = MQ && p.causal ? tc + 16 > L - n_q + 1 : tail;
@@ -1212,11 +1248,11 @@ paged_attn_stream_kernel(AttnParams p) {
                     if (live[t]) {
                         if (whole) {
                             const float sc_o = p.v_scale / l_tot;
-                            float* orow = p.out + out_row[t] + 4 * j4;
+                            float* orow = obase + out_row[t] + 4 * j4;
 #pragma unroll
                             for (int s = 0; s < D / 16; ++s)
                                 *reinterpret_cast<f32x4*>(orow + 16 * s) = o[t][s] * sc_o;
-                            if (p.lse && j4 == 0) p.lse[out_row[t] / D] = m_run[t] + __log2f(l_tot);
+                            if (lbase && j4 == 0) lbase[out_row[t] / D] = m_run[t] + __log2f(l_tot);
                         } else {
                             const size_t rr = (size_t)(2 * w + (seg_at_range_start ? 0 : 1)) * C + 16 * t + r16;
                             const size_t nrec = (size_t)p.n_rec;
@@ -1620,6 +1656,8 @@ AttnKernel pick_stream(int d, int bs, int mode, int tiles) {
     }
     if (mode == SM_STEP)
         return d == 64 ? pick_stream_bs<KV, 64, SM_STEP, 1>(bs) : pick_stream_bs<KV, 128, SM_STEP, 1>(bs);
+    if (mode == SM_SHARED)
+        return d == 64 ? pick_stream_bs<KV, 64, SM_SHARED, 1>(bs) : pick_stream_bs<KV, 128, SM_SHARED, 1>(bs);
     return d == 64 ? pick_stream_bs<KV, 64, SM_DECODE, 1>(bs) : pick_stream_bs<KV, 128, SM_DECODE, 1>(bs);
 }
 
@@ -1830,7 +1868,7 @@ pkv_status attn_launch(const char* fn, float* out, const void* q, const void* k_
     if (n_upper > 0x7FFFFFFFLL) return fail(PKV_E_INVALID, "%s: too many work items", fn);
     if (validate_only) return ok();
 
-    AttnParams prm;
+    AttnParams prm{};
     prm.out = out;
     prm.q = q;
     prm.k = k_cache;
@@ -2033,7 +2071,9 @@ extern "C" pkv_status pkv_merge_attn_states(float* out, float* lse_out, const fl
 namespace {
 
 // Workspace of pkv_paged_shared_prefix_decode: the prefix pass's balanced
-// workspace, the suffix pass's, then both passes' rows and lse values.
+// workspace (with room for the descriptors of every prefix and suffix
+// segment, for the one-launch form), the suffix pass's, then both passes'
+// rows and lse values.
 struct SharedPrefixLayout {
     size_t a, b, out_a, lse_a, out_b, lse_b, total;
 };
@@ -2043,7 +2083,8 @@ SharedPrefixLayout shared_prefix_layout(int32_t n_groups, int32_t M, int32_t Hq,
     const size_t S = (size_t)n_groups * (size_t)M;
     const size_t rows = S * (size_t)Hq;
     L.a = 0;
-    L.b = L.a + up(attn_workspace_size(n_groups, M, Hq, Hkv, d, 0, PKV_PARTITION_BALANCED));
+    L.b = L.a + up(attn_workspace_size(n_groups, M, Hq, Hkv, d, 0, PKV_PARTITION_BALANCED) +
+                   2 * S * (size_t)Hkv * sizeof(int));
     L.out_a = L.b + up(attn_workspace_size((int32_t)S, 1, Hq, Hkv, d, 0, PKV_PARTITION_BALANCED));
     L.lse_a = L.out_a + up(rows * d * sizeof(float));
     L.out_b = L.lse_a + up(rows * sizeof(float));
@@ -2098,18 +2139,98 @@ extern "C" pkv_status pkv_paged_shared_prefix_decode(
     step.k_inv = cache_dtype == PKV_FP8_E4M3 ? k_inv_scale : 1.f;
     step.v_inv = cache_dtype == PKV_FP8_E4M3 ? v_inv_scale : 1.f;
     AttnParams pb, pa;
-    // both passes' arguments are checked before either is launched
+    const int32_t G = Hq / Hkv;
+    const QueryGroups qa = query_groups(M, G, d);
+    // A group's M queries fit one 16-column tile: prefixes and suffixes go
+    // through one launch of the stream kernel (the prefix segments as windows
+    // without a causal mask, the suffix segments as decode-step segments).
+    // Otherwise two launches: the suffix pass, then the prefix pass.
+    const bool one_launch = qa.tiles == 1 && (int64_t)n_groups + S <= 0x7FFFFFFF;
+    // both passes' arguments are checked before anything is launched
     for (int launch = 0; launch < 2; ++launch) {
+        const bool check_only = launch == 0 || one_launch;
         pkv_status rc = attn_launch(fn, out_b, q, k_cache, v_cache, suffix_tables, suffix_lens, S, 1, Hq, Hkv,
                                     d, bs, P, suffix_max_blocks, max_suffix_len, softmax_scale, k_scale,
                                     v_scale, q_dtype, cache_dtype, PKV_PARTITION_BALANCED, ws + lay.b,
-                                    lay.out_a - lay.b, stream, step, lse_b, true, false, &pb, launch == 0);
+                                    lay.out_a - lay.b, stream, step, lse_b, true, false, &pb, check_only);
         if (rc != PKV_OK) return rc;
         rc = attn_launch(fn, out_a, q, k_cache, v_cache, prefix_tables, prefix_lens, n_groups, M, Hq, Hkv, d,
                          bs, P, prefix_max_blocks, max_prefix_len, softmax_scale, k_scale, v_scale, q_dtype,
                          cache_dtype, PKV_PARTITION_BALANCED, ws + lay.a, lay.b - lay.a, stream, StepWrite(),
-                         lse_a, false, false, &pa, launch == 0);
+                         lse_a, false, false, &pa, check_only);
         if (rc != PKV_OK) return rc;
+    }
+    if (one_launch) {
+        const int64_t n_seq = (int64_t)n_groups + S;
+        const int64_t n_upper = n_seq * Hkv * (((int64_t)std::max(max_prefix_len, max_suffix_len) + 15) / 16 +
+                                               kSegCostMax);
+        if (n_upper > 0x7FFFFFFFLL) return fail(PKV_E_INVALID, "%s: too many work items", fn);
+        const int kv = cache_dtype == PKV_F32 ? KV_F32 : cache_dtype == PKV_BF16 ? KV_BF16 : KV_FP8;
+        AttnKernel kern = kv == KV_F32 ? pick_stream<KV_F32>(d, bs, SM_SHARED, 1)
+                        : kv == KV_BF16 ? pick_stream<KV_BF16>(d, bs, SM_SHARED, 1)
+                                        : pick_stream<KV_FP8>(d, bs, SM_SHARED, 1);
+        AttnParams prm{};
+        prm.out = out_a;
+        prm.lse = lse_a;
+        prm.out2 = out_b;
+        prm.lse2 = lse_b;
+        prm.q = q;
+        prm.k = k_cache;
+        prm.v = v_cache;
+        prm.tables = prefix_tables;
+        prm.lens = prefix_lens;
+        prm.max_blocks = prefix_max_blocks;
+        prm.max_len = max_prefix_len;
+        prm.tables2 = suffix_tables;
+        prm.lens2 = suffix_lens;
+        prm.max_blocks2 = suffix_max_blocks;
+        prm.max_len2 = max_suffix_len;
+        prm.n_pre = n_groups;
+        prm.S = (int)n_seq;
+        prm.Hq = Hq;
+        prm.Hkv = Hkv;
+        prm.G = G;
+        prm.P = P;
+        prm.n_q = M;
+        prm.qgs = qa.qgs;
+        prm.n_qg = qa.n_qg;
+        prm.cols = qa.cols;
+        prm.part_tokens = 32;
+        prm.n_part = 1;
+        prm.balanced = 1;
+        prm.causal = 0;
+        prm.ws = reinterpret_cast<float*>(ws + lay.a);
+        prm.desc = reinterpret_cast<int*>(ws + lay.a + balanced_records_bytes((size_t)qa.cols, d));
+        prm.k_new = k_new;
+        prm.v_new = v_new;
+        prm.k_inv = step.k_inv;
+        prm.v_inv = step.v_inv;
+        prm.qk_scale = softmax_scale * (cache_dtype == PKV_FP8_E4M3 ? k_scale : 1.f) * kLog2e;
+        prm.v_scale = cache_dtype == PKV_FP8_E4M3 ? v_scale : 1.f;
+        prm.cache_lens = n_seq <= kMaxCachedLens;
+        const size_t lds = (size_t)(prm.cache_lens ? n_seq : 0) * sizeof(int);
+        const int resident = resident_workgroups(kern, lds);
+        const int cus = compute_units();
+        if (resident <= 0 || cus <= 0) return fail(PKV_E_HIP, "%s: device query failed", fn);
+        int64_t grid = std::min(cus, resident);
+        if (grid * kWaves > kMaxWorkers) grid = kMaxWorkers / kWaves;
+        prm.n_workers = (int)(grid * kWaves);
+        prm.n_rec = 2 * prm.n_workers;
+        hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kThreads), lds, static_cast<hipStream_t>(stream), prm);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return fail(PKV_E_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+        // the merge's two views of the one launch: prefix rows and records,
+        // and suffix rows with the same records and the suffix descriptors
+        pa = prm;
+        pa.S = n_groups;
+        pb = prm;
+        pb.out = out_b;
+        pb.lse = lse_b;
+        pb.lens = suffix_lens;
+        pb.max_len = max_suffix_len;
+        pb.S = S;
+        pb.n_pre = 0;
+        pb.desc = prm.desc + 2 * (size_t)n_groups * Hkv * qa.n_qg;
     }
     const unsigned grid = (unsigned)(((int64_t)S * Hq + kWaves - 1) / kWaves);
     auto st = static_cast<hipStream_t>(stream);

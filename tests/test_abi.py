@@ -395,7 +395,7 @@ def test_shared_prefix_decode_workspace_and_empty_call():
     suf = lib.pkv_paged_decode_attn_workspace_size(128, 32, 8, 128, 0, pkv.PKV_PARTITION_BALANCED)
     rows = 128 * 32
     up = lambda x: -(-x // 256) * 256  # noqa: E731
-    assert n == up(pre) + up(suf) + 2 * (up(rows * 128 * 4) + up(rows * 4))
+    assert n == up(pre + 2 * 128 * 8 * 4) + up(suf) + 2 * (up(rows * 128 * 4) + up(rows * 4))
     assert lib.pkv_paged_shared_prefix_decode_workspace_size(0, 4, 32, 8, 128) == 0
     assert lib.pkv_paged_shared_prefix_decode_workspace_size(4, 4, 30, 8, 128) == 0
     assert _shared(ng=0, out=None, q=None, ws=None, wsb=0) == _lib.PKV_OK     # nothing to do

@@ -639,6 +639,23 @@ def test_shared_prefix_edge_groups():
     _shared_prefix_case(w, 3, step=True)
 
 
+def test_shared_prefix_wide_groups_two_launches():
+    # 3 members x 8 query heads per kv head = 24 columns: more than one MFMA
+    # tile, so the suffix and prefix passes run as two launches
+    bs, Hq, Hkv, d = 16, 16, 2, 128
+    lens = [300, 310, 290, 47, 100, 60]
+    w = W.make_custom(lens=lens, Hq=Hq, Hkv=Hkv, d=d, bs=bs, cfg=993, pool_factor=2.0)
+    tab = w.block_tables.copy()
+    tab[1, :18] = tab[0, :18]
+    tab[2, :18] = tab[0, :18]
+    tab[4, :2] = tab[3, :2]
+    tab[5, :2] = tab[3, :2]
+    w.block_tables[:] = tab
+    assert list(pkv.shared_prefix_plan(tab, lens, 3, bs)[1]) == [288, 32]
+    _shared_prefix_case(w, 3)
+    _shared_prefix_case(w, 3, step=True)
+
+
 def test_shared_prefix_decode_empty_suffix_plan():
     # a hand-made plan: group 0's members list the same 4 blocks and keep no
     # suffix; group 1 shares one block and keeps suffixes of 14 and 34 tokens
