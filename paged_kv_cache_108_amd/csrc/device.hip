@@ -1137,6 +1137,15 @@ paged_attn_stream_kernel(AttnParams p) {
         m_run[t] = -INFINITY;
         l_run[t] = 0.f;
     }
+    // this lane's column in tile t is query col_j[t] of its query group and
+    // head col_r[t] of the kv head's G (the same for every segment)
+    int col_j[NT], col_r[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        const int c = 16 * t + r16;
+        col_j[t] = MQ ? c / G : 0;
+        col_r[t] = MQ ? c - col_j[t] * G : r16;
+    }
     bool started = false;                     // this wave has begun its first chunk
     bool seg_from_start = false;              // the current segment began at its chunk 0
     bool seg_at_range_start = false;          // ... and at this wave's first chunk
@@ -1176,12 +1185,10 @@ paged_attn_stream_kernel(AttnParams p) {
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
                 const int c = 16 * t + r16;
-                const int jj = MQ ? c / G : 0;
-                const int r = MQ ? c - jj * G : r16;
-                j[t] = qg * (MQ ? p.qgs : 1) + jj;
+                j[t] = qg * (MQ ? p.qgs : 1) + col_j[t];
                 live[t] = c < (MQ ? p.cols : G) && j[t] < (sfx ? 1 : n_q);
                 const size_t row = sfx ? (size_t)(i - p.n_pre) : (size_t)i * n_q + j[t];
-                out_row[t] = (row * p.Hq + g * G + r) * D;
+                out_row[t] = (row * p.Hq + g * G + col_r[t]) * D;
             }
             float* const obase = sfx ? p.out2 : p.out;
             float* const lbase = sfx ? p.lse2 : p.lse;
