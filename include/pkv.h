@@ -323,14 +323,19 @@ pkv_status pkv_merge_attn_states(float* out, float* lse_out, const float* a, con
  *
  * k_new/v_new ([S][Hkv][d], as for pkv_kv_cache_write; both NULL: no write)
  * are each sequence's new token: it is written at the suffix's last position
- * (suffix_lens[i] - 1; sequences with an empty suffix write nothing), before
- * any attention reads the pools, and attended to. So a plan whose suffixes
- * keep each sequence's last block (the one that takes the new token) makes
- * this one decode step, like pkv_paged_decode_step.
+ * (suffix_lens[i] - 1; sequences with an empty suffix write nothing) and
+ * attended to, as by pkv_paged_decode_step. So a plan whose suffixes keep each
+ * sequence's last block (the one that takes the new token) makes this one
+ * decode step.
  *
- * Order on `stream`: the suffix pass (with the write), the prefix pass (every
- * query of a group sees every prefix token), then one merge kernel over the
- * partial states of both. workspace: pkv_paged_shared_prefix_decode_workspace_size
+ * Launches on `stream`: when a group's M queries fit one 16-column MFMA tile
+ * (M * Hq/Hkv <= 16), one attention kernel takes the prefixes (every query of
+ * a group sees every prefix token) and the suffixes (with the write) together;
+ * otherwise the suffix pass (with the write) runs first, then the prefix
+ * pass. Then one merge kernel combines the partial states of both. A new
+ * token's slot must lie in its sequence's suffix blocks (the plan of
+ * pkv_shared_prefix_plan guarantees it), since prefix blocks may be read
+ * while the write runs. workspace: pkv_paged_shared_prefix_decode_workspace_size
  * bytes (device, caller-owned, any contents). Limits and dtypes as for
  * pkv_paged_decode_step and pkv_paged_multi_query_attn (1 <= M <= 4096);
  * k_inv_scale/v_inv_scale are used only for an fp8 cache with a write.
