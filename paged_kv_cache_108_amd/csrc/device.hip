@@ -1341,7 +1341,11 @@ paged_attn_merge_kernel(AttnParams p) {
         rec0 = (i * p.Hkv + g) * p.n_part;
     }
     // record k of this segment
+    // record k of this segment; k past the last is read as the last one, so
+    // loads the compiler issues ahead of their use stay inside this call's
+    // records (their values are never used)
     auto rec_of = [&](int k) -> size_t {
+        k = min(k, n - 1);
         if (balanced) return k == 0 ? (size_t)rec0 : (size_t)(2 * (w_lo + k));
         return (size_t)(rec0 + k);
     };
@@ -1389,9 +1393,15 @@ paged_attn_merge_kernel(AttnParams p) {
         const float lk = lane < n ? l_at(lane) : 0.f;
         VT ov[32];
 #pragma unroll
-        for (int u = 0; u < 32; ++u) {
-            if (u < n) ov[u] = *reinterpret_cast<const VT*>(p.ws + (rec_of(u) * G + r) * D + PER * lane);
-            else ov[u] = VT{};
+        for (int u0 = 0; u0 < 32; u0 += 8) {
+            if (u0 < n) {                     // whole groups of 8 past the last record are skipped
+#pragma unroll
+                for (int u = u0; u < u0 + 8; ++u)
+                    ov[u] = *reinterpret_cast<const VT*>(p.ws + (rec_of(u) * G + r) * D + PER * lane);
+            } else {
+#pragma unroll
+                for (int u = u0; u < u0 + 8; ++u) ov[u] = VT{};
+            }
         }
         float M = mk;
 #pragma unroll
@@ -1513,8 +1523,11 @@ struct SideState {
     int rec0;            // first record (descriptor)
 };
 
+// Record k of a side (k past the last is read as the last one, so loads
+// issued ahead of their use stay inside this call's records).
 template <int D>
 __device__ __forceinline__ size_t side_rec(const SideState& x, int k) {
+    k = min(k, max(x.n - 1, 0));
     return k == 0 ? (size_t)x.rec0 : (size_t)(2 * ((x.rec0 >> 1) + k));
 }
 
@@ -1564,9 +1577,12 @@ shared_prefix_merge_kernel(AttnParams a, AttnParams b, float* __restrict__ out, 
     const int2 da = *reinterpret_cast<const int2*>(a.desc + 2 * seg_a);
     const int2 db = *reinterpret_cast<const int2*>(b.desc + 2 * seg_b);
     SideState x[2];
-    x[0] = SideState{a.out, a.lse, a.ws, (size_t)a.n_rec, a.cols, (mm - qg * a.qgs) * G + r,
-                     La > 0 ? max(da.y, 1) : 0, da.x};
-    x[1] = SideState{b.out, b.lse, b.ws, (size_t)b.n_rec, b.cols, r, Lb > 0 ? max(db.y, 1) : 0, db.x};
+    // a descriptor is this call's only where its side has tokens; otherwise
+    // its record index is not used (and is set to 0)
+    const int na = La > 0 ? max(da.y, 1) : 0, nb = Lb > 0 ? max(db.y, 1) : 0;
+    x[0] = SideState{a.out, a.lse, a.ws, (size_t)a.n_rec, a.cols, (mm - qg * a.qgs) * G + r, na,
+                     na > 1 ? da.x : 0};
+    x[1] = SideState{b.out, b.lse, b.ws, (size_t)b.n_rec, b.cols, r, nb, nb > 1 ? db.x : 0};
     constexpr int PER = D / 64;
     float num[PER] = {};
     float den = 0.f, Mx = -INFINITY;
