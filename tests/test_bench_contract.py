@@ -1,0 +1,33 @@
+"""The bench's contract on the CPU: one GPU only, and the recorded HBM traffic
+is reported only for the kernel source it was measured on."""
+
+import json
+import os
+import subprocess
+import sys
+
+import bench
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_is_refused_with_a_message():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode != 0
+    msg = json.loads(r.stdout.strip().splitlines()[-1])
+    assert "one GPU" in msg["error"] and msg["n_gpus_requested"] == 2
+
+
+def test_recorded_traffic_follows_the_kernel_source(monkeypatch, tmp_path):
+    import hashlib
+    got = bench.measured_traffic("llama8b", "bf16", 16, -1, "fused")
+    m = bench.MEASURED_TRAFFIC[("llama8b", "bf16", 16, -1, "fused")]
+    want = int(round(1024 * (m["fetch_kib"] * m["fetch_scale"] + m["write_kib"] * m["write_scale"])))
+    same = hashlib.sha256(open(bench.DEVICE_SOURCE, "rb").read()).hexdigest() == m["source_sha256"]
+    assert got == (want if same else None)
+    other = tmp_path / "device.hip"
+    other.write_bytes(open(bench.DEVICE_SOURCE, "rb").read() + b"\n")
+    monkeypatch.setattr(bench, "DEVICE_SOURCE", str(other))
+    assert bench.measured_traffic("llama8b", "bf16", 16, -1, "fused") is None    # any edit voids it
+    assert bench.measured_traffic("small", "bf16", 16, -1, "fused") is None       # never measured
