@@ -272,7 +272,9 @@ template <int D> struct Frag<KV_BF16, D> {
 };
 template <int D> struct Frag<KV_FP8, D> {
     uint4 k[D / 64];       // token r16, channels 64f + 16j4 .. +15
-    uint32_t v[D / 16];    // channel 16s + r16, tokens 4j4 .. +3
+    uint32_t v[D / 16];    // channel 16s + r16, tokens 4j4 .. +3 (for bs >= 16 as loaded:
+                           // v[4t + c] = tokens 4c .. +3 of channel 16(4t + j4) + r16, until
+                           // v_rows_to_operand)
 };
 
 template <int KV> struct QFragT;
@@ -351,9 +353,48 @@ __device__ __forceinline__ void load_chunk(Frag<KV, D>& f, const AttnParams& p, 
 #pragma unroll
         for (int x = 0; x < D / 64; ++x)
             f.k[x] = ld_kv<BS>(reinterpret_cast<const uint4*>(krow + 64 * x + 16 * j4));
+        if constexpr (BS >= 16) {
+            // whole 16-token rows, 16 bytes per lane: lane (r16, j4) reads the row
+            // of channel 16(4t + j4) + r16; v_rows_to_operand moves the tokens
+            // to the lanes the P.V MFMA wants
+            const E* vsub = vt - 4 * j4;
 #pragma unroll
-        for (int s = 0; s < D / 16; ++s)
-            f.v[s] = ld_kv<BS>(reinterpret_cast<const uint32_t*>(vt + (size_t)(16 * s + r16) * VS));
+            for (int t = 0; t < D / 64; ++t) {
+                const uint4 row = ld_kv<BS>(reinterpret_cast<const uint4*>(vsub + (size_t)(16 * (4 * t + j4) + r16) * 16));
+                f.v[4 * t + 0] = row.x;
+                f.v[4 * t + 1] = row.y;
+                f.v[4 * t + 2] = row.z;
+                f.v[4 * t + 3] = row.w;
+            }
+        } else {
+#pragma unroll
+            for (int s = 0; s < D / 16; ++s)
+                f.v[s] = ld_kv<BS>(reinterpret_cast<const uint32_t*>(vt + (size_t)(16 * s + r16) * VS));
+        }
+    }
+}
+
+// fp8 V at bs >= 16 arrives as whole rows: within each group of 4 dim blocks
+// 4t .. 4t+3, row q of lanes (lanes 16q .. 16q+15) holds block 4t + q's 16
+// tokens in v[4t .. 4t+3] (4 tokens per word), and the P.V operand wants
+// block 4t + q' in v[4t + q'], tokens 4q .. 4q+3 in row q: a 4 x 4 transpose
+// of (lane row, word), done with two rounds of row swaps.
+template <int KV, int D, int BS>
+__device__ __forceinline__ void v_rows_to_operand(Frag<KV, D>& f) {
+    if constexpr (KV == KV_FP8 && BS >= 16) {
+#pragma unroll
+        for (int t = 0; t < D / 64; ++t) {
+            // rows 0/1 and 2/3 exchange between words 0/1 and 2/3 ...
+            const auto a = __builtin_amdgcn_permlane16_swap(f.v[4 * t + 0], f.v[4 * t + 1], false, false);
+            const auto b = __builtin_amdgcn_permlane16_swap(f.v[4 * t + 2], f.v[4 * t + 3], false, false);
+            // ... then lane halves between words (0, 2) and (1, 3)
+            const auto c = __builtin_amdgcn_permlane32_swap(a[0], b[0], false, false);
+            const auto d = __builtin_amdgcn_permlane32_swap(a[1], b[1], false, false);
+            f.v[4 * t + 0] = c[0];
+            f.v[4 * t + 2] = c[1];
+            f.v[4 * t + 1] = d[0];
+            f.v[4 * t + 3] = d[1];
+        }
     }
 }
 
@@ -569,12 +610,14 @@ __device__ __forceinline__ void load_new_token(const AttnParams& p, size_t row, 
 
 // Put the new token (chunk row rr) into a loaded chunk fragment.
 template <int KV, int D>
-__device__ __forceinline__ void patch_new_token(Frag<KV, D>& f, const NewTok<KV, D>& nt, int rr,
-                                                int r16, int j4) {
+__device__ __forceinline__ void patch_new_k(Frag<KV, D>& f, const NewTok<KV, D>& nt, int rr, int r16) {
     if (r16 == rr) {
 #pragma unroll
         for (int x = 0; x < (int)(sizeof(nt.k) / sizeof(nt.k[0])); ++x) f.k[x] = nt.k[x];
     }
+}
+template <int KV, int D>
+__device__ __forceinline__ void patch_new_v(Frag<KV, D>& f, const NewTok<KV, D>& nt, int rr, int j4) {
     if (j4 == (rr >> 2)) {
         const int e = rr & 3;
 #pragma unroll
@@ -665,6 +708,7 @@ __device__ __forceinline__ void attend_item(const AttnParams& p, float* smem, co
 #pragma unroll
             for (int s = 0; s < D / 16; ++s) o[s] *= alpha;
         }
+        v_rows_to_operand<KV, D, BS>(f);
         chunk_pv<KV, D>(f, pr, o, tail, first_tok, t1);
     };
 
@@ -1212,8 +1256,9 @@ paged_attn_stream_kernel(AttnParams p) {
             const int tc = 16 * kc;
             // the write of position L - 1 runs concurrently: take its value
             // from the new token instead of the pool
+            const bool patch = STEP && kc == nch - 1 && (!SH || (sfx && p.k_new));
             if constexpr (STEP)
-                if (kc == nch - 1 && (!SH || (sfx && p.k_new))) patch_new_token<KV, D>(f, nt, L - 1 - tc, r16, j4);
+                if (patch) patch_new_k<KV, D>(f, nt, L - 1 - tc, r16);
             const bool tail = tc + 16 > L;        // tokens >= L hold no data
             // query j sees tokens < L - n_q + 1 + j (causal inside the window)
             const bool masked = MQ && p.causal ? tc + 16 > L - n_q + 1 : tail;
@@ -1242,6 +1287,11 @@ paged_attn_stream_kernel(AttnParams p) {
                 if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
 #pragma unroll
                     for (int s = 0; s < D / 16; ++s) o[t][s] *= alpha;
+                }
+                if (t == 0) {                     // V is first needed here
+                    v_rows_to_operand<KV, D, BS>(f);
+                    if constexpr (STEP)
+                        if (patch) patch_new_v<KV, D>(f, nt, L - 1 - tc, j4);
                 }
                 chunk_pv<KV, D>(f, pr, o[t], tail, first_tok, L);
             }
