@@ -1257,8 +1257,14 @@ paged_attn_stream_kernel(AttnParams p) {
             // the write of position L - 1 runs concurrently: take its value
             // from the new token instead of the pool
             const bool patch = STEP && kc == nch - 1 && (!SH || (sfx && p.k_new));
+            // fp8 V rows are moved to their lanes only before the P.V, so their
+            // patch waits until then; other caches patch K and V here
+            constexpr bool kVRows = KV == KV_FP8 && BS >= 16;
             if constexpr (STEP)
-                if (patch) patch_new_k<KV, D>(f, nt, L - 1 - tc, r16);
+                if (patch) {
+                    patch_new_k<KV, D>(f, nt, L - 1 - tc, r16);
+                    if constexpr (!kVRows) patch_new_v<KV, D>(f, nt, L - 1 - tc, j4);
+                }
             const bool tail = tc + 16 > L;        // tokens >= L hold no data
             // query j sees tokens < L - n_q + 1 + j (causal inside the window)
             const bool masked = MQ && p.causal ? tc + 16 > L - n_q + 1 : tail;
@@ -1288,11 +1294,12 @@ paged_attn_stream_kernel(AttnParams p) {
 #pragma unroll
                     for (int s = 0; s < D / 16; ++s) o[t][s] *= alpha;
                 }
-                if (t == 0) {                     // V is first needed here
-                    v_rows_to_operand<KV, D, BS>(f);
-                    if constexpr (STEP)
-                        if (patch) patch_new_v<KV, D>(f, nt, L - 1 - tc, j4);
-                }
+                if constexpr (kVRows)
+                    if (t == 0) {                 // V is first needed here
+                        v_rows_to_operand<KV, D, BS>(f);
+                        if constexpr (STEP)
+                            if (patch) patch_new_v<KV, D>(f, nt, L - 1 - tc, j4);
+                    }
                 chunk_pv<KV, D>(f, pr, o[t], tail, first_tok, L);
             }
 
