@@ -115,8 +115,12 @@ def test_e4m3_brute_force_nearest():
         assert gi == best[0]
 
 
-@pytest.mark.parametrize("code", [0x00, 0x80, 0x01, 0x7E, 0xFE, 0x38])
-def test_e4m3_scale_is_exact(code):
-    s = np.float32(0.0123)
-    v = oracle.attention.widen(np.array([code], dtype=np.uint8), "fp8", s)[0]
-    assert v == TABLE[code] * np.float64(s)
+def test_e4m3_scaled_widening_matches_torch():
+    # every finite code times a float32 scale: torch's float8_e4m3fn decode in
+    # float64 times the scale (exact: 4 significant bits times 24)
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).double().numpy()
+    for s in (np.float32(0.0123), np.float32(3.0), np.float32(448.0 / 7.3)):
+        got = oracle.attention.widen(codes, "fp8", s)
+        assert np.array_equal(got, ref * float(s))
+        assert np.array_equal(np.signbit(got), np.signbit(ref))
