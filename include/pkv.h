@@ -81,7 +81,9 @@ const char* pkv_version(void);
  * into the current block").
  *
  * For each t < T with 0 <= slot_mapping[t] < P*bs: (b, o) = divmod(slot, bs);
- *   k_cache[b][h][o][c] = cvt(k_new[t][h][c]),  v_cache[b][h][c][o] = cvt(v_new[t][h][c])
+ *   k_cache[b][h][o][c]                 = cvt(k_new[t][h][c])
+ *   v_cache[b][h][o / vs][c][o % vs]    = cvt(v_new[t][h][c])     (vs = min(bs, 16);
+ *                                         for bs <= 16 that is v_cache[b][h][c][o])
  * for all h < Hkv, c < d. Any other slot value (-1 by convention) skips the
  * token. Every other byte of the pools is left unchanged.
  *
@@ -392,12 +394,17 @@ typedef struct {
     double waste;             /* 1 - tokens_stored / slots_allocated (0 if none) */
 } pkv_stats;
 
-/* Create an allocator (P > 0, bs > 0). *out receives the handle. */
+/* Create an allocator over a pool of P blocks of bs tokens, all free, set up
+ * once for the whole cache ("03 · PagedAttention", "Blocks and block tables":
+ * the pool is carved into equal blocks up front). P > 0, bs > 0; *out (host)
+ * receives the handle, which the caller owns until pkv_allocator_destroy. */
 pkv_status pkv_allocator_create(int32_t P, int32_t bs, pkv_allocator** out);
-/* Destroy an allocator; NULL is ignored. */
+/* Destroy an allocator and every sequence in it; NULL is ignored. */
 void pkv_allocator_destroy(pkv_allocator* a);
 
-/* Register an empty sequence. PKV_E_STATE if the id exists. */
+/* Register an empty sequence: a block table with no entries, blocks taken on
+ * demand as tokens arrive ("03 · PagedAttention", "Blocks and block tables").
+ * PKV_E_STATE if the id exists. */
 pkv_status pkv_seq_create(pkv_allocator* a, int64_t seq_id);
 
 /*
@@ -424,12 +431,22 @@ pkv_status pkv_seq_append(pkv_allocator* a, int64_t seq_id, int32_t n_tokens,
                           int64_t* slots_out, int32_t* cow_src, int32_t* cow_dst,
                           int32_t* n_cow);
 
-/* child shares every block of parent (refcount + 1 each) and its length.
- * PKV_E_NOT_FOUND if parent is unknown, PKV_E_STATE if child exists. */
+/* Fork: child shares every block of parent (refcount + 1 each) and its
+ * length, so both tables list the same physical blocks until one of them
+ * writes into a shared, partly filled block and pkv_seq_append reports the
+ * copy-on-write pair ("03 · PagedAttention", "Sharing: copy-on-write";
+ * "PagedAttention" daily term, copy-on-write figure: beams and parallel
+ * samples start from one prompt's blocks).
+ * PKV_E_NOT_FOUND if parent is unknown, PKV_E_STATE if child exists; nothing
+ * changes on an error. */
 pkv_status pkv_seq_fork(pkv_allocator* a, int64_t parent, int64_t child);
 
-/* Release a sequence: refcount - 1 for each block, last logical block first;
- * a block whose count reaches 0 returns to the free list. */
+/* Release a finished sequence: refcount - 1 for each of its blocks, last
+ * logical block first; a block whose count reaches 0 goes back on the free
+ * list, where the next append can take it ("PagedAttention" daily term,
+ * "Pros": a plain free list of blocks; "03 · PagedAttention", "Sharing:
+ * copy-on-write": a shared block is freed only when no table lists it).
+ * PKV_E_NOT_FOUND for an unknown id; nothing changes then. */
 pkv_status pkv_seq_free(pkv_allocator* a, int64_t seq_id);
 
 /* Current context length and block count of a sequence. */
@@ -437,10 +454,15 @@ pkv_status pkv_seq_info(const pkv_allocator* a, int64_t seq_id, int64_t* length,
                         int32_t* num_blocks);
 
 /*
- * Block tables for the listed sequences: tables_out int32 [S][max_blocks]
- * (row i = sequence seq_ids[i]'s physical blocks, padded with -1) and
- * lens_out int32 [S] (their lengths). PKV_E_INVALID if a sequence holds more
- * than max_blocks blocks or is longer than INT32_MAX; PKV_E_NOT_FOUND for an
+ * Block tables for the listed sequences, the per-sequence map from logical
+ * block j (token positions j*bs .. j*bs + bs - 1) to the physical block that
+ * holds it ("03 · PagedAttention", "Blocks and block tables"; "Serving: vLLM
+ * and PagedAttention", section 2.2, the block table as a page table):
+ * tables_out int32 [S][max_blocks] (row i = sequence seq_ids[i]'s physical
+ * blocks in logical order, padded with -1) and lens_out int32 [S] (their
+ * lengths, the token being written this step included). Both are host
+ * arrays the caller owns. PKV_E_INVALID if a sequence holds more than
+ * max_blocks blocks or is longer than INT32_MAX; PKV_E_NOT_FOUND for an
  * unknown id. Outputs are written only on success.
  */
 pkv_status pkv_build_block_tables(const pkv_allocator* a, const int64_t* seq_ids,
@@ -448,10 +470,15 @@ pkv_status pkv_build_block_tables(const pkv_allocator* a, const int64_t* seq_ids
                                   int32_t* tables_out, int32_t* lens_out);
 
 /*
- * Slot of token position positions[i] of each sequence from its table row:
- * tables[i][p / bs] * bs + p % bs; a negative position gives -1. PKV_E_INVALID
- * if p / bs >= max_blocks or the entry is negative (nothing written then).
- * For a decode step the position is L_i - 1 (the token being written).
+ * Slot mapping: the flat slot of token position positions[i] (0-based) of each
+ * sequence from its table row, tables[i][p / bs] * bs + p % bs: logical block
+ * p / bs at offset p % bs ("03 · PagedAttention", "Blocks and block tables";
+ * "Serving: vLLM and PagedAttention", section 2.2, the last block filled
+ * from its start). A negative position gives -1 (pkv_kv_cache_write skips
+ * it). tables, positions and slots_out are host arrays the caller owns.
+ * PKV_E_INVALID if p / bs >= max_blocks or the entry is negative (nothing
+ * written then). For a decode step the position is L_i - 1, the token being
+ * written.
  */
 pkv_status pkv_slots_from_tables(const int32_t* tables, const int32_t* positions,
                                  int32_t S, int32_t max_blocks, int32_t bs,

@@ -9,6 +9,10 @@ import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("PKV_LIB", os.path.join(HERE, "libpkv.so"))
+# PKV_HOST_ONLY=1: PKV_LIB is the host part alone (the allocator, builders and
+# hashes, e.g. a sanitizer build of csrc/host.cpp); device entry points are
+# then absent and raise AttributeError when called
+HOST_ONLY = os.environ.get("PKV_HOST_ONLY") == "1"
 
 PKV_OK, PKV_E_INVALID, PKV_E_WORKSPACE, PKV_E_NO_BLOCKS, PKV_E_NOT_FOUND, PKV_E_STATE, PKV_E_HIP = range(7)
 STATUS_NAMES = {
@@ -94,6 +98,8 @@ def lib():
                 "`python -m paged_kv_cache_108_amd.build` (there is no fallback path)")
         handle = ctypes.CDLL(LIB_PATH)
         for name, (res, args) in SIGNATURES.items():
+            if HOST_ONLY and not hasattr(handle, name):
+                continue
             fn = getattr(handle, name)
             fn.restype = res
             fn.argtypes = args

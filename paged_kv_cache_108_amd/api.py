@@ -73,18 +73,49 @@ def v_shape_ok(v_cache, P, Hkv, d, bs):
     return bs <= 16 and shp == (P, Hkv, d, bs)
 
 
+def _pools(fn, k_cache, v_cache):
+    """(P, Hkv, bs, d) of a K pool [P][Hkv][bs][d] and the V pool that goes with
+    it: same dtype, same device, V in the layout v_shape_ok describes."""
+    if k_cache.dim() != 4:
+        raise ValueError(f"{fn}: k_cache must be [P][Hkv][bs][d]")
+    P, Hkv, bs, d = k_cache.shape
+    if v_cache.dtype != k_cache.dtype:
+        raise ValueError(f"{fn}: v_cache dtype {v_cache.dtype} differs from k_cache dtype {k_cache.dtype}")
+    if not v_shape_ok(v_cache, P, Hkv, d, bs):
+        raise ValueError(f"{fn}: v_cache shape {tuple(v_cache.shape)} does not match k_cache {tuple(k_cache.shape)}")
+    _dtype_code(k_cache)
+    return P, Hkv, bs, d
+
+
+def _src_dtype_ok(fn, name, t, k_cache):
+    """New K/V (and q) elements: float32 for a float32 cache, bfloat16 for a
+    bfloat16 or fp8 cache."""
+    import torch
+    want = torch.float32 if k_cache.dtype == torch.float32 else torch.bfloat16
+    if t.dtype != want:
+        raise ValueError(f"{fn}: {name} dtype {t.dtype} does not go with a {k_cache.dtype} cache (needs {want})")
+
+
+def _one_device(fn, *tensors):
+    devs = {t.device for t in tensors if t is not None}
+    if len(devs) > 1:
+        raise ValueError(f"{fn}: tensors on several devices {sorted(str(x) for x in devs)}")
+
+
 def kv_cache_write(k_new, v_new, k_cache, v_cache, slot_mapping, *, k_inv_scale=1.0,
                    v_inv_scale=1.0, stream=None):
     """pkv_kv_cache_write. k_new/v_new [T][Hkv][d]; k_cache [P][Hkv][bs][d];
     v_cache as v_shape_ok describes; slot_mapping int64 [T]."""
     import torch
-    T, Hkv, d = k_new.shape
-    P, _, bs, _ = k_cache.shape
-    if v_new.shape != k_new.shape or not v_shape_ok(v_cache, P, Hkv, d, bs) \
-            or tuple(k_cache.shape) != (P, Hkv, bs, d):
-        raise ValueError("kv_cache_write: shape mismatch")
+    P, Hkv, bs, d = _pools("kv_cache_write", k_cache, v_cache)
+    if k_new.dim() != 3 or tuple(k_new.shape[1:]) != (Hkv, d) or v_new.shape != k_new.shape:
+        raise ValueError("kv_cache_write: k_new and v_new must both be [T][Hkv][d]")
+    T = k_new.shape[0]
+    _src_dtype_ok("kv_cache_write", "k_new", k_new, k_cache)
+    _src_dtype_ok("kv_cache_write", "v_new", v_new, k_cache)
     if slot_mapping.dtype != torch.int64 or slot_mapping.shape != (T,):
         raise ValueError("kv_cache_write: slot_mapping must be int64 [T]")
+    _one_device("kv_cache_write", k_new, v_new, k_cache, v_cache, slot_mapping)
     check(lib().pkv_kv_cache_write(
         _dev(k_new, "k_new"), _dev(v_new, "v_new"), _dev(k_cache, "k_cache"),
         _dev(v_cache, "v_cache"), _dev(slot_mapping, "slot_mapping"), T, Hkv, d, bs, P,
@@ -97,11 +128,10 @@ def copy_blocks(k_cache, v_cache, src, dst, *, stream=None):
     src[k]. src, dst: int32 device tensors [n]; the dst ids must be distinct
     and none of them a src of the same call."""
     import torch
-    P, Hkv, bs, d = k_cache.shape
-    if not v_shape_ok(v_cache, P, Hkv, d, bs) or v_cache.dtype != k_cache.dtype:
-        raise ValueError("copy_blocks: pools disagree")
+    P, Hkv, bs, d = _pools("copy_blocks", k_cache, v_cache)
     if src.dtype != torch.int32 or dst.dtype != torch.int32 or src.shape != dst.shape or src.dim() != 1:
         raise ValueError("copy_blocks: src and dst must be int32 [n]")
+    _one_device("copy_blocks", k_cache, v_cache, src, dst)
     n = src.shape[0]
     if n == 0:
         return
@@ -123,6 +153,25 @@ def paged_decode_attn_workspace(S, Hq, Hkv, d, max_context_len, partition_size, 
     return torch.empty(need, dtype=torch.uint8, device=device) if need else None
 
 
+def _attn_args(fn, out, q, k_cache, block_tables, context_lens, d, n_q=None):
+    """Check q ([S][Hq][d], or [S][n_q][Hq][d] when n_q is given), the float32
+    output of the same shape, int32 tables [S][max_blocks] and lengths [S];
+    returns (S, Hq)."""
+    import torch
+    want_dim = 3 if n_q is None else 4
+    if q.dim() != want_dim or q.shape[-1] != d:
+        raise ValueError(f"{fn}: q must be {'[S][Hq][d]' if n_q is None else '[S][n_q][Hq][d]'} with d={d}")
+    S, Hq = q.shape[0], q.shape[-2]
+    if tuple(out.shape) != tuple(q.shape) or out.dtype != torch.float32:
+        raise ValueError(f"{fn}: out must be float32 of q's shape {tuple(q.shape)}")
+    _src_dtype_ok(fn, "q", q, k_cache)
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise ValueError(f"{fn}: tables and lengths must be int32")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or tuple(context_lens.shape) != (S,):
+        raise ValueError(f"{fn}: tables/lengths shape mismatch")
+    return S, Hq
+
+
 def paged_decode_attn(out, q, k_cache, v_cache, block_tables, context_lens, *, max_context_len,
                       softmax_scale, k_scale=1.0, v_scale=1.0, partition_size=PKV_PARTITION_BALANCED,
                       workspace=None, stream=None):
@@ -134,15 +183,9 @@ def paged_decode_attn(out, q, k_cache, v_cache, block_tables, context_lens, *, m
     partition_size PKV_PARTITION_BALANCED (default: equal cost-weighted chunk
     ranges, one per wave), 0 (one pass per sequence and kv head) or a multiple
     of 32 (fixed partitions of that many tokens)."""
-    import torch
-    S, Hq, d = q.shape
-    P, Hkv, bs, _ = k_cache.shape
-    if tuple(out.shape) != (S, Hq, d) or out.dtype != torch.float32:
-        raise ValueError("paged_decode_attn: out must be float32 [S][Hq][d]")
-    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
-        raise ValueError("paged_decode_attn: tables and lengths must be int32")
-    if block_tables.shape[0] != S or context_lens.shape != (S,):
-        raise ValueError("paged_decode_attn: tables/lengths shape mismatch")
+    P, Hkv, bs, d = _pools("paged_decode_attn", k_cache, v_cache)
+    S, Hq = _attn_args("paged_decode_attn", out, q, k_cache, block_tables, context_lens, d)
+    _one_device("paged_decode_attn", out, q, k_cache, v_cache, block_tables, context_lens, workspace)
     if workspace is None:                     # convenience: a fresh zeroed one for this call
         workspace = paged_decode_attn_workspace(S, Hq, Hkv, d, int(max_context_len),
                                                 int(partition_size), device=q.device)
@@ -163,19 +206,14 @@ def paged_decode_step(out, q, k_new, v_new, k_cache, v_cache, block_tables, cont
     """pkv_paged_decode_step: write each sequence's new token (k_new, v_new
     [S][Hkv][d]) at position L_i - 1 and attend, in one launch. Same result as
     kv_cache_write followed by paged_decode_attn with the balanced split."""
-    import torch
-    S, Hq, d = q.shape
-    P, Hkv, bs, _ = k_cache.shape
-    if tuple(out.shape) != (S, Hq, d) or out.dtype != torch.float32:
-        raise ValueError("paged_decode_step: out must be float32 [S][Hq][d]")
+    P, Hkv, bs, d = _pools("paged_decode_step", k_cache, v_cache)
+    S, Hq = _attn_args("paged_decode_step", out, q, k_cache, block_tables, context_lens, d)
     if tuple(k_new.shape) != (S, Hkv, d) or tuple(v_new.shape) != (S, Hkv, d):
         raise ValueError("paged_decode_step: k_new/v_new must be [S][Hkv][d]")
-    if not v_shape_ok(v_cache, P, Hkv, d, bs):
-        raise ValueError("paged_decode_step: v_cache shape")
-    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
-        raise ValueError("paged_decode_step: tables and lengths must be int32")
-    if block_tables.shape[0] != S or context_lens.shape != (S,):
-        raise ValueError("paged_decode_step: tables/lengths shape mismatch")
+    _src_dtype_ok("paged_decode_step", "k_new", k_new, k_cache)
+    _src_dtype_ok("paged_decode_step", "v_new", v_new, k_cache)
+    _one_device("paged_decode_step", out, q, k_new, v_new, k_cache, v_cache, block_tables, context_lens,
+                workspace)
     if workspace is None:
         workspace = paged_decode_attn_workspace(S, Hq, Hkv, d, int(max_context_len),
                                                 PKV_PARTITION_BALANCED, device=q.device)
@@ -203,15 +241,10 @@ def paged_multi_query_attn(out, q, k_cache, v_cache, block_tables, context_lens,
     query j of sequence i sits at position L_i - n_q + j and sees the tokens up to
     it (causal inside the window). workspace as from paged_multi_query_attn_workspace
     (None allocates one for this call)."""
-    import torch
-    S, n_q, Hq, d = q.shape
-    P, Hkv, bs, _ = k_cache.shape
-    if tuple(out.shape) != (S, n_q, Hq, d) or out.dtype != torch.float32:
-        raise ValueError("paged_multi_query_attn: out must be float32 [S][n_q][Hq][d]")
-    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
-        raise ValueError("paged_multi_query_attn: tables and lengths must be int32")
-    if block_tables.shape[0] != S or context_lens.shape != (S,):
-        raise ValueError("paged_multi_query_attn: tables/lengths shape mismatch")
+    P, Hkv, bs, d = _pools("paged_multi_query_attn", k_cache, v_cache)
+    S, Hq = _attn_args("paged_multi_query_attn", out, q, k_cache, block_tables, context_lens, d, n_q=True)
+    n_q = q.shape[1]
+    _one_device("paged_multi_query_attn", out, q, k_cache, v_cache, block_tables, context_lens, workspace)
     if workspace is None:
         workspace = paged_multi_query_attn_workspace(S, n_q, Hq, Hkv, d, device=q.device)
     check(lib().pkv_paged_multi_query_attn(
@@ -228,18 +261,11 @@ def paged_decode_attn_lse(out, lse, q, k_cache, v_cache, block_tables, context_l
     """pkv_paged_decode_attn_lse: balanced decode attention that also writes
     lse float32 [S][Hq], the base-2 log of each row's softmax sum."""
     import torch
-    S, Hq, d = q.shape
-    P, Hkv, bs, _ = k_cache.shape
-    if tuple(out.shape) != (S, Hq, d) or out.dtype != torch.float32:
-        raise ValueError("paged_decode_attn_lse: out must be float32 [S][Hq][d]")
+    P, Hkv, bs, d = _pools("paged_decode_attn_lse", k_cache, v_cache)
+    S, Hq = _attn_args("paged_decode_attn_lse", out, q, k_cache, block_tables, context_lens, d)
     if tuple(lse.shape) != (S, Hq) or lse.dtype != torch.float32:
         raise ValueError("paged_decode_attn_lse: lse must be float32 [S][Hq]")
-    if not v_shape_ok(v_cache, P, Hkv, d, bs):
-        raise ValueError("paged_decode_attn_lse: v_cache shape")
-    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
-        raise ValueError("paged_decode_attn_lse: tables and lengths must be int32")
-    if block_tables.shape[0] != S or context_lens.shape != (S,):
-        raise ValueError("paged_decode_attn_lse: tables/lengths shape mismatch")
+    _one_device("paged_decode_attn_lse", out, lse, q, k_cache, v_cache, block_tables, context_lens, workspace)
     if workspace is None:
         workspace = paged_decode_attn_workspace(S, Hq, Hkv, d, int(max_context_len),
                                                 PKV_PARTITION_BALANCED, device=q.device)
@@ -258,18 +284,14 @@ def paged_shared_prefix_attn(out, lse, q, k_cache, v_cache, prefix_tables, prefi
     group attends to all of the group's prefix tokens. out float32
     [n_groups][M][Hq][d], lse float32 [n_groups][M][Hq]."""
     import torch
-    n_groups, M, Hq, d = q.shape
-    P, Hkv, bs, _ = k_cache.shape
-    if tuple(out.shape) != (n_groups, M, Hq, d) or out.dtype != torch.float32:
-        raise ValueError("paged_shared_prefix_attn: out must be float32 [n_groups][M][Hq][d]")
+    P, Hkv, bs, d = _pools("paged_shared_prefix_attn", k_cache, v_cache)
+    n_groups, Hq = _attn_args("paged_shared_prefix_attn", out, q, k_cache, prefix_tables, prefix_lens, d,
+                              n_q=True)
+    M = q.shape[1]
     if tuple(lse.shape) != (n_groups, M, Hq) or lse.dtype != torch.float32:
         raise ValueError("paged_shared_prefix_attn: lse must be float32 [n_groups][M][Hq]")
-    if not v_shape_ok(v_cache, P, Hkv, d, bs):
-        raise ValueError("paged_shared_prefix_attn: v_cache shape")
-    if prefix_tables.dtype != torch.int32 or prefix_lens.dtype != torch.int32:
-        raise ValueError("paged_shared_prefix_attn: tables and lengths must be int32")
-    if prefix_tables.shape[0] != n_groups or prefix_lens.shape != (n_groups,):
-        raise ValueError("paged_shared_prefix_attn: tables/lengths shape mismatch")
+    _one_device("paged_shared_prefix_attn", out, lse, q, k_cache, v_cache, prefix_tables, prefix_lens,
+                workspace)
     if workspace is None:
         workspace = paged_multi_query_attn_workspace(n_groups, M, Hq, Hkv, d, device=q.device)
     check(lib().pkv_paged_shared_prefix_attn(
@@ -335,16 +357,12 @@ def paged_shared_prefix_decode(out, q, k_cache, v_cache, prefix_tables, prefix_l
     the step's write) for groups of group_size sequences over their group's
     prefix blocks followed by their own suffix blocks. out float32 [S][Hq][d]."""
     import torch
-    S, Hq, d = q.shape
-    P, Hkv, bs, _ = k_cache.shape
+    P, Hkv, bs, d = _pools("paged_shared_prefix_decode", k_cache, v_cache)
+    S, Hq = _attn_args("paged_shared_prefix_decode", out, q, k_cache, suffix_tables, suffix_lens, d)
     M = int(group_size)
     if M < 1 or S % M:
         raise ValueError("paged_shared_prefix_decode: S must be a multiple of group_size")
     n_groups = S // M
-    if tuple(out.shape) != (S, Hq, d) or out.dtype != torch.float32:
-        raise ValueError("paged_shared_prefix_decode: out must be float32 [S][Hq][d]")
-    if not v_shape_ok(v_cache, P, Hkv, d, bs):
-        raise ValueError("paged_shared_prefix_decode: v_cache shape")
     for t, name in ((prefix_tables, "prefix_tables"), (prefix_lens, "prefix_lens"),
                     (suffix_tables, "suffix_tables"), (suffix_lens, "suffix_lens")):
         if t.dtype != torch.int32:
@@ -359,6 +377,9 @@ def paged_shared_prefix_decode(out, q, k_cache, v_cache, prefix_tables, prefix_l
         for t, name in ((k_new, "k_new"), (v_new, "v_new")):
             if tuple(t.shape) != (S, Hkv, d):
                 raise ValueError(f"paged_shared_prefix_decode: {name} must be [S][Hkv][d]")
+            _src_dtype_ok("paged_shared_prefix_decode", name, t, k_cache)
+    _one_device("paged_shared_prefix_decode", out, q, k_new, v_new, k_cache, v_cache, prefix_tables, prefix_lens,
+                suffix_tables, suffix_lens, workspace)
     if workspace is None:
         workspace = paged_shared_prefix_decode_workspace(n_groups, M, Hq, Hkv, d, device=q.device)
     check(lib().pkv_paged_shared_prefix_decode(

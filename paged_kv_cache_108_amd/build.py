@@ -55,5 +55,33 @@ def build(verbose=False, out=LIB, extra_hip_flags=()):
     return out
 
 
+# The host part alone (allocator, table and slot builders, hashes), built with
+# AddressSanitizer and UndefinedBehaviorSanitizer for CPU test runs. It is
+# loaded with PKV_LIB pointing at it, PKV_HOST_ONLY=1 and the sanitizer
+# runtimes preloaded (see tests/test_host_sanitizers.py). No device code is in it.
+SAN_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",
+             "-fno-omit-frame-pointer", "-g", "-O1"]
+
+
+def build_host_sanitized(out, verbose=False):
+    cxx = os.environ.get("CXX", shutil.which("g++") or "g++")
+    _run([cxx, *SAN_FLAGS, "-std=c++17", "-fPIC", "-shared", "-Wall", "-Wextra", "-I", INCLUDE,
+          os.path.join(CSRC, "host.cpp"), "-o", out], verbose)
+    return out
+
+
+def sanitizer_runtimes():
+    """Paths of the compiler's ASan and UBSan runtimes, to preload."""
+    cxx = os.environ.get("CXX", shutil.which("g++") or "g++")
+    paths = []
+    for name in ("libasan.so", "libubsan.so"):
+        r = subprocess.run([cxx, f"-print-file-name={name}"], stdout=subprocess.PIPE, text=True)
+        paths.append(r.stdout.strip())
+    return paths
+
+
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    if "--host-sanitized" in sys.argv:
+        print(build_host_sanitized(os.path.join(HERE, "libpkv_host_san.so"), verbose="-v" in sys.argv))
+    else:
+        print(build(verbose="-v" in sys.argv))

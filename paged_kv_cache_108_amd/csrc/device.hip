@@ -1058,7 +1058,11 @@ paged_attn_stream_kernel(AttnParams p) {
             const int L = seq_len(sq);
             if (L <= 0) continue;
             const int pos = L - 1;
-            const int b = min(max(table_row(sq)[pos / BS], 0), p.P - 1);
+            // an entry outside the pool (e.g. -1: no block appended) is
+            // skipped, as the separate write skips a slot outside the pool
+            const int raw = table_row(sq)[pos / BS];
+            const bool in_pool = raw >= 0 && raw < p.P;
+            const int b = min(max(raw, 0), p.P - 1);
             const int o = pos % BS;
             const size_t src_row = ((size_t)i * p.Hkv + g) * D;
             uint32_t val[NCH];
@@ -1071,6 +1075,7 @@ paged_attn_stream_kernel(AttnParams p) {
                     val[u] = static_cast<const uint16_t*>(is_v ? p.v_new : p.k_new)[src_row + c];
             }
             if (q0 == (int)w) between();
+            if (!in_pool) continue;
 #pragma unroll
             for (int u = 0; u < NCH; ++u) {
                 const int c = lane + 64 * u;

@@ -263,15 +263,24 @@ def _poison(pool_k, pool_v, valid, dtype):
         pool_v[b_idx, :, o_idx // 16, :, o_idx % 16] = nan
 
 
-def generate(s, tables, lens, P, *, extra=None, poison_new=True):
-    """Draw q, pools and new tokens for a spec with given tables and lengths."""
+def generate(s, tables, lens, P, *, extra=None, poison_new=True, value_scales=(1.0, 1.0)):
+    """Draw q, pools and new tokens for a spec with given tables and lengths.
+    K values (pool and new tokens) are N(0, 1) times value_scales[0], V values
+    times value_scales[1]."""
     cfg, S, Hq, Hkv, d, bs = s.cfg, s.S, s.Hq, s.Hkv, s.d, s.bs
     assert tables.shape[0] == S and len(lens) == S
+    ks, vs = (np.float32(x) for x in value_scales)
     q32 = _rng(cfg, 2).standard_normal((S, Hq, d), dtype=np.float32)
     k32 = _rng(cfg, 3).standard_normal((P, Hkv, bs, d), dtype=np.float32)
     v32 = _rng(cfg, 4).standard_normal(v_pool_shape(P, Hkv, d, bs), dtype=np.float32)
     kn32 = _rng(cfg, 5).standard_normal((S, Hkv, d), dtype=np.float32)
     vn32 = _rng(cfg, 6).standard_normal((S, Hkv, d), dtype=np.float32)
+    if ks != 1.0:
+        k32 *= ks
+        kn32 *= ks
+    if vs != 1.0:
+        v32 *= vs
+        vn32 *= vs
     pool_dtype = F32 if s.cache_dtype == F32 else BF16
     k_pool = _store(k32, pool_dtype)
     del k32
@@ -356,8 +365,9 @@ def make(name, *, bs=None, cache_dtype=None, poison_new=True):
 
 
 def make_custom(*, lens, Hq, Hkv, d, bs, q_dtype=BF16, cache_dtype=BF16, cfg=900,
-                pool_factor=1.5, partition_size=512, poison_new=True):
-    """A small ad-hoc workload (edge cases): ``lens`` may hold zeros; ids permuted."""
+                pool_factor=1.5, partition_size=512, poison_new=True, value_scales=(1.0, 1.0)):
+    """A small ad-hoc workload (edge cases): ``lens`` may hold zeros; ids permuted.
+    value_scales multiplies the K and the V values (see ``generate``)."""
     dtype_src = F32 if cache_dtype == F32 else BF16
     s = Spec("custom", cfg, len(lens), Hq, Hkv, d, bs, q_dtype, cache_dtype, dtype_src,
              partition_size)
@@ -366,4 +376,4 @@ def make_custom(*, lens, Hq, Hkv, d, bs, q_dtype=BF16, cache_dtype=BF16, cfg=900
     P = max(int(math.ceil(pool_factor * used)), 1)
     perm = _rng(cfg, 1).permutation(P)
     tables = _tables_from_permutation(np.maximum(lens, 0), bs, P, perm)
-    return generate(s, tables, lens, P, poison_new=poison_new)
+    return generate(s, tables, lens, P, poison_new=poison_new, value_scales=value_scales)
