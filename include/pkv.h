@@ -210,6 +210,39 @@ pkv_status pkv_paged_decode_step(float* out, const void* q, const void* k_new, c
                                  void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * pkv_paged_decode_step for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same step, the same kernels and the same result as
+ * pkv_paged_decode_step, with no workspace argument. The balanced split's
+ * partial records and segment descriptors go to a file-scope device array of
+ * PKV_STEP_SCRATCH_BYTES (16 MiB) that every GPU the library runs on holds
+ * from the library's load until the process ends; the call allocates nothing.
+ *
+ * A call needs R + 2 * S * Hkv * 4 bytes of it, R = 2 * W * (Hq/Hkv) * (d + 2) * 4
+ * rounded up to a multiple of 256, with W = 4 waves per compute unit (1024 on
+ * MI355X): Hq/Hkv up to 8 at d 128 and 16 at d 64 fit, for up to hundreds of
+ * thousands of (sequence, kv head) pairs. A call that needs more returns
+ * PKV_E_WORKSPACE (nothing launched); pkv_paged_decode_step takes any size.
+ *
+ * Every call on one GPU uses that GPU's one array, and the array keeps what
+ * the last call left in it (nothing in it needs clearing: each call writes
+ * every record and descriptor it reads). Calls whose execution overlaps on one
+ * GPU (different streams, no ordering between them) race on the array and
+ * may return wrong results: serialise them. Arguments and result otherwise
+ * exactly as for pkv_paged_decode_step.
+ */
+#define PKV_STEP_SCRATCH_BYTES (16u << 20)
+size_t pkv_paged_decode_step_scratch_bytes(void);
+pkv_status pkv_paged_decode_step_noalloc(float* out, const void* q, const void* k_new, const void* v_new,
+                                         void* k_cache, void* v_cache,
+                                         const int32_t* block_tables, const int32_t* context_lens,
+                                         int32_t S, int32_t Hq, int32_t Hkv, int32_t d, int32_t bs,
+                                         int32_t P, int32_t max_blocks, int32_t max_context_len,
+                                         float softmax_scale, float k_scale, float v_scale,
+                                         float k_inv_scale, float v_inv_scale,
+                                         pkv_dtype q_dtype, pkv_dtype cache_dtype, void* stream);
+
+/*
  * Bytes of workspace pkv_paged_multi_query_attn needs: R + 2 * S * Hkv * n_qg * 4
  * with G = Hq/Hkv, T = 1 column tile when n_q * G <= 16 and otherwise T = 2,
  * qgs = min(n_q, max(1, 16 * T / G)) queries per

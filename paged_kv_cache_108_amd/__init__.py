@@ -5,7 +5,8 @@ host allocator, C ABI in ``include/pkv.h``); this package only passes
 arguments to it. ``workloads`` draws the seeded synthetic inputs.
 """
 
-from .api import (kv_cache_write, copy_blocks, paged_decode_attn, paged_decode_step, paged_decode_attn_workspace_size,
+from .api import (kv_cache_write, copy_blocks, paged_decode_attn, paged_decode_step, paged_decode_step_noalloc,
+                  paged_decode_attn_workspace_size,
                   paged_decode_attn_workspace, paged_multi_query_attn,
                   paged_multi_query_attn_workspace, Allocator,
                   slots_from_tables, waste_stats, block_hashes, last_error, version, quantise_pool, PkvError,
@@ -15,7 +16,7 @@ from .api import (kv_cache_write, copy_blocks, paged_decode_attn, paged_decode_s
 from ._lib import lib, LIB_PATH, SIGNATURES, PKV_F32, PKV_BF16, PKV_FP8_E4M3
 
 __all__ = [
-    "kv_cache_write", "copy_blocks", "paged_decode_attn", "paged_decode_step",
+    "kv_cache_write", "copy_blocks", "paged_decode_attn", "paged_decode_step", "paged_decode_step_noalloc",
     "paged_decode_attn_workspace_size",
     "paged_decode_attn_workspace", "paged_multi_query_attn", "paged_multi_query_attn_workspace",
     "Allocator",

@@ -15,7 +15,7 @@ from ._lib import (lib, check, PkvError, PkvStats, PKV_F32, PKV_BF16, PKV_FP8_E4
                    PKV_E_NO_BLOCKS, P_i32, P_i64, P_f64, c_vp, c_i64, c_i32, c_f64)
 
 __all__ = [
-    "kv_cache_write", "copy_blocks", "paged_decode_attn", "paged_decode_step",
+    "kv_cache_write", "copy_blocks", "paged_decode_attn", "paged_decode_step", "paged_decode_step_noalloc",
     "paged_decode_attn_workspace_size",
     "paged_decode_attn_workspace", "paged_multi_query_attn", "paged_multi_query_attn_workspace",
     "Allocator",
@@ -224,6 +224,29 @@ def paged_decode_step(out, q, k_new, v_new, k_cache, v_cache, block_tables, cont
         int(max_context_len), float(softmax_scale), float(k_scale), float(v_scale),
         float(k_inv_scale), float(v_inv_scale), _dtype_code(q), _dtype_code(k_cache),
         _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def paged_decode_step_noalloc(out, q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, *,
+                              max_context_len, softmax_scale, k_scale=1.0, v_scale=1.0, k_inv_scale=1.0,
+                              v_inv_scale=1.0, stream=None):
+    """pkv_paged_decode_step_noalloc: paged_decode_step with no workspace; its
+    records live in the library's per-GPU scratch array (calls on one GPU must
+    not overlap). Raises PkvError (PKV_E_WORKSPACE) for a call that needs more
+    than pkv_paged_decode_step_scratch_bytes()."""
+    P, Hkv, bs, d = _pools("paged_decode_step_noalloc", k_cache, v_cache)
+    S, Hq = _attn_args("paged_decode_step_noalloc", out, q, k_cache, block_tables, context_lens, d)
+    if tuple(k_new.shape) != (S, Hkv, d) or tuple(v_new.shape) != (S, Hkv, d):
+        raise ValueError("paged_decode_step_noalloc: k_new/v_new must be [S][Hkv][d]")
+    _src_dtype_ok("paged_decode_step_noalloc", "k_new", k_new, k_cache)
+    _src_dtype_ok("paged_decode_step_noalloc", "v_new", v_new, k_cache)
+    _one_device("paged_decode_step_noalloc", out, q, k_new, v_new, k_cache, v_cache, block_tables,
+                context_lens)
+    check(lib().pkv_paged_decode_step_noalloc(
+        _dev(out, "out"), _dev(q, "q"), _dev(k_new, "k_new"), _dev(v_new, "v_new"),
+        _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dev(block_tables, "block_tables"),
+        _dev(context_lens, "context_lens"), S, Hq, Hkv, d, bs, P, block_tables.shape[1],
+        int(max_context_len), float(softmax_scale), float(k_scale), float(v_scale),
+        float(k_inv_scale), float(v_inv_scale), _dtype_code(q), _dtype_code(k_cache), _stream(stream)))
 
 
 def paged_multi_query_attn_workspace(S, n_q, Hq, Hkv, d, device="cuda"):

@@ -1788,6 +1788,12 @@ size_t balanced_records_bytes(size_t G, int d) {
     return (b + 255) / 256 * 256;
 }
 
+// Records of a balanced call with n_workers waves (256-byte multiple).
+size_t grid_records_bytes(int n_workers, size_t G, int d) {
+    const size_t b = 2 * (size_t)n_workers * G * (size_t)(d + 2) * sizeof(float);
+    return (b + 255) / 256 * 256;
+}
+
 int64_t n_partitions(int32_t max_len, int32_t partition_size) {
     if (partition_size <= 0 || max_len <= 0) return 1;
     return ((int64_t)max_len + partition_size - 1) / partition_size;
@@ -1909,7 +1915,7 @@ pkv_status attn_launch(const char* fn, float* out, const void* q, const void* k_
                        int32_t partition_size, void* workspace, size_t workspace_bytes, void* stream,
                        const StepWrite& step = StepWrite(), float* lse = nullptr,
                        bool causal = true, bool run_merge = true, AttnParams* used = nullptr,
-                       bool validate_only = false) {
+                       bool validate_only = false, bool grid_sized_workspace = false) {
     const bool is_step = step.k_new != nullptr || step.v_new != nullptr;
     if (S < 0 || Hq <= 0 || Hkv <= 0) return fail(PKV_E_INVALID, "%s: S=%d Hq=%d Hkv=%d", fn, S, Hq, Hkv);
     if (n_q < 1 || n_q > 4096) return fail(PKV_E_INVALID, "%s: n_q=%d outside [1, 4096]", fn, n_q);
@@ -1943,7 +1949,10 @@ pkv_status attn_launch(const char* fn, float* out, const void* q, const void* k_
         return fail(PKV_E_INVALID, "%s: NULL pointer", fn);
     const QueryGroups qgr = query_groups(n_q, G, d);
     const int64_t n_part = balanced ? 1 : n_partitions(max_context_len, partition_size);
-    const size_t need = attn_workspace_size(S, n_q, Hq, Hkv, d, max_context_len, partition_size);
+    // grid_sized_workspace (balanced only): the records are sized to this
+    // call's grid, not to the largest one, and checked once the grid is known
+    const size_t need = grid_sized_workspace ? 0
+                      : attn_workspace_size(S, n_q, Hq, Hkv, d, max_context_len, partition_size);
     if (need > 0 && (!workspace || workspace_bytes < need))
         return fail(PKV_E_WORKSPACE, "%s: workspace %zu bytes, need %zu", fn, workspace_bytes, need);
     // upper bound on work items (fixed partitions) or positions (balanced)
@@ -2020,6 +2029,15 @@ pkv_status attn_launch(const char* fn, float* out, const void* q, const void* k_
     if (grid < 1) grid = 1;
     prm.n_workers = (int)(balanced ? grid * kWaves : grid);
     prm.n_rec = balanced ? 2 * prm.n_workers : (int)(n_part * (int64_t)S * Hkv);
+    if (balanced && grid_sized_workspace) {
+        const size_t rec = grid_records_bytes(prm.n_workers, (size_t)qgr.cols, d);
+        const size_t need_g = rec + 2 * (size_t)S * (size_t)Hkv * (size_t)qgr.n_qg * sizeof(int);
+        if (!workspace || workspace_bytes < need_g)
+            return fail(PKV_E_WORKSPACE, "%s: this call needs %zu bytes of workspace (%d waves, %d columns, "
+                        "d %d, %d sequences x %d kv heads); %zu are available", fn, need_g, prm.n_workers,
+                        qgr.cols, d, S, Hkv, workspace_bytes);
+        prm.desc = reinterpret_cast<int*>(static_cast<char*>(workspace) + rec);
+    }
     if (used) *used = prm;
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kThreads), lds, st, prm);
     hipError_t e = hipGetLastError();
@@ -2096,6 +2114,76 @@ extern "C" pkv_status pkv_paged_decode_step(float* out, const void* q, const voi
     return attn_launch("paged_decode_step", out, q, k_cache, v_cache, block_tables, context_lens, S, 1,
                        Hq, Hkv, d, bs, P, max_blocks, max_context_len, softmax_scale, k_scale, v_scale,
                        q_dtype, cache_dtype, PKV_PARTITION_BALANCED, workspace, workspace_bytes, stream, w);
+}
+
+// ----------------------------------------------------------------------------
+// Decode step without any allocation: the records and descriptors of the
+// balanced split live in a file-scope device array instead of a caller
+// workspace. Each device that runs it holds its own copy of the array for the
+// life of the process; its address on a device is looked up once, with that
+// device current, and kept.
+// ----------------------------------------------------------------------------
+
+namespace {
+
+constexpr size_t kScratchBytes = (size_t)PKV_STEP_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+// Address of this device's copy of `scratch` (nullptr and *err set on failure).
+void* scratch_on_current_device(hipError_t* err) {
+    static void* addr[64] = {};
+    static std::mutex mu;
+    int dev = 0;
+    *err = hipGetDevice(&dev);
+    if (*err != hipSuccess) return nullptr;
+    if (dev < 0 || dev >= 64) {
+        *err = hipErrorInvalidDevice;
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void* ptr = nullptr;
+        *err = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (*err != hipSuccess) return nullptr;
+        addr[dev] = ptr;
+    }
+    return addr[dev];
+}
+
+}  // namespace
+
+extern "C" size_t pkv_paged_decode_step_scratch_bytes(void) { return kScratchBytes; }
+
+extern "C" pkv_status pkv_paged_decode_step_noalloc(float* out, const void* q, const void* k_new,
+                                                    const void* v_new, void* k_cache, void* v_cache,
+                                                    const int32_t* block_tables,
+                                                    const int32_t* context_lens, int32_t S, int32_t Hq,
+                                                    int32_t Hkv, int32_t d, int32_t bs, int32_t P,
+                                                    int32_t max_blocks, int32_t max_context_len,
+                                                    float softmax_scale, float k_scale, float v_scale,
+                                                    float k_inv_scale, float v_inv_scale,
+                                                    pkv_dtype q_dtype, pkv_dtype cache_dtype,
+                                                    void* stream) {
+    const char* fn = "paged_decode_step_noalloc";
+    StepWrite w;
+    w.k_new = k_new;
+    w.v_new = v_new;
+    w.k_inv = cache_dtype == PKV_FP8_E4M3 ? k_inv_scale : 1.f;
+    w.v_inv = cache_dtype == PKV_FP8_E4M3 ? v_inv_scale : 1.f;
+    if (S > 0 && (!k_new || !v_new)) return fail(PKV_E_INVALID, "%s: NULL pointer", fn);
+    // every argument check first (no HIP call), then the scratch address
+    pkv_status rc = attn_launch(fn, out, q, k_cache, v_cache, block_tables, context_lens, S, 1, Hq, Hkv, d,
+                                bs, P, max_blocks, max_context_len, softmax_scale, k_scale, v_scale, q_dtype,
+                                cache_dtype, PKV_PARTITION_BALANCED, nullptr, 0, stream, w, nullptr, true,
+                                true, nullptr, true, true);
+    if (rc != PKV_OK || S == 0) return rc;
+    hipError_t e = hipSuccess;
+    void* ws = scratch_on_current_device(&e);
+    if (!ws) return fail(PKV_E_HIP, "%s: scratch address lookup failed: %s", fn, hipGetErrorString(e));
+    return attn_launch(fn, out, q, k_cache, v_cache, block_tables, context_lens, S, 1, Hq, Hkv, d, bs, P,
+                       max_blocks, max_context_len, softmax_scale, k_scale, v_scale, q_dtype, cache_dtype,
+                       PKV_PARTITION_BALANCED, ws, kScratchBytes, stream, w, nullptr, true, true, nullptr,
+                       false, true);
 }
 
 extern "C" pkv_status pkv_paged_decode_attn_lse(float* out, float* lse, const void* q,
