@@ -35,8 +35,19 @@ HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published peak
 
 ELEM = {"f32": 4, "bf16": 2, "fp8": 1}
 
-DEVICE_SOURCE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "paged_kv_cache_108_amd",
-                             "csrc", "device.hip")
+CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "paged_kv_cache_108_amd", "csrc")
+# every file of device code: the counters hold only while all of them are unchanged
+DEVICE_SOURCES = [os.path.join(CSRC, f) for f in ("device.hip", "attn_kernels.h", "attn_inst.hip")]
+
+
+def device_source_sha256(paths=None):
+    """SHA-256 over the device sources, in order."""
+    import hashlib
+    h = hashlib.sha256()
+    for path in paths or DEVICE_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 # HBM traffic of one measured call (its two kernels), from
 # rocprofv3 --pmc FETCH_SIZE and --pmc WRITE_SIZE runs of this script's default
@@ -54,13 +65,11 @@ MEASURED_TRAFFIC = {
 def measured_traffic(name, cache_dtype, bs, part, step="split"):
     """Bytes per attention call from the counters, or None when none were taken
     for this configuration or the kernel source has changed since."""
-    import hashlib
     m = MEASURED_TRAFFIC.get((name, cache_dtype, bs, part, step))
     if m is None:
         return None
-    with open(DEVICE_SOURCE, "rb") as f:
-        if hashlib.sha256(f.read()).hexdigest() != m["source_sha256"]:
-            return None
+    if device_source_sha256() != m["source_sha256"]:
+        return None
     return int(round(1024 * (m["fetch_kib"] * m["fetch_scale"] + m["write_kib"] * m["write_scale"])))
 
 

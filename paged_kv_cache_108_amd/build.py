@@ -37,19 +37,38 @@ def _run(cmd, verbose):
         print(out)
 
 
-def build(verbose=False, out=LIB, extra_hip_flags=()):
+# The attention kernels are instantiated once per (cache type, head dim) in
+# attn_inst.hip, each its own translation unit: 0/1/2 = f32/bf16/fp8 caches.
+INSTANCES = [(kv, d) for kv in (0, 1, 2) for d in (64, 128)]
+
+
+def build(verbose=False, out=LIB, extra_hip_flags=(), jobs=None):
+    """Compile every translation unit (in parallel) and link libpkv.so."""
+    from concurrent.futures import ThreadPoolExecutor
     hipcc = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
     cxx = os.environ.get("CXX", shutil.which("g++") or "g++")
+    jobs = jobs or min(8, os.cpu_count() or 1, int(os.environ.get("MAX_JOBS", "8")))
     with tempfile.TemporaryDirectory(prefix="pkv_build_") as tmp:
         host_o = os.path.join(tmp, "host.o")
+        cmds = [[cxx, "-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-I", INCLUDE, "-c",
+                 os.path.join(CSRC, "host.cpp"), "-o", host_o]]
+        objs = [host_o]
+        for kv, d in INSTANCES:
+            o = os.path.join(tmp, f"attn_{kv}_{d}.o")
+            cmds.append([hipcc, *HIP_FLAGS, *extra_hip_flags, f"-DPKV_INST_KV={kv}", f"-DPKV_INST_D={d}",
+                         "-I", INCLUDE, "-c", os.path.join(CSRC, "attn_inst.hip"), "-o", o])
+            objs.append(o)
         dev_o = os.path.join(tmp, "device.o")
-        _run([cxx, "-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-I", INCLUDE, "-c",
-              os.path.join(CSRC, "host.cpp"), "-o", host_o], verbose)
-        _run([hipcc, *HIP_FLAGS, *extra_hip_flags, "-I", INCLUDE, "-c",
-              os.path.join(CSRC, "device.hip"), "-o", dev_o], verbose)
+        cmds.append([hipcc, *HIP_FLAGS, *extra_hip_flags, "-I", INCLUDE, "-c",
+                     os.path.join(CSRC, "device.hip"), "-o", dev_o])
+        objs.append(dev_o)
+        # the longest compiles first
+        cmds = cmds[1:] + cmds[:1]
+        with ThreadPoolExecutor(max_workers=jobs) as ex:
+            for f in [ex.submit(_run, c, verbose) for c in cmds]:
+                f.result()
         tmp_so = os.path.join(tmp, "libpkv.so")
-        _run([hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", host_o, dev_o, "-o", tmp_so],
-             verbose)
+        _run([hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp_so], verbose)
         shutil.move(tmp_so, out + ".tmp")
         os.replace(out + ".tmp", out)
     return out

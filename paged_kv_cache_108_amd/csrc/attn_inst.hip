@@ -1,0 +1,60 @@
+// Instantiations of the attention kernels for one cache type and head dim,
+// chosen at compile time (-DPKV_INST_KV=0|1|2 for f32|bf16|fp8 caches,
+// -DPKV_INST_D=64|128); the build compiles this file once per pair, in
+// parallel. pick_kernel returns the kernel for a block size and mode.
+#include "attn_kernels.h"
+
+#ifndef PKV_INST_KV
+#error "PKV_INST_KV must be defined (0: f32, 1: bf16, 2: fp8)"
+#endif
+#ifndef PKV_INST_D
+#error "PKV_INST_D must be defined (64 or 128)"
+#endif
+
+namespace pkv_dev {
+
+namespace {
+
+template <int KV, int D, int MODE, int NT>
+AttnKernel stream_for_bs(int bs) {
+    switch (bs) {
+        case 8: return paged_attn_stream_kernel<KV, D, 8, MODE, NT>;
+        case 16: return paged_attn_stream_kernel<KV, D, 16, MODE, NT>;
+        case 32: return paged_attn_stream_kernel<KV, D, 32, MODE, NT>;
+        case 64: return paged_attn_stream_kernel<KV, D, 64, MODE, NT>;
+        case 128: return paged_attn_stream_kernel<KV, D, 128, MODE, NT>;
+    }
+    return nullptr;
+}
+
+template <int KV, int D>
+AttnKernel partition_for_bs(int bs) {
+    switch (bs) {
+        case 8: return paged_attn_partition_kernel<KV, D, 8>;
+        case 16: return paged_attn_partition_kernel<KV, D, 16>;
+        case 32: return paged_attn_partition_kernel<KV, D, 32>;
+        case 64: return paged_attn_partition_kernel<KV, D, 64>;
+        case 128: return paged_attn_partition_kernel<KV, D, 128>;
+    }
+    return nullptr;
+}
+
+}  // namespace
+
+// tiles: 16-column MFMA tiles per pass (query windows: 1 or wide_tiles(D))
+template <int KV, int D>
+AttnKernel pick_kernel(int bs, int mode, int tiles, bool partition) {
+    if (partition) return partition_for_bs<KV, D>(bs);
+    switch (mode) {
+        case SM_WINDOW:
+            return tiles == 1 ? stream_for_bs<KV, D, SM_WINDOW, 1>(bs)
+                              : stream_for_bs<KV, D, SM_WINDOW, wide_tiles(D)>(bs);
+        case SM_STEP: return stream_for_bs<KV, D, SM_STEP, 1>(bs);
+        case SM_SHARED: return stream_for_bs<KV, D, SM_SHARED, 1>(bs);
+        default: return stream_for_bs<KV, D, SM_DECODE, 1>(bs);
+    }
+}
+
+template AttnKernel pick_kernel<PKV_INST_KV, PKV_INST_D>(int, int, int, bool);
+
+}  // namespace pkv_dev

@@ -49,101 +49,14 @@
 #include <type_traits>
 
 #include "common.h"
+#include "attn_kernels.h"
 
 using pkv::fail;
 using pkv::ok;
 
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-#ifndef PKV_WAVES
-#define PKV_WAVES 4
-#endif
-constexpr int kWaves = PKV_WAVES;         // waves per workgroup
-constexpr int kThreads = kWaves * 64;
-constexpr int kMaxCachedLens = 4096;      // sequences whose lengths a workgroup keeps in LDS
-constexpr int kMaxWorkers = 4096;         // waves of the balanced split, at most (sizes its workspace)
-#ifndef PKV_MIN_POS
-#define PKV_MIN_POS 4
-#endif
-constexpr unsigned kMinPositions = PKV_MIN_POS;   // balanced split: positions per wave, at least
-constexpr int kMergeBatch = 32;           // records per round trip for rows that merge 32 or more
-// 16-column tiles per pass for wide query windows. Each tile adds its own
-// q fragment, accumulator and softmax to every chunk: four tiles at d 128
-// spill registers, and four at d 64 made a chunk's compute outlast its load.
-constexpr int wide_tiles(int) { return 2; }
-constexpr float kLog2e = 1.4426950408889634f;
-
-enum KvKind { KV_F32 = 0, KV_BF16 = 1, KV_FP8 = 2 };
-
-// Balanced split: positions a segment costs beyond its chunks. Starting and
-// finishing a segment costs about one memory round trip, which is one chunk
-// time for 8 KiB chunks (bf16 at d 128) and proportionally more chunks for
-// smaller ones.
-__host__ __device__ constexpr int seg_cost(int kv, int d) {
-    const int chunk_bytes = 16 * 2 * d * (kv == KV_F32 ? 4 : kv == KV_BF16 ? 2 : 1);
-    return chunk_bytes >= 8192 ? 1 : 8192 / chunk_bytes;
-}
-constexpr int kSegCostMax = seg_cost(KV_FP8, 64);
-
-// ----------------------------------------------------------------------------
-// Small device helpers
-// ----------------------------------------------------------------------------
-
-// OCP E4M3 encoder written from the format definition: round to nearest,
-// ties to even mantissa, |y| > 448 (and infinities) saturate to 448, NaN keeps
-// its sign with the all-ones code, zero keeps its sign. Both candidate codes
-// (subnormal and normal) are formed and one is selected, so the encoder has
-// no branches.
-__device__ __forceinline__ uint32_t e4m3_encode(float y) {
-    const uint32_t sign = (__float_as_uint(y) >> 24) & 0x80u;
-    const float a = fminf(fabsf(y), 448.0f);    // saturate first: 448 is code 0x7E
-    // below 2^-6 the quantum is 2^-9: exact scaling, round half to even; the
-    // count 8 is the smallest normal, code 0x08
-    const uint32_t sub = (uint32_t)rintf(a * 512.0f);
-    uint32_t ua = __float_as_uint(a);
-    ua += 0x7FFFFu + ((ua >> 20) & 1u);         // round the 23-bit mantissa to 3 bits, RNE
-    const uint32_t nrm = (((ua >> 23) - 120u) << 3) | ((ua >> 20) & 7u);   // rebias 127 -> 7
-    const uint32_t code = a < 0.015625f ? sub : nrm;
-    return sign | (y != y ? 0x7Fu : code);
-}
-
-__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
-    return __uint_as_float((uint32_t)b << 16);
-}
-
-// Reduction over the 4 lanes that hold one head (lanes h, h+16, h+32, h+48).
-__device__ __forceinline__ float head_max(float x) {
-    auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-    auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
-
-__device__ __forceinline__ float head_sum(float x) {
-    auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-    auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
-}
-
-// Two fp8 codes (low or high 16 bits of `w`) -> two bf16 (exact).
-template <bool HI>
-__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
-    bf16x2 r = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI);
-    return __builtin_bit_cast(uint32_t, r);
-}
-
-__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-    bf16x2 r = {(__bf16)a, (__bf16)b};          // v_cvt_pk_bf16_f32: round to nearest even
-    return __builtin_bit_cast(uint32_t, r);
-}
-
-__device__ __forceinline__ float bf16_lo_as_f32(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf16_hi_as_f32(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+using namespace pkv_dev;
 
 // ----------------------------------------------------------------------------
 // Block copy (copy-on-write)
@@ -208,1155 +121,6 @@ kv_cache_write_kernel(const void* __restrict__ k_new, const void* __restrict__ v
             }
             static_cast<uint8_t*>(k_cache)[kd] = (uint8_t)e4m3_encode(kx * k_inv);
             static_cast<uint8_t*>(v_cache)[vd] = (uint8_t)e4m3_encode(vx * v_inv);
-        }
-    }
-}
-
-// ----------------------------------------------------------------------------
-// Paged decode attention
-// ----------------------------------------------------------------------------
-
-struct AttnParams {
-    float* out;
-    const void* q;
-    const void* k;
-    const void* v;
-    const int32_t* tables;
-    const int32_t* lens;
-    float* ws;             // partial records: o [n_rec][G][D], m [n_rec][G], l [n_rec][G]
-    int S, Hq, Hkv, G, P, max_blocks, max_len, part_tokens, n_part;
-    int cache_lens;        // workgroups keep all S context lengths in LDS
-    int balanced;          // 1: balanced split over the grid; 0: fixed partitions
-    int n_workers;         // grid size (balanced split)
-    int n_rec;             // partial records in the workspace
-    int* desc;             // balanced split: per segment (first record, record count)
-    int n_q;               // queries per sequence (1: decode)
-    int qgs;               // queries per query group (G * qgs <= 16 columns)
-    int n_qg;              // query groups per (sequence, kv head)
-    int cols;              // MFMA columns in use: G * qgs; partial records hold this many rows
-    const void* k_new;     // decode step: sequence i's new token [S][Hkv][D] (src dtype)
-    const void* v_new;
-    float k_inv, v_inv;    // decode step, fp8 cache: inverse scales of the write
-    float qk_scale;        // softmax_scale * k_scale * log2(e): scores in the log2 domain
-    float v_scale;
-    float* lse;            // optional [rows]: base-2 log of each output row's softmax sum
-    int causal;            // query windows: 1 causal inside the window, 0 every query sees all L
-    // Shared-prefix launches: sequences 0 .. n_pre-1 are group prefixes (n_q
-    // queries each, tables/lens/max_blocks/max_len, rows in out/lse) and
-    // sequences n_pre .. S-1 are member suffixes (one query each, the
-    // arrays below, rows in out2/lse2; member m's query is q row m).
-    int n_pre;             // 0 for every other launch
-    const int32_t* tables2;
-    const int32_t* lens2;
-    int max_blocks2, max_len2;
-    float* out2;
-    float* lse2;
-};
-
-// Clamped context length of sequence s (of either table set).
-__device__ __forceinline__ int clamped_len(const AttnParams& p, int s) {
-    if (p.n_pre > 0 && s >= p.n_pre) return min(p.lens2[s - p.n_pre], p.max_len2);
-    return min(p.lens[s], p.max_len);
-}
-
-// Per-cache-type register fragments of one 16-token chunk.
-template <int KV, int D> struct Frag;
-
-template <int D> struct Frag<KV_F32, D> {
-    float4 k[D / 16];      // token r16, channels 16f + 4j4 .. +3
-    float4 v[D / 16];      // channel 16s + r16, tokens 4j4 .. +3
-};
-template <int D> struct Frag<KV_BF16, D> {
-    uint4 k[D / 32];       // token r16, channels 32s + 8j4 .. +7
-    uint2 v[D / 16];       // channel 16s + r16, tokens 4j4 .. +3
-};
-template <int D> struct Frag<KV_FP8, D> {
-    uint4 k[D / 64];       // token r16, channels 64f + 16j4 .. +15
-    uint32_t v[D / 16];    // channel 16s + r16, tokens 4j4 .. +3 (for bs >= 16 as loaded:
-                           // v[4t + c] = tokens 4c .. +3 of channel 16(4t + j4) + r16, until
-                           // v_rows_to_operand)
-};
-
-template <int KV> struct QFragT;
-template <> struct QFragT<KV_F32> { using T = float4; };
-template <> struct QFragT<KV_BF16> { using T = uint4; };
-template <> struct QFragT<KV_FP8> { using T = uint4; };
-
-// Number of 16-byte q loads per lane, matching the K fragment's channel map.
-template <int KV, int D> constexpr int q_loads() { return KV == KV_F32 ? D / 16 : D / 32; }
-
-// Load the K and V fragments of the chunk starting at token `tc` (absolute).
-// b0 is the physical block holding token tc; for bs 8, b1 holds token tc + 8.
-// Streaming loads of the cache: the nontemporal hint marks the lines
-// evict-first, since each K/V byte is read once per call: a 16-token chunk
-// reads 16 whole K rows and one whole V sub-tile of its block.
-__device__ __forceinline__ uint4 ld_stream(const uint4* a) {
-    typedef unsigned v4u __attribute__((ext_vector_type(4)));
-    const v4u t = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(a));
-    return make_uint4(t.x, t.y, t.z, t.w);
-}
-__device__ __forceinline__ float4 ld_stream(const float4* a) {
-    typedef float v4f __attribute__((ext_vector_type(4)));
-    const v4f t = __builtin_nontemporal_load(reinterpret_cast<const v4f*>(a));
-    return make_float4(t.x, t.y, t.z, t.w);
-}
-__device__ __forceinline__ uint2 ld_stream(const uint2* a) {
-    typedef unsigned v2u __attribute__((ext_vector_type(2)));
-    const v2u t = __builtin_nontemporal_load(reinterpret_cast<const v2u*>(a));
-    return make_uint2(t.x, t.y);
-}
-__device__ __forceinline__ uint32_t ld_stream(const uint32_t* a) { return __builtin_nontemporal_load(a); }
-template <int BS, typename T>
-__device__ __forceinline__ T ld_kv(const T* a) {
-    return ld_stream(a);
-}
-
-template <int KV, int D, int BS>
-__device__ __forceinline__ void load_chunk(Frag<KV, D>& f, const AttnParams& p, int b0, int b1,
-                                           int tc, int g, int r16, int j4) {
-    using E = typename std::conditional<KV == KV_F32, float,
-              typename std::conditional<KV == KV_BF16, uint16_t, uint8_t>::type>::type;
-    const E* kbase = static_cast<const E*>(p.k);
-    const E* vbase = static_cast<const E*>(p.v);
-    int bk, bv;            // physical blocks for this lane's K row and V tokens
-    int ok_, ov;           // offsets within those blocks
-    if constexpr (BS == 8) {
-        bk = r16 < 8 ? b0 : b1;
-        ok_ = r16 & 7;
-        bv = j4 < 2 ? b0 : b1;
-        ov = (4 * j4) & 7;
-    } else {
-        bk = b0;
-        bv = b0;
-        ok_ = (tc % BS) + r16;
-        ov = ((tc % BS) / 16) * 16 * D + 4 * j4;    // the chunk's 16-token V sub-tile
-    }
-    constexpr int VS = BS < 16 ? BS : 16;           // tokens per V sub-tile row
-    const size_t tile = (size_t)BS * D;
-    const E* krow = kbase + ((size_t)bk * p.Hkv + g) * tile + (size_t)ok_ * D;
-    const E* vt = vbase + ((size_t)bv * p.Hkv + g) * tile + ov;
-    if constexpr (KV == KV_F32) {
-#pragma unroll
-        for (int x = 0; x < D / 16; ++x)
-            f.k[x] = ld_kv<BS>(reinterpret_cast<const float4*>(krow + 16 * x + 4 * j4));
-#pragma unroll
-        for (int s = 0; s < D / 16; ++s)
-            f.v[s] = ld_kv<BS>(reinterpret_cast<const float4*>(vt + (size_t)(16 * s + r16) * VS));
-    } else if constexpr (KV == KV_BF16) {
-#pragma unroll
-        for (int s = 0; s < D / 32; ++s)
-            f.k[s] = ld_kv<BS>(reinterpret_cast<const uint4*>(krow + 32 * s + 8 * j4));
-#pragma unroll
-        for (int s = 0; s < D / 16; ++s)
-            f.v[s] = ld_kv<BS>(reinterpret_cast<const uint2*>(vt + (size_t)(16 * s + r16) * VS));
-    } else {
-#pragma unroll
-        for (int x = 0; x < D / 64; ++x)
-            f.k[x] = ld_kv<BS>(reinterpret_cast<const uint4*>(krow + 64 * x + 16 * j4));
-        if constexpr (BS >= 16) {
-            // whole 16-token rows, 16 bytes per lane: lane (r16, j4) reads the row
-            // of channel 16(4t + j4) + r16; v_rows_to_operand moves the tokens
-            // to the lanes the P.V MFMA wants
-            const E* vsub = vt - 4 * j4;
-#pragma unroll
-            for (int t = 0; t < D / 64; ++t) {
-                const uint4 row = ld_kv<BS>(reinterpret_cast<const uint4*>(vsub + (size_t)(16 * (4 * t + j4) + r16) * 16));
-                f.v[4 * t + 0] = row.x;
-                f.v[4 * t + 1] = row.y;
-                f.v[4 * t + 2] = row.z;
-                f.v[4 * t + 3] = row.w;
-            }
-        } else {
-#pragma unroll
-            for (int s = 0; s < D / 16; ++s)
-                f.v[s] = ld_kv<BS>(reinterpret_cast<const uint32_t*>(vt + (size_t)(16 * s + r16) * VS));
-        }
-    }
-}
-
-// fp8 V at bs >= 16 arrives as whole rows: within each group of 4 dim blocks
-// 4t .. 4t+3, row q of lanes (lanes 16q .. 16q+15) holds block 4t + q's 16
-// tokens in v[4t .. 4t+3] (4 tokens per word), and the P.V operand wants
-// block 4t + q' in v[4t + q'], tokens 4q .. 4q+3 in row q: a 4 x 4 transpose
-// of (lane row, word), done with two rounds of row swaps.
-template <int KV, int D, int BS>
-__device__ __forceinline__ void v_rows_to_operand(Frag<KV, D>& f) {
-    if constexpr (KV == KV_FP8 && BS >= 16) {
-#pragma unroll
-        for (int t = 0; t < D / 64; ++t) {
-            // rows 0/1 and 2/3 exchange between words 0/1 and 2/3 ...
-            const auto a = __builtin_amdgcn_permlane16_swap(f.v[4 * t + 0], f.v[4 * t + 1], false, false);
-            const auto b = __builtin_amdgcn_permlane16_swap(f.v[4 * t + 2], f.v[4 * t + 3], false, false);
-            // ... then lane halves between words (0, 2) and (1, 3)
-            const auto c = __builtin_amdgcn_permlane32_swap(a[0], b[0], false, false);
-            const auto d = __builtin_amdgcn_permlane32_swap(a[1], b[1], false, false);
-            f.v[4 * t + 0] = c[0];
-            f.v[4 * t + 2] = c[1];
-            f.v[4 * t + 1] = d[0];
-            f.v[4 * t + 3] = d[1];
-        }
-    }
-}
-
-// Scores of the chunk: S^T[token 4*j4+i][head r16] in acc[i].
-template <int KV, int D>
-__device__ __forceinline__ f32x4 chunk_scores(const Frag<KV, D>& f,
-                                              const typename QFragT<KV>::T* qf) {
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    if constexpr (KV == KV_F32) {
-#pragma unroll
-        for (int x = 0; x < D / 16; ++x) {
-            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(f.k[x].x, qf[x].x, acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(f.k[x].y, qf[x].y, acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(f.k[x].z, qf[x].z, acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(f.k[x].w, qf[x].w, acc, 0, 0, 0);
-        }
-    } else if constexpr (KV == KV_BF16) {
-#pragma unroll
-        for (int s = 0; s < D / 32; ++s)
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, f.k[s]),
-                                                          __builtin_bit_cast(bf16x8, qf[s]),
-                                                          acc, 0, 0, 0);
-    } else {
-#pragma unroll
-        for (int x = 0; x < D / 64; ++x) {
-            const uint32_t w[4] = {f.k[x].x, f.k[x].y, f.k[x].z, f.k[x].w};
-            uint4 lo, hi;          // channels +0..7 and +8..15 as bf16
-            lo.x = fp8x2_to_bf16x2<false>(w[0]); lo.y = fp8x2_to_bf16x2<true>(w[0]);
-            lo.z = fp8x2_to_bf16x2<false>(w[1]); lo.w = fp8x2_to_bf16x2<true>(w[1]);
-            hi.x = fp8x2_to_bf16x2<false>(w[2]); hi.y = fp8x2_to_bf16x2<true>(w[2]);
-            hi.z = fp8x2_to_bf16x2<false>(w[3]); hi.w = fp8x2_to_bf16x2<true>(w[3]);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, lo),
-                                                          __builtin_bit_cast(bf16x8, qf[2 * x]),
-                                                          acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, hi),
-                                                          __builtin_bit_cast(bf16x8, qf[2 * x + 1]),
-                                                          acc, 0, 0, 0);
-        }
-    }
-    return acc;
-}
-
-// O^T += V^T . P^T for the chunk; `tail_mask` zeroes V of tokens >= t_end.
-template <int KV, int D>
-__device__ __forceinline__ void chunk_pv(Frag<KV, D>& f, const float p[4], f32x4* o,
-                                         bool tail, int first_tok, int t_end) {
-    if constexpr (KV == KV_F32) {
-        if (tail) {
-#pragma unroll
-            for (int s = 0; s < D / 16; ++s) {
-                f.v[s].x = first_tok + 0 < t_end ? f.v[s].x : 0.f;
-                f.v[s].y = first_tok + 1 < t_end ? f.v[s].y : 0.f;
-                f.v[s].z = first_tok + 2 < t_end ? f.v[s].z : 0.f;
-                f.v[s].w = first_tok + 3 < t_end ? f.v[s].w : 0.f;
-            }
-        }
-#pragma unroll
-        for (int s = 0; s < D / 16; ++s) {
-            o[s] = __builtin_amdgcn_mfma_f32_16x16x4f32(f.v[s].x, p[0], o[s], 0, 0, 0);
-            o[s] = __builtin_amdgcn_mfma_f32_16x16x4f32(f.v[s].y, p[1], o[s], 0, 0, 0);
-            o[s] = __builtin_amdgcn_mfma_f32_16x16x4f32(f.v[s].z, p[2], o[s], 0, 0, 0);
-            o[s] = __builtin_amdgcn_mfma_f32_16x16x4f32(f.v[s].w, p[3], o[s], 0, 0, 0);
-        }
-    } else {
-        // P = hi + lo, both bf16 (|lo| <= 2^-9 |P|, so the pair carries ~16 bits).
-        // One 16x16x32 MFMA takes both halves: this lane's 8 k-slots are
-        // (hi of its 4 tokens, lo of its 4 tokens) on the P side and the same
-        // 4 V values twice on the V side, so the sum over k is sum_t v_t (hi_t + lo_t).
-        const uint32_t h01 = pack_bf16x2(p[0], p[1]);
-        const uint32_t h23 = pack_bf16x2(p[2], p[3]);
-        const uint32_t l01 = pack_bf16x2(p[0] - bf16_lo_as_f32(h01), p[1] - bf16_hi_as_f32(h01));
-        const uint32_t l23 = pack_bf16x2(p[2] - bf16_lo_as_f32(h23), p[3] - bf16_hi_as_f32(h23));
-        const bf16x8 php = __builtin_bit_cast(bf16x8, make_uint4(h01, h23, l01, l23));
-        // keep-masks for the two bf16 halves of each 32-bit word (tokens +0/+1, +2/+3)
-        uint32_t m01 = 0xFFFFFFFFu, m23 = 0xFFFFFFFFu;
-        uint32_t m8 = 0xFFFFFFFFu;
-        if (tail) {
-            m01 = (first_tok + 0 < t_end ? 0x0000FFFFu : 0u) | (first_tok + 1 < t_end ? 0xFFFF0000u : 0u);
-            m23 = (first_tok + 2 < t_end ? 0x0000FFFFu : 0u) | (first_tok + 3 < t_end ? 0xFFFF0000u : 0u);
-            m8 = (first_tok + 0 < t_end ? 0x000000FFu : 0u) | (first_tok + 1 < t_end ? 0x0000FF00u : 0u) |
-                 (first_tok + 2 < t_end ? 0x00FF0000u : 0u) | (first_tok + 3 < t_end ? 0xFF000000u : 0u);
-        }
-#pragma unroll
-        for (int s = 0; s < D / 16; ++s) {
-            uint2 vv;
-            if constexpr (KV == KV_BF16) {
-                vv = make_uint2(f.v[s].x & m01, f.v[s].y & m23);
-            } else {
-                const uint32_t w = f.v[s] & m8;   // masked codes become +0
-                vv = make_uint2(fp8x2_to_bf16x2<false>(w), fp8x2_to_bf16x2<true>(w));
-            }
-            const bf16x8 a = __builtin_bit_cast(bf16x8, make_uint4(vv.x, vv.y, vv.x, vv.y));
-            o[s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, php, o[s], 0, 0, 0);
-        }
-    }
-}
-
-// A work item: sequence i, kv head g, tokens [t0, t1). `rec` < 0: the item is
-// the whole sequence and writes the final output rows; otherwise it writes
-// partial-result record `rec` (m, l and unnormalised o of its G heads).
-struct Item {
-    int i, g, L, t0, t1, n_chunks, rec;
-};
-
-// Block ids of one wave's chunks c_k = wave + kWaves*k for k in [kb, kb+64):
-// lane k - kb holds the physical block of chunk c_k's first token (id0) and,
-// for bs 8, of its token +8 (id1). Only table entries that exist are read.
-// q fragment of this lane (head r16 of kv head g's group, zero for padding
-// heads): the channel map is the K fragment's.
-template <int KV, int D>
-__device__ __forceinline__ void load_q(const AttnParams& p, int i, int g, int r16, int j4,
-                                       typename QFragT<KV>::T* qf) {
-    using QF = typename QFragT<KV>::T;
-    const bool live = r16 < p.G;
-    const size_t qoff = ((size_t)i * p.Hq + g * p.G + (live ? r16 : 0)) * D;
-#pragma unroll
-    for (int x = 0; x < q_loads<KV, D>(); ++x) {
-        int c;
-        if constexpr (KV == KV_F32) c = 16 * x + 4 * j4;
-        else if constexpr (KV == KV_BF16) c = 32 * x + 8 * j4;
-        else c = 64 * (x >> 1) + 16 * j4 + 8 * (x & 1);
-        QF val;
-        if constexpr (KV == KV_F32)
-            val = *reinterpret_cast<const float4*>(static_cast<const float*>(p.q) + qoff + c);
-        else
-            val = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.q) + qoff + c);
-        if (!live) val = QF{};
-        qf[x] = val;
-    }
-}
-
-// The q fragment of one column from an explicit row offset (elements) of q;
-// zero when the column is not live.
-template <int KV, int D>
-__device__ __forceinline__ void load_q_row(const AttnParams& p, size_t row, bool live, int j4,
-                                           typename QFragT<KV>::T* qf) {
-    using QF = typename QFragT<KV>::T;
-    const size_t qoff = live ? row : 0;
-#pragma unroll
-    for (int x = 0; x < q_loads<KV, D>(); ++x) {
-        int c;
-        if constexpr (KV == KV_F32) c = 16 * x + 4 * j4;
-        else if constexpr (KV == KV_BF16) c = 32 * x + 8 * j4;
-        else c = 64 * (x >> 1) + 16 * j4 + 8 * (x & 1);
-        QF val;
-        if constexpr (KV == KV_F32)
-            val = *reinterpret_cast<const float4*>(static_cast<const float*>(p.q) + qoff + c);
-        else
-            val = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.q) + qoff + c);
-        if (!live) val = QF{};
-        qf[x] = val;
-    }
-}
-
-// The new token's K row and V values of one (sequence, kv head), in the
-// chunk fragments' register layout and already in the cache's encoding
-// (the write's): nk like Frag::k for the lane's channels, nv[s] the value of
-// channel 16s + r16 (bits of an f32, a bf16 or an E4M3 code). `stage` is the
-// wave's LDS staging area of D/2 words, used by the fp8 encoding.
-template <int KV, int D> struct NewTok;
-template <int D> struct NewTok<KV_F32, D> { float4 k[D / 16]; uint32_t v[D / 16]; };
-template <int D> struct NewTok<KV_BF16, D> { uint4 k[D / 32]; uint32_t v[D / 16]; };
-template <int D> struct NewTok<KV_FP8, D> { uint4 k[D / 64]; uint32_t v[D / 16]; };
-
-template <int KV, int D>
-__device__ __forceinline__ void load_new_token(const AttnParams& p, size_t row, int r16, int j4,
-                                               uint32_t* stage, NewTok<KV, D>& nt) {
-    if constexpr (KV == KV_F32) {
-        const float* kn = static_cast<const float*>(p.k_new) + row;
-        const float* vn = static_cast<const float*>(p.v_new) + row;
-#pragma unroll
-        for (int x = 0; x < D / 16; ++x) nt.k[x] = *reinterpret_cast<const float4*>(kn + 16 * x + 4 * j4);
-#pragma unroll
-        for (int s = 0; s < D / 16; ++s) nt.v[s] = __float_as_uint(vn[16 * s + r16]);
-    } else if constexpr (KV == KV_BF16) {
-        const uint16_t* kn = static_cast<const uint16_t*>(p.k_new) + row;
-        const uint16_t* vn = static_cast<const uint16_t*>(p.v_new) + row;
-#pragma unroll
-        for (int x = 0; x < D / 32; ++x) nt.k[x] = *reinterpret_cast<const uint4*>(kn + 32 * x + 8 * j4);
-#pragma unroll
-        for (int s = 0; s < D / 16; ++s) nt.v[s] = vn[16 * s + r16];
-    } else {
-        // encode cooperatively: lane l turns channels 4l..4l+3 of the row
-        // [K | V] (2D codes) into one word of the wave's staging area, then
-        // every lane reads back what its fragment layout needs
-        const int lane = 16 * j4 + r16;
-        if (lane < D / 2) {
-            const int c0 = 4 * lane;
-            const bool is_v = c0 >= D;
-            const uint16_t* src = static_cast<const uint16_t*>(is_v ? p.v_new : p.k_new) + row +
-                                  (is_v ? c0 - D : c0);
-            const uint2 w = *reinterpret_cast<const uint2*>(src);
-            // both scales as scalars first: a lane-dependent choice between
-            // the two parameters would otherwise become a per-lane load
-            float k_inv = p.k_inv, v_inv = p.v_inv;
-            asm volatile("" : "+s"(k_inv), "+s"(v_inv));
-            const float inv = is_v ? v_inv : k_inv;
-            stage[lane] = e4m3_encode(bf16_bits_to_f32((uint16_t)w.x) * inv) |
-                          e4m3_encode(bf16_bits_to_f32((uint16_t)(w.x >> 16)) * inv) << 8 |
-                          e4m3_encode(bf16_bits_to_f32((uint16_t)w.y) * inv) << 16 |
-                          e4m3_encode(bf16_bits_to_f32((uint16_t)(w.y >> 16)) * inv) << 24;
-        }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-#pragma unroll
-        for (int x = 0; x < D / 64; ++x) nt.k[x] = *reinterpret_cast<const uint4*>(stage + 16 * x + 4 * j4);
-#pragma unroll
-        for (int s = 0; s < D / 16; ++s)
-            nt.v[s] = (stage[D / 4 + 4 * s + (r16 >> 2)] >> (8 * (r16 & 3))) & 0xFFu;
-    }
-}
-
-// Put the new token (chunk row rr) into a loaded chunk fragment.
-template <int KV, int D>
-__device__ __forceinline__ void patch_new_k(Frag<KV, D>& f, const NewTok<KV, D>& nt, int rr, int r16) {
-    if (r16 == rr) {
-#pragma unroll
-        for (int x = 0; x < (int)(sizeof(nt.k) / sizeof(nt.k[0])); ++x) f.k[x] = nt.k[x];
-    }
-}
-template <int KV, int D>
-__device__ __forceinline__ void patch_new_v(Frag<KV, D>& f, const NewTok<KV, D>& nt, int rr, int j4) {
-    if (j4 == (rr >> 2)) {
-        const int e = rr & 3;
-#pragma unroll
-        for (int s = 0; s < D / 16; ++s) {
-            if constexpr (KV == KV_F32) {
-                const float v = __uint_as_float(nt.v[s]);
-                if (e == 0) f.v[s].x = v; else if (e == 1) f.v[s].y = v;
-                else if (e == 2) f.v[s].z = v; else f.v[s].w = v;
-            } else if constexpr (KV == KV_BF16) {
-                uint32_t& word = (e >> 1) ? f.v[s].y : f.v[s].x;
-                const int sh = 16 * (e & 1);
-                word = (word & ~(0xFFFFu << sh)) | (nt.v[s] << sh);
-            } else {
-                const int sh = 8 * e;
-                f.v[s] = (f.v[s] & ~(0xFFu << sh)) | (nt.v[s] << sh);
-            }
-        }
-    }
-}
-
-template <int BS>
-__device__ __forceinline__ void load_ids(const AttnParams& p, const Item& it, int wave, int lane,
-                                         int kb, int& id0, int& id1) {
-    const int nk = it.n_chunks > wave ? (it.n_chunks - wave + kWaves - 1) / kWaves : 0;
-    const int nw = min(64, nk - kb);
-    id0 = 0;
-    id1 = 0;
-    if (lane < nw) {
-        const int32_t* __restrict__ row = p.tables + (size_t)it.i * p.max_blocks;
-        const int tc = it.t0 + 16 * (wave + kWaves * (kb + lane));
-        if constexpr (BS == 8) {
-            id0 = row[tc / 8];
-            id1 = tc + 8 < it.t1 ? row[tc / 8 + 1] : id0;
-        } else {
-            id0 = row[tc / BS];
-        }
-        id0 = min(max(id0, 0), p.P - 1);
-        id1 = min(max(id1, 0), p.P - 1);
-    }
-}
-
-// One work item by the whole workgroup. `cid0/cid1` are this wave's block ids
-// for the item's first 64 chunks (loaded earlier); the next item's ids are
-// fetched at once into `nid0/nid1`, so an item starts with a single memory
-// round trip. LDS `smem` holds m[waves][16], l[waves][16], o[waves][G][D].
-template <int KV, int D, int BS>
-__device__ __forceinline__ void attend_item(const AttnParams& p, float* smem, const Item& it,
-                                            int cid0, int cid1, bool has_next, const Item& nxt,
-                                            int& nid0, int& nid1) {
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
-    const int r16 = lane & 15;               // MFMA row / column index
-    const int j4 = lane >> 4;                // token group (scores) / k-group (operands)
-    const int G = p.G;
-    const int i = it.i, g = it.g, t0 = it.t0, t1 = it.t1;
-    const int n_chunks = it.n_chunks;
-    if (has_next) load_ids<BS>(p, nxt, wave, lane, 0, nid0, nid1);
-    using QF = typename QFragT<KV>::T;
-    QF qf[q_loads<KV, D>()];
-    load_q<KV, D>(p, i, g, r16, j4, qf);
-
-    f32x4 o[D / 16];
-#pragma unroll
-    for (int s = 0; s < D / 16; ++s) o[s] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m_run = -INFINITY;
-    float l_run = 0.f;
-
-    auto process = [&](Frag<KV, D>& f, int c) {
-        const int tc = t0 + 16 * c;
-        const f32x4 sc = chunk_scores<KV, D>(f, qf);
-        const bool tail = tc + 16 > t1;
-        const int first_tok = tc + 4 * j4;
-        float x[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            x[e] = sc[e] * p.qk_scale;
-            if (tail && first_tok + e >= t1) x[e] = -INFINITY;
-        }
-        const float cm = head_max(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
-        const float m_new = fmaxf(m_run, cm);
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-        float pr[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) pr[e] = __builtin_amdgcn_exp2f(x[e] - m_new);
-        l_run = l_run * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
-        m_run = m_new;
-        if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
-#pragma unroll
-            for (int s = 0; s < D / 16; ++s) o[s] *= alpha;
-        }
-        v_rows_to_operand<KV, D, BS>(f);
-        chunk_pv<KV, D>(f, pr, o, tail, first_tok, t1);
-    };
-
-    // This wave's chunks are c_k = wave + 4k, k < nk, their block ids read
-    // back from a VGPR with v_readlane (one VGPR load per 64 chunks).
-    const int nk = n_chunks > wave ? (n_chunks - wave + kWaves - 1) / kWaves : 0;
-    for (int kb = 0; kb < nk; kb += 64) {
-        const int nw = min(64, nk - kb);
-        int id0 = cid0, id1 = cid1;
-        if (kb > 0) load_ids<BS>(p, it, wave, lane, kb, id0, id1);
-        auto chunk_tc = [&](int k) { return t0 + 16 * (wave + kWaves * (kb + k)); };
-        // The scheduling barriers keep each prefetch at its place in program
-        // order: nothing of the next chunk's math moves above it (which would
-        // make the prefetch wait for that chunk's data).
-        auto issue = [&](Frag<KV, D>& f, int k) {
-            __builtin_amdgcn_sched_barrier(0);
-            const int b0 = __builtin_amdgcn_readlane(id0, k);
-            const int b1 = BS == 8 ? __builtin_amdgcn_readlane(id1, k) : b0;
-            load_chunk<KV, D, BS>(f, p, b0, b1, chunk_tc(k), g, r16, j4);
-            __builtin_amdgcn_sched_barrier(0);
-        };
-        // Two register buffers: chunk k+1 loads while chunk k computes. Every
-        // load inside the loop is unconditional, so each wait the compiler
-        // places covers exactly the buffer about to be used; the last one or
-        // two chunks run after the loop.
-        Frag<KV, D> fa, fb;
-        issue(fa, 0);
-        int k = 0;
-        for (; k + 2 < nw; k += 2) {
-            issue(fb, k + 1);
-            process(fa, wave + kWaves * (kb + k));
-            issue(fa, k + 2);
-            process(fb, wave + kWaves * (kb + k + 1));
-        }
-        if (k + 1 < nw) {
-            issue(fb, k + 1);
-            process(fa, wave + kWaves * (kb + k));
-            process(fb, wave + kWaves * (kb + k + 1));
-        } else {
-            process(fa, wave + kWaves * (kb + k));
-        }
-    }
-    // ---- merge the waves' states (exact rescaling to a common max) ----
-    const float l_tot = head_sum(l_run);
-    float* sm_m = smem;                       // [waves][16]
-    float* sm_l = smem + kWaves * 16;         // [waves][16]
-    float* sm_o = smem + 2 * kWaves * 16;     // [waves][G][D]
-    if (j4 == 0) {
-        sm_m[wave * 16 + r16] = m_run;
-        sm_l[wave * 16 + r16] = l_tot;
-    }
-    if (r16 < G) {
-#pragma unroll
-        for (int s = 0; s < D / 16; ++s)
-            *reinterpret_cast<f32x4*>(sm_o + ((size_t)wave * G + r16) * D + 16 * s + 4 * j4) = o[s];
-    }
-    __syncthreads();
-
-    const size_t nrec = (size_t)p.n_rec;
-    for (int e = threadIdx.x; e < G * D; e += kThreads) {
-        const int r = e / D;
-        const int ch = e - r * D;
-        float M = -INFINITY;
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm_m[w * 16 + r]);
-        float num = 0.f, den = 0.f;
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w) {
-            const float wt = __builtin_amdgcn_exp2f(sm_m[w * 16 + r] - M);
-            num += wt * sm_o[((size_t)w * G + r) * D + ch];
-            den += wt * sm_l[w * 16 + r];
-        }
-        if (it.rec < 0) {
-            p.out[((size_t)i * p.Hq + g * G + r) * D + ch] = num / den * p.v_scale;
-        } else {
-            const size_t rr = (size_t)it.rec * G + r;
-            p.ws[rr * D + ch] = num * p.v_scale;
-            if (ch == 0) {
-                p.ws[nrec * G * D + rr] = M;
-                p.ws[nrec * G * (D + 1) + rr] = den;
-            }
-        }
-    }
-    __syncthreads();                          // LDS is reused by the next item
-}
-
-// Per-sequence counts over all S sequences, prefix-summed once per workgroup:
-// thread t owns sequences [t*per, t*per + per); pre[t] is the sum over the
-// sequences of threads < t (pre[kThreads] = total). `count(s, L)` is called
-// with the clamped length; the lengths are also stored to `sL` when non-null.
-template <typename F>
-__device__ __forceinline__ void prefix_over_sequences(const AttnParams& p, int* pre, int* wsum,
-                                                      int* sL, F count) {
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int per = (p.S + kThreads - 1) / kThreads;
-    const int s_lo = min(p.S, tid * per);
-    const int s_hi = min(p.S, s_lo + per);
-    int cnt = 0;
-    for (int s = s_lo; s < s_hi; ++s) {
-        const int L = clamped_len(p, s);
-        if (sL) sL[s] = L;
-        cnt += count(s, L);
-    }
-    int x = cnt;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const int y = __shfl_up(x, off);
-        if (lane >= off) x += y;
-    }
-    if (lane == 63) wsum[wave] = x;
-    __syncthreads();
-    for (int w = 0; w < wave; ++w) x += wsum[w];
-    pre[tid + 1] = x;
-    if (tid == 0) pre[0] = 0;
-    __syncthreads();
-}
-
-// Sequence holding prefix position f (0 <= f < pre[kThreads]) and f's offset in
-// it: binary search over the thread ranges, then a scan of one range.
-template <typename F>
-__device__ __forceinline__ int find_sequence(const AttnParams& p, const int* pre, long long f,
-                                             long long scale, F count, long long& offset) {
-    const int per = (p.S + kThreads - 1) / kThreads;
-    int lo = 0, hi = kThreads;                // pre[lo]*scale <= f < pre[hi]*scale
-    while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if ((long long)pre[mid] * scale <= f) lo = mid; else hi = mid;
-    }
-    long long pos = (long long)pre[lo] * scale;
-    int s = lo * per;
-    for (; s < p.S - 1; ++s) {
-        const long long c = (long long)count(s) * scale;
-        if (f < pos + c) break;
-        pos += c;
-    }
-    offset = f - pos;
-    return s;
-}
-
-// Balanced split, in 32-bit arithmetic (the launcher keeps every position
-// below 2^31): n positions cut into W ranges, range w being
-// [start(w), start(w + 1)) with the first n % W ranges one longer.
-struct Split {
-    unsigned q, r;
-    __device__ Split(unsigned n, unsigned W) : q(n / W), r(n % W) {}
-    __device__ unsigned start(unsigned w) const { return w * q + min(w, r); }
-    __device__ unsigned owner(unsigned c) const {
-        const unsigned big = r * (q + 1);
-        return c < big ? c / (q + 1) : r + (c - big) / q;
-    }
-};
-
-// find_sequence for positions below 2^31.
-template <typename F>
-__device__ __forceinline__ int find_sequence32(const AttnParams& p, const int* pre, unsigned f,
-                                               unsigned scale, F count, unsigned& offset) {
-    const int per = (p.S + kThreads - 1) / kThreads;
-    int lo = 0, hi = kThreads;                // pre[lo]*scale <= f < pre[hi]*scale
-    while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if ((unsigned)pre[mid] * scale <= f) lo = mid; else hi = mid;
-    }
-    unsigned pos = (unsigned)pre[lo] * scale;
-    int s = lo * per;
-    for (; s < p.S - 1; ++s) {
-        const unsigned c = (unsigned)count(s) * scale;
-        if (f < pos + c) break;
-        pos += c;
-    }
-    offset = f - pos;
-    return s;
-}
-
-// Persistent grid (at most the workgroups the GPU holds at once); the work is
-// enumerated on the device from the context lengths, which each workgroup
-// reads once (kept in LDS when p.cache_lens). Items are (sequence, kv head,
-// partition): first every full partition of every sequence, then each
-// sequence's last, ragged one, kv heads fastest; workgroups take items
-// round-robin in snake order. A sequence with several partitions writes one
-// partial record per partition.
-template <int KV, int D, int BS>
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(KV == KV_F32 ? 2 : 3)))
-paged_attn_partition_kernel(AttnParams p) {
-    extern __shared__ float smem[];           // merge area, then the length cache
-    __shared__ int pre[kThreads + 1];
-    __shared__ int wsum[kWaves];
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    int* sL = p.cache_lens ? reinterpret_cast<int*>(smem + 2 * kWaves * 16 + kWaves * p.G * D) : nullptr;
-    auto seq_len = [&](int s) { return sL ? sL[s] : min(p.lens[s], p.max_len); };
-    auto n_parts = [&](int L) { return L > 0 ? (L + p.part_tokens - 1) / p.part_tokens : 0; };
-
-    prefix_over_sequences(p, pre, wsum, sL, [&](int, int L) { return max(n_parts(L) - 1, 0); });
-
-    // `fetch` fills this workgroup's next item (round-robin, snake order), or
-    // returns false.
-    long long round = 0;
-    const long long W = gridDim.x;
-    const long long nA = (long long)pre[kThreads] * p.Hkv;
-    const long long n_items = nA + (long long)p.S * p.Hkv;
-    auto finish = [&](Item& it) {
-        it.i = __builtin_amdgcn_readfirstlane(it.i);
-        it.g = __builtin_amdgcn_readfirstlane(it.g);
-        it.L = __builtin_amdgcn_readfirstlane(it.L);
-        it.t0 = __builtin_amdgcn_readfirstlane(it.t0);
-        it.t1 = __builtin_amdgcn_readfirstlane(it.t1);
-        it.n_chunks = __builtin_amdgcn_readfirstlane(it.n_chunks);
-        it.rec = __builtin_amdgcn_readfirstlane(it.rec);
-    };
-    auto fetch = [&](Item& it) -> bool {
-        const long long idx = round * W + ((round & 1) ? W - 1 - blockIdx.x : blockIdx.x);
-        if (idx >= n_items) return false;
-        ++round;
-        int part;
-        if (idx < nA) {
-            long long off;
-            it.g = (int)(idx % p.Hkv);
-            it.i = find_sequence(p, pre, idx / p.Hkv, 1,
-                                 [&](int s) { return max(n_parts(seq_len(s)) - 1, 0); }, off);
-            part = (int)off;
-        } else {
-            const long long b = idx - nA;
-            it.i = (int)(b / p.Hkv);
-            it.g = (int)(b - (long long)it.i * p.Hkv);
-            part = max(n_parts(seq_len(it.i)) - 1, 0);
-        }
-        it.L = seq_len(it.i);
-        it.t0 = part * p.part_tokens;
-        it.t1 = min(it.L, it.t0 + p.part_tokens);
-        it.n_chunks = it.L > 0 ? (it.t1 - it.t0 + 15) >> 4 : 0;
-        it.rec = it.L > p.part_tokens ? (it.i * p.Hkv + it.g) * p.n_part + part : -1;
-        finish(it);
-        return true;
-    };
-
-    Item cur;
-    if (!fetch(cur)) return;
-    int cid0, cid1;
-    load_ids<BS>(p, cur, wave, lane, 0, cid0, cid1);
-    while (true) {
-        Item nxt = cur;
-        const bool has_next = fetch(nxt);
-        int nid0 = 0, nid1 = 0;
-        if (cur.L <= 0) {                     // empty sequence (fixed partitions): zero rows
-            if (has_next) load_ids<BS>(p, nxt, wave, lane, 0, nid0, nid1);
-            for (int e = threadIdx.x; e < p.G * D; e += kThreads)
-                p.out[((size_t)cur.i * p.Hq + cur.g * p.G) * D + e] = 0.f;
-        } else {
-            attend_item<KV, D, BS>(p, smem, cur, cid0, cid1, has_next, nxt, nid0, nid1);
-        }
-        if (!has_next) break;
-        cur = nxt;
-        cid0 = nid0;
-        cid1 = nid1;
-    }
-}
-
-// Balanced split at wave granularity. Work positions run sequence-major, then
-// kv head, then position within the (sequence, kv head) segment: a segment of
-// n chunks has seg_cost + n positions, the first seg_cost standing for the
-// fixed cost of starting and finishing a segment (q, the epilogue, the partly
-// filled last chunk). The W = gridDim.x * kWaves waves each take one of W
-// near-equal contiguous ranges of positions and stream the chunks in them
-// without workgroup barriers. A piece of a segment that is the whole segment
-// writes its output rows; otherwise it writes record 2w (the piece that starts
-// wave w's chunks) or 2w + 1 (the piece that ends them). The wave that holds a
-// segment's first chunk writes the segment's descriptor (first record, record
-// count) for the merge kernel. Launched one workgroup per compute unit (one
-// wave per SIMD), so the kernel may use the whole register file.
-enum StreamMode { SM_DECODE = 0, SM_WINDOW = 1, SM_STEP = 2, SM_SHARED = 3 };
-
-template <int KV, int D, int BS, int MODE, int NT>
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1)))
-paged_attn_stream_kernel(AttnParams p) {
-    // SM_SHARED: group prefixes (a window of the group's queries, no causal
-    // mask) and member suffixes (decode, with the step's write) in one launch
-    constexpr bool SH = MODE == SM_SHARED;
-    constexpr bool MQ = MODE == SM_WINDOW || SH;   // several queries per sequence
-    static_assert(NT == 1 || MODE == SM_WINDOW, "several column tiles only for query windows");
-    constexpr bool STEP = MODE == SM_STEP || SH;   // this step's write fused in
-    constexpr int kSegCost = seg_cost(KV, D);
-    extern __shared__ float smem[];           // the length cache (p.cache_lens)
-    __shared__ int pre[kThreads + 1];
-    __shared__ int wsum[kWaves];
-    __shared__ int wmeta[kWaves][4][64];      // per wave: compacted chunk metadata of a window
-    __shared__ __align__(16) uint32_t ntstage[kWaves][D / 2];   // per wave: fp8 new-token codes
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int r16 = lane & 15;
-    const int j4 = lane >> 4;
-    const int G = p.G;
-    // segments per sequence: kv heads x query groups (one group when decoding)
-    const int n_qg = MQ ? p.n_qg : 1;
-    const int HS = p.Hkv * n_qg;
-    const int n_q = MQ ? p.n_q : 1;
-    int* sL = p.cache_lens ? reinterpret_cast<int*>(smem) : nullptr;
-    auto seq_len = [&](int s) { return sL ? sL[s] : clamped_len(p, s); };
-    auto is_sfx = [&](int s) { return SH && s >= p.n_pre; };      // a member suffix
-    auto table_row = [&](int s) -> const int32_t* {
-        if (is_sfx(s)) return p.tables2 + (size_t)(s - p.n_pre) * p.max_blocks2;
-        return p.tables + (size_t)s * p.max_blocks;
-    };
-    auto n_chunks_of = [&](int L) { return L > 0 ? (L + 15) >> 4 : 0; };
-    auto span_of = [&](int L) { return L > 0 ? kSegCost + ((L + 15) >> 4) : 0; };   // positions per segment
-    auto span = [&](int s) { return span_of(seq_len(s)); };
-
-    prefix_over_sequences(p, pre, wsum, sL, [&](int, int L) { return span_of(L); });
-    for (int s = blockIdx.x; s < p.S; s += gridDim.x)       // sequences with no tokens: zero rows
-        if (seq_len(s) <= 0) {
-            const bool sf = is_sfx(s);
-            const int rows = sf ? 1 : n_q;
-            float* ob = sf ? p.out2 + (size_t)(s - p.n_pre) * p.Hq * D : p.out + (size_t)s * n_q * p.Hq * D;
-            float* lb = sf ? p.lse2 + (size_t)(s - p.n_pre) * p.Hq : p.lse ? p.lse + (size_t)s * n_q * p.Hq : nullptr;
-            for (int e = threadIdx.x; e < rows * p.Hq * D; e += kThreads) ob[e] = 0.f;
-            if (lb)
-                for (int e = threadIdx.x; e < rows * p.Hq; e += kThreads) lb[e] = -INFINITY;
-        }
-
-    const unsigned V = (unsigned)pre[kThreads] * (unsigned)HS;   // positions in all
-    const unsigned W_all = gridDim.x * kWaves;
-    const unsigned w = blockIdx.x * kWaves + wave;
-    // A short input is cut into fewer, longer ranges (at least kMinPositions
-    // positions each), so that a merged row has fewer records; the waves past
-    // the last range only take part in the write.
-    const unsigned W = min(W_all, max(1u, (V + kMinPositions - 1) / kMinPositions));
-    const Split split(V, W);
-    const unsigned v_beg = w < W ? split.start(w) : V;
-    const unsigned v_end = w < W ? split.start(w + 1) : V;
-    const int n_pos = (int)(v_end - v_beg);
-
-    // Decode step: this wave's share of the write of every sequence's new token
-    // (position L - 1): part q = (sequence, kv head, K or V), parts w, w + W_all, ...
-    // Lane l handles channels l and l + 64. The reads are issued here and the
-    // stores after the first window's table reads have returned.
-    auto write_parts = [&](auto&& between) {
-        constexpr int NCH = D / 64;
-        const int n_tok = SH ? p.S - p.n_pre : p.S;  // sequences with a new token
-        const int n_parts = STEP && (!SH || p.k_new) ? n_tok * p.Hkv * 2 : 0;
-        for (int q0 = (int)w; q0 < n_parts; q0 += (int)W_all) {
-            const int i = q0 / (2 * p.Hkv);        // new token i (k_new/v_new row)
-            const int rem = q0 - i * 2 * p.Hkv;
-            const int g = rem >> 1;
-            const bool is_v = rem & 1;
-            const int sq = SH ? p.n_pre + i : i;     // its sequence
-            const int L = seq_len(sq);
-            if (L <= 0) continue;
-            const int pos = L - 1;
-            // an entry outside the pool (e.g. -1: no block appended) is
-            // skipped, as the separate write skips a slot outside the pool
-            const int raw = table_row(sq)[pos / BS];
-            const bool in_pool = raw >= 0 && raw < p.P;
-            const int b = min(max(raw, 0), p.P - 1);
-            const int o = pos % BS;
-            const size_t src_row = ((size_t)i * p.Hkv + g) * D;
-            uint32_t val[NCH];
-#pragma unroll
-            for (int u = 0; u < NCH; ++u) {
-                const int c = lane + 64 * u;
-                if constexpr (KV == KV_F32)
-                    val[u] = __float_as_uint(static_cast<const float*>(is_v ? p.v_new : p.k_new)[src_row + c]);
-                else
-                    val[u] = static_cast<const uint16_t*>(is_v ? p.v_new : p.k_new)[src_row + c];
-            }
-            if (q0 == (int)w) between();
-            if (!in_pool) continue;
-#pragma unroll
-            for (int u = 0; u < NCH; ++u) {
-                const int c = lane + 64 * u;
-                constexpr int VS = BS < 16 ? BS : 16;      // V sub-tiles of VS tokens
-                const size_t dst = is_v ? ((size_t)b * p.Hkv + g) * BS * D + (size_t)(o / VS) * VS * D +
-                                              (size_t)c * VS + o % VS
-                                        : (((size_t)b * p.Hkv + g) * BS + o) * D + c;
-                void* pool = const_cast<void*>(is_v ? p.v : p.k);
-                if constexpr (KV == KV_F32) static_cast<float*>(pool)[dst] = __uint_as_float(val[u]);
-                else if constexpr (KV == KV_BF16) static_cast<uint16_t*>(pool)[dst] = (uint16_t)val[u];
-                else static_cast<uint8_t*>(pool)[dst] =
-                         (uint8_t)e4m3_encode(bf16_bits_to_f32((uint16_t)val[u]) * (is_v ? p.v_inv : p.k_inv));
-            }
-        }
-    };
-    if (n_pos <= 0) {                         // no barriers below: waves are independent
-        if constexpr (STEP) write_parts([] {});
-        return;
-    }
-    // position v -> segment (i * HS + kv head * n_qg + query group) and chunk
-    // index (< 0: a cost position)
-    auto locate = [&](unsigned v, int& seg, int& kc, int& L) {
-        unsigned off;
-        const int i = find_sequence32(p, pre, v, (unsigned)HS, span, off);
-        L = seq_len(i);
-        const unsigned sp = (unsigned)span_of(L);
-        const unsigned g = off / sp;
-        seg = i * HS + (int)g;
-        kc = (int)(off - g * sp) - kSegCost;
-    };
-
-    // Chunk metadata of window kb (64 positions), compacted to the window's
-    // chunks: lane k holds the block ids, segment, chunk index and window
-    // offset of the window's k-th chunk; nw chunks in all. `fetch_window`
-    // locates the positions and starts the table reads (lane 63, when free,
-    // locates this wave's last position); `compact_window` uses their results.
-    int id0 = 0, id1 = 0, mseg = 0, mkc = 0, mvo = 0, nw = 0;
-    int a0 = 0, a1 = 0, a_seg = 0, a_kc = -1, a_nv = 0;
-    auto fetch_window = [&](int kb) {
-        a_nv = min(64, n_pos - kb);
-        a0 = 0; a1 = 0; a_seg = 0; a_kc = -1;
-        const bool in = lane < a_nv;
-        if (in || (kb == 0 && lane == 63)) {
-            int L;
-            locate(in ? v_beg + kb + lane : v_end - 1, a_seg, a_kc, L);
-            if (in && a_kc >= 0) {
-                const int i = a_seg / HS;
-                const int32_t* __restrict__ row = table_row(i);
-                const int tok = 16 * a_kc;
-                if constexpr (BS == 8) {
-                    a0 = row[tok / 8];
-                    a1 = tok + 8 < L ? row[tok / 8 + 1] : a0;
-                } else {
-                    a0 = row[tok / BS];
-                }
-            }
-        }
-    };
-    auto compact_window = [&]() {
-        const bool real = lane < a_nv && a_kc >= 0;
-        const unsigned long long mask = __builtin_amdgcn_ballot_w64(real);
-        const int dst = __builtin_amdgcn_mbcnt_hi((unsigned)(mask >> 32),
-                                                  __builtin_amdgcn_mbcnt_lo((unsigned)mask, 0u));
-        if (real) {
-            wmeta[wave][0][dst] = min(max(a0, 0), p.P - 1);
-            wmeta[wave][1][dst] = min(max(a1, 0), p.P - 1);
-            wmeta[wave][2][dst] = a_seg;
-            wmeta[wave][3][dst] = a_kc | (lane << 24);
-        }
-        nw = __builtin_popcountll(mask);
-        id0 = wmeta[wave][0][lane];
-        id1 = wmeta[wave][1][lane];
-        mseg = wmeta[wave][2][lane];
-        const int x = wmeta[wave][3][lane];
-        mkc = x & 0xFFFFFF;
-        mvo = x >> 24;
-    };
-    fetch_window(0);
-    bool window_done = false;
-    if constexpr (STEP) write_parts([&] { compact_window(); window_done = true; });
-    // this wave's last chunk: its last position, or the one before a trailing
-    // cost position
-    int last_seg, last_kc;
-    if (n_pos < 64) {
-        last_seg = __builtin_amdgcn_readlane(a_seg, 63);
-        last_kc = __builtin_amdgcn_readlane(a_kc, 63);
-    } else {
-        int L;
-        locate(v_end - 1, last_seg, last_kc, L);
-        last_seg = __builtin_amdgcn_readfirstlane(last_seg);
-        last_kc = __builtin_amdgcn_readfirstlane(last_kc);
-    }
-    const unsigned v_last = last_kc >= 0 ? v_end - 1 : v_end - 2 - (unsigned)(last_kc + kSegCost);
-
-    if (!window_done) compact_window();
-
-    // NT tiles of 16 MFMA columns share every loaded chunk (query windows:
-    // column c = 16t + r16 of tile t is query c / G of the group, head c % G)
-    using QF = typename QFragT<KV>::T;
-    QF qf[NT][q_loads<KV, D>()];
-    NewTok<KV, D> nt;                         // decode step: the segment's new token
-    f32x4 o[NT][D / 16];
-    float m_run[NT], l_run[NT];
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-#pragma unroll
-        for (int s = 0; s < D / 16; ++s) o[t][s] = f32x4{0.f, 0.f, 0.f, 0.f};
-        m_run[t] = -INFINITY;
-        l_run[t] = 0.f;
-    }
-    // this lane's column in tile t is query col_j[t] of its query group and
-    // head col_r[t] of the kv head's G (the same for every segment)
-    int col_j[NT], col_r[NT];
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-        const int c = 16 * t + r16;
-        col_j[t] = MQ ? c / G : 0;
-        col_r[t] = MQ ? c - col_j[t] * G : r16;
-    }
-    bool started = false;                     // this wave has begun its first chunk
-    bool seg_from_start = false;              // the current segment began at its chunk 0
-    bool seg_at_range_start = false;          // ... and at this wave's first chunk
-
-    for (int kb = 0; kb < n_pos; kb += 64) {
-        if (kb > 0) {
-            fetch_window(kb);
-            compact_window();
-        }
-        if (nw == 0) continue;
-        auto issue = [&](Frag<KV, D>& f, int k) {
-            __builtin_amdgcn_sched_barrier(0);
-            const int b0 = __builtin_amdgcn_readlane(id0, k);
-            const int b1 = BS == 8 ? __builtin_amdgcn_readlane(id1, k) : b0;
-            const int seg = __builtin_amdgcn_readlane(mseg, k);
-            const int kc = __builtin_amdgcn_readlane(mkc, k);
-            const int g = (seg % HS) / n_qg;
-            load_chunk<KV, D, BS>(f, p, b0, b1, 16 * kc, g, r16, j4);
-            __builtin_amdgcn_sched_barrier(0);
-        };
-        auto step = [&](Frag<KV, D>& f, int k) {
-            const int seg = __builtin_amdgcn_readlane(mseg, k);
-            const int kc = __builtin_amdgcn_readlane(mkc, k);
-            const unsigned v = v_beg + kb + __builtin_amdgcn_readlane(mvo, k);
-            const int i = seg / HS;
-            const int g2 = seg - i * HS;
-            const int g = g2 / n_qg;
-            const int qg = g2 - g * n_qg;
-            const int L = __builtin_amdgcn_readfirstlane(seq_len(i));
-            const int nch = n_chunks_of(L);
-            const bool sfx = is_sfx(i);
-            // this lane's column in tile t: query j[t] of the window, head g*G + r;
-            // out_row[t] is also the q row's offset (q and out share their row order)
-            int j[NT];
-            bool live[NT];
-            size_t out_row[NT];
-#pragma unroll
-            for (int t = 0; t < NT; ++t) {
-                const int c = 16 * t + r16;
-                j[t] = qg * (MQ ? p.qgs : 1) + col_j[t];
-                live[t] = c < (MQ ? p.cols : G) && j[t] < (sfx ? 1 : n_q);
-                const size_t row = sfx ? (size_t)(i - p.n_pre) : (size_t)i * n_q + j[t];
-                out_row[t] = (row * p.Hq + g * G + col_r[t]) * D;
-            }
-            float* const obase = sfx ? p.out2 : p.out;
-            float* const lbase = sfx ? p.lse2 : p.lse;
-            const bool first = !started;
-            started = true;
-            if (kc == 0 || first) {               // a segment starts
-#pragma unroll
-                for (int t = 0; t < NT; ++t) load_q_row<KV, D>(p, out_row[t], live[t], j4, qf[t]);
-                if constexpr (STEP)
-                    if (!SH || (sfx && p.k_new))
-                        load_new_token<KV, D>(p, ((size_t)(SH ? i - p.n_pre : i) * p.Hkv + g) * D, r16, j4,
-                                              ntstage[wave], nt);
-                seg_from_start = kc == 0;
-                seg_at_range_start = first;
-                if (kc == 0 && lane == 0) {       // descriptor for the merge kernel
-                    const unsigned w_hi = split.owner(v + nch - 1);
-                    p.desc[2 * seg] = (int)(2 * w + (first ? 0 : 1));
-                    p.desc[2 * seg + 1] = (int)(w_hi - w + 1);
-                }
-            }
-            const int tc = 16 * kc;
-            // the write of position L - 1 runs concurrently: take its value
-            // from the new token instead of the pool
-            const bool patch = STEP && kc == nch - 1 && (!SH || (sfx && p.k_new));
-            // fp8 V rows are moved to their lanes only before the P.V, so their
-            // patch waits until then; other caches patch K and V here
-            constexpr bool kVRows = KV == KV_FP8 && BS >= 16;
-            if constexpr (STEP)
-                if (patch) {
-                    patch_new_k<KV, D>(f, nt, L - 1 - tc, r16);
-                    if constexpr (!kVRows) patch_new_v<KV, D>(f, nt, L - 1 - tc, j4);
-                }
-            const bool tail = tc + 16 > L;        // tokens >= L hold no data
-            // query j sees tokens < L - n_q + 1 + j (causal inside the window)
-            const bool masked = MQ && p.causal ? tc + 16 > L - n_q + 1 : tail;
-            const int first_tok = tc + 4 * j4;
-#pragma unroll
-            for (int t = 0; t < NT; ++t) {
-                const f32x4 sc = chunk_scores<KV, D>(f, qf[t]);
-                const int lim = MQ && p.causal ? L - n_q + 1 + j[t] : L;
-                float x[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    x[e] = sc[e] * p.qk_scale;
-                    if (masked && first_tok + e >= lim) x[e] = -INFINITY;
-                }
-                const float cm = head_max(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
-                float m_new = fmaxf(m_run[t], cm);
-                // a column that has seen no visible token yet keeps m = -inf;
-                // its exponentials are taken against 0 so they stay 0, not NaN
-                const float m_ref = MQ && m_new == -INFINITY ? 0.f : m_new;
-                const float alpha = __builtin_amdgcn_exp2f(m_run[t] - m_ref);
-                float pr[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) pr[e] = __builtin_amdgcn_exp2f(x[e] - m_ref);
-                l_run[t] = l_run[t] * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
-                m_run[t] = m_new;
-                if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
-#pragma unroll
-                    for (int s = 0; s < D / 16; ++s) o[t][s] *= alpha;
-                }
-                if constexpr (kVRows)
-                    if (t == 0) {                 // V is first needed here
-                        v_rows_to_operand<KV, D, BS>(f);
-                        if constexpr (STEP)
-                            if (patch) patch_new_v<KV, D>(f, nt, L - 1 - tc, j4);
-                    }
-                chunk_pv<KV, D>(f, pr, o[t], tail, first_tok, L);
-            }
-
-            if (kc == nch - 1 || v == v_last) {   // the segment ends here for this wave
-                const bool whole = seg_from_start && kc == nch - 1;
-                const int C = MQ ? p.cols : G;
-#pragma unroll
-                for (int t = 0; t < NT; ++t) {
-                    const float l_tot = head_sum(l_run[t]);
-                    if (live[t]) {
-                        if (whole) {
-                            const float sc_o = p.v_scale / l_tot;
-                            float* orow = obase + out_row[t] + 4 * j4;
-#pragma unroll
-                            for (int s = 0; s < D / 16; ++s)
-                                *reinterpret_cast<f32x4*>(orow + 16 * s) = o[t][s] * sc_o;
-                            if (lbase && j4 == 0) lbase[out_row[t] / D] = m_run[t] + __log2f(l_tot);
-                        } else {
-                            const size_t rr = (size_t)(2 * w + (seg_at_range_start ? 0 : 1)) * C + 16 * t + r16;
-                            const size_t nrec = (size_t)p.n_rec;
-                            float* orec = p.ws + rr * D + 4 * j4;
-#pragma unroll
-                            for (int s = 0; s < D / 16; ++s)
-                                *reinterpret_cast<f32x4*>(orec + 16 * s) = o[t][s] * p.v_scale;
-                            if (j4 == 0) {
-                                p.ws[nrec * C * D + rr] = m_run[t];
-                                p.ws[nrec * C * (D + 1) + rr] = l_tot;
-                            }
-                        }
-                    }
-#pragma unroll
-                    for (int s = 0; s < D / 16; ++s) o[t][s] = f32x4{0.f, 0.f, 0.f, 0.f};
-                    m_run[t] = -INFINITY;
-                    l_run[t] = 0.f;
-                }
-            }
-        };
-        Frag<KV, D> fa, fb;
-        issue(fa, 0);
-        int k = 0;
-        for (; k + 2 < nw; k += 2) {
-            issue(fb, k + 1);
-            step(fa, k);
-            issue(fa, k + 2);
-            step(fb, k + 1);
-        }
-        if (k + 1 < nw) {
-            issue(fb, k + 1);
-            step(fa, k);
-            step(fb, k + 1);
-        } else {
-            step(fa, k);
         }
     }
 }
@@ -1699,51 +463,15 @@ shared_prefix_merge_kernel(AttnParams a, AttnParams b, float* __restrict__ out, 
 // Dispatch
 // ----------------------------------------------------------------------------
 
-using AttnKernel = void (*)(AttnParams);
-
-template <int KV, int D>
-AttnKernel pick_bs(int bs) {
-    switch (bs) {
-        case 8: return paged_attn_partition_kernel<KV, D, 8>;
-        case 16: return paged_attn_partition_kernel<KV, D, 16>;
-        case 32: return paged_attn_partition_kernel<KV, D, 32>;
-        case 64: return paged_attn_partition_kernel<KV, D, 64>;
-        case 128: return paged_attn_partition_kernel<KV, D, 128>;
-    }
-    return nullptr;
-}
-
-template <int KV>
-AttnKernel pick_d(int d, int bs) {
-    return d == 64 ? pick_bs<KV, 64>(bs) : pick_bs<KV, 128>(bs);
-}
-
-template <int KV, int D, int MODE, int NT>
-AttnKernel pick_stream_bs(int bs) {
-    switch (bs) {
-        case 8: return paged_attn_stream_kernel<KV, D, 8, MODE, NT>;
-        case 16: return paged_attn_stream_kernel<KV, D, 16, MODE, NT>;
-        case 32: return paged_attn_stream_kernel<KV, D, 32, MODE, NT>;
-        case 64: return paged_attn_stream_kernel<KV, D, 64, MODE, NT>;
-        case 128: return paged_attn_stream_kernel<KV, D, 128, MODE, NT>;
-    }
-    return nullptr;
-}
-
-// tiles: 16-column MFMA tiles per pass (query windows: 1 or wide_tiles(d))
-template <int KV>
-AttnKernel pick_stream(int d, int bs, int mode, int tiles) {
-    if (mode == SM_WINDOW) {
-        if (tiles == 1)
-            return d == 64 ? pick_stream_bs<KV, 64, SM_WINDOW, 1>(bs) : pick_stream_bs<KV, 128, SM_WINDOW, 1>(bs);
-        return d == 64 ? pick_stream_bs<KV, 64, SM_WINDOW, wide_tiles(64)>(bs)
-                       : pick_stream_bs<KV, 128, SM_WINDOW, wide_tiles(128)>(bs);
-    }
-    if (mode == SM_STEP)
-        return d == 64 ? pick_stream_bs<KV, 64, SM_STEP, 1>(bs) : pick_stream_bs<KV, 128, SM_STEP, 1>(bs);
-    if (mode == SM_SHARED)
-        return d == 64 ? pick_stream_bs<KV, 64, SM_SHARED, 1>(bs) : pick_stream_bs<KV, 128, SM_SHARED, 1>(bs);
-    return d == 64 ? pick_stream_bs<KV, 64, SM_DECODE, 1>(bs) : pick_stream_bs<KV, 128, SM_DECODE, 1>(bs);
+// The instantiations live in attn_inst.hip, one translation unit per (cache
+// type, head dim).
+AttnKernel pick(int kv, int d, int bs, int mode, int tiles, bool partition) {
+    if (kv == KV_F32) return d == 64 ? pick_kernel<KV_F32, 64>(bs, mode, tiles, partition)
+                                     : pick_kernel<KV_F32, 128>(bs, mode, tiles, partition);
+    if (kv == KV_BF16) return d == 64 ? pick_kernel<KV_BF16, 64>(bs, mode, tiles, partition)
+                                      : pick_kernel<KV_BF16, 128>(bs, mode, tiles, partition);
+    return d == 64 ? pick_kernel<KV_FP8, 64>(bs, mode, tiles, partition)
+                   : pick_kernel<KV_FP8, 128>(bs, mode, tiles, partition);
 }
 
 // Compute units of the current device (cached per device).
@@ -2004,12 +732,10 @@ pkv_status attn_launch(const char* fn, float* out, const void* q, const void* k_
     if (balanced) {
         const int mode = is_step ? SM_STEP : n_q > 1 ? SM_WINDOW : SM_DECODE;
         const int tiles = mode == SM_WINDOW ? qgr.tiles : 1;
-        kern = kv == KV_F32 ? pick_stream<KV_F32>(d, bs, mode, tiles)
-             : kv == KV_BF16 ? pick_stream<KV_BF16>(d, bs, mode, tiles) : pick_stream<KV_FP8>(d, bs, mode, tiles);
+        kern = pick(kv, d, bs, mode, tiles, false);
         lds = (size_t)(prm.cache_lens ? S : 0) * sizeof(int);
     } else {
-        kern = kv == KV_F32 ? pick_d<KV_F32>(d, bs)
-             : kv == KV_BF16 ? pick_d<KV_BF16>(d, bs) : pick_d<KV_FP8>(d, bs);
+        kern = pick(kv, d, bs, SM_DECODE, 1, true);
         lds = (size_t)(2 * kWaves * 16 + kWaves * G * d + (prm.cache_lens ? S : 0)) * sizeof(float);
     }
     auto st = static_cast<hipStream_t>(stream);
@@ -2339,9 +1065,7 @@ extern "C" pkv_status pkv_paged_shared_prefix_decode(
                                                kSegCostMax);
         if (n_upper > 0x7FFFFFFFLL) return fail(PKV_E_INVALID, "%s: too many work items", fn);
         const int kv = cache_dtype == PKV_F32 ? KV_F32 : cache_dtype == PKV_BF16 ? KV_BF16 : KV_FP8;
-        AttnKernel kern = kv == KV_F32 ? pick_stream<KV_F32>(d, bs, SM_SHARED, 1)
-                        : kv == KV_BF16 ? pick_stream<KV_BF16>(d, bs, SM_SHARED, 1)
-                                        : pick_stream<KV_FP8>(d, bs, SM_SHARED, 1);
+        AttnKernel kern = pick(kv, d, bs, SM_SHARED, 1, false);
         AttnParams prm{};
         prm.out = out_a;
         prm.lse = lse_a;

@@ -20,14 +20,17 @@ def test_more_than_one_gpu_is_refused_with_a_message():
 
 
 def test_recorded_traffic_follows_the_kernel_source(monkeypatch, tmp_path):
-    import hashlib
     got = bench.measured_traffic("llama8b", "bf16", 16, -1, "fused")
     m = bench.MEASURED_TRAFFIC[("llama8b", "bf16", 16, -1, "fused")]
     want = int(round(1024 * (m["fetch_kib"] * m["fetch_scale"] + m["write_kib"] * m["write_scale"])))
-    same = hashlib.sha256(open(bench.DEVICE_SOURCE, "rb").read()).hexdigest() == m["source_sha256"]
+    same = bench.device_source_sha256() == m["source_sha256"]
     assert got == (want if same else None)
-    other = tmp_path / "device.hip"
-    other.write_bytes(open(bench.DEVICE_SOURCE, "rb").read() + b"\n")
-    monkeypatch.setattr(bench, "DEVICE_SOURCE", str(other))
-    assert bench.measured_traffic("llama8b", "bf16", 16, -1, "fused") is None    # any edit voids it
+    # an edit of any device source voids the recorded figure
+    for k in range(len(bench.DEVICE_SOURCES)):
+        paths = list(bench.DEVICE_SOURCES)
+        other = tmp_path / f"edited_{k}"
+        other.write_bytes(open(paths[k], "rb").read() + b"\n")
+        paths[k] = str(other)
+        monkeypatch.setattr(bench, "DEVICE_SOURCES", paths)
+        assert bench.measured_traffic("llama8b", "bf16", 16, -1, "fused") is None
     assert bench.measured_traffic("small", "bf16", 16, -1, "fused") is None       # never measured
