@@ -210,6 +210,67 @@ pkv_status pkv_paged_decode_step(float* out, const void* q, const void* k_new, c
                                  void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Planned decode step. The balanced split of pkv_paged_decode_step (the
+ * decode attention work cut into equal cost-weighted ranges, one per wave)
+ * depends only on the context lengths, so a caller that holds them on the
+ * host -- as the scheduler does when it builds the block tables and the slot
+ * mapping ("03 · PagedAttention", "Blocks and block tables") -- can compute it
+ * there, once per step, with pkv_build_paged_decode_plan. The planned kernel
+ * then reads each wave's chunk list from the plan instead of scanning the
+ * lengths and searching its positions on the device, and the merge reads the
+ * plan's descriptors. It still walks the block tables, gathers every K/V
+ * tile and writes the new tokens, and its result is that of
+ * pkv_paged_decode_step (or, without new tokens, pkv_paged_decode_attn with
+ * the balanced split), bit for bit.
+ *
+ * pkv_paged_decode_plan_workers: the number of waves the planned kernel runs
+ * on the current device for this head dim, block size and cache type (the
+ * plan is built for it); -1 on an invalid argument or a failed device query.
+ */
+int32_t pkv_paged_decode_plan_workers(int32_t d, int32_t bs, pkv_dtype cache_dtype);
+
+/*
+ * Build the plan on the host. context_lens: host int32 [S], the same lengths
+ * the call passes on the device (clamped to max_context_len as the kernels
+ * clamp them); n_workers from pkv_paged_decode_plan_workers. plan: caller-
+ * owned host memory of plan_bytes; *plan_bytes_needed (when not NULL) gets
+ * the size the plan needs, and a call with plan NULL or too small returns
+ * PKV_E_WORKSPACE after setting it. The plan is int32 words: a 16-word header
+ * (magic "PKVP", version, n_workers, waves used, S, Hkv, segment cost, entries
+ * per wave, max_context_len, d, cache kind), then per wave its chunk entries
+ * {sequence, kv head | flags << 16, chunk index, L} (unused: sequence -1),
+ * then one (first record, record count) descriptor per (sequence, kv head).
+ * Requires S > 0, Hkv > 0, d in {64, 128}, n_workers > 0.
+ */
+pkv_status pkv_build_paged_decode_plan(const int32_t* context_lens, int32_t S, int32_t Hkv, int32_t d,
+                                       pkv_dtype cache_dtype, int32_t max_context_len, int32_t n_workers,
+                                       void* plan, size_t plan_bytes, size_t* plan_bytes_needed);
+
+/* Workspace bytes of a planned call: 2 * n_workers * (Hq/Hkv) * (d + 2) * 4,
+ * rounded up to a multiple of 256 (the partial records); 0 for invalid sizes. */
+size_t pkv_paged_decode_plan_workspace_size(int32_t n_workers, int32_t Hq, int32_t Hkv, int32_t d);
+
+/*
+ * The planned step. Arguments as for pkv_paged_decode_step, plus the plan:
+ * plan_host (its host copy; only the header is read, to check that it was
+ * built for these S, Hkv, d, cache type and max_context_len and for this
+ * device's wave count) and plan_dev (a device copy of all plan_bytes, read by
+ * the kernels; the caller uploads it). k_new and v_new may both be NULL: the
+ * attention alone, with no write. Contents of the workspace on entry do not
+ * matter; calls that overlap in time must not share it.
+ */
+pkv_status pkv_paged_decode_step_planned(float* out, const void* q, const void* k_new, const void* v_new,
+                                         void* k_cache, void* v_cache,
+                                         const int32_t* block_tables, const int32_t* context_lens,
+                                         int32_t S, int32_t Hq, int32_t Hkv, int32_t d, int32_t bs,
+                                         int32_t P, int32_t max_blocks, int32_t max_context_len,
+                                         float softmax_scale, float k_scale, float v_scale,
+                                         float k_inv_scale, float v_inv_scale,
+                                         pkv_dtype q_dtype, pkv_dtype cache_dtype,
+                                         const void* plan_host, const void* plan_dev, size_t plan_bytes,
+                                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * pkv_paged_decode_step for callers that cannot allocate device memory (code
  * under HIP graph capture, tight serving loops, harnesses that forbid
  * hipMalloc): the same step, the same kernels and the same result as

@@ -16,6 +16,7 @@ from ._lib import (lib, check, PkvError, PkvStats, PKV_F32, PKV_BF16, PKV_FP8_E4
 
 __all__ = [
     "kv_cache_write", "copy_blocks", "paged_decode_attn", "paged_decode_step", "paged_decode_step_noalloc",
+    "paged_decode_plan_workers", "build_paged_decode_plan", "paged_decode_step_planned", "DecodePlan",
     "paged_decode_attn_workspace_size",
     "paged_decode_attn_workspace", "paged_multi_query_attn", "paged_multi_query_attn_workspace",
     "Allocator",
@@ -247,6 +248,86 @@ def paged_decode_step_noalloc(out, q, k_new, v_new, k_cache, v_cache, block_tabl
         _dev(context_lens, "context_lens"), S, Hq, Hkv, d, bs, P, block_tables.shape[1],
         int(max_context_len), float(softmax_scale), float(k_scale), float(v_scale),
         float(k_inv_scale), float(v_inv_scale), _dtype_code(q), _dtype_code(k_cache), _stream(stream)))
+
+
+def paged_decode_plan_workers(d, bs, cache_dtype_code):
+    """pkv_paged_decode_plan_workers: waves of the planned kernel's grid on the
+    current device (the plan is built for this many)."""
+    n = int(lib().pkv_paged_decode_plan_workers(d, bs, cache_dtype_code))
+    if n <= 0:
+        raise PkvError(PKV_E_INVALID, f"paged_decode_plan_workers: no grid for d={d} bs={bs}")
+    return n
+
+
+def build_paged_decode_plan(context_lens, Hkv, d, cache_dtype_code, max_context_len, n_workers):
+    """pkv_build_paged_decode_plan on host lengths: the plan as an int32 numpy array."""
+    lens = _i32(context_lens)
+    S = len(lens)
+    need = ctypes.c_size_t(0)
+    st = lib().pkv_build_paged_decode_plan(_ptr(lens, P_i32), S, Hkv, d, cache_dtype_code, int(max_context_len),
+                                           int(n_workers), None, 0, ctypes.byref(need))
+    if st not in (PKV_OK, 2):                  # 2: PKV_E_WORKSPACE, the size query
+        check(st)
+    plan = np.zeros(need.value // 4, dtype=np.int32)
+    check(lib().pkv_build_paged_decode_plan(_ptr(lens, P_i32), S, Hkv, d, cache_dtype_code, int(max_context_len),
+                                            int(n_workers), plan.ctypes.data_as(c_vp), plan.nbytes,
+                                            ctypes.byref(need)))
+    return plan
+
+
+def paged_decode_step_planned(out, q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, *,
+                              max_context_len, softmax_scale, plan_host, plan_dev, workspace, k_scale=1.0,
+                              v_scale=1.0, k_inv_scale=1.0, v_inv_scale=1.0, stream=None):
+    """pkv_paged_decode_step_planned. plan_host: the int32 numpy plan; plan_dev:
+    its device copy (int32 tensor); k_new/v_new None for attention alone."""
+    import torch
+    P, Hkv, bs, d = _pools("paged_decode_step_planned", k_cache, v_cache)
+    S, Hq = _attn_args("paged_decode_step_planned", out, q, k_cache, block_tables, context_lens, d)
+    if (k_new is None) != (v_new is None):
+        raise ValueError("paged_decode_step_planned: give both k_new and v_new, or neither")
+    if k_new is not None:
+        if tuple(k_new.shape) != (S, Hkv, d) or tuple(v_new.shape) != (S, Hkv, d):
+            raise ValueError("paged_decode_step_planned: k_new/v_new must be [S][Hkv][d]")
+        _src_dtype_ok("paged_decode_step_planned", "k_new", k_new, k_cache)
+        _src_dtype_ok("paged_decode_step_planned", "v_new", v_new, k_cache)
+    plan_host = np.ascontiguousarray(plan_host, dtype=np.int32)
+    if plan_dev.dtype != torch.int32 or plan_dev.numel() != plan_host.size:
+        raise ValueError("paged_decode_step_planned: plan_dev must be the int32 device copy of plan_host")
+    _one_device("paged_decode_step_planned", out, q, k_new, v_new, k_cache, v_cache, block_tables, context_lens,
+                plan_dev, workspace)
+    check(lib().pkv_paged_decode_step_planned(
+        _dev(out, "out"), _dev(q, "q"), _dev(k_new, "k_new") if k_new is not None else None,
+        _dev(v_new, "v_new") if v_new is not None else None, _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+        _dev(block_tables, "block_tables"), _dev(context_lens, "context_lens"), S, Hq, Hkv, d, bs, P,
+        block_tables.shape[1], int(max_context_len), float(softmax_scale), float(k_scale), float(v_scale),
+        float(k_inv_scale), float(v_inv_scale), _dtype_code(q), _dtype_code(k_cache),
+        plan_host.ctypes.data_as(c_vp), _dev(plan_dev, "plan_dev"), plan_host.nbytes,
+        _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+class DecodePlan:
+    """A decode step's work plan: built on the host from the host lengths (as
+    the block tables are), uploaded once, with the workspace it needs. Holds
+    while the lengths do: the next step (one more token per sequence) needs a
+    new plan. __call__ runs pkv_paged_decode_step_planned."""
+
+    def __init__(self, context_lens, *, Hq, Hkv, d, bs, cache_dtype_code, max_context_len, device="cuda"):
+        import torch
+        self.n_workers = paged_decode_plan_workers(d, bs, cache_dtype_code)
+        self.max_context_len = int(max_context_len)
+        self.host = build_paged_decode_plan(context_lens, Hkv, d, cache_dtype_code, self.max_context_len,
+                                            self.n_workers)
+        self.dev = torch.from_numpy(self.host).to(device)
+        need = int(lib().pkv_paged_decode_plan_workspace_size(self.n_workers, Hq, Hkv, d))
+        self.workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
+
+    def __call__(self, out, q, k_cache, v_cache, block_tables, context_lens, *, softmax_scale, k_new=None,
+                 v_new=None, k_scale=1.0, v_scale=1.0, k_inv_scale=1.0, v_inv_scale=1.0, stream=None):
+        paged_decode_step_planned(out, q, k_new, v_new, k_cache, v_cache, block_tables, context_lens,
+                                  max_context_len=self.max_context_len, softmax_scale=softmax_scale,
+                                  plan_host=self.host, plan_dev=self.dev, workspace=self.workspace,
+                                  k_scale=k_scale, v_scale=v_scale, k_inv_scale=k_inv_scale,
+                                  v_inv_scale=v_inv_scale, stream=stream)
 
 
 def paged_multi_query_attn_workspace(S, n_q, Hq, Hkv, d, device="cuda"):

@@ -40,6 +40,8 @@ def _run(cmd, verbose):
 # The attention kernels are instantiated once per (cache type, head dim) in
 # attn_inst.hip, each its own translation unit: 0/1/2 = f32/bf16/fp8 caches.
 INSTANCES = [(kv, d) for kv in (0, 1, 2) for d in (64, 128)]
+# host code (g++): the allocator, builders and hashes; the decode work plan
+HOST_SOURCES = ["host.cpp", "plan.cpp"]
 
 
 def build(verbose=False, out=LIB, extra_hip_flags=(), jobs=None):
@@ -49,10 +51,12 @@ def build(verbose=False, out=LIB, extra_hip_flags=(), jobs=None):
     cxx = os.environ.get("CXX", shutil.which("g++") or "g++")
     jobs = jobs or min(8, os.cpu_count() or 1, int(os.environ.get("MAX_JOBS", "8")))
     with tempfile.TemporaryDirectory(prefix="pkv_build_") as tmp:
-        host_o = os.path.join(tmp, "host.o")
-        cmds = [[cxx, "-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-I", INCLUDE, "-c",
-                 os.path.join(CSRC, "host.cpp"), "-o", host_o]]
-        objs = [host_o]
+        cmds, objs = [], []
+        for name in HOST_SOURCES:
+            o = os.path.join(tmp, name.replace(".cpp", ".o"))
+            cmds.append([cxx, "-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-I", INCLUDE, "-c",
+                         os.path.join(CSRC, name), "-o", o])
+            objs.append(o)
         for kv, d in INSTANCES:
             o = os.path.join(tmp, f"attn_{kv}_{d}.o")
             cmds.append([hipcc, *HIP_FLAGS, *extra_hip_flags, f"-DPKV_INST_KV={kv}", f"-DPKV_INST_D={d}",
@@ -63,7 +67,7 @@ def build(verbose=False, out=LIB, extra_hip_flags=(), jobs=None):
                      os.path.join(CSRC, "device.hip"), "-o", dev_o])
         objs.append(dev_o)
         # the longest compiles first
-        cmds = cmds[1:] + cmds[:1]
+        cmds = cmds[len(HOST_SOURCES):] + cmds[:len(HOST_SOURCES)]
         with ThreadPoolExecutor(max_workers=jobs) as ex:
             for f in [ex.submit(_run, c, verbose) for c in cmds]:
                 f.result()
@@ -74,7 +78,8 @@ def build(verbose=False, out=LIB, extra_hip_flags=(), jobs=None):
     return out
 
 
-# The host part alone (allocator, table and slot builders, hashes), built with
+# The host part alone (allocator, table and slot builders, hashes, the decode
+# work plan), built with
 # AddressSanitizer and UndefinedBehaviorSanitizer for CPU test runs. It is
 # loaded with PKV_LIB pointing at it, PKV_HOST_ONLY=1 and the sanitizer
 # runtimes preloaded (see tests/test_host_sanitizers.py). No device code is in it.
@@ -85,7 +90,7 @@ SAN_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",
 def build_host_sanitized(out, verbose=False):
     cxx = os.environ.get("CXX", shutil.which("g++") or "g++")
     _run([cxx, *SAN_FLAGS, "-std=c++17", "-fPIC", "-shared", "-Wall", "-Wextra", "-I", INCLUDE,
-          os.path.join(CSRC, "host.cpp"), "-o", out], verbose)
+          *[os.path.join(CSRC, n) for n in HOST_SOURCES], "-o", out], verbose)
     return out
 
 

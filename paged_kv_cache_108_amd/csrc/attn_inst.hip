@@ -57,4 +57,18 @@ AttnKernel pick_kernel(int bs, int mode, int tiles, bool partition) {
 
 template AttnKernel pick_kernel<PKV_INST_KV, PKV_INST_D>(int, int, int, bool);
 
+template <int KV, int D>
+AttnKernel pick_plan_kernel(int bs, bool step) {
+    switch (bs) {
+        case 8: return step ? paged_attn_plan_kernel<KV, D, 8, true> : paged_attn_plan_kernel<KV, D, 8, false>;
+        case 16: return step ? paged_attn_plan_kernel<KV, D, 16, true> : paged_attn_plan_kernel<KV, D, 16, false>;
+        case 32: return step ? paged_attn_plan_kernel<KV, D, 32, true> : paged_attn_plan_kernel<KV, D, 32, false>;
+        case 64: return step ? paged_attn_plan_kernel<KV, D, 64, true> : paged_attn_plan_kernel<KV, D, 64, false>;
+        case 128: return step ? paged_attn_plan_kernel<KV, D, 128, true> : paged_attn_plan_kernel<KV, D, 128, false>;
+    }
+    return nullptr;
+}
+
+template AttnKernel pick_plan_kernel<PKV_INST_KV, PKV_INST_D>(int, bool);
+
 }  // namespace pkv_dev

@@ -13,6 +13,8 @@
 #include <cstdint>
 #include <type_traits>
 
+#include "split.h"
+
 namespace pkv_dev {
 
 
@@ -27,10 +29,7 @@ constexpr int kWaves = PKV_WAVES;         // waves per workgroup
 constexpr int kThreads = kWaves * 64;
 constexpr int kMaxCachedLens = 4096;      // sequences whose lengths a workgroup keeps in LDS
 constexpr int kMaxWorkers = 4096;         // waves of the balanced split, at most (sizes its workspace)
-#ifndef PKV_MIN_POS
-#define PKV_MIN_POS 4
-#endif
-constexpr unsigned kMinPositions = PKV_MIN_POS;   // balanced split: positions per wave, at least
+using pkv_split::kMinPositions;          // balanced split: positions per wave, at least (split.h)
 constexpr int kMergeBatch = 32;           // records per round trip for rows that merge 32 or more
 // 16-column tiles per pass for wide query windows. Each tile adds its own
 // q fragment, accumulator and softmax to every chunk: four tiles at d 128
@@ -40,14 +39,10 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 enum KvKind { KV_F32 = 0, KV_BF16 = 1, KV_FP8 = 2 };
 
-// Balanced split: positions a segment costs beyond its chunks. Starting and
-// finishing a segment costs about one memory round trip, which is one chunk
-// time for 8 KiB chunks (bf16 at d 128) and proportionally more chunks for
-// smaller ones.
-__host__ __device__ constexpr int seg_cost(int kv, int d) {
-    const int chunk_bytes = 16 * 2 * d * (kv == KV_F32 ? 4 : kv == KV_BF16 ? 2 : 1);
-    return chunk_bytes >= 8192 ? 1 : 8192 / chunk_bytes;
-}
+// Balanced split: positions a segment costs beyond its chunks (split.h).
+using pkv_split::seg_cost;
+static_assert(KV_F32 == pkv_split::kKvF32 && KV_BF16 == pkv_split::kKvBf16 && KV_FP8 == pkv_split::kKvFp8,
+              "cache kinds numbered as in split.h");
 constexpr int kSegCostMax = seg_cost(KV_FP8, 64);
 
 // ----------------------------------------------------------------------------
@@ -146,6 +141,10 @@ struct AttnParams {
     int max_blocks2, max_len2;
     float* out2;
     float* lse2;
+    // Planned calls: each wave's chunk entries (see split.h), plan_stride
+    // entries per wave; the merge reads the plan's descriptors (desc)
+    const int32_t* plan;
+    int plan_stride;
 };
 
 // Clamped context length of sequence s (of either table set).
@@ -746,17 +745,8 @@ __device__ __forceinline__ int find_sequence(const AttnParams& p, const int* pre
 }
 
 // Balanced split, in 32-bit arithmetic (the launcher keeps every position
-// below 2^31): n positions cut into W ranges, range w being
-// [start(w), start(w + 1)) with the first n % W ranges one longer.
-struct Split {
-    unsigned q, r;
-    __device__ Split(unsigned n, unsigned W) : q(n / W), r(n % W) {}
-    __device__ unsigned start(unsigned w) const { return w * q + min(w, r); }
-    __device__ unsigned owner(unsigned c) const {
-        const unsigned big = r * (q + 1);
-        return c < big ? c / (q + 1) : r + (c - big) / q;
-    }
-};
+// below 2^31): see split.h.
+using pkv_split::Split;
 
 // find_sequence for positions below 2^31.
 template <typename F>
@@ -930,7 +920,7 @@ paged_attn_stream_kernel(AttnParams p) {
     // A short input is cut into fewer, longer ranges (at least kMinPositions
     // positions each), so that a merged row has fewer records; the waves past
     // the last range only take part in the write.
-    const unsigned W = min(W_all, max(1u, (V + kMinPositions - 1) / kMinPositions));
+    const unsigned W = pkv_split::waves_used(V, W_all);
     const Split split(V, W);
     const unsigned v_beg = w < W ? split.start(w) : V;
     const unsigned v_end = w < W ? split.start(w + 1) : V;
@@ -1001,6 +991,27 @@ paged_attn_stream_kernel(AttnParams p) {
         seg = i * HS + (int)g;
         kc = (int)(off - g * sp) - kSegCost;
     };
+    // locate for positions v >= v0 of one window, v0 the same in every lane:
+    // one search for v0 (every lane reads the same LDS words), then each lane
+    // walks on from v0's sequence (again the same words in every active
+    // lane). A lane-parallel search for 64 different positions reads 64
+    // different addresses at every step.
+    auto locate_from = [&](unsigned v0, unsigned v, int& seg, int& kc, int& L) {
+        unsigned off;
+        int i = find_sequence32(p, pre, v0, (unsigned)HS, span, off);
+        off += v - v0;                        // offset from sequence i's first position
+        unsigned tot = (unsigned)span(i) * (unsigned)HS;
+        while (off >= tot && i < p.S - 1) {
+            off -= tot;
+            ++i;
+            tot = (unsigned)span(i) * (unsigned)HS;
+        }
+        L = seq_len(i);
+        const unsigned sp = (unsigned)span_of(L);
+        const unsigned g = off / sp;
+        seg = i * HS + (int)g;
+        kc = (int)(off - g * sp) - kSegCost;
+    };
 
     // Chunk metadata of window kb (64 positions), compacted to the window's
     // chunks: lane k holds the block ids, segment, chunk index and window
@@ -1015,7 +1026,7 @@ paged_attn_stream_kernel(AttnParams p) {
         const bool in = lane < a_nv;
         if (in || (kb == 0 && lane == 63)) {
             int L;
-            locate(in ? v_beg + kb + lane : v_end - 1, a_seg, a_kc, L);
+            locate_from(v_beg + kb, in ? v_beg + kb + lane : v_end - 1, a_seg, a_kc, L);
             if (in && a_kc >= 0) {
                 const int i = a_seg / HS;
                 const int32_t* __restrict__ row = table_row(i);
@@ -1256,6 +1267,239 @@ paged_attn_stream_kernel(AttnParams p) {
     }
 }
 
+// Planned decode (and decode step): the balanced split of the stream kernel,
+// with each wave's chunks listed in a host-built plan (split.h) instead of
+// derived from the context lengths on the device. The wave reads its window
+// of entries {sequence, kv head | flags, chunk, L} in one load, the table
+// entries of those chunks in a second, and streams them exactly as the stream
+// kernel does (same chunk order, same arithmetic, same records), so outputs
+// are bit-identical; the merge kernel reads the plan's descriptors. What goes
+// away is the per-workgroup lengths scan and prefix, the position search and
+// the window compaction, and their code.
+template <int KV, int D, int BS, bool STEP>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1)))
+paged_attn_plan_kernel(AttnParams p) {
+    __shared__ __align__(16) uint32_t ntstage[kWaves][D / 2];   // per wave: fp8 new-token codes
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int r16 = lane & 15;
+    const int j4 = lane >> 4;
+    const int G = p.G;
+    const unsigned W_all = gridDim.x * kWaves;
+    const unsigned w = blockIdx.x * kWaves + wave;
+    const int stride = p.plan_stride;
+    const int4* ent = reinterpret_cast<const int4*>(p.plan) + (size_t)w * stride;
+
+    // window kb: lane k holds entry kb + k (i < 0: none) and its block ids
+    int mi = -1, mgf = 0, mkc = 0, mL = 0, id0 = 0, id1 = 0;
+    auto load_entries = [&](int kb) {
+        int4 e = make_int4(-1, 0, 0, 0);
+        if (kb + lane < stride) e = ent[kb + lane];
+        mi = e.x;
+        mgf = e.y;
+        mkc = e.z;
+        mL = e.w;
+    };
+    auto load_ids = [&]() {
+        id0 = 0;
+        id1 = 0;
+        if (mi >= 0) {
+            const int32_t* __restrict__ row = p.tables + (size_t)mi * p.max_blocks;
+            const int tok = 16 * mkc;
+            if constexpr (BS == 8) {
+                id0 = row[tok / 8];
+                id1 = tok + 8 < mL ? row[tok / 8 + 1] : id0;
+            } else {
+                id0 = row[tok / BS];
+            }
+            id0 = min(max(id0, 0), p.P - 1);
+            id1 = min(max(id1, 0), p.P - 1);
+        }
+    };
+    load_entries(0);
+
+    // Decode step: this wave's share of the write of every sequence's new token
+    // (position L - 1), as in the stream kernel: part q = (sequence, kv head, K
+    // or V), parts w, w + W_all, ...; lane l handles channels l and l + 64.
+    auto write_parts = [&](auto&& between) {
+        constexpr int NCH = D / 64;
+        const int n_parts = STEP ? p.S * p.Hkv * 2 : 0;
+        bool done = false;
+        for (int q0 = (int)w; q0 < n_parts; q0 += (int)W_all) {
+            const int i = q0 / (2 * p.Hkv);
+            const int rem = q0 - i * 2 * p.Hkv;
+            const int g = rem >> 1;
+            const bool is_v = rem & 1;
+            const int L = clamped_len(p, i);
+            if (L <= 0) continue;
+            const int pos = L - 1;
+            const int raw = p.tables[(size_t)i * p.max_blocks + pos / BS];
+            const bool in_pool = raw >= 0 && raw < p.P;
+            const int b = min(max(raw, 0), p.P - 1);
+            const int o = pos % BS;
+            const size_t src_row = ((size_t)i * p.Hkv + g) * D;
+            uint32_t val[NCH];
+#pragma unroll
+            for (int u = 0; u < NCH; ++u) {
+                const int c = lane + 64 * u;
+                if constexpr (KV == KV_F32)
+                    val[u] = __float_as_uint(static_cast<const float*>(is_v ? p.v_new : p.k_new)[src_row + c]);
+                else
+                    val[u] = static_cast<const uint16_t*>(is_v ? p.v_new : p.k_new)[src_row + c];
+            }
+            if (!done) {
+                between();
+                done = true;
+            }
+            if (!in_pool) continue;
+#pragma unroll
+            for (int u = 0; u < NCH; ++u) {
+                const int c = lane + 64 * u;
+                constexpr int VS = BS < 16 ? BS : 16;
+                const size_t dst = is_v ? ((size_t)b * p.Hkv + g) * BS * D + (size_t)(o / VS) * VS * D +
+                                              (size_t)c * VS + o % VS
+                                        : (((size_t)b * p.Hkv + g) * BS + o) * D + c;
+                void* pool = const_cast<void*>(is_v ? p.v : p.k);
+                if constexpr (KV == KV_F32) static_cast<float*>(pool)[dst] = __uint_as_float(val[u]);
+                else if constexpr (KV == KV_BF16) static_cast<uint16_t*>(pool)[dst] = (uint16_t)val[u];
+                else static_cast<uint8_t*>(pool)[dst] =
+                         (uint8_t)e4m3_encode(bf16_bits_to_f32((uint16_t)val[u]) * (is_v ? p.v_inv : p.k_inv));
+            }
+        }
+        if (!done) between();
+    };
+    if constexpr (STEP) write_parts([&] { load_ids(); });
+    else load_ids();
+    // sequences with no tokens: zero rows
+    for (int s = blockIdx.x; s < p.S; s += gridDim.x)
+        if (clamped_len(p, s) <= 0) {
+            for (int e = threadIdx.x; e < p.Hq * D; e += kThreads) p.out[(size_t)s * p.Hq * D + e] = 0.f;
+            if (p.lse)
+                for (int e = threadIdx.x; e < p.Hq; e += kThreads) p.lse[(size_t)s * p.Hq + e] = -INFINITY;
+        }
+
+    using QF = typename QFragT<KV>::T;
+    QF qf[q_loads<KV, D>()];
+    NewTok<KV, D> nt;
+    f32x4 o[D / 16];
+    float m_run = -INFINITY, l_run = 0.f;
+#pragma unroll
+    for (int s2 = 0; s2 < D / 16; ++s2) o[s2] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const bool live = r16 < G;
+
+    for (int kb = 0; kb < stride; kb += 64) {
+        if (kb > 0) {
+            load_entries(kb);
+            load_ids();
+        }
+        const int nw = __builtin_popcountll(__builtin_amdgcn_ballot_w64(mi >= 0));
+        if (nw == 0) break;
+        auto issue = [&](Frag<KV, D>& f, int k) {
+            __builtin_amdgcn_sched_barrier(0);
+            const int b0 = __builtin_amdgcn_readlane(id0, k);
+            const int b1 = BS == 8 ? __builtin_amdgcn_readlane(id1, k) : b0;
+            const int g = __builtin_amdgcn_readlane(mgf, k) & 0xFFFF;
+            const int kc = __builtin_amdgcn_readlane(mkc, k);
+            load_chunk<KV, D, BS>(f, p, b0, b1, 16 * kc, g, r16, j4);
+            __builtin_amdgcn_sched_barrier(0);
+        };
+        auto step = [&](Frag<KV, D>& f, int k) {
+            const int i = __builtin_amdgcn_readlane(mi, k);
+            const int gf = __builtin_amdgcn_readlane(mgf, k);
+            const int kc = __builtin_amdgcn_readlane(mkc, k);
+            const int L = __builtin_amdgcn_readlane(mL, k);
+            const int g = gf & 0xFFFF;
+            const int flags = gf >> 16;
+            const int nch = (L + 15) >> 4;
+            const size_t out_row = ((size_t)i * p.Hq + g * G + r16) * D;
+            if (flags & pkv_split::kFirst) {      // a piece of a segment starts
+                load_q_row<KV, D>(p, out_row, live, j4, qf);
+                if constexpr (STEP) load_new_token<KV, D>(p, ((size_t)i * p.Hkv + g) * D, r16, j4, ntstage[wave], nt);
+            }
+            const int tc = 16 * kc;
+            const bool patch = STEP && kc == nch - 1;
+            constexpr bool kVRows = KV == KV_FP8 && BS >= 16;
+            if constexpr (STEP)
+                if (patch) {
+                    patch_new_k<KV, D>(f, nt, L - 1 - tc, r16);
+                    if constexpr (!kVRows) patch_new_v<KV, D>(f, nt, L - 1 - tc, j4);
+                }
+            const bool tail = tc + 16 > L;
+            const int first_tok = tc + 4 * j4;
+            const f32x4 sc = chunk_scores<KV, D>(f, qf);
+            float x[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                x[e] = sc[e] * p.qk_scale;
+                if (tail && first_tok + e >= L) x[e] = -INFINITY;
+            }
+            const float cm = head_max(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
+            const float m_new = fmaxf(m_run, cm);
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+            float pr[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) pr[e] = __builtin_amdgcn_exp2f(x[e] - m_new);
+            l_run = l_run * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
+            m_run = m_new;
+            if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
+#pragma unroll
+                for (int s2 = 0; s2 < D / 16; ++s2) o[s2] *= alpha;
+            }
+            if constexpr (kVRows) {
+                v_rows_to_operand<KV, D, BS>(f);
+                if constexpr (STEP)
+                    if (patch) patch_new_v<KV, D>(f, nt, L - 1 - tc, j4);
+            }
+            chunk_pv<KV, D>(f, pr, o, tail, first_tok, L);
+
+            if (flags & pkv_split::kLast) {       // the piece ends here
+                const float l_tot = head_sum(l_run);
+                if (live) {
+                    if (flags & pkv_split::kWhole) {
+                        const float sc_o = p.v_scale / l_tot;
+                        float* orow = p.out + out_row + 4 * j4;
+#pragma unroll
+                        for (int s2 = 0; s2 < D / 16; ++s2) *reinterpret_cast<f32x4*>(orow + 16 * s2) = o[s2] * sc_o;
+                        if (p.lse && j4 == 0) p.lse[out_row / D] = m_run + __log2f(l_tot);
+                    } else {
+                        const size_t rr = (size_t)(2 * w + ((flags & pkv_split::kOdd) ? 1 : 0)) * G + r16;
+                        const size_t nrec = (size_t)p.n_rec;
+                        float* orec = p.ws + rr * D + 4 * j4;
+#pragma unroll
+                        for (int s2 = 0; s2 < D / 16; ++s2)
+                            *reinterpret_cast<f32x4*>(orec + 16 * s2) = o[s2] * p.v_scale;
+                        if (j4 == 0) {
+                            p.ws[nrec * G * D + rr] = m_run;
+                            p.ws[nrec * G * (D + 1) + rr] = l_tot;
+                        }
+                    }
+                }
+#pragma unroll
+                for (int s2 = 0; s2 < D / 16; ++s2) o[s2] = f32x4{0.f, 0.f, 0.f, 0.f};
+                m_run = -INFINITY;
+                l_run = 0.f;
+            }
+        };
+        Frag<KV, D> fa, fb;
+        issue(fa, 0);
+        int k = 0;
+        for (; k + 2 < nw; k += 2) {
+            issue(fb, k + 1);
+            step(fa, k);
+            issue(fa, k + 2);
+            step(fb, k + 1);
+        }
+        if (k + 1 < nw) {
+            issue(fb, k + 1);
+            step(fa, k);
+            step(fb, k + 1);
+        } else {
+            step(fa, k);
+        }
+        if (nw < 64) break;
+    }
+}
+
 using AttnKernel = void (*)(AttnParams);
 
 // Kernel for one cache type and head dim (defined in attn_inst.hip, one
@@ -1264,5 +1508,9 @@ using AttnKernel = void (*)(AttnParams);
 // block size outside {8, 16, 32, 64, 128}.
 template <int KV, int D>
 AttnKernel pick_kernel(int bs, int mode, int tiles, bool partition);
+
+// The planned kernel for one cache type and head dim (attn_inst.hip).
+template <int KV, int D>
+AttnKernel pick_plan_kernel(int bs, bool step);
 
 }  // namespace pkv_dev

@@ -474,6 +474,12 @@ AttnKernel pick(int kv, int d, int bs, int mode, int tiles, bool partition) {
                    : pick_kernel<KV_FP8, 128>(bs, mode, tiles, partition);
 }
 
+AttnKernel pick_plan(int kv, int d, int bs, bool step) {
+    if (kv == KV_F32) return d == 64 ? pick_plan_kernel<KV_F32, 64>(bs, step) : pick_plan_kernel<KV_F32, 128>(bs, step);
+    if (kv == KV_BF16) return d == 64 ? pick_plan_kernel<KV_BF16, 64>(bs, step) : pick_plan_kernel<KV_BF16, 128>(bs, step);
+    return d == 64 ? pick_plan_kernel<KV_FP8, 64>(bs, step) : pick_plan_kernel<KV_FP8, 128>(bs, step);
+}
+
 // Compute units of the current device (cached per device).
 int compute_units() {
     static int cache[64] = {};
@@ -910,6 +916,150 @@ extern "C" pkv_status pkv_paged_decode_step_noalloc(float* out, const void* q, c
                        max_blocks, max_context_len, softmax_scale, k_scale, v_scale, q_dtype, cache_dtype,
                        PKV_PARTITION_BALANCED, ws, kScratchBytes, stream, w, nullptr, true, true, nullptr,
                        false, true);
+}
+
+// ----------------------------------------------------------------------------
+// Planned decode: the balanced split read from a host-built plan
+// ----------------------------------------------------------------------------
+
+namespace {
+
+// Waves of the planned kernel's grid on the current device (one 4-wave
+// workgroup per compute unit, as the stream kernel).
+int plan_workers(int kv, int d, int bs, bool step) {
+    const AttnKernel kern = pick_plan(kv, d, bs, step);
+    if (!kern) return -1;
+    const int resident = resident_workgroups(kern, 0);
+    const int cus = compute_units();
+    if (resident <= 0 || cus <= 0) return -1;
+    int grid = cus < resident ? cus : resident;
+    if (grid * kWaves > kMaxWorkers) grid = kMaxWorkers / kWaves;
+    return grid * kWaves;
+}
+
+pkv_status plan_launch(const char* fn, float* out, const void* q, const void* k_new, const void* v_new,
+                       void* k_cache, void* v_cache, const int32_t* block_tables, const int32_t* context_lens,
+                       int32_t S, int32_t Hq, int32_t Hkv, int32_t d, int32_t bs, int32_t P, int32_t max_blocks,
+                       int32_t max_context_len, float softmax_scale, float k_scale, float v_scale,
+                       float k_inv_scale, float v_inv_scale, pkv_dtype q_dtype, pkv_dtype cache_dtype,
+                       const void* plan_host, const void* plan_dev, size_t plan_bytes, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+    const bool is_step = k_new != nullptr || v_new != nullptr;
+    StepWrite wr;
+    wr.k_new = k_new;
+    wr.v_new = v_new;
+    wr.k_inv = cache_dtype == PKV_FP8_E4M3 ? k_inv_scale : 1.f;
+    wr.v_inv = cache_dtype == PKV_FP8_E4M3 ? v_inv_scale : 1.f;
+    // the arguments shared with the unplanned call, checked the same way
+    pkv_status rc = attn_launch(fn, out, q, k_cache, v_cache, block_tables, context_lens, S, 1, Hq, Hkv, d, bs,
+                                P, max_blocks, max_context_len, softmax_scale, k_scale, v_scale, q_dtype,
+                                cache_dtype, PKV_PARTITION_BALANCED, nullptr, 0, stream, wr, nullptr, true, true,
+                                nullptr, true, true);
+    if (rc != PKV_OK || S == 0) return rc;
+    if (!plan_host || !plan_dev) return fail(PKV_E_INVALID, "%s: NULL plan", fn);
+    const int32_t* h = static_cast<const int32_t*>(plan_host);
+    const int kv = cache_dtype == PKV_F32 ? KV_F32 : cache_dtype == PKV_BF16 ? KV_BF16 : KV_FP8;
+    if (h[0] != pkv_split::kPlanMagic || h[1] != pkv_split::kPlanVersion)
+        return fail(PKV_E_INVALID, "%s: not a decode plan (magic %#x version %d)", fn, h[0], h[1]);
+    if (h[4] != S || h[5] != Hkv || h[8] != max_context_len || h[9] != d || h[10] != kv)
+        return fail(PKV_E_INVALID, "%s: the plan was built for S=%d Hkv=%d max_context_len=%d d=%d kv=%d, "
+                    "not S=%d Hkv=%d max_context_len=%d d=%d kv=%d", fn, h[4], h[5], h[8], h[9], h[10], S, Hkv,
+                    max_context_len, d, kv);
+    const int32_t n_workers = h[2], stride = h[7];
+    const size_t words = (size_t)pkv_split::kPlanHeader + (size_t)n_workers * stride * 4 + (size_t)S * Hkv * 2;
+    if (stride <= 0 || n_workers <= 0 || plan_bytes < words * sizeof(int32_t))
+        return fail(PKV_E_INVALID, "%s: plan of %zu bytes, its header describes %zu", fn, plan_bytes,
+                    words * sizeof(int32_t));
+    const int workers = plan_workers(kv, d, bs, is_step);
+    if (workers <= 0) return fail(PKV_E_HIP, "%s: device query failed", fn);
+    if (workers != n_workers)
+        return fail(PKV_E_INVALID, "%s: the plan was built for %d waves, this device runs %d "
+                    "(pkv_paged_decode_plan_workers)", fn, n_workers, workers);
+    const int32_t G = Hq / Hkv;
+    const size_t need = grid_records_bytes(n_workers, (size_t)G, d);
+    if (!workspace || workspace_bytes < need)
+        return fail(PKV_E_WORKSPACE, "%s: workspace %zu bytes, need %zu", fn, workspace_bytes, need);
+
+    AttnParams prm{};
+    prm.out = out;
+    prm.q = q;
+    prm.k = k_cache;
+    prm.v = v_cache;
+    prm.tables = block_tables;
+    prm.lens = context_lens;
+    prm.ws = static_cast<float*>(workspace);
+    const int32_t* pd = static_cast<const int32_t*>(plan_dev);
+    prm.plan = pd + pkv_split::kPlanHeader;
+    prm.plan_stride = stride;
+    prm.desc = const_cast<int*>(pd + pkv_split::kPlanHeader + (size_t)n_workers * stride * 4);
+    prm.S = S;
+    prm.Hq = Hq;
+    prm.Hkv = Hkv;
+    prm.G = G;
+    prm.P = P;
+    prm.max_blocks = max_blocks;
+    prm.max_len = max_context_len;
+    prm.n_q = 1;
+    prm.qgs = 1;
+    prm.n_qg = 1;
+    prm.cols = G;
+    prm.part_tokens = 32;
+    prm.n_part = 1;
+    prm.balanced = 1;
+    prm.k_new = k_new;
+    prm.v_new = v_new;
+    prm.k_inv = wr.k_inv;
+    prm.v_inv = wr.v_inv;
+    prm.qk_scale = softmax_scale * (kv == KV_FP8 ? k_scale : 1.f) * kLog2e;
+    prm.v_scale = kv == KV_FP8 ? v_scale : 1.f;
+    prm.causal = 1;
+    prm.n_workers = n_workers;
+    prm.n_rec = 2 * n_workers;
+    auto st = static_cast<hipStream_t>(stream);
+    hipLaunchKernelGGL(pick_plan(kv, d, bs, is_step), dim3((unsigned)(n_workers / kWaves)), dim3(kThreads), 0, st,
+                       prm);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(PKV_E_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+    const unsigned rgrid = (unsigned)(((int64_t)S * Hq + kWaves - 1) / kWaves);
+    if (d == 64)
+        hipLaunchKernelGGL(paged_attn_merge_kernel<64>, dim3(rgrid), dim3(kThreads), 0, st, prm);
+    else
+        hipLaunchKernelGGL(paged_attn_merge_kernel<128>, dim3(rgrid), dim3(kThreads), 0, st, prm);
+    e = hipGetLastError();
+    if (e != hipSuccess) return fail(PKV_E_HIP, "%s: merge launch failed: %s", fn, hipGetErrorString(e));
+    return ok();
+}
+
+}  // namespace
+
+extern "C" int32_t pkv_paged_decode_plan_workers(int32_t d, int32_t bs, pkv_dtype cache_dtype) {
+    if (!pkv::is_head_dim(d) || !pkv::is_pow2_block(bs)) return -1;
+    const int kv = cache_dtype == PKV_F32 ? KV_F32 : cache_dtype == PKV_BF16 ? KV_BF16
+                 : cache_dtype == PKV_FP8_E4M3 ? KV_FP8 : -1;
+    if (kv < 0) return -1;
+    // the step and the attention-only kernels share the grid
+    const int a = plan_workers(kv, d, bs, true), b = plan_workers(kv, d, bs, false);
+    return a == b ? a : -1;
+}
+
+extern "C" size_t pkv_paged_decode_plan_workspace_size(int32_t n_workers, int32_t Hq, int32_t Hkv, int32_t d) {
+    if (n_workers <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || !pkv::is_head_dim(d)) return 0;
+    return grid_records_bytes(n_workers, (size_t)(Hq / Hkv), d);
+}
+
+extern "C" pkv_status pkv_paged_decode_step_planned(
+    float* out, const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+    const int32_t* block_tables, const int32_t* context_lens, int32_t S, int32_t Hq, int32_t Hkv, int32_t d,
+    int32_t bs, int32_t P, int32_t max_blocks, int32_t max_context_len, float softmax_scale, float k_scale,
+    float v_scale, float k_inv_scale, float v_inv_scale, pkv_dtype q_dtype, pkv_dtype cache_dtype,
+    const void* plan_host, const void* plan_dev, size_t plan_bytes, void* workspace, size_t workspace_bytes,
+    void* stream) {
+    if (S > 0 && (k_new == nullptr) != (v_new == nullptr))
+        return fail(PKV_E_INVALID, "paged_decode_step_planned: k_new and v_new must both be given or both be NULL");
+    return plan_launch("paged_decode_step_planned", out, q, k_new, v_new, k_cache, v_cache, block_tables,
+                       context_lens, S, Hq, Hkv, d, bs, P, max_blocks, max_context_len, softmax_scale, k_scale,
+                       v_scale, k_inv_scale, v_inv_scale, q_dtype, cache_dtype, plan_host, plan_dev, plan_bytes,
+                       workspace, workspace_bytes, stream);
 }
 
 extern "C" pkv_status pkv_paged_decode_attn_lse(float* out, float* lse, const void* q,

@@ -1,0 +1,83 @@
+// The balanced split of the decode attention work, shared by the device
+// kernels (which compute it from the context lengths on the device) and the
+// host plan builder (which computes the same split on the CPU, so that the
+// planned kernel runs exactly the work of the unplanned one).
+//
+// Work positions run sequence-major, then kv head, then position inside the
+// (sequence, kv head) segment. A segment of n 16-token chunks has
+// seg_cost + n positions: the first seg_cost stand for the fixed cost of
+// starting and finishing a segment (q load, epilogue, partly filled last
+// chunk), about one memory round trip. V positions in all are cut into W
+// near-equal contiguous ranges, one per wave, range w being
+// [start(w), start(w + 1)) with the first V % W ranges one longer.
+#pragma once
+
+#include <cstdint>
+
+#ifdef __HIPCC__
+#define PKV_HD __host__ __device__
+#else
+#define PKV_HD
+#endif
+
+namespace pkv_split {
+
+// Cache element kinds (the same numbering as the kernels' KvKind).
+enum : int { kKvF32 = 0, kKvBf16 = 1, kKvFp8 = 2 };
+
+#ifndef PKV_MIN_POS
+#define PKV_MIN_POS 4
+#endif
+// Positions per wave, at least: a short input is cut into fewer, longer
+// ranges, so that a merged row has fewer records.
+constexpr unsigned kMinPositions = PKV_MIN_POS;
+
+// Positions a segment costs beyond its chunks: one chunk time for 8 KiB
+// chunks (bf16 at d 128), proportionally more chunks for smaller ones.
+PKV_HD constexpr int seg_cost(int kv, int d) {
+    return 16 * 2 * d * (kv == kKvF32 ? 4 : kv == kKvBf16 ? 2 : 1) >= 8192
+               ? 1
+               : 8192 / (16 * 2 * d * (kv == kKvF32 ? 4 : kv == kKvBf16 ? 2 : 1));
+}
+
+// Positions of one (sequence, kv head) segment of L tokens.
+PKV_HD inline unsigned span_of(int L, int cost) { return L > 0 ? (unsigned)cost + (unsigned)((L + 15) >> 4) : 0u; }
+
+// Waves that get a range: all of them, unless the input is short.
+PKV_HD inline unsigned waves_used(unsigned V, unsigned W_all) {
+    const unsigned w = (V + kMinPositions - 1) / kMinPositions;
+    return W_all < (w > 1u ? w : 1u) ? W_all : (w > 1u ? w : 1u);
+}
+
+// n positions cut into W ranges (32-bit: callers keep positions below 2^31).
+struct Split {
+    unsigned q, r;
+    PKV_HD Split(unsigned n, unsigned W) : q(n / W), r(n % W) {}
+    PKV_HD unsigned start(unsigned w) const { return w * q + (w < r ? w : r); }
+    PKV_HD unsigned owner(unsigned c) const {
+        const unsigned big = r * (q + 1);
+        return c < big ? c / (q + 1) : r + (c - big) / q;
+    }
+};
+
+// ---------------------------------------------------------------------------
+// The work plan (pkv_build_paged_decode_plan, int32 words):
+//   header[16]: kPlanMagic, kPlanVersion, n_workers (waves of the grid it was
+//               built for), W (waves with a range), S, Hkv, seg_cost, stride
+//               (entries per wave), max_context_len, d, kv kind, 5 x 0
+//   entries[n_workers][stride][4]: wave w's chunks in processing order, each
+//               {sequence i, kv head g | flags << 16, chunk index kc, L_i};
+//               unused entries have i = -1
+//   desc[S * Hkv][2]: per segment (first record, record count) for the merge
+//               (a count of 1 or less: the segment was processed whole)
+// ---------------------------------------------------------------------------
+constexpr int32_t kPlanMagic = 0x504B5650;   // "PKVP"
+constexpr int32_t kPlanVersion = 1;
+constexpr int kPlanHeader = 16;
+// entry flags
+constexpr int kFirst = 1;    // the first chunk of this wave's piece of the segment
+constexpr int kLast = 2;     // the last chunk of this wave's piece
+constexpr int kWhole = 4;    // the piece is the whole segment (rows are written directly)
+constexpr int kOdd = 8;      // the piece's partial record is 2w + 1 (else 2w)
+
+}  // namespace pkv_split

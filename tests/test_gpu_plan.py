@@ -1,0 +1,121 @@
+"""GPU parity of the planned decode step (pkv_paged_decode_step_planned).
+
+The plan holds the balanced split that the unplanned kernels compute on the
+device, so the planned step must give the unplanned step's outputs and pools
+bit for bit, and the planned attention alone (no new tokens) the balanced
+pkv_paged_decode_attn's; both are also checked against the fp64 oracle.
+A plan built for other lengths, another head count or another wave count is
+refused.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+import paged_kv_cache_108_amd as pkv
+from paged_kv_cache_108_amd import workloads as W
+from helpers import (TOL, DeviceStep, assert_rows_close, device_decode_step, need_gpu, oracle_pools,
+                     same_bits, to_dev, to_host)
+
+pytestmark = pytest.mark.gpu
+BAL = pkv.PKV_PARTITION_BALANCED
+CODE = {"f32": 0, "bf16": 1, "fp8": 2}
+
+
+@pytest.fixture(autouse=True)
+def _gpu_present():
+    need_gpu()
+
+
+def _plan(w, device="cuda"):
+    s = w.spec
+    return pkv.DecodePlan(w.context_lens, Hq=s.Hq, Hkv=s.Hkv, d=s.d, bs=s.bs, cache_dtype_code=CODE[s.cache_dtype],
+                          max_context_len=w.max_context_len, device=device)
+
+
+def _planned_case(w, seqs=None):
+    torch = need_gpu()
+    s = w.spec
+    print(f"[case] planned {s.name} bs={s.bs} cache={s.cache_dtype} S={s.S}", flush=True)
+    ref = DeviceStep(w)                        # unplanned fused step
+    want = to_host(device_decode_step(ref)).copy()
+    want_attn = to_host(ref.attend(BAL)).copy()
+    dev = DeviceStep(w)                        # planned fused step
+    plan = _plan(w)
+    out = torch.full((s.S, s.Hq, s.d), float("nan"), dtype=torch.float32, device="cuda")
+    plan(out, dev.q, dev.k_cache, dev.v_cache, dev.tables, dev.lens, softmax_scale=w.softmax_scale,
+         k_new=dev.k_new, v_new=dev.v_new, k_scale=w.k_scale, v_scale=w.v_scale, k_inv_scale=w.k_inv_scale,
+         v_inv_scale=w.v_inv_scale)
+    torch.cuda.synchronize()
+    got = to_host(out).copy()
+    assert np.array_equal(got, want), "planned step differs from the unplanned step"
+    assert same_bits(to_host(dev.k_cache), to_host(ref.k_cache)), "K pool differs"
+    assert same_bits(to_host(dev.v_cache), to_host(ref.v_cache)), "V pool differs"
+    # attention alone, on the pools after the step
+    out2 = torch.full_like(out, float("nan"))
+    plan(out2, dev.q, dev.k_cache, dev.v_cache, dev.tables, dev.lens, softmax_scale=w.softmax_scale,
+         k_scale=w.k_scale, v_scale=w.v_scale)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host(out2), want_attn), "planned attention differs from the balanced call"
+    kc, vc = oracle_pools(w, seqs)
+    ref_o = oracle.paged_decode_attn(w.q, kc, vc, w.block_tables, w.context_lens, bs=s.bs,
+                                     softmax_scale=w.softmax_scale, q_dtype=s.q_dtype, cache_dtype=s.cache_dtype,
+                                     k_scale=w.k_scale, v_scale=w.v_scale, seqs=seqs)
+    e = assert_rows_close(got if seqs is None else got[seqs], ref_o, TOL[s.cache_dtype], "planned step")
+    print(f"[case] max row err {e:.3e}", flush=True)
+
+
+@pytest.mark.parametrize("name,bs,cache", [("tiny", None, None), ("small", None, None), ("small", None, "fp8"),
+                                           ("llama8b", None, None), ("llama8b", None, "fp8"), ("beam", 8, None),
+                                           ("beam", 32, None), ("llama8b", 128, None)])
+def test_planned_step_equals_unplanned(name, bs, cache):
+    w = W.make(name, bs=bs, cache_dtype=cache)
+    # the oracle computes all rows of the small workloads and a sample of the others
+    seqs = None if name in ("tiny", "small") else list(range(0, w.spec.S, 7))[:10]
+    _planned_case(w, seqs=seqs)
+
+
+def test_planned_step_long_sampled():
+    _planned_case(W.make("long"), seqs=[0, 15])
+
+
+@pytest.mark.parametrize("lens,Hq,Hkv,d,bs,dt", [
+    ([1, 2, 16, 17, 0, 33], 4, 4, 64, 16, "bf16"),
+    ([0, 1, 7, 8, 9, 100], 16, 1, 128, 8, "f32"),
+    ([1, 64, 65, 300, 0], 8, 2, 128, 64, "bf16"),
+    ([1, 17, 33, 700], 16, 4, 128, 32, "fp8"),
+])
+def test_planned_step_edge_shapes(lens, Hq, Hkv, d, bs, dt):
+    _planned_case(W.make_custom(lens=lens, Hq=Hq, Hkv=Hkv, d=d, bs=bs, q_dtype="f32" if dt == "f32" else "bf16",
+                                cache_dtype=dt, cfg=1700 + len(lens) + Hq))
+
+
+def test_planned_many_sequences():
+    rng = np.random.default_rng(4103)
+    lens = [int(x) for x in rng.integers(1, 41, 4100)]
+    lens[::97] = [0] * len(lens[::97])
+    _planned_case(W.make_custom(lens=lens, Hq=4, Hkv=2, d=64, bs=16, cfg=4103))
+
+
+def test_plan_for_other_inputs_is_refused():
+    torch = need_gpu()
+    w = W.make_custom(lens=[5, 40, 300], Hq=8, Hkv=2, d=128, bs=16, cfg=1750)
+    s = w.spec
+    dev = DeviceStep(w)
+    out = torch.zeros((s.S, s.Hq, s.d), dtype=torch.float32, device="cuda")
+    good = _plan(w)
+    # another max_context_len
+    bad = pkv.DecodePlan(w.context_lens, Hq=s.Hq, Hkv=s.Hkv, d=s.d, bs=s.bs, cache_dtype_code=1,
+                         max_context_len=w.max_context_len + 16)
+    with pytest.raises(pkv.PkvError):
+        pkv.paged_decode_step_planned(out, dev.q, None, None, dev.k_cache, dev.v_cache, dev.tables, dev.lens,
+                                      max_context_len=w.max_context_len, softmax_scale=w.softmax_scale,
+                                      plan_host=bad.host, plan_dev=bad.dev, workspace=bad.workspace)
+    # built for another wave count
+    other = pkv.build_paged_decode_plan(w.context_lens, s.Hkv, s.d, 1, w.max_context_len, good.n_workers // 2)
+    with pytest.raises(pkv.PkvError):
+        pkv.paged_decode_step_planned(out, dev.q, None, None, dev.k_cache, dev.v_cache, dev.tables, dev.lens,
+                                      max_context_len=w.max_context_len, softmax_scale=w.softmax_scale,
+                                      plan_host=other, plan_dev=to_dev(other), workspace=good.workspace)
+    torch.cuda.synchronize()
+    assert np.all(to_host(out) == 0)          # nothing ran
