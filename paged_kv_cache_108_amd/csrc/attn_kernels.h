@@ -153,6 +153,30 @@ __device__ __forceinline__ int clamped_len(const AttnParams& p, int s) {
     return min(p.lens[s], p.max_len);
 }
 
+// Stores that the compiler's wait-count tracking does not see. Loads and
+// stores share one counter here, and while a store it knows of is pending the
+// compiler takes the counter as unordered, so every later wait for a load
+// becomes a wait for all outstanding accesses, which drains the chunk
+// pipeline at each piece end. Loads still complete in issue order among
+// themselves, so waits counted over the loads alone stay correct; a pending
+// store can only make such a wait longer. The s_nop gives the one wait state
+// a VALU write to the data registers of a store wider than 8 bytes needs.
+__device__ __forceinline__ void st_untracked(float* a, f32x4 v) {
+    asm volatile("global_store_dwordx4 %0, %1, off\n\ts_nop 1" : : "v"(a), "v"(v) : "memory");
+}
+__device__ __forceinline__ void st_untracked(float* a, float v) {
+    asm volatile("global_store_dword %0, %1, off" : : "v"(a), "v"(v) : "memory");
+}
+__device__ __forceinline__ void st_untracked(int* a, int v) {
+    asm volatile("global_store_dword %0, %1, off" : : "v"(a), "v"(v) : "memory");
+}
+__device__ __forceinline__ void st_untracked(uint16_t* a, uint32_t v) {
+    asm volatile("global_store_short %0, %1, off" : : "v"(a), "v"(v) : "memory");
+}
+__device__ __forceinline__ void st_untracked(uint8_t* a, uint32_t v) {
+    asm volatile("global_store_byte %0, %1, off" : : "v"(a), "v"(v) : "memory");
+}
+
 // Per-cache-type register fragments of one 16-token chunk.
 template <int KV, int D> struct Frag;
 
@@ -443,6 +467,23 @@ __device__ __forceinline__ void load_q_row(const AttnParams& p, size_t row, bool
     }
 }
 
+// The q fragment of one column from a row offset (elements) of q, as loaded:
+// no masking, so that the loads can stay in flight.
+template <int KV, int D>
+__device__ __forceinline__ void load_q_raw(const AttnParams& p, size_t row, int j4, typename QFragT<KV>::T* qf) {
+#pragma unroll
+    for (int x = 0; x < q_loads<KV, D>(); ++x) {
+        int c;
+        if constexpr (KV == KV_F32) c = 16 * x + 4 * j4;
+        else if constexpr (KV == KV_BF16) c = 32 * x + 8 * j4;
+        else c = 64 * (x >> 1) + 16 * j4 + 8 * (x & 1);
+        if constexpr (KV == KV_F32)
+            qf[x] = *reinterpret_cast<const float4*>(static_cast<const float*>(p.q) + row + c);
+        else
+            qf[x] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.q) + row + c);
+    }
+}
+
 // The new token's K row and V values of one (sequence, kv head), in the
 // chunk fragments' register layout and already in the cache's encoding
 // (the write's): nk like Frag::k for the lane's channels, nv[s] the value of
@@ -453,39 +494,60 @@ template <int D> struct NewTok<KV_F32, D> { float4 k[D / 16]; uint32_t v[D / 16]
 template <int D> struct NewTok<KV_BF16, D> { uint4 k[D / 32]; uint32_t v[D / 16]; };
 template <int D> struct NewTok<KV_FP8, D> { uint4 k[D / 64]; uint32_t v[D / 16]; };
 
+// The new token as loaded, before its encoding: for f32 and bf16 caches the
+// fragment values themselves, for fp8 the bf16 words lane l turns into codes
+// (channels 4l .. 4l+3 of the row [K | V], lanes < D/2).
+template <int KV, int D> struct NewTokRaw { NewTok<KV, D> t; };
+template <int D> struct NewTokRaw<KV_FP8, D> { uint2 w; };
+
 template <int KV, int D>
-__device__ __forceinline__ void load_new_token(const AttnParams& p, size_t row, int r16, int j4,
-                                               uint32_t* stage, NewTok<KV, D>& nt) {
+__device__ __forceinline__ void fetch_new_token(const AttnParams& p, size_t row, int r16, int j4,
+                                                NewTokRaw<KV, D>& raw) {
     if constexpr (KV == KV_F32) {
         const float* kn = static_cast<const float*>(p.k_new) + row;
         const float* vn = static_cast<const float*>(p.v_new) + row;
 #pragma unroll
-        for (int x = 0; x < D / 16; ++x) nt.k[x] = *reinterpret_cast<const float4*>(kn + 16 * x + 4 * j4);
+        for (int x = 0; x < D / 16; ++x) raw.t.k[x] = *reinterpret_cast<const float4*>(kn + 16 * x + 4 * j4);
 #pragma unroll
-        for (int s = 0; s < D / 16; ++s) nt.v[s] = __float_as_uint(vn[16 * s + r16]);
+        for (int s = 0; s < D / 16; ++s) raw.t.v[s] = __float_as_uint(vn[16 * s + r16]);
     } else if constexpr (KV == KV_BF16) {
         const uint16_t* kn = static_cast<const uint16_t*>(p.k_new) + row;
         const uint16_t* vn = static_cast<const uint16_t*>(p.v_new) + row;
 #pragma unroll
-        for (int x = 0; x < D / 32; ++x) nt.k[x] = *reinterpret_cast<const uint4*>(kn + 32 * x + 8 * j4);
+        for (int x = 0; x < D / 32; ++x) raw.t.k[x] = *reinterpret_cast<const uint4*>(kn + 32 * x + 8 * j4);
 #pragma unroll
-        for (int s = 0; s < D / 16; ++s) nt.v[s] = vn[16 * s + r16];
+        for (int s = 0; s < D / 16; ++s) raw.t.v[s] = vn[16 * s + r16];
     } else {
-        // encode cooperatively: lane l turns channels 4l..4l+3 of the row
-        // [K | V] (2D codes) into one word of the wave's staging area, then
-        // every lane reads back what its fragment layout needs
         const int lane = 16 * j4 + r16;
+        raw.w = make_uint2(0u, 0u);
         if (lane < D / 2) {
             const int c0 = 4 * lane;
             const bool is_v = c0 >= D;
             const uint16_t* src = static_cast<const uint16_t*>(is_v ? p.v_new : p.k_new) + row +
                                   (is_v ? c0 - D : c0);
-            const uint2 w = *reinterpret_cast<const uint2*>(src);
+            raw.w = *reinterpret_cast<const uint2*>(src);
+        }
+    }
+}
+
+template <int KV, int D>
+__device__ __forceinline__ void finish_new_token(const AttnParams& p, const NewTokRaw<KV, D>& raw, int r16,
+                                                 int j4, uint32_t* stage, NewTok<KV, D>& nt) {
+    if constexpr (KV != KV_FP8) {
+        nt = raw.t;
+    } else {
+        // encode cooperatively: lane l turns its 4 channels into one word of
+        // the wave's staging area, then every lane reads back what its
+        // fragment layout needs
+        const int lane = 16 * j4 + r16;
+        if (lane < D / 2) {
+            const bool is_v = 4 * lane >= D;
             // both scales as scalars first: a lane-dependent choice between
             // the two parameters would otherwise become a per-lane load
             float k_inv = p.k_inv, v_inv = p.v_inv;
             asm volatile("" : "+s"(k_inv), "+s"(v_inv));
             const float inv = is_v ? v_inv : k_inv;
+            const uint2 w = raw.w;
             stage[lane] = e4m3_encode(bf16_bits_to_f32((uint16_t)w.x) * inv) |
                           e4m3_encode(bf16_bits_to_f32((uint16_t)(w.x >> 16)) * inv) << 8 |
                           e4m3_encode(bf16_bits_to_f32((uint16_t)w.y) * inv) << 16 |
@@ -500,6 +562,14 @@ __device__ __forceinline__ void load_new_token(const AttnParams& p, size_t row, 
         for (int s = 0; s < D / 16; ++s)
             nt.v[s] = (stage[D / 4 + 4 * s + (r16 >> 2)] >> (8 * (r16 & 3))) & 0xFFu;
     }
+}
+
+template <int KV, int D>
+__device__ __forceinline__ void load_new_token(const AttnParams& p, size_t row, int r16, int j4,
+                                               uint32_t* stage, NewTok<KV, D>& nt) {
+    NewTokRaw<KV, D> raw;
+    fetch_new_token<KV, D>(p, row, r16, j4, raw);
+    finish_new_token<KV, D>(p, raw, r16, j4, stage, nt);
 }
 
 // Put the new token (chunk row rr) into a loaded chunk fragment.
@@ -909,9 +979,9 @@ paged_attn_stream_kernel(AttnParams p) {
             const int rows = sf ? 1 : n_q;
             float* ob = sf ? p.out2 + (size_t)(s - p.n_pre) * p.Hq * D : p.out + (size_t)s * n_q * p.Hq * D;
             float* lb = sf ? p.lse2 + (size_t)(s - p.n_pre) * p.Hq : p.lse ? p.lse + (size_t)s * n_q * p.Hq : nullptr;
-            for (int e = threadIdx.x; e < rows * p.Hq * D; e += kThreads) ob[e] = 0.f;
+            for (int e = threadIdx.x; e < rows * p.Hq * D; e += kThreads) st_untracked(ob + e, 0.f);
             if (lb)
-                for (int e = threadIdx.x; e < rows * p.Hq; e += kThreads) lb[e] = -INFINITY;
+                for (int e = threadIdx.x; e < rows * p.Hq; e += kThreads) st_untracked(lb + e, -INFINITY);
         }
 
     const unsigned V = (unsigned)pre[kThreads] * (unsigned)HS;   // positions in all
@@ -969,10 +1039,10 @@ paged_attn_stream_kernel(AttnParams p) {
                                               (size_t)c * VS + o % VS
                                         : (((size_t)b * p.Hkv + g) * BS + o) * D + c;
                 void* pool = const_cast<void*>(is_v ? p.v : p.k);
-                if constexpr (KV == KV_F32) static_cast<float*>(pool)[dst] = __uint_as_float(val[u]);
-                else if constexpr (KV == KV_BF16) static_cast<uint16_t*>(pool)[dst] = (uint16_t)val[u];
-                else static_cast<uint8_t*>(pool)[dst] =
-                         (uint8_t)e4m3_encode(bf16_bits_to_f32((uint16_t)val[u]) * (is_v ? p.v_inv : p.k_inv));
+                if constexpr (KV == KV_F32) st_untracked(static_cast<float*>(pool) + dst, __uint_as_float(val[u]));
+                else if constexpr (KV == KV_BF16) st_untracked(static_cast<uint16_t*>(pool) + dst, val[u]);
+                else st_untracked(static_cast<uint8_t*>(pool) + dst,
+                                  e4m3_encode(bf16_bits_to_f32((uint16_t)val[u]) * (is_v ? p.v_inv : p.k_inv)));
             }
         }
     };
@@ -1160,8 +1230,8 @@ paged_attn_stream_kernel(AttnParams p) {
                 seg_at_range_start = first;
                 if (kc == 0 && lane == 0) {       // descriptor for the merge kernel
                     const unsigned w_hi = split.owner(v + nch - 1);
-                    p.desc[2 * seg] = (int)(2 * w + (first ? 0 : 1));
-                    p.desc[2 * seg + 1] = (int)(w_hi - w + 1);
+                    st_untracked(p.desc + 2 * seg, (int)(2 * w + (first ? 0 : 1)));
+                    st_untracked(p.desc + 2 * seg + 1, (int)(w_hi - w + 1));
                 }
             }
             const int tc = 16 * kc;
@@ -1226,18 +1296,18 @@ paged_attn_stream_kernel(AttnParams p) {
                             float* orow = obase + out_row[t] + 4 * j4;
 #pragma unroll
                             for (int s = 0; s < D / 16; ++s)
-                                *reinterpret_cast<f32x4*>(orow + 16 * s) = o[t][s] * sc_o;
-                            if (lbase && j4 == 0) lbase[out_row[t] / D] = m_run[t] + __log2f(l_tot);
+                                st_untracked(orow + 16 * s, o[t][s] * sc_o);
+                            if (lbase && j4 == 0) st_untracked(lbase + out_row[t] / D, m_run[t] + __log2f(l_tot));
                         } else {
                             const size_t rr = (size_t)(2 * w + (seg_at_range_start ? 0 : 1)) * C + 16 * t + r16;
                             const size_t nrec = (size_t)p.n_rec;
                             float* orec = p.ws + rr * D + 4 * j4;
 #pragma unroll
                             for (int s = 0; s < D / 16; ++s)
-                                *reinterpret_cast<f32x4*>(orec + 16 * s) = o[t][s] * p.v_scale;
+                                st_untracked(orec + 16 * s, o[t][s] * p.v_scale);
                             if (j4 == 0) {
-                                p.ws[nrec * C * D + rr] = m_run[t];
-                                p.ws[nrec * C * (D + 1) + rr] = l_tot;
+                                st_untracked(p.ws + nrec * C * D + rr, m_run[t]);
+                                st_untracked(p.ws + nrec * C * (D + 1) + rr, l_tot);
                             }
                         }
                     }
@@ -1276,6 +1346,20 @@ paged_attn_stream_kernel(AttnParams p) {
 // are bit-identical; the merge kernel reads the plan's descriptors. What goes
 // away is the per-workgroup lengths scan and prefix, the position search and
 // the window compaction, and their code.
+// Pipeline depth of the planned kernel: chunks of 4 KiB or less (fp8, or bf16
+// at d 64) keep three slots, larger ones two (measured: a fourth slot, or a
+// third for larger chunks, gains nothing).
+#ifndef PKV_PLAN_SLOTS_SMALL
+#define PKV_PLAN_SLOTS_SMALL 3
+#endif
+#ifndef PKV_PLAN_SLOTS_LARGE
+#define PKV_PLAN_SLOTS_LARGE 2
+#endif
+template <int KV, int D> constexpr int plan_slots() {
+    constexpr int elem = KV == KV_F32 ? 4 : KV == KV_BF16 ? 2 : 1;
+    return 16 * 2 * D * elem <= 4096 ? PKV_PLAN_SLOTS_SMALL : PKV_PLAN_SLOTS_LARGE;
+}
+
 template <int KV, int D, int BS, bool STEP>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1)))
 paged_attn_plan_kernel(AttnParams p) {
@@ -1360,10 +1444,10 @@ paged_attn_plan_kernel(AttnParams p) {
                                               (size_t)c * VS + o % VS
                                         : (((size_t)b * p.Hkv + g) * BS + o) * D + c;
                 void* pool = const_cast<void*>(is_v ? p.v : p.k);
-                if constexpr (KV == KV_F32) static_cast<float*>(pool)[dst] = __uint_as_float(val[u]);
-                else if constexpr (KV == KV_BF16) static_cast<uint16_t*>(pool)[dst] = (uint16_t)val[u];
-                else static_cast<uint8_t*>(pool)[dst] =
-                         (uint8_t)e4m3_encode(bf16_bits_to_f32((uint16_t)val[u]) * (is_v ? p.v_inv : p.k_inv));
+                if constexpr (KV == KV_F32) st_untracked(static_cast<float*>(pool) + dst, __uint_as_float(val[u]));
+                else if constexpr (KV == KV_BF16) st_untracked(static_cast<uint16_t*>(pool) + dst, val[u]);
+                else st_untracked(static_cast<uint8_t*>(pool) + dst,
+                                  e4m3_encode(bf16_bits_to_f32((uint16_t)val[u]) * (is_v ? p.v_inv : p.k_inv)));
             }
         }
         if (!done) between();
@@ -1373,14 +1457,25 @@ paged_attn_plan_kernel(AttnParams p) {
     // sequences with no tokens: zero rows
     for (int s = blockIdx.x; s < p.S; s += gridDim.x)
         if (clamped_len(p, s) <= 0) {
-            for (int e = threadIdx.x; e < p.Hq * D; e += kThreads) p.out[(size_t)s * p.Hq * D + e] = 0.f;
+            for (int e = threadIdx.x; e < p.Hq * D; e += kThreads) st_untracked(p.out + (size_t)s * p.Hq * D + e, 0.f);
             if (p.lse)
-                for (int e = threadIdx.x; e < p.Hq; e += kThreads) p.lse[(size_t)s * p.Hq + e] = -INFINITY;
+                for (int e = threadIdx.x; e < p.Hq; e += kThreads) st_untracked(p.lse + (size_t)s * p.Hq + e, -INFINITY);
         }
 
+    // Pipeline slots: a chunk in flight with, when its entry starts a piece,
+    // the piece's q row and, when it is the segment's last chunk in a decode
+    // step, the new token, all issued together so that a piece start does not
+    // wait for a load of its own. Chunks of 4 KiB or less keep three in
+    // flight, larger ones one, while the wave works on another.
     using QF = typename QFragT<KV>::T;
+    struct Slot {
+        Frag<KV, D> f;
+        QF q[q_loads<KV, D>()];
+        NewTokRaw<KV, D> nt;
+    };
+    constexpr int NB = plan_slots<KV, D>();
+    Slot sl[NB];
     QF qf[q_loads<KV, D>()];
-    NewTok<KV, D> nt;
     f32x4 o[D / 16];
     float m_run = -INFINITY, l_run = 0.f;
 #pragma unroll
@@ -1394,16 +1489,33 @@ paged_attn_plan_kernel(AttnParams p) {
         }
         const int nw = __builtin_popcountll(__builtin_amdgcn_ballot_w64(mi >= 0));
         if (nw == 0) break;
-        auto issue = [&](Frag<KV, D>& f, int k) {
+        // Entry k's loads into slot x. Past the window's last entry the slot
+        // loads block 0's first chunk (kv head 0) instead and is never used:
+        // the chunk loads are issued on every path, so the compiler counts
+        // the same loads in flight after each slot whichever way the loop
+        // went, and its waits cover one slot, not the whole pipeline.
+        auto issue = [&](Slot& x, int k) {
             __builtin_amdgcn_sched_barrier(0);
-            const int b0 = __builtin_amdgcn_readlane(id0, k);
-            const int b1 = BS == 8 ? __builtin_amdgcn_readlane(id1, k) : b0;
-            const int g = __builtin_amdgcn_readlane(mgf, k) & 0xFFFF;
-            const int kc = __builtin_amdgcn_readlane(mkc, k);
-            load_chunk<KV, D, BS>(f, p, b0, b1, 16 * kc, g, r16, j4);
+            const bool real = k < nw;
+            const int kk = real ? k : 0;
+            const int b0 = real ? __builtin_amdgcn_readlane(id0, kk) : 0;
+            const int b1 = BS == 8 ? (real ? __builtin_amdgcn_readlane(id1, kk) : 0) : b0;
+            const int i = __builtin_amdgcn_readlane(mi, kk);
+            const int gf = real ? __builtin_amdgcn_readlane(mgf, kk) : 0;
+            const int kc = real ? __builtin_amdgcn_readlane(mkc, kk) : 0;
+            const int g = gf & 0xFFFF;
+            load_chunk<KV, D, BS>(x.f, p, b0, b1, 16 * kc, g, r16, j4);
+            if ((gf >> 16) & pkv_split::kFirst)     // padding heads read row 0; step zeroes them
+                load_q_raw<KV, D>(p, live ? ((size_t)i * p.Hq + g * G + r16) * D : 0, j4, x.q);
+            if constexpr (STEP) {
+                const int L = __builtin_amdgcn_readlane(mL, kk);
+                if (real && kc == ((L + 15) >> 4) - 1)
+                    fetch_new_token<KV, D>(p, ((size_t)i * p.Hkv + g) * D, r16, j4, x.nt);
+            }
             __builtin_amdgcn_sched_barrier(0);
         };
-        auto step = [&](Frag<KV, D>& f, int k) {
+        auto step = [&](Slot& x, int k) {
+            Frag<KV, D>& f = x.f;
             const int i = __builtin_amdgcn_readlane(mi, k);
             const int gf = __builtin_amdgcn_readlane(mgf, k);
             const int kc = __builtin_amdgcn_readlane(mkc, k);
@@ -1413,32 +1525,34 @@ paged_attn_plan_kernel(AttnParams p) {
             const int nch = (L + 15) >> 4;
             const size_t out_row = ((size_t)i * p.Hq + g * G + r16) * D;
             if (flags & pkv_split::kFirst) {      // a piece of a segment starts
-                load_q_row<KV, D>(p, out_row, live, j4, qf);
-                if constexpr (STEP) load_new_token<KV, D>(p, ((size_t)i * p.Hkv + g) * D, r16, j4, ntstage[wave], nt);
+#pragma unroll
+                for (int u = 0; u < q_loads<KV, D>(); ++u) qf[u] = live ? x.q[u] : QF{};
             }
             const int tc = 16 * kc;
             const bool patch = STEP && kc == nch - 1;
             constexpr bool kVRows = KV == KV_FP8 && BS >= 16;
+            NewTok<KV, D> nt;
             if constexpr (STEP)
                 if (patch) {
+                    finish_new_token<KV, D>(p, x.nt, r16, j4, ntstage[wave], nt);
                     patch_new_k<KV, D>(f, nt, L - 1 - tc, r16);
                     if constexpr (!kVRows) patch_new_v<KV, D>(f, nt, L - 1 - tc, j4);
                 }
             const bool tail = tc + 16 > L;
             const int first_tok = tc + 4 * j4;
             const f32x4 sc = chunk_scores<KV, D>(f, qf);
-            float x[4];
+            float xs[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                x[e] = sc[e] * p.qk_scale;
-                if (tail && first_tok + e >= L) x[e] = -INFINITY;
+                xs[e] = sc[e] * p.qk_scale;
+                if (tail && first_tok + e >= L) xs[e] = -INFINITY;
             }
-            const float cm = head_max(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
+            const float cm = head_max(fmaxf(fmaxf(xs[0], xs[1]), fmaxf(xs[2], xs[3])));
             const float m_new = fmaxf(m_run, cm);
             const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
             float pr[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) pr[e] = __builtin_amdgcn_exp2f(x[e] - m_new);
+            for (int e = 0; e < 4; ++e) pr[e] = __builtin_amdgcn_exp2f(xs[e] - m_new);
             l_run = l_run * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
             m_run = m_new;
             if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
@@ -1459,18 +1573,17 @@ paged_attn_plan_kernel(AttnParams p) {
                         const float sc_o = p.v_scale / l_tot;
                         float* orow = p.out + out_row + 4 * j4;
 #pragma unroll
-                        for (int s2 = 0; s2 < D / 16; ++s2) *reinterpret_cast<f32x4*>(orow + 16 * s2) = o[s2] * sc_o;
-                        if (p.lse && j4 == 0) p.lse[out_row / D] = m_run + __log2f(l_tot);
+                        for (int s2 = 0; s2 < D / 16; ++s2) st_untracked(orow + 16 * s2, o[s2] * sc_o);
+                        if (p.lse && j4 == 0) st_untracked(p.lse + out_row / D, m_run + __log2f(l_tot));
                     } else {
                         const size_t rr = (size_t)(2 * w + ((flags & pkv_split::kOdd) ? 1 : 0)) * G + r16;
                         const size_t nrec = (size_t)p.n_rec;
                         float* orec = p.ws + rr * D + 4 * j4;
 #pragma unroll
-                        for (int s2 = 0; s2 < D / 16; ++s2)
-                            *reinterpret_cast<f32x4*>(orec + 16 * s2) = o[s2] * p.v_scale;
+                        for (int s2 = 0; s2 < D / 16; ++s2) st_untracked(orec + 16 * s2, o[s2] * p.v_scale);
                         if (j4 == 0) {
-                            p.ws[nrec * G * D + rr] = m_run;
-                            p.ws[nrec * G * (D + 1) + rr] = l_tot;
+                            st_untracked(p.ws + nrec * G * D + rr, m_run);
+                            st_untracked(p.ws + nrec * G * (D + 1) + rr, l_tot);
                         }
                     }
                 }
@@ -1480,22 +1593,21 @@ paged_attn_plan_kernel(AttnParams p) {
                 l_run = 0.f;
             }
         };
-        Frag<KV, D> fa, fb;
-        issue(fa, 0);
+        // entries k, k + 1, ... run through slots k mod NB; entry k + NB - 1
+        // is issued before entry k's step
+#pragma unroll
+        for (int u = 0; u < NB - 1; ++u) issue(sl[u], u);
         int k = 0;
-        for (; k + 2 < nw; k += 2) {
-            issue(fb, k + 1);
-            step(fa, k);
-            issue(fa, k + 2);
-            step(fb, k + 1);
+        for (; k + NB <= nw; k += NB) {
+#pragma unroll
+            for (int u = 0; u < NB; ++u) {
+                issue(sl[(u + NB - 1) % NB], k + u + NB - 1);
+                step(sl[u], k + u);
+            }
         }
-        if (k + 1 < nw) {
-            issue(fb, k + 1);
-            step(fa, k);
-            step(fb, k + 1);
-        } else {
-            step(fa, k);
-        }
+#pragma unroll
+        for (int u = 0; u < NB - 1; ++u)
+            if (k + u < nw) step(sl[u], k + u);
         if (nw < 64) break;
     }
 }
