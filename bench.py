@@ -3,25 +3,36 @@
 
 A step is the whole hot path over one batch: the KV-cache write of each
 sequence's new token and paged decode attention over every sequence's context
-including that token. By default one pkv_paged_decode_step call does both
-(the stream kernel with the write fused in, then the merge kernel);
---step split times pkv_kv_cache_write, then pkv_paged_decode_attn (balanced
-split by default; --partition N selects fixed partitions of N tokens). Inputs
-are seeded synthetic workloads already resident in HBM.
+including that token. By default one pkv_paged_decode_step_planned call does
+both (the planned attention kernel with the write fused in, then the merge
+kernel), with the work plan built on the host before the timed region, as the
+block tables are; --step fused times the unplanned pkv_paged_decode_step
+(the stream kernel derives the same split on the device); --step split times
+pkv_kv_cache_write, then pkv_paged_decode_attn (balanced split by default;
+--partition N selects fixed partitions of N tokens). Inputs are seeded
+synthetic workloads already resident in HBM.
 
-Timing: W untimed warm-up steps, then K timed steps. Before each timed step
-(outside its event pair) a 1 GiB buffer is read so neither the 256 MB
-Infinity Cache nor L2 still holds the KV pool; each step is bracketed by HIP
-events on the stream the kernels run on (with --step split, a third event
-between the write and the attention call). Bytes are algorithmic: what the method must move (each
-valid token's K and V once, shared blocks once, q, the fp32 output, the table
-entries and lengths; for the write, the new tokens read and stored and the slot
-mapping).
+Timing: W untimed warm-up steps, then K timed steps (50 by default). Before
+each timed step (outside its event pair) a 1 GiB buffer is read so neither the
+256 MB Infinity Cache nor L2 still holds the KV pool; each step is bracketed by
+HIP events on the stream the kernels run on (with --step split, a third event
+between the write and the attention call). Python's garbage collector is off
+while the timed steps are enqueued. `value` uses the median step time.
+Bytes are algorithmic: what the method must move (each valid token's K and V
+once, shared blocks once, q, the fp32 output, the table entries and lengths;
+for the write, the new tokens read and stored and the slot mapping).
+
+Alongside the step (unless --no-companions), in the same process and with the
+same flush and event protocol: pkv_stream_read over the step's byte count in
+a few launch shapes (the practical read ceiling), the attention call with
+512-token partitions, and the unplanned fused step.
 
 Prints ONE JSON line.
 """
 
 import argparse
+import contextlib
+import gc
 import json
 import math
 import os
@@ -37,7 +48,7 @@ ELEM = {"f32": 4, "bf16": 2, "fp8": 1}
 
 CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "paged_kv_cache_108_amd", "csrc")
 # every file of device code: the counters hold only while all of them are unchanged
-DEVICE_SOURCES = [os.path.join(CSRC, f) for f in ("device.hip", "attn_kernels.h", "attn_inst.hip")]
+DEVICE_SOURCES = [os.path.join(CSRC, f) for f in ("device.hip", "attn_kernels.h", "attn_inst.hip", "split.h")]
 
 
 def device_source_sha256(paths=None):
@@ -55,14 +66,30 @@ def device_source_sha256(paths=None):
 # (what the counter reads for a plain copy of known size). Reported only while
 # the kernel source is the one the counters were taken with.
 MEASURED_TRAFFIC = {
-    ("llama8b", "bf16", 16, -1, "fused"): {
-        "source_sha256": "079044a4759d8a5bc60f5fe50c0d33f2a5cbdbef33f7439d4eddbe6e17271aa2",
-        "fetch_kib": 170441.2, "write_kib": 5991.5, "fetch_scale": 2.0, "write_scale": 1.0,
+    ("llama8b", "bf16", 16, -1, "planned"): {
+        "source_sha256": "15378e0b1c4d2859ffc403e6a341cd55b69302a354ee9ed17f8befab6189b745",
+        "fetch_kib": 170653.7, "write_kib": 5982.6, "fetch_scale": 2.0, "write_scale": 1.0,
+    },
+    ("small", "bf16", 16, -1, "planned"): {
+        "source_sha256": "15378e0b1c4d2859ffc403e6a341cd55b69302a354ee9ed17f8befab6189b745",
+        "fetch_kib": 34596.4, "write_kib": 4412.8, "fetch_scale": 2.0, "write_scale": 1.0,
+    },
+    ("llama8b", "fp8", 16, -1, "planned"): {
+        "source_sha256": "15378e0b1c4d2859ffc403e6a341cd55b69302a354ee9ed17f8befab6189b745",
+        "fetch_kib": 86660.6, "write_kib": 4849.9, "fetch_scale": 2.0, "write_scale": 1.0,
+    },
+    ("long", "bf16", 16, -1, "planned"): {
+        "source_sha256": "15378e0b1c4d2859ffc403e6a341cd55b69302a354ee9ed17f8befab6189b745",
+        "fetch_kib": 1054872.5, "write_kib": 5730.0, "fetch_scale": 2.0, "write_scale": 1.0,
+    },
+    ("long", "fp8", 16, -1, "planned"): {
+        "source_sha256": "15378e0b1c4d2859ffc403e6a341cd55b69302a354ee9ed17f8befab6189b745",
+        "fetch_kib": 530123.3, "write_kib": 5457.8, "fetch_scale": 2.0, "write_scale": 1.0,
     },
 }
 
 
-def measured_traffic(name, cache_dtype, bs, part, step="split"):
+def measured_traffic(name, cache_dtype, bs, part, step="planned"):
     """Bytes per attention call from the counters, or None when none were taken
     for this configuration or the kernel source has changed since."""
     m = MEASURED_TRAFFIC.get((name, cache_dtype, bs, part, step))
@@ -158,26 +185,94 @@ def cpu_baseline(w, cache_dtype, budget_s=12.0):
     }
 
 
-def _timed(args, torch, fn, flush, stream):
-    """Mean and median event time in ms of fn over args.steps calls (after
-    args.warmup), each preceded by the flush read outside the events."""
-    for _ in range(args.warmup):
+@contextlib.contextmanager
+def _no_gc():
+    """Python's collector off while a timed loop enqueues work: a full
+    collection over the objects torch holds pauses the host for tens of ms,
+    and an event pair that waits on the host then times an idle GPU."""
+    gc.collect()
+    gc.disable()
+    try:
+        yield
+    finally:
+        gc.enable()
+
+
+def _timed(args, torch, fn, flush, stream, steps=None, warmup=None):
+    """Mean, median and min event time in ms of fn over the timed calls (after
+    the warm-up calls), each preceded by the flush read outside the events;
+    also the wall time of the timed region."""
+    steps = args.steps if steps is None else steps
+    for _ in range(args.warmup if warmup is None else warmup):
         fn()
     torch.cuda.synchronize()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
+          for _ in range(steps)]
     torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    for a, b in ev:
-        if not args.no_flush:
-            flush.max()
-        a.record(stream)
-        fn()
-        b.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
+    with _no_gc():
+        wall0 = time.perf_counter()
+        for a, b in ev:
+            if not args.no_flush:
+                flush.max()
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - wall0
     ms = [a.elapsed_time(b) for a, b in ev]
     return statistics.mean(ms), statistics.median(ms), min(ms), wall
+
+
+# Launch shapes of the streaming-read reference (unroll, workgroups); the best
+# median is reported. Measured on MI355X: each is the best at one of the byte
+# counts of the workloads here (66 MB .. 2.1 GB).
+READ_SHAPES = [(4, 512), (8, 256), (16, 2048), (16, 8192)]
+
+
+def companions(args, torch, pkv, w, flush, stream, bufs, step_bytes, attn_bytes):
+    """The read ceiling over step_bytes, the 512-token-partition attention call
+    and the unplanned fused step, each timed like the step (median)."""
+    s = w.spec
+    q, k_new, v_new, k_cache, v_cache, tables, lens, out = bufs
+    res = {}
+    src = torch.empty(step_bytes + 16, dtype=torch.uint8, device="cuda")
+    src.fill_(1)
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    shapes = []
+    for unroll, blocks in READ_SHAPES:
+        _, med, mn, _ = _timed(args, torch, lambda: pkv.stream_read(src, sink, nbytes=step_bytes, blocks=blocks,
+                                                                     unroll=unroll, stream=stream),
+                               flush, stream)
+        shapes.append({"unroll": unroll, "workgroups": blocks, "ms_median": round(med, 5),
+                       "gbs": round(step_bytes / (med * 1e-3) / 1e9, 1)})
+    best = max(shapes, key=lambda x: x["gbs"])
+    res["read_ceiling"] = {
+        "kernel": "pkv_stream_read (nontemporal 16-byte loads, grid-stride)", "bytes": int(step_bytes),
+        "gbs": best["gbs"], "ms_median": best["ms_median"], "frac_of_peak": round(best["gbs"] / HBM_PEAK_GBS, 4),
+        "best_shape": {"unroll": best["unroll"], "workgroups": best["workgroups"]}, "shapes": shapes,
+    }
+    del src
+    # attention alone with 512-token partitions (split-K), and the unplanned fused step
+    ws512 = pkv.paged_decode_attn_workspace(s.S, s.Hq, s.Hkv, s.d, w.max_context_len, 512)
+    _, med, _, _ = _timed(args, torch, lambda: pkv.paged_decode_attn(
+        out, q, k_cache, v_cache, tables, lens, max_context_len=w.max_context_len, softmax_scale=w.softmax_scale,
+        k_scale=w.k_scale, v_scale=w.v_scale, partition_size=512, workspace=ws512, stream=stream), flush, stream)
+    g = attn_bytes / (med * 1e-3) / 1e9
+    res["partition_512_attention"] = {
+        "call": "pkv_paged_decode_attn, partition_size 512 (partition kernel + merge kernel), no write",
+        "bytes": int(attn_bytes), "ms_median": round(med, 5), "gbs": round(g, 1),
+        "pct_of_peak": round(100 * g / HBM_PEAK_GBS, 2)}
+    wsb = pkv.paged_decode_attn_workspace(s.S, s.Hq, s.Hkv, s.d, w.max_context_len, pkv.PKV_PARTITION_BALANCED)
+    _, med, _, _ = _timed(args, torch, lambda: pkv.paged_decode_step(
+        out, q, k_new, v_new, k_cache, v_cache, tables, lens, max_context_len=w.max_context_len,
+        softmax_scale=w.softmax_scale, k_scale=w.k_scale, v_scale=w.v_scale, k_inv_scale=w.k_inv_scale,
+        v_inv_scale=w.v_inv_scale, workspace=wsb, stream=stream), flush, stream)
+    g = step_bytes / (med * 1e-3) / 1e9
+    res["unplanned_fused_step"] = {
+        "call": "pkv_paged_decode_step (stream kernel deriving the split on the device + merge kernel)",
+        "bytes": int(step_bytes), "ms_median": round(med, 5), "gbs": round(g, 1),
+        "pct_of_peak": round(100 * g / HBM_PEAK_GBS, 2)}
+    return res
 
 
 def run_other_op(args, w, torch, pkv):
@@ -322,7 +417,7 @@ def run_prefix(args):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="llama8b",
                     choices=["tiny", "small", "llama8b", "beam", "long"])
@@ -331,9 +426,13 @@ def main():
     ap.add_argument("--partition", type=int, default=-1,
                     help="partition_size for paged_decode_attn: -1 = balanced split (default), "
                          "0 = one pass per (sequence, kv head), else tokens per partition")
-    ap.add_argument("--step", choices=["fused", "split"], default="fused",
-                    help="fused: one pkv_paged_decode_step call writes the new tokens and attends "
-                         "(balanced split only); split: pkv_kv_cache_write, then pkv_paged_decode_attn")
+    ap.add_argument("--step", choices=["planned", "fused", "split"], default="planned",
+                    help="planned: one pkv_paged_decode_step_planned call writes the new tokens and attends, "
+                         "its plan built on the host before the timed region (default); fused: one "
+                         "pkv_paged_decode_step call (balanced split derived on the device); split: "
+                         "pkv_kv_cache_write, then pkv_paged_decode_attn")
+    ap.add_argument("--no-companions", action="store_true",
+                    help="skip the read ceiling, the 512-partition call and the unplanned step")
     ap.add_argument("--no-flush", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
@@ -386,9 +485,9 @@ def main():
         return
     cache_dtype = s.cache_dtype
     part = args.partition
-    fused = args.step == "fused"
-    if fused and part != pkv.PKV_PARTITION_BALANCED:
-        print(json.dumps({"error": "--step fused takes the balanced split (--partition -1)"}))
+    one_call = args.step in ("planned", "fused")
+    if one_call and part != pkv.PKV_PARTITION_BALANCED:
+        print(json.dumps({"error": f"--step {args.step} takes the balanced split (--partition -1)"}))
         sys.exit(2)
 
     def dev(a):
@@ -436,9 +535,33 @@ def main():
                               k_scale=w.k_scale, v_scale=w.v_scale, k_inv_scale=w.k_inv_scale,
                               v_inv_scale=w.v_inv_scale, workspace=ws, stream=stream)
 
+    plan_info = None
+    if args.step == "planned":
+        # step a0 on the host, before the timed region: the plan from the host
+        # lengths (as the block tables are built), uploaded once
+        code = {"f32": pkv.PKV_F32, "bf16": pkv.PKV_BF16, "fp8": pkv.PKV_FP8_E4M3}[cache_dtype]
+        t0 = time.perf_counter()
+        plan = pkv.DecodePlan(w.context_lens, Hq=s.Hq, Hkv=s.Hkv, d=s.d, bs=s.bs, cache_dtype_code=code,
+                              max_context_len=w.max_context_len)
+        torch.cuda.synchronize()
+        t_plan = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        pkv.build_paged_decode_plan(w.context_lens, s.Hkv, s.d, code, w.max_context_len, plan.n_workers)
+        t_build = time.perf_counter() - t0
+        plan_info = {"host_build_ms": round(1e3 * t_build, 3), "build_and_upload_ms": round(1e3 * t_plan, 3),
+                     "bytes": int(plan.host.nbytes), "waves": int(plan.n_workers),
+                     "note": "built on the host from the host lengths before the timed region (step a0, as the "
+                             "block tables); one plan serves every layer of a step"}
+
+        def planned_step():
+            plan(out, q, k_cache, v_cache, tables, lens, softmax_scale=w.softmax_scale, k_new=k_new,
+                 v_new=v_new, k_scale=w.k_scale, v_scale=w.v_scale, k_inv_scale=w.k_inv_scale,
+                 v_inv_scale=w.v_inv_scale, stream=stream)
+
+    one = planned_step if args.step == "planned" else fused_step
     for _ in range(args.warmup):
-        if fused:
-            fused_step()
+        if one_call:
+            one()
         else:
             write()
             attend()
@@ -447,37 +570,45 @@ def main():
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
            torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    for k in range(args.steps):
-        if not args.no_flush:
-            flush.max()
-        a, b, c = ev[k]
-        a.record(stream)
-        if fused:
-            fused_step()
-        else:
-            write()
-            b.record(stream)
-            attend()
-        c.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
+    with _no_gc():
+        wall0 = time.perf_counter()
+        for k in range(args.steps):
+            if not args.no_flush:
+                flush.max()
+            a, b, c = ev[k]
+            a.record(stream)
+            if one_call:
+                one()
+            else:
+                write()
+                b.record(stream)
+                attend()
+            c.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - wall0
 
     step_ms = [a.elapsed_time(c) for a, b, c in ev]
-    if fused:                                  # one call does both
+    if one_call:                               # one call does both
         write_ms, attn_ms = None, step_ms
     else:
         write_ms = [a.elapsed_time(b) for a, b, c in ev]
         attn_ms = [b.elapsed_time(c) for a, b, c in ev]
     step_mean = statistics.mean(step_ms)
+    step_med = statistics.median(step_ms)
     attn_mean = statistics.mean(attn_ms)
 
     attn_bytes, write_bytes, logical_kv, unique_tokens = algorithmic_bytes(w, cache_dtype)
     step_bytes = attn_bytes + write_bytes
-    value = step_bytes / (step_mean * 1e-3) / 1e9
+    value = step_bytes / (step_med * 1e-3) / 1e9
     attn_gbs = attn_bytes / (attn_mean * 1e-3) / 1e9
-    if fused:
-        kernel_name = "paged_decode_step call (stream kernel with the write fused in + merge kernel)"
+    if args.step == "planned":
+        kernel_name = ("paged_decode_step_planned call (planned attention kernel with the write fused in + "
+                       "merge kernel), mean event time")
+        split = "balanced: equal cost-weighted chunk ranges, one per wave, listed in a host-built plan"
+        attn_gbs = step_bytes / (step_mean * 1e-3) / 1e9     # the call moves the write's bytes too
+    elif one_call:
+        kernel_name = ("paged_decode_step call (stream kernel with the write fused in + merge kernel), "
+                       "mean event time")
         split = "balanced: equal cost-weighted chunk ranges, one per wave"
         attn_gbs = step_bytes / (step_mean * 1e-3) / 1e9     # the call moves the write's bytes too
     elif part == pkv.PKV_PARTITION_BALANCED:
@@ -495,25 +626,28 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(step_mean, 5),
+        "ms_per_step": round(step_med, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": {"f32": "f32", "bf16": "bf16", "fp8": "fp8-e4m3 KV, bf16 q"}[cache_dtype],
         "data": "synthetic (seeded; N(0,1) values, lognormal lengths)",
         "pct_of_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
-        "seq_steps_per_s": round(s.S / (step_mean * 1e-3), 1),
+        "seq_steps_per_s": round(s.S / (step_med * 1e-3), 1),
         "config": {
             "workload": f"{s.name}: {s.description}",
             "sequences": s.S, "q_heads": s.Hq, "kv_heads": s.Hkv, "head_dim": s.d,
             "block_size": s.bs, "kv_dtype": cache_dtype, "partition_size": part, "split": split,
-            "step": "one fused call (write + attention)" if fused else "write call, then attention call",
+            "step": {"planned": "one planned call (write + attention)", "fused": "one fused call (write + attention)",
+                     "split": "write call, then attention call"}[args.step],
             "context_tokens": int(w.context_lens.sum()), "unique_tokens": int(unique_tokens),
             "max_context_len": w.max_context_len, "pool_blocks": w.P,
             "cache_flush_between_steps": not args.no_flush,
         },
         "timing": {
-            "step_ms_mean": round(step_mean, 5), "step_ms_median": round(statistics.median(step_ms), 5),
+            "value_from": "median step time",
+            "step_ms_mean": round(step_mean, 5), "step_ms_median": round(step_med, 5),
+            "step_ms_min": round(min(step_ms), 5),
             "write_ms_mean": None if write_ms is None else round(statistics.mean(write_ms), 5),
             "attn_ms_mean": round(attn_mean, 5), "attn_ms_median": round(statistics.median(attn_ms), 5),
             "attn_ms_min": round(min(attn_ms), 5),
@@ -529,6 +663,13 @@ def main():
         },
         "device": torch.cuda.get_device_name(0),
     }
+    if plan_info is not None:
+        result["plan"] = plan_info
+    if not args.no_companions:
+        comp = companions(args, torch, pkv, w, flush, stream, (q, k_new, v_new, k_cache, v_cache, tables, lens, out),
+                          step_bytes, attn_bytes)
+        comp["step_over_read_ceiling"] = round(value / comp["read_ceiling"]["gbs"], 4)
+        result["companions"] = comp
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, cache_dtype, args.cpu_budget)
     print(json.dumps(result), flush=True)

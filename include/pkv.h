@@ -653,6 +653,22 @@ pkv_status pkv_waste_stats(const int32_t* lens, int32_t n, int32_t bs, int32_t m
                            int64_t* paged_slots, int64_t* naive_slots, int64_t* used,
                            double* waste_paged, double* waste_naive);
 
+/*
+ * Streaming read of `bytes` of device memory at src (16-byte aligned; the
+ * floor(bytes / 16) whole 16-byte units are read, each once), with the same
+ * nontemporal 16-byte loads the attention kernels stream the cache with:
+ * the practical read ceiling of the device, timed next to a decode step over
+ * the same byte count. A decode step is bound by reading the whole cache of
+ * every active sequence, so its time is about those bytes over the achieved
+ * bandwidth ("Serving: vLLM and PagedAttention", section 4.2, the step-time
+ * model). blocks: workgroups of 256 threads, 1 .. 2^20; unroll: loads in
+ * flight per thread, 4, 8 or 16. sink: one device uint32 that a thread
+ * writes only when the xor of the words it loaded equals 0x9E3779B9 (it
+ * keeps the loads from being dropped). Enqueued on stream; nothing allocated.
+ */
+pkv_status pkv_stream_read(const void* src, size_t bytes, int32_t blocks, int32_t unroll, uint32_t* sink,
+                           void* stream);
+
 #ifdef __cplusplus
 }
 #endif

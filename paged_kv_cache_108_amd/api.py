@@ -141,6 +141,23 @@ def copy_blocks(k_cache, v_cache, src, dst, *, stream=None):
                                 _stream(stream)))
 
 
+def stream_read(src, sink, *, nbytes=None, blocks=512, unroll=4, stream=None):
+    """pkv_stream_read: read the first nbytes (default all) of the device tensor
+    src once with the cache-streaming loads; sink: an int32 device tensor of at
+    least one element (a thread writes it only when the xor of its words is a
+    fixed value)."""
+    import torch
+    if not src.is_cuda or not sink.is_cuda or sink.numel() < 1 or sink.element_size() != 4:
+        raise ValueError("stream_read: src and sink must be device tensors, sink 32-bit with one element")
+    _one_device("stream_read", src, sink)
+    total = src.numel() * src.element_size()
+    n = total if nbytes is None else int(nbytes)
+    if n < 0 or n > total:
+        raise ValueError(f"stream_read: nbytes={n} outside [0, {total}]")
+    check(lib().pkv_stream_read(_dev(src, "src"), n, int(blocks), int(unroll), _dev(sink, "sink"),
+                                _stream(stream)))
+
+
 def paged_decode_attn_workspace_size(S, Hq, Hkv, d, max_context_len, partition_size):
     return int(lib().pkv_paged_decode_attn_workspace_size(S, Hq, Hkv, d, max_context_len,
                                                           partition_size))

@@ -575,6 +575,50 @@ extern "C" pkv_status pkv_kv_cache_write(const void* k_new, const void* v_new, v
     return ok();
 }
 
+// Streaming read: every 16-byte unit of src once, with the nontemporal
+// 16-byte loads the attention kernels stream the cache with, grid-stride
+// (thread t reads units t, t + T, ...), U loads in flight per thread. Each
+// thread xor-folds the words it loaded, so the loads stay, and writes sink[0]
+// only when its fold hits one fixed value.
+template <int U>
+__global__ void __launch_bounds__(256) stream_read_kernel(const uint4* __restrict__ src, size_t n16,
+                                                          uint32_t* sink) {
+    typedef unsigned v4u __attribute__((ext_vector_type(4)));
+    const size_t nt = (size_t)gridDim.x * blockDim.x;
+    size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    unsigned acc = 0;
+    for (; i + (U - 1) * nt < n16; i += U * nt) {
+        v4u v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) v[u] = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(src + i + u * nt));
+#pragma unroll
+        for (int u = 0; u < U; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+    }
+    for (; i < n16; i += nt) {
+        const v4u v = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(src + i));
+        acc ^= v.x ^ v.y ^ v.z ^ v.w;
+    }
+    if (acc == 0x9E3779B9u) sink[0] = acc;
+}
+
+extern "C" pkv_status pkv_stream_read(const void* src, size_t bytes, int32_t blocks, int32_t unroll,
+                                      uint32_t* sink, void* stream) {
+    if (!src || !sink) return fail(PKV_E_INVALID, "stream_read: NULL pointer");
+    if (reinterpret_cast<uintptr_t>(src) % 16 != 0) return fail(PKV_E_INVALID, "stream_read: src not 16-byte aligned");
+    if (blocks < 1 || blocks > (1 << 20)) return fail(PKV_E_INVALID, "stream_read: blocks=%d not in [1, 2^20]", blocks);
+    const size_t n16 = bytes / 16;
+    if (n16 == 0) return ok();
+    auto st = static_cast<hipStream_t>(stream);
+    const auto s = reinterpret_cast<const uint4*>(src);
+    if (unroll == 4) hipLaunchKernelGGL(stream_read_kernel<4>, dim3((unsigned)blocks), dim3(256), 0, st, s, n16, sink);
+    else if (unroll == 8) hipLaunchKernelGGL(stream_read_kernel<8>, dim3((unsigned)blocks), dim3(256), 0, st, s, n16, sink);
+    else if (unroll == 16) hipLaunchKernelGGL(stream_read_kernel<16>, dim3((unsigned)blocks), dim3(256), 0, st, s, n16, sink);
+    else return fail(PKV_E_INVALID, "stream_read: unroll=%d not in {4, 8, 16}", unroll);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(PKV_E_HIP, "stream_read: launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
 extern "C" pkv_status pkv_copy_blocks(void* k_cache, void* v_cache, const int32_t* src,
                                       const int32_t* dst, int32_t n, int32_t P, int32_t Hkv,
                                       int32_t d, int32_t bs, pkv_dtype cache_dtype, void* stream) {

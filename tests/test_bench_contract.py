@@ -20,8 +20,8 @@ def test_more_than_one_gpu_is_refused_with_a_message():
 
 
 def test_recorded_traffic_follows_the_kernel_source(monkeypatch, tmp_path):
-    got = bench.measured_traffic("llama8b", "bf16", 16, -1, "fused")
-    m = bench.MEASURED_TRAFFIC[("llama8b", "bf16", 16, -1, "fused")]
+    got = bench.measured_traffic("llama8b", "bf16", 16, -1, "planned")
+    m = bench.MEASURED_TRAFFIC[("llama8b", "bf16", 16, -1, "planned")]
     want = int(round(1024 * (m["fetch_kib"] * m["fetch_scale"] + m["write_kib"] * m["write_scale"])))
     same = bench.device_source_sha256() == m["source_sha256"]
     assert got == (want if same else None)
@@ -32,5 +32,6 @@ def test_recorded_traffic_follows_the_kernel_source(monkeypatch, tmp_path):
         other.write_bytes(open(paths[k], "rb").read() + b"\n")
         paths[k] = str(other)
         monkeypatch.setattr(bench, "DEVICE_SOURCES", paths)
-        assert bench.measured_traffic("llama8b", "bf16", 16, -1, "fused") is None
+        assert bench.measured_traffic("llama8b", "bf16", 16, -1, "planned") is None
     assert bench.measured_traffic("small", "bf16", 16, -1, "fused") is None       # never measured
+    assert bench.measured_traffic("beam", "bf16", 8, -1, "planned") is None       # never measured
