@@ -144,9 +144,11 @@ def test_fp8_write_every_bf16_pattern():
         assert np.array_equal(to_host(vc), ov), f"V codes differ at inverse scale {inv_v!r}"
 
 
-def test_fp8_fused_step_write_every_bf16_pattern():
+@pytest.mark.parametrize("planned", [False, True])
+def test_fp8_fused_step_write_every_bf16_pattern(planned):
     # 64 sequences x 8 kv heads x 128 channels: one step writes every bf16
-    # pattern once into K and once into V
+    # pattern once into K and once into V (the unplanned step's stream kernel
+    # and the planned kernel each carry their own copy of the write)
     torch = need_gpu()
     S, Hkv, d, bs = 64, 8, 128, 16
     lens = [1 + 37 * i % 300 for i in range(S)]
@@ -156,12 +158,19 @@ def test_fp8_fused_step_write_every_bf16_pattern():
     dev = DeviceStep(w)
     slots = oracle.decode_slots(w.block_tables, w.context_lens, bs)
     ws = pkv.paged_decode_attn_workspace(S, w.spec.Hq, Hkv, d, w.max_context_len, BAL)
+    plan = pkv.DecodePlan(w.context_lens, Hq=w.spec.Hq, Hkv=Hkv, d=d, bs=bs, cache_dtype_code=pkv.PKV_FP8_E4M3,
+                          max_context_len=w.max_context_len) if planned else None
     for inv_k in _inverse_scales():
         inv_v = float(np.float32(inv_k * 0.75))
-        print(f"[case] every bf16 pattern, fused step, inv ({inv_k!r}, {inv_v!r})", flush=True)
-        pkv.paged_decode_step(dev.out, dev.q, dev.k_new, dev.v_new, dev.k_cache, dev.v_cache, dev.tables,
-                              dev.lens, max_context_len=w.max_context_len, softmax_scale=w.softmax_scale,
-                              k_scale=1.0, v_scale=1.0, k_inv_scale=inv_k, v_inv_scale=inv_v, workspace=ws)
+        print(f"[case] every bf16 pattern, {'planned' if planned else 'fused'} step, inv ({inv_k!r}, {inv_v!r})",
+              flush=True)
+        if planned:
+            plan(dev.out, dev.q, dev.k_cache, dev.v_cache, dev.tables, dev.lens, softmax_scale=w.softmax_scale,
+                 k_new=dev.k_new, v_new=dev.v_new, k_inv_scale=inv_k, v_inv_scale=inv_v)
+        else:
+            pkv.paged_decode_step(dev.out, dev.q, dev.k_new, dev.v_new, dev.k_cache, dev.v_cache, dev.tables,
+                                  dev.lens, max_context_len=w.max_context_len, softmax_scale=w.softmax_scale,
+                                  k_scale=1.0, v_scale=1.0, k_inv_scale=inv_k, v_inv_scale=inv_v, workspace=ws)
         torch.cuda.synchronize()
         gk, gv = to_host(dev.k_cache), to_host(dev.v_cache)
         want_k = oracle.quantise(w.k_new, "bf16", inv_k)
