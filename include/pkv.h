@@ -219,9 +219,13 @@ pkv_status pkv_paged_decode_step(float* out, const void* q, const void* k_new, c
  * then reads each wave's chunk list from the plan instead of scanning the
  * lengths and searching its positions on the device, and the merge reads the
  * plan's descriptors. It still walks the block tables, gathers every K/V
- * tile and writes the new tokens, and its result is that of
- * pkv_paged_decode_step (or, without new tokens, pkv_paged_decode_attn with
- * the balanced split), bit for bit.
+ * tile and writes the new tokens. Its pools are those of
+ * pkv_paged_decode_step byte for byte, and so are its outputs (or, without
+ * new tokens, those of pkv_paged_decode_attn with the balanced split) when
+ * both run the same number of waves: one 4-wave workgroup per compute unit.
+ * Where a 16-token chunk is 2 KiB or less (fp8 at d 64) the planned kernel
+ * runs two workgroups per compute unit; its split into pieces then differs
+ * and the outputs agree to rounding.
  *
  * pkv_paged_decode_plan_workers: the number of waves the planned kernel runs
  * on the current device for this head dim, block size and cache type (the

@@ -968,15 +968,23 @@ extern "C" pkv_status pkv_paged_decode_step_noalloc(float* out, const void* q, c
 
 namespace {
 
-// Waves of the planned kernel's grid on the current device (one 4-wave
-// workgroup per compute unit, as the stream kernel).
-int plan_workers(int kv, int d, int bs, bool step) {
-    const AttnKernel kern = pick_plan(kv, d, bs, step);
-    if (!kern) return -1;
-    const int resident = resident_workgroups(kern, 0);
+// Waves of the planned kernel's grid on the current device: one 4-wave
+// workgroup per compute unit, as the stream kernel, or two where a chunk is
+// 2 KiB or less (fp8 at d 64) and both fit. Measured: such chunks stream
+// faster with twice the waves in flight (`small` fp8 24.7 -> 22.1 us), larger
+// ones slower (`llama8b` 69.4 -> 71.0 us, `long` 356 -> 364 us).
+// The step and the attention-only kernels share the grid (one plan serves
+// both): the smaller of their residencies decides.
+int plan_workers(int kv, int d, int bs) {
+    const AttnKernel ks = pick_plan(kv, d, bs, true), ka = pick_plan(kv, d, bs, false);
+    if (!ks || !ka) return -1;
+    const int rs = resident_workgroups(ks, 0), ra = resident_workgroups(ka, 0);
+    const int resident = rs < ra ? rs : ra;
     const int cus = compute_units();
     if (resident <= 0 || cus <= 0) return -1;
-    int grid = cus < resident ? cus : resident;
+    const int chunk_bytes = 16 * 2 * d * (kv == KV_F32 ? 4 : kv == KV_BF16 ? 2 : 1);
+    const int per_cu = chunk_bytes <= 2048 ? 2 : 1;
+    int grid = cus * per_cu < resident ? cus * per_cu : resident;
     if (grid * kWaves > kMaxWorkers) grid = kMaxWorkers / kWaves;
     return grid * kWaves;
 }
@@ -1014,7 +1022,7 @@ pkv_status plan_launch(const char* fn, float* out, const void* q, const void* k_
     if (stride <= 0 || n_workers <= 0 || plan_bytes < words * sizeof(int32_t))
         return fail(PKV_E_INVALID, "%s: plan of %zu bytes, its header describes %zu", fn, plan_bytes,
                     words * sizeof(int32_t));
-    const int workers = plan_workers(kv, d, bs, is_step);
+    const int workers = plan_workers(kv, d, bs);
     if (workers <= 0) return fail(PKV_E_HIP, "%s: device query failed", fn);
     if (workers != n_workers)
         return fail(PKV_E_INVALID, "%s: the plan was built for %d waves, this device runs %d "
@@ -1081,9 +1089,7 @@ extern "C" int32_t pkv_paged_decode_plan_workers(int32_t d, int32_t bs, pkv_dtyp
     const int kv = cache_dtype == PKV_F32 ? KV_F32 : cache_dtype == PKV_BF16 ? KV_BF16
                  : cache_dtype == PKV_FP8_E4M3 ? KV_FP8 : -1;
     if (kv < 0) return -1;
-    // the step and the attention-only kernels share the grid
-    const int a = plan_workers(kv, d, bs, true), b = plan_workers(kv, d, bs, false);
-    return a == b ? a : -1;
+    return plan_workers(kv, d, bs);
 }
 
 extern "C" size_t pkv_paged_decode_plan_workspace_size(int32_t n_workers, int32_t Hq, int32_t Hkv, int32_t d) {

@@ -1,11 +1,14 @@
 """GPU parity of the planned decode step (pkv_paged_decode_step_planned).
 
 The plan holds the balanced split that the unplanned kernels compute on the
-device, so the planned step must give the unplanned step's outputs and pools
-bit for bit, and the planned attention alone (no new tokens) the balanced
-pkv_paged_decode_attn's; both are also checked against the fp64 oracle.
-A plan built for other lengths, another head count or another wave count is
-refused.
+device. Where both run the same number of waves (one 4-wave workgroup per
+compute unit) the split is the same one, so the planned step must give the
+unplanned step's outputs and pools bit for bit, and the planned attention
+alone (no new tokens) the balanced pkv_paged_decode_attn's. Where the planned
+kernel runs twice the waves (chunks of 2 KiB or less: fp8 at d 64) its pieces
+differ, so outputs must agree within the tolerance and pools still byte for
+byte. Every case is also checked against the fp64 oracle. A plan built for
+other lengths, another head count or another wave count is refused.
 """
 
 import numpy as np
@@ -48,7 +51,12 @@ def _planned_case(w, seqs=None):
          v_inv_scale=w.v_inv_scale)
     torch.cuda.synchronize()
     got = to_host(out).copy()
-    assert np.array_equal(got, want), "planned step differs from the unplanned step"
+    same_split = plan.n_workers == 4 * torch.cuda.get_device_properties(0).multi_processor_count
+    print(f"[case] {plan.n_workers} waves, same split as the unplanned step: {same_split}", flush=True)
+    if same_split:
+        assert np.array_equal(got, want), "planned step differs from the unplanned step"
+    else:
+        assert_rows_close(got, want.astype(np.float64), TOL[s.cache_dtype], "planned vs unplanned step")
     assert same_bits(to_host(dev.k_cache), to_host(ref.k_cache)), "K pool differs"
     assert same_bits(to_host(dev.v_cache), to_host(ref.v_cache)), "V pool differs"
     # attention alone, on the pools after the step
@@ -56,7 +64,10 @@ def _planned_case(w, seqs=None):
     plan(out2, dev.q, dev.k_cache, dev.v_cache, dev.tables, dev.lens, softmax_scale=w.softmax_scale,
          k_scale=w.k_scale, v_scale=w.v_scale)
     torch.cuda.synchronize()
-    assert np.array_equal(to_host(out2), want_attn), "planned attention differs from the balanced call"
+    if same_split:
+        assert np.array_equal(to_host(out2), want_attn), "planned attention differs from the balanced call"
+    else:
+        assert_rows_close(to_host(out2), want_attn.astype(np.float64), TOL[s.cache_dtype], "planned attention")
     kc, vc = oracle_pools(w, seqs)
     ref_o = oracle.paged_decode_attn(w.q, kc, vc, w.block_tables, w.context_lens, bs=s.bs,
                                      softmax_scale=w.softmax_scale, q_dtype=s.q_dtype, cache_dtype=s.cache_dtype,
@@ -84,6 +95,8 @@ def test_planned_step_long_sampled():
     ([0, 1, 7, 8, 9, 100], 16, 1, 128, 8, "f32"),
     ([1, 64, 65, 300, 0], 8, 2, 128, 64, "bf16"),
     ([1, 17, 33, 700], 16, 4, 128, 32, "fp8"),
+    ([1, 17, 0, 33, 700, 64], 8, 2, 64, 16, "fp8"),        # 2 KiB chunks: twice the waves
+    ([5, 300, 16], 16, 1, 64, 8, "fp8"),
 ])
 def test_planned_step_edge_shapes(lens, Hq, Hkv, d, bs, dt):
     _planned_case(W.make_custom(lens=lens, Hq=Hq, Hkv=Hkv, d=d, bs=bs, q_dtype="f32" if dt == "f32" else "bf16",
