@@ -261,7 +261,10 @@ size_t pkv_paged_decode_plan_workspace_size(int32_t n_workers, int32_t Hq, int32
  * device's wave count) and plan_dev (a device copy of all plan_bytes, read by
  * the kernels; the caller uploads it). k_new and v_new may both be NULL: the
  * attention alone, with no write. Contents of the workspace on entry do not
- * matter; calls that overlap in time must not share it.
+ * matter; calls that overlap in time must not share it. attn_done_event:
+ * NULL, or a hipEvent_t that the call records on stream after the attention
+ * kernel and before the merge kernel, so that a caller can time the two
+ * apart (the call's work is the same either way).
  */
 pkv_status pkv_paged_decode_step_planned(float* out, const void* q, const void* k_new, const void* v_new,
                                          void* k_cache, void* v_cache,
@@ -272,7 +275,8 @@ pkv_status pkv_paged_decode_step_planned(float* out, const void* q, const void* 
                                          float k_inv_scale, float v_inv_scale,
                                          pkv_dtype q_dtype, pkv_dtype cache_dtype,
                                          const void* plan_host, const void* plan_dev, size_t plan_bytes,
-                                         void* workspace, size_t workspace_bytes, void* stream);
+                                         void* workspace, size_t workspace_bytes, void* stream,
+                                         void* attn_done_event);
 
 /*
  * pkv_paged_decode_step for callers that cannot allocate device memory (code

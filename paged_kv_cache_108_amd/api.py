@@ -57,6 +57,15 @@ def _dev(t, name):
     return ctypes.c_void_p(t.data_ptr())
 
 
+def _event(ev):
+    if ev is None:
+        return None
+    handle = int(ev.cuda_event)
+    if handle == 0:
+        raise ValueError("attn_done_event: record the event once first, so that it exists")
+    return ctypes.c_void_p(handle)
+
+
 def _stream(stream):
     import torch
     s = torch.cuda.current_stream() if stream is None else stream
@@ -294,9 +303,11 @@ def build_paged_decode_plan(context_lens, Hkv, d, cache_dtype_code, max_context_
 
 def paged_decode_step_planned(out, q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, *,
                               max_context_len, softmax_scale, plan_host, plan_dev, workspace, k_scale=1.0,
-                              v_scale=1.0, k_inv_scale=1.0, v_inv_scale=1.0, stream=None):
+                              v_scale=1.0, k_inv_scale=1.0, v_inv_scale=1.0, stream=None, attn_done_event=None):
     """pkv_paged_decode_step_planned. plan_host: the int32 numpy plan; plan_dev:
-    its device copy (int32 tensor); k_new/v_new None for attention alone."""
+    its device copy (int32 tensor); k_new/v_new None for attention alone;
+    attn_done_event: None, or a torch.cuda.Event (already recorded once, so
+    that it exists) that the call records between its two kernels."""
     import torch
     P, Hkv, bs, d = _pools("paged_decode_step_planned", k_cache, v_cache)
     S, Hq = _attn_args("paged_decode_step_planned", out, q, k_cache, block_tables, context_lens, d)
@@ -319,7 +330,8 @@ def paged_decode_step_planned(out, q, k_new, v_new, k_cache, v_cache, block_tabl
         block_tables.shape[1], int(max_context_len), float(softmax_scale), float(k_scale), float(v_scale),
         float(k_inv_scale), float(v_inv_scale), _dtype_code(q), _dtype_code(k_cache),
         plan_host.ctypes.data_as(c_vp), _dev(plan_dev, "plan_dev"), plan_host.nbytes,
-        _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(), _stream(stream)))
+        _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(), _stream(stream),
+        _event(attn_done_event)))
 
 
 class DecodePlan:
@@ -339,12 +351,13 @@ class DecodePlan:
         self.workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
 
     def __call__(self, out, q, k_cache, v_cache, block_tables, context_lens, *, softmax_scale, k_new=None,
-                 v_new=None, k_scale=1.0, v_scale=1.0, k_inv_scale=1.0, v_inv_scale=1.0, stream=None):
+                 v_new=None, k_scale=1.0, v_scale=1.0, k_inv_scale=1.0, v_inv_scale=1.0, stream=None,
+                 attn_done_event=None):
         paged_decode_step_planned(out, q, k_new, v_new, k_cache, v_cache, block_tables, context_lens,
                                   max_context_len=self.max_context_len, softmax_scale=softmax_scale,
                                   plan_host=self.host, plan_dev=self.dev, workspace=self.workspace,
                                   k_scale=k_scale, v_scale=v_scale, k_inv_scale=k_inv_scale,
-                                  v_inv_scale=v_inv_scale, stream=stream)
+                                  v_inv_scale=v_inv_scale, stream=stream, attn_done_event=attn_done_event)
 
 
 def paged_multi_query_attn_workspace(S, n_q, Hq, Hkv, d, device="cuda"):

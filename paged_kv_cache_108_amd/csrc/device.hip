@@ -995,7 +995,7 @@ pkv_status plan_launch(const char* fn, float* out, const void* q, const void* k_
                        int32_t max_context_len, float softmax_scale, float k_scale, float v_scale,
                        float k_inv_scale, float v_inv_scale, pkv_dtype q_dtype, pkv_dtype cache_dtype,
                        const void* plan_host, const void* plan_dev, size_t plan_bytes, void* workspace,
-                       size_t workspace_bytes, void* stream) {
+                       size_t workspace_bytes, void* stream, void* attn_done_event) {
     const bool is_step = k_new != nullptr || v_new != nullptr;
     StepWrite wr;
     wr.k_new = k_new;
@@ -1072,6 +1072,10 @@ pkv_status plan_launch(const char* fn, float* out, const void* q, const void* k_
                        prm);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(PKV_E_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+    if (attn_done_event) {
+        e = hipEventRecord(static_cast<hipEvent_t>(attn_done_event), st);
+        if (e != hipSuccess) return fail(PKV_E_HIP, "%s: event record failed: %s", fn, hipGetErrorString(e));
+    }
     const unsigned rgrid = (unsigned)(((int64_t)S * Hq + kWaves - 1) / kWaves);
     if (d == 64)
         hipLaunchKernelGGL(paged_attn_merge_kernel<64>, dim3(rgrid), dim3(kThreads), 0, st, prm);
@@ -1103,13 +1107,13 @@ extern "C" pkv_status pkv_paged_decode_step_planned(
     int32_t bs, int32_t P, int32_t max_blocks, int32_t max_context_len, float softmax_scale, float k_scale,
     float v_scale, float k_inv_scale, float v_inv_scale, pkv_dtype q_dtype, pkv_dtype cache_dtype,
     const void* plan_host, const void* plan_dev, size_t plan_bytes, void* workspace, size_t workspace_bytes,
-    void* stream) {
+    void* stream, void* attn_done_event) {
     if (S > 0 && (k_new == nullptr) != (v_new == nullptr))
         return fail(PKV_E_INVALID, "paged_decode_step_planned: k_new and v_new must both be given or both be NULL");
     return plan_launch("paged_decode_step_planned", out, q, k_new, v_new, k_cache, v_cache, block_tables,
                        context_lens, S, Hq, Hkv, d, bs, P, max_blocks, max_context_len, softmax_scale, k_scale,
                        v_scale, k_inv_scale, v_inv_scale, q_dtype, cache_dtype, plan_host, plan_dev, plan_bytes,
-                       workspace, workspace_bytes, stream);
+                       workspace, workspace_bytes, stream, attn_done_event);
 }
 
 extern "C" pkv_status pkv_paged_decode_attn_lse(float* out, float* lse, const void* q,
