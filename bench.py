@@ -24,8 +24,9 @@ for the write, the new tokens read and stored and the slot mapping).
 
 Alongside the step (unless --no-companions), in the same process and with the
 same flush and event protocol: pkv_stream_read over the step's byte count in
-a few launch shapes (the practical read ceiling), the attention call with
-512-token partitions, and the unplanned fused step.
+a few launch shapes (the practical read ceiling), pkv_paged_gather_read of the
+plan's chunks (the step's own scattered reads without arithmetic), the
+attention call with 512-token partitions, and the unplanned fused step.
 
 Prints ONE JSON line.
 """
@@ -229,12 +230,23 @@ def _timed(args, torch, fn, flush, stream, steps=None, warmup=None):
 READ_SHAPES = [(4, 512), (8, 256), (16, 2048), (16, 8192)]
 
 
-def companions(args, torch, pkv, w, flush, stream, bufs, step_bytes, attn_bytes):
-    """The read ceiling over step_bytes, the 512-token-partition attention call
-    and the unplanned fused step, each timed like the step (median)."""
+def companions(args, torch, pkv, w, flush, stream, bufs, step_bytes, attn_bytes, plan=None):
+    """The read ceiling over step_bytes, the gather of the step's own chunks
+    (with a plan), the 512-token-partition attention call and the unplanned
+    fused step, each timed like the step (median)."""
     s = w.spec
     q, k_new, v_new, k_cache, v_cache, tables, lens, out = bufs
     res = {}
+    if plan is not None:
+        sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+        _, med, _, _ = _timed(args, torch, lambda: plan.gather(k_cache, v_cache, tables, sink, stream=stream),
+                              flush, stream)
+        chunks = int(sum(-(-int(L) // 16) for L in np.minimum(w.context_lens, w.max_context_len) if L > 0)) * s.Hkv
+        kv_bytes = chunks * 16 * 2 * s.d * ELEM[s.cache_dtype]
+        res["gather_ceiling"] = {
+            "kernel": "pkv_paged_gather_read: the plan's K/V chunks through the block tables with the planned "
+                      "kernel's loads, pipeline and grid, no arithmetic",
+            "bytes_read": kv_bytes, "ms_median": round(med, 5), "gbs": round(kv_bytes / (med * 1e-3) / 1e9, 1)}
     src = torch.empty(step_bytes + 16, dtype=torch.uint8, device="cuda")
     src.fill_(1)
     sink = torch.zeros(4, dtype=torch.int32, device="cuda")
@@ -697,8 +709,10 @@ def main():
         result["plan"] = plan_info
     if not args.no_companions:
         comp = companions(args, torch, pkv, w, flush, stream, (q, k_new, v_new, k_cache, v_cache, tables, lens, out),
-                          step_bytes, attn_bytes)
+                          step_bytes, attn_bytes, plan if args.step == "planned" else None)
         comp["step_over_read_ceiling"] = round(value / comp["read_ceiling"]["gbs"], 4)
+        if "gather_ceiling" in comp:
+            comp["gather_ms_over_step_ms"] = round(comp["gather_ceiling"]["ms_median"] / step_med, 4)
         result["companions"] = comp
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, cache_dtype, args.cpu_budget)

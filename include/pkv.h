@@ -662,6 +662,26 @@ pkv_status pkv_waste_stats(const int32_t* lens, int32_t n, int32_t bs, int32_t m
                            double* waste_paged, double* waste_naive);
 
 /*
+ * Gather only: read the K/V chunks that a decode plan lists -- every chunk of
+ * every (sequence, kv head) the step attends over, through the block tables --
+ * with the planned kernel's loads, pipeline and grid, and no arithmetic. Its
+ * time is the read rate of the step's own scattered tiles: the ceiling of the
+ * planned step without its compute, q loads, new-token write, records and
+ * merge, timed next to it. A decode step reads the whole cache of every
+ * active sequence through its block table ("Serving: vLLM and
+ * PagedAttention", section 4.2, the step-time model; "03 · PagedAttention",
+ * "Blocks and block tables"). Arguments as for pkv_paged_decode_step_planned
+ * (the plan must be built for this S, Hkv, d, cache type, max_context_len
+ * and device); sink: one device uint32 that a thread writes only when the xor
+ * of the words it loaded equals 0x9E3779B9. Nothing is written otherwise;
+ * nothing allocated.
+ */
+pkv_status pkv_paged_gather_read(const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                                 int32_t S, int32_t Hkv, int32_t d, int32_t bs, int32_t P, int32_t max_blocks,
+                                 int32_t max_context_len, pkv_dtype cache_dtype, const void* plan_host,
+                                 const void* plan_dev, size_t plan_bytes, uint32_t* sink, void* stream);
+
+/*
  * Streaming read of `bytes` of device memory at src (16-byte aligned; the
  * floor(bytes / 16) whole 16-byte units are read, each once), with the same
  * nontemporal 16-byte loads the attention kernels stream the cache with:

@@ -44,6 +44,8 @@ SIGNATURES = {
     "pkv_paged_decode_step": (ctypes.c_int, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_i32,
                                              c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_f32, c_f32, c_f32,
                                              c_f32, c_f32, ctypes.c_int, ctypes.c_int, c_vp, c_sz, c_vp]),
+    "pkv_paged_gather_read": (ctypes.c_int, [c_vp, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32,
+                                             ctypes.c_int, c_vp, c_vp, c_sz, c_vp, c_vp]),
     "pkv_stream_read": (ctypes.c_int, [c_vp, c_sz, c_i32, c_i32, c_vp, c_vp]),
     "pkv_paged_decode_plan_workers": (c_i32, [c_i32, c_i32, ctypes.c_int]),
     "pkv_build_paged_decode_plan": (ctypes.c_int, [P_i32, c_i32, c_i32, c_i32, ctypes.c_int, c_i32, c_i32, c_vp,

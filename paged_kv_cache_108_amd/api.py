@@ -334,6 +334,27 @@ def paged_decode_step_planned(out, q, k_new, v_new, k_cache, v_cache, block_tabl
         _event(attn_done_event)))
 
 
+def paged_gather_read(k_cache, v_cache, block_tables, sink, *, max_context_len, plan_host, plan_dev, stream=None):
+    """pkv_paged_gather_read: the plan's K/V chunks read through the tables, no
+    arithmetic (the step's own read pattern, for timing). sink: an int32
+    device tensor of at least one element."""
+    import torch
+    P, Hkv, bs, d = _pools("paged_gather_read", k_cache, v_cache)
+    if block_tables.dtype != torch.int32 or block_tables.dim() != 2:
+        raise ValueError("paged_gather_read: block_tables must be int32 [S][max_blocks]")
+    if sink.dtype != torch.int32 or sink.numel() < 1:
+        raise ValueError("paged_gather_read: sink must be an int32 tensor of at least one element")
+    _one_device("paged_gather_read", k_cache, v_cache, block_tables, sink, plan_dev)
+    plan_host = np.ascontiguousarray(plan_host, dtype=np.int32)
+    if plan_dev.dtype != torch.int32 or plan_dev.numel() != plan_host.size:
+        raise ValueError("paged_gather_read: plan_dev must be the int32 device copy of plan_host")
+    S = block_tables.shape[0]
+    check(lib().pkv_paged_gather_read(
+        _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dev(block_tables, "block_tables"), S, Hkv, d, bs, P,
+        block_tables.shape[1], int(max_context_len), _dtype_code(k_cache), plan_host.ctypes.data_as(c_vp),
+        _dev(plan_dev, "plan_dev"), plan_host.nbytes, _dev(sink, "sink"), _stream(stream)))
+
+
 class DecodePlan:
     """A decode step's work plan: built on the host from the host lengths (as
     the block tables are), uploaded once, with the workspace it needs. Holds
@@ -349,6 +370,11 @@ class DecodePlan:
         self.dev = torch.from_numpy(self.host).to(device)
         need = int(lib().pkv_paged_decode_plan_workspace_size(self.n_workers, Hq, Hkv, d))
         self.workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
+
+    def gather(self, k_cache, v_cache, block_tables, sink, *, stream=None):
+        """pkv_paged_gather_read of this plan's chunks (no arithmetic)."""
+        paged_gather_read(k_cache, v_cache, block_tables, sink, max_context_len=self.max_context_len,
+                          plan_host=self.host, plan_dev=self.dev, stream=stream)
 
     def __call__(self, out, q, k_cache, v_cache, block_tables, context_lens, *, softmax_scale, k_new=None,
                  v_new=None, k_scale=1.0, v_scale=1.0, k_inv_scale=1.0, v_inv_scale=1.0, stream=None,

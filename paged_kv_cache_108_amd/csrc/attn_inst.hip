@@ -1,7 +1,9 @@
 // Instantiations of the attention kernels for one cache type and head dim,
 // chosen at compile time (-DPKV_INST_KV=0|1|2 for f32|bf16|fp8 caches,
 // -DPKV_INST_D=64|128); the build compiles this file once per pair, in
-// parallel. pick_kernel returns the kernel for a block size and mode.
+// parallel. pick_kernel returns the kernel for a block size and mode;
+// pick_plan_kernel the planned kernel and pick_gather_kernel the gather-only
+// kernel for a block size.
 #include "attn_kernels.h"
 
 #ifndef PKV_INST_KV
@@ -70,5 +72,19 @@ AttnKernel pick_plan_kernel(int bs, bool step) {
 }
 
 template AttnKernel pick_plan_kernel<PKV_INST_KV, PKV_INST_D>(int, bool);
+
+template <int KV, int D>
+AttnKernel pick_gather_kernel(int bs) {
+    switch (bs) {
+        case 8: return paged_gather_kernel<KV, D, 8>;
+        case 16: return paged_gather_kernel<KV, D, 16>;
+        case 32: return paged_gather_kernel<KV, D, 32>;
+        case 64: return paged_gather_kernel<KV, D, 64>;
+        case 128: return paged_gather_kernel<KV, D, 128>;
+    }
+    return nullptr;
+}
+
+template AttnKernel pick_gather_kernel<PKV_INST_KV, PKV_INST_D>(int);
 
 }  // namespace pkv_dev

@@ -1612,6 +1612,97 @@ paged_attn_plan_kernel(AttnParams p) {
     }
 }
 
+// Gather only (pkv_paged_gather_read): the chunks a plan lists, read through
+// the block tables with the planned kernel's loads, slot ring and grid, and no
+// arithmetic beyond folding every loaded word into one xor (a thread writes
+// it to the sink word only when it equals one fixed value, so the loads
+// stay). Its time is the read rate of the step's own scattered tiles, the
+// ceiling of the planned kernel without its compute, q, write and records.
+template <int KV, int D>
+__device__ __forceinline__ unsigned frag_fold(const Frag<KV, D>& f) {
+    unsigned a = 0;
+    if constexpr (KV == KV_F32) {
+#pragma unroll
+        for (int x = 0; x < D / 16; ++x)
+            a ^= __float_as_uint(f.k[x].x) ^ __float_as_uint(f.k[x].y) ^ __float_as_uint(f.k[x].z) ^
+                 __float_as_uint(f.k[x].w) ^ __float_as_uint(f.v[x].x) ^ __float_as_uint(f.v[x].y) ^
+                 __float_as_uint(f.v[x].z) ^ __float_as_uint(f.v[x].w);
+    } else if constexpr (KV == KV_BF16) {
+#pragma unroll
+        for (int x = 0; x < D / 32; ++x) a ^= f.k[x].x ^ f.k[x].y ^ f.k[x].z ^ f.k[x].w;
+#pragma unroll
+        for (int x = 0; x < D / 16; ++x) a ^= f.v[x].x ^ f.v[x].y;
+    } else {
+#pragma unroll
+        for (int x = 0; x < D / 64; ++x) a ^= f.k[x].x ^ f.k[x].y ^ f.k[x].z ^ f.k[x].w;
+#pragma unroll
+        for (int x = 0; x < D / 16; ++x) a ^= f.v[x];
+    }
+    return a;
+}
+
+template <int KV, int D, int BS>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1)))
+paged_gather_kernel(AttnParams p) {
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int r16 = lane & 15;
+    const int j4 = lane >> 4;
+    const unsigned w = blockIdx.x * kWaves + wave;
+    const int stride = p.plan_stride;
+    const int4* ent = reinterpret_cast<const int4*>(p.plan) + (size_t)w * stride;
+    constexpr int NB = plan_slots<KV, D>();
+    Frag<KV, D> sl[NB];
+    unsigned acc = 0;
+    for (int kb = 0; kb < stride; kb += 64) {
+        // lane k: entry kb + k and its blocks, as the planned kernel reads them
+        int4 e = make_int4(-1, 0, 0, 0);
+        if (kb + lane < stride) e = ent[kb + lane];
+        int id0 = 0, id1 = 0;
+        if (e.x >= 0) {
+            const int32_t* __restrict__ row = p.tables + (size_t)e.x * p.max_blocks;
+            const int tok = 16 * e.z;
+            if constexpr (BS == 8) {
+                id0 = row[tok / 8];
+                id1 = tok + 8 < e.w ? row[tok / 8 + 1] : id0;
+            } else {
+                id0 = row[tok / BS];
+            }
+            id0 = min(max(id0, 0), p.P - 1);
+            id1 = min(max(id1, 0), p.P - 1);
+        }
+        const int nw = __builtin_popcountll(__builtin_amdgcn_ballot_w64(e.x >= 0));
+        if (nw == 0) break;
+        // past the window's end: block 0's first chunk, never folded
+        auto issue = [&](Frag<KV, D>& f, int k) {
+            __builtin_amdgcn_sched_barrier(0);
+            const bool real = k < nw;
+            const int kk = real ? k : 0;
+            const int b0 = real ? __builtin_amdgcn_readlane(id0, kk) : 0;
+            const int b1 = BS == 8 ? (real ? __builtin_amdgcn_readlane(id1, kk) : 0) : b0;
+            const int g = real ? __builtin_amdgcn_readlane(e.y, kk) & 0xFFFF : 0;
+            const int kc = real ? __builtin_amdgcn_readlane(e.z, kk) : 0;
+            load_chunk<KV, D, BS>(f, p, b0, b1, 16 * kc, g, r16, j4);
+            __builtin_amdgcn_sched_barrier(0);
+        };
+#pragma unroll
+        for (int u = 0; u < NB - 1; ++u) issue(sl[u], u);
+        int k = 0;
+        for (; k + NB <= nw; k += NB) {
+#pragma unroll
+            for (int u = 0; u < NB; ++u) {
+                issue(sl[(u + NB - 1) % NB], k + u + NB - 1);
+                acc ^= frag_fold<KV, D>(sl[u]);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < NB - 1; ++u)
+            if (k + u < nw) acc ^= frag_fold<KV, D>(sl[u]);
+        if (nw < 64) break;
+    }
+    if (acc == 0x9E3779B9u) reinterpret_cast<unsigned*>(p.ws)[0] = acc;
+}
+
 using AttnKernel = void (*)(AttnParams);
 
 // Kernel for one cache type and head dim (defined in attn_inst.hip, one
@@ -1624,5 +1715,9 @@ AttnKernel pick_kernel(int bs, int mode, int tiles, bool partition);
 // The planned kernel for one cache type and head dim (attn_inst.hip).
 template <int KV, int D>
 AttnKernel pick_plan_kernel(int bs, bool step);
+
+// The gather-only kernel for one cache type and head dim (attn_inst.hip).
+template <int KV, int D>
+AttnKernel pick_gather_kernel(int bs);
 
 }  // namespace pkv_dev

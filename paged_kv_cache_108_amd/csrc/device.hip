@@ -474,6 +474,12 @@ AttnKernel pick(int kv, int d, int bs, int mode, int tiles, bool partition) {
                    : pick_kernel<KV_FP8, 128>(bs, mode, tiles, partition);
 }
 
+AttnKernel pick_gather(int kv, int d, int bs) {
+    if (kv == KV_F32) return d == 64 ? pick_gather_kernel<KV_F32, 64>(bs) : pick_gather_kernel<KV_F32, 128>(bs);
+    if (kv == KV_BF16) return d == 64 ? pick_gather_kernel<KV_BF16, 64>(bs) : pick_gather_kernel<KV_BF16, 128>(bs);
+    return d == 64 ? pick_gather_kernel<KV_FP8, 64>(bs) : pick_gather_kernel<KV_FP8, 128>(bs);
+}
+
 AttnKernel pick_plan(int kv, int d, int bs, bool step) {
     if (kv == KV_F32) return d == 64 ? pick_plan_kernel<KV_F32, 64>(bs, step) : pick_plan_kernel<KV_F32, 128>(bs, step);
     if (kv == KV_BF16) return d == 64 ? pick_plan_kernel<KV_BF16, 64>(bs, step) : pick_plan_kernel<KV_BF16, 128>(bs, step);
@@ -989,6 +995,35 @@ int plan_workers(int kv, int d, int bs) {
     return grid * kWaves;
 }
 
+// The plan's header against the call (S, Hkv, d, cache kind, max_context_len,
+// size) and this device's wave count; n_workers and stride from it.
+pkv_status check_plan(const char* fn, const void* plan_host, const void* plan_dev, size_t plan_bytes, int32_t S,
+                      int32_t Hkv, int32_t d, int32_t bs, int kv, int32_t max_context_len, int32_t* n_workers,
+                      int32_t* stride) {
+    if (!plan_host || !plan_dev) return fail(PKV_E_INVALID, "%s: NULL plan", fn);
+    if (plan_bytes < pkv_split::kPlanHeader * sizeof(int32_t))
+        return fail(PKV_E_INVALID, "%s: plan of %zu bytes", fn, plan_bytes);
+    const int32_t* h = static_cast<const int32_t*>(plan_host);
+    if (h[0] != pkv_split::kPlanMagic || h[1] != pkv_split::kPlanVersion)
+        return fail(PKV_E_INVALID, "%s: not a decode plan (magic %#x version %d)", fn, h[0], h[1]);
+    if (h[4] != S || h[5] != Hkv || h[8] != max_context_len || h[9] != d || h[10] != kv)
+        return fail(PKV_E_INVALID, "%s: the plan was built for S=%d Hkv=%d max_context_len=%d d=%d kv=%d, "
+                    "not S=%d Hkv=%d max_context_len=%d d=%d kv=%d", fn, h[4], h[5], h[8], h[9], h[10], S, Hkv,
+                    max_context_len, d, kv);
+    *n_workers = h[2];
+    *stride = h[7];
+    const size_t words = (size_t)pkv_split::kPlanHeader + (size_t)*n_workers * *stride * 4 + (size_t)S * Hkv * 2;
+    if (*stride <= 0 || *n_workers <= 0 || plan_bytes < words * sizeof(int32_t))
+        return fail(PKV_E_INVALID, "%s: plan of %zu bytes, its header describes %zu", fn, plan_bytes,
+                    words * sizeof(int32_t));
+    const int workers = plan_workers(kv, d, bs);
+    if (workers <= 0) return fail(PKV_E_HIP, "%s: device query failed", fn);
+    if (workers != *n_workers)
+        return fail(PKV_E_INVALID, "%s: the plan was built for %d waves, this device runs %d "
+                    "(pkv_paged_decode_plan_workers)", fn, *n_workers, workers);
+    return ok();
+}
+
 pkv_status plan_launch(const char* fn, float* out, const void* q, const void* k_new, const void* v_new,
                        void* k_cache, void* v_cache, const int32_t* block_tables, const int32_t* context_lens,
                        int32_t S, int32_t Hq, int32_t Hkv, int32_t d, int32_t bs, int32_t P, int32_t max_blocks,
@@ -1008,25 +1043,10 @@ pkv_status plan_launch(const char* fn, float* out, const void* q, const void* k_
                                 cache_dtype, PKV_PARTITION_BALANCED, nullptr, 0, stream, wr, nullptr, true, true,
                                 nullptr, true, true);
     if (rc != PKV_OK || S == 0) return rc;
-    if (!plan_host || !plan_dev) return fail(PKV_E_INVALID, "%s: NULL plan", fn);
-    const int32_t* h = static_cast<const int32_t*>(plan_host);
     const int kv = cache_dtype == PKV_F32 ? KV_F32 : cache_dtype == PKV_BF16 ? KV_BF16 : KV_FP8;
-    if (h[0] != pkv_split::kPlanMagic || h[1] != pkv_split::kPlanVersion)
-        return fail(PKV_E_INVALID, "%s: not a decode plan (magic %#x version %d)", fn, h[0], h[1]);
-    if (h[4] != S || h[5] != Hkv || h[8] != max_context_len || h[9] != d || h[10] != kv)
-        return fail(PKV_E_INVALID, "%s: the plan was built for S=%d Hkv=%d max_context_len=%d d=%d kv=%d, "
-                    "not S=%d Hkv=%d max_context_len=%d d=%d kv=%d", fn, h[4], h[5], h[8], h[9], h[10], S, Hkv,
-                    max_context_len, d, kv);
-    const int32_t n_workers = h[2], stride = h[7];
-    const size_t words = (size_t)pkv_split::kPlanHeader + (size_t)n_workers * stride * 4 + (size_t)S * Hkv * 2;
-    if (stride <= 0 || n_workers <= 0 || plan_bytes < words * sizeof(int32_t))
-        return fail(PKV_E_INVALID, "%s: plan of %zu bytes, its header describes %zu", fn, plan_bytes,
-                    words * sizeof(int32_t));
-    const int workers = plan_workers(kv, d, bs);
-    if (workers <= 0) return fail(PKV_E_HIP, "%s: device query failed", fn);
-    if (workers != n_workers)
-        return fail(PKV_E_INVALID, "%s: the plan was built for %d waves, this device runs %d "
-                    "(pkv_paged_decode_plan_workers)", fn, n_workers, workers);
+    int32_t n_workers = 0, stride = 0;
+    rc = check_plan(fn, plan_host, plan_dev, plan_bytes, S, Hkv, d, bs, kv, max_context_len, &n_workers, &stride);
+    if (rc != PKV_OK) return rc;
     const int32_t G = Hq / Hkv;
     const size_t need = grid_records_bytes(n_workers, (size_t)G, d);
     if (!workspace || workspace_bytes < need)
@@ -1099,6 +1119,49 @@ extern "C" int32_t pkv_paged_decode_plan_workers(int32_t d, int32_t bs, pkv_dtyp
 extern "C" size_t pkv_paged_decode_plan_workspace_size(int32_t n_workers, int32_t Hq, int32_t Hkv, int32_t d) {
     if (n_workers <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || !pkv::is_head_dim(d)) return 0;
     return grid_records_bytes(n_workers, (size_t)(Hq / Hkv), d);
+}
+
+extern "C" pkv_status pkv_paged_gather_read(const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                                            int32_t S, int32_t Hkv, int32_t d, int32_t bs, int32_t P,
+                                            int32_t max_blocks, int32_t max_context_len, pkv_dtype cache_dtype,
+                                            const void* plan_host, const void* plan_dev, size_t plan_bytes,
+                                            uint32_t* sink, void* stream) {
+    const char* fn = "paged_gather_read";
+    if (S <= 0 || Hkv <= 0 || P <= 0 || max_blocks <= 0 || max_context_len < 0)
+        return fail(PKV_E_INVALID, "%s: S=%d Hkv=%d P=%d max_blocks=%d max_context_len=%d", fn, S, Hkv, P,
+                    max_blocks, max_context_len);
+    if (!pkv::is_head_dim(d)) return fail(PKV_E_INVALID, "%s: d=%d not in {64,128}", fn, d);
+    if (!pkv::is_pow2_block(bs)) return fail(PKV_E_INVALID, "%s: bs=%d not in {8,16,32,64,128}", fn, bs);
+    if (cache_dtype != PKV_F32 && cache_dtype != PKV_BF16 && cache_dtype != PKV_FP8_E4M3)
+        return fail(PKV_E_INVALID, "%s: unsupported cache dtype %d", fn, cache_dtype);
+    if (!k_cache || !v_cache || !block_tables || !sink) return fail(PKV_E_INVALID, "%s: NULL pointer", fn);
+    if ((int64_t)max_context_len > (int64_t)max_blocks * bs)
+        return fail(PKV_E_INVALID, "%s: max_context_len=%d exceeds max_blocks*bs=%lld", fn, max_context_len,
+                    (long long)max_blocks * bs);
+    const int kv = cache_dtype == PKV_F32 ? KV_F32 : cache_dtype == PKV_BF16 ? KV_BF16 : KV_FP8;
+    int32_t n_workers = 0, stride = 0;
+    pkv_status rc = check_plan(fn, plan_host, plan_dev, plan_bytes, S, Hkv, d, bs, kv, max_context_len, &n_workers,
+                               &stride);
+    if (rc != PKV_OK) return rc;
+    AttnParams prm{};
+    prm.k = k_cache;
+    prm.v = v_cache;
+    prm.tables = block_tables;
+    prm.ws = reinterpret_cast<float*>(sink);
+    prm.plan = static_cast<const int32_t*>(plan_dev) + pkv_split::kPlanHeader;
+    prm.plan_stride = stride;
+    prm.S = S;
+    prm.Hkv = Hkv;
+    prm.P = P;
+    prm.max_blocks = max_blocks;
+    prm.max_len = max_context_len;
+    const AttnKernel kern = pick_gather(kv, d, bs);
+    if (!kern) return fail(PKV_E_INVALID, "%s: no kernel for d=%d bs=%d", fn, d, bs);
+    hipLaunchKernelGGL(kern, dim3((unsigned)(n_workers / kWaves)), dim3(kThreads), 0, static_cast<hipStream_t>(stream),
+                       prm);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(PKV_E_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+    return ok();
 }
 
 extern "C" pkv_status pkv_paged_decode_step_planned(

@@ -1,0 +1,85 @@
+"""pkv_paged_gather_read, the bench's read of the step's own chunks: it must
+read every chunk the plan lists, through the block tables, and no block that
+no sequence lists. The pools are zero except for one fixed 32-bit word; a
+thread writes the sink only when the xor of the words it loaded equals that
+word, so the sink is written exactly when the word's chunk is read."""
+
+import numpy as np
+import pytest
+
+import paged_kv_cache_108_amd as pkv
+from paged_kv_cache_108_amd import workloads as W
+from helpers import need_gpu
+
+pytestmark = pytest.mark.gpu
+MAGIC = 0x9E3779B9
+CODE = {"f32": 0, "bf16": 1, "fp8": 2}
+ELEM = {"f32": np.uint32, "bf16": np.uint16, "fp8": np.uint8}
+
+
+@pytest.fixture(autouse=True)
+def _gpu_present():
+    need_gpu()
+
+
+def _run(torch, w, dt, pool_name, block, head, tok, chan):
+    s = w.spec
+    k = np.zeros(w.k_pool.shape, ELEM[dt])
+    v = np.zeros(w.v_pool.shape, ELEM[dt])
+    target = k if pool_name == "k" else v
+    words = target.reshape(-1).view(np.uint32)     # whole 32-bit words of the pool
+    flat = np.ravel_multi_index((block, head, tok, chan), target.shape) * target.itemsize // 4
+    words[flat] = MAGIC
+    dev = lambda a: torch.from_numpy(a.view(np.int32 if a.itemsize == 4 else np.int16 if a.itemsize == 2
+                                            else np.uint8)).cuda()
+    kc, vc = dev(k), dev(v)
+    if dt == "bf16":
+        kc, vc = kc.view(torch.bfloat16), vc.view(torch.bfloat16)
+    elif dt == "f32":
+        kc, vc = kc.view(torch.float32), vc.view(torch.float32)
+    plan = pkv.DecodePlan(w.context_lens, Hq=s.Hq, Hkv=s.Hkv, d=s.d, bs=s.bs, cache_dtype_code=CODE[dt],
+                          max_context_len=w.max_context_len)
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    plan.gather(kc, vc, torch.from_numpy(w.block_tables).cuda(), sink)
+    torch.cuda.synchronize()
+    return int(sink.cpu().numpy().view(np.uint32)[0])
+
+
+@pytest.mark.parametrize("dt,d,bs", [("bf16", 128, 16), ("bf16", 64, 8), ("fp8", 64, 16), ("fp8", 128, 32),
+                                     ("f32", 64, 16), ("bf16", 128, 128)])
+def test_gather_reads_the_listed_chunks_and_no_free_block(dt, d, bs):
+    torch = need_gpu()
+    lens = [40, 5, 0, 300, 17, 1000]
+    w = W.make_custom(lens=lens, Hq=8, Hkv=2, d=d, bs=bs, q_dtype="f32" if dt == "f32" else "bf16",
+                      cache_dtype=dt, cfg=3100 + d + bs)
+    step = 4 // np.dtype(ELEM[dt]).itemsize        # pool elements per 32-bit word
+    used = set(int(b) for b in w.block_tables.reshape(-1) if b >= 0)
+    free = [b for b in range(w.P) if b not in used and b != 0]
+    print(f"[case] gather {dt} d{d} bs{bs}", flush=True)
+    # a word inside a listed chunk: sequence 3, token 16 * 5 + 2 (chunk 5), kv head 1
+    tok = 16 * 5 + 2
+    b = int(w.block_tables[3, tok // bs])
+    assert _run(torch, w, dt, "k", b, 1, tok % bs, 2 * step) == MAGIC
+    if bs <= 16:                                   # V tile [d][bs]: channel 7, the chunk's token word
+        assert _run(torch, w, dt, "v", b, 1, 7, (tok % bs) // step * step) == MAGIC
+    # the last chunk of the longest sequence
+    tok = 999
+    b = int(w.block_tables[5, tok // bs])
+    assert _run(torch, w, dt, "k", b, 0, tok % bs, 0) == MAGIC
+    # a block no sequence lists
+    if free:
+        assert _run(torch, w, dt, "k", free[0], 1, 3, step) == 0
+
+
+def test_gather_refuses_a_plan_for_other_inputs():
+    torch = need_gpu()
+    w = W.make_custom(lens=[5, 40, 300], Hq=8, Hkv=2, d=128, bs=16, cfg=3150)
+    s = w.spec
+    plan = pkv.DecodePlan(w.context_lens, Hq=s.Hq, Hkv=s.Hkv, d=s.d, bs=s.bs, cache_dtype_code=1,
+                          max_context_len=w.max_context_len + 16)
+    kc = torch.zeros(w.k_pool.shape, dtype=torch.bfloat16, device="cuda")
+    vc = torch.zeros(w.v_pool.shape, dtype=torch.bfloat16, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    with pytest.raises(pkv.PkvError):
+        pkv.paged_gather_read(kc, vc, torch.from_numpy(w.block_tables).cuda(), sink,
+                              max_context_len=w.max_context_len, plan_host=plan.host, plan_dev=plan.dev)
