@@ -132,40 +132,26 @@ kv_cache_write_kernel(const void* __restrict__ k_new, const void* __restrict__ v
 // segment) and 2*w for the others; the attention kernel left the first record
 // and the count in the segment's descriptor. Records are combined in that
 // fixed order.
+//
+// Planned calls whose segments fit take the descriptors in the merge
+// kernel's arguments instead (paged_attn_merge_args_kernel), packed first
+// record | count << 13 (records are below 2 * kMaxWorkers = 8192, counts at
+// most kMaxWorkers); a workgroup reads its segment's word with the other
+// arguments at the start, so the records follow in one round trip. A segment
+// with one record or none (an empty sequence) needs no merge, so the lengths
+// are not read.
+constexpr int kArgDescs = 768;
+struct MergeArgDesc {
+    uint32_t d[kArgDescs];
+};
+
+// Merge row h (column r of its segment) from its n records, the first rec0
+// (balanced: then 2 * (w_lo + k) for k >= 1; partitions: rec0 + k).
 template <int D>
-__global__ void __launch_bounds__(kThreads)
-paged_attn_merge_kernel(AttnParams p) {
-    const bool balanced = p.balanced != 0;
+__device__ __forceinline__ void merge_records(const AttnParams& p, long long h, int r, int n, int rec0,
+                                              bool balanced) {
     const int lane = threadIdx.x & 63;
-    // output row h = (i * n_q + j) * Hq + head
-    const long long h = (long long)blockIdx.x * kWaves + (threadIdx.x >> 6);
-    if (h >= (long long)p.S * p.n_q * p.Hq) return;
-    const int i = (int)(h / ((long long)p.n_q * p.Hq));
-    const int jh = (int)(h - (long long)i * p.n_q * p.Hq);
-    const int j = jh / p.Hq;
-    const int head = jh - j * p.Hq;
-    const int g = head / p.G;
-    const int qg = j / p.qgs;
-    const int r = (j - qg * p.qgs) * p.G + (head - g * p.G);     // column of this row
-    // the length and (balanced) the segment's descriptor are read together:
-    // one memory round trip before the records
-    const int seg = (i * p.Hkv + g) * p.n_qg + qg;
-    int2 dsc = make_int2(0, 0);
-    if (balanced) dsc = *reinterpret_cast<const int2*>(p.desc + 2 * seg);
-    const int L = min(p.lens[i], p.max_len);
-    if (L <= 0) return;
-    int n, rec0;                              // records rec0 .. (see below), n of them
-    long long w_lo = 0;
-    if (balanced) {
-        rec0 = dsc.x;
-        n = dsc.y;
-        if (n <= 1) return;                   // one wave wrote the rows
-        w_lo = rec0 >> 1;
-    } else {
-        if (L <= p.part_tokens) return;       // written by the partition kernel
-        n = (L + p.part_tokens - 1) / p.part_tokens;
-        rec0 = (i * p.Hkv + g) * p.n_part;
-    }
+    const long long w_lo = rec0 >> 1;
     // record k of this segment
     // record k of this segment; k past the last is read as the last one, so
     // loads the compiler issues ahead of their use stay inside this call's
@@ -300,6 +286,65 @@ paged_attn_merge_kernel(AttnParams p) {
 #pragma unroll
     for (int x = 0; x < PER; ++x) p.out[h * D + lane + 64 * x] = num[x] / den;
     if (p.lse && lane == 0) p.lse[h] = M + __log2f(den);
+}
+
+template <int D>
+__global__ void __launch_bounds__(kThreads)
+paged_attn_merge_kernel(AttnParams p) {
+    const bool balanced = p.balanced != 0;
+
+    // output row h = (i * n_q + j) * Hq + head
+    const long long h = (long long)blockIdx.x * kWaves + (threadIdx.x >> 6);
+    if (h >= (long long)p.S * p.n_q * p.Hq) return;
+    const int i = (int)(h / ((long long)p.n_q * p.Hq));
+    const int jh = (int)(h - (long long)i * p.n_q * p.Hq);
+    const int j = jh / p.Hq;
+    const int head = jh - j * p.Hq;
+    const int g = head / p.G;
+    const int qg = j / p.qgs;
+    const int r = (j - qg * p.qgs) * p.G + (head - g * p.G);     // column of this row
+    // the length and (balanced) the segment's descriptor are read together:
+    // one memory round trip before the records
+    const int seg = (i * p.Hkv + g) * p.n_qg + qg;
+    int2 dsc = make_int2(0, 0);
+    if (balanced) dsc = *reinterpret_cast<const int2*>(p.desc + 2 * seg);
+    const int L = min(p.lens[i], p.max_len);
+    if (L <= 0) return;
+    int n, rec0;                              // records rec0 .. (see below), n of them
+    if (balanced) {
+        rec0 = dsc.x;
+        n = dsc.y;
+        if (n <= 1) return;                   // one wave wrote the rows
+    } else {
+        if (L <= p.part_tokens) return;       // written by the partition kernel
+        n = (L + p.part_tokens - 1) / p.part_tokens;
+        rec0 = (i * p.Hkv + g) * p.n_part;
+    }
+    merge_records<D>(p, h, r, n, rec0, balanced);
+}
+
+// Planned calls whose segments fit the arguments: workgroup (s, y) merges
+// rows 4y .. 4y + 3 of (sequence, kv head) segment s, one per wave, and reads
+// the segment's descriptor at once by its index.
+template <int D>
+__global__ void __launch_bounds__(kThreads)
+paged_attn_merge_args_kernel(AttnParams p, MergeArgDesc md) {
+    const uint32_t x = md.d[blockIdx.x];
+    // every argument the merge reads, loaded together with the descriptor
+    // (the compiler would otherwise wait for each before the next branch)
+    const float* ws = p.ws;
+    float* out = p.out;
+    float* lse = p.lse;
+    const int nrec = p.n_rec, cols = p.cols, Hkv = p.Hkv, Hq = p.Hq, G = p.G;
+    asm volatile("" : : "s"(x), "s"(ws), "s"(out), "s"(lse), "s"(nrec), "s"(cols), "s"(Hkv), "s"(Hq), "s"(G));
+    const int n = (int)(x >> 13);
+    if (n <= 1) return;                       // whole, or an empty sequence
+    const int rec0 = (int)(x & 0x1FFFu);
+    const int i = (int)blockIdx.x / Hkv;
+    const int g = (int)blockIdx.x - i * Hkv;
+    const int r = kWaves * (int)blockIdx.y + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (r >= G) return;
+    merge_records<D>(p, (long long)i * Hq + g * G + r, r, n, rec0, true);
 }
 
 // Two attention states of the same rows over disjoint token sets (a shared
@@ -1097,10 +1142,25 @@ pkv_status plan_launch(const char* fn, float* out, const void* q, const void* k_
         if (e != hipSuccess) return fail(PKV_E_HIP, "%s: event record failed: %s", fn, hipGetErrorString(e));
     }
     const unsigned rgrid = (unsigned)(((int64_t)S * Hq + kWaves - 1) / kWaves);
-    if (d == 64)
+    if ((int64_t)S * Hkv <= kArgDescs) {
+        // the plan's descriptors by value (the host copy holds them)
+        MergeArgDesc md;
+        const int32_t* hd = static_cast<const int32_t*>(plan_host) + pkv_split::kPlanHeader +
+                            (size_t)n_workers * stride * 4;
+        for (int64_t x = 0; x < (int64_t)S * Hkv; ++x) {
+            const uint32_t rec0 = (uint32_t)hd[2 * x], cnt = (uint32_t)hd[2 * x + 1];
+            md.d[x] = cnt <= 1 ? 0u : (rec0 & 0x1FFFu) | (cnt << 13);
+        }
+        const dim3 sgrid((unsigned)(S * Hkv), (unsigned)((G + kWaves - 1) / kWaves));
+        if (d == 64)
+            hipLaunchKernelGGL(paged_attn_merge_args_kernel<64>, sgrid, dim3(kThreads), 0, st, prm, md);
+        else
+            hipLaunchKernelGGL(paged_attn_merge_args_kernel<128>, sgrid, dim3(kThreads), 0, st, prm, md);
+    } else if (d == 64) {
         hipLaunchKernelGGL(paged_attn_merge_kernel<64>, dim3(rgrid), dim3(kThreads), 0, st, prm);
-    else
+    } else {
         hipLaunchKernelGGL(paged_attn_merge_kernel<128>, dim3(rgrid), dim3(kThreads), 0, st, prm);
+    }
     e = hipGetLastError();
     if (e != hipSuccess) return fail(PKV_E_HIP, "%s: merge launch failed: %s", fn, hipGetErrorString(e));
     return ok();
