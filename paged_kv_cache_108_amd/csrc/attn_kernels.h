@@ -1343,7 +1343,9 @@ paged_attn_stream_kernel(AttnParams p) {
 // of entries {sequence, kv head | flags, chunk, L} in one load, the table
 // entries of those chunks in a second, and streams them exactly as the stream
 // kernel does (same chunk order, same arithmetic, same records), so outputs
-// are bit-identical; the merge kernel reads the plan's descriptors. What goes
+// are bit-identical when both run the same number of waves (the planned grid
+// doubles them for chunks of 2 KiB or less); the merge kernel reads the plan's
+// descriptors. What goes
 // away is the per-workgroup lengths scan and prefix, the position search and
 // the window compaction, and their code.
 // Pipeline depth of the planned kernel: chunks of 4 KiB or less (fp8, or bf16

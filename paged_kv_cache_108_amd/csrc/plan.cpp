@@ -4,7 +4,9 @@
 // and the slot mapping. The planned kernel reads each wave's chunk list and
 // the merge descriptors from the plan instead of deriving them from the
 // lengths on the device; the split is the same one (split.h), position for
-// position, so the result is the unplanned kernel's, bit for bit.
+// position, so with the same wave count the result is the unplanned kernel's,
+// bit for bit (with another wave count the pieces differ and the result agrees
+// within rounding).
 #include <algorithm>
 #include <cstdint>
 #include <cstring>

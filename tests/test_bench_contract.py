@@ -25,13 +25,26 @@ def test_recorded_traffic_follows_the_kernel_source(monkeypatch, tmp_path):
     want = int(round(1024 * (m["fetch_kib"] * m["fetch_scale"] + m["write_kib"] * m["write_scale"])))
     same = bench.device_source_sha256() == m["source_sha256"]
     assert got == (want if same else None)
-    # an edit of any device source voids the recorded figure
-    for k in range(len(bench.DEVICE_SOURCES)):
-        paths = list(bench.DEVICE_SOURCES)
+    # an edit of the code of any device source voids the recorded figure; an
+    # added comment or blank line does not (the compiled kernels are the same)
+    sources = list(bench.DEVICE_SOURCES)
+    for k in range(len(sources)):
+        paths = list(sources)
+        text = open(paths[k], "rb").read()
+        other = tmp_path / f"commented_{k}"
+        other.write_bytes(text + b"\n// a note\n\n/* another */\n")
+        paths[k] = str(other)
+        monkeypatch.setattr(bench, "DEVICE_SOURCES", paths)
+        assert bench.measured_traffic("llama8b", "bf16", 16, -1, "planned") == got
         other = tmp_path / f"edited_{k}"
-        other.write_bytes(open(paths[k], "rb").read() + b"\n")
+        other.write_bytes(text + b"\nstatic int pkv_edit_marker;\n")
         paths[k] = str(other)
         monkeypatch.setattr(bench, "DEVICE_SOURCES", paths)
         assert bench.measured_traffic("llama8b", "bf16", 16, -1, "planned") is None
     assert bench.measured_traffic("small", "bf16", 16, -1, "fused") is None       # never measured
     assert bench.measured_traffic("beam", "bf16", 8, -1, "planned") is None       # never measured
+
+
+def test_code_only_keeps_literals_and_drops_comments():
+    src = 'int a = 1; // x\n/* y\n z */ const char* s = "//not a comment";\n\n  char c = \'"\';  \n'
+    assert bench._code_only(src) == 'int a = 1;\n const char* s = "//not a comment";\n  char c = \'"\';'
