@@ -7,8 +7,10 @@ unplanned step's outputs and pools bit for bit, and the planned attention
 alone (no new tokens) the balanced pkv_paged_decode_attn's. Where the planned
 kernel runs twice the waves (chunks of 2 KiB or less: fp8 at d 64) its pieces
 differ, so outputs must agree within the tolerance and pools still byte for
-byte. Every case is also checked against the fp64 oracle. A plan built for
-other lengths, another head count or another wave count is refused.
+byte. A call leaves its plan unchanged, and call after call on one plan
+gives the same bits. Every case is also checked against the fp64 oracle. A
+plan built for other lengths, another head count or another wave count is
+refused.
 """
 
 import numpy as np
@@ -68,6 +70,7 @@ def _planned_case(w, seqs=None):
         assert np.array_equal(to_host(out2), want_attn), "planned attention differs from the balanced call"
     else:
         assert_rows_close(to_host(out2), want_attn.astype(np.float64), TOL[s.cache_dtype], "planned attention")
+    assert np.array_equal(to_host(plan.dev), plan.host), "the call changed its plan"
     kc, vc = oracle_pools(w, seqs)
     ref_o = oracle.paged_decode_attn(w.q, kc, vc, w.block_tables, w.context_lens, bs=s.bs,
                                      softmax_scale=w.softmax_scale, q_dtype=s.q_dtype, cache_dtype=s.cache_dtype,
@@ -108,6 +111,32 @@ def test_planned_many_sequences():
     lens = [int(x) for x in rng.integers(1, 41, 4100)]
     lens[::97] = [0] * len(lens[::97])
     _planned_case(W.make_custom(lens=lens, Hq=4, Hkv=2, d=64, bs=16, cfg=4103))
+
+
+@pytest.mark.parametrize("name,cache", [("llama8b", None), ("small", "fp8"), ("tiny", None)])
+def test_planned_repeated_calls_give_the_same_bits(name, cache):
+    """Call after call on one plan and one workspace gives the same outputs,
+    bit for bit (the split and the merge order depend on the lengths alone)."""
+    torch = need_gpu()
+    w = W.make(name, cache_dtype=cache)
+    s = w.spec
+    print(f"[case] repeated planned calls {s.name} cache={s.cache_dtype}", flush=True)
+    dev = DeviceStep(w)
+    dev.write()                               # the new tokens: attention reads up to L - 1
+    plan = _plan(w)
+    first = None
+    for _ in range(5):
+        out = torch.full((s.S, s.Hq, s.d), float("nan"), dtype=torch.float32, device="cuda")
+        plan(out, dev.q, dev.k_cache, dev.v_cache, dev.tables, dev.lens, softmax_scale=w.softmax_scale,
+             k_scale=w.k_scale, v_scale=w.v_scale)
+        torch.cuda.synchronize()
+        got = to_host(out).copy()
+        if first is None:
+            first = got
+            assert not np.isnan(first).any()
+        else:
+            assert np.array_equal(got, first), "a later call differs"
+    assert np.array_equal(to_host(plan.dev), plan.host)
 
 
 def test_plan_for_other_inputs_is_refused():
