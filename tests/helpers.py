@@ -136,22 +136,33 @@ def oracle_step(w, seqs=None):
     return slots, kc, vc, out
 
 
+_QUANTISE_TABLES = {}
+
+
+def oracle_quantise_bf16(x_bits, inv_scale):
+    """oracle.quantise of bf16 elements at one inverse scale, for pools of any
+    size. The encoder is a function of the 16-bit pattern and the scale alone,
+    so the oracle encodes all 65536 patterns once per scale and the elements
+    are mapped through that table: the same codes as calling the oracle on
+    every element (tests/test_oracle_codec.py checks this), in seconds rather
+    than minutes for a gigabyte pool."""
+    key = float(inv_scale)
+    if key not in _QUANTISE_TABLES:
+        _QUANTISE_TABLES[key] = oracle.quantise(np.arange(1 << 16, dtype=np.uint16), "bf16", key)
+    return _QUANTISE_TABLES[key][np.asarray(x_bits, dtype=np.uint16)]
+
+
 def oracle_pools(w, seqs=None):
     """The oracle's pools after this step's write. fp8: the oracle quantises the
-    blocks that the listed sequences read (all blocks when seqs is None) from the
-    bf16 values itself; other blocks stay zero."""
+    whole bf16 pools (oracle_quantise_bf16) before the write. `seqs` is kept for
+    callers that compare a sample of rows; the pools are always whole."""
     s = w.spec
     slots = oracle.decode_slots(w.block_tables, w.context_lens, s.bs)
     if s.cache_dtype != "fp8":
         return oracle.kv_cache_write(w.k_new, w.v_new, w.k_pool, w.v_pool, slots, bs=s.bs,
                                      src_dtype=s.src_dtype, cache_dtype=s.cache_dtype)
-    rows = range(s.S) if seqs is None else seqs
-    blocks = np.unique(w.block_tables[list(rows)].reshape(-1))
-    blocks = blocks[blocks >= 0]
-    kq = np.zeros(w.k_pool.shape, dtype=np.uint8)
-    vq = np.zeros(w.v_pool.shape, dtype=np.uint8)
-    kq[blocks] = oracle.quantise(w.k_pool[blocks], "bf16", w.k_inv_scale)
-    vq[blocks] = oracle.quantise(w.v_pool[blocks], "bf16", w.v_inv_scale)
+    kq = oracle_quantise_bf16(w.k_pool, w.k_inv_scale)
+    vq = oracle_quantise_bf16(w.v_pool, w.v_inv_scale)
     return oracle.kv_cache_write(w.k_new, w.v_new, kq, vq, slots, bs=s.bs, src_dtype="bf16",
                                  cache_dtype="fp8", k_inv_scale=w.k_inv_scale,
                                  v_inv_scale=w.v_inv_scale)

@@ -16,8 +16,7 @@ import oracle
 import paged_kv_cache_108_amd as pkv
 from paged_kv_cache_108_amd import workloads as W
 from helpers import (TOL, DeviceStep, assert_rows_close, device_decode_step, need_gpu, oracle_pools,
-                     oracle_step, same_bits,
-                     to_dev, to_host)
+                     oracle_quantise_bf16, oracle_step, same_bits, to_dev, to_host)
 
 pytestmark = pytest.mark.gpu
 BAL = pkv.PKV_PARTITION_BALANCED
@@ -68,45 +67,39 @@ def test_beam_block_sizes(bs):
     _full_case(W.make("beam", bs=bs), [0, 512, BAL])
 
 
-def test_long_bf16_sampled():
-    # full-size pool and launch; the oracle computes 3 of the 16 sequences
-    _full_case(W.make("long"), [512, BAL], seqs=[0, 7, 15])
+def test_long_bf16_all_sequences():
+    # full-size pool and launch; the oracle computes all 16 sequences
+    _full_case(W.make("long"), [512, BAL])
 
 
-def test_long_fp8_sampled():
+def test_long_fp8_whole_pool():
+    """`long` with an fp8 cache: the whole quantised pool (every block, K and V)
+    byte for byte against the oracle's encoder, the pools after the write, and
+    every sequence's attention."""
     need_gpu()
     w = W.make("long", cache_dtype="fp8")
     print("[case] long fp8", flush=True)
     dev = DeviceStep(w)
     s = w.spec
-    seqs = [0, 9]
-    blocks = np.unique(w.block_tables[seqs].reshape(-1))
-    blocks = blocks[blocks >= 0]
-    # oracle quantisation of exactly the blocks the sampled sequences read
-    kq = np.zeros(w.k_pool.shape, dtype=np.uint8)
-    vq = np.zeros(w.v_pool.shape, dtype=np.uint8)
-    kq[blocks] = oracle.quantise(w.k_pool[blocks], "bf16", w.k_inv_scale)
-    vq[blocks] = oracle.quantise(w.v_pool[blocks], "bf16", w.v_inv_scale)
-    gk = to_host(dev.k_cache)
-    gv = to_host(dev.v_cache)
-    assert np.array_equal(gk[blocks], kq[blocks]), "quantised K pool differs"
-    assert np.array_equal(gv[blocks], vq[blocks]), "quantised V pool differs"
+    kq = oracle_quantise_bf16(w.k_pool, w.k_inv_scale)
+    vq = oracle_quantise_bf16(w.v_pool, w.v_inv_scale)
+    assert np.array_equal(to_host(dev.k_cache), kq), "quantised K pool differs"
+    assert np.array_equal(to_host(dev.v_cache), vq), "quantised V pool differs"
     slots = oracle.decode_slots(w.block_tables, w.context_lens, s.bs)
     assert np.array_equal(dev.slots_host, slots)
     kc, vc = oracle.kv_cache_write(w.k_new, w.v_new, kq, vq, slots, bs=s.bs, src_dtype="bf16",
                                    cache_dtype="fp8", k_inv_scale=w.k_inv_scale,
                                    v_inv_scale=w.v_inv_scale)
+    del kq, vq
     dev.write()
-    gk = to_host(dev.k_cache)
-    gv = to_host(dev.v_cache)
-    assert np.array_equal(gk[blocks], kc[blocks]) and np.array_equal(gv[blocks], vc[blocks])
+    assert np.array_equal(to_host(dev.k_cache), kc) and np.array_equal(to_host(dev.v_cache), vc)
     ref = oracle.paged_decode_attn(w.q, kc, vc, w.block_tables, w.context_lens, bs=s.bs,
                                    softmax_scale=w.softmax_scale, q_dtype="bf16", cache_dtype="fp8",
-                                   k_scale=w.k_scale, v_scale=w.v_scale, seqs=seqs)
+                                   k_scale=w.k_scale, v_scale=w.v_scale)
     e = 0.0
     for part in (512, BAL):
         out = to_host(dev.attend(part))
-        e = max(e, assert_rows_close(out[seqs], ref, TOL["fp8"], f"long fp8 part={part}"))
+        e = max(e, assert_rows_close(out, ref, TOL["fp8"], f"long fp8 part={part}"))
     print(f"[case] fp8 max row err {e:.3e}", flush=True)
 
 
@@ -428,8 +421,8 @@ def test_window_edge_shapes(lens, Hq, Hkv, d, bs, dt, n_q):
             assert np.all(got[i] == 0.0)
 
 
-def test_window_long_fp8_sampled():
-    _window_case(W.make("long", cache_dtype="fp8"), 3, seqs=[0, 11])
+def test_window_long_fp8_all_sequences():
+    _window_case(W.make("long", cache_dtype="fp8"), 3)
 
 
 # ------------------------------------------------------------------ prefix caching end to end
@@ -495,6 +488,8 @@ def _step_case(w, seqs=None):
     # the same kernels see the same values: bit-identical to the two-call path
     assert np.array_equal(got, want), "fused step differs from write + attend"
     kc, vc = oracle_pools(w, seqs)
+    # the pools after the fused write, every block, against the oracle's
+    assert same_bits(k2, kc) and same_bits(v2, vc), "pools after the step differ from the oracle's"
     ref = oracle.paged_decode_attn(w.q, kc, vc, w.block_tables, w.context_lens, bs=s.bs,
                                    softmax_scale=w.softmax_scale, q_dtype=s.q_dtype,
                                    cache_dtype=s.cache_dtype, k_scale=w.k_scale, v_scale=w.v_scale,
@@ -509,8 +504,8 @@ def test_decode_step(name, bs):
     _step_case(W.make(name, bs=bs))
 
 
-def test_decode_step_long_fp8_sampled():
-    _step_case(W.make("long", cache_dtype="fp8"), seqs=[0, 13])
+def test_decode_step_long_fp8_all_sequences():
+    _step_case(W.make("long", cache_dtype="fp8"))
 
 
 def test_decode_step_edge_shapes():

@@ -84,13 +84,11 @@ def _planned_case(w, seqs=None):
                                            ("beam", 32, None), ("llama8b", 128, None)])
 def test_planned_step_equals_unplanned(name, bs, cache):
     w = W.make(name, bs=bs, cache_dtype=cache)
-    # the oracle computes all rows of the small workloads and a sample of the others
-    seqs = None if name in ("tiny", "small") else list(range(0, w.spec.S, 7))[:10]
-    _planned_case(w, seqs=seqs)
+    _planned_case(w)
 
 
-def test_planned_step_long_sampled():
-    _planned_case(W.make("long"), seqs=[0, 15])
+def test_planned_step_long():
+    _planned_case(W.make("long"))
 
 
 @pytest.mark.parametrize("lens,Hq,Hkv,d,bs,dt", [

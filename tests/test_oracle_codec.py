@@ -124,3 +124,17 @@ def test_e4m3_scaled_widening_matches_torch():
         got = oracle.attention.widen(codes, "fp8", s)
         assert np.array_equal(got, ref * float(s))
         assert np.array_equal(np.signbit(got), np.signbit(ref))
+
+
+@pytest.mark.parametrize("inv_scale", [1.0, 0.125, 3.0])
+def test_table_mapped_quantise_equals_the_oracle(inv_scale):
+    """The GPU tests quantise gigabyte pools by mapping each bf16 pattern
+    through the oracle's codes for all 65536 patterns (helpers.oracle_quantise_bf16).
+    That is the oracle's own result element for element: checked here on every
+    pattern and on a random pool-shaped sample."""
+    from helpers import oracle_quantise_bf16
+    every = np.arange(1 << 16, dtype=np.uint16)
+    assert np.array_equal(oracle_quantise_bf16(every, inv_scale), oracle.quantise(every, "bf16", inv_scale))
+    g = np.random.default_rng([7, int(inv_scale * 8)])
+    pool = g.integers(0, 1 << 16, size=(5, 2, 16, 64), dtype=np.uint16)
+    assert np.array_equal(oracle_quantise_bf16(pool, inv_scale), oracle.quantise(pool, "bf16", inv_scale))
