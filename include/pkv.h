@@ -158,8 +158,9 @@ size_t pkv_paged_decode_attn_workspace_size(int32_t S, int32_t Hq, int32_t Hkv, 
  *    sequence longer than partition_size is split into
  *    ceil(L_i / partition_size) partitions;
  *  - PKV_PARTITION_BALANCED: all (sequence, kv head, 16-token chunk) work,
- *    with each (sequence, kv head) weighted by one extra chunk for its fixed
- *    costs, is cut into equal contiguous shares, one per wave of a grid of one
+ *    with each (sequence, kv head) weighted by 1, 2 or 4 extra chunks (fp32,
+ *    bf16, fp8 caches) for its fixed costs, is cut into equal contiguous
+ *    shares, one per wave of a grid of one
  *    workgroup per compute unit; a long sequence is split wherever the shares
  *    cut it, and every wave finishes at about the same time.
  * workspace: device memory of at least

@@ -7,7 +7,7 @@
 // (sequence, kv head) segment. A segment of n 16-token chunks has
 // seg_cost + n positions: the first seg_cost stand for the fixed cost of
 // starting and finishing a segment (q load, epilogue, partly filled last
-// chunk), about one memory round trip. V positions in all are cut into W
+// chunk). V positions in all are cut into W
 // near-equal contiguous ranges, one per wave, range w being
 // [start(w), start(w + 1)) with the first V % W ranges one longer.
 #pragma once
@@ -32,13 +32,13 @@ enum : int { kKvF32 = 0, kKvBf16 = 1, kKvFp8 = 2 };
 // ranges, so that a merged row has fewer records.
 constexpr unsigned kMinPositions = PKV_MIN_POS;
 
-// Positions a segment costs beyond its chunks: one chunk time for 8 KiB
-// chunks (bf16 at d 128), proportionally more chunks for smaller ones.
-PKV_HD constexpr int seg_cost(int kv, int d) {
-    return 16 * 2 * d * (kv == kKvF32 ? 4 : kv == kKvBf16 ? 2 : 1) >= 8192
-               ? 1
-               : 8192 / (16 * 2 * d * (kv == kKvF32 ? 4 : kv == kKvBf16 ? 2 : 1));
-}
+// Positions a segment costs beyond its chunks: its fixed work (the q rows,
+// the epilogue and its record, the pipeline refill), which grows with d as
+// the chunk does, weighs as much as streaming 128 * d bytes of K and V. That
+// is 4 / (cache element bytes) chunks whatever d: 1 for fp32, 2 for bf16, 4
+// for fp8 caches (measured: half or double these weights leave the waves of
+// a call ending less evenly).
+PKV_HD constexpr int seg_cost(int kv, int) { return kv == kKvF32 ? 1 : kv == kKvBf16 ? 2 : 4; }
 
 // Positions of one (sequence, kv head) segment of L tokens.
 PKV_HD inline unsigned span_of(int L, int cost) { return L > 0 ? (unsigned)cost + (unsigned)((L + 15) >> 4) : 0u; }

@@ -6,8 +6,8 @@ entries are consecutive positions, pieces and descriptors agree.
 The split (the library's, restated here from its definition): work positions
 run sequence-major, then kv head, then position in the (sequence, kv head)
 segment; a segment of n 16-token chunks has c + n positions, the first c
-standing for its fixed cost (c = 1 when a chunk is 8 KiB or more, else
-8192 / chunk bytes); V positions are cut into W = min(n_workers,
+standing for its fixed cost (c = 4 / cache element bytes: 1 for fp32, 2 for
+bf16, 4 for fp8); V positions are cut into W = min(n_workers,
 max(1, ceil(V / 4))) ranges, the first V mod W of them one longer.
 """
 
@@ -22,8 +22,7 @@ ELEM = {"f32": 4, "bf16": 2, "fp8": 1}
 
 
 def seg_cost(dtype, d):
-    cb = 16 * 2 * d * ELEM[dtype]
-    return 1 if cb >= 8192 else 8192 // cb
+    return 4 // ELEM[dtype]
 
 
 def reference_plan(lens, Hkv, d, dtype, max_len, n_workers):
