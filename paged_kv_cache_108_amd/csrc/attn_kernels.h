@@ -147,6 +147,22 @@ struct AttnParams {
     int plan_stride;
 };
 
+// Workgroups go to the XCDs in turn (workgroup b to XCD b mod kXcds), and
+// each XCD has its own L2. xcd_order(b, n) renumbers a grid's workgroups so
+// that each XCD takes runs of kXcdRun consecutive logical workgroups (32
+// waves, a few neighbouring ranges of the balanced split): neighbouring
+// sequences that share prefix blocks, and the waves of one long segment with
+// its q rows and table row, then meet in one L2. Whole rounds of
+// kXcds * kXcdRun workgroups are renumbered and the rest keep their number,
+// so it is a bijection on [0, n) for every n.
+constexpr unsigned kXcds = 8, kXcdRun = 8;
+__device__ __forceinline__ unsigned xcd_order(unsigned b, unsigned n) {
+    constexpr unsigned R = kXcds * kXcdRun;
+    if (b >= n / R * R) return b;
+    const unsigned t = b % R;
+    return b - t + (t % kXcds) * kXcdRun + t / kXcds;
+}
+
 // Clamped context length of sequence s (of either table set).
 __device__ __forceinline__ int clamped_len(const AttnParams& p, int s) {
     if (p.n_pre > 0 && s >= p.n_pre) return min(p.lens2[s - p.n_pre], p.max_len2);
@@ -986,7 +1002,7 @@ paged_attn_stream_kernel(AttnParams p) {
 
     const unsigned V = (unsigned)pre[kThreads] * (unsigned)HS;   // positions in all
     const unsigned W_all = gridDim.x * kWaves;
-    const unsigned w = blockIdx.x * kWaves + wave;
+    const unsigned w = xcd_order(blockIdx.x, gridDim.x) * kWaves + wave;
     // A short input is cut into fewer, longer ranges (at least kMinPositions
     // positions each), so that a merged row has fewer records; the waves past
     // the last range only take part in the write.
@@ -1372,7 +1388,7 @@ paged_attn_plan_kernel(AttnParams p) {
     const int j4 = lane >> 4;
     const int G = p.G;
     const unsigned W_all = gridDim.x * kWaves;
-    const unsigned w = blockIdx.x * kWaves + wave;
+    const unsigned w = xcd_order(blockIdx.x, gridDim.x) * kWaves + wave;
     const int stride = p.plan_stride;
     const int4* ent = reinterpret_cast<const int4*>(p.plan) + (size_t)w * stride;
 
@@ -1650,7 +1666,7 @@ paged_gather_kernel(AttnParams p) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int r16 = lane & 15;
     const int j4 = lane >> 4;
-    const unsigned w = blockIdx.x * kWaves + wave;
+    const unsigned w = xcd_order(blockIdx.x, gridDim.x) * kWaves + wave;
     const int stride = p.plan_stride;
     const int4* ent = reinterpret_cast<const int4*>(p.plan) + (size_t)w * stride;
     constexpr int NB = plan_slots<KV, D>();
