@@ -251,6 +251,26 @@ pkv_status pkv_build_paged_decode_plan(const int32_t* context_lens, int32_t S, i
                                        pkv_dtype cache_dtype, int32_t max_context_len, int32_t n_workers,
                                        void* plan, size_t plan_bytes, size_t* plan_bytes_needed);
 
+/*
+ * The plan of a query window (pkv_paged_multi_query_attn_planned): n_q
+ * queries per sequence, query j at position L_i - n_q + j seeing the tokens
+ * up to it, as in pkv_paged_multi_query_attn ("Serving: vLLM and
+ * PagedAttention", sections 2.4 and 2.7). The (query,
+ * head) pairs of each kv head are cut into n_qg groups of qgs queries, qgs =
+ * min(n_q, max(1, 16 / G)) with G = Hq / Hkv (one 16-column MFMA tile per
+ * group), and every group is a segment of the balanced split with the
+ * sequence's whole chunk list, the kv head's groups next to each other. The
+ * layout is that of the decode plan, with header words 11..14 = n_q, G, qgs,
+ * n_qg (zero in a decode plan), entry field g2 = kv head * n_qg + group, and
+ * one descriptor per (sequence, kv head, group). n_workers from
+ * pkv_paged_decode_plan_workers. Requires n_q > 0, 1 <= Hq/Hkv <= 16 and what
+ * pkv_build_paged_decode_plan requires.
+ */
+pkv_status pkv_build_paged_window_plan(const int32_t* context_lens, int32_t S, int32_t n_q, int32_t Hq,
+                                       int32_t Hkv, int32_t d, pkv_dtype cache_dtype, int32_t max_context_len,
+                                       int32_t n_workers, void* plan, size_t plan_bytes,
+                                       size_t* plan_bytes_needed);
+
 /* Workspace bytes of a planned call: 2 * n_workers * (Hq/Hkv) * (d + 2) * 4,
  * rounded up to a multiple of 256 (the partial records); 0 for invalid sizes. */
 size_t pkv_paged_decode_plan_workspace_size(int32_t n_workers, int32_t Hq, int32_t Hkv, int32_t d);

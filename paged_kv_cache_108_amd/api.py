@@ -17,6 +17,7 @@ from ._lib import (lib, check, PkvError, PkvStats, PKV_F32, PKV_BF16, PKV_FP8_E4
 __all__ = [
     "kv_cache_write", "copy_blocks", "paged_decode_attn", "paged_decode_step", "paged_decode_step_noalloc",
     "paged_decode_plan_workers", "build_paged_decode_plan", "paged_decode_step_planned", "DecodePlan",
+    "build_paged_window_plan",
     "paged_decode_attn_workspace_size",
     "paged_decode_attn_workspace", "paged_multi_query_attn", "paged_multi_query_attn_workspace",
     "Allocator",
@@ -298,6 +299,22 @@ def build_paged_decode_plan(context_lens, Hkv, d, cache_dtype_code, max_context_
     check(lib().pkv_build_paged_decode_plan(_ptr(lens, P_i32), S, Hkv, d, cache_dtype_code, int(max_context_len),
                                             int(n_workers), plan.ctypes.data_as(c_vp), plan.nbytes,
                                             ctypes.byref(need)))
+    return plan
+
+
+def build_paged_window_plan(context_lens, n_q, Hq, Hkv, d, cache_dtype_code, max_context_len, n_workers):
+    """pkv_build_paged_window_plan on host lengths: the plan as an int32 numpy array."""
+    lens = _i32(context_lens)
+    S = len(lens)
+    need = ctypes.c_size_t(0)
+    st = lib().pkv_build_paged_window_plan(_ptr(lens, P_i32), S, int(n_q), Hq, Hkv, d, cache_dtype_code,
+                                           int(max_context_len), int(n_workers), None, 0, ctypes.byref(need))
+    if st not in (PKV_OK, 2):                  # 2: PKV_E_WORKSPACE, the size query
+        check(st)
+    plan = np.zeros(need.value // 4, dtype=np.int32)
+    check(lib().pkv_build_paged_window_plan(_ptr(lens, P_i32), S, int(n_q), Hq, Hkv, d, cache_dtype_code,
+                                            int(max_context_len), int(n_workers), plan.ctypes.data_as(c_vp),
+                                            plan.nbytes, ctypes.byref(need)))
     return plan
 
 

@@ -707,9 +707,10 @@ struct QueryGroups {
 QueryGroups query_groups(int32_t n_q, int32_t G, int32_t d) {
     QueryGroups r;
     r.tiles = (int64_t)n_q * G <= 16 ? 1 : wide_tiles(d);
-    r.qgs = std::min<int32_t>(n_q, std::max<int32_t>(1, 16 * r.tiles / G));
-    r.n_qg = (n_q + r.qgs - 1) / r.qgs;
-    r.cols = G * r.qgs;
+    const pkv_split::QueryGroups q = pkv_split::query_groups_in(n_q, G, r.tiles);
+    r.qgs = q.qgs;
+    r.n_qg = q.n_qg;
+    r.cols = q.cols;
     return r;
 }
 

@@ -26,11 +26,11 @@ struct Entry {
     int flags;
 };
 
-// One decode step's plan, or the number of int32 words it needs.
-pkv_status build_plan(const int32_t* lens, int32_t S, int32_t Hkv, int32_t d, pkv_dtype cache_dtype,
-                      int32_t max_context_len, int32_t n_workers, int32_t* plan, size_t plan_bytes,
-                      size_t* plan_bytes_needed) {
-    const char* fn = "build_paged_decode_plan";
+// One step's plan, or the number of int32 words it needs: decode (n_q = 0)
+// or a window of n_q queries per sequence over G query heads per kv head.
+pkv_status build_plan(const char* fn, const int32_t* lens, int32_t S, int32_t n_q, int32_t G, int32_t Hkv,
+                      int32_t d, pkv_dtype cache_dtype, int32_t max_context_len, int32_t n_workers, int32_t* plan,
+                      size_t plan_bytes, size_t* plan_bytes_needed) {
     if (S <= 0 || Hkv <= 0 || n_workers <= 0 || max_context_len < 0)
         return fail(PKV_E_INVALID, "%s: S=%d Hkv=%d n_workers=%d max_context_len=%d", fn, S, Hkv, n_workers,
                     max_context_len);
@@ -43,13 +43,19 @@ pkv_status build_plan(const int32_t* lens, int32_t S, int32_t Hkv, int32_t d, pk
     if (!lens) return fail(PKV_E_INVALID, "%s: NULL pointer", fn);
     if (n_workers > (1 << 20)) return fail(PKV_E_INVALID, "%s: n_workers=%d too large", fn, n_workers);
     const int cost = seg_cost(kv, d);
+    // decode: one segment per (sequence, kv head); a window: n_qg per kv head
+    // (one 16-column tile each), the kv head's groups next to each other
+    const QueryGroups qgr = n_q > 0 ? query_groups_in(n_q, G, 1) : QueryGroups{1, 1, G};
+    const int64_t HS64 = (int64_t)Hkv * qgr.n_qg;
+    if (HS64 > 0xFFFF) return fail(PKV_E_INVALID, "%s: %lld segments per sequence", fn, (long long)HS64);
+    const int32_t HS = (int32_t)HS64;
 
     // positions, sequence-major, as the kernel enumerates them
     std::vector<int32_t> L(S);
     uint64_t V64 = 0;
     for (int32_t i = 0; i < S; ++i) {
         L[i] = std::min(lens[i], max_context_len);
-        V64 += (uint64_t)span_of(L[i], cost) * (uint64_t)Hkv;
+        V64 += (uint64_t)span_of(L[i], cost) * (uint64_t)HS;
     }
     if (V64 > 0x7FFFFFFFull) return fail(PKV_E_INVALID, "%s: too many work positions", fn);
     const unsigned V = (unsigned)V64;
@@ -57,7 +63,7 @@ pkv_status build_plan(const int32_t* lens, int32_t S, int32_t Hkv, int32_t d, pk
 
     // each wave's chunks, in order
     std::vector<std::vector<Entry>> waves(W);
-    std::vector<int32_t> desc((size_t)S * Hkv * 2, 0);
+    std::vector<int32_t> desc((size_t)S * HS * 2, 0);
     if (W > 0) {
         const Split split(V, W);
         unsigned pos = 0;
@@ -65,7 +71,7 @@ pkv_status build_plan(const int32_t* lens, int32_t S, int32_t Hkv, int32_t d, pk
             const unsigned sp = span_of(L[i], cost);
             if (sp == 0) continue;
             const int nch = (L[i] + 15) >> 4;
-            for (int32_t g = 0; g < Hkv; ++g) {
+            for (int32_t g = 0; g < HS; ++g) {
                 // the segment's chunks sit at positions pos + cost .. pos + sp - 1
                 const unsigned p0 = pos + (unsigned)cost;
                 const unsigned w_lo = split.owner(p0), w_hi = split.owner(pos + sp - 1);
@@ -75,8 +81,8 @@ pkv_status build_plan(const int32_t* lens, int32_t S, int32_t Hkv, int32_t d, pk
                 }
                 // w_lo's record is 2 w_lo when the segment holds its first chunk
                 const bool lo_first = split.start(w_lo) + (unsigned)cost >= p0;
-                desc[((size_t)i * Hkv + g) * 2] = (int32_t)(2 * w_lo + (lo_first ? 0 : 1));
-                desc[((size_t)i * Hkv + g) * 2 + 1] = (int32_t)(w_hi - w_lo + 1);
+                desc[((size_t)i * HS + g) * 2] = (int32_t)(2 * w_lo + (lo_first ? 0 : 1));
+                desc[((size_t)i * HS + g) * 2 + 1] = (int32_t)(w_hi - w_lo + 1);
                 pos += sp;
             }
         }
@@ -118,6 +124,12 @@ pkv_status build_plan(const int32_t* lens, int32_t S, int32_t Hkv, int32_t d, pk
     h[8] = max_context_len;
     h[9] = d;
     h[10] = kv;
+    if (n_q > 0) {
+        h[11] = n_q;
+        h[12] = G;
+        h[13] = qgr.qgs;
+        h[14] = qgr.n_qg;
+    }
     int32_t* ent = plan + kPlanHeader;
     for (size_t w = 0; w < (size_t)n_workers; ++w) {
         for (size_t k = 0; k < stride; ++k) {
@@ -146,6 +158,18 @@ extern "C" pkv_status pkv_build_paged_decode_plan(const int32_t* context_lens, i
                                                   pkv_dtype cache_dtype, int32_t max_context_len,
                                                   int32_t n_workers, void* plan, size_t plan_bytes,
                                                   size_t* plan_bytes_needed) {
-    return build_plan(context_lens, S, Hkv, d, cache_dtype, max_context_len, n_workers,
+    return build_plan("build_paged_decode_plan", context_lens, S, 0, 0, Hkv, d, cache_dtype, max_context_len,
+                      n_workers, static_cast<int32_t*>(plan), plan_bytes, plan_bytes_needed);
+}
+
+extern "C" pkv_status pkv_build_paged_window_plan(const int32_t* context_lens, int32_t S, int32_t n_q, int32_t Hq,
+                                                  int32_t Hkv, int32_t d, pkv_dtype cache_dtype,
+                                                  int32_t max_context_len, int32_t n_workers, void* plan,
+                                                  size_t plan_bytes, size_t* plan_bytes_needed) {
+    const char* fn = "build_paged_window_plan";
+    if (n_q <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || Hq / Hkv > 16)
+        return fail(PKV_E_INVALID, "%s: n_q=%d Hq=%d Hkv=%d (need n_q > 0 and 1 <= Hq/Hkv <= 16)", fn, n_q, Hq,
+                    Hkv);
+    return build_plan(fn, context_lens, S, n_q, Hq / Hkv, Hkv, d, cache_dtype, max_context_len, n_workers,
                       static_cast<int32_t*>(plan), plan_bytes, plan_bytes_needed);
 }

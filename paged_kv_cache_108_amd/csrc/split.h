@@ -60,16 +60,36 @@ struct Split {
     }
 };
 
+// Query windows (n_q queries per sequence): the (query, head) pairs of one kv
+// head are cut into n_qg groups of qgs queries, so that a group's cols =
+// G * qgs columns fit `tiles` 16-column MFMA tiles; each group is a segment
+// of its own, with the chunks of the whole sequence. Decode is n_q = 1: one
+// group of G columns.
+struct QueryGroups {
+    int qgs, n_qg, cols;
+};
+PKV_HD inline QueryGroups query_groups_in(int n_q, int G, int tiles) {
+    QueryGroups r;
+    const int per = 16 * tiles / G;
+    r.qgs = n_q < (per > 1 ? per : 1) ? n_q : (per > 1 ? per : 1);
+    r.n_qg = (n_q + r.qgs - 1) / r.qgs;
+    r.cols = G * r.qgs;
+    return r;
+}
+
 // ---------------------------------------------------------------------------
-// The work plan (pkv_build_paged_decode_plan, int32 words):
+// The work plan (pkv_build_paged_decode_plan, pkv_build_paged_window_plan;
+// int32 words):
 //   header[16]: kPlanMagic, kPlanVersion, n_workers (waves of the grid it was
 //               built for), W (waves with a range), S, Hkv, seg_cost, stride
-//               (entries per wave), max_context_len, d, kv kind, 5 x 0
+//               (entries per wave), max_context_len, d, kv kind, then for a
+//               window plan n_q, G, qgs, n_qg (0 0 0 0 in a decode plan), 0
 //   entries[n_workers][stride][4]: wave w's chunks in processing order, each
-//               {sequence i, kv head g | flags << 16, chunk index kc, L_i};
-//               unused entries have i = -1
-//   desc[S * Hkv][2]: per segment (first record, record count) for the merge
-//               (a count of 1 or less: the segment was processed whole)
+//               {sequence i, segment column group g2 | flags << 16, chunk
+//               index kc, L_i}, g2 = kv head * n_qg + query group (the kv
+//               head in a decode plan); unused entries have i = -1
+//   desc[S * Hkv * n_qg][2]: per segment (first record, record count) for
+//               the merge (a count of 1 or less: processed whole)
 // ---------------------------------------------------------------------------
 constexpr int32_t kPlanMagic = 0x504B5650;   // "PKVP"
 constexpr int32_t kPlanVersion = 1;

@@ -25,18 +25,23 @@ def seg_cost(dtype, d):
     return 4 // ELEM[dtype]
 
 
-def reference_plan(lens, Hkv, d, dtype, max_len, n_workers):
-    """The plan, from the definition (plain Python)."""
+def reference_plan(lens, Hkv, d, dtype, max_len, n_workers, n_q=0, G=0):
+    """The plan, from the definition (plain Python). n_q > 0: a window plan,
+    whose segments are (sequence, kv head, query group) with groups of
+    qgs = min(n_q, max(1, 16 // G)) queries (one 16-column tile)."""
     c = seg_cost(dtype, d)
     L = [min(int(x), max_len) for x in lens]
     S = len(L)
-    segs = []                                 # (i, g, first position, n chunks)
+    qgs = min(n_q, max(1, 16 // G)) if n_q else 1
+    n_qg = -(-n_q // qgs) if n_q else 1
+    HS = Hkv * n_qg                           # segments per sequence
+    segs = []                                 # (i, g2, first position, n chunks)
     pos = 0
     for i in range(S):
         n = -(-L[i] // 16) if L[i] > 0 else 0
         if n == 0:
             continue
-        for g in range(Hkv):
+        for g in range(HS):
             segs.append((i, g, pos, n))
             pos += c + n
     V = pos
@@ -49,13 +54,13 @@ def reference_plan(lens, Hkv, d, dtype, max_len, n_workers):
         return x // (q + 1) if x < big else r + (x - big) // q
 
     waves = [[] for _ in range(Wn)]
-    desc = np.zeros((S * Hkv, 2), dtype=np.int64)
+    desc = np.zeros((S * HS, 2), dtype=np.int64)
     for i, g, p, n in segs:
         p0 = p + c
         for kc in range(n):
             waves[owner(p0 + kc)].append([i, g, kc, L[i], 0])
         w_lo, w_hi = owner(p0), owner(p0 + n - 1)
-        desc[i * Hkv + g] = (2 * w_lo + (0 if start[w_lo] >= p else 1), w_hi - w_lo + 1)
+        desc[i * HS + g] = (2 * w_lo + (0 if start[w_lo] >= p else 1), w_hi - w_lo + 1)
     for ent in waves:
         a = 0
         while a < len(ent):
@@ -70,7 +75,8 @@ def reference_plan(lens, Hkv, d, dtype, max_len, n_workers):
                     ent[k][4] |= 8
             a = b + 1
     stride = max([len(e) for e in waves] + [1])
-    out = [0x504B5650, 1, n_workers, Wn, S, Hkv, c, stride, max_len, d, KIND[dtype], 0, 0, 0, 0, 0]
+    window = [n_q, G, qgs, n_qg] if n_q else [0, 0, 0, 0]
+    out = [0x504B5650, 1, n_workers, Wn, S, Hkv, c, stride, max_len, d, KIND[dtype]] + window + [0]
     for w in range(n_workers):
         ent = waves[w] if w < Wn else []
         for k in range(stride):
@@ -136,3 +142,45 @@ def test_plan_clamps_lengths_and_rejects_bad_arguments():
         kw.update(bad)
         with pytest.raises(pkv.PkvError):
             pkv.build_paged_decode_plan([10, 20], kw["Hkv"], kw["d"], 1, 32, kw["workers"])
+
+
+@pytest.mark.parametrize("name,kv,n_q,workers", [
+    ("llama8b", None, 4, 1024), ("llama8b", None, 8, 1024), ("llama8b", None, 16, 1024),
+    ("small", None, 4, 1024), ("small", "fp8", 3, 2048), ("tiny", None, 20, 1024),
+])
+def test_window_plan_matches_the_definition(name, kv, n_q, workers):
+    w = W.make(name, cache_dtype=kv)
+    s = w.spec
+    G = s.Hq // s.Hkv
+    got = pkv.build_paged_window_plan(w.context_lens, n_q, s.Hq, s.Hkv, s.d, KIND[s.cache_dtype],
+                                      w.max_context_len, workers)
+    want = reference_plan(w.context_lens, s.Hkv, s.d, s.cache_dtype, w.max_context_len, workers, n_q=n_q, G=G)
+    assert got.shape == want.shape
+    assert np.array_equal(got.astype(np.int64), want)
+    qgs = int(got[13])
+    assert got[11] == n_q and got[12] == G and qgs * G <= 16 and got[14] * qgs >= n_q
+
+
+def test_window_plan_long_lengths():
+    # the long-context shape (16 x 32768 tokens, 8 kv heads, G 8), lengths only
+    lens = [32768] * 16
+    got = pkv.build_paged_window_plan(lens, 3, 64, 8, 128, 1, 32768, 1024)
+    want = reference_plan(lens, 8, 128, "bf16", 32768, 1024, n_q=3, G=8)
+    assert np.array_equal(got.astype(np.int64), want)
+
+
+def test_window_plan_of_one_query_is_the_decode_plan_but_the_header():
+    w = W.make("llama8b")
+    s = w.spec
+    dec = pkv.build_paged_decode_plan(w.context_lens, s.Hkv, s.d, 1, w.max_context_len, 1024)
+    win = pkv.build_paged_window_plan(w.context_lens, 1, s.Hq, s.Hkv, s.d, 1, w.max_context_len, 1024)
+    assert np.array_equal(dec[16:], win[16:]) and np.array_equal(dec[:11], win[:11])
+    assert list(win[11:15]) == [1, s.Hq // s.Hkv, 1, 1] and list(dec[11:15]) == [0, 0, 0, 0]
+
+
+def test_window_plan_rejects_bad_arguments():
+    for kw in [dict(n_q=0), dict(Hq=12, Hkv=8), dict(Hq=34, Hkv=2)]:
+        a = dict(n_q=2, Hq=8, Hkv=2)
+        a.update(kw)
+        with pytest.raises(pkv.PkvError):
+            pkv.build_paged_window_plan([10, 20], a["n_q"], a["Hq"], a["Hkv"], 64, 1, 32, 16)
