@@ -353,12 +353,25 @@ def run_other_op(args, w, torch, pkv):
         tables, lens = dev(w.block_tables), dev(w.context_lens)
         out = torch.empty((s.S, n_q, s.Hq, s.d), dtype=torch.float32, device="cuda")
         ws = pkv.paged_multi_query_attn_workspace(s.S, n_q, s.Hq, s.Hkv, s.d)
+        plan = pkv.WindowPlan(w.context_lens, n_q=n_q, Hq=s.Hq, Hkv=s.Hkv, d=s.d, bs=s.bs,
+                              cache_dtype_code={"f32": 0, "bf16": 1, "fp8": 2}[cache_dtype],
+                              max_context_len=w.max_context_len)
 
-        def fn():
+        def fn_unplanned():
             pkv.paged_multi_query_attn(out, q, k_cache, v_cache, tables, lens,
                                        max_context_len=w.max_context_len,
                                        softmax_scale=w.softmax_scale, k_scale=w.k_scale,
                                        v_scale=w.v_scale, workspace=ws, stream=stream)
+
+        def fn_planned():
+            plan(out, q, k_cache, v_cache, tables, lens, softmax_scale=w.softmax_scale, k_scale=w.k_scale,
+                 v_scale=w.v_scale, stream=stream)
+        # the planned call for windows that fit one 16-column group per kv head;
+        # wider ones take two tiles per pass in the unplanned call, which is faster
+        planned = args.window_call == "planned" or (args.window_call == "auto" and n_q * G <= 16)
+        fn, other = (fn_planned, fn_unplanned) if planned else (fn_unplanned, fn_planned)
+        if planned:
+            tiles, qgs, n_qg = 1, int(plan.host[13]), int(plan.host[14])
         attn, _, _, unique_tokens = algorithmic_bytes(w, cache_dtype)
         dec_q = s.S * s.Hq * s.d * ELEM[s.q_dtype]
         dec_out = s.S * s.Hq * s.d * 4
@@ -366,9 +379,10 @@ def run_other_op(args, w, torch, pkv):
         byts = once + n_q * (dec_q + dec_out)
         passes = once * n_qg + n_q * (dec_q + dec_out)
         metric = "paged multi-query (window) attention: achieved HBM GB/s at 1 GPU"
-        kernel = "paged_multi_query_attn call (stream kernel, window instantiation + merge kernel)"
-        cfg = {"window": n_q, "column_tiles": tiles, "queries_per_pass": qgs, "passes": n_qg,
-               "bytes_with_passes": passes,
+        kernel = ("paged_multi_query_attn_planned call (planned kernel, window mode + merge kernel)" if planned
+                  else "paged_multi_query_attn call (stream kernel, window instantiation + merge kernel)")
+        cfg = {"window": n_q, "call": "planned" if planned else "unplanned", "column_tiles": tiles,
+               "queries_per_pass": qgs, "passes": n_qg, "bytes_with_passes": passes,
                "note": "value counts K/V once; a window needing several passes reads K/V once per pass "
                        "(bytes_with_passes)"}
     elif args.op == "shared":
@@ -402,6 +416,11 @@ def run_other_op(args, w, torch, pkv):
         cfg = {"pairs": n, "bytes_per_pair": 4 * per_pool}
     mean, med, mn, wall = _timed(args, torch, fn, flush, stream)
     gbs = byts / (mean * 1e-3) / 1e9
+    if args.op == "window":
+        # the other window call on the same inputs, for comparison
+        o_mean, o_med, _, _ = _timed(args, torch, other, flush, stream)
+        cfg["other_call"] = {"call": "unplanned" if planned else "planned", "ms_mean": round(o_mean, 5),
+                             "ms_median": round(o_med, 5)}
     print(json.dumps({
         "metric": metric, "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(mean, 5),
@@ -485,6 +504,9 @@ def main():
                          "(pkv_seq_create_prefixed), no GPU; shared: shared-prefix decode step "
                          "(pkv_paged_shared_prefix_decode) for groups of --group sequences")
     ap.add_argument("--window", type=int, default=4, help="queries per sequence for --op window")
+    ap.add_argument("--window-call", default="auto", choices=["auto", "planned", "unplanned"],
+                    help="--op window: the call timed (auto: planned when the window fits one 16-column group "
+                         "per kv head, else unplanned); the other is timed beside it")
     ap.add_argument("--pairs", type=int, default=1024, help="block pairs for --op copy")
     ap.add_argument("--group", type=int, default=4, help="sequences per group for --op shared")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",

@@ -271,6 +271,33 @@ pkv_status pkv_build_paged_window_plan(const int32_t* context_lens, int32_t S, i
                                        int32_t n_workers, void* plan, size_t plan_bytes,
                                        size_t* plan_bytes_needed);
 
+/* Workspace bytes of a planned window call: 2 * n_workers * cols * (d + 2) * 4
+ * rounded up to a multiple of 256, cols = G * qgs (the partial records); 0
+ * for invalid sizes. */
+size_t pkv_paged_window_plan_workspace_size(int32_t n_workers, int32_t n_q, int32_t Hq, int32_t Hkv, int32_t d);
+
+/*
+ * pkv_paged_multi_query_attn with its work split by a window plan built on
+ * the host (pkv_build_paged_window_plan), in the planned kernel. Arguments,
+ * layouts and result as for pkv_paged_multi_query_attn, plus plan_host (its
+ * header is checked against the call: S, n_q, Hq/Hkv, Hkv, d, cache type,
+ * max_context_len and this device's wave count) and plan_dev (a device copy
+ * of all plan_bytes, read by the kernels). Where the unplanned call also runs
+ * one 16-column tile per pass (n_q * Hq/Hkv <= 16) the split is the same and
+ * so are the outputs, bit for bit; wider windows take one pass per group of
+ * 16 columns here (the unplanned call takes 32 per pass) and agree to
+ * rounding. The workspace (pkv_paged_window_plan_workspace_size bytes) need
+ * not be initialised; calls that overlap in time must not share it.
+ */
+pkv_status pkv_paged_multi_query_attn_planned(float* out, const void* q, const void* k_cache, const void* v_cache,
+                                              const int32_t* block_tables, const int32_t* context_lens, int32_t S,
+                                              int32_t n_q, int32_t Hq, int32_t Hkv, int32_t d, int32_t bs,
+                                              int32_t P, int32_t max_blocks, int32_t max_context_len,
+                                              float softmax_scale, float k_scale, float v_scale, pkv_dtype q_dtype,
+                                              pkv_dtype cache_dtype, const void* plan_host, const void* plan_dev,
+                                              size_t plan_bytes, void* workspace, size_t workspace_bytes,
+                                              void* stream);
+
 /* Workspace bytes of a planned call: 2 * n_workers * (Hq/Hkv) * (d + 2) * 4,
  * rounded up to a multiple of 256 (the partial records); 0 for invalid sizes. */
 size_t pkv_paged_decode_plan_workspace_size(int32_t n_workers, int32_t Hq, int32_t Hkv, int32_t d);

@@ -57,6 +57,11 @@ SIGNATURES = {
                                                      c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_f32, c_f32, c_f32,
                                                      c_f32, c_f32, ctypes.c_int, ctypes.c_int, c_vp, c_vp, c_sz,
                                                      c_vp, c_sz, c_vp, c_vp]),
+    "pkv_paged_window_plan_workspace_size": (c_sz, [c_i32, c_i32, c_i32, c_i32, c_i32]),
+    "pkv_paged_multi_query_attn_planned": (ctypes.c_int, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_i32, c_i32,
+                                                          c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_f32, c_f32,
+                                                          c_f32, ctypes.c_int, ctypes.c_int, c_vp, c_vp, c_sz, c_vp,
+                                                          c_sz, c_vp]),
     "pkv_paged_decode_step_scratch_bytes": (c_sz, []),
     "pkv_paged_decode_step_noalloc": (ctypes.c_int, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32,
                                                      c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_f32,

@@ -17,7 +17,7 @@ from ._lib import (lib, check, PkvError, PkvStats, PKV_F32, PKV_BF16, PKV_FP8_E4
 __all__ = [
     "kv_cache_write", "copy_blocks", "paged_decode_attn", "paged_decode_step", "paged_decode_step_noalloc",
     "paged_decode_plan_workers", "build_paged_decode_plan", "paged_decode_step_planned", "DecodePlan",
-    "build_paged_window_plan",
+    "build_paged_window_plan", "paged_multi_query_attn_planned", "WindowPlan",
     "paged_decode_attn_workspace_size",
     "paged_decode_attn_workspace", "paged_multi_query_attn", "paged_multi_query_attn_workspace",
     "Allocator",
@@ -351,6 +351,31 @@ def paged_decode_step_planned(out, q, k_new, v_new, k_cache, v_cache, block_tabl
         _event(attn_done_event)))
 
 
+def paged_multi_query_attn_planned(out, q, k_cache, v_cache, block_tables, context_lens, *, max_context_len,
+                                   softmax_scale, plan_host, plan_dev, workspace, k_scale=1.0, v_scale=1.0,
+                                   stream=None):
+    """pkv_paged_multi_query_attn_planned: pkv_paged_multi_query_attn with a
+    window plan (build_paged_window_plan). out float32 [S][n_q][Hq][d]; q
+    [S][n_q][Hq][d]; plan_host the int32 numpy plan, plan_dev its int32 device
+    copy; workspace of pkv_paged_window_plan_workspace_size bytes."""
+    import torch
+    P, Hkv, bs, d = _pools("paged_multi_query_attn_planned", k_cache, v_cache)
+    S, Hq = _attn_args("paged_multi_query_attn_planned", out, q, k_cache, block_tables, context_lens, d, n_q=True)
+    n_q = q.shape[1]
+    plan_host = np.ascontiguousarray(plan_host, dtype=np.int32)
+    if plan_dev.dtype != torch.int32 or plan_dev.numel() != plan_host.size:
+        raise ValueError("paged_multi_query_attn_planned: plan_dev must be the int32 device copy of plan_host")
+    _one_device("paged_multi_query_attn_planned", out, q, k_cache, v_cache, block_tables, context_lens, plan_dev,
+                workspace)
+    check(lib().pkv_paged_multi_query_attn_planned(
+        _dev(out, "out"), _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+        _dev(block_tables, "block_tables"), _dev(context_lens, "context_lens"), S, n_q, Hq, Hkv, d, bs, P,
+        block_tables.shape[1], int(max_context_len), float(softmax_scale), float(k_scale), float(v_scale),
+        _dtype_code(q), _dtype_code(k_cache), plan_host.ctypes.data_as(c_vp), _dev(plan_dev, "plan_dev"),
+        plan_host.nbytes, _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+        _stream(stream)))
+
+
 def paged_gather_read(k_cache, v_cache, block_tables, sink, *, max_context_len, plan_host, plan_dev, stream=None):
     """pkv_paged_gather_read: the plan's K/V chunks read through the tables, no
     arithmetic (the step's own read pattern, for timing). sink: an int32
@@ -401,6 +426,31 @@ class DecodePlan:
                                   plan_host=self.host, plan_dev=self.dev, workspace=self.workspace,
                                   k_scale=k_scale, v_scale=v_scale, k_inv_scale=k_inv_scale,
                                   v_inv_scale=v_inv_scale, stream=stream, attn_done_event=attn_done_event)
+
+
+class WindowPlan:
+    """A query window's work plan (build_paged_window_plan), uploaded once, with
+    the workspace it needs; __call__ runs pkv_paged_multi_query_attn_planned."""
+
+    def __init__(self, context_lens, *, n_q, Hq, Hkv, d, bs, cache_dtype_code, max_context_len, device="cuda"):
+        import torch
+        self.n_q = int(n_q)
+        self.n_workers = paged_decode_plan_workers(d, bs, cache_dtype_code)
+        self.max_context_len = int(max_context_len)
+        self.host = build_paged_window_plan(context_lens, self.n_q, Hq, Hkv, d, cache_dtype_code,
+                                            self.max_context_len, self.n_workers)
+        self.dev = torch.from_numpy(self.host).to(device)
+        need = int(lib().pkv_paged_window_plan_workspace_size(self.n_workers, self.n_q, Hq, Hkv, d))
+        if need == 0:
+            raise ValueError("WindowPlan: invalid sizes")
+        self.workspace = torch.empty(need, dtype=torch.uint8, device=device)
+
+    def __call__(self, out, q, k_cache, v_cache, block_tables, context_lens, *, softmax_scale, k_scale=1.0,
+                 v_scale=1.0, stream=None):
+        paged_multi_query_attn_planned(out, q, k_cache, v_cache, block_tables, context_lens,
+                                       max_context_len=self.max_context_len, softmax_scale=softmax_scale,
+                                       plan_host=self.host, plan_dev=self.dev, workspace=self.workspace,
+                                       k_scale=k_scale, v_scale=v_scale, stream=stream)
 
 
 def paged_multi_query_attn_workspace(S, n_q, Hq, Hkv, d, device="cuda"):

@@ -59,19 +59,30 @@ AttnKernel pick_kernel(int bs, int mode, int tiles, bool partition) {
 
 template AttnKernel pick_kernel<PKV_INST_KV, PKV_INST_D>(int, int, int, bool);
 
-template <int KV, int D>
-AttnKernel pick_plan_kernel(int bs, bool step) {
+template <int KV, int D, int PM>
+AttnKernel plan_for_bs(int bs) {
     switch (bs) {
-        case 8: return step ? paged_attn_plan_kernel<KV, D, 8, true> : paged_attn_plan_kernel<KV, D, 8, false>;
-        case 16: return step ? paged_attn_plan_kernel<KV, D, 16, true> : paged_attn_plan_kernel<KV, D, 16, false>;
-        case 32: return step ? paged_attn_plan_kernel<KV, D, 32, true> : paged_attn_plan_kernel<KV, D, 32, false>;
-        case 64: return step ? paged_attn_plan_kernel<KV, D, 64, true> : paged_attn_plan_kernel<KV, D, 64, false>;
-        case 128: return step ? paged_attn_plan_kernel<KV, D, 128, true> : paged_attn_plan_kernel<KV, D, 128, false>;
+        case 8: return paged_attn_plan_kernel<KV, D, 8, PM>;
+        case 16: return paged_attn_plan_kernel<KV, D, 16, PM>;
+        case 32: return paged_attn_plan_kernel<KV, D, 32, PM>;
+        case 64: return paged_attn_plan_kernel<KV, D, 64, PM>;
+        case 128: return paged_attn_plan_kernel<KV, D, 128, PM>;
     }
     return nullptr;
 }
 
-template AttnKernel pick_plan_kernel<PKV_INST_KV, PKV_INST_D>(int, bool);
+// mode: PM_ATTN, PM_STEP or PM_WINDOW
+template <int KV, int D>
+AttnKernel pick_plan_kernel(int bs, int mode) {
+    switch (mode) {
+        case PM_ATTN: return plan_for_bs<KV, D, PM_ATTN>(bs);
+        case PM_STEP: return plan_for_bs<KV, D, PM_STEP>(bs);
+        case PM_WINDOW: return plan_for_bs<KV, D, PM_WINDOW>(bs);
+    }
+    return nullptr;
+}
+
+template AttnKernel pick_plan_kernel<PKV_INST_KV, PKV_INST_D>(int, int);
 
 template <int KV, int D>
 AttnKernel pick_gather_kernel(int bs) {

@@ -1378,15 +1378,28 @@ template <int KV, int D> constexpr int plan_slots() {
     return 16 * 2 * D * elem <= 4096 ? PKV_PLAN_SLOTS_SMALL : PKV_PLAN_SLOTS_LARGE;
 }
 
-template <int KV, int D, int BS, bool STEP>
+// Planned kernel modes: decode attention alone, the decode step (attention
+// with the new token's write fused in), and a query window (n_q queries per
+// sequence, causal inside the window; each segment of the plan is one group
+// of qgs queries, G * qgs <= 16 columns of one MFMA tile).
+enum PlanMode { PM_ATTN = 0, PM_STEP = 1, PM_WINDOW = 2 };
+
+template <int KV, int D, int BS, int PM>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1)))
 paged_attn_plan_kernel(AttnParams p) {
+    constexpr bool STEP = PM == PM_STEP;
+    constexpr bool MQ = PM == PM_WINDOW;
     __shared__ __align__(16) uint32_t ntstage[kWaves][D / 2];   // per wave: fp8 new-token codes
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int r16 = lane & 15;
     const int j4 = lane >> 4;
     const int G = p.G;
+    // a window: this lane's column r16 is query col_j of its group, head col_r
+    // of the kv head's G; decode: query 0, head r16
+    const int n_q = MQ ? p.n_q : 1;
+    const int col_j = MQ ? r16 / G : 0;
+    const int col_r = MQ ? r16 - col_j * G : r16;
     const unsigned W_all = gridDim.x * kWaves;
     const unsigned w = xcd_order(blockIdx.x, gridDim.x) * kWaves + wave;
     const int stride = p.plan_stride;
@@ -1475,9 +1488,10 @@ paged_attn_plan_kernel(AttnParams p) {
     // sequences with no tokens: zero rows
     for (int s = blockIdx.x; s < p.S; s += gridDim.x)
         if (clamped_len(p, s) <= 0) {
-            for (int e = threadIdx.x; e < p.Hq * D; e += kThreads) st_untracked(p.out + (size_t)s * p.Hq * D + e, 0.f);
+            const size_t rows = (size_t)n_q * p.Hq;
+            for (int e = threadIdx.x; e < (int)rows * D; e += kThreads) st_untracked(p.out + (size_t)s * rows * D + e, 0.f);
             if (p.lse)
-                for (int e = threadIdx.x; e < p.Hq; e += kThreads) st_untracked(p.lse + (size_t)s * p.Hq + e, -INFINITY);
+                for (int e = threadIdx.x; e < (int)rows; e += kThreads) st_untracked(p.lse + (size_t)s * rows + e, -INFINITY);
         }
 
     // Pipeline slots: a chunk in flight with, when its entry starts a piece,
@@ -1498,7 +1512,29 @@ paged_attn_plan_kernel(AttnParams p) {
     float m_run = -INFINITY, l_run = 0.f;
 #pragma unroll
     for (int s2 = 0; s2 < D / 16; ++s2) o[s2] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const bool live = r16 < G;
+    // segment column group g2 -> kv head g; this lane's query j (windows), its
+    // q/out row and whether its column is in use
+    struct Col {
+        int g, j;
+        bool live;
+        size_t row;
+    };
+    auto column = [&](int i, int g2) {
+        Col c;
+        if constexpr (MQ) {
+            c.g = g2 / p.n_qg;
+            c.j = (g2 - c.g * p.n_qg) * p.qgs + col_j;
+            c.live = r16 < p.cols && c.j < n_q;
+            c.row = (((size_t)i * n_q + c.j) * p.Hq + c.g * G + col_r) * D;
+        } else {
+            c.g = g2;
+            c.j = 0;
+            c.live = r16 < G;
+            c.row = ((size_t)i * p.Hq + g2 * G + r16) * D;
+        }
+        return c;
+    };
+    const int C = MQ ? p.cols : G;            // record rows per piece
 
     for (int kb = 0; kb < stride; kb += 64) {
         if (kb > 0) {
@@ -1521,10 +1557,11 @@ paged_attn_plan_kernel(AttnParams p) {
             const int i = __builtin_amdgcn_readlane(mi, kk);
             const int gf = real ? __builtin_amdgcn_readlane(mgf, kk) : 0;
             const int kc = real ? __builtin_amdgcn_readlane(mkc, kk) : 0;
-            const int g = gf & 0xFFFF;
+            const Col c = column(i, gf & 0xFFFF);
+            const int g = c.g;
             load_chunk<KV, D, BS>(x.f, p, b0, b1, 16 * kc, g, r16, j4);
-            if ((gf >> 16) & pkv_split::kFirst)     // padding heads read row 0; step zeroes them
-                load_q_raw<KV, D>(p, live ? ((size_t)i * p.Hq + g * G + r16) * D : 0, j4, x.q);
+            if ((gf >> 16) & pkv_split::kFirst)     // unused columns read row 0; step zeroes them
+                load_q_raw<KV, D>(p, c.live ? c.row : 0, j4, x.q);
             if constexpr (STEP) {
                 const int L = __builtin_amdgcn_readlane(mL, kk);
                 if (real && kc == ((L + 15) >> 4) - 1)
@@ -1538,10 +1575,11 @@ paged_attn_plan_kernel(AttnParams p) {
             const int gf = __builtin_amdgcn_readlane(mgf, k);
             const int kc = __builtin_amdgcn_readlane(mkc, k);
             const int L = __builtin_amdgcn_readlane(mL, k);
-            const int g = gf & 0xFFFF;
+            const Col c = column(i, gf & 0xFFFF);
+            const bool live = c.live;
+            const size_t out_row = c.row;
             const int flags = gf >> 16;
             const int nch = (L + 15) >> 4;
-            const size_t out_row = ((size_t)i * p.Hq + g * G + r16) * D;
             if (flags & pkv_split::kFirst) {      // a piece of a segment starts
 #pragma unroll
                 for (int u = 0; u < q_loads<KV, D>(); ++u) qf[u] = live ? x.q[u] : QF{};
@@ -1557,20 +1595,26 @@ paged_attn_plan_kernel(AttnParams p) {
                     if constexpr (!kVRows) patch_new_v<KV, D>(f, nt, L - 1 - tc, j4);
                 }
             const bool tail = tc + 16 > L;
+            // a window: query j sees tokens < L - n_q + 1 + j (causal inside it)
+            const bool masked = MQ ? tc + 16 > L - n_q + 1 : tail;
+            const int lim = MQ ? L - n_q + 1 + c.j : L;
             const int first_tok = tc + 4 * j4;
             const f32x4 sc = chunk_scores<KV, D>(f, qf);
             float xs[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 xs[e] = sc[e] * p.qk_scale;
-                if (tail && first_tok + e >= L) xs[e] = -INFINITY;
+                if (masked && first_tok + e >= lim) xs[e] = -INFINITY;
             }
             const float cm = head_max(fmaxf(fmaxf(xs[0], xs[1]), fmaxf(xs[2], xs[3])));
             const float m_new = fmaxf(m_run, cm);
-            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+            // a column that has seen no visible token yet keeps m = -inf; its
+            // exponentials are taken against 0 so they stay 0, not NaN
+            const float m_ref = MQ && m_new == -INFINITY ? 0.f : m_new;
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_ref);
             float pr[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) pr[e] = __builtin_amdgcn_exp2f(xs[e] - m_new);
+            for (int e = 0; e < 4; ++e) pr[e] = __builtin_amdgcn_exp2f(xs[e] - m_ref);
             l_run = l_run * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
             m_run = m_new;
             if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
@@ -1594,14 +1638,14 @@ paged_attn_plan_kernel(AttnParams p) {
                         for (int s2 = 0; s2 < D / 16; ++s2) st_untracked(orow + 16 * s2, o[s2] * sc_o);
                         if (p.lse && j4 == 0) st_untracked(p.lse + out_row / D, m_run + __log2f(l_tot));
                     } else {
-                        const size_t rr = (size_t)(2 * w + ((flags & pkv_split::kOdd) ? 1 : 0)) * G + r16;
+                        const size_t rr = (size_t)(2 * w + ((flags & pkv_split::kOdd) ? 1 : 0)) * C + r16;
                         const size_t nrec = (size_t)p.n_rec;
                         float* orec = p.ws + rr * D + 4 * j4;
 #pragma unroll
                         for (int s2 = 0; s2 < D / 16; ++s2) st_untracked(orec + 16 * s2, o[s2] * p.v_scale);
                         if (j4 == 0) {
-                            st_untracked(p.ws + nrec * G * D + rr, m_run);
-                            st_untracked(p.ws + nrec * G * (D + 1) + rr, l_tot);
+                            st_untracked(p.ws + nrec * C * D + rr, m_run);
+                            st_untracked(p.ws + nrec * C * (D + 1) + rr, l_tot);
                         }
                     }
                 }
@@ -1732,7 +1776,7 @@ AttnKernel pick_kernel(int bs, int mode, int tiles, bool partition);
 
 // The planned kernel for one cache type and head dim (attn_inst.hip).
 template <int KV, int D>
-AttnKernel pick_plan_kernel(int bs, bool step);
+AttnKernel pick_plan_kernel(int bs, int mode);
 
 // The gather-only kernel for one cache type and head dim (attn_inst.hip).
 template <int KV, int D>

@@ -335,16 +335,26 @@ paged_attn_merge_args_kernel(AttnParams p, MergeArgDesc md) {
     const float* ws = p.ws;
     float* out = p.out;
     float* lse = p.lse;
-    const int nrec = p.n_rec, cols = p.cols, Hkv = p.Hkv, Hq = p.Hq, G = p.G;
-    asm volatile("" : : "s"(x), "s"(ws), "s"(out), "s"(lse), "s"(nrec), "s"(cols), "s"(Hkv), "s"(Hq), "s"(G));
+    const int nrec = p.n_rec, cols = p.cols, Hkv = p.Hkv, Hq = p.Hq, G = p.G, n_q = p.n_q, qgs = p.qgs,
+              n_qg = p.n_qg;
+    asm volatile("" : : "s"(x), "s"(ws), "s"(out), "s"(lse), "s"(nrec), "s"(cols), "s"(Hkv), "s"(Hq), "s"(G),
+                 "s"(n_q), "s"(qgs), "s"(n_qg));
     const int n = (int)(x >> 13);
     if (n <= 1) return;                       // whole, or an empty sequence
     const int rec0 = (int)(x & 0x1FFFu);
-    const int i = (int)blockIdx.x / Hkv;
-    const int g = (int)blockIdx.x - i * Hkv;
+    // segment (sequence i, kv head g, query group qg); column r of its cols is
+    // query qg * qgs + r / G of the window, head g * G + r % G
+    const int HS = Hkv * n_qg;
+    const int i = (int)blockIdx.x / HS;
+    const int g2 = (int)blockIdx.x - i * HS;
+    const int g = g2 / n_qg;
+    const int qg = g2 - g * n_qg;
     const int r = kWaves * (int)blockIdx.y + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    if (r >= G) return;
-    merge_records<D>(p, (long long)i * Hq + g * G + r, r, n, rec0, true);
+    if (r >= cols) return;
+    const int jr = r / G;
+    const int j = qg * qgs + jr;
+    if (j >= n_q) return;
+    merge_records<D>(p, ((long long)i * n_q + j) * Hq + g * G + (r - jr * G), r, n, rec0, true);
 }
 
 // Two attention states of the same rows over disjoint token sets (a shared
@@ -525,10 +535,10 @@ AttnKernel pick_gather(int kv, int d, int bs) {
     return d == 64 ? pick_gather_kernel<KV_FP8, 64>(bs) : pick_gather_kernel<KV_FP8, 128>(bs);
 }
 
-AttnKernel pick_plan(int kv, int d, int bs, bool step) {
-    if (kv == KV_F32) return d == 64 ? pick_plan_kernel<KV_F32, 64>(bs, step) : pick_plan_kernel<KV_F32, 128>(bs, step);
-    if (kv == KV_BF16) return d == 64 ? pick_plan_kernel<KV_BF16, 64>(bs, step) : pick_plan_kernel<KV_BF16, 128>(bs, step);
-    return d == 64 ? pick_plan_kernel<KV_FP8, 64>(bs, step) : pick_plan_kernel<KV_FP8, 128>(bs, step);
+AttnKernel pick_plan(int kv, int d, int bs, int mode) {
+    if (kv == KV_F32) return d == 64 ? pick_plan_kernel<KV_F32, 64>(bs, mode) : pick_plan_kernel<KV_F32, 128>(bs, mode);
+    if (kv == KV_BF16) return d == 64 ? pick_plan_kernel<KV_BF16, 64>(bs, mode) : pick_plan_kernel<KV_BF16, 128>(bs, mode);
+    return d == 64 ? pick_plan_kernel<KV_FP8, 64>(bs, mode) : pick_plan_kernel<KV_FP8, 128>(bs, mode);
 }
 
 // Compute units of the current device (cached per device).
@@ -1028,10 +1038,14 @@ namespace {
 // The step and the attention-only kernels share the grid (one plan serves
 // both): the smaller of their residencies decides.
 int plan_workers(int kv, int d, int bs) {
-    const AttnKernel ks = pick_plan(kv, d, bs, true), ka = pick_plan(kv, d, bs, false);
-    if (!ks || !ka) return -1;
-    const int rs = resident_workgroups(ks, 0), ra = resident_workgroups(ka, 0);
-    const int resident = rs < ra ? rs : ra;
+    // the smallest residency of the three modes: a plan serves any of them
+    int resident = 1 << 30;
+    for (int mode : {PM_ATTN, PM_STEP, PM_WINDOW}) {
+        const AttnKernel k = pick_plan(kv, d, bs, mode);
+        if (!k) return -1;
+        const int r = resident_workgroups(k, 0);
+        if (r < resident) resident = r;
+    }
     const int cus = compute_units();
     if (resident <= 0 || cus <= 0) return -1;
     const int chunk_bytes = 16 * 2 * d * (kv == KV_F32 ? 4 : kv == KV_BF16 ? 2 : 1);
@@ -1042,10 +1056,12 @@ int plan_workers(int kv, int d, int bs) {
 }
 
 // The plan's header against the call (S, Hkv, d, cache kind, max_context_len,
-// size) and this device's wave count; n_workers and stride from it.
+// the window: n_q queries over G heads per kv head, 0 for a decode plan; its
+// size) and this device's wave count; n_workers, stride and the query
+// grouping (qgs, n_qg; 1 and 1 for decode) from it.
 pkv_status check_plan(const char* fn, const void* plan_host, const void* plan_dev, size_t plan_bytes, int32_t S,
-                      int32_t Hkv, int32_t d, int32_t bs, int kv, int32_t max_context_len, int32_t* n_workers,
-                      int32_t* stride) {
+                      int32_t n_q, int32_t G, int32_t Hkv, int32_t d, int32_t bs, int kv, int32_t max_context_len,
+                      int32_t* n_workers, int32_t* stride, int32_t* qgs, int32_t* n_qg) {
     if (!plan_host || !plan_dev) return fail(PKV_E_INVALID, "%s: NULL plan", fn);
     if (plan_bytes < pkv_split::kPlanHeader * sizeof(int32_t))
         return fail(PKV_E_INVALID, "%s: plan of %zu bytes", fn, plan_bytes);
@@ -1056,9 +1072,23 @@ pkv_status check_plan(const char* fn, const void* plan_host, const void* plan_de
         return fail(PKV_E_INVALID, "%s: the plan was built for S=%d Hkv=%d max_context_len=%d d=%d kv=%d, "
                     "not S=%d Hkv=%d max_context_len=%d d=%d kv=%d", fn, h[4], h[5], h[8], h[9], h[10], S, Hkv,
                     max_context_len, d, kv);
+    if (h[11] != n_q || (n_q > 0 && h[12] != G))
+        return fail(PKV_E_INVALID, "%s: the plan was built for a window of %d queries over %d heads per kv head "
+                    "(0: a decode plan), not %d over %d", fn, h[11], h[12], n_q, G);
+    *qgs = 1;
+    *n_qg = 1;
+    if (n_q > 0) {
+        const pkv_split::QueryGroups q = pkv_split::query_groups_in(n_q, G, 1);
+        if (h[13] != q.qgs || h[14] != q.n_qg)
+            return fail(PKV_E_INVALID, "%s: the plan's query groups (%d x %d) are not those of %d queries over %d "
+                        "heads", fn, h[14], h[13], n_q, G);
+        *qgs = q.qgs;
+        *n_qg = q.n_qg;
+    }
     *n_workers = h[2];
     *stride = h[7];
-    const size_t words = (size_t)pkv_split::kPlanHeader + (size_t)*n_workers * *stride * 4 + (size_t)S * Hkv * 2;
+    const size_t words = (size_t)pkv_split::kPlanHeader + (size_t)*n_workers * *stride * 4 +
+                         (size_t)S * Hkv * (size_t)*n_qg * 2;
     if (*stride <= 0 || *n_workers <= 0 || plan_bytes < words * sizeof(int32_t))
         return fail(PKV_E_INVALID, "%s: plan of %zu bytes, its header describes %zu", fn, plan_bytes,
                     words * sizeof(int32_t));
@@ -1070,9 +1100,12 @@ pkv_status check_plan(const char* fn, const void* plan_host, const void* plan_de
     return ok();
 }
 
+// A planned call: the decode step or attention (n_q = 0, a decode plan) or a
+// query window of n_q queries per sequence (a window plan; no write).
 pkv_status plan_launch(const char* fn, float* out, const void* q, const void* k_new, const void* v_new,
                        void* k_cache, void* v_cache, const int32_t* block_tables, const int32_t* context_lens,
-                       int32_t S, int32_t Hq, int32_t Hkv, int32_t d, int32_t bs, int32_t P, int32_t max_blocks,
+                       int32_t S, int32_t n_q, int32_t Hq, int32_t Hkv, int32_t d, int32_t bs, int32_t P,
+                       int32_t max_blocks,
                        int32_t max_context_len, float softmax_scale, float k_scale, float v_scale,
                        float k_inv_scale, float v_inv_scale, pkv_dtype q_dtype, pkv_dtype cache_dtype,
                        const void* plan_host, const void* plan_dev, size_t plan_bytes, void* workspace,
@@ -1084,17 +1117,20 @@ pkv_status plan_launch(const char* fn, float* out, const void* q, const void* k_
     wr.k_inv = cache_dtype == PKV_FP8_E4M3 ? k_inv_scale : 1.f;
     wr.v_inv = cache_dtype == PKV_FP8_E4M3 ? v_inv_scale : 1.f;
     // the arguments shared with the unplanned call, checked the same way
-    pkv_status rc = attn_launch(fn, out, q, k_cache, v_cache, block_tables, context_lens, S, 1, Hq, Hkv, d, bs,
-                                P, max_blocks, max_context_len, softmax_scale, k_scale, v_scale, q_dtype,
+    if (n_q > 0 && is_step) return fail(PKV_E_INVALID, "%s: a window call writes no new tokens", fn);
+    pkv_status rc = attn_launch(fn, out, q, k_cache, v_cache, block_tables, context_lens, S, n_q > 0 ? n_q : 1, Hq,
+                                Hkv, d, bs, P, max_blocks, max_context_len, softmax_scale, k_scale, v_scale, q_dtype,
                                 cache_dtype, PKV_PARTITION_BALANCED, nullptr, 0, stream, wr, nullptr, true, true,
                                 nullptr, true, true);
     if (rc != PKV_OK || S == 0) return rc;
     const int kv = cache_dtype == PKV_F32 ? KV_F32 : cache_dtype == PKV_BF16 ? KV_BF16 : KV_FP8;
-    int32_t n_workers = 0, stride = 0;
-    rc = check_plan(fn, plan_host, plan_dev, plan_bytes, S, Hkv, d, bs, kv, max_context_len, &n_workers, &stride);
-    if (rc != PKV_OK) return rc;
     const int32_t G = Hq / Hkv;
-    const size_t need = grid_records_bytes(n_workers, (size_t)G, d);
+    int32_t n_workers = 0, stride = 0, qgs = 1, n_qg = 1;
+    rc = check_plan(fn, plan_host, plan_dev, plan_bytes, S, n_q, G, Hkv, d, bs, kv, max_context_len, &n_workers,
+                    &stride, &qgs, &n_qg);
+    if (rc != PKV_OK) return rc;
+    const int32_t cols = G * qgs;             // record rows per piece
+    const size_t need = grid_records_bytes(n_workers, (size_t)cols, d);
     if (!workspace || workspace_bytes < need)
         return fail(PKV_E_WORKSPACE, "%s: workspace %zu bytes, need %zu", fn, workspace_bytes, need);
 
@@ -1117,10 +1153,10 @@ pkv_status plan_launch(const char* fn, float* out, const void* q, const void* k_
     prm.P = P;
     prm.max_blocks = max_blocks;
     prm.max_len = max_context_len;
-    prm.n_q = 1;
-    prm.qgs = 1;
-    prm.n_qg = 1;
-    prm.cols = G;
+    prm.n_q = n_q > 0 ? n_q : 1;
+    prm.qgs = qgs;
+    prm.n_qg = n_qg;
+    prm.cols = cols;
     prm.part_tokens = 32;
     prm.n_part = 1;
     prm.balanced = 1;
@@ -1134,7 +1170,8 @@ pkv_status plan_launch(const char* fn, float* out, const void* q, const void* k_
     prm.n_workers = n_workers;
     prm.n_rec = 2 * n_workers;
     auto st = static_cast<hipStream_t>(stream);
-    hipLaunchKernelGGL(pick_plan(kv, d, bs, is_step), dim3((unsigned)(n_workers / kWaves)), dim3(kThreads), 0, st,
+    const int mode = n_q > 0 ? PM_WINDOW : is_step ? PM_STEP : PM_ATTN;
+    hipLaunchKernelGGL(pick_plan(kv, d, bs, mode), dim3((unsigned)(n_workers / kWaves)), dim3(kThreads), 0, st,
                        prm);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(PKV_E_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
@@ -1142,17 +1179,18 @@ pkv_status plan_launch(const char* fn, float* out, const void* q, const void* k_
         e = hipEventRecord(static_cast<hipEvent_t>(attn_done_event), st);
         if (e != hipSuccess) return fail(PKV_E_HIP, "%s: event record failed: %s", fn, hipGetErrorString(e));
     }
-    const unsigned rgrid = (unsigned)(((int64_t)S * Hq + kWaves - 1) / kWaves);
-    if ((int64_t)S * Hkv <= kArgDescs) {
+    const unsigned rgrid = (unsigned)(((int64_t)S * prm.n_q * Hq + kWaves - 1) / kWaves);
+    const int64_t n_seg = (int64_t)S * Hkv * n_qg;
+    if (n_seg <= kArgDescs) {
         // the plan's descriptors by value (the host copy holds them)
         MergeArgDesc md;
         const int32_t* hd = static_cast<const int32_t*>(plan_host) + pkv_split::kPlanHeader +
                             (size_t)n_workers * stride * 4;
-        for (int64_t x = 0; x < (int64_t)S * Hkv; ++x) {
+        for (int64_t x = 0; x < n_seg; ++x) {
             const uint32_t rec0 = (uint32_t)hd[2 * x], cnt = (uint32_t)hd[2 * x + 1];
             md.d[x] = cnt <= 1 ? 0u : (rec0 & 0x1FFFu) | (cnt << 13);
         }
-        const dim3 sgrid((unsigned)(S * Hkv), (unsigned)((G + kWaves - 1) / kWaves));
+        const dim3 sgrid((unsigned)n_seg, (unsigned)((cols + kWaves - 1) / kWaves));
         if (d == 64)
             hipLaunchKernelGGL(paged_attn_merge_args_kernel<64>, sgrid, dim3(kThreads), 0, st, prm, md);
         else
@@ -1200,9 +1238,9 @@ extern "C" pkv_status pkv_paged_gather_read(const void* k_cache, const void* v_c
         return fail(PKV_E_INVALID, "%s: max_context_len=%d exceeds max_blocks*bs=%lld", fn, max_context_len,
                     (long long)max_blocks * bs);
     const int kv = cache_dtype == PKV_F32 ? KV_F32 : cache_dtype == PKV_BF16 ? KV_BF16 : KV_FP8;
-    int32_t n_workers = 0, stride = 0;
-    pkv_status rc = check_plan(fn, plan_host, plan_dev, plan_bytes, S, Hkv, d, bs, kv, max_context_len, &n_workers,
-                               &stride);
+    int32_t n_workers = 0, stride = 0, qgs = 1, n_qg = 1;
+    pkv_status rc = check_plan(fn, plan_host, plan_dev, plan_bytes, S, 0, 0, Hkv, d, bs, kv, max_context_len,
+                               &n_workers, &stride, &qgs, &n_qg);
     if (rc != PKV_OK) return rc;
     AttnParams prm{};
     prm.k = k_cache;
@@ -1235,9 +1273,30 @@ extern "C" pkv_status pkv_paged_decode_step_planned(
     if (S > 0 && (k_new == nullptr) != (v_new == nullptr))
         return fail(PKV_E_INVALID, "paged_decode_step_planned: k_new and v_new must both be given or both be NULL");
     return plan_launch("paged_decode_step_planned", out, q, k_new, v_new, k_cache, v_cache, block_tables,
-                       context_lens, S, Hq, Hkv, d, bs, P, max_blocks, max_context_len, softmax_scale, k_scale,
+                       context_lens, S, 0, Hq, Hkv, d, bs, P, max_blocks, max_context_len, softmax_scale, k_scale,
                        v_scale, k_inv_scale, v_inv_scale, q_dtype, cache_dtype, plan_host, plan_dev, plan_bytes,
                        workspace, workspace_bytes, stream, attn_done_event);
+}
+
+extern "C" size_t pkv_paged_window_plan_workspace_size(int32_t n_workers, int32_t n_q, int32_t Hq, int32_t Hkv,
+                                                      int32_t d) {
+    if (n_workers <= 0 || n_q <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || Hq / Hkv > 16 || !pkv::is_head_dim(d))
+        return 0;
+    const pkv_split::QueryGroups q = pkv_split::query_groups_in(n_q, Hq / Hkv, 1);
+    return grid_records_bytes(n_workers, (size_t)q.cols, d);
+}
+
+extern "C" pkv_status pkv_paged_multi_query_attn_planned(
+    float* out, const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
+    const int32_t* context_lens, int32_t S, int32_t n_q, int32_t Hq, int32_t Hkv, int32_t d, int32_t bs, int32_t P,
+    int32_t max_blocks, int32_t max_context_len, float softmax_scale, float k_scale, float v_scale,
+    pkv_dtype q_dtype, pkv_dtype cache_dtype, const void* plan_host, const void* plan_dev, size_t plan_bytes,
+    void* workspace, size_t workspace_bytes, void* stream) {
+    if (n_q <= 0) return fail(PKV_E_INVALID, "paged_multi_query_attn_planned: n_q=%d", n_q);
+    return plan_launch("paged_multi_query_attn_planned", out, q, nullptr, nullptr, const_cast<void*>(k_cache),
+                       const_cast<void*>(v_cache), block_tables, context_lens, S, n_q, Hq, Hkv, d, bs, P,
+                       max_blocks, max_context_len, softmax_scale, k_scale, v_scale, 1.f, 1.f, q_dtype,
+                       cache_dtype, plan_host, plan_dev, plan_bytes, workspace, workspace_bytes, stream, nullptr);
 }
 
 extern "C" pkv_status pkv_paged_decode_attn_lse(float* out, float* lse, const void* q,
