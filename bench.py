@@ -94,28 +94,28 @@ def device_source_sha256(paths=None):
 # the kernel source is the one the counters were taken with.
 MEASURED_TRAFFIC = {
     ("llama8b", "bf16", 16, -1, "planned"): {
-        "source_sha256": "314f771d98c68c9ee3b7e14929b4446214477aeb8a6eaf913b0b8eeed7eea01a",
-        "fetch_kib": 170395.4, "write_kib": 5939.0, "fetch_scale": 2.0, "write_scale": 1.0,
+        "source_sha256": "122b7c1568bf262c8f1f1566eccb2373b0c2e3cf56885bc4d8e0ce99a7a3a632",
+        "fetch_kib": 170403.5, "write_kib": 5938.9, "fetch_scale": 2.0, "write_scale": 1.0,
     },
     ("small", "bf16", 16, -1, "planned"): {
-        "source_sha256": "314f771d98c68c9ee3b7e14929b4446214477aeb8a6eaf913b0b8eeed7eea01a",
-        "fetch_kib": 34309.2, "write_kib": 4412.8, "fetch_scale": 2.0, "write_scale": 1.0,
+        "source_sha256": "122b7c1568bf262c8f1f1566eccb2373b0c2e3cf56885bc4d8e0ce99a7a3a632",
+        "fetch_kib": 34320.6, "write_kib": 4412.8, "fetch_scale": 2.0, "write_scale": 1.0,
     },
     ("llama8b", "fp8", 16, -1, "planned"): {
-        "source_sha256": "314f771d98c68c9ee3b7e14929b4446214477aeb8a6eaf913b0b8eeed7eea01a",
-        "fetch_kib": 86437.5, "write_kib": 4805.6, "fetch_scale": 2.0, "write_scale": 1.0,
+        "source_sha256": "122b7c1568bf262c8f1f1566eccb2373b0c2e3cf56885bc4d8e0ce99a7a3a632",
+        "fetch_kib": 86439.1, "write_kib": 4805.8, "fetch_scale": 2.0, "write_scale": 1.0,
     },
     ("small", "fp8", 16, -1, "planned"): {
-        "source_sha256": "314f771d98c68c9ee3b7e14929b4446214477aeb8a6eaf913b0b8eeed7eea01a",
-        "fetch_kib": 19026.2, "write_kib": 5530.5, "fetch_scale": 2.0, "write_scale": 1.0,
+        "source_sha256": "122b7c1568bf262c8f1f1566eccb2373b0c2e3cf56885bc4d8e0ce99a7a3a632",
+        "fetch_kib": 19034.8, "write_kib": 5530.5, "fetch_scale": 2.0, "write_scale": 1.0,
     },
     ("long", "bf16", 16, -1, "planned"): {
-        "source_sha256": "314f771d98c68c9ee3b7e14929b4446214477aeb8a6eaf913b0b8eeed7eea01a",
-        "fetch_kib": 1054216.0, "write_kib": 5730.8, "fetch_scale": 2.0, "write_scale": 1.0,
+        "source_sha256": "122b7c1568bf262c8f1f1566eccb2373b0c2e3cf56885bc4d8e0ce99a7a3a632",
+        "fetch_kib": 1054201.8, "write_kib": 5730.1, "fetch_scale": 2.0, "write_scale": 1.0,
     },
     ("long", "fp8", 16, -1, "planned"): {
-        "source_sha256": "314f771d98c68c9ee3b7e14929b4446214477aeb8a6eaf913b0b8eeed7eea01a",
-        "fetch_kib": 529504.9, "write_kib": 5453.5, "fetch_scale": 2.0, "write_scale": 1.0,
+        "source_sha256": "122b7c1568bf262c8f1f1566eccb2373b0c2e3cf56885bc4d8e0ce99a7a3a632",
+        "fetch_kib": 529509.3, "write_kib": 5453.8, "fetch_scale": 2.0, "write_scale": 1.0,
     },
 }
 
