@@ -606,7 +606,7 @@ def main():
         code = {"f32": pkv.PKV_F32, "bf16": pkv.PKV_BF16, "fp8": pkv.PKV_FP8_E4M3}[cache_dtype]
         t0 = time.perf_counter()
         plan = pkv.DecodePlan(w.context_lens, Hq=s.Hq, Hkv=s.Hkv, d=s.d, bs=s.bs, cache_dtype_code=code,
-                              max_context_len=w.max_context_len)
+                              max_context_len=w.max_context_len, block_tables=w.block_tables)
         torch.cuda.synchronize()
         t_plan = time.perf_counter() - t0
         t0 = time.perf_counter()
@@ -614,8 +614,10 @@ def main():
         t_build = time.perf_counter() - t0
         plan_info = {"host_build_ms": round(1e3 * t_build, 3), "build_and_upload_ms": round(1e3 * t_plan, 3),
                      "bytes": int(plan.host.nbytes), "waves": int(plan.n_workers),
+                     "shared_blocks": plan.shared_blocks,
                      "note": "built on the host from the host lengths before the timed region (step a0, as the "
-                             "block tables); one plan serves every layer of a step"}
+                             "block tables), and marked from the host tables when sequences share blocks "
+                             "(cacheable K/V loads); one plan serves every layer of a step"}
 
         def planned_step():
             plan(out, q, k_cache, v_cache, tables, lens, softmax_scale=w.softmax_scale, k_new=k_new,

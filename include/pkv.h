@@ -242,7 +242,8 @@ int32_t pkv_paged_decode_plan_workers(int32_t d, int32_t bs, pkv_dtype cache_dty
  * the size the plan needs, and a call with plan NULL or too small returns
  * PKV_E_WORKSPACE after setting it. The plan is int32 words: a 16-word header
  * (magic "PKVP", version, n_workers, waves used, S, Hkv, segment cost, entries
- * per wave, max_context_len, d, cache kind), then per wave its chunk entries
+ * per wave, max_context_len, d, cache kind, four window words that are zero
+ * here, flags), then per wave its chunk entries
  * {sequence, kv head | flags << 16, chunk index, L} (unused: sequence -1),
  * then one (first record, record count) descriptor per (sequence, kv head).
  * Requires S > 0, Hkv > 0, d in {64, 128}, n_workers > 0.
@@ -250,6 +251,25 @@ int32_t pkv_paged_decode_plan_workers(int32_t d, int32_t bs, pkv_dtype cache_dty
 pkv_status pkv_build_paged_decode_plan(const int32_t* context_lens, int32_t S, int32_t Hkv, int32_t d,
                                        pkv_dtype cache_dtype, int32_t max_context_len, int32_t n_workers,
                                        void* plan, size_t plan_bytes, size_t* plan_bytes_needed);
+
+/*
+ * Mark in a decode plan whether its batch shares physical blocks: whether any
+ * block id appears more than once among the blocks the sequences read (the
+ * first ceil(min(L_i, max_context_len) / bs) entries of each table row) --
+ * the prefix blocks of beams or of sequences forked from one prompt ("03 ·
+ * PagedAttention", "Sharing: copy-on-write": a shared block is listed by
+ * every table that uses it). block_tables: host int32 [S][max_blocks], the
+ * tables the call passes on the device; context_lens: host int32 [S]. Sets
+ * or clears the plan's flags word (header word 15) and *shared (when not
+ * NULL). A plan so marked runs its decode kernels with cacheable K/V loads,
+ * so that the waves reading one shared block can meet in L2 instead of each
+ * reading it from HBM; unmarked plans keep streaming (evict-first) loads,
+ * which are faster when every block is read once. The result is the same
+ * either way, bit for bit; upload the plan after marking it.
+ */
+pkv_status pkv_plan_mark_shared_blocks(void* plan, size_t plan_bytes, const int32_t* block_tables,
+                                       const int32_t* context_lens, int32_t S, int32_t max_blocks, int32_t bs,
+                                       int32_t* shared);
 
 /*
  * The plan of a query window (pkv_paged_multi_query_attn_planned): n_q

@@ -7,7 +7,7 @@ arguments to it. ``workloads`` draws the seeded synthetic inputs.
 
 from .api import (kv_cache_write, copy_blocks, paged_decode_attn, paged_decode_step, paged_decode_step_noalloc,
                   paged_decode_plan_workers, build_paged_decode_plan, paged_decode_step_planned, DecodePlan,
-                  build_paged_window_plan, paged_multi_query_attn_planned, WindowPlan,
+                  build_paged_window_plan, paged_multi_query_attn_planned, WindowPlan, plan_mark_shared_blocks,
                   stream_read, paged_gather_read, paged_decode_attn_workspace_size,
                   paged_decode_attn_workspace, paged_multi_query_attn,
                   paged_multi_query_attn_workspace, Allocator,
@@ -20,7 +20,7 @@ from ._lib import lib, LIB_PATH, SIGNATURES, PKV_F32, PKV_BF16, PKV_FP8_E4M3
 __all__ = [
     "kv_cache_write", "copy_blocks", "paged_decode_attn", "paged_decode_step", "paged_decode_step_noalloc",
     "paged_decode_plan_workers", "build_paged_decode_plan", "paged_decode_step_planned", "DecodePlan",
-    "build_paged_window_plan", "paged_multi_query_attn_planned", "WindowPlan",
+    "build_paged_window_plan", "paged_multi_query_attn_planned", "WindowPlan", "plan_mark_shared_blocks",
     "stream_read", "paged_gather_read", "paged_decode_attn_workspace_size",
     "paged_decode_attn_workspace", "paged_multi_query_attn", "paged_multi_query_attn_workspace",
     "Allocator",

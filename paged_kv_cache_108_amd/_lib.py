@@ -53,6 +53,7 @@ SIGNATURES = {
     "pkv_build_paged_window_plan": (ctypes.c_int, [P_i32, c_i32, c_i32, c_i32, c_i32, c_i32, ctypes.c_int, c_i32,
                                                    c_i32, c_vp, c_sz, ctypes.POINTER(c_sz)]),
     "pkv_paged_decode_plan_workspace_size": (c_sz, [c_i32, c_i32, c_i32, c_i32]),
+    "pkv_plan_mark_shared_blocks": (ctypes.c_int, [c_vp, c_sz, P_i32, P_i32, c_i32, c_i32, c_i32, P_i32]),
     "pkv_paged_decode_step_planned": (ctypes.c_int, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_i32,
                                                      c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_f32, c_f32, c_f32,
                                                      c_f32, c_f32, ctypes.c_int, ctypes.c_int, c_vp, c_vp, c_sz,

@@ -17,7 +17,7 @@ from ._lib import (lib, check, PkvError, PkvStats, PKV_F32, PKV_BF16, PKV_FP8_E4
 __all__ = [
     "kv_cache_write", "copy_blocks", "paged_decode_attn", "paged_decode_step", "paged_decode_step_noalloc",
     "paged_decode_plan_workers", "build_paged_decode_plan", "paged_decode_step_planned", "DecodePlan",
-    "build_paged_window_plan", "paged_multi_query_attn_planned", "WindowPlan",
+    "build_paged_window_plan", "paged_multi_query_attn_planned", "WindowPlan", "plan_mark_shared_blocks",
     "paged_decode_attn_workspace_size",
     "paged_decode_attn_workspace", "paged_multi_query_attn", "paged_multi_query_attn_workspace",
     "Allocator",
@@ -302,6 +302,21 @@ def build_paged_decode_plan(context_lens, Hkv, d, cache_dtype_code, max_context_
     return plan
 
 
+def plan_mark_shared_blocks(plan, block_tables, context_lens, bs):
+    """pkv_plan_mark_shared_blocks on a host plan (int32 numpy, changed in
+    place) from the host tables [S][max_blocks] and lengths [S]; returns
+    whether the batch shares blocks."""
+    tables = np.ascontiguousarray(block_tables, dtype=np.int32)
+    lens = _i32(context_lens)
+    if tables.ndim != 2 or tables.shape[0] != len(lens):
+        raise ValueError("plan_mark_shared_blocks: tables must be [S][max_blocks] with S = len(context_lens)")
+    shared = ctypes.c_int32(0)
+    check(lib().pkv_plan_mark_shared_blocks(plan.ctypes.data_as(c_vp), plan.nbytes, _ptr(tables, P_i32),
+                                            _ptr(lens, P_i32), len(lens), tables.shape[1], int(bs),
+                                            ctypes.byref(shared)))
+    return bool(shared.value)
+
+
 def build_paged_window_plan(context_lens, n_q, Hq, Hkv, d, cache_dtype_code, max_context_len, n_workers):
     """pkv_build_paged_window_plan on host lengths: the plan as an int32 numpy array."""
     lens = _i32(context_lens)
@@ -403,12 +418,18 @@ class DecodePlan:
     while the lengths do: the next step (one more token per sequence) needs a
     new plan. __call__ runs pkv_paged_decode_step_planned."""
 
-    def __init__(self, context_lens, *, Hq, Hkv, d, bs, cache_dtype_code, max_context_len, device="cuda"):
+    def __init__(self, context_lens, *, Hq, Hkv, d, bs, cache_dtype_code, max_context_len, block_tables=None,
+                 device="cuda"):
+        """block_tables: the host copy of the tables (optional); when given, the
+        plan records whether the batch shares blocks (plan_mark_shared_blocks),
+        which selects cacheable K/V loads."""
         import torch
         self.n_workers = paged_decode_plan_workers(d, bs, cache_dtype_code)
         self.max_context_len = int(max_context_len)
         self.host = build_paged_decode_plan(context_lens, Hkv, d, cache_dtype_code, self.max_context_len,
                                             self.n_workers)
+        self.shared_blocks = (plan_mark_shared_blocks(self.host, block_tables, context_lens, bs)
+                              if block_tables is not None else False)
         self.dev = torch.from_numpy(self.host).to(device)
         need = int(lib().pkv_paged_decode_plan_workspace_size(self.n_workers, Hq, Hkv, d))
         self.workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=device)

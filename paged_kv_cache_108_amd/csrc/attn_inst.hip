@@ -59,30 +59,31 @@ AttnKernel pick_kernel(int bs, int mode, int tiles, bool partition) {
 
 template AttnKernel pick_kernel<PKV_INST_KV, PKV_INST_D>(int, int, int, bool);
 
-template <int KV, int D, int PM>
+template <int KV, int D, int PM, bool CACHED>
 AttnKernel plan_for_bs(int bs) {
     switch (bs) {
-        case 8: return paged_attn_plan_kernel<KV, D, 8, PM>;
-        case 16: return paged_attn_plan_kernel<KV, D, 16, PM>;
-        case 32: return paged_attn_plan_kernel<KV, D, 32, PM>;
-        case 64: return paged_attn_plan_kernel<KV, D, 64, PM>;
-        case 128: return paged_attn_plan_kernel<KV, D, 128, PM>;
+        case 8: return paged_attn_plan_kernel<KV, D, 8, PM, CACHED>;
+        case 16: return paged_attn_plan_kernel<KV, D, 16, PM, CACHED>;
+        case 32: return paged_attn_plan_kernel<KV, D, 32, PM, CACHED>;
+        case 64: return paged_attn_plan_kernel<KV, D, 64, PM, CACHED>;
+        case 128: return paged_attn_plan_kernel<KV, D, 128, PM, CACHED>;
     }
     return nullptr;
 }
 
-// mode: PM_ATTN, PM_STEP or PM_WINDOW
+// mode: PM_ATTN, PM_STEP or PM_WINDOW; cached: cacheable K/V loads (decode
+// modes only, for plans that list shared blocks)
 template <int KV, int D>
-AttnKernel pick_plan_kernel(int bs, int mode) {
+AttnKernel pick_plan_kernel(int bs, int mode, bool cached) {
     switch (mode) {
-        case PM_ATTN: return plan_for_bs<KV, D, PM_ATTN>(bs);
-        case PM_STEP: return plan_for_bs<KV, D, PM_STEP>(bs);
-        case PM_WINDOW: return plan_for_bs<KV, D, PM_WINDOW>(bs);
+        case PM_ATTN: return cached ? plan_for_bs<KV, D, PM_ATTN, true>(bs) : plan_for_bs<KV, D, PM_ATTN, false>(bs);
+        case PM_STEP: return cached ? plan_for_bs<KV, D, PM_STEP, true>(bs) : plan_for_bs<KV, D, PM_STEP, false>(bs);
+        case PM_WINDOW: return cached ? nullptr : plan_for_bs<KV, D, PM_WINDOW, false>(bs);
     }
     return nullptr;
 }
 
-template AttnKernel pick_plan_kernel<PKV_INST_KV, PKV_INST_D>(int, int);
+template AttnKernel pick_plan_kernel<PKV_INST_KV, PKV_INST_D>(int, int, bool);
 
 template <int KV, int D>
 AttnKernel pick_gather_kernel(int bs) {

@@ -240,12 +240,15 @@ __device__ __forceinline__ uint2 ld_stream(const uint2* a) {
     return make_uint2(t.x, t.y);
 }
 __device__ __forceinline__ uint32_t ld_stream(const uint32_t* a) { return __builtin_nontemporal_load(a); }
-template <int BS, typename T>
+// CACHED: plain (cacheable) loads instead, for batches whose sequences share
+// blocks, so that the waves reading one block can meet in L2.
+template <int BS, bool CACHED, typename T>
 __device__ __forceinline__ T ld_kv(const T* a) {
-    return ld_stream(a);
+    if constexpr (CACHED) return *a;
+    else return ld_stream(a);
 }
 
-template <int KV, int D, int BS>
+template <int KV, int D, int BS, bool CACHED = false>
 __device__ __forceinline__ void load_chunk(Frag<KV, D>& f, const AttnParams& p, int b0, int b1,
                                            int tc, int g, int r16, int j4) {
     using E = typename std::conditional<KV == KV_F32, float,
@@ -272,21 +275,21 @@ __device__ __forceinline__ void load_chunk(Frag<KV, D>& f, const AttnParams& p, 
     if constexpr (KV == KV_F32) {
 #pragma unroll
         for (int x = 0; x < D / 16; ++x)
-            f.k[x] = ld_kv<BS>(reinterpret_cast<const float4*>(krow + 16 * x + 4 * j4));
+            f.k[x] = ld_kv<BS, CACHED>(reinterpret_cast<const float4*>(krow + 16 * x + 4 * j4));
 #pragma unroll
         for (int s = 0; s < D / 16; ++s)
-            f.v[s] = ld_kv<BS>(reinterpret_cast<const float4*>(vt + (size_t)(16 * s + r16) * VS));
+            f.v[s] = ld_kv<BS, CACHED>(reinterpret_cast<const float4*>(vt + (size_t)(16 * s + r16) * VS));
     } else if constexpr (KV == KV_BF16) {
 #pragma unroll
         for (int s = 0; s < D / 32; ++s)
-            f.k[s] = ld_kv<BS>(reinterpret_cast<const uint4*>(krow + 32 * s + 8 * j4));
+            f.k[s] = ld_kv<BS, CACHED>(reinterpret_cast<const uint4*>(krow + 32 * s + 8 * j4));
 #pragma unroll
         for (int s = 0; s < D / 16; ++s)
-            f.v[s] = ld_kv<BS>(reinterpret_cast<const uint2*>(vt + (size_t)(16 * s + r16) * VS));
+            f.v[s] = ld_kv<BS, CACHED>(reinterpret_cast<const uint2*>(vt + (size_t)(16 * s + r16) * VS));
     } else {
 #pragma unroll
         for (int x = 0; x < D / 64; ++x)
-            f.k[x] = ld_kv<BS>(reinterpret_cast<const uint4*>(krow + 64 * x + 16 * j4));
+            f.k[x] = ld_kv<BS, CACHED>(reinterpret_cast<const uint4*>(krow + 64 * x + 16 * j4));
         if constexpr (BS >= 16) {
             // whole 16-token rows, 16 bytes per lane: lane (r16, j4) reads the row
             // of channel 16(4t + j4) + r16; v_rows_to_operand moves the tokens
@@ -294,7 +297,7 @@ __device__ __forceinline__ void load_chunk(Frag<KV, D>& f, const AttnParams& p, 
             const E* vsub = vt - 4 * j4;
 #pragma unroll
             for (int t = 0; t < D / 64; ++t) {
-                const uint4 row = ld_kv<BS>(reinterpret_cast<const uint4*>(vsub + (size_t)(16 * (4 * t + j4) + r16) * 16));
+                const uint4 row = ld_kv<BS, CACHED>(reinterpret_cast<const uint4*>(vsub + (size_t)(16 * (4 * t + j4) + r16) * 16));
                 f.v[4 * t + 0] = row.x;
                 f.v[4 * t + 1] = row.y;
                 f.v[4 * t + 2] = row.z;
@@ -303,7 +306,7 @@ __device__ __forceinline__ void load_chunk(Frag<KV, D>& f, const AttnParams& p, 
         } else {
 #pragma unroll
             for (int s = 0; s < D / 16; ++s)
-                f.v[s] = ld_kv<BS>(reinterpret_cast<const uint32_t*>(vt + (size_t)(16 * s + r16) * VS));
+                f.v[s] = ld_kv<BS, CACHED>(reinterpret_cast<const uint32_t*>(vt + (size_t)(16 * s + r16) * VS));
         }
     }
 }
@@ -1384,7 +1387,7 @@ template <int KV, int D> constexpr int plan_slots() {
 // of qgs queries, G * qgs <= 16 columns of one MFMA tile).
 enum PlanMode { PM_ATTN = 0, PM_STEP = 1, PM_WINDOW = 2 };
 
-template <int KV, int D, int BS, int PM>
+template <int KV, int D, int BS, int PM, bool CACHED>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1)))
 paged_attn_plan_kernel(AttnParams p) {
     constexpr bool STEP = PM == PM_STEP;
@@ -1559,7 +1562,7 @@ paged_attn_plan_kernel(AttnParams p) {
             const int kc = real ? __builtin_amdgcn_readlane(mkc, kk) : 0;
             const Col c = column(i, gf & 0xFFFF);
             const int g = c.g;
-            load_chunk<KV, D, BS>(x.f, p, b0, b1, 16 * kc, g, r16, j4);
+            load_chunk<KV, D, BS, CACHED>(x.f, p, b0, b1, 16 * kc, g, r16, j4);
             if ((gf >> 16) & pkv_split::kFirst)     // unused columns read row 0; step zeroes them
                 load_q_raw<KV, D>(p, c.live ? c.row : 0, j4, x.q);
             if constexpr (STEP) {
@@ -1776,7 +1779,7 @@ AttnKernel pick_kernel(int bs, int mode, int tiles, bool partition);
 
 // The planned kernel for one cache type and head dim (attn_inst.hip).
 template <int KV, int D>
-AttnKernel pick_plan_kernel(int bs, int mode);
+AttnKernel pick_plan_kernel(int bs, int mode, bool cached);
 
 // The gather-only kernel for one cache type and head dim (attn_inst.hip).
 template <int KV, int D>

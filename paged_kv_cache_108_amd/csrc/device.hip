@@ -535,10 +535,13 @@ AttnKernel pick_gather(int kv, int d, int bs) {
     return d == 64 ? pick_gather_kernel<KV_FP8, 64>(bs) : pick_gather_kernel<KV_FP8, 128>(bs);
 }
 
-AttnKernel pick_plan(int kv, int d, int bs, int mode) {
-    if (kv == KV_F32) return d == 64 ? pick_plan_kernel<KV_F32, 64>(bs, mode) : pick_plan_kernel<KV_F32, 128>(bs, mode);
-    if (kv == KV_BF16) return d == 64 ? pick_plan_kernel<KV_BF16, 64>(bs, mode) : pick_plan_kernel<KV_BF16, 128>(bs, mode);
-    return d == 64 ? pick_plan_kernel<KV_FP8, 64>(bs, mode) : pick_plan_kernel<KV_FP8, 128>(bs, mode);
+AttnKernel pick_plan(int kv, int d, int bs, int mode, bool cached = false) {
+    if (kv == KV_F32)
+        return d == 64 ? pick_plan_kernel<KV_F32, 64>(bs, mode, cached) : pick_plan_kernel<KV_F32, 128>(bs, mode, cached);
+    if (kv == KV_BF16)
+        return d == 64 ? pick_plan_kernel<KV_BF16, 64>(bs, mode, cached)
+                       : pick_plan_kernel<KV_BF16, 128>(bs, mode, cached);
+    return d == 64 ? pick_plan_kernel<KV_FP8, 64>(bs, mode, cached) : pick_plan_kernel<KV_FP8, 128>(bs, mode, cached);
 }
 
 // Compute units of the current device (cached per device).
@@ -1038,14 +1041,17 @@ namespace {
 // The step and the attention-only kernels share the grid (one plan serves
 // both): the smaller of their residencies decides.
 int plan_workers(int kv, int d, int bs) {
-    // the smallest residency of the three modes: a plan serves any of them
+    // the smallest residency of the planned kernel's variants: a plan serves
+    // any of them
     int resident = 1 << 30;
-    for (int mode : {PM_ATTN, PM_STEP, PM_WINDOW}) {
-        const AttnKernel k = pick_plan(kv, d, bs, mode);
-        if (!k) return -1;
-        const int r = resident_workgroups(k, 0);
-        if (r < resident) resident = r;
-    }
+    for (int mode : {PM_ATTN, PM_STEP, PM_WINDOW})
+        for (bool cached : {false, true}) {
+            if (mode == PM_WINDOW && cached) continue;
+            const AttnKernel k = pick_plan(kv, d, bs, mode, cached);
+            if (!k) return -1;
+            const int r = resident_workgroups(k, 0);
+            if (r < resident) resident = r;
+        }
     const int cus = compute_units();
     if (resident <= 0 || cus <= 0) return -1;
     const int chunk_bytes = 16 * 2 * d * (kv == KV_F32 ? 4 : kv == KV_BF16 ? 2 : 1);
@@ -1171,8 +1177,11 @@ pkv_status plan_launch(const char* fn, float* out, const void* q, const void* k_
     prm.n_rec = 2 * n_workers;
     auto st = static_cast<hipStream_t>(stream);
     const int mode = n_q > 0 ? PM_WINDOW : is_step ? PM_STEP : PM_ATTN;
-    hipLaunchKernelGGL(pick_plan(kv, d, bs, mode), dim3((unsigned)(n_workers / kWaves)), dim3(kThreads), 0, st,
-                       prm);
+    // a decode plan that lists shared blocks: cacheable K/V loads
+    const bool cached = n_q == 0 &&
+                        (static_cast<const int32_t*>(plan_host)[pkv_split::kPlanFlagsWord] & pkv_split::kPlanSharedBlocks);
+    hipLaunchKernelGGL(pick_plan(kv, d, bs, mode, cached), dim3((unsigned)(n_workers / kWaves)), dim3(kThreads), 0,
+                       st, prm);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(PKV_E_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
     if (attn_done_event) {

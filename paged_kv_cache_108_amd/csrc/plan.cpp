@@ -173,3 +173,30 @@ extern "C" pkv_status pkv_build_paged_window_plan(const int32_t* context_lens, i
     return build_plan(fn, context_lens, S, n_q, Hq / Hkv, Hkv, d, cache_dtype, max_context_len, n_workers,
                       static_cast<int32_t*>(plan), plan_bytes, plan_bytes_needed);
 }
+
+extern "C" pkv_status pkv_plan_mark_shared_blocks(void* plan, size_t plan_bytes, const int32_t* block_tables,
+                                                  const int32_t* context_lens, int32_t S, int32_t max_blocks,
+                                                  int32_t bs, int32_t* shared) {
+    const char* fn = "plan_mark_shared_blocks";
+    if (!plan || !block_tables || !context_lens || S <= 0 || max_blocks <= 0 || bs <= 0)
+        return fail(PKV_E_INVALID, "%s: NULL pointer or S=%d max_blocks=%d bs=%d", fn, S, max_blocks, bs);
+    if (plan_bytes < kPlanHeader * sizeof(int32_t))
+        return fail(PKV_E_INVALID, "%s: plan of %zu bytes", fn, plan_bytes);
+    int32_t* h = static_cast<int32_t*>(plan);
+    if (h[0] != kPlanMagic || h[1] != kPlanVersion || h[4] != S)
+        return fail(PKV_E_INVALID, "%s: not a plan for S=%d", fn, S);
+    // the blocks each sequence reads: ceil(L / bs) entries of its row
+    const int32_t max_len = h[8];
+    std::vector<int32_t> seen;
+    seen.reserve(1024);
+    for (int32_t i = 0; i < S; ++i) {
+        const int32_t L = std::min(context_lens[i], max_len);
+        const int32_t nb = L > 0 ? std::min<int32_t>((L + bs - 1) / bs, max_blocks) : 0;
+        for (int32_t j = 0; j < nb; ++j) seen.push_back(block_tables[(size_t)i * max_blocks + j]);
+    }
+    std::sort(seen.begin(), seen.end());
+    const bool dup = std::adjacent_find(seen.begin(), seen.end()) != seen.end();
+    h[kPlanFlagsWord] = dup ? (h[kPlanFlagsWord] | kPlanSharedBlocks) : (h[kPlanFlagsWord] & ~kPlanSharedBlocks);
+    if (shared) *shared = dup ? 1 : 0;
+    return ok();
+}

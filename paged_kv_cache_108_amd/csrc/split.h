@@ -83,7 +83,8 @@ PKV_HD inline QueryGroups query_groups_in(int n_q, int G, int tiles) {
 //   header[16]: kPlanMagic, kPlanVersion, n_workers (waves of the grid it was
 //               built for), W (waves with a range), S, Hkv, seg_cost, stride
 //               (entries per wave), max_context_len, d, kv kind, then for a
-//               window plan n_q, G, qgs, n_qg (0 0 0 0 in a decode plan), 0
+//               window plan n_q, G, qgs, n_qg (0 0 0 0 in a decode plan),
+//               then flags (kPlanSharedBlocks)
 //   entries[n_workers][stride][4]: wave w's chunks in processing order, each
 //               {sequence i, segment column group g2 | flags << 16, chunk
 //               index kc, L_i}, g2 = kv head * n_qg + query group (the kv
@@ -94,6 +95,11 @@ PKV_HD inline QueryGroups query_groups_in(int n_q, int G, int tiles) {
 constexpr int32_t kPlanMagic = 0x504B5650;   // "PKVP"
 constexpr int32_t kPlanVersion = 1;
 constexpr int kPlanHeader = 16;
+constexpr int kPlanFlagsWord = 15;
+// flags: some physical block is listed by more than one sequence (or twice
+// in one), so the kernels read K/V with cacheable loads, and sequences that
+// read the same block can meet in L2
+constexpr int32_t kPlanSharedBlocks = 1;
 // entry flags
 constexpr int kFirst = 1;    // the first chunk of this wave's piece of the segment
 constexpr int kLast = 2;     // the last chunk of this wave's piece

@@ -32,13 +32,19 @@ def _gpu_present():
     need_gpu()
 
 
-def _plan(w, device="cuda"):
+def _plan(w, device="cuda", shared=None):
+    """shared None: an unmarked plan (streaming loads); True/False: the plan
+    marked from the host tables, which must then find shared blocks or not."""
     s = w.spec
-    return pkv.DecodePlan(w.context_lens, Hq=s.Hq, Hkv=s.Hkv, d=s.d, bs=s.bs, cache_dtype_code=CODE[s.cache_dtype],
-                          max_context_len=w.max_context_len, device=device)
+    plan = pkv.DecodePlan(w.context_lens, Hq=s.Hq, Hkv=s.Hkv, d=s.d, bs=s.bs, cache_dtype_code=CODE[s.cache_dtype],
+                          max_context_len=w.max_context_len, device=device,
+                          block_tables=None if shared is None else w.block_tables)
+    if shared is not None:
+        assert plan.shared_blocks == shared
+    return plan
 
 
-def _planned_case(w, seqs=None):
+def _planned_case(w, seqs=None, shared=None):
     torch = need_gpu()
     s = w.spec
     print(f"[case] planned {s.name} bs={s.bs} cache={s.cache_dtype} S={s.S}", flush=True)
@@ -46,7 +52,7 @@ def _planned_case(w, seqs=None):
     want = to_host(device_decode_step(ref)).copy()
     want_attn = to_host(ref.attend(BAL)).copy()
     dev = DeviceStep(w)                        # planned fused step
-    plan = _plan(w)
+    plan = _plan(w, shared=shared)
     out = torch.full((s.S, s.Hq, s.d), float("nan"), dtype=torch.float32, device="cuda")
     plan(out, dev.q, dev.k_cache, dev.v_cache, dev.tables, dev.lens, softmax_scale=w.softmax_scale,
          k_new=dev.k_new, v_new=dev.v_new, k_scale=w.k_scale, v_scale=w.v_scale, k_inv_scale=w.k_inv_scale,
@@ -135,6 +141,18 @@ def test_planned_repeated_calls_give_the_same_bits(name, cache):
         else:
             assert np.array_equal(got, first), "a later call differs"
     assert np.array_equal(to_host(plan.dev), plan.host)
+
+
+@pytest.mark.parametrize("bs,cache", [(8, None), (16, None), (32, None), (16, "fp8")])
+def test_planned_step_shared_blocks(bs, cache):
+    """Beams sharing a prefix: the plan is marked from the host tables and runs
+    with cacheable K/V loads; the result is the unplanned step's, bit for bit."""
+    _planned_case(W.make("beam", bs=bs, cache_dtype=cache), shared=True)
+
+
+def test_planned_step_marked_without_sharing():
+    # a batch with no shared block stays unmarked (streaming loads)
+    _planned_case(W.make("llama8b"), shared=False)
 
 
 def test_plan_for_other_inputs_is_refused():

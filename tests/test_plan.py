@@ -184,3 +184,28 @@ def test_window_plan_rejects_bad_arguments():
         a.update(kw)
         with pytest.raises(pkv.PkvError):
             pkv.build_paged_window_plan([10, 20], a["n_q"], a["Hq"], a["Hkv"], 64, 1, 32, 16)
+
+
+def test_shared_blocks_mark():
+    """pkv_plan_mark_shared_blocks sets the flags word (header word 15) exactly
+    when a block id repeats among the blocks the sequences read, and changes no
+    other word."""
+    beam = W.make("beam")
+    s = beam.spec
+    plan = pkv.build_paged_decode_plan(beam.context_lens, s.Hkv, s.d, 1, beam.max_context_len, 1024)
+    before = plan.copy()
+    assert pkv.plan_mark_shared_blocks(plan, beam.block_tables, beam.context_lens, s.bs)
+    assert plan[15] == 1 and np.array_equal(np.delete(plan, 15), np.delete(before, 15))
+    w = W.make("llama8b")
+    s = w.spec
+    plan = pkv.build_paged_decode_plan(w.context_lens, s.Hkv, s.d, 1, w.max_context_len, 1024)
+    assert not pkv.plan_mark_shared_blocks(plan, w.block_tables, w.context_lens, s.bs) and plan[15] == 0
+    # a repeat past a row's read range does not count; one inside it does
+    tables = np.array([[3, 4, 5, -1], [6, 7, 3, -1]], dtype=np.int32)
+    lens = [40, 20]                                          # 3 and 2 blocks of 16 are read
+    plan = pkv.build_paged_decode_plan(lens, 1, 64, 1, 64, 16)
+    assert not pkv.plan_mark_shared_blocks(plan, tables, lens, 16)
+    assert pkv.plan_mark_shared_blocks(plan, tables, [40, 40], 16) and plan[15] == 1
+    assert not pkv.plan_mark_shared_blocks(plan, tables, [40, 20], 16) and plan[15] == 0    # cleared again
+    same_row = np.array([[9, 9, -1, -1], [1, 2, -1, -1]], dtype=np.int32)
+    assert pkv.plan_mark_shared_blocks(plan, same_row, [20, 20], 16)
