@@ -732,7 +732,8 @@ pkv_status pkv_waste_stats(const int32_t* lens, int32_t n, int32_t bs, int32_t m
 /*
  * Gather only: read the K/V chunks that a decode plan lists -- every chunk of
  * every (sequence, kv head) the step attends over, through the block tables --
- * with the planned kernel's loads, pipeline and grid, and no arithmetic. Its
+ * with the planned kernel's loads (cacheable ones for a plan marked by
+ * pkv_plan_mark_shared_blocks), pipeline and grid, and no arithmetic. Its
  * time is the read rate of the step's own scattered tiles: the ceiling of the
  * planned step without its compute, q loads, new-token write, records and
  * merge, timed next to it. A decode step reads the whole cache of every

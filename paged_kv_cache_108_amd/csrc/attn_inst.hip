@@ -85,18 +85,24 @@ AttnKernel pick_plan_kernel(int bs, int mode, bool cached) {
 
 template AttnKernel pick_plan_kernel<PKV_INST_KV, PKV_INST_D>(int, int, bool);
 
-template <int KV, int D>
-AttnKernel pick_gather_kernel(int bs) {
+template <int KV, int D, bool CACHED>
+AttnKernel gather_for_bs(int bs) {
     switch (bs) {
-        case 8: return paged_gather_kernel<KV, D, 8>;
-        case 16: return paged_gather_kernel<KV, D, 16>;
-        case 32: return paged_gather_kernel<KV, D, 32>;
-        case 64: return paged_gather_kernel<KV, D, 64>;
-        case 128: return paged_gather_kernel<KV, D, 128>;
+        case 8: return paged_gather_kernel<KV, D, 8, CACHED>;
+        case 16: return paged_gather_kernel<KV, D, 16, CACHED>;
+        case 32: return paged_gather_kernel<KV, D, 32, CACHED>;
+        case 64: return paged_gather_kernel<KV, D, 64, CACHED>;
+        case 128: return paged_gather_kernel<KV, D, 128, CACHED>;
     }
     return nullptr;
 }
 
-template AttnKernel pick_gather_kernel<PKV_INST_KV, PKV_INST_D>(int);
+// cached: the loads of a plan marked for shared blocks, as the planned kernel
+template <int KV, int D>
+AttnKernel pick_gather_kernel(int bs, bool cached) {
+    return cached ? gather_for_bs<KV, D, true>(bs) : gather_for_bs<KV, D, false>(bs);
+}
+
+template AttnKernel pick_gather_kernel<PKV_INST_KV, PKV_INST_D>(int, bool);
 
 }  // namespace pkv_dev

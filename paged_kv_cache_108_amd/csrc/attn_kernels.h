@@ -1706,7 +1706,7 @@ __device__ __forceinline__ unsigned frag_fold(const Frag<KV, D>& f) {
     return a;
 }
 
-template <int KV, int D, int BS>
+template <int KV, int D, int BS, bool CACHED>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1)))
 paged_gather_kernel(AttnParams p) {
     const int lane = threadIdx.x & 63;
@@ -1747,7 +1747,7 @@ paged_gather_kernel(AttnParams p) {
             const int b1 = BS == 8 ? (real ? __builtin_amdgcn_readlane(id1, kk) : 0) : b0;
             const int g = real ? __builtin_amdgcn_readlane(e.y, kk) & 0xFFFF : 0;
             const int kc = real ? __builtin_amdgcn_readlane(e.z, kk) : 0;
-            load_chunk<KV, D, BS>(f, p, b0, b1, 16 * kc, g, r16, j4);
+            load_chunk<KV, D, BS, CACHED>(f, p, b0, b1, 16 * kc, g, r16, j4);
             __builtin_amdgcn_sched_barrier(0);
         };
 #pragma unroll
@@ -1783,6 +1783,6 @@ AttnKernel pick_plan_kernel(int bs, int mode, bool cached);
 
 // The gather-only kernel for one cache type and head dim (attn_inst.hip).
 template <int KV, int D>
-AttnKernel pick_gather_kernel(int bs);
+AttnKernel pick_gather_kernel(int bs, bool cached);
 
 }  // namespace pkv_dev

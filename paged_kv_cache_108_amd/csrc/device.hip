@@ -529,10 +529,12 @@ AttnKernel pick(int kv, int d, int bs, int mode, int tiles, bool partition) {
                    : pick_kernel<KV_FP8, 128>(bs, mode, tiles, partition);
 }
 
-AttnKernel pick_gather(int kv, int d, int bs) {
-    if (kv == KV_F32) return d == 64 ? pick_gather_kernel<KV_F32, 64>(bs) : pick_gather_kernel<KV_F32, 128>(bs);
-    if (kv == KV_BF16) return d == 64 ? pick_gather_kernel<KV_BF16, 64>(bs) : pick_gather_kernel<KV_BF16, 128>(bs);
-    return d == 64 ? pick_gather_kernel<KV_FP8, 64>(bs) : pick_gather_kernel<KV_FP8, 128>(bs);
+AttnKernel pick_gather(int kv, int d, int bs, bool cached) {
+    if (kv == KV_F32)
+        return d == 64 ? pick_gather_kernel<KV_F32, 64>(bs, cached) : pick_gather_kernel<KV_F32, 128>(bs, cached);
+    if (kv == KV_BF16)
+        return d == 64 ? pick_gather_kernel<KV_BF16, 64>(bs, cached) : pick_gather_kernel<KV_BF16, 128>(bs, cached);
+    return d == 64 ? pick_gather_kernel<KV_FP8, 64>(bs, cached) : pick_gather_kernel<KV_FP8, 128>(bs, cached);
 }
 
 AttnKernel pick_plan(int kv, int d, int bs, int mode, bool cached = false) {
@@ -1263,7 +1265,8 @@ extern "C" pkv_status pkv_paged_gather_read(const void* k_cache, const void* v_c
     prm.P = P;
     prm.max_blocks = max_blocks;
     prm.max_len = max_context_len;
-    const AttnKernel kern = pick_gather(kv, d, bs);
+    const bool cached = static_cast<const int32_t*>(plan_host)[pkv_split::kPlanFlagsWord] & pkv_split::kPlanSharedBlocks;
+    const AttnKernel kern = pick_gather(kv, d, bs, cached);
     if (!kern) return fail(PKV_E_INVALID, "%s: no kernel for d=%d bs=%d", fn, d, bs);
     hipLaunchKernelGGL(kern, dim3((unsigned)(n_workers / kWaves)), dim3(kThreads), 0, static_cast<hipStream_t>(stream),
                        prm);

@@ -22,7 +22,7 @@ def _gpu_present():
     need_gpu()
 
 
-def _run(torch, w, dt, pool_name, block, head, tok, chan):
+def _run(torch, w, dt, pool_name, block, head, tok, chan, marked=False):
     s = w.spec
     k = np.zeros(w.k_pool.shape, ELEM[dt])
     v = np.zeros(w.v_pool.shape, ELEM[dt])
@@ -39,15 +39,21 @@ def _run(torch, w, dt, pool_name, block, head, tok, chan):
         kc, vc = kc.view(torch.float32), vc.view(torch.float32)
     plan = pkv.DecodePlan(w.context_lens, Hq=s.Hq, Hkv=s.Hkv, d=s.d, bs=s.bs, cache_dtype_code=CODE[dt],
                           max_context_len=w.max_context_len)
+    if marked:                                     # the flags word of a plan marked for shared blocks
+        plan.host[15] = 1
+        plan.dev = torch.from_numpy(plan.host).cuda()
     sink = torch.zeros(4, dtype=torch.int32, device="cuda")
     plan.gather(kc, vc, torch.from_numpy(w.block_tables).cuda(), sink)
     torch.cuda.synchronize()
     return int(sink.cpu().numpy().view(np.uint32)[0])
 
 
-@pytest.mark.parametrize("dt,d,bs", [("bf16", 128, 16), ("bf16", 64, 8), ("fp8", 64, 16), ("fp8", 128, 32),
-                                     ("f32", 64, 16), ("bf16", 128, 128)])
-def test_gather_reads_the_listed_chunks_and_no_free_block(dt, d, bs):
+@pytest.mark.parametrize("dt,d,bs,marked", [("bf16", 128, 16, False), ("bf16", 64, 8, False), ("fp8", 64, 16, False),
+                                            ("fp8", 128, 32, False), ("f32", 64, 16, False),
+                                            ("bf16", 128, 128, False), ("bf16", 128, 16, True),
+                                            ("fp8", 64, 16, True)])
+def test_gather_reads_the_listed_chunks_and_no_free_block(dt, d, bs, marked):
+    """marked: the plan's shared-blocks flag set, so the cacheable-load variant runs."""
     torch = need_gpu()
     lens = [40, 5, 0, 300, 17, 1000]
     w = W.make_custom(lens=lens, Hq=8, Hkv=2, d=d, bs=bs, q_dtype="f32" if dt == "f32" else "bf16",
@@ -55,20 +61,20 @@ def test_gather_reads_the_listed_chunks_and_no_free_block(dt, d, bs):
     step = 4 // np.dtype(ELEM[dt]).itemsize        # pool elements per 32-bit word
     used = set(int(b) for b in w.block_tables.reshape(-1) if b >= 0)
     free = [b for b in range(w.P) if b not in used and b != 0]
-    print(f"[case] gather {dt} d{d} bs{bs}", flush=True)
+    print(f"[case] gather {dt} d{d} bs{bs} marked={marked}", flush=True)
     # a word inside a listed chunk: sequence 3, token 16 * 5 + 2 (chunk 5), kv head 1
     tok = 16 * 5 + 2
     b = int(w.block_tables[3, tok // bs])
-    assert _run(torch, w, dt, "k", b, 1, tok % bs, 2 * step) == MAGIC
+    assert _run(torch, w, dt, "k", b, 1, tok % bs, 2 * step, marked) == MAGIC
     if bs <= 16:                                   # V tile [d][bs]: channel 7, the chunk's token word
-        assert _run(torch, w, dt, "v", b, 1, 7, (tok % bs) // step * step) == MAGIC
+        assert _run(torch, w, dt, "v", b, 1, 7, (tok % bs) // step * step, marked) == MAGIC
     # the last chunk of the longest sequence
     tok = 999
     b = int(w.block_tables[5, tok // bs])
-    assert _run(torch, w, dt, "k", b, 0, tok % bs, 0) == MAGIC
+    assert _run(torch, w, dt, "k", b, 0, tok % bs, 0, marked) == MAGIC
     # a block no sequence lists
     if free:
-        assert _run(torch, w, dt, "k", free[0], 1, 3, step) == 0
+        assert _run(torch, w, dt, "k", free[0], 1, 3, step, marked) == 0
 
 
 def test_gather_refuses_a_plan_for_other_inputs():
