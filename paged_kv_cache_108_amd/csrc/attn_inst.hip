@@ -17,14 +17,14 @@ namespace pkv_dev {
 
 namespace {
 
-template <int KV, int D, int MODE, int NT>
+template <int KV, int D, int MODE, int NT, bool CACHED = false>
 AttnKernel stream_for_bs(int bs) {
     switch (bs) {
-        case 8: return paged_attn_stream_kernel<KV, D, 8, MODE, NT>;
-        case 16: return paged_attn_stream_kernel<KV, D, 16, MODE, NT>;
-        case 32: return paged_attn_stream_kernel<KV, D, 32, MODE, NT>;
-        case 64: return paged_attn_stream_kernel<KV, D, 64, MODE, NT>;
-        case 128: return paged_attn_stream_kernel<KV, D, 128, MODE, NT>;
+        case 8: return paged_attn_stream_kernel<KV, D, 8, MODE, NT, CACHED>;
+        case 16: return paged_attn_stream_kernel<KV, D, 16, MODE, NT, CACHED>;
+        case 32: return paged_attn_stream_kernel<KV, D, 32, MODE, NT, CACHED>;
+        case 64: return paged_attn_stream_kernel<KV, D, 64, MODE, NT, CACHED>;
+        case 128: return paged_attn_stream_kernel<KV, D, 128, MODE, NT, CACHED>;
     }
     return nullptr;
 }
@@ -43,21 +43,23 @@ AttnKernel partition_for_bs(int bs) {
 
 }  // namespace
 
-// tiles: 16-column MFMA tiles per pass (query windows: 1 or wide_tiles(D))
+// tiles: 16-column MFMA tiles per pass (query windows: 1 or wide_tiles(D));
+// cached: plain K/V loads (wide windows of several passes)
 template <int KV, int D>
-AttnKernel pick_kernel(int bs, int mode, int tiles, bool partition) {
+AttnKernel pick_kernel(int bs, int mode, int tiles, bool partition, bool cached) {
     if (partition) return partition_for_bs<KV, D>(bs);
     switch (mode) {
         case SM_WINDOW:
-            return tiles == 1 ? stream_for_bs<KV, D, SM_WINDOW, 1>(bs)
-                              : stream_for_bs<KV, D, SM_WINDOW, wide_tiles(D)>(bs);
+            if (tiles == 1) return stream_for_bs<KV, D, SM_WINDOW, 1>(bs);
+            return cached ? stream_for_bs<KV, D, SM_WINDOW, wide_tiles(D), true>(bs)
+                          : stream_for_bs<KV, D, SM_WINDOW, wide_tiles(D)>(bs);
         case SM_STEP: return stream_for_bs<KV, D, SM_STEP, 1>(bs);
         case SM_SHARED: return stream_for_bs<KV, D, SM_SHARED, 1>(bs);
         default: return stream_for_bs<KV, D, SM_DECODE, 1>(bs);
     }
 }
 
-template AttnKernel pick_kernel<PKV_INST_KV, PKV_INST_D>(int, int, int, bool);
+template AttnKernel pick_kernel<PKV_INST_KV, PKV_INST_D>(int, int, int, bool, bool);
 
 template <int KV, int D, int PM, bool CACHED>
 AttnKernel plan_for_bs(int bs) {

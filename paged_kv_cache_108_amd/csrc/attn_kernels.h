@@ -953,10 +953,13 @@ paged_attn_partition_kernel(AttnParams p) {
 // wave w's chunks) or 2w + 1 (the piece that ends them). The wave that holds a
 // segment's first chunk writes the segment's descriptor (first record, record
 // count) for the merge kernel. Launched one workgroup per compute unit (one
-// wave per SIMD), so the kernel may use the whole register file.
+// wave per SIMD), so the kernel may use the whole register file. CACHED:
+// plain K/V loads instead of streaming ones, for a window whose query groups
+// take several passes over the same blocks (the passes' segments sit next to
+// each other in the work order, so a later pass can find the blocks in cache).
 enum StreamMode { SM_DECODE = 0, SM_WINDOW = 1, SM_STEP = 2, SM_SHARED = 3 };
 
-template <int KV, int D, int BS, int MODE, int NT>
+template <int KV, int D, int BS, int MODE, int NT, bool CACHED>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1)))
 paged_attn_stream_kernel(AttnParams p) {
     // SM_SHARED: group prefixes (a window of the group's queries, no causal
@@ -1207,7 +1210,7 @@ paged_attn_stream_kernel(AttnParams p) {
             const int seg = __builtin_amdgcn_readlane(mseg, k);
             const int kc = __builtin_amdgcn_readlane(mkc, k);
             const int g = (seg % HS) / n_qg;
-            load_chunk<KV, D, BS>(f, p, b0, b1, 16 * kc, g, r16, j4);
+            load_chunk<KV, D, BS, CACHED>(f, p, b0, b1, 16 * kc, g, r16, j4);
             __builtin_amdgcn_sched_barrier(0);
         };
         auto step = [&](Frag<KV, D>& f, int k) {
@@ -1775,7 +1778,7 @@ using AttnKernel = void (*)(AttnParams);
 // 16-column tiles, or (partition) the fixed-partition kernel; nullptr for a
 // block size outside {8, 16, 32, 64, 128}.
 template <int KV, int D>
-AttnKernel pick_kernel(int bs, int mode, int tiles, bool partition);
+AttnKernel pick_kernel(int bs, int mode, int tiles, bool partition, bool cached);
 
 // The planned kernel for one cache type and head dim (attn_inst.hip).
 template <int KV, int D>

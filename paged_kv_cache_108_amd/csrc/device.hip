@@ -520,13 +520,13 @@ shared_prefix_merge_kernel(AttnParams a, AttnParams b, float* __restrict__ out, 
 
 // The instantiations live in attn_inst.hip, one translation unit per (cache
 // type, head dim).
-AttnKernel pick(int kv, int d, int bs, int mode, int tiles, bool partition) {
-    if (kv == KV_F32) return d == 64 ? pick_kernel<KV_F32, 64>(bs, mode, tiles, partition)
-                                     : pick_kernel<KV_F32, 128>(bs, mode, tiles, partition);
-    if (kv == KV_BF16) return d == 64 ? pick_kernel<KV_BF16, 64>(bs, mode, tiles, partition)
-                                      : pick_kernel<KV_BF16, 128>(bs, mode, tiles, partition);
-    return d == 64 ? pick_kernel<KV_FP8, 64>(bs, mode, tiles, partition)
-                   : pick_kernel<KV_FP8, 128>(bs, mode, tiles, partition);
+AttnKernel pick(int kv, int d, int bs, int mode, int tiles, bool partition, bool cached = false) {
+    if (kv == KV_F32) return d == 64 ? pick_kernel<KV_F32, 64>(bs, mode, tiles, partition, cached)
+                                     : pick_kernel<KV_F32, 128>(bs, mode, tiles, partition, cached);
+    if (kv == KV_BF16) return d == 64 ? pick_kernel<KV_BF16, 64>(bs, mode, tiles, partition, cached)
+                                      : pick_kernel<KV_BF16, 128>(bs, mode, tiles, partition, cached);
+    return d == 64 ? pick_kernel<KV_FP8, 64>(bs, mode, tiles, partition, cached)
+                   : pick_kernel<KV_FP8, 128>(bs, mode, tiles, partition, cached);
 }
 
 AttnKernel pick_gather(int kv, int d, int bs, bool cached) {
@@ -849,7 +849,10 @@ pkv_status attn_launch(const char* fn, float* out, const void* q, const void* k_
     if (balanced) {
         const int mode = is_step ? SM_STEP : n_q > 1 ? SM_WINDOW : SM_DECODE;
         const int tiles = mode == SM_WINDOW ? qgr.tiles : 1;
-        kern = pick(kv, d, bs, mode, tiles, false);
+        // a wide window of several passes: plain loads, so that a pass can
+        // find the blocks the neighbouring pass's segments just read
+        const bool cached = mode == SM_WINDOW && tiles > 1 && qgr.n_qg > 1;
+        kern = pick(kv, d, bs, mode, tiles, false, cached);
         lds = (size_t)(prm.cache_lens ? S : 0) * sizeof(int);
     } else {
         kern = pick(kv, d, bs, SM_DECODE, 1, true);
