@@ -30,7 +30,6 @@ constexpr int kThreads = kWaves * 64;
 constexpr int kMaxCachedLens = 4096;      // sequences whose lengths a workgroup keeps in LDS
 constexpr int kMaxWorkers = 4096;         // waves of the balanced split, at most (sizes its workspace)
 using pkv_split::kMinPositions;          // balanced split: positions per wave, at least (split.h)
-constexpr int kMergeBatch = 32;           // records per round trip for rows that merge 32 or more
 // 16-column tiles per pass for wide query windows. Each tile adds its own
 // q fragment, accumulator and softmax to every chunk: four tiles at d 128
 // spill registers, and four at d 64 made a chunk's compute outlast its load.

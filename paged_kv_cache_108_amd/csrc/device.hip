@@ -146,8 +146,11 @@ struct MergeArgDesc {
 };
 
 // Merge row h (column r of its segment) from its n records, the first rec0
-// (balanced: then 2 * (w_lo + k) for k >= 1; partitions: rec0 + k).
-template <int D>
+// (balanced: then 2 * (w_lo + k) for k >= 1; partitions: rec0 + k). KB:
+// records whose columns one round trip loads beyond the first eight (32, or
+// 8 for a kernel that wants fewer registers and more resident waves); the
+// records are summed in the same order either way.
+template <int D, int KB = 32>
 __device__ __forceinline__ void merge_records(const AttnParams& p, long long h, int r, int n, int rec0,
                                               bool balanced) {
     const int lane = threadIdx.x & 63;
@@ -198,23 +201,11 @@ __device__ __forceinline__ void merge_records(const AttnParams& p, long long h, 
         return;
     }
     if (n <= 32) {
-        // up to 32 records, also in one round trip: lane k reads record k's
-        // m and l, and every lane its PER adjacent columns of every record
+        // up to 32 records, KB per round trip: lane k reads record k's m and
+        // l, and every lane its PER adjacent columns of every record
         using VT = typename std::conditional<PER == 2, float2, float>::type;
         const float mk = lane < n ? m_at(lane) : -INFINITY;
         const float lk = lane < n ? l_at(lane) : 0.f;
-        VT ov[32];
-#pragma unroll
-        for (int u0 = 0; u0 < 32; u0 += 8) {
-            if (u0 < n) {                     // whole groups of 8 past the last record are skipped
-#pragma unroll
-                for (int u = u0; u < u0 + 8; ++u)
-                    ov[u] = *reinterpret_cast<const VT*>(p.ws + (rec_of(u) * G + r) * D + PER * lane);
-            } else {
-#pragma unroll
-                for (int u = u0; u < u0 + 8; ++u) ov[u] = VT{};
-            }
-        }
         float M = mk;
 #pragma unroll
         for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
@@ -224,14 +215,30 @@ __device__ __forceinline__ void merge_records(const AttnParams& p, long long h, 
         for (int off = 32; off > 0; off >>= 1) dn += __shfl_xor(dn, off);
         float acc[PER] = {};
 #pragma unroll
-        for (int u = 0; u < 32; ++u) {
-            if (u < n) {
-                const float wt = __shfl(wl, u);
-                if constexpr (PER == 2) {
-                    acc[0] += wt * ov[u].x;
-                    acc[1] += wt * ov[u].y;
+        for (int b0 = 0; b0 < 32; b0 += KB) {
+            if (b0 >= n) break;
+            VT ov[KB];
+#pragma unroll
+            for (int u0 = 0; u0 < KB; u0 += 8) {
+                if (b0 + u0 < n) {            // whole groups of 8 past the last record are skipped
+#pragma unroll
+                    for (int u = u0; u < u0 + 8; ++u)
+                        ov[u] = *reinterpret_cast<const VT*>(p.ws + (rec_of(b0 + u) * G + r) * D + PER * lane);
                 } else {
-                    acc[0] += wt * ov[u];
+#pragma unroll
+                    for (int u = u0; u < u0 + 8; ++u) ov[u] = VT{};
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < KB; ++u) {
+                if (b0 + u < n) {
+                    const float wt = __shfl(wl, b0 + u);
+                    if constexpr (PER == 2) {
+                        acc[0] += wt * ov[u].x;
+                        acc[1] += wt * ov[u].y;
+                    } else {
+                        acc[0] += wt * ov[u];
+                    }
                 }
             }
         }
@@ -251,16 +258,16 @@ __device__ __forceinline__ void merge_records(const AttnParams& p, long long h, 
         const float wl = k0 + lane < n ? __builtin_amdgcn_exp2f(m_at(k0 + lane) - M) : 0.f;
         den += wl * (k0 + lane < n ? l_at(k0 + lane) : 0.f);
         int k = 0;
-        for (; k + kMergeBatch <= kn; k += kMergeBatch) {
-            // long rows: kMergeBatch records per memory round trip
-            float ov[kMergeBatch][PER];
+        for (; k + KB <= kn; k += KB) {
+            // long rows: KB records per memory round trip
+            float ov[KB][PER];
 #pragma unroll
-            for (int u = 0; u < kMergeBatch; ++u)
+            for (int u = 0; u < KB; ++u)
 #pragma unroll
                 for (int x = 0; x < PER; ++x)
                     ov[u][x] = p.ws[(rec_of(k0 + k + u) * G + r) * D + lane + 64 * x];
 #pragma unroll
-            for (int u = 0; u < kMergeBatch; ++u) {
+            for (int u = 0; u < KB; ++u) {
                 const float wt = __shfl(wl, (k + u) & 63);
 #pragma unroll
                 for (int x = 0; x < PER; ++x) num[x] += wt * ov[u][x];
@@ -320,7 +327,10 @@ paged_attn_merge_kernel(AttnParams p) {
         n = (L + p.part_tokens - 1) / p.part_tokens;
         rec0 = (i * p.Hkv + g) * p.n_part;
     }
-    merge_records<D>(p, h, r, n, rec0, balanced);
+    // eight records per round trip: 72 VGPRs at d 128 instead of 129, so
+    // seven waves per SIMD instead of three for the many rows of a window
+    // (one wave per row)
+    merge_records<D, 8>(p, h, r, n, rec0, balanced);
 }
 
 // Planned calls whose segments fit the arguments: workgroup (s, y) merges
