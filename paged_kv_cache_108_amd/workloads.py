@@ -40,6 +40,7 @@ against the same op sequences in the tests; it is not used here.
 
 from dataclasses import dataclass, field, replace
 import math
+import re
 
 import numpy as np
 
@@ -326,6 +327,17 @@ def _fp8_scales(w, valid):
         setattr(w, f"{which}_inv_scale", float(inv))
 
 
+def _described(base, s):
+    """s with its description naming the block size and cache type it was made
+    with, where they differ from the named workload's."""
+    text = s.description
+    if s.bs != base.bs:
+        text = re.sub(r"\bbs\d+\b", f"bs{s.bs}", text) if re.search(r"\bbs\d+\b", text) else f"{text}, bs{s.bs}"
+    if s.cache_dtype != base.cache_dtype:
+        text = f"{text}, {s.cache_dtype} cache"
+    return replace(s, description=text)
+
+
 def make(name, *, bs=None, cache_dtype=None, poison_new=True):
     """The named workload (see the module docstring)."""
     s = SPECS[name]
@@ -333,6 +345,7 @@ def make(name, *, bs=None, cache_dtype=None, poison_new=True):
         s = replace(s, bs=bs)
     if cache_dtype is not None:
         s = replace(s, cache_dtype=cache_dtype)
+    s = _described(SPECS[name], s)
     if name == "tiny":
         lens = np.array([512, 37, 1900, 128, 4], dtype=np.int64)
         P = 256
