@@ -370,12 +370,13 @@ def run_other_op(args, w, torch, pkv):
         def fn_planned():
             plan(out, q, k_cache, v_cache, tables, lens, softmax_scale=w.softmax_scale, k_scale=w.k_scale,
                  v_scale=w.v_scale, stream=stream)
-        # the planned call for windows that fit one 16-column group per kv head;
-        # wider ones take two tiles per pass in the unplanned call, which is faster
-        planned = args.window_call == "planned" or (args.window_call == "auto" and n_q * G <= 16)
+        # both calls group the window's columns alike (one or two 16-column
+        # tiles per pass); the planned one is the faster at every width measured
+        planned = args.window_call == "planned"
         fn, other = (fn_planned, fn_unplanned) if planned else (fn_unplanned, fn_planned)
         if planned:
-            tiles, qgs, n_qg = 1, int(plan.host[13]), int(plan.host[14])
+            qgs, n_qg = int(plan.host[13]), int(plan.host[14])
+            tiles = 1 if qgs * G <= 16 else 2
         attn, _, _, unique_tokens = algorithmic_bytes(w, cache_dtype)
         dec_q = s.S * s.Hq * s.d * ELEM[s.q_dtype]
         dec_out = s.S * s.Hq * s.d * 4
@@ -508,9 +509,8 @@ def main():
                          "(pkv_seq_create_prefixed), no GPU; shared: shared-prefix decode step "
                          "(pkv_paged_shared_prefix_decode) for groups of --group sequences")
     ap.add_argument("--window", type=int, default=4, help="queries per sequence for --op window")
-    ap.add_argument("--window-call", default="auto", choices=["auto", "planned", "unplanned"],
-                    help="--op window: the call timed (auto: planned when the window fits one 16-column group "
-                         "per kv head, else unplanned); the other is timed beside it")
+    ap.add_argument("--window-call", default="planned", choices=["planned", "unplanned"],
+                    help="--op window: the call timed (default: the planned call); the other is timed beside it")
     ap.add_argument("--pairs", type=int, default=1024, help="block pairs for --op copy")
     ap.add_argument("--group", type=int, default=4, help="sequences per group for --op shared")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",

@@ -277,9 +277,11 @@ pkv_status pkv_plan_mark_shared_blocks(void* plan, size_t plan_bytes, const int3
  * up to it, as in pkv_paged_multi_query_attn ("Serving: vLLM and
  * PagedAttention", sections 2.4 and 2.7). The (query,
  * head) pairs of each kv head are cut into n_qg groups of qgs queries, qgs =
- * min(n_q, max(1, 16 / G)) with G = Hq / Hkv (one 16-column MFMA tile per
- * group), and every group is a segment of the balanced split with the
- * sequence's whole chunk list, the kv head's groups next to each other. The
+ * min(n_q, max(1, 16 * T / G)) with G = Hq / Hkv and T = 1 16-column MFMA
+ * tile per group when n_q * G <= 16, else T = 2 (the grouping of
+ * pkv_paged_multi_query_attn), and every group is a segment of the balanced
+ * split with the sequence's whole chunk list, the kv head's groups next to
+ * each other. The
  * layout is that of the decode plan, with header words 11..14 = n_q, G, qgs,
  * n_qg (zero in a decode plan), entry field g2 = kv head * n_qg + group, and
  * one descriptor per (sequence, kv head, group). n_workers from
@@ -302,12 +304,12 @@ size_t pkv_paged_window_plan_workspace_size(int32_t n_workers, int32_t n_q, int3
  * layouts and result as for pkv_paged_multi_query_attn, plus plan_host (its
  * header is checked against the call: S, n_q, Hq/Hkv, Hkv, d, cache type,
  * max_context_len and this device's wave count) and plan_dev (a device copy
- * of all plan_bytes, read by the kernels). Where the unplanned call also runs
- * one 16-column tile per pass (n_q * Hq/Hkv <= 16) the split is the same and
- * so are the outputs, bit for bit; wider windows take one pass per group of
- * 16 columns here (the unplanned call takes 32 per pass) and agree to
- * rounding. The workspace (pkv_paged_window_plan_workspace_size bytes) need
- * not be initialised; calls that overlap in time must not share it.
+ * of all plan_bytes, read by the kernels). Both calls group the columns alike
+ * and, with the same number of waves, split the work alike, so their outputs
+ * are equal bit for bit. A window of several groups per kv head reads K/V
+ * with cacheable loads (its groups read the same blocks). The workspace
+ * (pkv_paged_window_plan_workspace_size bytes) need not be initialised; calls
+ * that overlap in time must not share it.
  */
 pkv_status pkv_paged_multi_query_attn_planned(float* out, const void* q, const void* k_cache, const void* v_cache,
                                               const int32_t* block_tables, const int32_t* context_lens, int32_t S,

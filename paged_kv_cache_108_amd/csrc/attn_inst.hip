@@ -73,14 +73,17 @@ AttnKernel plan_for_bs(int bs) {
     return nullptr;
 }
 
-// mode: PM_ATTN, PM_STEP or PM_WINDOW; cached: cacheable K/V loads (decode
-// modes only, for plans that list shared blocks)
+// mode: PM_ATTN, PM_STEP, PM_WINDOW or PM_WINDOW2 (two tiles); cached:
+// cacheable K/V loads (decode modes, for plans that list shared blocks; two-
+// tile windows of several query groups, whose groups read the same blocks)
 template <int KV, int D>
 AttnKernel pick_plan_kernel(int bs, int mode, bool cached) {
     switch (mode) {
         case PM_ATTN: return cached ? plan_for_bs<KV, D, PM_ATTN, true>(bs) : plan_for_bs<KV, D, PM_ATTN, false>(bs);
         case PM_STEP: return cached ? plan_for_bs<KV, D, PM_STEP, true>(bs) : plan_for_bs<KV, D, PM_STEP, false>(bs);
         case PM_WINDOW: return cached ? nullptr : plan_for_bs<KV, D, PM_WINDOW, false>(bs);
+        case PM_WINDOW2:
+            return cached ? plan_for_bs<KV, D, PM_WINDOW2, true>(bs) : plan_for_bs<KV, D, PM_WINDOW2, false>(bs);
     }
     return nullptr;
 }

@@ -1386,25 +1386,33 @@ template <int KV, int D> constexpr int plan_slots() {
 // Planned kernel modes: decode attention alone, the decode step (attention
 // with the new token's write fused in), and a query window (n_q queries per
 // sequence, causal inside the window; each segment of the plan is one group
-// of qgs queries, G * qgs <= 16 columns of one MFMA tile).
-enum PlanMode { PM_ATTN = 0, PM_STEP = 1, PM_WINDOW = 2 };
+// of qgs queries: G * qgs <= 16 columns of one MFMA tile, or, for a window of
+// more than 16 columns, G * qgs <= 32 columns in two tiles that share every
+// loaded chunk).
+enum PlanMode { PM_ATTN = 0, PM_STEP = 1, PM_WINDOW = 2, PM_WINDOW2 = 3 };
 
 template <int KV, int D, int BS, int PM, bool CACHED>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1)))
 paged_attn_plan_kernel(AttnParams p) {
     constexpr bool STEP = PM == PM_STEP;
-    constexpr bool MQ = PM == PM_WINDOW;
+    constexpr bool MQ = PM == PM_WINDOW || PM == PM_WINDOW2;
+    constexpr int NT = PM == PM_WINDOW2 ? 2 : 1;     // 16-column tiles per segment
     __shared__ __align__(16) uint32_t ntstage[kWaves][D / 2];   // per wave: fp8 new-token codes
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int r16 = lane & 15;
     const int j4 = lane >> 4;
     const int G = p.G;
-    // a window: this lane's column r16 is query col_j of its group, head col_r
-    // of the kv head's G; decode: query 0, head r16
+    // a window: this lane's column 16 t + r16 of tile t is query col_j[t] of
+    // its group, head col_r[t] of the kv head's G; decode: query 0, head r16
     const int n_q = MQ ? p.n_q : 1;
-    const int col_j = MQ ? r16 / G : 0;
-    const int col_r = MQ ? r16 - col_j * G : r16;
+    int col_j[NT], col_r[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        const int c = 16 * t + r16;
+        col_j[t] = MQ ? c / G : 0;
+        col_r[t] = MQ ? c - col_j[t] * G : r16;
+    }
     const unsigned W_all = gridDim.x * kWaves;
     const unsigned w = xcd_order(blockIdx.x, gridDim.x) * kWaves + wave;
     const int stride = p.plan_stride;
@@ -1507,30 +1515,35 @@ paged_attn_plan_kernel(AttnParams p) {
     using QF = typename QFragT<KV>::T;
     struct Slot {
         Frag<KV, D> f;
-        QF q[q_loads<KV, D>()];
+        QF q[NT][q_loads<KV, D>()];
         NewTokRaw<KV, D> nt;
     };
     constexpr int NB = plan_slots<KV, D>();
     Slot sl[NB];
-    QF qf[q_loads<KV, D>()];
-    f32x4 o[D / 16];
-    float m_run = -INFINITY, l_run = 0.f;
+    QF qf[NT][q_loads<KV, D>()];
+    f32x4 o[NT][D / 16];
+    float m_run[NT], l_run[NT];
 #pragma unroll
-    for (int s2 = 0; s2 < D / 16; ++s2) o[s2] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // segment column group g2 -> kv head g; this lane's query j (windows), its
-    // q/out row and whether its column is in use
+    for (int t = 0; t < NT; ++t) {
+#pragma unroll
+        for (int s2 = 0; s2 < D / 16; ++s2) o[t][s2] = f32x4{0.f, 0.f, 0.f, 0.f};
+        m_run[t] = -INFINITY;
+        l_run[t] = 0.f;
+    }
+    // segment column group g2 -> kv head g; this lane's query j in tile t
+    // (windows), its q/out row and whether its column is in use
     struct Col {
         int g, j;
         bool live;
         size_t row;
     };
-    auto column = [&](int i, int g2) {
+    auto column = [&](int i, int g2, int t) {
         Col c;
         if constexpr (MQ) {
             c.g = g2 / p.n_qg;
-            c.j = (g2 - c.g * p.n_qg) * p.qgs + col_j;
-            c.live = r16 < p.cols && c.j < n_q;
-            c.row = (((size_t)i * n_q + c.j) * p.Hq + c.g * G + col_r) * D;
+            c.j = (g2 - c.g * p.n_qg) * p.qgs + col_j[t];
+            c.live = 16 * t + r16 < p.cols && c.j < n_q;
+            c.row = (((size_t)i * n_q + c.j) * p.Hq + c.g * G + col_r[t]) * D;
         } else {
             c.g = g2;
             c.j = 0;
@@ -1562,11 +1575,15 @@ paged_attn_plan_kernel(AttnParams p) {
             const int i = __builtin_amdgcn_readlane(mi, kk);
             const int gf = real ? __builtin_amdgcn_readlane(mgf, kk) : 0;
             const int kc = real ? __builtin_amdgcn_readlane(mkc, kk) : 0;
-            const Col c = column(i, gf & 0xFFFF);
-            const int g = c.g;
+            const int g = column(i, gf & 0xFFFF, 0).g;
             load_chunk<KV, D, BS, CACHED>(x.f, p, b0, b1, 16 * kc, g, r16, j4);
-            if ((gf >> 16) & pkv_split::kFirst)     // unused columns read row 0; step zeroes them
-                load_q_raw<KV, D>(p, c.live ? c.row : 0, j4, x.q);
+            if ((gf >> 16) & pkv_split::kFirst) {   // unused columns read row 0; step zeroes them
+#pragma unroll
+                for (int t = 0; t < NT; ++t) {
+                    const Col c = column(i, gf & 0xFFFF, t);
+                    load_q_raw<KV, D>(p, c.live ? c.row : 0, j4, x.q[t]);
+                }
+            }
             if constexpr (STEP) {
                 const int L = __builtin_amdgcn_readlane(mL, kk);
                 if (real && kc == ((L + 15) >> 4) - 1)
@@ -1580,14 +1597,16 @@ paged_attn_plan_kernel(AttnParams p) {
             const int gf = __builtin_amdgcn_readlane(mgf, k);
             const int kc = __builtin_amdgcn_readlane(mkc, k);
             const int L = __builtin_amdgcn_readlane(mL, k);
-            const Col c = column(i, gf & 0xFFFF);
-            const bool live = c.live;
-            const size_t out_row = c.row;
+            Col c[NT];
+#pragma unroll
+            for (int t = 0; t < NT; ++t) c[t] = column(i, gf & 0xFFFF, t);
             const int flags = gf >> 16;
             const int nch = (L + 15) >> 4;
             if (flags & pkv_split::kFirst) {      // a piece of a segment starts
 #pragma unroll
-                for (int u = 0; u < q_loads<KV, D>(); ++u) qf[u] = live ? x.q[u] : QF{};
+                for (int t = 0; t < NT; ++t)
+#pragma unroll
+                    for (int u = 0; u < q_loads<KV, D>(); ++u) qf[t][u] = c[t].live ? x.q[t][u] : QF{};
             }
             const int tc = 16 * kc;
             const bool patch = STEP && kc == nch - 1;
@@ -1602,62 +1621,70 @@ paged_attn_plan_kernel(AttnParams p) {
             const bool tail = tc + 16 > L;
             // a window: query j sees tokens < L - n_q + 1 + j (causal inside it)
             const bool masked = MQ ? tc + 16 > L - n_q + 1 : tail;
-            const int lim = MQ ? L - n_q + 1 + c.j : L;
             const int first_tok = tc + 4 * j4;
-            const f32x4 sc = chunk_scores<KV, D>(f, qf);
-            float xs[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                xs[e] = sc[e] * p.qk_scale;
-                if (masked && first_tok + e >= lim) xs[e] = -INFINITY;
-            }
-            const float cm = head_max(fmaxf(fmaxf(xs[0], xs[1]), fmaxf(xs[2], xs[3])));
-            const float m_new = fmaxf(m_run, cm);
-            // a column that has seen no visible token yet keeps m = -inf; its
-            // exponentials are taken against 0 so they stay 0, not NaN
-            const float m_ref = MQ && m_new == -INFINITY ? 0.f : m_new;
-            const float alpha = __builtin_amdgcn_exp2f(m_run - m_ref);
-            float pr[4];
+            for (int t = 0; t < NT; ++t) {
+                const int lim = MQ ? L - n_q + 1 + c[t].j : L;
+                const f32x4 sc = chunk_scores<KV, D>(f, qf[t]);
+                float xs[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) pr[e] = __builtin_amdgcn_exp2f(xs[e] - m_ref);
-            l_run = l_run * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
-            m_run = m_new;
-            if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
+                for (int e = 0; e < 4; ++e) {
+                    xs[e] = sc[e] * p.qk_scale;
+                    if (masked && first_tok + e >= lim) xs[e] = -INFINITY;
+                }
+                const float cm = head_max(fmaxf(fmaxf(xs[0], xs[1]), fmaxf(xs[2], xs[3])));
+                const float m_new = fmaxf(m_run[t], cm);
+                // a column that has seen no visible token yet keeps m = -inf;
+                // its exponentials are taken against 0 so they stay 0, not NaN
+                const float m_ref = MQ && m_new == -INFINITY ? 0.f : m_new;
+                const float alpha = __builtin_amdgcn_exp2f(m_run[t] - m_ref);
+                float pr[4];
 #pragma unroll
-                for (int s2 = 0; s2 < D / 16; ++s2) o[s2] *= alpha;
+                for (int e = 0; e < 4; ++e) pr[e] = __builtin_amdgcn_exp2f(xs[e] - m_ref);
+                l_run[t] = l_run[t] * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
+                m_run[t] = m_new;
+                if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
+#pragma unroll
+                    for (int s2 = 0; s2 < D / 16; ++s2) o[t][s2] *= alpha;
+                }
+                if constexpr (kVRows)
+                    if (t == 0) {                 // V is first needed here
+                        v_rows_to_operand<KV, D, BS>(f);
+                        if constexpr (STEP)
+                            if (patch) patch_new_v<KV, D>(f, nt, L - 1 - tc, j4);
+                    }
+                chunk_pv<KV, D>(f, pr, o[t], tail, first_tok, L);
             }
-            if constexpr (kVRows) {
-                v_rows_to_operand<KV, D, BS>(f);
-                if constexpr (STEP)
-                    if (patch) patch_new_v<KV, D>(f, nt, L - 1 - tc, j4);
-            }
-            chunk_pv<KV, D>(f, pr, o, tail, first_tok, L);
 
             if (flags & pkv_split::kLast) {       // the piece ends here
-                const float l_tot = head_sum(l_run);
-                if (live) {
-                    if (flags & pkv_split::kWhole) {
-                        const float sc_o = p.v_scale / l_tot;
-                        float* orow = p.out + out_row + 4 * j4;
 #pragma unroll
-                        for (int s2 = 0; s2 < D / 16; ++s2) st_untracked(orow + 16 * s2, o[s2] * sc_o);
-                        if (p.lse && j4 == 0) st_untracked(p.lse + out_row / D, m_run + __log2f(l_tot));
-                    } else {
-                        const size_t rr = (size_t)(2 * w + ((flags & pkv_split::kOdd) ? 1 : 0)) * C + r16;
-                        const size_t nrec = (size_t)p.n_rec;
-                        float* orec = p.ws + rr * D + 4 * j4;
+                for (int t = 0; t < NT; ++t) {
+                    const float l_tot = head_sum(l_run[t]);
+                    if (c[t].live) {
+                        if (flags & pkv_split::kWhole) {
+                            const float sc_o = p.v_scale / l_tot;
+                            float* orow = p.out + c[t].row + 4 * j4;
 #pragma unroll
-                        for (int s2 = 0; s2 < D / 16; ++s2) st_untracked(orec + 16 * s2, o[s2] * p.v_scale);
-                        if (j4 == 0) {
-                            st_untracked(p.ws + nrec * C * D + rr, m_run);
-                            st_untracked(p.ws + nrec * C * (D + 1) + rr, l_tot);
+                            for (int s2 = 0; s2 < D / 16; ++s2) st_untracked(orow + 16 * s2, o[t][s2] * sc_o);
+                            if (p.lse && j4 == 0) st_untracked(p.lse + c[t].row / D, m_run[t] + __log2f(l_tot));
+                        } else {
+                            const size_t rr =
+                                (size_t)(2 * w + ((flags & pkv_split::kOdd) ? 1 : 0)) * C + 16 * t + r16;
+                            const size_t nrec = (size_t)p.n_rec;
+                            float* orec = p.ws + rr * D + 4 * j4;
+#pragma unroll
+                            for (int s2 = 0; s2 < D / 16; ++s2) st_untracked(orec + 16 * s2, o[t][s2] * p.v_scale);
+                            if (j4 == 0) {
+                                st_untracked(p.ws + nrec * C * D + rr, m_run[t]);
+                                st_untracked(p.ws + nrec * C * (D + 1) + rr, l_tot);
+                            }
                         }
                     }
-                }
 #pragma unroll
-                for (int s2 = 0; s2 < D / 16; ++s2) o[s2] = f32x4{0.f, 0.f, 0.f, 0.f};
-                m_run = -INFINITY;
-                l_run = 0.f;
+                    for (int s2 = 0; s2 < D / 16; ++s2) o[t][s2] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    m_run[t] = -INFINITY;
+                    l_run[t] = 0.f;
+                }
             }
         };
         // entries k, k + 1, ... run through slots k mod NB; entry k + NB - 1

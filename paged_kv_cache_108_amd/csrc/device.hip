@@ -1059,7 +1059,7 @@ int plan_workers(int kv, int d, int bs) {
     // the smallest residency of the planned kernel's variants: a plan serves
     // any of them
     int resident = 1 << 30;
-    for (int mode : {PM_ATTN, PM_STEP, PM_WINDOW})
+    for (int mode : {PM_ATTN, PM_STEP, PM_WINDOW, PM_WINDOW2})
         for (bool cached : {false, true}) {
             if (mode == PM_WINDOW && cached) continue;
             const AttnKernel k = pick_plan(kv, d, bs, mode, cached);
@@ -1099,7 +1099,7 @@ pkv_status check_plan(const char* fn, const void* plan_host, const void* plan_de
     *qgs = 1;
     *n_qg = 1;
     if (n_q > 0) {
-        const pkv_split::QueryGroups q = pkv_split::query_groups_in(n_q, G, 1);
+        const pkv_split::QueryGroups q = pkv_split::query_groups_in(n_q, G, pkv_split::window_plan_tiles(n_q, G));
         if (h[13] != q.qgs || h[14] != q.n_qg)
             return fail(PKV_E_INVALID, "%s: the plan's query groups (%d x %d) are not those of %d queries over %d "
                         "heads", fn, h[14], h[13], n_q, G);
@@ -1191,10 +1191,13 @@ pkv_status plan_launch(const char* fn, float* out, const void* q, const void* k_
     prm.n_workers = n_workers;
     prm.n_rec = 2 * n_workers;
     auto st = static_cast<hipStream_t>(stream);
-    const int mode = n_q > 0 ? PM_WINDOW : is_step ? PM_STEP : PM_ATTN;
-    // a decode plan that lists shared blocks: cacheable K/V loads
-    const bool cached = n_q == 0 &&
-                        (static_cast<const int32_t*>(plan_host)[pkv_split::kPlanFlagsWord] & pkv_split::kPlanSharedBlocks);
+    const int mode = n_q > 0 ? (cols > 16 ? PM_WINDOW2 : PM_WINDOW) : is_step ? PM_STEP : PM_ATTN;
+    // cacheable K/V loads for a decode plan that lists shared blocks, and for
+    // a window of several query groups per kv head (neighbouring segments
+    // that read the same blocks at about the same time)
+    const bool cached =
+        n_q == 0 ? (static_cast<const int32_t*>(plan_host)[pkv_split::kPlanFlagsWord] & pkv_split::kPlanSharedBlocks) != 0
+                 : mode == PM_WINDOW2 && n_qg > 1;
     hipLaunchKernelGGL(pick_plan(kv, d, bs, mode, cached), dim3((unsigned)(n_workers / kWaves)), dim3(kThreads), 0,
                        st, prm);
     hipError_t e = hipGetLastError();
@@ -1307,7 +1310,8 @@ extern "C" size_t pkv_paged_window_plan_workspace_size(int32_t n_workers, int32_
                                                       int32_t d) {
     if (n_workers <= 0 || n_q <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || Hq / Hkv > 16 || !pkv::is_head_dim(d))
         return 0;
-    const pkv_split::QueryGroups q = pkv_split::query_groups_in(n_q, Hq / Hkv, 1);
+    const int32_t G = Hq / Hkv;
+    const pkv_split::QueryGroups q = pkv_split::query_groups_in(n_q, G, pkv_split::window_plan_tiles(n_q, G));
     return grid_records_bytes(n_workers, (size_t)q.cols, d);
 }
 

@@ -44,8 +44,8 @@ pkv_status build_plan(const char* fn, const int32_t* lens, int32_t S, int32_t n_
     if (n_workers > (1 << 20)) return fail(PKV_E_INVALID, "%s: n_workers=%d too large", fn, n_workers);
     const int cost = seg_cost(kv, d);
     // decode: one segment per (sequence, kv head); a window: n_qg per kv head
-    // (one 16-column tile each), the kv head's groups next to each other
-    const QueryGroups qgr = n_q > 0 ? query_groups_in(n_q, G, 1) : QueryGroups{1, 1, G};
+    // (one or two 16-column tiles each), the kv head's groups next to each other
+    const QueryGroups qgr = n_q > 0 ? query_groups_in(n_q, G, window_plan_tiles(n_q, G)) : QueryGroups{1, 1, G};
     const int64_t HS64 = (int64_t)Hkv * qgr.n_qg;
     if (HS64 > 0xFFFF) return fail(PKV_E_INVALID, "%s: %lld segments per sequence", fn, (long long)HS64);
     const int32_t HS = (int32_t)HS64;

@@ -77,6 +77,11 @@ PKV_HD inline QueryGroups query_groups_in(int n_q, int G, int tiles) {
     return r;
 }
 
+// Tiles per query group of a window plan: one when the window's n_q * G
+// columns fit one 16-column tile, else two (32 columns per group, as the
+// unplanned window call takes per pass).
+PKV_HD inline int window_plan_tiles(int n_q, int G) { return (long long)n_q * G <= 16 ? 1 : 2; }
+
 // ---------------------------------------------------------------------------
 // The work plan (pkv_build_paged_decode_plan, pkv_build_paged_window_plan;
 // int32 words):

@@ -1,13 +1,13 @@
 """GPU parity of planned query windows (pkv_paged_multi_query_attn_planned).
 
 A window plan cuts each kv head's (query, head) columns into groups of one
-16-column tile and makes each group a segment of the balanced split. Where the
-unplanned window call also takes one tile per pass (n_q * G <= 16) and both run
-the same number of waves, the split is the same one and the planned outputs
-must equal the unplanned call's bit for bit; wider windows take one pass per
-16 columns here (32 in the unplanned call) and agree within the tolerance.
-Every case is checked against the fp64 oracle's windowed attention. A decode
-plan, or a window plan for another window, is refused.
+16-column tile (a window of n_q * G <= 16 columns) or two (a wider one) and
+makes each group a segment of the balanced split, as the unplanned window call
+groups them per pass. Where both run the same number of waves the split is the
+same one and the planned outputs must equal the unplanned call's bit for bit;
+otherwise they agree within the tolerance. Every case is checked against the
+fp64 oracle's windowed attention. A decode plan, or a window plan for another
+window, is refused.
 """
 
 import numpy as np
@@ -59,8 +59,7 @@ def _case(w, n_q):
          k_scale=w.k_scale, v_scale=w.v_scale)
     torch.cuda.synchronize()
     got_h, want_h = to_host(got).copy(), to_host(want).copy()
-    same_split = (n_q * G <= 16 and
-                  plan.n_workers == 4 * torch.cuda.get_device_properties(0).multi_processor_count)
+    same_split = plan.n_workers == 4 * torch.cuda.get_device_properties(0).multi_processor_count
     print(f"[case] {plan.n_workers} waves, {int(plan.host[14])} query groups of {int(plan.host[13])}; "
           f"same split as the unplanned call: {same_split}", flush=True)
     if same_split:
@@ -87,9 +86,11 @@ def test_planned_window_one_tile(name, cache, n_q):
     _case(W.make(name, cache_dtype=cache), n_q)
 
 
-# several groups per kv head (one pass over the blocks for each)
+# two tiles per group (more than 16 columns), and several groups per kv head
+# (one pass over the blocks for each)
 @pytest.mark.parametrize("name,cache,n_q", [
     ("llama8b", None, 8), ("llama8b", None, 16), ("llama8b", None, 20), ("small", None, 5), ("small", None, 12),
+    ("llama8b", "fp8", 8), ("small", "fp8", 5),
 ])
 def test_planned_window_several_groups(name, cache, n_q):
     _case(W.make(name, cache_dtype=cache), n_q)

@@ -28,11 +28,13 @@ def seg_cost(dtype, d):
 def reference_plan(lens, Hkv, d, dtype, max_len, n_workers, n_q=0, G=0):
     """The plan, from the definition (plain Python). n_q > 0: a window plan,
     whose segments are (sequence, kv head, query group) with groups of
-    qgs = min(n_q, max(1, 16 // G)) queries (one 16-column tile)."""
+    qgs = min(n_q, max(1, 16 T // G)) queries: T = 1 16-column tile when the
+    window's n_q G columns fit one, else T = 2."""
     c = seg_cost(dtype, d)
     L = [min(int(x), max_len) for x in lens]
     S = len(L)
-    qgs = min(n_q, max(1, 16 // G)) if n_q else 1
+    T = 1 if n_q * G <= 16 else 2
+    qgs = min(n_q, max(1, 16 * T // G)) if n_q else 1
     n_qg = -(-n_q // qgs) if n_q else 1
     HS = Hkv * n_qg                           # segments per sequence
     segs = []                                 # (i, g2, first position, n chunks)
@@ -158,7 +160,9 @@ def test_window_plan_matches_the_definition(name, kv, n_q, workers):
     assert got.shape == want.shape
     assert np.array_equal(got.astype(np.int64), want)
     qgs = int(got[13])
-    assert got[11] == n_q and got[12] == G and qgs * G <= 16 and got[14] * qgs >= n_q
+    assert got[11] == n_q and got[12] == G and got[14] * qgs >= n_q
+    # one tile when the window fits it, else two tiles (32 columns) per group
+    assert qgs * G <= (16 if n_q * G <= 16 else 32) and (n_q * G <= 16 or qgs == min(n_q, max(1, 32 // G)))
 
 
 def test_window_plan_long_lengths():
