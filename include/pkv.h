@@ -246,7 +246,8 @@ int32_t pkv_paged_decode_plan_workers(int32_t d, int32_t bs, pkv_dtype cache_dty
  * here, flags), then per wave its chunk entries
  * {sequence, kv head | flags << 16, chunk index, L} (unused: sequence -1),
  * then one (first record, record count) descriptor per (sequence, kv head).
- * Requires S > 0, Hkv > 0, d in {64, 128}, n_workers > 0.
+ * Requires S > 0, Hkv > 0, d in {64, 128}, n_workers > 0 and
+ * 0 <= max_context_len <= 2^30; PKV_E_INVALID otherwise.
  */
 pkv_status pkv_build_paged_decode_plan(const int32_t* context_lens, int32_t S, int32_t Hkv, int32_t d,
                                        pkv_dtype cache_dtype, int32_t max_context_len, int32_t n_workers,

@@ -42,6 +42,9 @@ pkv_status build_plan(const char* fn, const int32_t* lens, int32_t S, int32_t n_
     else return fail(PKV_E_INVALID, "%s: unsupported cache dtype %d", fn, cache_dtype);
     if (!lens) return fail(PKV_E_INVALID, "%s: NULL pointer", fn);
     if (n_workers > (1 << 20)) return fail(PKV_E_INVALID, "%s: n_workers=%d too large", fn, n_workers);
+    // chunk counts are formed in 32-bit arithmetic (split.h)
+    if (max_context_len > (1 << 30))
+        return fail(PKV_E_INVALID, "%s: max_context_len=%d above 2^30", fn, max_context_len);
     const int cost = seg_cost(kv, d);
     // decode: one segment per (sequence, kv head); a window: n_qg per kv head
     // (one or two 16-column tiles each), the kv head's groups next to each other
@@ -190,8 +193,8 @@ extern "C" pkv_status pkv_plan_mark_shared_blocks(void* plan, size_t plan_bytes,
     std::vector<int32_t> seen;
     seen.reserve(1024);
     for (int32_t i = 0; i < S; ++i) {
-        const int32_t L = std::min(context_lens[i], max_len);
-        const int32_t nb = L > 0 ? std::min<int32_t>((L + bs - 1) / bs, max_blocks) : 0;
+        const int64_t L = std::min(context_lens[i], max_len);
+        const int32_t nb = L > 0 ? (int32_t)std::min<int64_t>((L + bs - 1) / bs, max_blocks) : 0;
         for (int32_t j = 0; j < nb; ++j) seen.push_back(block_tables[(size_t)i * max_blocks + j]);
     }
     std::sort(seen.begin(), seen.end());

@@ -213,3 +213,17 @@ def test_shared_blocks_mark():
     assert not pkv.plan_mark_shared_blocks(plan, tables, [40, 20], 16) and plan[15] == 0    # cleared again
     same_row = np.array([[9, 9, -1, -1], [1, 2, -1, -1]], dtype=np.int32)
     assert pkv.plan_mark_shared_blocks(plan, same_row, [20, 20], 16)
+
+
+def test_plan_rejects_lengths_past_two_to_the_thirty():
+    big = 2**31 - 1
+    with pytest.raises(pkv.PkvError):
+        pkv.build_paged_decode_plan([big, 5], 1, 64, 1, big, 16)
+    with pytest.raises(pkv.PkvError):
+        pkv.build_paged_window_plan([big, 5], 2, 4, 1, 64, 1, big, 16)
+    # lengths past max_context_len are clamped, and the mark reads no more of a
+    # table row than it holds
+    plan = pkv.build_paged_decode_plan([big, 5], 1, 64, 1, 64, 16)
+    tables = np.array([[3, 4], [5, -1]], dtype=np.int32)
+    assert not pkv.plan_mark_shared_blocks(plan, tables, [big, 5], 16)
+    assert pkv.plan_mark_shared_blocks(plan, np.array([[3, 4], [4, -1]], dtype=np.int32), [big, 5], 16)
