@@ -148,7 +148,8 @@ size_t pkv_paged_decode_attn_workspace_size(int32_t S, int32_t Hq, int32_t Hkv, 
  * Supported (q_dtype, cache_dtype): (F32, F32), (BF16, BF16), (BF16, FP8_E4M3).
  * Requires S > 0, Hkv > 0, Hq % Hkv == 0, 1 <= Hq/Hkv <= 16, d in {64, 128},
  * bs in {8, 16, 32, 64, 128}, P > 0, max_blocks > 0, 0 <= max_context_len <=
- * max_blocks * bs, softmax_scale finite; for FP8 finite k_scale, v_scale.
+ * min(max_blocks * bs, 2^30), softmax_scale finite; for FP8 finite k_scale,
+ * v_scale.
  *
  * partition_size selects how sequences are split across workgroups (split-K);
  * partial results are always merged exactly (running max, sum of

@@ -783,6 +783,9 @@ pkv_status attn_launch(const char* fn, float* out, const void* q, const void* k_
     if (max_context_len < 0 || (int64_t)max_context_len > (int64_t)max_blocks * bs)
         return fail(PKV_E_INVALID, "%s: max_context_len=%d outside [0, max_blocks*bs=%lld]", fn,
                     max_context_len, (long long)max_blocks * bs);
+    // the kernels form chunk counts in 32-bit arithmetic (split.h)
+    if (max_context_len > (1 << 30))
+        return fail(PKV_E_INVALID, "%s: max_context_len=%d above 2^30", fn, max_context_len);
     int kv;
     if (q_dtype == PKV_F32 && cache_dtype == PKV_F32) kv = KV_F32;
     else if (q_dtype == PKV_BF16 && cache_dtype == PKV_BF16) kv = KV_BF16;
@@ -1261,8 +1264,8 @@ extern "C" pkv_status pkv_paged_gather_read(const void* k_cache, const void* v_c
     if (cache_dtype != PKV_F32 && cache_dtype != PKV_BF16 && cache_dtype != PKV_FP8_E4M3)
         return fail(PKV_E_INVALID, "%s: unsupported cache dtype %d", fn, cache_dtype);
     if (!k_cache || !v_cache || !block_tables || !sink) return fail(PKV_E_INVALID, "%s: NULL pointer", fn);
-    if ((int64_t)max_context_len > (int64_t)max_blocks * bs)
-        return fail(PKV_E_INVALID, "%s: max_context_len=%d exceeds max_blocks*bs=%lld", fn, max_context_len,
+    if ((int64_t)max_context_len > (int64_t)max_blocks * bs || max_context_len > (1 << 30))
+        return fail(PKV_E_INVALID, "%s: max_context_len=%d exceeds max_blocks*bs=%lld or 2^30", fn, max_context_len,
                     (long long)max_blocks * bs);
     const int kv = cache_dtype == PKV_F32 ? KV_F32 : cache_dtype == PKV_BF16 ? KV_BF16 : KV_FP8;
     int32_t n_workers = 0, stride = 0, qgs = 1, n_qg = 1;

@@ -206,6 +206,7 @@ def _attn(**kw):
     dict(maxb=0), dict(maxlen=161), dict(maxlen=-1), dict(qd=0), dict(qd=1, cd=0),
     dict(qd=2, cd=2), dict(part=16), dict(part=-32), dict(part=-2), dict(scale=float("inf")),
     dict(qd=1, cd=2, ks=float("nan")), dict(out=None), dict(tab=None), dict(S=-1), dict(Hkv=0),
+    dict(maxb=1 << 24, bs=128, maxlen=(1 << 30) + 1),          # above 2^30, within the table
 ])
 def test_attn_rejects_invalid_arguments(kw):
     assert _attn(**kw) == _lib.PKV_E_INVALID
