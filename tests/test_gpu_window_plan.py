@@ -107,6 +107,9 @@ def test_planned_window_long_fp8():
     ([9, 64, 65, 700], 14, 2, 64, 32, "bf16", 9),             # G 7: five groups of 2 queries
     ([3, 3, 50, 129], 16, 1, 128, 128, "fp8", 3),             # G 16: one query per group
     ([7, 300, 16, 0, 1], 8, 2, 64, 16, "fp8", 1),             # fp8 at d 64: two workgroups per CU
+    ([7, 8, 90, 333, 0], 12, 4, 64, 16, "bf16", 7),           # G 3: 21 columns, a tile boundary inside a query
+    ([6, 41, 500, 1200], 10, 2, 128, 32, "fp8", 6),           # G 5: 30 columns in two tiles
+    ([12, 13, 64, 260], 4, 2, 128, 8, "f32", 12),             # G 2, bs 8: 24 columns
 ])
 def test_planned_window_edge_shapes(lens, Hq, Hkv, d, bs, dt, n_q):
     w = W.make_custom(lens=lens, Hq=Hq, Hkv=Hkv, d=d, bs=bs, q_dtype="f32" if dt == "f32" else "bf16",
