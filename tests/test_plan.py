@@ -227,3 +227,21 @@ def test_plan_rejects_lengths_past_two_to_the_thirty():
     tables = np.array([[3, 4], [5, -1]], dtype=np.int32)
     assert not pkv.plan_mark_shared_blocks(plan, tables, [big, 5], 16)
     assert pkv.plan_mark_shared_blocks(plan, np.array([[3, 4], [4, -1]], dtype=np.int32), [big, 5], 16)
+
+
+@pytest.mark.parametrize("n_q,Hq,Hkv,d", [(1, 32, 8, 128), (4, 32, 8, 128), (5, 32, 8, 128), (8, 32, 8, 128),
+                                          (16, 32, 8, 128), (5, 14, 2, 64), (3, 16, 1, 128), (20, 2, 2, 64)])
+def test_window_plan_workspace_matches_its_grouping(n_q, Hq, Hkv, d):
+    """The planned window call's workspace holds two records per wave of the
+    plan's G * qgs columns, with the grouping the plan header states, which is
+    the unplanned call's (its workspace has the same column count)."""
+    n_workers = 1024
+    plan = pkv.build_paged_window_plan([300, 40, 7000], n_q, Hq, Hkv, d, 1, 8192, n_workers)
+    G = Hq // Hkv
+    qgs, n_qg = int(plan[13]), int(plan[14])
+    cols = G * qgs
+    want = -(-(2 * n_workers * cols * (d + 2) * 4) // 256) * 256
+    got = int(pkv.lib().pkv_paged_window_plan_workspace_size(n_workers, n_q, Hq, Hkv, d))
+    assert got == want
+    T = 1 if n_q * G <= 16 else 2
+    assert cols <= 16 * T and qgs == min(n_q, max(1, 16 * T // G)) and n_qg == -(-n_q // qgs)
