@@ -336,7 +336,12 @@ size_t pkv_paged_decode_plan_workspace_size(int32_t n_workers, int32_t Hq, int32
  * matter; calls that overlap in time must not share it. attn_done_event:
  * NULL, or a hipEvent_t that the call records on stream after the attention
  * kernel and before the merge kernel, so that a caller can time the two
- * apart (the call's work is the same either way).
+ * apart (the call's work is the same either way). Over an FP8_E4M3 cache the
+ * wave that holds a sequence's last chunk writes that token and then reads
+ * it back from the pool instead of taking it from k_new/v_new; the result
+ * is the same, bit for bit, except for a token whose table entry lies
+ * outside [0, P): it is not stored, and that sequence's output is then
+ * unspecified (as for any out-of-range entry).
  */
 pkv_status pkv_paged_decode_step_planned(float* out, const void* q, const void* k_new, const void* v_new,
                                          void* k_cache, void* v_cache,
