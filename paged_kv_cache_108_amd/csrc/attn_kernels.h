@@ -1550,8 +1550,9 @@ paged_attn_plan_kernel(AttnParams p) {
     // Pipeline slots: a chunk in flight with, when its entry starts a piece,
     // the piece's q row and, when it is the segment's last chunk in a decode
     // step over an f32 or bf16 cache, the new token, all issued together so
-    // that a piece start does not wait for a load of its own. Chunks of 4 KiB or less keep three in
-    // flight, larger ones one, while the wave works on another.
+    // that a piece start does not wait for a load of its own. Chunks of 4 KiB
+    // or less keep three in flight, larger ones one, while the wave works on
+    // another.
     using QF = typename QFragT<KV>::T;
     struct Slot {
         Frag<KV, D> f;
