@@ -192,6 +192,31 @@ __device__ __forceinline__ void st_untracked(uint8_t* a, uint32_t v) {
     asm volatile("global_store_byte %0, %1, off" : : "v"(a), "v"(v) : "memory");
 }
 
+// The decode step's stores of its new tokens into the pools, untracked as
+// above: one element per lane, the V ones one per channel row of a sub-tile
+// (2 or 4 bytes in each of d rows of 32 or 64 bytes). NT sets the
+// nontemporal bit, taken for f32 and bf16 caches at d 128 (same-box medians,
+// planned step: `llama8b` 67.4-67.7 -> 65.8-65.9 us, `long` unchanged; at
+// d 64 `small` went from 23.4 to 23.8-24.0 us). An fp8 step reads its
+// tokens back from the pool in the same kernel and keeps plain stores
+// (`llama8b` fp8 39.2-39.4 us, 40.5-40.7 with the bit).
+#ifndef PKV_TOKEN_NT_MIN_D
+#define PKV_TOKEN_NT_MIN_D 128
+#endif
+template <int KV, int D> constexpr bool token_nt() { return KV != KV_FP8 && D >= PKV_TOKEN_NT_MIN_D; }
+template <bool NT> __device__ __forceinline__ void st_token(float* a, float v) {
+    if constexpr (NT) asm volatile("global_store_dword %0, %1, off nt" : : "v"(a), "v"(v) : "memory");
+    else asm volatile("global_store_dword %0, %1, off" : : "v"(a), "v"(v) : "memory");
+}
+template <bool NT> __device__ __forceinline__ void st_token(uint16_t* a, uint32_t v) {
+    if constexpr (NT) asm volatile("global_store_short %0, %1, off nt" : : "v"(a), "v"(v) : "memory");
+    else asm volatile("global_store_short %0, %1, off" : : "v"(a), "v"(v) : "memory");
+}
+template <bool NT> __device__ __forceinline__ void st_token(uint8_t* a, uint32_t v) {
+    if constexpr (NT) asm volatile("global_store_byte %0, %1, off nt" : : "v"(a), "v"(v) : "memory");
+    else asm volatile("global_store_byte %0, %1, off" : : "v"(a), "v"(v) : "memory");
+}
+
 // Per-cache-type register fragments of one 16-token chunk.
 template <int KV, int D> struct Frag;
 
@@ -1060,9 +1085,11 @@ paged_attn_stream_kernel(AttnParams p) {
                                               (size_t)c * VS + o % VS
                                         : (((size_t)b * p.Hkv + g) * BS + o) * D + c;
                 void* pool = const_cast<void*>(is_v ? p.v : p.k);
-                if constexpr (KV == KV_F32) st_untracked(static_cast<float*>(pool) + dst, __uint_as_float(val[u]));
-                else if constexpr (KV == KV_BF16) st_untracked(static_cast<uint16_t*>(pool) + dst, val[u]);
-                else st_untracked(static_cast<uint8_t*>(pool) + dst,
+                constexpr bool kTokNt = token_nt<KV, D>();
+                if constexpr (KV == KV_F32)
+                    st_token<kTokNt>(static_cast<float*>(pool) + dst, __uint_as_float(val[u]));
+                else if constexpr (KV == KV_BF16) st_token<kTokNt>(static_cast<uint16_t*>(pool) + dst, val[u]);
+                else st_token<kTokNt>(static_cast<uint8_t*>(pool) + dst,
                                   e4m3_encode(bf16_bits_to_f32((uint16_t)val[u]) * (is_v ? p.v_inv : p.k_inv)));
             }
         }
@@ -1469,9 +1496,10 @@ paged_attn_plan_kernel(AttnParams p) {
                                           (size_t)c * VS + o % VS
                                     : (((size_t)b * p.Hkv + g) * BS + o) * D + c;
             void* pool = const_cast<void*>(is_v ? p.v : p.k);
-            if constexpr (KV == KV_F32) st_untracked(static_cast<float*>(pool) + dst, __uint_as_float(val[u]));
-            else if constexpr (KV == KV_BF16) st_untracked(static_cast<uint16_t*>(pool) + dst, val[u]);
-            else st_untracked(static_cast<uint8_t*>(pool) + dst,
+            constexpr bool kTokNt = token_nt<KV, D>();
+            if constexpr (KV == KV_F32) st_token<kTokNt>(static_cast<float*>(pool) + dst, __uint_as_float(val[u]));
+            else if constexpr (KV == KV_BF16) st_token<kTokNt>(static_cast<uint16_t*>(pool) + dst, val[u]);
+            else st_token<kTokNt>(static_cast<uint8_t*>(pool) + dst,
                               e4m3_encode(bf16_bits_to_f32((uint16_t)val[u]) * (is_v ? p.v_inv : p.k_inv)));
         }
     };
