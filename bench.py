@@ -94,32 +94,32 @@ def device_source_sha256(paths=None):
 # the kernel source is the one the counters were taken with.
 MEASURED_TRAFFIC = {
     ("beam", "bf16", 16, -1, "planned"): {
-        "source_sha256": "1e4a78b126e4cd1c485d1669cf632af477bd5ea863a4be915714b4f5b55b8193",
-        "fetch_kib": 244582.4, "write_kib": 10434.4, "fetch_scale": 2.0, "write_scale": 1.0,
+        "source_sha256": "c9dba6b0f5d5dd04ce8c97c907142e3ffc1563e2d6323b27e5e9604bc61a6b36",
+        "fetch_kib": 245496.1, "write_kib": 10433.9, "fetch_scale": 2.0, "write_scale": 1.0,
     },
     ("llama8b", "bf16", 16, -1, "planned"): {
-        "source_sha256": "1e4a78b126e4cd1c485d1669cf632af477bd5ea863a4be915714b4f5b55b8193",
-        "fetch_kib": 170406.4, "write_kib": 5938.9, "fetch_scale": 2.0, "write_scale": 1.0,
+        "source_sha256": "c9dba6b0f5d5dd04ce8c97c907142e3ffc1563e2d6323b27e5e9604bc61a6b36",
+        "fetch_kib": 170307.7, "write_kib": 5939.1, "fetch_scale": 2.0, "write_scale": 1.0,
     },
     ("small", "bf16", 16, -1, "planned"): {
-        "source_sha256": "1e4a78b126e4cd1c485d1669cf632af477bd5ea863a4be915714b4f5b55b8193",
-        "fetch_kib": 34311.4, "write_kib": 4412.9, "fetch_scale": 2.0, "write_scale": 1.0,
+        "source_sha256": "c9dba6b0f5d5dd04ce8c97c907142e3ffc1563e2d6323b27e5e9604bc61a6b36",
+        "fetch_kib": 34306.3, "write_kib": 4412.8, "fetch_scale": 2.0, "write_scale": 1.0,
     },
     ("llama8b", "fp8", 16, -1, "planned"): {
-        "source_sha256": "1e4a78b126e4cd1c485d1669cf632af477bd5ea863a4be915714b4f5b55b8193",
-        "fetch_kib": 86290.9, "write_kib": 4806.2, "fetch_scale": 2.0, "write_scale": 1.0,
+        "source_sha256": "c9dba6b0f5d5dd04ce8c97c907142e3ffc1563e2d6323b27e5e9604bc61a6b36",
+        "fetch_kib": 86288.0, "write_kib": 4805.9, "fetch_scale": 2.0, "write_scale": 1.0,
     },
     ("small", "fp8", 16, -1, "planned"): {
-        "source_sha256": "1e4a78b126e4cd1c485d1669cf632af477bd5ea863a4be915714b4f5b55b8193",
-        "fetch_kib": 18918.9, "write_kib": 5530.5, "fetch_scale": 2.0, "write_scale": 1.0,
+        "source_sha256": "c9dba6b0f5d5dd04ce8c97c907142e3ffc1563e2d6323b27e5e9604bc61a6b36",
+        "fetch_kib": 18919.0, "write_kib": 5530.5, "fetch_scale": 2.0, "write_scale": 1.0,
     },
     ("long", "bf16", 16, -1, "planned"): {
-        "source_sha256": "1e4a78b126e4cd1c485d1669cf632af477bd5ea863a4be915714b4f5b55b8193",
-        "fetch_kib": 1054234.1, "write_kib": 5730.4, "fetch_scale": 2.0, "write_scale": 1.0,
+        "source_sha256": "c9dba6b0f5d5dd04ce8c97c907142e3ffc1563e2d6323b27e5e9604bc61a6b36",
+        "fetch_kib": 1054198.5, "write_kib": 5730.6, "fetch_scale": 2.0, "write_scale": 1.0,
     },
     ("long", "fp8", 16, -1, "planned"): {
-        "source_sha256": "1e4a78b126e4cd1c485d1669cf632af477bd5ea863a4be915714b4f5b55b8193",
-        "fetch_kib": 529617.8, "write_kib": 5454.2, "fetch_scale": 2.0, "write_scale": 1.0,
+        "source_sha256": "c9dba6b0f5d5dd04ce8c97c907142e3ffc1563e2d6323b27e5e9604bc61a6b36",
+        "fetch_kib": 529618.0, "write_kib": 5454.3, "fetch_scale": 2.0, "write_scale": 1.0,
     },
 }
 
