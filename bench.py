@@ -94,32 +94,32 @@ def device_source_sha256(paths=None):
 # the kernel source is the one the counters were taken with.
 MEASURED_TRAFFIC = {
     ("beam", "bf16", 16, -1, "planned"): {
-        "source_sha256": "c9dba6b0f5d5dd04ce8c97c907142e3ffc1563e2d6323b27e5e9604bc61a6b36",
-        "fetch_kib": 245496.1, "write_kib": 10433.9, "fetch_scale": 2.0, "write_scale": 1.0,
+        "source_sha256": "820800b3ff5373f9f148bf35ac40925d69bcc578f999c8d58b411164ae5ff0dd",
+        "fetch_kib": 245784.3, "write_kib": 10434.2, "fetch_scale": 2.0, "write_scale": 1.0,
     },
     ("llama8b", "bf16", 16, -1, "planned"): {
-        "source_sha256": "c9dba6b0f5d5dd04ce8c97c907142e3ffc1563e2d6323b27e5e9604bc61a6b36",
-        "fetch_kib": 170307.7, "write_kib": 5939.1, "fetch_scale": 2.0, "write_scale": 1.0,
+        "source_sha256": "820800b3ff5373f9f148bf35ac40925d69bcc578f999c8d58b411164ae5ff0dd",
+        "fetch_kib": 170306.3, "write_kib": 5939.4, "fetch_scale": 2.0, "write_scale": 1.0,
     },
     ("small", "bf16", 16, -1, "planned"): {
-        "source_sha256": "c9dba6b0f5d5dd04ce8c97c907142e3ffc1563e2d6323b27e5e9604bc61a6b36",
-        "fetch_kib": 34306.3, "write_kib": 4412.8, "fetch_scale": 2.0, "write_scale": 1.0,
+        "source_sha256": "820800b3ff5373f9f148bf35ac40925d69bcc578f999c8d58b411164ae5ff0dd",
+        "fetch_kib": 34303.6, "write_kib": 4412.8, "fetch_scale": 2.0, "write_scale": 1.0,
     },
     ("llama8b", "fp8", 16, -1, "planned"): {
-        "source_sha256": "c9dba6b0f5d5dd04ce8c97c907142e3ffc1563e2d6323b27e5e9604bc61a6b36",
-        "fetch_kib": 86288.0, "write_kib": 4805.9, "fetch_scale": 2.0, "write_scale": 1.0,
+        "source_sha256": "820800b3ff5373f9f148bf35ac40925d69bcc578f999c8d58b411164ae5ff0dd",
+        "fetch_kib": 86285.4, "write_kib": 4806.0, "fetch_scale": 2.0, "write_scale": 1.0,
     },
     ("small", "fp8", 16, -1, "planned"): {
-        "source_sha256": "c9dba6b0f5d5dd04ce8c97c907142e3ffc1563e2d6323b27e5e9604bc61a6b36",
-        "fetch_kib": 18919.0, "write_kib": 5530.5, "fetch_scale": 2.0, "write_scale": 1.0,
+        "source_sha256": "820800b3ff5373f9f148bf35ac40925d69bcc578f999c8d58b411164ae5ff0dd",
+        "fetch_kib": 18918.9, "write_kib": 5530.5, "fetch_scale": 2.0, "write_scale": 1.0,
     },
     ("long", "bf16", 16, -1, "planned"): {
-        "source_sha256": "c9dba6b0f5d5dd04ce8c97c907142e3ffc1563e2d6323b27e5e9604bc61a6b36",
-        "fetch_kib": 1054198.5, "write_kib": 5730.6, "fetch_scale": 2.0, "write_scale": 1.0,
+        "source_sha256": "820800b3ff5373f9f148bf35ac40925d69bcc578f999c8d58b411164ae5ff0dd",
+        "fetch_kib": 1054201.7, "write_kib": 5730.8, "fetch_scale": 2.0, "write_scale": 1.0,
     },
     ("long", "fp8", 16, -1, "planned"): {
-        "source_sha256": "c9dba6b0f5d5dd04ce8c97c907142e3ffc1563e2d6323b27e5e9604bc61a6b36",
-        "fetch_kib": 529618.0, "write_kib": 5454.3, "fetch_scale": 2.0, "write_scale": 1.0,
+        "source_sha256": "820800b3ff5373f9f148bf35ac40925d69bcc578f999c8d58b411164ae5ff0dd",
+        "fetch_kib": 529611.1, "write_kib": 5453.8, "fetch_scale": 2.0, "write_scale": 1.0,
     },
 }
 
