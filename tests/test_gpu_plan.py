@@ -177,3 +177,48 @@ def test_plan_for_other_inputs_is_refused():
                                       plan_host=other, plan_dev=to_dev(other), workspace=good.workspace)
     torch.cuda.synchronize()
     assert np.all(to_host(out) == 0)          # nothing ran
+
+
+@pytest.mark.parametrize("Hq,Hkv,d,bs,dt", [(32, 8, 128, 16, "bf16"), (14, 2, 64, 16, "bf16"),
+                                            (8, 2, 128, 32, "fp8"), (8, 8, 64, 8, "f32")])
+def test_planned_steps_in_sequence(Hq, Hkv, d, bs, dt):
+    """Three decode steps in a row, each with its plan for lengths one longer
+    than the step before: the tokens one step stores (after the chunk loop and
+    nontemporal at d 128 over bf16, by the owner of the last chunk over fp8)
+    are read from the pool by the next. Outputs and pools match the unplanned
+    step run beside it on its own copy of the pools."""
+    torch = need_gpu()
+    final = np.array([3, 17, 40, 333, 1000, 2049, 16, 64])
+    w = W.make_custom(lens=final, Hq=Hq, Hkv=Hkv, d=d, bs=bs, q_dtype="f32" if dt == "f32" else "bf16",
+                      cache_dtype=dt, cfg=2100 + d + bs)
+    s = w.spec
+    pl, ref = DeviceStep(w), DeviceStep(w)
+    rng = np.random.default_rng([108, 2101, d, bs])
+    ws = pkv.paged_decode_attn_workspace(s.S, s.Hq, s.Hkv, s.d, w.max_context_len, BAL)
+
+    def draw(shape):
+        x = rng.standard_normal(shape).astype(np.float32)
+        return to_dev(x if dt == "f32" else W.to_bf16_bits(x))
+    for t in range(3):
+        lens = (final - 2 + t).astype(w.context_lens.dtype)
+        print(f"[case] step {t} d={d} bs={bs} cache={dt} lens={lens.tolist()}", flush=True)
+        lens_d = to_dev(lens)
+        q, kn, vn = draw((s.S, s.Hq, s.d)), draw((s.S, s.Hkv, s.d)), draw((s.S, s.Hkv, s.d))
+        kw = dict(softmax_scale=w.softmax_scale, k_scale=w.k_scale, v_scale=w.v_scale, k_inv_scale=w.k_inv_scale,
+                  v_inv_scale=w.v_inv_scale)
+        plan = pkv.DecodePlan(lens, Hq=s.Hq, Hkv=s.Hkv, d=s.d, bs=s.bs, cache_dtype_code=CODE[dt],
+                              max_context_len=w.max_context_len)
+        got = torch.full((s.S, s.Hq, s.d), float("nan"), dtype=torch.float32, device="cuda")
+        plan(got, q, pl.k_cache, pl.v_cache, pl.tables, lens_d, k_new=kn, v_new=vn, **kw)
+        want = torch.full_like(got, float("nan"))
+        pkv.paged_decode_step(want, q, kn, vn, ref.k_cache, ref.v_cache, ref.tables, lens_d,
+                              max_context_len=w.max_context_len, workspace=ws, **kw)
+        torch.cuda.synchronize()
+        got_h, want_h = to_host(got), to_host(want)
+        if plan.n_workers == 4 * torch.cuda.get_device_properties(0).multi_processor_count:
+            assert np.array_equal(got_h, want_h), f"step {t}: planned step differs from the unplanned step"
+        else:
+            assert_rows_close(got_h, want_h.astype(np.float64), TOL[dt], f"step {t}")
+        assert not np.isnan(got_h).any()
+        assert same_bits(to_host(pl.k_cache), to_host(ref.k_cache)), f"step {t}: K pool differs"
+        assert same_bits(to_host(pl.v_cache), to_host(ref.v_cache)), f"step {t}: V pool differs"
